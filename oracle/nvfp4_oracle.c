@@ -1,0 +1,630 @@
+/*
+ * nvfp4_oracle.c -- plain, slow CPU oracle for NVFP4 block quantization with
+ * ScaleSearch.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library. The product path (the HIP
+ * library and its Python binding) never calls, links or imports it, and this
+ * file shares no code, header, table or helper with the product.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [SS]  "技術サマリー：ブロック浮動小数点スケールを検索せよ！" (gist.science summary
+ *        of the ScaleSearch paper), section 手法 > ScaleSearch: the max-scaling
+ *        default s = round(amax/6), the offset rule s(f) = reinterpret(
+ *        reinterpret(s, int8) + f, UE4M3) (メカニズム), the exhaustive search of
+ *        a small offset range for the least block MSE (検索戦略), and the
+ *        bimodal optimum (根拠).
+ *  [SSA] same page, ScaleSearchAttention: Hadamard incoherence processing
+ *        (非干渉処理（IP）と絶対値低減) and the attention-sink cache that keeps the
+ *        first and last KV blocks at full precision (アテンション・シンク対応混合精度
+ *        キャッシング).
+ *  [NV]  "NVIDIAのFP4推論が50倍の効率を実現", section 超低精度推論を支えるアーキテクチャ:
+ *        E2M1 elements, one E4M3 scale per 16-value micro-block, and a second
+ *        FP32 per-tensor scale.
+ *  [BEV] "自動運転モデル BEVFormer の NVIDIA Blackwell B200 FP8/FP4 CUDAカーネル・
+ *        チューニング", sections 7 and 1-A/1-B: e4m3 = 1 sign/4 exponent/3 mantissa
+ *        bits, e2m1 = 1/2/1 bits, FP8 range max/448 and FP4 range max/6, two FP4
+ *        values packed per byte.
+ *
+ * Where the pages leave a step open, the reading taken is stated at the step.
+ *
+ * Arithmetic: every float operation below is one IEEE-754 binary32 operation
+ * rounded to nearest-even (x86-64 SSE, FLT_EVAL_METHOD == 0). The file must be
+ * built with -ffp-contract=off and without -ffast-math, so that no product and
+ * sum are fused. Subnormals are kept.
+ *
+ * Parity status: every function here is pinned by the CPU tests (closed forms,
+ * a hand-derived worked example, invariants, an independent NumPy brute force
+ * and published statistics of the offset optimum). The Hadamard transform is
+ * pinned against closed forms and a library Hadamard matrix.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+#define ORACLE_ENOMEM 2
+
+/* dtype tags used by the oracle's own entry points */
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* ------------------------------------------------------------------------ */
+/* Element format: E2M1 ([BEV] 1-A/1-B, [NV]).                              */
+/* 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit. The non-negative   */
+/* values, by magnitude code 0..7, are 0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, */
+/* 6; 6 is the largest, as the default scale amax/6 of [SS] implies.       */
+/* ------------------------------------------------------------------------ */
+static const float E2M1_MAG[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+/* Magnitude code of y >= 0: the nearest grid value; a value exactly halfway
+ * between two grid values takes the even code (round-to-nearest-even of the
+ * format, whose mantissa LSB is the code LSB); anything above 6, +Inf
+ * included, saturates to code 7. Returns -1 for NaN or negative input. */
+int oracle_e2m1_code(float y)
+{
+    if (!(y >= 0.0f))
+        return -1;
+    int c = 0;
+    for (int k = 0; k < 7; ++k) {
+        /* midpoint of two neighbouring grid values: exact in double */
+        double mid = 0.5 * ((double)E2M1_MAG[k] + (double)E2M1_MAG[k + 1]);
+        double yy = (double)y;
+        int up = (yy > mid) || (yy == mid && ((k + 1) % 2 == 0));
+        if (!up)
+            break;
+        c = k + 1;
+    }
+    return c;
+}
+
+float oracle_e2m1_value(int code)
+{
+    float m = E2M1_MAG[code & 7];
+    return (code & 8) ? -m : m;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block-scale format: unsigned E4M3 ([BEV] 1-A: 4 exponent bits, 3        */
+/* mantissa bits, bias 7; [BEV] sec. 7: largest value 448). The sign bit is */
+/* unused (the scale is non-negative), so a scale is a pattern p in 0..127; */
+/* 127 (exponent and mantissa all ones) is NaN and never a scale.           */
+/* ------------------------------------------------------------------------ */
+float oracle_e4m3_value(int p)
+{
+    if (p < 0 || p >= 127)
+        return NAN;
+    int e = p >> 3, m = p & 7;
+    if (e == 0)
+        return (float)ldexp((double)m, -9); /* subnormal: m * 2^-9 */
+    return (float)ldexp(1.0 + m / 8.0, e - 7);
+}
+
+/* Round t >= 0 to the nearest E4M3 value (ties to the even pattern, i.e.
+ * even mantissa), saturating at 448 (pattern 126). Reading: the pages write
+ * "round" in s = round(amax/6); round-to-nearest-even with saturation is the
+ * plain meaning for a float format with no infinity. -1 for NaN/negative. */
+int oracle_e4m3_encode(float t)
+{
+    if (!(t >= 0.0f))
+        return -1;
+    if (t >= 448.0f)
+        return 126;
+    /* values grow with the pattern, so binary search the largest p with
+     * value(p) <= t */
+    int lo = 0, hi = 126;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if ((double)oracle_e4m3_value(mid) <= (double)t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int p = lo; /* p <= 125 because t < 448 */
+    double below = oracle_e4m3_value(p), above = oracle_e4m3_value(p + 1);
+    double mid = 0.5 * (below + above); /* exact in double */
+    if ((double)t > mid)
+        return p + 1;
+    if ((double)t < mid)
+        return p;
+    return (p % 2 == 0) ? p : p + 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Input access.                                                            */
+/* ------------------------------------------------------------------------ */
+static float bf16_bits_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static float load_elem(const void *x, int dtype, int64_t i)
+{
+    if (dtype == ORACLE_BF16)
+        return bf16_bits_to_float(((const uint16_t *)x)[i]);
+    return ((const float *)x)[i];
+}
+
+static uint32_t float_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return u;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Global scale. [NV]: a second, FP32 per-tensor scale sets the global      */
+/* range. Reading (the [SS] formula has no tensor scale): the tensor scale  */
+/* is a decode scale S_g = A / (6 * 448), A = max |x| over the quantized    */
+/* region, so that the block scale t = (amax_b / 6) / S_g of the largest    */
+/* block lands on the largest E4M3 value 448; reconstruction is             */
+/* x ~ V[code] * s_block * S_g. S_g = 0 (all-zero region or underflow)      */
+/* becomes 1.                                                               */
+/* ------------------------------------------------------------------------ */
+static float global_scale_from_amax(float A)
+{
+    float sg = A / 2688.0f; /* 2688 = 6 * 448 */
+    if (sg == 0.0f)
+        sg = 1.0f;
+    return sg;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One 16-element block ([NV]: 16-value micro-block; [SS]: ScaleSearch).    */
+/* ------------------------------------------------------------------------ */
+
+/* Squared error of coding the 16 magnitudes ax[] with block-scale pattern p
+ * under tensor scale sg, as the sum of squared differences between each
+ * element and its reconstruction, added strictly left to right in FP32
+ * (the search ranks candidates by MSE = this / 16, [SS] 検索戦略).
+ * Reading: the quantizer multiplies by the encode scale r = 1/d of the
+ * candidate's decode scale d = s_p * S_g; a candidate whose r is not finite
+ * (p = 0, or d so small that 1/d overflows) codes every element as 0. */
+static float block_sse(const float ax[16], int p, float sg, uint8_t mag_codes[16])
+{
+    float s = oracle_e4m3_value(p);
+    float d = s * sg;
+    float r = 1.0f / d;
+    int zero = !isfinite(r);
+    float sse = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+        int c;
+        float xhat;
+        if (zero) {
+            c = 0;
+            xhat = 0.0f;
+        } else {
+            float y = ax[i] * r;
+            c = oracle_e2m1_code(y);
+            xhat = E2M1_MAG[c] * d;
+        }
+        float e = ax[i] - xhat;
+        float q = e * e;
+        sse = (i == 0) ? q : sse + q;
+        if (mag_codes)
+            mag_codes[i] = (uint8_t)c;
+    }
+    return sse;
+}
+
+float oracle_block_sse(const float x[16], float sg, int p)
+{
+    float ax[16];
+    for (int i = 0; i < 16; ++i)
+        ax[i] = fabsf(x[i]);
+    if (p < 0 || p > 126)
+        return NAN;
+    return block_sse(ax, p, sg, NULL);
+}
+
+/* Default pattern of a block ([SS] メカニズム: s = round(amax / 6)), in units
+ * of the tensor scale: t = (a_b / 6) / S_g, each division rounded once. */
+static int default_pattern(float amax_b, float sg)
+{
+    float t = (amax_b / 6.0f) / sg;
+    return oracle_e4m3_encode(t);
+}
+
+/* ScaleSearch on one block. x[16] is the block (signed), sg a positive
+ * finite tensor scale. Writes 8 code bytes and returns the scale pattern.
+ * The candidates are the E4M3 patterns p0 + f for integer f in [f_lo, f_hi]
+ * ([SS] メカニズム: the offset is added to the scale's bit pattern, so p0 + f
+ * is the f-th neighbouring representable scale). f = 0 is visited first,
+ * then f_lo, f_lo+1, ..., f_hi; a pattern outside 0..126 is skipped (the
+ * int8 reinterpretation would flip the sign or give NaN); the first visited
+ * candidate with strictly smaller squared error wins, so ties keep f = 0 and
+ * then the lowest f. */
+static int search_block(const float x[16], float sg, int f_lo, int f_hi,
+                        uint8_t codes[8], int *chosen_f)
+{
+    float ax[16];
+    float amax_b = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+        ax[i] = fabsf(x[i]);
+        if (ax[i] > amax_b)
+            amax_b = ax[i];
+    }
+    int p0 = default_pattern(amax_b, sg);
+
+    int best_p = p0, best_f = 0;
+    uint8_t best_mag[16];
+    float best_sse = block_sse(ax, p0, sg, best_mag);
+    for (int f = f_lo; f <= f_hi; ++f) {
+        if (f == 0)
+            continue;
+        int p = p0 + f;
+        if (p < 0 || p > 126)
+            continue;
+        uint8_t mag[16];
+        float sse = block_sse(ax, p, sg, mag);
+        if (sse < best_sse) {
+            best_sse = sse;
+            best_p = p;
+            best_f = f;
+            memcpy(best_mag, mag, 16);
+        }
+    }
+    /* Codes: a nibble is sign << 3 | magnitude code (E2M1 sign-magnitude),
+     * the sign copied from the input even for a zero code. Reading: two
+     * nibbles per byte with the even element in the low nibble. */
+    for (int j = 0; j < 8; ++j) {
+        uint8_t n0 = (uint8_t)((signbit(x[2 * j]) ? 8 : 0) | best_mag[2 * j]);
+        uint8_t n1 = (uint8_t)((signbit(x[2 * j + 1]) ? 8 : 0) | best_mag[2 * j + 1]);
+        codes[j] = (uint8_t)(n0 | (n1 << 4));
+    }
+    if (chosen_f)
+        *chosen_f = best_f;
+    return best_p;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Threads: a static partition of block rows; every block is computed the   */
+/* same way whatever the thread count, so results do not depend on it.      */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const void *x;
+    int dtype;
+    int64_t rows, cols, r0, r1;
+    int f_lo, f_hi;
+    float sg;
+    int sg_ok;
+    uint8_t *codes, *scales;
+    int8_t *chosen_f;
+} qjob_t;
+
+static void quantize_rows(const qjob_t *J)
+{
+    int64_t nb = J->cols / 16;
+    for (int64_t r = J->r0; r < J->r1; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            float x[16];
+            int finite = 1;
+            for (int i = 0; i < 16; ++i) {
+                x[i] = load_elem(J->x, J->dtype, r * J->cols + b * 16 + i);
+                if (!isfinite(x[i]))
+                    finite = 0;
+            }
+            uint8_t *cb = J->codes + r * (J->cols / 2) + b * 8;
+            uint8_t *sb = J->scales + r * nb + b;
+            int fsel = 0;
+            if (!J->sg_ok || !finite) {
+                /* non-finite contract: scale NaN pattern, codes zero */
+                memset(cb, 0, 8);
+                *sb = 0x7F;
+            } else {
+                *sb = (uint8_t)search_block(x, J->sg, J->f_lo, J->f_hi, cb, &fsel);
+            }
+            if (J->chosen_f)
+                J->chosen_f[r * nb + b] = (int8_t)fsel;
+        }
+    }
+}
+
+static void *quantize_thread(void *arg)
+{
+    quantize_rows((const qjob_t *)arg);
+    return NULL;
+}
+
+static int run_quantize_rows(qjob_t base, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nthreads == 1 || base.rows < 2) {
+        base.r0 = 0;
+        base.r1 = base.rows;
+        quantize_rows(&base);
+        return ORACLE_OK;
+    }
+    pthread_t th[256];
+    int running[256];
+    qjob_t jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = base;
+        jobs[t].r0 = base.rows * t / nthreads;
+        jobs[t].r1 = base.rows * (t + 1) / nthreads;
+        running[t] = pthread_create(&th[t], NULL, quantize_thread, &jobs[t]) == 0;
+        if (!running[t])
+            quantize_rows(&jobs[t]); /* could not start a thread: do it here */
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (running[t])
+            pthread_join(th[t], NULL);
+    return ORACLE_OK;
+}
+
+/* Global amax A = max |x| over the region, as the largest absolute-value
+ * bit pattern (exact and order-free). Returns 0 if a NaN/Inf was seen. */
+static int region_amax(const void *x, int dtype, int64_t n, float *A)
+{
+    uint32_t best = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u = float_bits(load_elem(x, dtype, i)) & 0x7FFFFFFFu;
+        if (u > best)
+            best = u;
+    }
+    float a;
+    memcpy(&a, &best, 4);
+    *A = a;
+    return best < 0x7F800000u;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Hadamard pre-transform ([SSA] 非干渉処理: a Hadamard transform as in      */
+/* QuIP#). Reading: per contiguous 128-vector, y = x * H / sqrt(128) with H */
+/* the 128 x 128 Sylvester matrix in natural order (H[j][k] = (-1)^popcount */
+/* (j & k)), no random signs. The sum is taken in double in natural order   */
+/* (exact while the 128 inputs span less than about 2^38 in magnitude),     */
+/* multiplied by the double nearest 1/sqrt(128), then rounded to binary32.   */
+/* ------------------------------------------------------------------------ */
+static int popcount_parity(unsigned v)
+{
+    int p = 0;
+    while (v) {
+        p ^= 1;
+        v &= v - 1;
+    }
+    return p;
+}
+
+int oracle_hadamard128(const void *x, int dtype, int64_t nvec, float *y)
+{
+    if (!x || !y || nvec < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    const double c = sqrt(1.0 / 128.0); /* correctly rounded 2^-3.5 */
+    for (int64_t v = 0; v < nvec; ++v) {
+        double in[128];
+        for (int k = 0; k < 128; ++k)
+            in[k] = (double)load_elem(x, dtype, v * 128 + k);
+        for (int j = 0; j < 128; ++j) {
+            double s = 0.0;
+            for (int k = 0; k < 128; ++k)
+                s += popcount_parity((unsigned)(j & k)) ? -in[k] : in[k];
+            y[v * 128 + j] = (float)(s * c);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Entry points.                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Quantize a contiguous rows x cols tensor (blocks of 16 along the last
+ * dimension). If gscale_given, *gscale is read as the tensor scale (it must be
+ * positive and finite, else every block gets the non-finite contract);
+ * otherwise it is computed from the global amax and written. A NaN/Inf in the
+ * region (computed mode) gives S_g = NaN and every block scale 0x7F with zero
+ * codes; in given mode only the blocks holding a NaN/Inf get that. hadamard:
+ * transform each 128-vector first (cols % 128 == 0) and quantize the FP32
+ * result. chosen_f (nullable) receives the winning offset per block. */
+int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int f_lo,
+                    int f_hi, int hadamard, int gscale_given, float *gscale,
+                    uint8_t *codes, uint8_t *scales, int8_t *chosen_f, int nthreads)
+{
+    if (!x || !gscale || !codes || !scales || rows < 0 || cols <= 0 || cols % 16 ||
+        f_lo > 0 || f_hi < 0 || f_lo < -126 || f_hi > 126 ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_BF16) || (hadamard && cols % 128))
+        return ORACLE_EINVAL;
+    const void *src = x;
+    int sdt = dtype;
+    float *ybuf = NULL;
+    int64_t n = rows * cols;
+    if (hadamard) {
+        ybuf = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+        if (!ybuf)
+            return ORACLE_ENOMEM;
+        oracle_hadamard128(x, dtype, n / 128, ybuf);
+        src = ybuf;
+        sdt = ORACLE_F32;
+    }
+    float sg;
+    int sg_ok;
+    if (gscale_given) {
+        sg = *gscale;
+        sg_ok = (sg > 0.0f) && isfinite(sg);
+    } else {
+        float A;
+        int finite = region_amax(src, sdt, n, &A);
+        if (finite) {
+            sg = global_scale_from_amax(A);
+            sg_ok = 1;
+        } else {
+            sg = NAN;
+            sg_ok = 0;
+        }
+        *gscale = sg;
+    }
+    qjob_t J;
+    memset(&J, 0, sizeof J);
+    J.x = src;
+    J.dtype = sdt;
+    J.rows = rows;
+    J.cols = cols;
+    J.f_lo = f_lo;
+    J.f_hi = f_hi;
+    J.sg = sg;
+    J.sg_ok = sg_ok;
+    J.codes = codes;
+    J.scales = scales;
+    J.chosen_f = chosen_f;
+    int rc = run_quantize_rows(J, nthreads);
+    free(ybuf);
+    return rc;
+}
+
+/* Round binary32 to bfloat16, nearest-even (NaN -> quiet NaN, sign kept). */
+static uint16_t float_to_bf16_rne(float f)
+{
+    uint32_t u = float_bits(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* Dequantize: x^ = (-1)^sign * (V[code] * (s_p * S_g)), the product of the
+ * block's decode scale and the grid value rounded once each, the same value
+ * the search scored. A scale byte >= 127 decodes as NaN. out_dtype 0: FP32,
+ * 1: bf16 (nearest-even of the FP32 value). */
+int oracle_dequantize(const uint8_t *codes, const uint8_t *scales, float gscale,
+                      int64_t rows, int64_t cols, int out_dtype, void *y)
+{
+    if (!codes || !scales || !y || rows < 0 || cols <= 0 || cols % 16 ||
+        (out_dtype != ORACLE_F32 && out_dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    int64_t nb = cols / 16;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            int p = scales[r * nb + b];
+            float d = oracle_e4m3_value(p) * gscale;
+            for (int i = 0; i < 16; ++i) {
+                int64_t e = r * cols + b * 16 + i;
+                uint8_t byte = codes[e / 2];
+                int nib = (e % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+                float v = E2M1_MAG[nib & 7] * d;
+                if (nib & 8)
+                    v = -v;
+                if (out_dtype == ORACLE_F32)
+                    ((float *)y)[e] = v;
+                else
+                    ((uint16_t *)y)[e] = float_to_bf16_rne(v);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Attention-sink KV mode ([SSA] アテンション・シンク対応混合精度キャッシング).
+ * kv is [B, H, T, D] contiguous (blocks of 16 along D). For each (b, h), the
+ * first n_first and last n_last tokens are kept verbatim in sink[B, H,
+ * n_first + n_last, D] (first, then last; same dtype as kv), and the middle
+ * T - n_first - n_last tokens are quantized as one region: the global amax is
+ * taken over the middle tokens only (reading: sink tokens are not coded, so
+ * they do not set the range). codes[B, H, Tm, D/2], scales[B, H, Tm, D/16]. */
+int oracle_quantize_kv_sink(const void *kv, int dtype, int64_t B, int64_t H, int64_t T,
+                            int64_t D, int64_t n_first, int64_t n_last, int f_lo,
+                            int f_hi, int hadamard, int gscale_given, float *gscale,
+                            uint8_t *codes, uint8_t *scales, void *sink, int nthreads)
+{
+    if (!kv || !sink || B < 0 || H < 0 || T < 0 || D <= 0 || n_first < 0 || n_last < 0 ||
+        n_first + n_last > T || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    size_t es = dtype == ORACLE_BF16 ? 2 : 4;
+    int64_t Tm = T - n_first - n_last, NS = n_first + n_last;
+    int64_t BH = B * H;
+    unsigned char *mid = (unsigned char *)malloc((size_t)(BH * Tm * D > 0 ? BH * Tm * D : 1) * es);
+    if (!mid)
+        return ORACLE_ENOMEM;
+    const unsigned char *src = (const unsigned char *)kv;
+    unsigned char *snk = (unsigned char *)sink;
+    for (int64_t g = 0; g < BH; ++g) {
+        const unsigned char *base = src + (size_t)(g * T * D) * es;
+        memcpy(snk + (size_t)(g * NS * D) * es, base, (size_t)(n_first * D) * es);
+        memcpy(snk + (size_t)((g * NS + n_first) * D) * es,
+               base + (size_t)((T - n_last) * D) * es, (size_t)(n_last * D) * es);
+        memcpy(mid + (size_t)(g * Tm * D) * es, base + (size_t)(n_first * D) * es,
+               (size_t)(Tm * D) * es);
+    }
+    int rc = oracle_quantize(mid, dtype, BH * Tm, D, f_lo, f_hi, hadamard, gscale_given,
+                             gscale, codes, scales, NULL, nthreads);
+    free(mid);
+    return rc;
+}
+
+/* Inverse of the sink mode: y[B, H, T, D] with the sink tokens copied exactly
+ * (converted to out_dtype; bf16 -> FP32 is exact) and the middle dequantized. */
+int oracle_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scales, float gscale,
+                              const void *sink, int sink_dtype, int64_t B, int64_t H,
+                              int64_t T, int64_t D, int64_t n_first, int64_t n_last,
+                              int out_dtype, void *y)
+{
+    if (!codes || !scales || !sink || !y || n_first < 0 || n_last < 0 || n_first + n_last > T ||
+        D <= 0 || D % 16)
+        return ORACLE_EINVAL;
+    int64_t Tm = T - n_first - n_last, NS = n_first + n_last, BH = B * H;
+    size_t os = out_dtype == ORACLE_BF16 ? 2 : 4;
+    void *mid = malloc((size_t)(BH * Tm * D > 0 ? BH * Tm * D : 1) * os);
+    if (!mid)
+        return ORACLE_ENOMEM;
+    int rc = oracle_dequantize(codes, scales, gscale, BH * Tm, D, out_dtype, mid);
+    if (rc) {
+        free(mid);
+        return rc;
+    }
+    for (int64_t g = 0; g < BH; ++g) {
+        for (int64_t t = 0; t < T; ++t) {
+            for (int64_t k = 0; k < D; ++k) {
+                float v;
+                int from_mid = 0;
+                int64_t mi = 0;
+                if (t < n_first)
+                    v = load_elem(sink, sink_dtype, (g * NS + t) * D + k);
+                else if (t >= T - n_last)
+                    v = load_elem(sink, sink_dtype, (g * NS + n_first + (t - (T - n_last))) * D + k);
+                else {
+                    from_mid = 1;
+                    mi = (g * Tm + (t - n_first)) * D + k;
+                    v = 0.0f;
+                }
+                int64_t o = (g * T + t) * D + k;
+                if (from_mid) {
+                    if (out_dtype == ORACLE_F32)
+                        ((float *)y)[o] = ((float *)mid)[mi];
+                    else
+                        ((uint16_t *)y)[o] = ((uint16_t *)mid)[mi];
+                } else {
+                    if (out_dtype == ORACLE_F32)
+                        ((float *)y)[o] = v;
+                    else
+                        ((uint16_t *)y)[o] = float_to_bf16_rne(v);
+                }
+            }
+        }
+    }
+    free(mid);
+    return rc;
+}
+
+int oracle_abi_version(void) { return 1; }
+
+/* Batched codec helpers for the exhaustive codec tests. */
+void oracle_e2m1_code_batch(const float *y, int64_t n, int8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (int8_t)oracle_e2m1_code(y[i]);
+}
+
+void oracle_e4m3_encode_batch(const float *t, int64_t n, int16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (int16_t)oracle_e4m3_encode(t[i]);
+}

@@ -1,0 +1,202 @@
+"""ctypes binding of the C oracle (``nvfp4_oracle.c``).
+
+TEST INFRASTRUCTURE (see the package docstring). Host NumPy arrays only:
+FP32 tensors are ``float32`` arrays and bf16 tensors are ``uint16`` arrays
+holding the bfloat16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+F32 = 0
+BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# The oracle is compiled with plain gcc: IEEE binary32 on x86-64 SSE, no
+# contraction of a*b+c into FMA, no fast-math.
+GCC_CMD = [
+    "gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+    "-fno-fast-math", "-fPIC", "-shared", "-pthread", _SRC, "-o", _LIB, "-lm",
+]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle library (``force=False``: only if it is missing)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = GCC_CMD[:-3] + ["-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            L = ctypes.CDLL(_LIB)
+            i64, i32, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_float
+            vp = ctypes.c_void_p
+            L.oracle_e2m1_code.argtypes = [f32]
+            L.oracle_e2m1_code.restype = i32
+            L.oracle_e4m3_value.argtypes = [i32]
+            L.oracle_e4m3_value.restype = f32
+            L.oracle_e4m3_encode.argtypes = [f32]
+            L.oracle_e4m3_encode.restype = i32
+            L.oracle_e2m1_code_batch.argtypes = [vp, i64, vp]
+            L.oracle_e2m1_code_batch.restype = None
+            L.oracle_e4m3_encode_batch.argtypes = [vp, i64, vp]
+            L.oracle_e4m3_encode_batch.restype = None
+            L.oracle_block_sse.argtypes = [vp, f32, i32]
+            L.oracle_block_sse.restype = f32
+            L.oracle_quantize.argtypes = [vp, i32, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, i32]
+            L.oracle_quantize.restype = i32
+            L.oracle_dequantize.argtypes = [vp, vp, f32, i64, i64, i32, vp]
+            L.oracle_dequantize.restype = i32
+            L.oracle_quantize_kv_sink.argtypes = [vp, i32, i64, i64, i64, i64, i64, i64, i32, i32,
+                                                  i32, i32, vp, vp, vp, vp, i32]
+            L.oracle_quantize_kv_sink.restype = i32
+            L.oracle_dequantize_kv_sink.argtypes = [vp, vp, f32, vp, i32, i64, i64, i64, i64, i64,
+                                                    i64, i32, vp]
+            L.oracle_dequantize_kv_sink.restype = i32
+            L.oracle_hadamard128.argtypes = [vp, i32, i64, vp]
+            L.oracle_hadamard128.restype = i32
+            _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _dtype_of(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs are float32 or uint16 (bf16 bits)")
+
+
+def _threads(n):
+    return int(n) if n else (os.cpu_count() or 1)
+
+
+def e2m1_code(y: np.ndarray) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.int8)
+    lib().oracle_e2m1_code_batch(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(t: np.ndarray) -> np.ndarray:
+    t = np.ascontiguousarray(t, dtype=np.float32)
+    out = np.empty(t.shape, dtype=np.int16)
+    lib().oracle_e4m3_encode_batch(_ptr(t), t.size, _ptr(out))
+    return out
+
+
+def e4m3_value(p: int) -> float:
+    return float(lib().oracle_e4m3_value(int(p)))
+
+
+def block_sse(x16, sg: float, p: int) -> float:
+    x = np.ascontiguousarray(x16, dtype=np.float32).reshape(16)
+    return float(np.float32(lib().oracle_block_sse(_ptr(x), ctypes.c_float(sg), int(p))))
+
+
+def quantize(x: np.ndarray, f_lo: int = -2, f_hi: int = 6, hadamard: bool = False,
+             gscale: float | None = None, want_f: bool = False, nthreads: int | None = None):
+    """Returns (codes[R, K/2] u8, scales[R, K/16] u8, gscale f32[, chosen_f[R, K/16] i8])."""
+    x = np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    K = x.shape[-1]
+    R = x.size // K if K else 0
+    codes = np.empty((R, K // 2), dtype=np.uint8)
+    scales = np.empty((R, K // 16), dtype=np.uint8)
+    g = np.array([0.0 if gscale is None else gscale], dtype=np.float32)
+    fsel = np.empty((R, K // 16), dtype=np.int8) if want_f else None
+    rc = lib().oracle_quantize(_ptr(x), dt, R, K, f_lo, f_hi, int(hadamard),
+                               int(gscale is not None), _ptr(g), _ptr(codes), _ptr(scales),
+                               _ptr(fsel) if want_f else None, _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_quantize failed ({rc})")
+    shp = x.shape[:-1]
+    out = (codes.reshape(*shp, K // 2), scales.reshape(*shp, K // 16), np.float32(g[0]))
+    if want_f:
+        return out + (fsel.reshape(*shp, K // 16),)
+    return out
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, gscale: float, out: str = "f32"):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    K = codes.shape[-1] * 2
+    R = codes.size * 2 // K if K else 0
+    odt = F32 if out == "f32" else BF16
+    y = np.empty(codes.shape[:-1] + (K,), dtype=np.float32 if odt == F32 else np.uint16)
+    rc = lib().oracle_dequantize(_ptr(codes), _ptr(scales), ctypes.c_float(gscale), R, K, odt,
+                                 _ptr(y))
+    if rc:
+        raise ValueError(f"oracle_dequantize failed ({rc})")
+    return y
+
+
+def quantize_kv_sink(kv: np.ndarray, n_first: int, n_last: int, f_lo: int = -2, f_hi: int = 6,
+                     hadamard: bool = False, gscale: float | None = None,
+                     nthreads: int | None = None):
+    """kv [B, H, T, D] -> (codes[B,H,Tm,D/2], scales[B,H,Tm,D/16], gscale, sink[B,H,nf+nl,D])."""
+    kv = np.ascontiguousarray(kv)
+    dt = _dtype_of(kv)
+    B, H, T, D = kv.shape
+    Tm = T - n_first - n_last
+    codes = np.empty((B, H, Tm, D // 2), dtype=np.uint8)
+    scales = np.empty((B, H, Tm, D // 16), dtype=np.uint8)
+    sink = np.empty((B, H, n_first + n_last, D), dtype=kv.dtype)
+    g = np.array([0.0 if gscale is None else gscale], dtype=np.float32)
+    rc = lib().oracle_quantize_kv_sink(_ptr(kv), dt, B, H, T, D, n_first, n_last, f_lo, f_hi,
+                                       int(hadamard), int(gscale is not None), _ptr(g),
+                                       _ptr(codes), _ptr(scales), _ptr(sink), _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_quantize_kv_sink failed ({rc})")
+    return codes, scales, np.float32(g[0]), sink
+
+
+def dequantize_kv_sink(codes, scales, gscale, sink, T: int, n_first: int, n_last: int,
+                       out: str = "f32"):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    sink = np.ascontiguousarray(sink)
+    B, H, _, D = sink.shape
+    odt = F32 if out == "f32" else BF16
+    y = np.empty((B, H, T, D), dtype=np.float32 if odt == F32 else np.uint16)
+    rc = lib().oracle_dequantize_kv_sink(_ptr(codes), _ptr(scales), ctypes.c_float(gscale),
+                                         _ptr(sink), _dtype_of(sink), B, H, T, D, n_first,
+                                         n_last, odt, _ptr(y))
+    if rc:
+        raise ValueError(f"oracle_dequantize_kv_sink failed ({rc})")
+    return y
+
+
+def hadamard128(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    if x.shape[-1] % 128:
+        raise ValueError("last dimension must be a multiple of 128")
+    y = np.empty(x.shape, dtype=np.float32)
+    rc = lib().oracle_hadamard128(_ptr(x), dt, x.size // 128, _ptr(y))
+    if rc:
+        raise ValueError(f"oracle_hadamard128 failed ({rc})")
+    return y

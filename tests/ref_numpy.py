@@ -1,0 +1,197 @@
+"""Independent NumPy brute force of NVFP4 ScaleSearch, used only to check the oracle.
+
+Written separately from the C oracle (no shared code or tables): codecs are
+nearest-value searches over value lists built from the bit layouts, and every
+block is scored against all 127 finite E4M3 scale patterns, each SSE summed
+with an explicit left-to-right loop over the 16 elements in float32.
+
+Formats (pages: "NVIDIAのFP4推論が50倍の効率を実現" 超低精度推論を支えるアーキテクチャ;
+BEVFormer B200 FP8/FP4 tuning article, 1-A and sec. 7): E2M1 = 1 sign, 2
+exponent (bias 1), 1 mantissa bit; UE4M3 = 4 exponent (bias 7), 3 mantissa
+bits, largest 448. Search: ScaleSearch summary page, 手法 > ScaleSearch.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def e2m1_values() -> np.ndarray:
+    """Magnitudes of E2M1 codes 0..7 from the bit layout (exponent bias 1)."""
+    vals = []
+    for code in range(8):
+        e, m = code >> 1, code & 1
+        vals.append(m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return np.array(vals, dtype=np.float64)
+
+
+def e4m3_values() -> np.ndarray:
+    """Values of UE4M3 patterns 0..126 (127 is NaN) from the bit layout."""
+    vals = []
+    for p in range(127):
+        e, m = p >> 3, p & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals, dtype=np.float64)
+
+
+_G = e2m1_values()
+_S = e4m3_values()
+
+
+def e2m1_nearest(y: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 magnitude code of y >= 0; exact halfway -> even code; y > 6 -> 7."""
+    y = np.asarray(y, dtype=np.float32)
+    yd = y.astype(np.float64)
+    best = np.zeros(y.shape, dtype=np.int64)
+    bestd = np.abs(yd - _G[0])
+    for c in range(1, 8):
+        d = np.abs(yd - _G[c])
+        better = d < bestd
+        tie = d == bestd
+        take = better | (tie & (c % 2 == 0))
+        best = np.where(take, c, best)
+        bestd = np.where(take, d, bestd)
+    # beyond the largest grid value the nearest is 6 (for huge y the float64
+    # distances above can tie by rounding)
+    best = np.where(yd >= _G[7], 7, best)
+    return best
+
+
+def e4m3_nearest(t: np.ndarray) -> np.ndarray:
+    """Nearest UE4M3 pattern of t >= 0; exact halfway -> even pattern; t >= 448 -> 126."""
+    t = np.asarray(t, dtype=np.float32).astype(np.float64)
+    hi = np.searchsorted(_S, t, side="left")  # first value >= t
+    hi = np.clip(hi, 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    dlo = np.abs(t - _S[lo])
+    dhi = np.abs(t - _S[hi])
+    p = np.where(dlo < dhi, lo, hi)
+    tie = (dlo == dhi) & (lo != hi)
+    p = np.where(tie, np.where(lo % 2 == 0, lo, hi), p)
+    p = np.where(t >= 448.0, 126, p)
+    return p.astype(np.int64)
+
+
+def sse_all_patterns(ax: np.ndarray, sg: np.float32) -> tuple[np.ndarray, np.ndarray]:
+    """ax [nb, 16] float32 magnitudes -> (sse [nb, 127] float32, codes [nb, 127, 16])."""
+    ax = np.asarray(ax, dtype=np.float32)
+    nb = ax.shape[0]
+    sse = np.empty((nb, 127), dtype=np.float32)
+    codes = np.empty((nb, 127, 16), dtype=np.int8)
+    sg = np.float32(sg)
+    G32 = _G.astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore", under="ignore"):
+        for p in range(127):
+            d = np.float32(np.float32(_S[p]) * sg)
+            r = np.float32(np.float32(1.0) / d)
+            if np.isfinite(r):
+                y = (ax * r).astype(np.float32)
+                c = e2m1_nearest(y)
+                xh = (G32[c] * d).astype(np.float32)
+            else:
+                c = np.zeros(ax.shape, dtype=np.int64)
+                xh = np.zeros(ax.shape, dtype=np.float32)
+            e = (ax - xh).astype(np.float32)
+            q = (e * e).astype(np.float32)
+            s = q[:, 0].copy()
+            for i in range(1, 16):
+                s = (s + q[:, i]).astype(np.float32)
+            sse[:, p] = s
+            codes[:, p, :] = c
+    return sse, codes
+
+
+def quantize_ref(x: np.ndarray, f_lo: int, f_hi: int, sg=None):
+    """x [R, K] float32 (finite) -> (codes [R, K/2], scales [R, K/16], sg, chosen_f)."""
+    x = np.asarray(x, dtype=np.float32)
+    R, K = x.shape
+    with np.errstate(over="ignore", under="ignore"):
+        if sg is None:
+            A = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+            sg = np.float32(A / np.float32(2688.0))
+            if sg == 0:
+                sg = np.float32(1.0)
+        sg = np.float32(sg)
+        blocks = x.reshape(-1, 16)
+        ax = np.abs(blocks)
+        amax = ax.max(axis=1)
+        t = ((amax / np.float32(6.0)).astype(np.float32) / sg).astype(np.float32)
+    p0 = e4m3_nearest(t)
+    sse, allcodes = sse_all_patterns(ax, sg)
+    nb = blocks.shape[0]
+    order = [0] + [f for f in range(f_lo, f_hi + 1) if f != 0]
+    best_p = p0.copy()
+    best_s = sse[np.arange(nb), p0]
+    best_f = np.zeros(nb, dtype=np.int64)
+    for f in order[1:]:
+        p = p0 + f
+        ok = (p >= 0) & (p <= 126)
+        pc = np.clip(p, 0, 126)
+        s = sse[np.arange(nb), pc]
+        win = ok & (s < best_s)
+        best_p = np.where(win, pc, best_p)
+        best_s = np.where(win, s, best_s)
+        best_f = np.where(win, f, best_f)
+    mag = allcodes[np.arange(nb), best_p, :].astype(np.uint8)
+    sign = (np.signbit(blocks)).astype(np.uint8) << 3
+    nib = (mag | sign).reshape(-1)
+    codes = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8).reshape(R, K // 2)
+    scales = best_p.astype(np.uint8).reshape(R, K // 16)
+    return codes, scales, sg, best_f.reshape(R, K // 16)
+
+
+def sse_patterns(ax: np.ndarray, sg: np.float32, p: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """SSE of each block ax[b] under its own pattern p[b] (0..126) -> (sse [nb], codes [nb,16])."""
+    ax = np.asarray(ax, dtype=np.float32)
+    sg = np.float32(sg)
+    G32 = _G.astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore", under="ignore"):
+        d = (_S[p].astype(np.float32) * sg).astype(np.float32)
+        r = (np.float32(1.0) / d).astype(np.float32)
+        zero = ~np.isfinite(r)
+        rr = np.where(zero, np.float32(0.0), r).astype(np.float32)
+        y = (ax * rr[:, None]).astype(np.float32)
+        c = e2m1_nearest(y)
+        c = np.where(zero[:, None], 0, c)
+        xh = (G32[c] * d[:, None]).astype(np.float32)
+        xh = np.where(zero[:, None], np.float32(0.0), xh)
+        e = (ax - xh).astype(np.float32)
+        q = (e * e).astype(np.float32)
+    s = q[:, 0].copy()
+    for i in range(1, 16):
+        s = (s + q[:, i]).astype(np.float32)
+    return s, c
+
+
+def quantize_ref_search(x: np.ndarray, f_lo: int, f_hi: int, sg=None):
+    """Same result as quantize_ref, scoring only the candidates p0 + f (faster)."""
+    x = np.asarray(x, dtype=np.float32)
+    R, K = x.shape
+    with np.errstate(over="ignore", under="ignore"):
+        if sg is None:
+            A = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+            sg = np.float32(A / np.float32(2688.0))
+            if sg == 0:
+                sg = np.float32(1.0)
+        sg = np.float32(sg)
+        blocks = x.reshape(-1, 16)
+        ax = np.abs(blocks)
+        amax = ax.max(axis=1)
+        t = ((amax / np.float32(6.0)).astype(np.float32) / sg).astype(np.float32)
+    p0 = e4m3_nearest(t)
+    best_s, best_c = sse_patterns(ax, sg, p0)
+    best_p = p0.copy()
+    best_f = np.zeros(p0.shape, dtype=np.int64)
+    for f in [f for f in range(f_lo, f_hi + 1) if f != 0]:
+        p = p0 + f
+        ok = (p >= 0) & (p <= 126)
+        pc = np.clip(p, 0, 126)
+        s, c = sse_patterns(ax, sg, pc)
+        win = ok & (s < best_s)
+        best_p = np.where(win, pc, best_p)
+        best_s = np.where(win, s, best_s)
+        best_f = np.where(win, f, best_f)
+        best_c = np.where(win[:, None], c, best_c)
+    sign = np.signbit(blocks).astype(np.uint8) << 3
+    nib = (best_c.astype(np.uint8) | sign).reshape(-1)
+    codes = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8).reshape(R, K // 2)
+    return codes, best_p.astype(np.uint8).reshape(R, K // 16), sg, best_f.reshape(R, K // 16)
