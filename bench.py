@@ -1,0 +1,230 @@
+"""Benchmark: NVFP4 ScaleSearch quantize GB/s (in+out) on MI355X.
+
+Workload (one step): the bf16 weight 8192 x 28672 ~ N(0, 0.02^2) (seeded,
+synthetic), ScaleSearch quantize with offsets [-2, 6] -- global amax pass,
+tensor scale, candidate search, packed codes and scales -- then dequantize
+back to bf16. value = algorithmic bytes of the step (each kernel's input
+read once plus its output written once) / time of the step, inputs resident
+in HBM.
+
+Also printed (same JSON line): the dominant kernel's roofline (the search
+kernel alone, timed with HIP events on its stream over its own launches), a
+per-pass breakdown, and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--profile]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 ScaleSearch quantize GB/s (in+out) and % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0
+ROWS, COLS = 8192, 28672
+OFFSETS = (-2, 6)
+
+
+def quantize_bytes(n_elem: int, in_bytes_per_elem: int) -> int:
+    """Input once + codes (1/2 B) + scales (1/16 B) + the 4-byte tensor scale."""
+    return n_elem * in_bytes_per_elem + n_elem // 2 + n_elem // 16 + 4
+
+
+def dequantize_bytes(n_elem: int, out_bytes_per_elem: int) -> int:
+    return n_elem // 2 + n_elem // 16 + 4 + n_elem * out_bytes_per_elem
+
+
+def search_pass_bytes(n_elem: int, in_bytes_per_elem: int) -> int:
+    """The search kernel alone (tensor scale given): input + codes + scales + S_g read."""
+    return quantize_bytes(n_elem, in_bytes_per_elem)
+
+
+def event_time_ms(torch, fn, iters: int, stream) -> float:
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline(x_host: np.ndarray, budget_s: float = 10.0) -> dict:
+    """The oracle, as it stands, on a row sample of the same tensor (quantize + dequantize)."""
+    import oracle
+
+    oracle.build(force=False)
+    threads = min(16, os.cpu_count() or 1)
+
+    def run(rows):
+        xs = x_host[:rows]
+        t0 = time.perf_counter()
+        c, s, g = oracle.quantize(xs, *OFFSETS, nthreads=threads)
+        oracle.dequantize(c, s, g, "bf16")
+        return time.perf_counter() - t0
+
+    rows = 256
+    t = run(rows)
+    rows = int(min(ROWS, max(256, rows * budget_s / max(t, 1e-3))))
+    rows -= rows % 64
+    t = run(rows)
+    n = rows * COLS
+    nbytes = quantize_bytes(n, 2) + dequantize_bytes(n, 2)
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the 8192x28672 bf16 tensor ({n} elements): "
+                      f"quantize [-2,6] + bf16 dequantize, {t:.2f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for rocprofv3: a few launches of each kernel plus a "
+                         "plain 1 GiB device copy for counter calibration; no JSON")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the quantizer has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import microscaling_fp4_block_amd as nv
+    import workloads
+
+    nv.load()
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating workload 4 ({ROWS}x{COLS} bf16)", file=sys.stderr, flush=True)
+    xh = workloads.workload(4)
+    x = torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16).to(dev)
+    n = x.numel()
+    ws = torch.empty(nv.workspace_bytes(ROWS, COLS), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    codes = scales = g = None
+    y = torch.empty_like(x)
+
+    def step():
+        nonlocal codes, scales, g
+        codes, scales, g = nv.quantize(x, OFFSETS, workspace=ws)
+        nv.dequantize(codes, scales, g, torch.bfloat16, out=y)
+
+    gfix = None
+
+    def search_only():
+        nv.quantize(x, OFFSETS, global_scale=gfix, workspace=ws)
+
+    def amax_only():
+        nv.global_scale(x, workspace=ws)
+
+    def control_only():
+        nv.quantize(x, (0, 0), global_scale=gfix, workspace=ws)
+
+    def dequant_only():
+        nv.dequantize(codes, scales, g, torch.bfloat16, out=y)
+
+    if args.profile:
+        step()
+        gfix = g.clone()
+        torch.cuda.synchronize()
+        for fn in (step, search_only, amax_only, control_only, dequant_only):
+            for _ in range(3):
+                fn()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] profile run done", file=sys.stderr, flush=True)
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gfix = g.clone()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = event_time_ms(torch, step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_bytes = quantize_bytes(n, 2) + dequantize_bytes(n, 2)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # per-pass breakdown, each timed over its own launches on the same stream
+    iters = max(args.steps, 10)
+    ms_search = event_time_ms(torch, search_only, iters, stream)
+    ms_amax = event_time_ms(torch, amax_only, iters, stream)
+    ms_ctrl = event_time_ms(torch, control_only, iters, stream)
+    ms_deq = event_time_ms(torch, dequant_only, iters, stream)
+    qbytes = quantize_bytes(n, 2)
+    search_gbs = search_pass_bytes(n, 2) / (ms_search * 1e-3) / 1e9
+    quant_call_ms = ms_amax + ms_search
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "bf16 weight 8192x28672 N(0,0.02^2) seed 3: ScaleSearch quantize "
+                        "offsets [-2,6] (global amax + search + pack) then bf16 dequantize",
+            "rows": ROWS, "cols": COLS, "block": 16, "offsets": list(OFFSETS),
+            "step_bytes": step_bytes,
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(search_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(search_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "quantize_kernel<true> (search pass, tensor scale given)",
+            "kernel_ms": round(ms_search, 4),
+            "bytes_per_launch": search_pass_bytes(n, 2),
+        },
+        "breakdown": {
+            "search_pass_ms": round(ms_search, 4),
+            "search_pass_gbs": round(search_gbs, 2),
+            "amax_pass_ms": round(ms_amax, 4),
+            "amax_pass_gbs": round(n * 2 / (ms_amax * 1e-3) / 1e9, 2),
+            "quantize_call_ms": round(quant_call_ms, 4),
+            "quantize_call_gbs": round(qbytes / (quant_call_ms * 1e-3) / 1e9, 2),
+            "max_scaling_control_ms": round(ms_ctrl, 4),
+            "scalesearch_over_max_scaling": round(ms_search / ms_ctrl, 3),
+            "dequantize_bf16_ms": round(ms_deq, 4),
+            "dequantize_bf16_gbs": round(dequantize_bytes(n, 2) / (ms_deq * 1e-3) / 1e9, 2),
+            "wall_s_timed_region": round(wall, 3),
+        },
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(xh)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

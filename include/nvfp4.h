@@ -1,0 +1,155 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 block quantizer with ScaleSearch.
+ *
+ * What is computed (web pages, cited by title and section):
+ *  - "NVIDIAのFP4推論が50倍の効率を実現", 超低精度推論を支えるアーキテクチャ: NVFP4
+ *    codes each value as E2M1 (1 sign, 2 exponent, 1 mantissa bit), with one
+ *    E4M3 scale per 16-value micro-block and a second FP32 per-tensor scale.
+ *  - "技術サマリー：ブロック浮動小数点スケールを検索せよ！" (ScaleSearch summary),
+ *    手法 > ScaleSearch: the default block scale is round(amax / 6); ScaleSearch
+ *    instead adds integer offsets f to the default scale's UE4M3 bit pattern
+ *    (メカニズム) and keeps, over a small range such as f in [-2, 6], the scale
+ *    with the least block MSE (検索戦略).
+ *  - same page, ScaleSearchAttention: a Hadamard transform of Q and K before
+ *    coding (非干渉処理（IP）と絶対値低減), and a KV cache whose first and last
+ *    blocks stay at full precision (アテンション・シンク対応混合精度キャッシング).
+ *
+ * Numerics (identical to the CPU oracle, bit for bit):
+ *  A     = max |x| over the quantized region; NaN/Inf anywhere -> S_g = NaN.
+ *  S_g   = fl(A / 2688) (2688 = 6 * 448), or 1 if that is 0. Decode scale.
+ *  block : a_b = max |x_i| over 16 consecutive elements of the last dimension;
+ *          p0 = UE4M3 round-to-nearest-even-saturating of fl(fl(a_b / 6) / S_g).
+ *  candidates p = p0 + f, f = 0 first, then f_lo..f_hi; p outside 0..126 is
+ *          skipped. d = fl(s_p * S_g), r = fl(1 / d); if r is not finite the
+ *          candidate codes everything as 0. Each element: y = fl(|x| * r),
+ *          c = E2M1 nearest-even-saturating(y), xhat = fl(V[c] * d),
+ *          e = fl(|x| - xhat); SSE = sum of fl(e * e) strictly left to right
+ *          in FP32 (no fused multiply-add). The first candidate with strictly
+ *          smaller SSE wins (ties keep f = 0, then the lowest f).
+ *  codes : nibble = sign(x) << 3 | c (sign copied even for c = 0); byte j of a
+ *          row holds elements 2j (low nibble) and 2j + 1 (high nibble).
+ *  scales: the winning pattern p (0..126), one byte per block; 0x7F (NaN) marks
+ *          a block coded under the non-finite contract (all code bytes 0).
+ *  dequantize: xhat = (-1)^sign * fl(V[c] * fl(s_p * S_g)); bf16 output is the
+ *          nearest-even bf16 of that FP32 value. A scale byte >= 127 gives NaN.
+ *
+ * Conventions for every entry point:
+ *  - Every tensor pointer is a device pointer (HIP global memory) owned by the
+ *    caller; the library allocates nothing and keeps no state between calls.
+ *  - Tensors are dense and row-major; blocks of 16 run along the last
+ *    dimension. Input tensors must be 16-byte aligned; codes 8-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream). All device work is
+ *    enqueued on it and the call returns without waiting. The returned status
+ *    reports argument checks (made on the host before anything is enqueued)
+ *    and launch errors; data-dependent cases follow the non-finite contract
+ *    above instead of an error.
+ *  - Calls that use the same workspace must not overlap in time.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+/* Exported symbols (the library is built with hidden default visibility). */
+#if defined(__GNUC__) || defined(__clang__)
+#define NVFP4_API __attribute__((visibility("default")))
+#else
+#define NVFP4_API
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_EINVAL = 1,     /* null pointer, unknown dtype/flag, block != 16, bad offsets */
+    NVFP4_ESHAPE = 2,     /* a size is negative, not a multiple of 16 (128 with the
+                             Hadamard), too large, or sink sizes exceed T */
+    NVFP4_EALIGN = 3,     /* input not 16-byte aligned or codes not 8-byte aligned */
+    NVFP4_EWORKSPACE = 4, /* workspace missing or smaller than nvfp4_workspace_bytes() */
+    NVFP4_EHIP = 5        /* a HIP launch failed */
+} nvfp4_status;
+
+typedef enum {
+    NVFP4_F32 = 0,  /* IEEE binary32 */
+    NVFP4_BF16 = 1  /* bfloat16 */
+} nvfp4_dtype;
+
+/* Flags for the quantize calls. */
+#define NVFP4_HADAMARD128 1u  /* transform each 128-vector by H/sqrt(128) first (bf16 input) */
+#define NVFP4_GSCALE_GIVEN 2u /* *global_scale is an input: skip the global amax pass */
+
+/* Text for a status code (static storage). */
+NVFP4_API const char *nvfp4_status_str(nvfp4_status s);
+
+/* NVFP4_ABI_VERSION of the built library. */
+NVFP4_API int nvfp4_abi_version(void);
+
+/* Bytes of device workspace the quantize calls need for a rows x cols region
+ * (it holds the per-workgroup partial maxima of the global amax pass). */
+NVFP4_API size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags);
+
+/* Quantize x[rows][cols] (xdt) to NVFP4 with ScaleSearch over offsets
+ * [f_lo, f_hi] (f_lo <= 0 <= f_hi, |f| <= 126; the pages' example range is
+ * [-2, 6]; [0, 0] is plain max scaling). block must be 16; cols % 16 == 0
+ * (cols % 128 == 0 and xdt == NVFP4_BF16 with NVFP4_HADAMARD128).
+ * Outputs: codes[rows][cols/2], scales[rows][cols/16], global_scale[1]
+ * (written, or read when NVFP4_GSCALE_GIVEN: then it must be positive and
+ * finite, and only blocks holding a NaN/Inf get the non-finite contract).
+ * With NVFP4_HADAMARD128 the codes are those of y = x H / sqrt(128) (FP32);
+ * dequantize then returns y-domain values (H/sqrt(128) is its own inverse). */
+NVFP4_API nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                            int block, int f_lo, int f_hi, uint32_t flags, uint8_t *codes,
+                            uint8_t *scales, float *global_scale, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Only the global scale: S_g of x[rows][cols] (after the Hadamard transform
+ * with NVFP4_HADAMARD128) into global_scale[1]. The first half of
+ * nvfp4_quantize; feed the result back with NVFP4_GSCALE_GIVEN. */
+NVFP4_API nvfp4_status nvfp4_global_scale(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                                uint32_t flags, float *global_scale, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Inverse: y[rows][cols] (ydt: FP32 or bf16) from codes, scales and the
+ * device-resident global_scale[1]. */
+NVFP4_API nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
+                              const float *global_scale, int64_t rows, int64_t cols, int block,
+                              void *y, nvfp4_dtype ydt, void *stream);
+
+/* Attention-sink KV mode. kv[B][H][T][D] (dt). For every (b, h) the first
+ * n_first and last n_last tokens are copied verbatim to
+ * sink[B][H][n_first + n_last][D] (dt; first, then last), and the middle
+ * Tm = T - n_first - n_last tokens are quantized as one region (its global
+ * amax excludes the sink tokens): codes[B][H][Tm][D/2],
+ * scales[B][H][Tm][D/16]. Requires n_first + n_last <= T and D % 16 == 0. */
+NVFP4_API nvfp4_status nvfp4_quantize_kv_sink(const void *kv, nvfp4_dtype dt, int64_t B, int64_t H,
+                                    int64_t T, int64_t D, int64_t n_first, int64_t n_last,
+                                    int block, int f_lo, int f_hi, uint32_t flags,
+                                    uint8_t *codes, uint8_t *scales, float *global_scale,
+                                    void *sink, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* Inverse of the sink mode: y[B][H][T][D] (ydt) with the sink tokens copied
+ * exactly (bf16 -> FP32 widening is exact; FP32 -> bf16 rounds to nearest
+ * even) and the middle tokens dequantized. */
+NVFP4_API nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scales,
+                                      const float *global_scale, const void *sink,
+                                      nvfp4_dtype sink_dt, int64_t B, int64_t H, int64_t T,
+                                      int64_t D, int64_t n_first, int64_t n_last, int block,
+                                      void *y, nvfp4_dtype ydt, void *stream);
+
+/* The FP32 Hadamard pre-transform alone: y[rows][128] = x[rows][128] H/sqrt(128)
+ * (x bf16), as the quantizer computes it on the fly. For inspection and split
+ * parity checks; the quantize path never writes it to memory. */
+NVFP4_API nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,
+                               void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

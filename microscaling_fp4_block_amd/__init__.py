@@ -1,0 +1,17 @@
+"""NVFP4 block quantization with ScaleSearch on MI355X (gfx950).
+
+The compute path is the HIP library ``libnvfp4.so`` (C ABI in
+``include/nvfp4.h``); this package is its thin Python binding.
+"""
+from .nvfp4 import (  # noqa: F401
+    LIB_PATH,
+    NVFP4Error,
+    dequantize,
+    dequantize_kv_sink,
+    global_scale,
+    hadamard128,
+    load,
+    quantize,
+    quantize_kv_sink,
+    workspace_bytes,
+)

@@ -1,0 +1,250 @@
+// nvfp4_api.hip -- the C ABI declared in include/nvfp4.h: host-side argument
+// checks (made before anything is enqueued, so they run without a GPU) and
+// kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+#include "nvfp4_internal.h"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t kMaxBlocks = 1ll << 29;  // 32-bit chunk and block indices never overflow
+
+bool dtype_ok(nvfp4_dtype d) { return d == NVFP4_F32 || d == NVFP4_BF16; }
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t workspace_needed() { return (size_t)kMaxAmaxGroups * sizeof(uint32_t); }
+
+nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
+
+int amax_groups(uint64_t nblocks, bool bf16) {
+  const uint64_t chunks = nblocks * (bf16 ? 2u : 4u);
+  uint64_t g = (chunks + 4ull * kThreads - 1) / (4ull * kThreads);
+  if (g < 1) g = 1;
+  if (g > (uint64_t)kMaxAmaxGroups) g = kMaxAmaxGroups;
+  return (int)g;
+}
+
+RegionMap plain_map(int64_t rows, int64_t cols) {
+  RegionMap m{};
+  m.nblocks = (uint32_t)(rows * (cols / 16));
+  m.bpr = (uint32_t)(cols / 16);
+  m.div_bpr = make_fastdiv(m.bpr ? m.bpr : 1);
+  m.segments = 0;
+  m.tm = 1;
+  m.div_tm = make_fastdiv(1);
+  m.cols = (uint32_t)cols;
+  return m;
+}
+
+// Global amax + finalize into gscale. The workspace holds the partials.
+nvfp4_status run_global_scale(const void *x, bool bf16, const RegionMap &m, float *gscale,
+                              void *ws, hipStream_t s) {
+  AmaxArgs a{x, (uint32_t *)ws, m};
+  const int groups = amax_groups(m.nblocks, bf16);
+  hipError_t e = launch_amax(a, bf16, groups, s);
+  if (e != hipSuccess) return NVFP4_EHIP;
+  return hip_status(launch_finalize((const uint32_t *)ws, groups, gscale, s));
+}
+
+nvfp4_status check_offsets(int block, int f_lo, int f_hi) {
+  if (block != 16) return NVFP4_EINVAL;
+  if (f_lo > 0 || f_hi < 0 || f_lo < -126 || f_hi > 126) return NVFP4_EINVAL;
+  return NVFP4_OK;
+}
+
+nvfp4_status check_shape(int64_t rows, int64_t cols, uint32_t flags, nvfp4_dtype dt) {
+  if (rows < 0 || cols <= 0 || cols % 16) return NVFP4_ESHAPE;
+  if (cols > (1ll << 30) || (rows > 0 && rows > kMaxBlocks / (cols / 16))) return NVFP4_ESHAPE;
+  if (flags & ~(NVFP4_HADAMARD128 | NVFP4_GSCALE_GIVEN)) return NVFP4_EINVAL;
+  if (flags & NVFP4_HADAMARD128) {
+    if (dt != NVFP4_BF16) return NVFP4_EINVAL;
+    if (cols % 128) return NVFP4_ESHAPE;
+  }
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nvfp4_status_str(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_EINVAL: return "invalid argument";
+    case NVFP4_ESHAPE: return "invalid shape";
+    case NVFP4_EALIGN: return "misaligned pointer";
+    case NVFP4_EWORKSPACE: return "workspace missing or too small";
+    case NVFP4_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags) {
+  (void)rows;
+  (void)cols;
+  (void)flags;
+  return workspace_needed();
+}
+
+nvfp4_status nvfp4_global_scale(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                                uint32_t flags, float *global_scale, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  if (!x || !global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
+  nvfp4_status st = check_shape(rows, cols, flags & ~NVFP4_GSCALE_GIVEN, xdt);
+  if (st) return st;
+  if (!aligned(x, 16)) return NVFP4_EALIGN;
+  if (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4))
+    return NVFP4_EWORKSPACE;
+  if (flags & NVFP4_HADAMARD128) return NVFP4_EINVAL;  // not available in this build
+  return run_global_scale(x, xdt == NVFP4_BF16, plain_map(rows, cols), global_scale, workspace,
+                          (hipStream_t)stream);
+}
+
+nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                            int block, int f_lo, int f_hi, uint32_t flags, uint8_t *codes,
+                            uint8_t *scales, float *global_scale, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  if (!x || !codes || !scales || !global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
+  nvfp4_status st = check_offsets(block, f_lo, f_hi);
+  if (st) return st;
+  st = check_shape(rows, cols, flags, xdt);
+  if (st) return st;
+  if (!aligned(x, 16) || !aligned(codes, 8)) return NVFP4_EALIGN;
+  const bool given = flags & NVFP4_GSCALE_GIVEN;
+  if (!given && (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4)))
+    return NVFP4_EWORKSPACE;
+  if (flags & NVFP4_HADAMARD128) return NVFP4_EINVAL;  // not available in this build
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = xdt == NVFP4_BF16;
+  const RegionMap m = plain_map(rows, cols);
+  if (!given) {
+    st = run_global_scale(x, bf16, m, global_scale, workspace, s);
+    if (st) return st;
+  }
+  if (m.nblocks == 0) return NVFP4_OK;
+  QuantArgs q{x, codes, scales, global_scale, m, f_lo, f_hi};
+  return hip_status(launch_quantize(q, bf16, s));
+}
+
+nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
+                              const float *global_scale, int64_t rows, int64_t cols, int block,
+                              void *y, nvfp4_dtype ydt, void *stream) {
+  if (!codes || !scales || !global_scale || !y || !dtype_ok(ydt)) return NVFP4_EINVAL;
+  if (block != 16) return NVFP4_EINVAL;
+  nvfp4_status st = check_shape(rows, cols, 0, ydt);
+  if (st) return st;
+  if (!aligned(codes, 8) || !aligned(y, 16)) return NVFP4_EALIGN;
+  DequantArgs a{codes, scales, global_scale, y, (uint32_t)(rows * (cols / 16))};
+  if (a.nblocks == 0) return NVFP4_OK;
+  return hip_status(launch_dequantize(a, ydt == NVFP4_BF16, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_quantize_kv_sink(const void *kv, nvfp4_dtype dt, int64_t B, int64_t H,
+                                    int64_t T, int64_t D, int64_t n_first, int64_t n_last,
+                                    int block, int f_lo, int f_hi, uint32_t flags,
+                                    uint8_t *codes, uint8_t *scales, float *global_scale,
+                                    void *sink, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  if (!kv || !codes || !scales || !global_scale || !sink || !dtype_ok(dt)) return NVFP4_EINVAL;
+  nvfp4_status st = check_offsets(block, f_lo, f_hi);
+  if (st) return st;
+  if (B < 0 || H < 0 || T < 0 || D <= 0 || n_first < 0 || n_last < 0 || n_first + n_last > T)
+    return NVFP4_ESHAPE;
+  if (T > (1ll << 31) || B * H > (1ll << 31)) return NVFP4_ESHAPE;
+  const int64_t BH = B * H, NS = n_first + n_last, Tm = T - NS;
+  st = check_shape(BH * T, D, flags, dt);
+  if (st) return st;
+  if (!aligned(kv, 16) || !aligned(codes, 8) || !aligned(sink, 16)) return NVFP4_EALIGN;
+  const bool given = flags & NVFP4_GSCALE_GIVEN;
+  if (!given && (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4)))
+    return NVFP4_EWORKSPACE;
+  if (flags & NVFP4_HADAMARD128) return NVFP4_EINVAL;  // not available in this build
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dt == NVFP4_BF16;
+  const uint32_t es = bf16 ? 2u : 4u;
+
+  if (BH > 0 && NS > 0) {
+    SinkArgs c{};
+    c.src = kv;
+    c.dst = sink;
+    c.bh = (uint32_t)BH;
+    c.T = (uint32_t)T;
+    c.D = (uint32_t)D;
+    c.n_first = (uint32_t)n_first;
+    c.n_last = (uint32_t)n_last;
+    c.chunks_per_row = (uint32_t)(D * es / 16);
+    c.nchunks = (uint32_t)(BH * NS) * c.chunks_per_row;
+    c.div_cpr = make_fastdiv(c.chunks_per_row);
+    c.div_ns = make_fastdiv((uint32_t)NS);
+    hipError_t e = launch_sink_copy(c, bf16, s);
+    if (e != hipSuccess) return NVFP4_EHIP;
+  }
+
+  RegionMap m{};
+  m.bpr = (uint32_t)(D / 16);
+  m.nblocks = (uint32_t)(BH * Tm) * m.bpr;
+  m.div_bpr = make_fastdiv(m.bpr);
+  m.segments = (uint32_t)BH;
+  m.tm = (uint32_t)(Tm > 0 ? Tm : 1);
+  m.div_tm = make_fastdiv(m.tm);
+  m.seg_tokens = (uint32_t)T;
+  m.n_first = (uint32_t)n_first;
+  m.cols = (uint32_t)D;
+  if (!given) {
+    st = run_global_scale(kv, bf16, m, global_scale, workspace, s);
+    if (st) return st;
+  }
+  if (m.nblocks == 0) return NVFP4_OK;
+  QuantArgs q{kv, codes, scales, global_scale, m, f_lo, f_hi};
+  return hip_status(launch_quantize(q, bf16, s));
+}
+
+nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scales,
+                                      const float *global_scale, const void *sink,
+                                      nvfp4_dtype sink_dt, int64_t B, int64_t H, int64_t T,
+                                      int64_t D, int64_t n_first, int64_t n_last, int block,
+                                      void *y, nvfp4_dtype ydt, void *stream) {
+  if (!codes || !scales || !global_scale || !sink || !y || !dtype_ok(sink_dt) || !dtype_ok(ydt))
+    return NVFP4_EINVAL;
+  if (block != 16) return NVFP4_EINVAL;
+  if (B < 0 || H < 0 || T < 0 || D <= 0 || D % 16 || n_first < 0 || n_last < 0 ||
+      n_first + n_last > T)
+    return NVFP4_ESHAPE;
+  if (T > (1ll << 31) || B * H > (1ll << 31)) return NVFP4_ESHAPE;
+  const int64_t BH = B * H;
+  nvfp4_status st = check_shape(BH * T, D, 0, ydt);
+  if (st) return st;
+  if (!aligned(codes, 8) || !aligned(sink, 16) || !aligned(y, 16)) return NVFP4_EALIGN;
+  DequantKvArgs a{};
+  a.codes = codes;
+  a.scales = scales;
+  a.gscale = global_scale;
+  a.sink = sink;
+  a.y = y;
+  a.bpr = (uint32_t)(D / 16);
+  a.nblocks = (uint32_t)(BH * T) * a.bpr;
+  a.div_bpr = make_fastdiv(a.bpr);
+  a.div_T = make_fastdiv((uint32_t)(T > 0 ? T : 1));
+  a.T = (uint32_t)T;
+  a.n_first = (uint32_t)n_first;
+  a.n_last = (uint32_t)n_last;
+  if (a.nblocks == 0) return NVFP4_OK;
+  return hip_status(
+      launch_dequantize_kv(a, sink_dt == NVFP4_BF16, ydt == NVFP4_BF16, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,
+                               void *stream) {
+  (void)stream;
+  if (!x || !y || xdt != NVFP4_BF16) return NVFP4_EINVAL;
+  if (rows < 0) return NVFP4_ESHAPE;
+  return NVFP4_EINVAL;  // not available in this build
+}
+
+}  // extern "C"

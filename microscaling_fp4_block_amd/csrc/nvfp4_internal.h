@@ -1,0 +1,102 @@
+// nvfp4_internal.h -- launch descriptors shared by the host API and the kernels
+// of the gfx950 NVFP4 library (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kThreads = 256;          // 4 wave64 per workgroup
+constexpr int kMaxAmaxGroups = 4096;   // partial maxima kept in the workspace
+constexpr int kMaxQuantGroups = 8192;  // grid cap of the block-parallel kernels
+
+// Division by a runtime constant with one high multiply (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994,
+// the round-up variant): q = (umulhi(n, m) + n) >> s for every 32-bit n,
+// for divisors 1 <= d <= 2^31.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, s};
+}
+
+// Where block b of the quantized region lives in the input. Plain tensors are
+// one contiguous region (segments == 0). The attention-sink mode quantizes the
+// middle tokens of every (batch, head) segment: row r of the region is token
+// n_first + (r mod tm) of segment r / tm, and a segment spans seg_tokens rows.
+struct RegionMap {
+  uint32_t nblocks;     // 16-element blocks in the region
+  uint32_t bpr;         // blocks per row (cols / 16)
+  FastDiv div_bpr;
+  uint32_t segments;    // 0: plain contiguous region
+  uint32_t tm;          // region rows per segment
+  FastDiv div_tm;
+  uint32_t seg_tokens;  // input rows per segment (T)
+  uint32_t n_first;     // first region row inside a segment
+  uint32_t cols;        // elements per row
+};
+
+struct QuantArgs {
+  const void *x;
+  uint8_t *codes;
+  uint8_t *scales;
+  const float *gscale;
+  RegionMap map;
+  int f_lo, f_hi;
+};
+
+struct AmaxArgs {
+  const void *x;
+  uint32_t *partials;
+  RegionMap map;
+};
+
+struct DequantArgs {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const float *gscale;
+  void *y;
+  uint32_t nblocks;
+};
+
+// Sink copy / reassembly: BH segments of T tokens of D elements; tokens
+// [0, n_first) and [T - n_last, T) live in sink[BH][n_first + n_last][D].
+struct SinkArgs {
+  const void *src;
+  void *dst;
+  uint32_t bh, T, D, n_first, n_last;
+  uint32_t nchunks;      // 16-byte chunks to move
+  uint32_t chunks_per_row;
+  FastDiv div_cpr;
+  FastDiv div_ns;        // n_first + n_last
+};
+
+struct DequantKvArgs {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const float *gscale;
+  const void *sink;
+  void *y;
+  uint32_t nblocks;      // output blocks: BH * T * D / 16
+  uint32_t bpr;          // D / 16
+  FastDiv div_bpr;
+  FastDiv div_T;
+  uint32_t T, n_first, n_last;
+};
+
+// Launchers (nvfp4_kernels.hip). Return hipSuccess or the launch error.
+hipError_t launch_amax(const AmaxArgs &a, bool bf16, int groups, hipStream_t s);
+hipError_t launch_finalize(const uint32_t *partials, int n, float *gscale, hipStream_t s);
+hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s);
+hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_dequantize_kv(const DequantKvArgs &a, bool sink_bf16, bool out_bf16,
+                                hipStream_t s);
+
+}  // namespace nvfp4

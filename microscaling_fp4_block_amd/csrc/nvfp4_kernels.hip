@@ -1,0 +1,450 @@
+// nvfp4_kernels.hip -- gfx950 kernels of the NVFP4 ScaleSearch quantizer.
+//
+// What is computed follows the ScaleSearch summary page
+// ("技術サマリー：ブロック浮動小数点スケールを検索せよ！", 手法 > ScaleSearch:
+// メカニズム, 検索戦略) and the NVFP4 layout of "NVIDIAのFP4推論が50倍の効率を実現"
+// (超低精度推論を支えるアーキテクチャ): E2M1 codes, one UE4M3 scale per 16
+// elements, an FP32 tensor scale. Every rounding point matches the CPU oracle
+// bit for bit; this file must be compiled with -ffp-contract=off so that no
+// product is fused into a following add.
+//
+// Kernels:
+//   amax      global max |x| as a max over absolute-value bit patterns
+//             (exact, order-free): 16-byte coalesced loads, DPP wave reduce,
+//             one partial per workgroup.
+//   finalize  one workgroup: partial maxima -> tensor scale S_g.
+//   quantize  one lane per 16-element block: block amax, default pattern, the
+//             candidate search held in VGPRs, then 8 code bytes + 1 scale byte.
+//   dequantize, sink copy, KV reassembly.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Small device helpers.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv &f) {
+  uint32_t t = __umulhi(n, f.m);
+  return (uint32_t)(((uint64_t)t + n) >> f.s);
+}
+
+// Value of UE4M3 pattern p in 0..126 (4 exponent bits, bias 7; 3 mantissa
+// bits; exponent field 0 is subnormal m * 2^-9). Exact in FP32.
+__device__ __forceinline__ float e4m3_value(uint32_t p) {
+  uint32_t e = p >> 3, m = p & 7u;
+  float sub = (float)m * 0x1p-9f;
+  float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nrm;
+}
+
+// UE4M3 round-to-nearest-even with saturation at 448 (pattern 126), t >= 0.
+// Normal range: keep 3 mantissa bits of the FP32 pattern with a nearest-even
+// carry, then rebias the exponent (127 -> 7). Below 2^-6 the format steps by
+// 2^-9, so the pattern is t * 2^9 rounded to an integer (exact scaling).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
+  uint32_t b = __float_as_uint(t);
+  uint32_t nrm = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u;
+  uint32_t sub = (uint32_t)__builtin_rintf(t * 512.0f);
+  uint32_t p = t < 0x1p-6f ? sub : nrm;
+  return t >= 448.0f ? 126u : p;
+}
+
+// Hardware E2M1 converts (gfx950). The byte selector must be a constant, so
+// the switch folds away once the callers' loops are unrolled.
+__device__ __forceinline__ uint32_t fp4_encode_pair(uint32_t old, float a, float b, int sel) {
+  switch (sel & 3) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 3);
+  }
+}
+
+__device__ __forceinline__ f32x2 fp4_decode_pair(uint32_t w, int sel) {
+  switch (sel & 3) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  }
+}
+
+// Input offset (in elements) of block b of the quantized region.
+__device__ __forceinline__ uint64_t block_offset(const RegionMap &m, uint32_t b) {
+  if (m.segments == 0) return (uint64_t)b * 16u;
+  uint32_t r = fastdiv(b, m.div_bpr);
+  uint32_t j = b - r * m.bpr;
+  uint32_t g = fastdiv(r, m.div_tm);
+  uint32_t t = r - g * m.tm;
+  uint64_t row = (uint64_t)g * m.seg_tokens + m.n_first + t;
+  return row * m.cols + (uint64_t)j * 16u;
+}
+
+// Wave64 max with DPP: xor-1 and xor-2 quad permutes, half-row and row
+// mirrors give every lane its row-of-16 maximum; row broadcasts 15 and 31
+// then fold the four rows into lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  __shared__ uint32_t red[kThreads / 64];
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
+  return m;
+}
+
+// Load one 16-element block as FP32 (bf16 widening is exact: a 16-bit shift).
+template <bool BF16>
+__device__ __forceinline__ void load_block(const void *x, uint64_t off, float (&v)[16]) {
+  if (BF16) {
+    const uint4 *p = (const uint4 *)((const uint16_t *)x + off);
+    uint4 a = p[0], b = p[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 *p = (const float4 *)((const float *)x + off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float4 a = p[k];
+      v[4 * k] = a.x;
+      v[4 * k + 1] = a.y;
+      v[4 * k + 2] = a.z;
+      v[4 * k + 3] = a.w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Global amax pass.
+// ---------------------------------------------------------------------------
+
+// Max of the absolute-value bit patterns of one 16-byte chunk.
+template <bool BF16>
+__device__ __forceinline__ uint32_t chunk_absmax(uint4 c) {
+  if (BF16) {
+    uint32_t m = 0;
+    uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max((w[k] << 16) & 0x7FFFFFFFu, w[k] & 0x7FFF0000u));
+    return m;
+  }
+  return max(max(c.x & 0x7FFFFFFFu, c.y & 0x7FFFFFFFu), max(c.z & 0x7FFFFFFFu, c.w & 0x7FFFFFFFu));
+}
+
+// Lanes take consecutive 16-byte chunks (a block is 2 chunks in bf16, 4 in
+// FP32), four independent loads in flight per lane.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
+  constexpr uint32_t CPB = BF16 ? 2 : 4;  // 16-byte chunks per block
+  constexpr uint32_t ES = BF16 ? 2 : 4;
+  const uint32_t nchunks = a.map.nblocks * CPB;
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t m = 0;
+  for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t c = c0 + u * stride;
+      if (c < nchunks) {
+        uint32_t b = c / CPB, sub = c % CPB;
+        const char *p = (const char *)a.x + block_offset(a.map, b) * ES + sub * 16u;
+        v[u] = *(const uint4 *)p;
+      } else {
+        v[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = max(m, chunk_absmax<BF16>(v[u]));
+  }
+  m = group_max_u32(m);
+  if (threadIdx.x == 0) a.partials[blockIdx.x] = m;
+}
+
+// Tensor (decode) scale from the global amax A: S_g = fl(A / 2688), 2688 =
+// 6 * 448 (largest E2M1 times largest UE4M3), 1 if that is 0, NaN if the
+// region holds a NaN/Inf.
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const uint32_t *partials, int n,
+                                                            float *gscale) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = max(m, partials[i]);
+  m = group_max_u32(m);
+  if (threadIdx.x == 0) {
+    float sg;
+    if (m >= 0x7F800000u) {
+      sg = __uint_as_float(0x7FC00000u);
+    } else {
+      sg = __uint_as_float(m) / 2688.0f;
+      if (sg == 0.0f) sg = 1.0f;
+    }
+    *gscale = sg;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// ScaleSearch quantize pass.
+// ---------------------------------------------------------------------------
+
+// Squared error of one candidate (decode scale d, encode scale r = 1/d; both 0
+// for a candidate that codes everything as 0). y = x * r keeps the sign of x,
+// so the hardware FP4 convert yields sign-magnitude nibbles directly (round to
+// nearest even on the E2M1 grid, saturating at 6); the paired decode gives
+// +-V[c]. Element pairs go through one convert each way.
+__device__ __forceinline__ float candidate_sse(const float (&x)[16], float d, float r,
+                                               uint32_t &c0, uint32_t &c1) {
+  uint32_t cw[2] = {0u, 0u};
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float y0 = x[2 * j] * r;
+    const float y1 = x[2 * j + 1] * r;
+    cw[j >> 2] = fp4_encode_pair(cw[j >> 2], y0, y1, j);
+    const f32x2 v = fp4_decode_pair(cw[j >> 2], j);
+    const float xh0 = v.x * d;
+    const float xh1 = v.y * d;
+    const float e0 = fabsf(x[2 * j]) - fabsf(xh0);
+    const float e1 = fabsf(x[2 * j + 1]) - fabsf(xh1);
+    const float q0 = e0 * e0;
+    s = s + q0;
+    const float q1 = e1 * e1;
+    s = s + q1;
+  }
+  c0 = cw[0];
+  c1 = cw[1];
+  return s;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  __shared__ f32x2 tbl[128];  // per pattern: (decode d, encode r)
+  const float sg = *a.gscale;
+  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+  if (threadIdx.x < 127) {
+    float d = e4m3_value(threadIdx.x) * sg;
+    float r = 1.0f / d;
+    if (!(r < INFINITY)) {  // pattern 0, or 1/d overflows: codes everything as 0
+      d = 0.0f;
+      r = 0.0f;
+    }
+    tbl[threadIdx.x] = f32x2{d, r};
+  }
+  __syncthreads();
+
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
+    float x[16];
+    load_block<BF16>(a.x, block_offset(a.map, b), x);
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+
+    uint32_t best_p = 0x7Fu, bc0 = 0u, bc1 = 0u;
+    if (sg_ok && am < 0x7F800000u) {
+      const float amax = __uint_as_float(am);
+      const float t = (amax / 6.0f) / sg;
+      const uint32_t p0 = e4m3_rne_sat(t);
+      f32x2 dr = tbl[p0];
+      float best = candidate_sse(x, dr.x, dr.y, bc0, bc1);
+      best_p = p0;
+      for (int f = a.f_lo; f <= a.f_hi; ++f) {
+        if (f == 0) continue;
+        const int p = (int)p0 + f;
+        const bool valid = (unsigned)p <= 126u;
+        dr = tbl[valid ? p : (int)p0];
+        uint32_t c0, c1;
+        const float s = candidate_sse(x, dr.x, dr.y, c0, c1);
+        const bool win = valid && (s < best);
+        best = win ? s : best;
+        best_p = win ? (uint32_t)p : best_p;
+        bc0 = win ? c0 : bc0;
+        bc1 = win ? c1 : bc1;
+      }
+    }
+    *(uint2 *)(a.codes + (uint64_t)b * 8u) = make_uint2(bc0, bc1);
+    a.scales[b] = (uint8_t)best_p;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float block_decode_scale(uint32_t p, float sg) {
+  const float s = p < 127u ? e4m3_value(p) : __uint_as_float(0x7FC00000u);
+  return s * sg;
+}
+
+__device__ __forceinline__ void decode_block(uint2 c, float d, float (&o)[16]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = j < 4 ? c.x : c.y;
+    const f32x2 v = fp4_decode_pair(w, j);
+    o[2 * j] = v.x * d;
+    o[2 * j + 1] = v.y * d;
+  }
+}
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_block(void *y, uint64_t off, const float (&o)[16]) {
+  if (OUT_BF16) {
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      bf16x2 h = __builtin_convertvector((f32x2{o[2 * k], o[2 * k + 1]}), bf16x2);
+      w[k] = __builtin_bit_cast(uint32_t, h);
+    }
+    uint4 *p = (uint4 *)((uint16_t *)y + off);
+    p[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    p[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    float4 *p = (float4 *)((float *)y + off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = make_float4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+  }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
+  const float sg = *a.gscale;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.nblocks; b += stride) {
+    const uint2 c = *(const uint2 *)(a.codes + (uint64_t)b * 8u);
+    const float d = block_decode_scale(a.scales[b], sg);
+    float o[16];
+    decode_block(c, d, o);
+    store_block<OUT_BF16>(a.y, (uint64_t)b * 16u, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention-sink helpers.
+// ---------------------------------------------------------------------------
+
+// Copy the sink tokens of kv[BH][T][D] into sink[BH][NS][D], 16 bytes a lane.
+__global__ __launch_bounds__(kThreads) void sink_copy_kernel(SinkArgs a, uint32_t esize) {
+  const uint32_t ns = a.n_first + a.n_last;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < a.nchunks; c += stride) {
+    const uint32_t row = fastdiv(c, a.div_cpr);  // sink row: g * ns + s
+    const uint32_t k = c - row * a.chunks_per_row;
+    const uint32_t g = fastdiv(row, a.div_ns);
+    const uint32_t s = row - g * ns;
+    const uint32_t t = s < a.n_first ? s : a.T - a.n_last + (s - a.n_first);
+    const uint64_t src = ((uint64_t)g * a.T + t) * a.D * esize + (uint64_t)k * 16u;
+    const uint64_t dst = (uint64_t)row * a.D * esize + (uint64_t)k * 16u;
+    *(uint4 *)((char *)a.dst + dst) = *(const uint4 *)((const char *)a.src + src);
+  }
+}
+
+// y[BH][T][D] from the sink tokens and the dequantized middle, one 16-element
+// block a lane.
+template <bool SINK_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void dequantize_kv_kernel(DequantKvArgs a) {
+  const float sg = *a.gscale;
+  const uint32_t ns = a.n_first + a.n_last;
+  const uint32_t tm = a.T - ns;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t ob = blockIdx.x * kThreads + threadIdx.x; ob < a.nblocks; ob += stride) {
+    const uint32_t row = fastdiv(ob, a.div_bpr);
+    const uint32_t j = ob - row * a.bpr;
+    const uint32_t g = fastdiv(row, a.div_T);
+    const uint32_t t = row - g * a.T;
+    float o[16];
+    if (t < a.n_first || t >= a.T - a.n_last) {
+      const uint32_t s = t < a.n_first ? t : a.n_first + (t - (a.T - a.n_last));
+      const uint64_t off = ((uint64_t)g * ns + s) * (a.bpr * 16u) + (uint64_t)j * 16u;
+      load_block<SINK_BF16>(a.sink, off, o);
+    } else {
+      const uint32_t mb = (g * tm + (t - a.n_first)) * a.bpr + j;
+      const uint2 c = *(const uint2 *)(a.codes + (uint64_t)mb * 8u);
+      decode_block(c, block_decode_scale(a.scales[mb], sg), o);
+    }
+    store_block<OUT_BF16>(a.y, (uint64_t)ob * 16u, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+
+static int grid_for(uint64_t items, int cap) {
+  uint64_t g = (items + kThreads - 1) / kThreads;
+  if (g < 1) g = 1;
+  return (int)(g > (uint64_t)cap ? cap : g);
+}
+
+hipError_t launch_amax(const AmaxArgs &a, bool bf16, int groups, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(amax_kernel<true>, dim3(groups), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(amax_kernel<false>, dim3(groups), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const uint32_t *partials, int n, float *gscale, hipStream_t s) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, partials, n, gscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
+  const int g = grid_for(a.map.nblocks, kMaxQuantGroups);
+  if (bf16)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3(g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s) {
+  const int g = grid_for(a.nblocks, kMaxQuantGroups);
+  if (out_bf16)
+    hipLaunchKernelGGL(dequantize_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(dequantize_kernel<false>, dim3(g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s) {
+  const int g = grid_for(a.nchunks, kMaxQuantGroups);
+  hipLaunchKernelGGL(sink_copy_kernel, dim3(g), dim3(kThreads), 0, s, a, bf16 ? 2u : 4u);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_kv(const DequantKvArgs &a, bool sink_bf16, bool out_bf16,
+                                hipStream_t s) {
+  const int g = grid_for(a.nblocks, kMaxQuantGroups);
+  if (sink_bf16 && out_bf16)
+    hipLaunchKernelGGL((dequantize_kv_kernel<true, true>), dim3(g), dim3(kThreads), 0, s, a);
+  else if (sink_bf16)
+    hipLaunchKernelGGL((dequantize_kv_kernel<true, false>), dim3(g), dim3(kThreads), 0, s, a);
+  else if (out_bf16)
+    hipLaunchKernelGGL((dequantize_kv_kernel<false, true>), dim3(g), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((dequantize_kv_kernel<false, false>), dim3(g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

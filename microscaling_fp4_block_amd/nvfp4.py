@@ -1,0 +1,233 @@
+"""Python binding of libnvfp4.so (the C ABI in include/nvfp4.h).
+
+Argument marshalling only: every step of the quantizer runs in the library's
+HIP kernels. torch supplies device memory and the current HIP stream. There is
+no CPU fallback: if the library is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+F32, BF16 = 0, 1
+HADAMARD128, GSCALE_GIVEN = 1, 2
+
+STATUS = {0: "NVFP4_OK", 1: "NVFP4_EINVAL", 2: "NVFP4_ESHAPE", 3: "NVFP4_EALIGN",
+          4: "NVFP4_EWORKSPACE", 5: "NVFP4_EHIP"}
+
+# exported symbol -> (argtypes, restype)
+_i64, _i32, _u32 = ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+SIGNATURES = {
+    "nvfp4_status_str": ([_i32], ctypes.c_char_p),
+    "nvfp4_abi_version": ([], _i32),
+    "nvfp4_workspace_bytes": ([_i64, _i64, _u32], _sz),
+    "nvfp4_quantize": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp, _sz,
+                        _vp], _i32),
+    "nvfp4_global_scale": ([_vp, _i32, _i64, _i64, _u32, _vp, _vp, _sz, _vp], _i32),
+    "nvfp4_dequantize": ([_vp, _vp, _vp, _i64, _i64, _i32, _vp, _i32, _vp], _i32),
+    "nvfp4_quantize_kv_sink": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
+                                _u32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "nvfp4_dequantize_kv_sink": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  _i32, _vp, _i32, _vp], _i32),
+    "nvfp4_hadamard128": ([_vp, _i32, _i64, _vp, _vp], _i32),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libnvfp4.so (built in-tree by ``build.py``); raise if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is not built; run microscaling_fp4_block_amd/build.py "
+                    "(or __graft_entry__.build()) first")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in SIGNATURES.items():
+                fn = getattr(L, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = L
+    return _lib
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        if st in (1, 2, 3, 4):
+            raise ValueError(f"{fn}: {STATUS.get(st, st)}")
+        raise NVFP4Error(fn, st)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("tensors must be on a HIP (cuda) device")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.device
+
+
+def workspace_bytes(rows: int, cols: int, flags: int = 0) -> int:
+    return int(load().nvfp4_workspace_bytes(rows, cols, flags))
+
+
+def _offsets(offsets):
+    lo, hi = int(offsets[0]), int(offsets[1])
+    return lo, hi
+
+
+def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
+             global_scale: torch.Tensor | None = None, block: int = 16, workspace=None):
+    """ScaleSearch NVFP4 quantize of x (last dim in blocks of 16).
+
+    Returns (codes uint8[..., K/2], scales uint8[..., K/16], global_scale float32[1]).
+    If ``global_scale`` (a device float32[1]) is given it is used as S_g.
+    """
+    L = load()
+    dev = _dev(x)
+    K = x.shape[-1]
+    R = x.numel() // K if K else 0
+    f_lo, f_hi = _offsets(offsets)
+    flags = HADAMARD128 if hadamard else 0
+    codes = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(*x.shape[:-1], K // 16, dtype=torch.uint8, device=dev)
+    if global_scale is not None:
+        flags |= GSCALE_GIVEN
+        g = global_scale
+        _dev(g)
+        if g.dtype != torch.float32 or g.numel() != 1:
+            raise ValueError("global_scale must be a device float32 tensor of one element")
+    else:
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    wsb = int(L.nvfp4_workspace_bytes(R, K, flags))
+    ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = L.nvfp4_quantize(x.data_ptr(), _dtype(x), R, K, block, f_lo, f_hi, flags,
+                          codes.data_ptr(), scales.data_ptr(), g.data_ptr(), ws.data_ptr(),
+                          ws.numel(), _stream(dev))
+    _check("nvfp4_quantize", st)
+    return codes, scales, g
+
+
+def global_scale(x: torch.Tensor, hadamard: bool = False, workspace=None) -> torch.Tensor:
+    """Tensor scale S_g = fl(max|x| / 2688) (1 if that is 0) as a device float32[1]."""
+    L = load()
+    dev = _dev(x)
+    K = x.shape[-1]
+    R = x.numel() // K if K else 0
+    flags = HADAMARD128 if hadamard else 0
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    wsb = int(L.nvfp4_workspace_bytes(R, K, flags))
+    ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = L.nvfp4_global_scale(x.data_ptr(), _dtype(x), R, K, flags, g.data_ptr(), ws.data_ptr(),
+                              ws.numel(), _stream(dev))
+    _check("nvfp4_global_scale", st)
+    return g
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor,
+               out_dtype=torch.float32, block: int = 16, out: torch.Tensor | None = None):
+    L = load()
+    dev = _dev(codes)
+    _dev(scales)
+    _dev(global_scale)
+    K = codes.shape[-1] * 2
+    R = codes.numel() * 2 // K if K else 0
+    if scales.numel() * 16 != R * K:
+        raise ValueError("codes and scales sizes disagree")
+    y = out if out is not None else torch.empty(*codes.shape[:-1], K, dtype=out_dtype, device=dev)
+    st = L.nvfp4_dequantize(codes.data_ptr(), scales.data_ptr(), global_scale.data_ptr(), R, K,
+                            block, y.data_ptr(), _dtype(y), _stream(dev))
+    _check("nvfp4_dequantize", st)
+    return y
+
+
+def quantize_kv_sink(kv: torch.Tensor, n_first: int = 128, n_last: int = 128, offsets=(-2, 6),
+                     hadamard: bool = False, global_scale: torch.Tensor | None = None,
+                     block: int = 16, workspace=None):
+    """Attention-sink KV mode on kv[B, H, T, D].
+
+    Returns (codes[B,H,Tm,D/2], scales[B,H,Tm,D/16], global_scale[1], sink[B,H,nf+nl,D]).
+    """
+    L = load()
+    dev = _dev(kv)
+    if kv.dim() != 4:
+        raise ValueError("kv must be [B, H, T, D]")
+    B, H, T, D = kv.shape
+    Tm = T - n_first - n_last
+    if Tm < 0 or n_first < 0 or n_last < 0:
+        raise ValueError("n_first + n_last must not exceed T")
+    f_lo, f_hi = _offsets(offsets)
+    flags = HADAMARD128 if hadamard else 0
+    codes = torch.empty(B, H, Tm, D // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(B, H, Tm, D // 16, dtype=torch.uint8, device=dev)
+    sink = torch.empty(B, H, n_first + n_last, D, dtype=kv.dtype, device=dev)
+    if global_scale is not None:
+        flags |= GSCALE_GIVEN
+        g = global_scale
+    else:
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    wsb = int(L.nvfp4_workspace_bytes(B * H * Tm, D, flags))
+    ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = L.nvfp4_quantize_kv_sink(kv.data_ptr(), _dtype(kv), B, H, T, D, n_first, n_last, block,
+                                  f_lo, f_hi, flags, codes.data_ptr(), scales.data_ptr(),
+                                  g.data_ptr(), sink.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  _stream(dev))
+    _check("nvfp4_quantize_kv_sink", st)
+    return codes, scales, g, sink
+
+
+def dequantize_kv_sink(codes, scales, global_scale, sink, T: int, n_first: int, n_last: int,
+                       out_dtype=torch.float32, block: int = 16):
+    L = load()
+    dev = _dev(codes)
+    _dev(scales)
+    _dev(sink)
+    B, H, NS, D = sink.shape
+    if NS != n_first + n_last:
+        raise ValueError("sink holds n_first + n_last tokens")
+    y = torch.empty(B, H, T, D, dtype=out_dtype, device=dev)
+    st = L.nvfp4_dequantize_kv_sink(codes.data_ptr(), scales.data_ptr(), global_scale.data_ptr(),
+                                    sink.data_ptr(), _dtype(sink), B, H, T, D, n_first, n_last,
+                                    block, y.data_ptr(), _dtype(y), _stream(dev))
+    _check("nvfp4_dequantize_kv_sink", st)
+    return y
+
+
+def hadamard128(x: torch.Tensor) -> torch.Tensor:
+    """FP32 y = x H / sqrt(128) per 128-vector (x bf16), as the quantizer computes it."""
+    L = load()
+    dev = _dev(x)
+    if x.shape[-1] % 128:
+        raise ValueError("last dimension must be a multiple of 128")
+    y = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    st = L.nvfp4_hadamard128(x.data_ptr(), _dtype(x), x.numel() // 128, y.data_ptr(),
+                             _stream(dev))
+    _check("nvfp4_hadamard128", st)
+    return y

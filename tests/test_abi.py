@@ -1,0 +1,112 @@
+"""The C-ABI library loads and exports every symbol include/nvfp4.h declares, and
+rejects bad arguments on the host (no GPU needed: checks run before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from microscaling_fp4_block_amd import build, nvfp4
+
+    if not os.path.exists(nvfp4.LIB_PATH):
+        build.build()
+    return nvfp4.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_quantize_kv_sink",
+              "nvfp4_dequantize_kv_sink", "nvfp4_hadamard128", "nvfp4_workspace_bytes",
+              "nvfp4_status_str", "nvfp4_abi_version", "nvfp4_global_scale"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from microscaling_fp4_block_amd import nvfp4
+
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert n in nvfp4.SIGNATURES, n
+
+
+def test_version_and_status_text(lib):
+    assert lib.nvfp4_abi_version() == 1
+    texts = {lib.nvfp4_status_str(s).decode() for s in range(6)}
+    assert len(texts) == 6
+    assert lib.nvfp4_status_str(99).decode() == "unknown status"
+    assert lib.nvfp4_workspace_bytes(8192, 28672, 0) >= 4 * 1024
+
+
+P = 0x10000  # a well-aligned fake device address: every call below fails its checks first
+
+
+def q(lib, **kw):
+    a = dict(x=P, xdt=1, rows=4, cols=64, block=16, f_lo=-2, f_hi=6, flags=0, codes=P,
+             scales=P, gs=P, ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.nvfp4_quantize(a["x"], a["xdt"], a["rows"], a["cols"], a["block"], a["f_lo"],
+                              a["f_hi"], a["flags"], a["codes"], a["scales"], a["gs"], a["ws"],
+                              a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(scales=None), 1), (dict(gs=None), 1),
+    (dict(xdt=7), 1), (dict(block=32), 1), (dict(f_lo=1), 1), (dict(f_hi=-1), 1),
+    (dict(f_lo=-127), 1), (dict(f_hi=127), 1), (dict(flags=8), 1),
+    (dict(cols=24), 2), (dict(cols=0), 2), (dict(rows=-1), 2), (dict(rows=1 << 40), 2),
+    (dict(flags=1, xdt=0), 1), (dict(flags=1, cols=64), 2),
+    (dict(x=P + 8), 3), (dict(codes=P + 4), 3),
+    (dict(ws=None), 4), (dict(wsb=16), 4),
+])
+def test_quantize_argument_checks(lib, kw, status):
+    assert q(lib, **kw) == status
+
+
+def test_dequantize_argument_checks(lib):
+    f = lib.nvfp4_dequantize
+    assert f(None, P, P, 4, 64, 16, P, 0, None) == 1
+    assert f(P, P, P, 4, 64, 8, P, 0, None) == 1
+    assert f(P, P, P, 4, 60, 16, P, 0, None) == 2
+    assert f(P, P, P, 4, 64, 16, P + 4, 0, None) == 3
+    assert f(P, P, P, 4, 64, 16, P, 5, None) == 1
+
+
+def test_sink_argument_checks(lib):
+    f = lib.nvfp4_quantize_kv_sink
+    base = [P, 1, 1, 8, 300, 128, 128, 128, 16, -2, 6, 0, P, P, P, P, P, 1 << 20, None]
+    a = list(base); a[6] = 200          # n_first + n_last > T
+    assert f(*a) == 2
+    a = list(base); a[5] = 120          # D not a multiple of 16
+    assert f(*a) == 2
+    a = list(base); a[15] = None        # sink missing
+    assert f(*a) == 1
+    g = lib.nvfp4_dequantize_kv_sink
+    assert g(P, P, P, P, 1, 1, 8, 300, 128, 200, 128, 16, P, 0, None) == 2
+    assert g(P, P, P, None, 1, 1, 8, 300, 128, 128, 128, 16, P, 0, None) == 1
+
+
+def test_hadamard_argument_checks(lib):
+    f = lib.nvfp4_hadamard128
+    assert f(P, 0, 4, P, None) == 1     # FP32 input is not supported by the MFMA transform
+    assert f(None, 1, 4, P, None) == 1
+    assert f(P, 1, -1, P, None) == 2
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+
+    import microscaling_fp4_block_amd as nv
+
+    with pytest.raises(ValueError):
+        nv.quantize(torch.zeros(4, 64))
