@@ -85,6 +85,62 @@ def cpu_baseline(x_host: np.ndarray, budget_s: float = 10.0) -> dict:
                       f"quantize [-2,6] + bf16 dequantize, {t:.2f} s wall on {threads} threads"}
 
 
+# quantize_kernel dispatches of a --profile run, in launch order
+PROFILE_PHASES = ["search [-2,6] in the warm-up step"] + ["search [-2,6], S_g given"] * 5 + \
+    ["max-scaling control [0,0], S_g given"] * 5
+COPY_BYTES = 1 << 30
+
+
+def rocpd_summary(dbs):
+    """Per-kernel durations and counters from rocprofv3 SQLite outputs of --profile."""
+    import sqlite3
+    from collections import defaultdict
+
+    for path in dbs:
+        db = sqlite3.connect(path)
+        print(f"== {path}")
+        rows = db.execute("select name, duration, grid_x, workgroup_x, vgpr_count, "
+                          "accum_vgpr_count, sgpr_count, lds_size from kernels "
+                          "order by start").fetchall()
+        if rows:
+            agg = defaultdict(list)
+            info = {}
+            for name, dur, gx, wx, vg, ag, sg, lds in rows:
+                agg[name].append(dur / 1000.0)
+                info[name] = (gx // max(wx, 1), wx, vg, ag, sg, lds)
+            print("kernel | calls | avg us | min us | max us | workgroups x threads | "
+                  "vgpr/agpr/sgpr | lds B")
+            for name, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+                gx, wx, vg, ag, sg, lds = info[name]
+                print(f"{name} | {len(ds)} | {sum(ds) / len(ds):.2f} | {min(ds):.2f} | "
+                      f"{max(ds):.2f} | {gx} x {wx} | {vg}/{ag}/{sg} | {lds}")
+            q = [d for n, d in ((n, d / 1000.0) for n, d, *_ in rows)
+                 if n.startswith("void nvfp4::quantize_kernel<true>")]
+            if len(q) >= len(PROFILE_PHASES):
+                by = defaultdict(list)
+                for ph, d in zip(PROFILE_PHASES, q):
+                    by[ph].append(d)
+                print("quantize_kernel<true> by phase:")
+                for ph, ds in by.items():
+                    print(f"  {ph}: n={len(ds)} avg {sum(ds) / len(ds):.2f} us")
+        crow = db.execute("select kernel_name, counter_name, value from counters_collection "
+                          "order by start").fetchall()
+        if crow:
+            agg = defaultdict(list)
+            for name, cn, v in crow:
+                agg[(name, cn)].append(v)
+            print("kernel | counter | dispatches | avg KiB per dispatch")
+            for (name, cn), vs in sorted(agg.items()):
+                print(f"{name} | {cn} | {len(vs)} | {sum(vs) / len(vs):.1f}")
+            for (name, cn), vs in agg.items():
+                if "copyBuffer" in name:
+                    big = [v for v in vs if v >= 0.5 * max(vs)]  # the 1 GiB copies only
+                    avg = sum(big) / len(big)
+                    f = (COPY_BYTES / 1024.0) / avg
+                    print(f"calibration: {cn} over {len(big)} copies of {COPY_BYTES} B reads "
+                          f"{avg:.1f} KiB per copy -> scale factor {f:.4f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,7 +150,12 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: a few launches of each kernel plus a "
                          "plain 1 GiB device copy for counter calibration; no JSON")
+    ap.add_argument("--rocpd-summary", nargs="+", metavar="DB",
+                    help="print a text summary of rocprofv3 databases of a --profile run")
     args = ap.parse_args()
+    if args.rocpd_summary:
+        rocpd_summary(args.rocpd_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the quantizer has no multi-GPU path.", file=sys.stderr)
@@ -137,11 +198,13 @@ def main():
         nv.dequantize(codes, scales, g, torch.bfloat16, out=y)
 
     if args.profile:
+        # Fixed launch order, so a profile can be split by phase (see PROFILE_PHASES):
+        # warm-up step, then 5 launches of each phase, then the 1 GiB copy.
         step()
         gfix = g.clone()
         torch.cuda.synchronize()
-        for fn in (step, search_only, amax_only, control_only, dequant_only):
-            for _ in range(3):
+        for fn in (search_only, control_only, amax_only, dequant_only):
+            for _ in range(5):
                 fn()
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -41,13 +41,24 @@ RegionMap plain_map(int64_t rows, int64_t cols) {
 }
 
 // Global amax + finalize into gscale. The workspace holds the partials.
-nvfp4_status run_global_scale(const void *x, bool bf16, const RegionMap &m, float *gscale,
-                              void *ws, hipStream_t s) {
+nvfp4_status run_global_scale(const void *x, bool bf16, bool hadamard, const RegionMap &m,
+                              float *gscale, void *ws, hipStream_t s) {
   AmaxArgs a{x, (uint32_t *)ws, m};
-  const int groups = amax_groups(m.nblocks, bf16);
-  hipError_t e = launch_amax(a, bf16, groups, s);
+  int groups;
+  hipError_t e;
+  if (hadamard) {
+    groups = amax_hadamard_groups(m.nblocks);
+    e = launch_amax_hadamard(a, groups, s);
+  } else {
+    groups = amax_groups(m.nblocks, bf16);
+    e = launch_amax(a, bf16, groups, s);
+  }
   if (e != hipSuccess) return NVFP4_EHIP;
   return hip_status(launch_finalize((const uint32_t *)ws, groups, gscale, s));
+}
+
+hipError_t run_quantize(const QuantArgs &q, bool bf16, bool hadamard, hipStream_t s) {
+  return hadamard ? launch_quantize_hadamard(q, s) : launch_quantize(q, bf16, s);
 }
 
 nvfp4_status check_offsets(int block, int f_lo, int f_hi) {
@@ -95,50 +106,52 @@ size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags) {
 nvfp4_status nvfp4_global_scale(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
                                 uint32_t flags, float *global_scale, void *workspace,
                                 size_t workspace_bytes, void *stream) {
-  if (!x || !global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
+  if (!global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
   nvfp4_status st = check_shape(rows, cols, flags & ~NVFP4_GSCALE_GIVEN, xdt);
   if (st) return st;
+  if (rows > 0 && !x) return NVFP4_EINVAL;
   if (!aligned(x, 16)) return NVFP4_EALIGN;
   if (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4))
     return NVFP4_EWORKSPACE;
-  if (flags & NVFP4_HADAMARD128) return NVFP4_EINVAL;  // not available in this build
-  return run_global_scale(x, xdt == NVFP4_BF16, plain_map(rows, cols), global_scale, workspace,
-                          (hipStream_t)stream);
+  return run_global_scale(x, xdt == NVFP4_BF16, flags & NVFP4_HADAMARD128, plain_map(rows, cols),
+                          global_scale, workspace, (hipStream_t)stream);
 }
 
 nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
                             int block, int f_lo, int f_hi, uint32_t flags, uint8_t *codes,
                             uint8_t *scales, float *global_scale, void *workspace,
                             size_t workspace_bytes, void *stream) {
-  if (!x || !codes || !scales || !global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
+  if (!global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
   nvfp4_status st = check_offsets(block, f_lo, f_hi);
   if (st) return st;
   st = check_shape(rows, cols, flags, xdt);
   if (st) return st;
+  if (rows > 0 && (!x || !codes || !scales)) return NVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 8)) return NVFP4_EALIGN;
   const bool given = flags & NVFP4_GSCALE_GIVEN;
   if (!given && (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4)))
     return NVFP4_EWORKSPACE;
-  if (flags & NVFP4_HADAMARD128) return NVFP4_EINVAL;  // not available in this build
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = xdt == NVFP4_BF16;
+  const bool had = flags & NVFP4_HADAMARD128;
   const RegionMap m = plain_map(rows, cols);
   if (!given) {
-    st = run_global_scale(x, bf16, m, global_scale, workspace, s);
+    st = run_global_scale(x, bf16, had, m, global_scale, workspace, s);
     if (st) return st;
   }
   if (m.nblocks == 0) return NVFP4_OK;
   QuantArgs q{x, codes, scales, global_scale, m, f_lo, f_hi};
-  return hip_status(launch_quantize(q, bf16, s));
+  return hip_status(run_quantize(q, bf16, had, s));
 }
 
 nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
                               const float *global_scale, int64_t rows, int64_t cols, int block,
                               void *y, nvfp4_dtype ydt, void *stream) {
-  if (!codes || !scales || !global_scale || !y || !dtype_ok(ydt)) return NVFP4_EINVAL;
+  if (!global_scale || !dtype_ok(ydt)) return NVFP4_EINVAL;
   if (block != 16) return NVFP4_EINVAL;
   nvfp4_status st = check_shape(rows, cols, 0, ydt);
   if (st) return st;
+  if (rows > 0 && (!codes || !scales || !y)) return NVFP4_EINVAL;
   if (!aligned(codes, 8) || !aligned(y, 16)) return NVFP4_EALIGN;
   DequantArgs a{codes, scales, global_scale, y, (uint32_t)(rows * (cols / 16))};
   if (a.nblocks == 0) return NVFP4_OK;
@@ -151,22 +164,25 @@ nvfp4_status nvfp4_quantize_kv_sink(const void *kv, nvfp4_dtype dt, int64_t B, i
                                     uint8_t *codes, uint8_t *scales, float *global_scale,
                                     void *sink, void *workspace, size_t workspace_bytes,
                                     void *stream) {
-  if (!kv || !codes || !scales || !global_scale || !sink || !dtype_ok(dt)) return NVFP4_EINVAL;
+  if (!global_scale || !dtype_ok(dt)) return NVFP4_EINVAL;
   nvfp4_status st = check_offsets(block, f_lo, f_hi);
   if (st) return st;
   if (B < 0 || H < 0 || T < 0 || D <= 0 || n_first < 0 || n_last < 0 || n_first + n_last > T)
     return NVFP4_ESHAPE;
   if (T > (1ll << 31) || B * H > (1ll << 31)) return NVFP4_ESHAPE;
   const int64_t BH = B * H, NS = n_first + n_last, Tm = T - NS;
+  if (BH * T > 0 && !kv) return NVFP4_EINVAL;
+  if (BH * NS > 0 && !sink) return NVFP4_EINVAL;
+  if (BH * Tm > 0 && (!codes || !scales)) return NVFP4_EINVAL;
   st = check_shape(BH * T, D, flags, dt);
   if (st) return st;
   if (!aligned(kv, 16) || !aligned(codes, 8) || !aligned(sink, 16)) return NVFP4_EALIGN;
   const bool given = flags & NVFP4_GSCALE_GIVEN;
   if (!given && (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4)))
     return NVFP4_EWORKSPACE;
-  if (flags & NVFP4_HADAMARD128) return NVFP4_EINVAL;  // not available in this build
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dt == NVFP4_BF16;
+  const bool had = flags & NVFP4_HADAMARD128;
   const uint32_t es = bf16 ? 2u : 4u;
 
   if (BH > 0 && NS > 0) {
@@ -197,12 +213,12 @@ nvfp4_status nvfp4_quantize_kv_sink(const void *kv, nvfp4_dtype dt, int64_t B, i
   m.n_first = (uint32_t)n_first;
   m.cols = (uint32_t)D;
   if (!given) {
-    st = run_global_scale(kv, bf16, m, global_scale, workspace, s);
+    st = run_global_scale(kv, bf16, had, m, global_scale, workspace, s);
     if (st) return st;
   }
   if (m.nblocks == 0) return NVFP4_OK;
   QuantArgs q{kv, codes, scales, global_scale, m, f_lo, f_hi};
-  return hip_status(launch_quantize(q, bf16, s));
+  return hip_status(run_quantize(q, bf16, had, s));
 }
 
 nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scales,
@@ -210,16 +226,18 @@ nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scale
                                       nvfp4_dtype sink_dt, int64_t B, int64_t H, int64_t T,
                                       int64_t D, int64_t n_first, int64_t n_last, int block,
                                       void *y, nvfp4_dtype ydt, void *stream) {
-  if (!codes || !scales || !global_scale || !sink || !y || !dtype_ok(sink_dt) || !dtype_ok(ydt))
-    return NVFP4_EINVAL;
+  if (!global_scale || !dtype_ok(sink_dt) || !dtype_ok(ydt)) return NVFP4_EINVAL;
   if (block != 16) return NVFP4_EINVAL;
   if (B < 0 || H < 0 || T < 0 || D <= 0 || D % 16 || n_first < 0 || n_last < 0 ||
       n_first + n_last > T)
     return NVFP4_ESHAPE;
   if (T > (1ll << 31) || B * H > (1ll << 31)) return NVFP4_ESHAPE;
-  const int64_t BH = B * H;
+  const int64_t BH = B * H, NS = n_first + n_last, Tm = T - NS;
   nvfp4_status st = check_shape(BH * T, D, 0, ydt);
   if (st) return st;
+  if (BH * T > 0 && !y) return NVFP4_EINVAL;
+  if (BH * NS > 0 && !sink) return NVFP4_EINVAL;
+  if (BH * Tm > 0 && (!codes || !scales)) return NVFP4_EINVAL;
   if (!aligned(codes, 8) || !aligned(sink, 16) || !aligned(y, 16)) return NVFP4_EALIGN;
   DequantKvArgs a{};
   a.codes = codes;
@@ -241,10 +259,12 @@ nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scale
 
 nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,
                                void *stream) {
-  (void)stream;
-  if (!x || !y || xdt != NVFP4_BF16) return NVFP4_EINVAL;
-  if (rows < 0) return NVFP4_ESHAPE;
-  return NVFP4_EINVAL;  // not available in this build
+  if (xdt != NVFP4_BF16) return NVFP4_EINVAL;
+  if (rows < 0 || rows > kMaxBlocks / 8) return NVFP4_ESHAPE;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !y) return NVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_EALIGN;
+  return hip_status(launch_hadamard((const uint16_t *)x, y, (uint32_t)rows, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -94,6 +94,10 @@ struct DequantKvArgs {
 hipError_t launch_amax(const AmaxArgs &a, bool bf16, int groups, hipStream_t s);
 hipError_t launch_finalize(const uint32_t *partials, int n, float *gscale, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s);
+int amax_hadamard_groups(uint32_t nblocks);
+hipError_t launch_amax_hadamard(const AmaxArgs &a, int groups, hipStream_t s);
+hipError_t launch_quantize_hadamard(const QuantArgs &a, hipStream_t s);
+hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s);
 hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_dequantize_kv(const DequantKvArgs &a, bool sink_bf16, bool out_bf16,

@@ -237,54 +237,236 @@ __device__ __forceinline__ float candidate_sse(const float (&x)[16], float d, fl
   return s;
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  __shared__ f32x2 tbl[128];  // per pattern: (decode d, encode r)
-  const float sg = *a.gscale;
-  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+// Per-workgroup table of every pattern's (decode d, encode r = 1/d); a pattern
+// whose r is not finite (p = 0, or 1/d overflows) stores (0, 0) so that the
+// candidate codes everything as 0 through the same arithmetic.
+__device__ __forceinline__ void build_scale_table(f32x2 *tbl, float sg) {
   if (threadIdx.x < 127) {
     float d = e4m3_value(threadIdx.x) * sg;
     float r = 1.0f / d;
-    if (!(r < INFINITY)) {  // pattern 0, or 1/d overflows: codes everything as 0
+    if (!(r < INFINITY)) {
       d = 0.0f;
       r = 0.0f;
     }
     tbl[threadIdx.x] = f32x2{d, r};
   }
   __syncthreads();
+}
+
+// ScaleSearch on one block held in registers: default pattern p0 from the
+// block amax, then f = 0, f_lo..f_hi; first strictly smaller SSE wins.
+// Writes the chosen pattern (0x7F and zero codes under the non-finite
+// contract) and the two code words.
+__device__ __forceinline__ void search_block(const float (&x)[16], float sg, bool sg_ok,
+                                             const f32x2 *tbl, int f_lo, int f_hi,
+                                             uint32_t &best_p, uint32_t &bc0, uint32_t &bc1) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  best_p = 0x7Fu;
+  bc0 = 0u;
+  bc1 = 0u;
+  if (sg_ok && am < 0x7F800000u) {
+    const float amax = __uint_as_float(am);
+    const float t = (amax / 6.0f) / sg;
+    const uint32_t p0 = e4m3_rne_sat(t);
+    f32x2 dr = tbl[p0];
+    float best = candidate_sse(x, dr.x, dr.y, bc0, bc1);
+    best_p = p0;
+    for (int f = f_lo; f <= f_hi; ++f) {
+      if (f == 0) continue;
+      const int p = (int)p0 + f;
+      const bool valid = (unsigned)p <= 126u;
+      dr = tbl[valid ? p : (int)p0];
+      uint32_t c0, c1;
+      const float s = candidate_sse(x, dr.x, dr.y, c0, c1);
+      const bool win = valid && (s < best);
+      best = win ? s : best;
+      best_p = win ? (uint32_t)p : best_p;
+      bc0 = win ? c0 : bc0;
+      bc1 = win ? c1 : bc1;
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  __shared__ f32x2 tbl[128];
+  const float sg = *a.gscale;
+  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+  build_scale_table(tbl, sg);
 
   const uint32_t stride = gridDim.x * kThreads;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
     float x[16];
     load_block<BF16>(a.x, block_offset(a.map, b), x);
-    uint32_t am = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
-
-    uint32_t best_p = 0x7Fu, bc0 = 0u, bc1 = 0u;
-    if (sg_ok && am < 0x7F800000u) {
-      const float amax = __uint_as_float(am);
-      const float t = (amax / 6.0f) / sg;
-      const uint32_t p0 = e4m3_rne_sat(t);
-      f32x2 dr = tbl[p0];
-      float best = candidate_sse(x, dr.x, dr.y, bc0, bc1);
-      best_p = p0;
-      for (int f = a.f_lo; f <= a.f_hi; ++f) {
-        if (f == 0) continue;
-        const int p = (int)p0 + f;
-        const bool valid = (unsigned)p <= 126u;
-        dr = tbl[valid ? p : (int)p0];
-        uint32_t c0, c1;
-        const float s = candidate_sse(x, dr.x, dr.y, c0, c1);
-        const bool win = valid && (s < best);
-        best = win ? s : best;
-        best_p = win ? (uint32_t)p : best_p;
-        bc0 = win ? c0 : bc0;
-        bc1 = win ? c1 : bc1;
-      }
-    }
+    uint32_t best_p, bc0, bc1;
+    search_block(x, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
     *(uint2 *)(a.codes + (uint64_t)b * 8u) = make_uint2(bc0, bc1);
     a.scales[b] = (uint8_t)best_p;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128-point Hadamard pre-transform on MFMA (ScaleSearch summary page,
+// ScaleSearchAttention, 非干渉処理（IP）と絶対値低減: Hadamard incoherence
+// processing of Q and K). y = x H / sqrt(128) per contiguous 128-vector, H the
+// Sylvester matrix H[j][k] = (-1)^popcount(j & k).
+//
+// One wave transforms 32 vectors with v_mfma_f32_32x32x16_bf16 as
+// Y^T = H' X^T: B (16 x 32) is a 16-element slice of the 32 vectors straight
+// from memory (lane: vector lane & 31, elements 8 (lane >> 5) .. +7 of the
+// slice), A (32 x 16) is the matching slice of 32 rows of H (entries +-1,
+// exact in bf16), generated in registers. The rows of H are taken in the
+// order that makes accumulator v of lane l hold feature 32 t + 16 (l >> 5) + v
+// of vector l & 31, i.e. one whole 16-element quantization block per lane and
+// per 32-feature tile t. The products are exact; the FP32 accumulation may
+// round, so the transform is within a few FP32 ulps of the exact one. The sum
+// is scaled in FP64 by the double nearest 2^-3.5 and rounded once to FP32.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr double kInvSqrt128 = 0x1.6a09e667f3bcdp-4;  // nearest double to 2^-3.5
+
+// Feature (row of H) held by accumulator row i of tile t.
+__device__ __forceinline__ uint32_t hadamard_feature(uint32_t t, uint32_t i) {
+  return 32u * t + 16u * ((i >> 2) & 1u) + 4u * (i >> 3) + (i & 3u);
+}
+
+struct HadamardLane {
+  uint32_t base[4];  // bf16 pairs of H[feat][8g + e] signs for e = 0..7 (feat & 7 part)
+  uint32_t lo;       // features of this lane's A row without the tile part
+  uint32_t g;        // lane >> 5: which 8 of each 16-element K slice
+};
+
+__device__ __forceinline__ HadamardLane hadamard_lane_setup() {
+  HadamardLane h;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t i = lane & 31u;
+  h.g = lane >> 5;
+  h.lo = hadamard_feature(0, i);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t e0 = 2u * q, e1 = 2u * q + 1u;
+    const uint32_t s0 = __builtin_popcount(h.lo & e0) & 1u;
+    const uint32_t s1 = __builtin_popcount(h.lo & e1) & 1u;
+    h.base[q] = (s0 ? 0xBF80u : 0x3F80u) | ((s1 ? 0xBF80u : 0x3F80u) << 16);
+  }
+  return h;
+}
+
+// A operand for tile t and K slice ks: the base signs times
+// (-1)^popcount(feat & (16 ks + 8 g)) (the high bits of k; bits 0..2 are in base).
+__device__ __forceinline__ bf16x8 hadamard_a(const HadamardLane &h, uint32_t t, uint32_t ks) {
+  const uint32_t feat = 32u * t + h.lo;
+  const uint32_t neg = __builtin_popcount(feat & (16u * ks + 8u * h.g)) & 1u;
+  const uint32_t m = neg ? 0x80008000u : 0u;
+  uint4 v = make_uint4(h.base[0] ^ m, h.base[1] ^ m, h.base[2] ^ m, h.base[3] ^ m);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Load this lane's B slices of one 128-vector: elements 16 ks + 8 g .. +7.
+__device__ __forceinline__ void hadamard_load(const uint16_t *x, uint64_t off, bool valid,
+                                              uint32_t g, uint4 (&b)[8]) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    b[ks] = valid ? *(const uint4 *)(x + off + 16u * ks + 8u * g) : make_uint4(0, 0, 0, 0);
+}
+
+// Tile t of the transform: y[v] = feature 32 t + 16 g + v of this lane's vector.
+__device__ __forceinline__ void hadamard_tile(const HadamardLane &h, const uint4 (&b)[8], uint32_t t,
+                                              float (&y)[16]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hadamard_a(h, t, ks),
+                                                  __builtin_bit_cast(bf16x8, b[ks]), acc, 0, 0, 0);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) y[v] = (float)((double)acc[v] * kInvSqrt128);
+}
+
+// Quantize with the Hadamard pre-transform (bf16 input, cols % 128 == 0). One
+// wave per 32 vectors; each lane codes four blocks of its vector.
+__global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a) {
+  __shared__ f32x2 tbl[128];
+  const float sg = *a.gscale;
+  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+  build_scale_table(tbl, sg);
+
+  const HadamardLane h = hadamard_lane_setup();
+  const uint32_t nvec = a.map.nblocks / 8u;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  for (uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile * 32u < nvec;
+       tile += nwaves) {
+    const uint32_t vec = tile * 32u + (lane & 31u);
+    const bool valid = vec < nvec;
+    uint4 b[8];
+    hadamard_load((const uint16_t *)a.x, valid ? block_offset(a.map, vec * 8u) : 0, valid, h.g, b);
+#pragma unroll 1
+    for (uint32_t t = 0; t < 4; ++t) {
+      float y[16];
+      hadamard_tile(h, b, t, y);
+      if (valid) {
+        uint32_t best_p, bc0, bc1;
+        search_block(y, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
+        const uint32_t blk = vec * 8u + 2u * t + h.g;
+        *(uint2 *)(a.codes + (uint64_t)blk * 8u) = make_uint2(bc0, bc1);
+        a.scales[blk] = (uint8_t)best_p;
+      }
+    }
+  }
+}
+
+// Global amax of the transformed values.
+__global__ __launch_bounds__(kThreads) void amax_hadamard_kernel(AmaxArgs a) {
+  const HadamardLane h = hadamard_lane_setup();
+  const uint32_t nvec = a.map.nblocks / 8u;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  uint32_t m = 0;
+  for (uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile * 32u < nvec;
+       tile += nwaves) {
+    const uint32_t vec = tile * 32u + (lane & 31u);
+    const bool valid = vec < nvec;
+    uint4 b[8];
+    hadamard_load((const uint16_t *)a.x, valid ? block_offset(a.map, vec * 8u) : 0, valid, h.g, b);
+#pragma unroll 1
+    for (uint32_t t = 0; t < 4; ++t) {
+      float y[16];
+      hadamard_tile(h, b, t, y);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) m = max(m, __float_as_uint(y[v]) & 0x7FFFFFFFu);
+    }
+  }
+  m = group_max_u32(m);
+  if (threadIdx.x == 0) a.partials[blockIdx.x] = m;
+}
+
+// The transform alone: y[nvec][128] FP32.
+__global__ __launch_bounds__(kThreads) void hadamard_kernel(const uint16_t *x, float *out,
+                                                            uint32_t nvec) {
+  const HadamardLane h = hadamard_lane_setup();
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  for (uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile * 32u < nvec;
+       tile += nwaves) {
+    const uint32_t vec = tile * 32u + (lane & 31u);
+    const bool valid = vec < nvec;
+    uint4 b[8];
+    hadamard_load(x, (uint64_t)(valid ? vec : 0) * 128u, valid, h.g, b);
+#pragma unroll 1
+    for (uint32_t t = 0; t < 4; ++t) {
+      float y[16];
+      hadamard_tile(h, b, t, y);
+      if (valid) {
+        float4 *o = (float4 *)(out + (uint64_t)vec * 128u + 32u * t + 16u * h.g);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = make_float4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]);
+      }
+    }
   }
 }
 
@@ -415,6 +597,32 @@ hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
     hipLaunchKernelGGL(quantize_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(quantize_kernel<false>, dim3(g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+static int hadamard_groups(uint32_t nvec, int cap) {
+  const uint64_t tiles = (nvec + 31u) / 32u;
+  uint64_t g = (tiles + (kThreads / 64) - 1) / (kThreads / 64);
+  if (g < 1) g = 1;
+  return (int)(g > (uint64_t)cap ? cap : g);
+}
+
+int amax_hadamard_groups(uint32_t nblocks) { return hadamard_groups(nblocks / 8u, kMaxAmaxGroups); }
+
+hipError_t launch_amax_hadamard(const AmaxArgs &a, int groups, hipStream_t s) {
+  hipLaunchKernelGGL(amax_hadamard_kernel, dim3(groups), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_hadamard(const QuantArgs &a, hipStream_t s) {
+  const int g = hadamard_groups(a.map.nblocks / 8u, kMaxQuantGroups);
+  hipLaunchKernelGGL(quantize_hadamard_kernel, dim3(g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, hipStream_t s) {
+  const int g = hadamard_groups(nvec, kMaxQuantGroups);
+  hipLaunchKernelGGL(hadamard_kernel, dim3(g), dim3(kThreads), 0, s, x, y, nvec);
   return hipGetLastError();
 }
 

@@ -395,23 +395,79 @@ static int popcount_parity(unsigned v)
     return p;
 }
 
+typedef struct {
+    const void *x;
+    int dtype;
+    int64_t v0, v1;
+    float *y;
+} hjob_t;
+
+/* The Sylvester matrix, entry by entry from its definition; filled before any
+ * worker thread starts, read-only afterwards. */
+static double H[128][128];
+
+static void fill_hadamard(void)
+{
+    for (int j = 0; j < 128; ++j)
+        for (int k = 0; k < 128; ++k)
+            H[j][k] = popcount_parity((unsigned)(j & k)) ? -1.0 : 1.0;
+}
+
+static void hadamard_vectors(const hjob_t *J)
+{
+    const double c = sqrt(1.0 / 128.0); /* correctly rounded 2^-3.5 */
+    for (int64_t v = J->v0; v < J->v1; ++v) {
+        double in[128];
+        for (int k = 0; k < 128; ++k)
+            in[k] = (double)load_elem(J->x, J->dtype, v * 128 + k);
+        for (int j = 0; j < 128; ++j) {
+            double s = 0.0;
+            for (int k = 0; k < 128; ++k)
+                s += H[j][k] * in[k];
+            J->y[v * 128 + j] = (float)(s * c);
+        }
+    }
+}
+
+static void *hadamard_thread(void *arg)
+{
+    hadamard_vectors((const hjob_t *)arg);
+    return NULL;
+}
+
+static int hadamard_threads(const void *x, int dtype, int64_t nvec, float *y, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    pthread_t th[256];
+    int running[256];
+    hjob_t jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].x = x;
+        jobs[t].dtype = dtype;
+        jobs[t].y = y;
+        jobs[t].v0 = nvec * t / nthreads;
+        jobs[t].v1 = nvec * (t + 1) / nthreads;
+    }
+    fill_hadamard();
+    for (int t = 0; t < nthreads; ++t) {
+        running[t] = pthread_create(&th[t], NULL, hadamard_thread, &jobs[t]) == 0;
+        if (!running[t])
+            hadamard_vectors(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (running[t])
+            pthread_join(th[t], NULL);
+    return ORACLE_OK;
+}
+
 int oracle_hadamard128(const void *x, int dtype, int64_t nvec, float *y)
 {
     if (!x || !y || nvec < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
         return ORACLE_EINVAL;
-    const double c = sqrt(1.0 / 128.0); /* correctly rounded 2^-3.5 */
-    for (int64_t v = 0; v < nvec; ++v) {
-        double in[128];
-        for (int k = 0; k < 128; ++k)
-            in[k] = (double)load_elem(x, dtype, v * 128 + k);
-        for (int j = 0; j < 128; ++j) {
-            double s = 0.0;
-            for (int k = 0; k < 128; ++k)
-                s += popcount_parity((unsigned)(j & k)) ? -in[k] : in[k];
-            y[v * 128 + j] = (float)(s * c);
-        }
-    }
-    return ORACLE_OK;
+    return hadamard_threads(x, dtype, nvec, y, 1);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -442,7 +498,7 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int f_
         ybuf = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
         if (!ybuf)
             return ORACLE_ENOMEM;
-        oracle_hadamard128(x, dtype, n / 128, ybuf);
+        hadamard_threads(x, dtype, n / 128, ybuf, nthreads);
         src = ybuf;
         sdt = ORACLE_F32;
     }
