@@ -308,6 +308,216 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Certified search for bf16 inputs.
+//
+// The exact search above spends ~105 VALU instructions per candidate on the
+// contract's FP32 arithmetic. For bf16 blocks the winner can be established
+// with less work and the same result:
+//
+//  * For candidate f the codes c_i (hence V_i) are computed exactly as in the
+//    contract (y = fl(x * r), hardware E2M1 convert). Let a_i = |x_i|,
+//    x^_i = V_i d (real product), E_f = sum (a_i - V_i d)^2 (real), and
+//    A2 = sum a_i^2. Then E_f = A2 + K_f with K_f = d (d S2 - 2 S1),
+//    S1 = sum a_i V_i, S2 = sum V_i^2.
+//  * S1 and S2 are exact in FP32 (v_dot2_f32_bf16): V_i is a multiple of 1/2
+//    up to 6; an element with V_i > 0 has y > 1/4, so for candidates within
+//    8 normal E4M3 steps of the default pattern (d within a factor 2.6 of
+//    it) a_i > amax/128: every nonzero product and partial sum is a multiple
+//    of 2^(E-15) below 2^(E+8), E the exponent of amax (23 bits). S2 is a
+//    multiple of 1/4 below 577.
+//  * K_f is formed in FP64: d S2 - 2 S1 is exact (< 40 significant bits),
+//    the product with d is rounded once (relative 2^-53).
+//  * The contract's FP32 SSE differs from E_f by at most
+//    delta_f <= 2u (sum x^_i^2 / 8 + 14 E_f) (u = 2^-24): per element the
+//    rounding of x^, e and e^2 moves e^2 by <= 2u(V_i d |t_i| + t_i^2) to
+//    first order, bounded with Cauchy-Schwarz and 2ab <= a^2/8 + 8b^2; the 15
+//    sequential adds contribute <= 15u E_f. With sum x^^2 <= 2 (A2 + E_f) and
+//    E_f <= |K_f - K_0| + E_0 this gives a per-candidate margin
+//    M_f = 2^-18 |D_f| + 2^-23 (0.3 A2 + 15 E_0) (+ FP64/FP32 rounding),
+//    D_f = K_f - K_0 (candidate 0 = offset 0 as reference).
+//  * Winner w = first candidate with least U_f = D_f + M_f. If every other
+//    candidate has L_f = D_f - M_f > U_w, its SSE is certainly larger and w is
+//    the contract's choice. Otherwise (near-ties, or a block outside the
+//    range where the argument holds: non-normal candidate patterns, amax
+//    outside [2^-40, 2^60]) the lane evaluates the contract's FP32 SSE
+//    exactly for the candidates that could win and applies the visiting-order
+//    rule among them.
+//
+// Offsets with one candidate ([0, 0], max scaling) need no search at all.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2 fp4_decode_pair_bf16(uint32_t w, int sel) {
+  switch (sel & 3) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+  }
+}
+
+// Codes of one candidate (encode scale r) and the exact sums S1 = sum x V,
+// S2 = sum V^2 (x and V carry the same sign, so S1 = sum |x| |V|).
+__device__ __forceinline__ void candidate_stats(const float (&x)[16], const uint32_t (&w)[8],
+                                                float r, uint32_t &c0, uint32_t &c1, float &s1,
+                                                float &s2) {
+  uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    cw[j >> 2] = fp4_encode_pair(cw[j >> 2], x[2 * j] * r, x[2 * j + 1] * r, j);
+  float a = 0.0f, b = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bf16x2 v = fp4_decode_pair_bf16(cw[j >> 2], j);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), v, a, false);
+    b = __builtin_amdgcn_fdot2_f32_bf16(v, v, b, false);
+  }
+  c0 = cw[0];
+  c1 = cw[1];
+  s1 = a;
+  s2 = b;
+}
+
+// Codes of a single candidate (no scoring).
+__device__ __forceinline__ void candidate_codes(const float (&x)[16], float r, uint32_t &c0,
+                                                uint32_t &c1) {
+  uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    cw[j >> 2] = fp4_encode_pair(cw[j >> 2], x[2 * j] * r, x[2 * j + 1] * r, j);
+  c0 = cw[0];
+  c1 = cw[1];
+}
+
+// Offset of visiting slot s: slot 0 is f = 0, then FLO, FLO+1, ... without 0.
+template <int FLO>
+__device__ __forceinline__ constexpr int slot_offset(int s) {
+  return s == 0 ? 0 : (FLO + s - 1 < 0 ? FLO + s - 1 : FLO + s);
+}
+
+template <int FLO, int FHI>
+__global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs a) {
+  constexpr int NC = FHI - FLO + 1;  // visiting slots (offset 0 included)
+  __shared__ f32x2 tbl[128];
+  const float sg = *a.gscale;
+  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+  build_scale_table(tbl, sg);
+
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
+    const uint64_t off = block_offset(a.map, b);
+    const uint4 *src = (const uint4 *)((const uint16_t *)a.x + off);
+    const uint4 q0 = src[0], q1 = src[1];
+    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      am = max(am, max((w[k] << 16) & 0x7FFFFFFFu, w[k] & 0x7FFF0000u));
+
+    uint32_t best_p = 0x7Fu, bc0 = 0u, bc1 = 0u;
+    if (sg_ok && am < 0x7F800000u) {
+      const float t = (__uint_as_float(am) / 6.0f) / sg;
+      const uint32_t p0 = e4m3_rne_sat(t);
+      if (NC == 1) {
+        best_p = p0;
+        candidate_codes(x, tbl[p0].y, bc0, bc1);
+      } else {
+        // certificate applies: normal candidate patterns, amax in [2^-40, 2^60]
+        const bool eligible = ((int)p0 + FLO >= 8) && am >= 0x2B800000u && am <= 0x5D800000u;
+        float a2 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
+                                               __builtin_bit_cast(bf16x2, w[k]), a2, false);
+        const double a2ub = (double)a2 * (1.0 + 0x1p-18) + 0x1p-120;
+
+        float D[NC], M[NC];
+        double k0 = 0.0;
+        float cst = 0.0f;  // block part of the margin
+        float best_u = INFINITY;
+        int wslot = 0;
+#pragma unroll
+        for (int sl = 0; sl < NC; ++sl) {
+          const int f = slot_offset<FLO>(sl);
+          const int p = (int)p0 + f;
+          const bool valid = f >= a.f_lo && f <= a.f_hi && p >= 0 && p <= 126;
+          const f32x2 dr = tbl[p < 0 ? 0 : (p > 126 ? 126 : p)];
+          uint32_t c0, c1;
+          float s1, s2;
+          candidate_stats(x, w, dr.y, c0, c1, s1, s2);
+          const double dd = (double)dr.x;
+          const double kf = dd * __builtin_fma(dd, (double)s2, -2.0 * (double)s1);
+          if (sl == 0) {
+            k0 = kf;
+            const double e0ub = kf + a2ub + __builtin_fabs(kf) * 0x1p-50;
+            cst = (float)((0.3 * a2ub + 15.0 * (e0ub > 0.0 ? e0ub : 0.0)) * 0x1p-23 +
+                          (__builtin_fabs(kf) + a2ub) * 0x1p-50) * (1.0f + 0x1p-20f) +
+                  0x1p-120f;
+          }
+          float df = (float)(kf - k0);
+          float mf = __builtin_fmaf(__builtin_fabsf(df), 0x1p-18f, cst);
+          if (!valid) {
+            df = INFINITY;
+            mf = 0.0f;
+          }
+          D[sl] = df;
+          M[sl] = mf;
+          const float u = df + mf;
+          if (sl == 0 || u < best_u) {
+            best_u = u;
+            wslot = sl;
+            bc0 = c0;
+            bc1 = c1;
+          }
+        }
+        // Candidates that might tie or beat w (w itself always counts once).
+        int contenders = 0;
+#pragma unroll
+        for (int sl = 0; sl < NC; ++sl) contenders += (D[sl] - M[sl] <= best_u) ? 1 : 0;
+        best_p = p0 + slot_offset<FLO>(0);
+#pragma unroll
+        for (int sl = 0; sl < NC; ++sl)
+          if (sl == wslot) best_p = (uint32_t)((int)p0 + slot_offset<FLO>(sl));
+        if (!eligible || contenders > 1) {
+          // Exact contract evaluation over the candidates that could win,
+          // in visiting order.
+          float best = INFINITY;
+          bool have = false;
+#pragma unroll
+          for (int sl = 0; sl < NC; ++sl) {
+            const int f = slot_offset<FLO>(sl);
+            const int p = (int)p0 + f;
+            const bool valid = f >= a.f_lo && f <= a.f_hi && p >= 0 && p <= 126;
+            const bool need = valid && (!eligible || sl == wslot || D[sl] - M[sl] <= best_u);
+            if (need) {
+              const f32x2 dr = tbl[p];
+              uint32_t c0, c1;
+              const float sse = candidate_sse(x, dr.x, dr.y, c0, c1);
+              if (!have || sse < best) {
+                have = true;
+                best = sse;
+                best_p = (uint32_t)p;
+                bc0 = c0;
+                bc1 = c1;
+              }
+            }
+          }
+        }
+      }
+    }
+    *(uint2 *)(a.codes + (uint64_t)b * 8u) = make_uint2(bc0, bc1);
+    a.scales[b] = (uint8_t)best_p;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 128-point Hadamard pre-transform on MFMA (ScaleSearch summary page,
 // ScaleSearchAttention, 非干渉処理（IP）と絶対値低減: Hadamard incoherence
 // processing of Q and K). y = x H / sqrt(128) per contiguous 128-vector, H the
@@ -593,7 +803,13 @@ hipError_t launch_finalize(const uint32_t *partials, int n, float *gscale, hipSt
 
 hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.map.nblocks, kMaxQuantGroups);
-  if (bf16)
+  if (bf16 && a.f_lo == 0 && a.f_hi == 0)
+    hipLaunchKernelGGL((quantize_certified_kernel<0, 0>), dim3(g), dim3(kThreads), 0, s, a);
+  else if (bf16 && a.f_lo == -2 && a.f_hi == 6)
+    hipLaunchKernelGGL((quantize_certified_kernel<-2, 6>), dim3(g), dim3(kThreads), 0, s, a);
+  else if (bf16 && a.f_lo >= -8 && a.f_hi <= 8)
+    hipLaunchKernelGGL((quantize_certified_kernel<-8, 8>), dim3(g), dim3(kThreads), 0, s, a);
+  else if (bf16)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(quantize_kernel<false>, dim3(g), dim3(kThreads), 0, s, a);

@@ -1,0 +1,92 @@
+"""The certified bf16 search must give the contract's result on blocks where the
+certificate cannot decide: candidates whose SSEs tie exactly or differ by a few
+parts per million. Inputs are chosen on the CPU with the independent NumPy
+reference (no GPU output is used to build them); results are compared bit for
+bit with the oracle under the same tensor scale."""
+import numpy as np
+import pytest
+import torch
+
+import ref_numpy as R
+import workloads
+from gpu_util import first_mismatch, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _relative_gaps(blocks_f32, sg, lo, hi):
+    ax = np.abs(blocks_f32)
+    t = ((ax.max(1) / np.float32(6)).astype(np.float32) / np.float32(sg)).astype(np.float32)
+    p0 = R.e4m3_nearest(t)
+    sse = []
+    for f in range(lo, hi + 1):
+        p = p0 + f
+        s, _ = R.sse_patterns(ax, np.float32(sg), np.clip(p, 0, 126))
+        sse.append(np.where((p >= 0) & (p <= 126), s, np.inf))
+    sse = np.sort(np.stack(sse, 1).astype(np.float64), axis=1)
+    return (sse[:, 1] - sse[:, 0]) / np.maximum(sse[:, 0], 1e-300)
+
+
+def check_given(nv, orc, xh, sg, offsets):
+    print(f"[case] {xh.shape} offsets={offsets} S_g={sg!r}", flush=True)
+    g = torch.tensor([sg], dtype=torch.float32, device="cuda:0")
+    c, s, _ = nv.quantize(to_dev(xh), offsets, global_scale=g)
+    torch.cuda.synchronize()
+    rc, rs, _ = orc.quantize(xh, *offsets, gscale=float(sg))
+    gs, gc = to_host(s), to_host(c)
+    assert np.array_equal(gs, rs), "scales: " + first_mismatch(gs, rs)
+    assert np.array_equal(gc, rc), "codes: " + first_mismatch(gc, rc)
+
+
+@pytest.mark.parametrize("offsets", [(-2, 6), (-8, 8)])
+def test_mined_near_ties(gpu, orc, offsets):
+    """The 1024 closest-call blocks out of 2^18 weight-style blocks."""
+    xh = workloads.workload(4, (256, 16384))
+    xf = workloads.bf16_bits_to_f32(xh).reshape(-1, 16)
+    sg = np.float32(np.abs(xf).max() / np.float32(2688))
+    gaps = _relative_gaps(xf, sg, *offsets)
+    pick = np.argsort(gaps, kind="stable")[:1024]
+    print(f"[near-ties] gaps of the picked blocks: min {gaps[pick].min():.2e} "
+          f"max {gaps[pick].max():.2e}; exact ties {int((gaps[pick] == 0).sum())}")
+    sel = xh.reshape(-1, 16)[pick].reshape(64, 256)
+    check_given(gpu, orc, np.ascontiguousarray(sel), sg, offsets)
+
+
+def test_perturbed_exact_ties(gpu, orc):
+    """Grid-aligned blocks (several candidates reach SSE 0 or equal SSEs), each
+    nudged by 0..3 bf16 ulps in one element."""
+    rng = np.random.default_rng(11)
+    n = 4096
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    vals = R.e4m3_values()
+    p = rng.integers(24, 110, n)
+    codes = rng.integers(0, 8, (n, 16))
+    codes[:, 0] = 7  # amax on the grid maximum: the default pattern is p itself
+    sign = rng.integers(0, 2, (n, 16)) * 2 - 1
+    x = (sign * grid[codes] * vals[p][:, None]).astype(np.float32)
+    xh = workloads.to_bf16_bits(x)
+    bump = rng.integers(0, 4, n).astype(np.uint16)
+    idx = rng.integers(1, 16, n)
+    nz = (xh[np.arange(n), idx] & 0x7FFF) != 0
+    xh[np.arange(n)[nz], idx[nz]] += bump[nz]
+    for offsets in [(-2, 6), (-8, 8)]:
+        check_given(gpu, orc, xh.reshape(-1, 256), np.float32(1.0), offsets)
+
+
+@pytest.mark.parametrize("offsets", [(0, 0), (-1, 1), (-3, 2), (-8, 0), (0, 8), (-2, 6)])
+def test_offset_subranges(gpu, orc, offsets):
+    xh = workloads.workload(2, (96, 4096))
+    xf = workloads.bf16_bits_to_f32(xh)
+    sg = np.float32(np.abs(xf).max() / np.float32(2688))
+    check_given(gpu, orc, xh, sg, offsets)
+
+
+def test_magnitude_edges(gpu, orc):
+    """Blocks just inside and outside [2^-40, 2^60], where the certificate stops applying."""
+    base = workloads.bf16_bits_to_f32(workloads.workload(4, (8, 1024))) / np.float32(0.02)
+    for e in (-45, -40, -39, 59, 60, 61):
+        x = (base * np.float32(2.0 ** e)).astype(np.float32)
+        xh = workloads.to_bf16_bits(x)
+        xf = workloads.bf16_bits_to_f32(xh)
+        sg = np.float32(np.abs(xf).max() / np.float32(2688))
+        check_given(gpu, orc, xh, sg, (-2, 6))
