@@ -22,7 +22,7 @@ nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP
 
 int amax_groups(uint64_t nblocks, bool bf16) {
   const uint64_t chunks = nblocks * (bf16 ? 2u : 4u);
-  uint64_t g = (chunks + 4ull * kThreads - 1) / (4ull * kThreads);
+  uint64_t g = (chunks + 8ull * kThreads - 1) / (8ull * kThreads);
   if (g < 1) g = 1;
   if (g > (uint64_t)kMaxAmaxGroups) g = kMaxAmaxGroups;
   return (int)g;
@@ -40,9 +40,10 @@ RegionMap plain_map(int64_t rows, int64_t cols) {
   return m;
 }
 
-// Global amax + finalize into gscale. The workspace holds the partials.
-nvfp4_status run_global_scale(const void *x, bool bf16, bool hadamard, const RegionMap &m,
-                              float *gscale, void *ws, hipStream_t s) {
+// Global amax pass: one partial maximum per workgroup into the workspace.
+// Returns the number of partials (0 on a launch error).
+int run_amax(const void *x, bool bf16, bool hadamard, const RegionMap &m, void *ws,
+             hipStream_t s) {
   AmaxArgs a{x, (uint32_t *)ws, m};
   int groups;
   hipError_t e;
@@ -53,13 +54,38 @@ nvfp4_status run_global_scale(const void *x, bool bf16, bool hadamard, const Reg
     groups = amax_groups(m.nblocks, bf16);
     e = launch_amax(a, bf16, groups, s);
   }
-  if (e != hipSuccess) return NVFP4_EHIP;
+  return e == hipSuccess ? groups : 0;
+}
+
+// Global amax + finalize into gscale (the tensor scale alone).
+nvfp4_status run_global_scale(const void *x, bool bf16, bool hadamard, const RegionMap &m,
+                              float *gscale, void *ws, hipStream_t s) {
+  const int groups = run_amax(x, bf16, hadamard, m, ws, s);
+  if (groups == 0) return NVFP4_EHIP;
   return hip_status(launch_finalize((const uint32_t *)ws, groups, gscale, s));
 }
 
 hipError_t run_quantize(const QuantArgs &q, bool bf16, bool hadamard, hipStream_t s) {
   return hadamard ? launch_quantize_hadamard(q, s) : launch_quantize(q, bf16, s);
 }
+
+// Quantize a region: the amax pass (unless the tensor scale is given), then the
+// search kernel, which reduces the partials to S_g in its prologue. An empty
+// region still gets its tensor scale.
+nvfp4_status run_quantize_region(const void *x, bool bf16, bool had, bool given,
+                                 const RegionMap &m, int f_lo, int f_hi, uint8_t *codes,
+                                 uint8_t *scales, float *gscale, void *ws, hipStream_t s) {
+  if (m.nblocks == 0)
+    return given ? NVFP4_OK : run_global_scale(x, bf16, had, m, gscale, ws, s);
+  int np = 0;
+  if (!given) {
+    np = run_amax(x, bf16, had, m, ws, s);
+    if (np == 0) return NVFP4_EHIP;
+  }
+  QuantArgs q{x, codes, scales, gscale, (const uint32_t *)ws, np, m, f_lo, f_hi};
+  return hip_status(run_quantize(q, bf16, had, s));
+}
+
 
 nvfp4_status check_offsets(int block, int f_lo, int f_hi) {
   if (block != 16) return NVFP4_EINVAL;
@@ -134,14 +160,8 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = xdt == NVFP4_BF16;
   const bool had = flags & NVFP4_HADAMARD128;
-  const RegionMap m = plain_map(rows, cols);
-  if (!given) {
-    st = run_global_scale(x, bf16, had, m, global_scale, workspace, s);
-    if (st) return st;
-  }
-  if (m.nblocks == 0) return NVFP4_OK;
-  QuantArgs q{x, codes, scales, global_scale, m, f_lo, f_hi};
-  return hip_status(run_quantize(q, bf16, had, s));
+  return run_quantize_region(x, bf16, had, given, plain_map(rows, cols), f_lo, f_hi, codes,
+                             scales, global_scale, workspace, s);
 }
 
 nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
@@ -212,13 +232,8 @@ nvfp4_status nvfp4_quantize_kv_sink(const void *kv, nvfp4_dtype dt, int64_t B, i
   m.seg_tokens = (uint32_t)T;
   m.n_first = (uint32_t)n_first;
   m.cols = (uint32_t)D;
-  if (!given) {
-    st = run_global_scale(kv, bf16, had, m, global_scale, workspace, s);
-    if (st) return st;
-  }
-  if (m.nblocks == 0) return NVFP4_OK;
-  QuantArgs q{kv, codes, scales, global_scale, m, f_lo, f_hi};
-  return hip_status(run_quantize(q, bf16, had, s));
+  return run_quantize_region(kv, bf16, had, given, m, f_lo, f_hi, codes, scales, global_scale,
+                             workspace, s);
 }
 
 nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scales,

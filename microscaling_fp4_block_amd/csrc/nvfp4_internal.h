@@ -8,7 +8,7 @@
 namespace nvfp4 {
 
 constexpr int kThreads = 256;          // 4 wave64 per workgroup
-constexpr int kMaxAmaxGroups = 4096;   // partial maxima kept in the workspace
+constexpr int kMaxAmaxGroups = 1024;   // partial maxima kept in the workspace
 constexpr int kMaxQuantGroups = 8192;  // grid cap of the block-parallel kernels
 
 // Division by a runtime constant with one high multiply (Granlund and
@@ -46,7 +46,9 @@ struct QuantArgs {
   const void *x;
   uint8_t *codes;
   uint8_t *scales;
-  const float *gscale;
+  float *gscale;              // read when npartials == 0, else written by workgroup 0
+  const uint32_t *partials;   // per-workgroup maxima of the amax pass
+  int npartials;              // 0: the tensor scale is given
   RegionMap map;
   int f_lo, f_hi;
 };

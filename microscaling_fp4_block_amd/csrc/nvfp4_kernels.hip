@@ -156,7 +156,7 @@ __device__ __forceinline__ uint32_t chunk_absmax(uint4 c) {
 }
 
 // Lanes take consecutive 16-byte chunks (a block is 2 chunks in bf16, 4 in
-// FP32), four independent loads in flight per lane.
+// FP32), eight independent loads in flight per lane.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
   constexpr uint32_t CPB = BF16 ? 2 : 4;  // 16-byte chunks per block
@@ -164,10 +164,11 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
   const uint32_t nchunks = a.map.nblocks * CPB;
   const uint32_t stride = gridDim.x * kThreads;
   uint32_t m = 0;
-  for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += 4 * stride) {
-    uint4 v[4];
+  constexpr int UNROLL = 8;
+  for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += UNROLL * stride) {
+    uint4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       uint32_t c = c0 + u * stride;
       if (c < nchunks) {
         uint32_t b = c / CPB, sub = c % CPB;
@@ -178,30 +179,41 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) m = max(m, chunk_absmax<BF16>(v[u]));
+    for (int u = 0; u < UNROLL; ++u) m = max(m, chunk_absmax<BF16>(v[u]));
   }
   m = group_max_u32(m);
   if (threadIdx.x == 0) a.partials[blockIdx.x] = m;
 }
 
-// Tensor (decode) scale from the global amax A: S_g = fl(A / 2688), 2688 =
-// 6 * 448 (largest E2M1 times largest UE4M3), 1 if that is 0, NaN if the
-// region holds a NaN/Inf.
-__global__ __launch_bounds__(kThreads) void finalize_kernel(const uint32_t *partials, int n,
-                                                            float *gscale) {
+// Tensor (decode) scale from the global amax bit pattern A: S_g = fl(A / 2688),
+// 2688 = 6 * 448 (largest E2M1 times largest UE4M3), 1 if that is 0, NaN if
+// the region holds a NaN/Inf.
+__device__ __forceinline__ float tensor_scale_from_amax(uint32_t m) {
+  if (m >= 0x7F800000u) return __uint_as_float(0x7FC00000u);
+  const float sg = __uint_as_float(m) / 2688.0f;
+  return sg == 0.0f ? 1.0f : sg;
+}
+
+__device__ __forceinline__ uint32_t reduce_partials(const uint32_t *partials, int n) {
   uint32_t m = 0;
   for (int i = threadIdx.x; i < n; i += kThreads) m = max(m, partials[i]);
-  m = group_max_u32(m);
-  if (threadIdx.x == 0) {
-    float sg;
-    if (m >= 0x7F800000u) {
-      sg = __uint_as_float(0x7FC00000u);
-    } else {
-      sg = __uint_as_float(m) / 2688.0f;
-      if (sg == 0.0f) sg = 1.0f;
-    }
-    *gscale = sg;
-  }
+  return group_max_u32(m);
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const uint32_t *partials, int n,
+                                                            float *gscale) {
+  const uint32_t m = reduce_partials(partials, n);
+  if (threadIdx.x == 0) *gscale = tensor_scale_from_amax(m);
+}
+
+// The tensor scale for a quantize workgroup: given, or reduced here from the
+// amax pass's partials (every workgroup reduces the same values in the same
+// way; workgroup 0 also stores the result).
+__device__ __forceinline__ float resolve_tensor_scale(const QuantArgs &a) {
+  if (a.npartials == 0) return *a.gscale;
+  const float sg = tensor_scale_from_amax(reduce_partials(a.partials, a.npartials));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.gscale = sg;
+  return sg;
 }
 
 // ---------------------------------------------------------------------------
@@ -292,7 +304,7 @@ __device__ __forceinline__ void search_block(const float (&x)[16], float sg, boo
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   __shared__ f32x2 tbl[128];
-  const float sg = *a.gscale;
+  const float sg = resolve_tensor_scale(a);
   const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
   build_scale_table(tbl, sg);
 
@@ -346,8 +358,6 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 // Offsets with one candidate ([0, 0], max scaling) need no search at all.
 // ---------------------------------------------------------------------------
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ bf16x2 fp4_decode_pair_bf16(uint32_t w, int sel) {
   switch (sel & 3) {
     case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
@@ -357,24 +367,37 @@ __device__ __forceinline__ bf16x2 fp4_decode_pair_bf16(uint32_t w, int sel) {
   }
 }
 
+// a . b + 0 in one VOP3P instruction (a chain start without a zeroed
+// accumulator register).
+__device__ __forceinline__ float dot2_first(bf16x2 a, bf16x2 b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Codes of one candidate (encode scale r) and the exact sums S1 = sum x V,
-// S2 = sum V^2 (x and V carry the same sign, so S1 = sum |x| |V|).
+// S2 = sum V^2 (x and V carry the same sign, so S1 = sum |x| |V|). Each code
+// word starts from the bits of its first product, a value that dies there:
+// the four byte-selected converts overwrite all of it, and the convert can
+// write in place without a copy.
 __device__ __forceinline__ void candidate_stats(const float (&x)[16], const uint32_t (&w)[8],
-                                                float r, uint32_t &c0, uint32_t &c1, float &s1,
+                                                float r, uint32_t (&cw)[2], float &s1,
                                                 float &s2) {
-  uint32_t cw[2] = {0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    cw[j >> 2] = fp4_encode_pair(cw[j >> 2], x[2 * j] * r, x[2 * j + 1] * r, j);
-  float a = 0.0f, b = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const bf16x2 v = fp4_decode_pair_bf16(cw[j >> 2], j);
+    const float y0 = x[2 * j] * r, y1 = x[2 * j + 1] * r;
+    const uint32_t old = (j & 3) == 0 ? __float_as_uint(y0) : cw[j >> 2];
+    cw[j >> 2] = fp4_encode_pair(old, y0, y1, j);
+  }
+  bf16x2 v = fp4_decode_pair_bf16(cw[0], 0);
+  float a = dot2_first(__builtin_bit_cast(bf16x2, w[0]), v);
+  float b = dot2_first(v, v);
+#pragma unroll
+  for (int j = 1; j < 8; ++j) {
+    v = fp4_decode_pair_bf16(cw[j >> 2], j);
     a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), v, a, false);
     b = __builtin_amdgcn_fdot2_f32_bf16(v, v, b, false);
   }
-  c0 = cw[0];
-  c1 = cw[1];
   s1 = a;
   s2 = b;
 }
@@ -396,13 +419,35 @@ __device__ __forceinline__ constexpr int slot_offset(int s) {
   return s == 0 ? 0 : (FLO + s - 1 < 0 ? FLO + s - 1 : FLO + s);
 }
 
-template <int FLO, int FHI>
+struct CertEntry {  // per pattern: decode d, encode r = 1/d, d in FP64
+  float d, r;
+  double dd;
+};
+
+// Max of |x| bit patterns of 16 bf16 values packed in 8 words (packed 16-bit max).
+__device__ __forceinline__ uint32_t bf16_block_absmax_bits(const uint32_t (&w)[8]) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int k = 1; k < 8; ++k)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu));
+  return (uint32_t)max(m.x, m.y) << 16;
+}
+
+// RANGE_FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI].
+template <int FLO, int FHI, bool RANGE_FIXED>
 __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs a) {
   constexpr int NC = FHI - FLO + 1;  // visiting slots (offset 0 included)
   __shared__ f32x2 tbl[128];
-  const float sg = *a.gscale;
+  __shared__ CertEntry ctbl[128];
+  const float sg = resolve_tensor_scale(a);
   const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
   build_scale_table(tbl, sg);
+  if (threadIdx.x < 127) {
+    const f32x2 dr = tbl[threadIdx.x];
+    ctbl[threadIdx.x] = CertEntry{dr.x, dr.y, (double)dr.x};
+  }
+  __syncthreads();
 
   const uint32_t stride = gridDim.x * kThreads;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
@@ -416,10 +461,7 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
       x[2 * k] = __uint_as_float(w[k] << 16);
       x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
-    uint32_t am = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      am = max(am, max((w[k] << 16) & 0x7FFFFFFFu, w[k] & 0x7FFF0000u));
+    const uint32_t am = bf16_block_absmax_bits(w);
 
     uint32_t best_p = 0x7Fu, bc0 = 0u, bc1 = 0u;
     if (sg_ok && am < 0x7F800000u) {
@@ -429,11 +471,15 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
         best_p = p0;
         candidate_codes(x, tbl[p0].y, bc0, bc1);
       } else {
-        // certificate applies: normal candidate patterns, amax in [2^-40, 2^60]
-        const bool eligible = ((int)p0 + FLO >= 8) && am >= 0x2B800000u && am <= 0x5D800000u;
-        float a2 = 0.0f;
+        // certificate applies: every candidate pattern normal and inside 0..126,
+        // amax in [2^-40, 2^60]; other blocks take the exact path below
+        const bool eligible = ((int)p0 + FLO >= 8) && ((int)p0 + FHI <= 126) &&
+                              am >= 0x2B800000u && am <= 0x5D800000u;
+        // table base such that p0b + f stays in 0..126 (p0b == p0 when eligible)
+        const int p0b = min(max((int)p0, -FLO), 126 - FHI);
+        float a2 = dot2_first(__builtin_bit_cast(bf16x2, w[0]), __builtin_bit_cast(bf16x2, w[0]));
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+        for (int k = 1; k < 8; ++k)
           a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
                                                __builtin_bit_cast(bf16x2, w[k]), a2, false);
         const double a2ub = (double)a2 * (1.0 + 0x1p-18) + 0x1p-120;
@@ -442,18 +488,16 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
         double k0 = 0.0;
         float cst = 0.0f;  // block part of the margin
         float best_u = INFINITY;
-        int wslot = 0;
+        uint32_t cw[2] = {0u, 0u};
 #pragma unroll
         for (int sl = 0; sl < NC; ++sl) {
           const int f = slot_offset<FLO>(sl);
-          const int p = (int)p0 + f;
-          const bool valid = f >= a.f_lo && f <= a.f_hi && p >= 0 && p <= 126;
-          const f32x2 dr = tbl[p < 0 ? 0 : (p > 126 ? 126 : p)];
-          uint32_t c0, c1;
+          const int p = p0b + f;
+          const bool valid = RANGE_FIXED || (f >= a.f_lo && f <= a.f_hi);
+          const CertEntry ce = ctbl[p];
           float s1, s2;
-          candidate_stats(x, w, dr.y, c0, c1, s1, s2);
-          const double dd = (double)dr.x;
-          const double kf = dd * __builtin_fma(dd, (double)s2, -2.0 * (double)s1);
+          candidate_stats(x, w, ce.r, cw, s1, s2);
+          const double kf = ce.dd * __builtin_fma(ce.dd, (double)s2, -2.0 * (double)s1);
           if (sl == 0) {
             k0 = kf;
             const double e0ub = kf + a2ub + __builtin_fabs(kf) * 0x1p-50;
@@ -472,30 +516,27 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
           const float u = df + mf;
           if (sl == 0 || u < best_u) {
             best_u = u;
-            wslot = sl;
-            bc0 = c0;
-            bc1 = c1;
+            best_p = (uint32_t)p;
+            bc0 = cw[0];
+            bc1 = cw[1];
           }
         }
-        // Candidates that might tie or beat w (w itself always counts once).
+        // Candidates that might tie or beat the leader (which always counts once).
         int contenders = 0;
 #pragma unroll
         for (int sl = 0; sl < NC; ++sl) contenders += (D[sl] - M[sl] <= best_u) ? 1 : 0;
-        best_p = p0 + slot_offset<FLO>(0);
-#pragma unroll
-        for (int sl = 0; sl < NC; ++sl)
-          if (sl == wslot) best_p = (uint32_t)((int)p0 + slot_offset<FLO>(sl));
         if (!eligible || contenders > 1) {
           // Exact contract evaluation over the candidates that could win,
           // in visiting order.
+          const uint32_t lead = best_p;
           float best = INFINITY;
           bool have = false;
 #pragma unroll
           for (int sl = 0; sl < NC; ++sl) {
             const int f = slot_offset<FLO>(sl);
             const int p = (int)p0 + f;
-            const bool valid = f >= a.f_lo && f <= a.f_hi && p >= 0 && p <= 126;
-            const bool need = valid && (!eligible || sl == wslot || D[sl] - M[sl] <= best_u);
+            const bool valid = (RANGE_FIXED || (f >= a.f_lo && f <= a.f_hi)) && p >= 0 && p <= 126;
+            const bool need = valid && (!eligible || (uint32_t)p == lead || D[sl] - M[sl] <= best_u);
             if (need) {
               const f32x2 dr = tbl[p];
               uint32_t c0, c1;
@@ -601,7 +642,7 @@ __device__ __forceinline__ void hadamard_tile(const HadamardLane &h, const uint4
 // wave per 32 vectors; each lane codes four blocks of its vector.
 __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a) {
   __shared__ f32x2 tbl[128];
-  const float sg = *a.gscale;
+  const float sg = resolve_tensor_scale(a);
   const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
   build_scale_table(tbl, sg);
 
@@ -718,16 +759,59 @@ __device__ __forceinline__ void store_block(void *y, uint64_t off, const float (
   }
 }
 
+// One lane writes one contiguous 16-byte output chunk (8 bf16 = half a block,
+// or 4 FP32 = a quarter block), so every store instruction of a wave covers
+// 1 KiB without gaps; its 4 (2) code bytes and the block's scale byte are
+// read directly. Four chunks in flight per lane.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
+  constexpr uint32_t EPU = OUT_BF16 ? 8u : 4u;  // elements per chunk
+  constexpr uint32_t SHIFT = OUT_BF16 ? 1u : 2u;  // log2(chunks per block)
+  constexpr int UNROLL = 4;
   const float sg = *a.gscale;
+  const uint32_t nunits = a.nblocks << SHIFT;
   const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.nblocks; b += stride) {
-    const uint2 c = *(const uint2 *)(a.codes + (uint64_t)b * 8u);
-    const float d = block_decode_scale(a.scales[b], sg);
-    float o[16];
-    decode_block(c, d, o);
-    store_block<OUT_BF16>(a.y, (uint64_t)b * 16u, o);
+  for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < nunits; u0 += UNROLL * stride) {
+    uint32_t cw[UNROLL];
+    uint32_t sp[UNROLL];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+      const uint32_t u = u0 + k * stride;
+      cw[k] = 0u;
+      sp[k] = 0u;
+      if (u < nunits) {
+        const uint32_t b = u >> SHIFT, part = u & ((1u << SHIFT) - 1u);
+        if (OUT_BF16)
+          cw[k] = *(const uint32_t *)(a.codes + (uint64_t)b * 8u + part * 4u);
+        else
+          cw[k] = *(const uint16_t *)(a.codes + (uint64_t)b * 8u + part * 2u);
+        sp[k] = a.scales[b];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+      const uint32_t u = u0 + k * stride;
+      if (u < nunits) {
+        const float d = block_decode_scale(sp[k], sg);
+        float o[EPU];
+#pragma unroll
+        for (int j = 0; j < (int)EPU / 2; ++j) {
+          const f32x2 v = fp4_decode_pair(cw[k], j);
+          o[2 * j] = v.x * d;
+          o[2 * j + 1] = v.y * d;
+        }
+        if (OUT_BF16) {
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w[j] = __builtin_bit_cast(uint32_t,
+                                      __builtin_convertvector((f32x2{o[2 * j], o[2 * j + 1]}), bf16x2));
+          *(uint4 *)((uint16_t *)a.y + (uint64_t)u * EPU) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          *(float4 *)((float *)a.y + (uint64_t)u * EPU) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    }
   }
 }
 
@@ -804,11 +888,13 @@ hipError_t launch_finalize(const uint32_t *partials, int n, float *gscale, hipSt
 hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.map.nblocks, kMaxQuantGroups);
   if (bf16 && a.f_lo == 0 && a.f_hi == 0)
-    hipLaunchKernelGGL((quantize_certified_kernel<0, 0>), dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((quantize_certified_kernel<0, 0, true>), dim3(g), dim3(kThreads), 0, s, a);
   else if (bf16 && a.f_lo == -2 && a.f_hi == 6)
-    hipLaunchKernelGGL((quantize_certified_kernel<-2, 6>), dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((quantize_certified_kernel<-2, 6, true>), dim3(g), dim3(kThreads), 0, s, a);
+  else if (bf16 && a.f_lo == -8 && a.f_hi == 8)
+    hipLaunchKernelGGL((quantize_certified_kernel<-8, 8, true>), dim3(g), dim3(kThreads), 0, s, a);
   else if (bf16 && a.f_lo >= -8 && a.f_hi <= 8)
-    hipLaunchKernelGGL((quantize_certified_kernel<-8, 8>), dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((quantize_certified_kernel<-8, 8, false>), dim3(g), dim3(kThreads), 0, s, a);
   else if (bf16)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
   else
@@ -843,7 +929,7 @@ hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, hipStream
 }
 
 hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s) {
-  const int g = grid_for(a.nblocks, kMaxQuantGroups);
+  const int g = grid_for((uint64_t)a.nblocks * (out_bf16 ? 2u : 4u) / 4u, kMaxQuantGroups);
   if (out_bf16)
     hipLaunchKernelGGL(dequantize_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
   else
