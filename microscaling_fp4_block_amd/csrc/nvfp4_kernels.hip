@@ -471,12 +471,11 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
         best_p = p0;
         candidate_codes(x, tbl[p0].y, bc0, bc1);
       } else {
-        // certificate applies: every candidate pattern normal and inside 0..126,
-        // amax in [2^-40, 2^60]; other blocks take the exact path below
-        const bool eligible = ((int)p0 + FLO >= 8) && ((int)p0 + FHI <= 126) &&
-                              am >= 0x2B800000u && am <= 0x5D800000u;
-        // table base such that p0b + f stays in 0..126 (p0b == p0 when eligible)
-        const int p0b = min(max((int)p0, -FLO), 126 - FHI);
+        // certificate applies: every candidate pattern normal, amax in
+        // [2^-40, 2^60]; other blocks take the exact path below. Candidates
+        // above pattern 126 are skipped (scored +inf).
+        const bool eligible = ((int)p0 + FLO >= 8) && am >= 0x2B800000u && am <= 0x5D800000u;
+        const int p0b = max((int)p0, -FLO);  // keeps table indices >= 0
         float a2 = dot2_first(__builtin_bit_cast(bf16x2, w[0]), __builtin_bit_cast(bf16x2, w[0]));
 #pragma unroll
         for (int k = 1; k < 8; ++k)
@@ -493,8 +492,8 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
         for (int sl = 0; sl < NC; ++sl) {
           const int f = slot_offset<FLO>(sl);
           const int p = p0b + f;
-          const bool valid = RANGE_FIXED || (f >= a.f_lo && f <= a.f_hi);
-          const CertEntry ce = ctbl[p];
+          const bool valid = (RANGE_FIXED || (f >= a.f_lo && f <= a.f_hi)) && p <= 126;
+          const CertEntry ce = ctbl[min(p, 126)];
           float s1, s2;
           candidate_stats(x, w, ce.r, cw, s1, s2);
           const double kf = ce.dd * __builtin_fma(ce.dd, (double)s2, -2.0 * (double)s1);
