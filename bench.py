@@ -29,6 +29,41 @@ if ROOT not in sys.path:
 
 METRIC = "NVFP4 ScaleSearch quantize GB/s (in+out) and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
+# VALU issue rate for plain (unfused, unpacked) FP32 operations: 256 CUs x 4 SIMDs x
+# 16 lanes x 2.4 GHz. The scored arithmetic may not use FMA and packed FP32 is
+# not used, so this is the applicable peak (the published 157.3 TFLOP/s counts
+# packed FMAs).
+VALU_PEAK_TFLOPS = 256 * 64 * 2.4e9 / 1e12
+# Algorithmic FP32 operations of the search per element and candidate:
+# y = x * r, xhat = V * d, e = |x| - xhat, e * e, running sum.
+OPS_PER_ELEMENT_CANDIDATE = 5
+SEARCH_KERNEL = "quantize_certified_kernel<-2, 6, true>"
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "quantize_search_bf16_8192x28672.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "microscaling_fp4_block_amd", "csrc", f)
+                  for f in ("nvfp4_kernels.hip", "nvfp4_api.hip", "nvfp4_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if that
+    summary was taken on the current kernel sources (else None)."""
+    if not os.path.exists(PROFILE_SUMMARY):
+        return None
+    src_hash, traffic = None, None
+    for line in open(PROFILE_SUMMARY):
+        if line.startswith("source_hash:"):
+            src_hash = line.split(":", 1)[1].strip()
+        if line.startswith("traffic_bytes_per_launch") and kernel in line:
+            traffic = int(line.rsplit("|", 1)[1].strip())
+    return traffic if src_hash == kernel_source_hash() else None
 ROWS, COLS = 8192, 28672
 OFFSETS = (-2, 6)
 
@@ -132,13 +167,19 @@ def rocpd_summary(dbs):
             print("kernel | counter | dispatches | avg KiB per dispatch")
             for (name, cn), vs in sorted(agg.items()):
                 print(f"{name} | {cn} | {len(vs)} | {sum(vs) / len(vs):.1f}")
+            factors = {}
             for (name, cn), vs in agg.items():
                 if "copyBuffer" in name:
                     big = [v for v in vs if v >= 0.5 * max(vs)]  # the 1 GiB copies only
                     avg = sum(big) / len(big)
                     f = (COPY_BYTES / 1024.0) / avg
+                    factors[cn] = f
                     print(f"calibration: {cn} over {len(big)} copies of {COPY_BYTES} B reads "
                           f"{avg:.1f} KiB per copy -> scale factor {f:.4f}")
+            for (name, cn), vs in sorted(agg.items()):
+                if cn in factors and "copyBuffer" not in name:
+                    b = sum(vs) / len(vs) * 1024.0 * factors[cn]
+                    print(f"scaled {cn} | {name} | {b:.0f} B per dispatch")
 
 
 def main():
@@ -154,6 +195,7 @@ def main():
                     help="print a text summary of rocprofv3 databases of a --profile run")
     args = ap.parse_args()
     if args.rocpd_summary:
+        print(f"source_hash: {kernel_source_hash()}")
         rocpd_summary(args.rocpd_summary)
         return
     if args.gpus != 1:
@@ -237,6 +279,9 @@ def main():
     ms_deq = event_time_ms(torch, dequant_only, iters, stream)
     qbytes = quantize_bytes(n, 2)
     search_gbs = search_pass_bytes(n, 2) / (ms_search * 1e-3) / 1e9
+    ncand = OFFSETS[1] - OFFSETS[0] + 1
+    alg_flops = OPS_PER_ELEMENT_CANDIDATE * ncand * n
+    alg_tflops = alg_flops / (ms_search * 1e-3) / 1e12
     quant_call_ms = ms_amax + ms_search
     out = {
         "metric": METRIC,
@@ -259,14 +304,17 @@ def main():
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {
-            "bound": "hbm",
-            "achieved": round(search_gbs, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(search_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "quantize_kernel<true> (search pass, tensor scale given)",
+            "bound": "alu",
+            "achieved": round(alg_tflops, 2),
+            "peak": round(VALU_PEAK_TFLOPS, 2),
+            "unit": "TFLOP/s",
+            "frac": round(alg_tflops / VALU_PEAK_TFLOPS, 4),
+            "traffic": committed_traffic(SEARCH_KERNEL),
+            "kernel": SEARCH_KERNEL,
             "kernel_ms": round(ms_search, 4),
+            "flops_per_launch": alg_flops,
+            "hbm_gbs": round(search_gbs, 2),
+            "hbm_frac": round(search_gbs / HBM_PEAK_GBS, 4),
             "bytes_per_launch": search_pass_bytes(n, 2),
         },
         "breakdown": {

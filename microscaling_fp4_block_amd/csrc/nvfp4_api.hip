@@ -22,7 +22,7 @@ nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP
 
 int amax_groups(uint64_t nblocks, bool bf16) {
   const uint64_t chunks = nblocks * (bf16 ? 2u : 4u);
-  uint64_t g = (chunks + 8ull * kThreads - 1) / (8ull * kThreads);
+  uint64_t g = (chunks + 4ull * kThreads - 1) / (4ull * kThreads);
   if (g < 1) g = 1;
   if (g > (uint64_t)kMaxAmaxGroups) g = kMaxAmaxGroups;
   return (int)g;

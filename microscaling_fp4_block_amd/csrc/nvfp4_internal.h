@@ -8,7 +8,8 @@
 namespace nvfp4 {
 
 constexpr int kThreads = 256;          // 4 wave64 per workgroup
-constexpr int kMaxAmaxGroups = 1024;   // partial maxima kept in the workspace
+constexpr int kMaxAmaxGroups = 512;    // partial maxima kept in the workspace
+constexpr int kMaxStreamGroups = 1024; // grid cap of the streaming dequantize
 constexpr int kMaxQuantGroups = 8192;  // grid cap of the block-parallel kernels
 
 // Division by a runtime constant with one high multiply (Granlund and

@@ -45,7 +45,7 @@ def test_version_and_status_text(lib):
     texts = {lib.nvfp4_status_str(s).decode() for s in range(6)}
     assert len(texts) == 6
     assert lib.nvfp4_status_str(99).decode() == "unknown status"
-    assert lib.nvfp4_workspace_bytes(8192, 28672, 0) >= 4 * 1024
+    assert lib.nvfp4_workspace_bytes(8192, 28672, 0) >= 4 * 256
 
 
 P = 0x10000  # a well-aligned fake device address: every call below fails its checks first
