@@ -12,6 +12,7 @@ kernel alone, timed with HIP events on its stream over its own launches), a
 per-pass breakdown, and the CPU oracle timed on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--profile]
+       python bench.py --rocpd-summary DB [DB ...]
 """
 from __future__ import annotations
 
@@ -169,7 +170,7 @@ def rocpd_summary(dbs):
                 print(f"{name} | {cn} | {len(vs)} | {sum(vs) / len(vs):.1f}")
             factors = {}
             for (name, cn), vs in agg.items():
-                if "copyBuffer" in name:
+                if "copyBuffer" in name and cn in ("FETCH_SIZE", "WRITE_SIZE") and max(vs) > 0:
                     big = [v for v in vs if v >= 0.5 * max(vs)]  # the 1 GiB copies only
                     avg = sum(big) / len(big)
                     f = (COPY_BYTES / 1024.0) / avg
@@ -185,8 +186,10 @@ def rocpd_summary(dbs):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # ~0.1 s of warm-up: kernel durations settle after a power-management transient
+    # of ~20 ms at the start of a run
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: a few launches of each kernel plus a "
