@@ -183,6 +183,79 @@ def rocpd_summary(dbs):
                     print(f"scaled {cn} | {name} | {b:.0f} B per dispatch")
 
 
+def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
+    """Markdown table of every workload: passes timed with HIP events, oracle beside."""
+    import oracle
+
+    oracle.build(force=False)
+    threads = min(16, os.cpu_count() or 1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    print("| # | workload | quantize call GB/s | search pass us (GB/s) | amax pass us | "
+          "max-scaling control us | SS / control | dequantize us (GB/s) | oracle quantize s "
+          f"({threads} threads) |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for idx in (1, 2, 3, 4, 5):
+        w = workloads.WORKLOADS[idx]
+        xh = workloads.workload(idx)
+        if xh.dtype == np.uint16:
+            x = torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16).to(dev)
+            esz = 2
+        else:
+            x = torch.from_numpy(xh).to(dev)
+            esz = 4
+        offs, had, sink = w["offsets"], w["hadamard"], w["sink"]
+        n_all = x.numel()
+        if sink:
+            nf, nl = sink
+            B, H, T, D = x.shape
+            n = B * H * (T - nf - nl) * D
+            ns = B * H * (nf + nl) * D
+            call = lambda: nv.quantize_kv_sink(x, nf, nl, offs, hadamard=had)
+            c, s, g, snk = call()
+            gfix = g.clone()
+            search = lambda: nv.quantize_kv_sink(x, nf, nl, offs, hadamard=had, global_scale=gfix)
+            control = lambda: nv.quantize_kv_sink(x, nf, nl, (0, 0), hadamard=had,
+                                                   global_scale=gfix)
+            mid = x[:, :, nf:T - nl].contiguous()
+            amax = lambda: nv.global_scale(mid, hadamard=had)
+            out_dt = x.dtype
+            deq = lambda: nv.dequantize_kv_sink(c, s, g, snk, T, nf, nl, out_dt)
+            qbytes = n * esz + n // 2 + n // 16 + 4 + 2 * ns * esz
+            dbytes = n // 2 + n // 16 + 4 + ns * esz + n_all * esz
+        else:
+            n = n_all
+            call = lambda: nv.quantize(x, offs, hadamard=had)
+            c, s, g = call()
+            gfix = g.clone()
+            search = lambda: nv.quantize(x, offs, hadamard=had, global_scale=gfix)
+            control = lambda: nv.quantize(x, (0, 0), hadamard=had, global_scale=gfix)
+            amax = lambda: nv.global_scale(x, hadamard=had)
+            out_dt = torch.float32 if esz == 4 or had else torch.bfloat16
+            deq = lambda: nv.dequantize(c, s, g, out_dt)
+            qbytes = quantize_bytes(n, esz)
+            dbytes = n // 2 + n // 16 + 4 + n * (4 if out_dt == torch.float32 else 2)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
+            call()
+        torch.cuda.synchronize()
+        ms = {k: event_time_ms(torch, f, iters, stream)
+              for k, f in (("call", call), ("search", search), ("amax", amax),
+                           ("control", control), ("deq", deq))}
+        t1 = time.perf_counter()
+        if sink:
+            oracle.quantize_kv_sink(xh, nf, nl, *offs, hadamard=had, nthreads=threads)
+        else:
+            oracle.quantize(xh, *offs, hadamard=had, nthreads=threads)
+        t_or = time.perf_counter() - t1
+        gbs = lambda b, m: b / (m * 1e-3) / 1e9
+        print(f"| {idx} | {w['name']} | {gbs(qbytes, ms['call']):.0f} | "
+              f"{ms['search'] * 1e3:.1f} ({gbs(qbytes, ms['search']):.0f}) | "
+              f"{ms['amax'] * 1e3:.1f} | {ms['control'] * 1e3:.1f} | "
+              f"{ms['search'] / ms['control']:.2f} | {ms['deq'] * 1e3:.1f} "
+              f"({gbs(dbytes, ms['deq']):.0f}) | {t_or:.2f} |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +267,8 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: a few launches of each kernel plus a "
                          "plain 1 GiB device copy for counter calibration; no JSON")
+    ap.add_argument("--workloads", action="store_true",
+                    help="print a markdown table timing all five workloads (no JSON line)")
     ap.add_argument("--rocpd-summary", nargs="+", metavar="DB",
                     help="print a text summary of rocprofv3 databases of a --profile run")
     args = ap.parse_args()
@@ -212,6 +287,9 @@ def main():
     import workloads
 
     nv.load()
+    if args.workloads:
+        workloads_table(torch, nv, workloads)
+        return
     dev = torch.device("cuda:0")
     print(f"[bench] generating workload 4 ({ROWS}x{COLS} bf16)", file=sys.stderr, flush=True)
     xh = workloads.workload(4)
