@@ -256,6 +256,31 @@ def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
               f"({gbs(dbytes, ms['deq']):.0f}) | {t_or:.2f} |", flush=True)
 
 
+def kv_append_table(torch, nv, workloads, iters: int = 200):
+    """Markdown table: KV append (K cache [1, 8, *, 128] bf16, sinks 128 + 128) per call."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    B, H, D, nf, nl = 1, 8, 128, 128, 128
+    print("| tokens appended per call | us per call | tokens/s (per head) | coded GB/s |")
+    print("|---|---|---|---|")
+    xh = workloads.workload(3, (B, H, 32768, D))
+    x = torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16).to(dev)
+    g = nv.global_scale(x[:, :, nf:32768 - nl].contiguous())
+    for t_new in (1, 16, 256, 4096):
+        cap_tokens = 32768 + (iters + 4) * t_new + 8
+        cache = nv.kv_cache_alloc(B, H, D, cap_tokens, nf, nl, torch.bfloat16, dev)
+        nv.kv_append(cache, x, g)  # prefill 32768 tokens
+        chunk = x[:, :, :t_new].contiguous()
+        for _ in range(3):
+            nv.kv_append(cache, chunk, g)
+        torch.cuda.synchronize()
+        ms = event_time_ms(torch, lambda: nv.kv_append(cache, chunk, g), iters, stream)
+        coded = B * H * t_new * D  # elements leaving the window per call (steady state)
+        nbytes = coded * 2 + coded // 2 + coded // 16 + B * H * t_new * D * 2
+        print(f"| {t_new} | {ms * 1e3:.1f} | {t_new / (ms * 1e-3):.0f} | "
+              f"{nbytes / (ms * 1e-3) / 1e9:.1f} |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,6 +292,8 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: a few launches of each kernel plus a "
                          "plain 1 GiB device copy for counter calibration; no JSON")
+    ap.add_argument("--kv-append", action="store_true",
+                    help="print a markdown table timing KV-cache appends (no JSON line)")
     ap.add_argument("--workloads", action="store_true",
                     help="print a markdown table timing all five workloads (no JSON line)")
     ap.add_argument("--rocpd-summary", nargs="+", metavar="DB",
@@ -289,6 +316,9 @@ def main():
     nv.load()
     if args.workloads:
         workloads_table(torch, nv, workloads)
+        return
+    if args.kv_append:
+        kv_append_table(torch, nv, workloads)
         return
     dev = torch.device("cuda:0")
     print(f"[bench] generating workload 4 ({ROWS}x{COLS} bf16)", file=sys.stderr, flush=True)

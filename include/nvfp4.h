@@ -142,6 +142,28 @@ NVFP4_API nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint
                                       int64_t D, int64_t n_first, int64_t n_last, int block,
                                       void *y, nvfp4_dtype ydt, void *stream);
 
+/* KV-cache append with attention sinks (decode-time streaming of the sink mode).
+ * The cache, per (b, h): head[B][H][n_first][D] (dt) holds the first n_first
+ * tokens verbatim; tail[B][H][n_last][D] (dt) is a ring of the n_last most recent
+ * tokens, token t at slot t mod n_last; codes[B][H][cap][D/2] and
+ * scales[B][H][cap][D/16] hold middle token t (n_first <= t < T - n_last) at row
+ * t - n_first. T is the number of tokens already in the cache. The call appends
+ * kv_new[B][H][t_new][D] as tokens T .. T + t_new - 1: tokens that leave the recent
+ * window are coded with the tensor scale *global_scale (a device float the caller
+ * holds fixed: the pages do not say how the tensor scale evolves as tokens arrive;
+ * one taken from the prefill's middle tokens with nvfp4_global_scale fits, larger
+ * values saturate), and the new tokens that stay in full precision go to the head
+ * or the ring. After the call the cache holds exactly what nvfp4_quantize_kv_sink
+ * with NVFP4_GSCALE_GIVEN and the same scale gives for tokens 0 .. T + t_new - 1
+ * (ring order aside). Requires the middle rows to fit: max(n_first, T + t_new -
+ * n_last) - n_first <= cap. flags: NVFP4_HADAMARD128 allowed (bf16, D % 128 == 0);
+ * the scale is always read. Calls on one cache must not overlap in time. */
+NVFP4_API nvfp4_status nvfp4_kv_append(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H,
+                                       int64_t T, int64_t t_new, int64_t D, int64_t n_first,
+                                       int64_t n_last, int64_t cap, int block, int f_lo, int f_hi,
+                                       uint32_t flags, const float *global_scale, void *head,
+                                       void *tail, uint8_t *codes, uint8_t *scales, void *stream);
+
 /* The FP32 Hadamard pre-transform alone: y[rows][128] = x[rows][128] H/sqrt(128)
  * (x bf16), as the quantizer computes it on the fly. For inspection and split
  * parity checks; the quantize path never writes it to memory. */

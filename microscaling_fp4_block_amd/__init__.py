@@ -10,6 +10,8 @@ from .nvfp4 import (  # noqa: F401
     dequantize_kv_sink,
     global_scale,
     hadamard128,
+    kv_append,
+    kv_cache_alloc,
     load,
     quantize,
     quantize_kv_sink,

@@ -272,6 +272,84 @@ nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scale
       launch_dequantize_kv(a, sink_dt == NVFP4_BF16, ydt == NVFP4_BF16, (hipStream_t)stream));
 }
 
+nvfp4_status nvfp4_kv_append(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H,
+                             int64_t T, int64_t t_new, int64_t D, int64_t n_first,
+                             int64_t n_last, int64_t cap, int block, int f_lo, int f_hi,
+                             uint32_t flags, const float *global_scale, void *head, void *tail,
+                             uint8_t *codes, uint8_t *scales, void *stream) {
+  if (!global_scale || !dtype_ok(dt)) return NVFP4_EINVAL;
+  nvfp4_status st = check_offsets(block, f_lo, f_hi);
+  if (st) return st;
+  if (flags & ~(NVFP4_HADAMARD128 | NVFP4_GSCALE_GIVEN)) return NVFP4_EINVAL;
+  if (B < 0 || H < 0 || T < 0 || t_new < 0 || D <= 0 || D % 16 || n_first < 0 || n_last < 0 ||
+      cap < 0)
+    return NVFP4_ESHAPE;
+  if (T + t_new > (1ll << 31) || B * H > (1ll << 31) || cap > (1ll << 31)) return NVFP4_ESHAPE;
+  const bool had = flags & NVFP4_HADAMARD128;
+  if (had && (dt != NVFP4_BF16)) return NVFP4_EINVAL;
+  if (had && D % 128) return NVFP4_ESHAPE;
+  const int64_t BH = B * H, T2 = T + t_new;
+  // tokens entering the middle: [lo, hi); the middle must hold rows up to hi - n_first
+  const int64_t lo = n_first > T - n_last ? n_first : T - n_last;
+  const int64_t hi = n_first > T2 - n_last ? n_first : T2 - n_last;
+  const int64_t npos = hi > lo ? hi - lo : 0;
+  if (hi - n_first > cap) return NVFP4_ESHAPE;
+  st = check_shape(BH * (npos > 0 ? npos : 0), D, 0, dt);
+  if (st) return st;
+  st = check_shape(BH * (cap > 0 ? cap : 0), D, 0, dt);
+  if (st) return st;
+  if (BH * t_new > 0 && !kv_new) return NVFP4_EINVAL;
+  if (BH * n_first > 0 && !head) return NVFP4_EINVAL;
+  if (BH * n_last > 0 && !tail) return NVFP4_EINVAL;
+  if (BH * cap > 0 && (!codes || !scales)) return NVFP4_EINVAL;
+  if (!aligned(kv_new, 16) || !aligned(head, 16) || !aligned(tail, 16) || !aligned(codes, 8))
+    return NVFP4_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dt == NVFP4_BF16;
+  const uint32_t es = bf16 ? 2u : 4u;
+
+  // 1. code the tokens that leave the recent window (before the ring is overwritten)
+  if (BH > 0 && npos > 0) {
+    RegionMap m{};
+    m.bpr = (uint32_t)(D / 16);
+    m.nblocks = (uint32_t)(BH * npos) * m.bpr;
+    m.div_bpr = make_fastdiv(m.bpr);
+    m.segments = (uint32_t)BH;
+    m.tm = (uint32_t)npos;
+    m.div_tm = make_fastdiv(m.tm);
+    m.cols = (uint32_t)D;
+    m.n_first = (uint32_t)n_first;
+    m.append = 1;
+    m.lo = (uint32_t)lo;
+    m.t_old = (uint32_t)T;
+    m.n_last = (uint32_t)n_last;
+    m.t_new = (uint32_t)t_new;
+    m.cap = (uint32_t)cap;
+    m.div_nlast = make_fastdiv((uint32_t)(n_last > 0 ? n_last : 1));
+    m.ring = tail;
+    QuantArgs q{kv_new, codes, scales, (float *)global_scale, nullptr, 0, m, f_lo, f_hi};
+    if (run_quantize(q, bf16, had, s) != hipSuccess) return NVFP4_EHIP;
+  }
+  // 2. store the new tokens that stay in full precision
+  if (BH > 0 && t_new > 0) {
+    AdmitArgs c{};
+    c.src = kv_new;
+    c.head = head;
+    c.tail = tail;
+    c.t_old = (uint32_t)T;
+    c.t_new = (uint32_t)t_new;
+    c.n_first = (uint32_t)n_first;
+    c.n_last = (uint32_t)n_last;
+    c.chunks_per_row = (uint32_t)(D * es / 16);
+    c.nchunks = (uint32_t)(BH * t_new) * c.chunks_per_row;
+    c.div_cpr = make_fastdiv(c.chunks_per_row);
+    c.div_tnew = make_fastdiv((uint32_t)t_new);
+    c.div_nlast = make_fastdiv((uint32_t)(n_last > 0 ? n_last : 1));
+    if (launch_admit(c, bf16, s) != hipSuccess) return NVFP4_EHIP;
+  }
+  return NVFP4_OK;
+}
+
 nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,
                                void *stream) {
   if (xdt != NVFP4_BF16) return NVFP4_EINVAL;

@@ -27,10 +27,16 @@ inline FastDiv make_fastdiv(uint32_t d) {
   return FastDiv{d, (uint32_t)m, s};
 }
 
-// Where block b of the quantized region lives in the input. Plain tensors are
-// one contiguous region (segments == 0). The attention-sink mode quantizes the
-// middle tokens of every (batch, head) segment: row r of the region is token
-// n_first + (r mod tm) of segment r / tm, and a segment spans seg_tokens rows.
+// Where block b of the quantized region lives in the input, and where its
+// codes go. Plain tensors are one contiguous region (segments == 0, output
+// block b). The attention-sink mode quantizes the middle tokens of every
+// (batch, head) segment: row r of the region is token n_first + (r mod tm) of
+// segment r / tm, a segment spans seg_tokens input rows; output block b.
+// Append mode (append != 0) quantizes the tokens that leave the recent window
+// of a KV cache: row r of the region is token pos = lo + (r mod tm) of segment
+// g = r / tm; a token below t_old comes from the ring [segments][n_last][cols]
+// (slot pos mod n_last), a later one from x [segments][t_new][cols] (row
+// pos - t_old); its codes go to row g * cap + pos - n_first of the cache.
 struct RegionMap {
   uint32_t nblocks;     // 16-element blocks in the region
   uint32_t bpr;         // blocks per row (cols / 16)
@@ -41,6 +47,10 @@ struct RegionMap {
   uint32_t seg_tokens;  // input rows per segment (T)
   uint32_t n_first;     // first region row inside a segment
   uint32_t cols;        // elements per row
+  uint32_t append;      // append mode
+  uint32_t lo, t_old, n_last, t_new, cap;
+  FastDiv div_nlast;
+  const void *ring;
 };
 
 struct QuantArgs {
@@ -66,6 +76,17 @@ struct DequantArgs {
   const float *gscale;
   void *y;
   uint32_t nblocks;
+};
+
+// Append: copy new tokens kv_new[BH][t_new][D] at positions t_old.. into the
+// cache head [BH][n_first][D] (positions < n_first) or tail ring
+// [BH][n_last][D] (positions >= t_old + t_new - n_last, slot pos mod n_last).
+struct AdmitArgs {
+  const void *src;
+  void *head, *tail;
+  uint32_t t_old, t_new, n_first, n_last;
+  uint32_t chunks_per_row, nchunks;
+  FastDiv div_cpr, div_tnew, div_nlast;
 };
 
 // Sink copy / reassembly: BH segments of T tokens of D elements; tokens
@@ -103,6 +124,7 @@ hipError_t launch_quantize_hadamard(const QuantArgs &a, hipStream_t s);
 hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s);
 hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_admit(const AdmitArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_dequantize_kv(const DequantKvArgs &a, bool sink_bf16, bool out_bf16,
                                 hipStream_t s);
 

@@ -101,6 +101,33 @@ __device__ __forceinline__ uint64_t block_offset(const RegionMap &m, uint32_t b)
   return row * m.cols + (uint64_t)j * 16u;
 }
 
+// Source address and destination block of block b of a quantize region.
+struct BlockIO {
+  const char *src;
+  uint64_t dst;
+};
+
+__device__ __forceinline__ BlockIO block_io(const void *x, const RegionMap &m, uint32_t b,
+                                            uint32_t esize) {
+  if (!m.append) return BlockIO{(const char *)x + block_offset(m, b) * esize, b};
+  const uint32_t r = fastdiv(b, m.div_bpr);
+  const uint32_t j = b - r * m.bpr;
+  const uint32_t g = fastdiv(r, m.div_tm);
+  const uint32_t pos = m.lo + (r - g * m.tm);
+  uint64_t row;
+  const char *base;
+  if (pos < m.t_old) {
+    const uint32_t q = fastdiv(pos, m.div_nlast);
+    row = (uint64_t)g * m.n_last + (pos - q * m.n_last);
+    base = (const char *)m.ring;
+  } else {
+    row = (uint64_t)g * m.t_new + (pos - m.t_old);
+    base = (const char *)x;
+  }
+  const uint64_t dst = ((uint64_t)g * m.cap + (pos - m.n_first)) * m.bpr + j;
+  return BlockIO{base + (row * m.cols + (uint64_t)j * 16u) * esize, dst};
+}
+
 // Wave64 max with DPP: xor-1 and xor-2 quad permutes, half-row and row
 // mirrors give every lane its row-of-16 maximum; row broadcasts 15 and 31
 // then fold the four rows into lane 63.
@@ -128,9 +155,9 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
 
 // Load one 16-element block as FP32 (bf16 widening is exact: a 16-bit shift).
 template <bool BF16>
-__device__ __forceinline__ void load_block(const void *x, uint64_t off, float (&v)[16]) {
+__device__ __forceinline__ void load_block_at(const void *src, float (&v)[16]) {
   if (BF16) {
-    const uint4 *p = (const uint4 *)((const uint16_t *)x + off);
+    const uint4 *p = (const uint4 *)src;
     uint4 a = p[0], b = p[1];
     uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -139,7 +166,7 @@ __device__ __forceinline__ void load_block(const void *x, uint64_t off, float (&
       v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
   } else {
-    const float4 *p = (const float4 *)((const float *)x + off);
+    const float4 *p = (const float4 *)src;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float4 a = p[k];
@@ -149,6 +176,11 @@ __device__ __forceinline__ void load_block(const void *x, uint64_t off, float (&
       v[4 * k + 3] = a.w;
     }
   }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load_block(const void *x, uint64_t off, float (&v)[16]) {
+  load_block_at<BF16>((const char *)x + off * (BF16 ? 2u : 4u), v);
 }
 
 // ---------------------------------------------------------------------------
@@ -325,11 +357,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   const uint32_t stride = gridDim.x * kThreads;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
     float x[16];
-    load_block<BF16>(a.x, block_offset(a.map, b), x);
+    const BlockIO io = block_io(a.x, a.map, b, BF16 ? 2u : 4u);
+    load_block_at<BF16>(io.src, x);
     uint32_t best_p, bc0, bc1;
     search_block(x, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
-    *(uint2 *)(a.codes + (uint64_t)b * 8u) = make_uint2(bc0, bc1);
-    a.scales[b] = (uint8_t)best_p;
+    *(uint2 *)(a.codes + io.dst * 8u) = make_uint2(bc0, bc1);
+    a.scales[io.dst] = (uint8_t)best_p;
   }
 }
 
@@ -465,9 +498,8 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
 
   const uint32_t stride = gridDim.x * kThreads;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
-    const uint64_t off = block_offset(a.map, b);
-    const uint16_t *src = (const uint16_t *)a.x + off;
-    const uint4 q0 = load_stream(src), q1 = load_stream(src + 8);
+    const BlockIO io = block_io(a.x, a.map, b, 2u);
+    const uint4 q0 = load_stream(io.src), q1 = load_stream(io.src + 16);
     const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     float x[16];
 #pragma unroll
@@ -566,8 +598,8 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
         }
       }
     }
-    *(uint2 *)(a.codes + (uint64_t)b * 8u) = make_uint2(bc0, bc1);
-    a.scales[b] = (uint8_t)best_p;
+    *(uint2 *)(a.codes + io.dst * 8u) = make_uint2(bc0, bc1);
+    a.scales[io.dst] = (uint8_t)best_p;
   }
 }
 
@@ -668,7 +700,8 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
     const uint32_t vec = tile * 32u + (lane & 31u);
     const bool valid = vec < nvec;
     uint4 b[8];
-    hadamard_load((const uint16_t *)a.x, valid ? block_offset(a.map, vec * 8u) : 0, valid, h.g, b);
+    const BlockIO io = block_io(a.x, a.map, valid ? vec * 8u : 0u, 2u);
+    hadamard_load((const uint16_t *)io.src, 0, valid, h.g, b);
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
@@ -676,8 +709,8 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
       if (valid) {
         uint32_t best_p, bc0, bc1;
         search_block(y, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
-        const uint32_t blk = vec * 8u + 2u * t + h.g;
-        *(uint2 *)(a.codes + (uint64_t)blk * 8u) = make_uint2(bc0, bc1);
+        const uint64_t blk = io.dst + 2u * t + h.g;
+        *(uint2 *)(a.codes + blk * 8u) = make_uint2(bc0, bc1);
         a.scales[blk] = (uint8_t)best_p;
       }
     }
@@ -849,6 +882,30 @@ __global__ __launch_bounds__(kThreads) void sink_copy_kernel(SinkArgs a, uint32_
   }
 }
 
+// New tokens of a KV append into the cache head or tail ring, 16 bytes a lane
+// (tokens bound for the middle are coded by the quantize kernel instead).
+__global__ __launch_bounds__(kThreads) void admit_kernel(AdmitArgs a, uint32_t row_bytes) {
+  const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t tail_from = a.t_old + a.t_new - min(a.n_last, a.t_old + a.t_new);
+  for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < a.nchunks; c += stride) {
+    const uint32_t row = fastdiv(c, a.div_cpr);  // g * t_new + k
+    const uint32_t k = c - row * a.chunks_per_row;
+    const uint32_t g = fastdiv(row, a.div_tnew);
+    const uint32_t pos = a.t_old + (row - g * a.t_new);
+    char *dst;
+    if (pos < a.n_first) {
+      dst = (char *)a.head + ((uint64_t)g * a.n_first + pos) * row_bytes;
+    } else if (pos >= tail_from) {
+      const uint32_t q = fastdiv(pos, a.div_nlast);
+      dst = (char *)a.tail + ((uint64_t)g * a.n_last + (pos - q * a.n_last)) * row_bytes;
+    } else {
+      continue;
+    }
+    *(uint4 *)(dst + (uint64_t)k * 16u) =
+        *(const uint4 *)((const char *)a.src + (uint64_t)row * row_bytes + (uint64_t)k * 16u);
+  }
+}
+
 // y[BH][T][D] from the sink tokens and the dequantized middle, one 16-element
 // block a lane.
 template <bool SINK_BF16, bool OUT_BF16>
@@ -954,6 +1011,12 @@ hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s)
 hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.nchunks, kMaxQuantGroups);
   hipLaunchKernelGGL(sink_copy_kernel, dim3(g), dim3(kThreads), 0, s, a, bf16 ? 2u : 4u);
+  return hipGetLastError();
+}
+
+hipError_t launch_admit(const AdmitArgs &a, bool bf16, hipStream_t s) {
+  const int g = grid_for(a.nchunks, kMaxQuantGroups);
+  hipLaunchKernelGGL(admit_kernel, dim3(g), dim3(kThreads), 0, s, a, a.chunks_per_row * 16u);
   return hipGetLastError();
 }
 

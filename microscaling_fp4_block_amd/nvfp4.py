@@ -37,6 +37,8 @@ SIGNATURES = {
     "nvfp4_dequantize_kv_sink": ([_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _i32, _vp, _i32, _vp], _i32),
     "nvfp4_hadamard128": ([_vp, _i32, _i64, _vp, _vp], _i32),
+    "nvfp4_kv_append": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32,
+                         _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
 }
 
 _lock = threading.Lock()
@@ -231,3 +233,39 @@ def hadamard128(x: torch.Tensor) -> torch.Tensor:
                              _stream(dev))
     _check("nvfp4_hadamard128", st)
     return y
+
+
+def kv_cache_alloc(B: int, H: int, D: int, capacity: int, n_first: int = 128, n_last: int = 128,
+                   dtype=torch.bfloat16, device="cuda"):
+    """Buffers of an attention-sink NVFP4 KV cache for up to `capacity` tokens per (b, h):
+    head [B, H, n_first, D], tail ring [B, H, n_last, D], codes [B, H, cap, D/2],
+    scales [B, H, cap, D/16] with cap = capacity - n_first - n_last middle rows."""
+    cap = max(capacity - n_first - n_last, 0)
+    return dict(
+        head=torch.empty(B, H, n_first, D, dtype=dtype, device=device),
+        tail=torch.empty(B, H, n_last, D, dtype=dtype, device=device),
+        codes=torch.empty(B, H, cap, D // 2, dtype=torch.uint8, device=device),
+        scales=torch.empty(B, H, cap, D // 16, dtype=torch.uint8, device=device),
+        n_first=n_first, n_last=n_last, length=0)
+
+
+def kv_append(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor, offsets=(-2, 6),
+              hadamard: bool = False, block: int = 16):
+    """Append kv_new [B, H, t_new, D] to a cache made by kv_cache_alloc (in place)."""
+    L = load()
+    dev = _dev(kv_new)
+    _dev(global_scale)
+    B, H, t_new, D = kv_new.shape
+    head, tail, codes, scales = cache["head"], cache["tail"], cache["codes"], cache["scales"]
+    if kv_new.dtype != head.dtype:
+        raise ValueError("kv_new must have the cache dtype")
+    f_lo, f_hi = _offsets(offsets)
+    flags = HADAMARD128 if hadamard else 0
+    T = cache["length"]
+    st = L.nvfp4_kv_append(kv_new.data_ptr(), _dtype(kv_new), B, H, T, t_new, D,
+                           cache["n_first"], cache["n_last"], codes.shape[2], block, f_lo, f_hi,
+                           flags, global_scale.data_ptr(), head.data_ptr(), tail.data_ptr(),
+                           codes.data_ptr(), scales.data_ptr(), _stream(dev))
+    _check("nvfp4_kv_append", st)
+    cache["length"] = T + t_new
+    return cache
