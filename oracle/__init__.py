@@ -18,4 +18,6 @@ from .oracle import (  # noqa: F401
     quantize_kv_sink,
     dequantize_kv_sink,
     hadamard128,
+    hadamard128_rht,
+    quantize_rht,
 )

@@ -400,6 +400,7 @@ typedef struct {
     int dtype;
     int64_t v0, v1;
     float *y;
+    const uint32_t *signs; /* NULL, or 128 bits: bit k set negates input feature k */
 } hjob_t;
 
 /* The Sylvester matrix, entry by entry from its definition; filled before any
@@ -418,8 +419,11 @@ static void hadamard_vectors(const hjob_t *J)
     const double c = sqrt(1.0 / 128.0); /* correctly rounded 2^-3.5 */
     for (int64_t v = J->v0; v < J->v1; ++v) {
         double in[128];
-        for (int k = 0; k < 128; ++k)
+        for (int k = 0; k < 128; ++k) {
             in[k] = (double)load_elem(J->x, J->dtype, v * 128 + k);
+            if (J->signs && ((J->signs[k >> 5] >> (k & 31)) & 1u))
+                in[k] = -in[k];
+        }
         for (int j = 0; j < 128; ++j) {
             double s = 0.0;
             for (int k = 0; k < 128; ++k)
@@ -435,7 +439,8 @@ static void *hadamard_thread(void *arg)
     return NULL;
 }
 
-static int hadamard_threads(const void *x, int dtype, int64_t nvec, float *y, int nthreads)
+static int hadamard_threads(const void *x, int dtype, int64_t nvec, float *y, int nthreads,
+                            const uint32_t *signs)
 {
     if (nthreads < 1)
         nthreads = 1;
@@ -450,6 +455,7 @@ static int hadamard_threads(const void *x, int dtype, int64_t nvec, float *y, in
         jobs[t].y = y;
         jobs[t].v0 = nvec * t / nthreads;
         jobs[t].v1 = nvec * (t + 1) / nthreads;
+        jobs[t].signs = signs;
     }
     fill_hadamard();
     for (int t = 0; t < nthreads; ++t) {
@@ -467,7 +473,18 @@ int oracle_hadamard128(const void *x, int dtype, int64_t nvec, float *y)
 {
     if (!x || !y || nvec < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
         return ORACLE_EINVAL;
-    return hadamard_threads(x, dtype, nvec, y, 1);
+    return hadamard_threads(x, dtype, nvec, y, 1, NULL);
+}
+
+/* Randomized Hadamard transform (QuIP#-style incoherence processing): each
+ * 128-vector has the features whose bit is set in signs[4] negated, then is
+ * transformed as above: y = (x o s) H / sqrt(128). The random signs are an
+ * input (the caller draws them). */
+int oracle_hadamard128_rht(const void *x, int dtype, int64_t nvec, const uint32_t *signs, float *y)
+{
+    if (!x || !y || !signs || nvec < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    return hadamard_threads(x, dtype, nvec, y, 1, signs);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -498,7 +515,7 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int f_
         ybuf = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
         if (!ybuf)
             return ORACLE_ENOMEM;
-        hadamard_threads(x, dtype, n / 128, ybuf, nthreads);
+        hadamard_threads(x, dtype, n / 128, ybuf, nthreads, NULL);
         src = ybuf;
         sdt = ORACLE_F32;
     }
@@ -533,6 +550,25 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int f_
     J.scales = scales;
     J.chosen_f = chosen_f;
     int rc = run_quantize_rows(J, nthreads);
+    free(ybuf);
+    return rc;
+}
+
+/* Quantize after the randomized Hadamard transform with the given signs. */
+int oracle_quantize_rht(const void *x, int dtype, int64_t rows, int64_t cols, const uint32_t *signs,
+                        int f_lo, int f_hi, int gscale_given, float *gscale, uint8_t *codes,
+                        uint8_t *scales, int nthreads)
+{
+    if (!x || !signs || rows < 0 || cols <= 0 || cols % 128 ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    int64_t n = rows * cols;
+    float *ybuf = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!ybuf)
+        return ORACLE_ENOMEM;
+    hadamard_threads(x, dtype, n / 128, ybuf, nthreads, signs);
+    int rc = oracle_quantize(ybuf, ORACLE_F32, rows, cols, f_lo, f_hi, 0, gscale_given, gscale,
+                             codes, scales, NULL, nthreads);
     free(ybuf);
     return rc;
 }

@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
             L.oracle_dequantize_kv_sink.restype = i32
             L.oracle_hadamard128.argtypes = [vp, i32, i64, vp]
             L.oracle_hadamard128.restype = i32
+            L.oracle_hadamard128_rht.argtypes = [vp, i32, i64, vp, vp]
+            L.oracle_hadamard128_rht.restype = i32
+            L.oracle_quantize_rht.argtypes = [vp, i32, i64, i64, vp, i32, i32, i32, vp, vp, vp, i32]
+            L.oracle_quantize_rht.restype = i32
             _lib = L
     return _lib
 
@@ -200,3 +204,40 @@ def hadamard128(x: np.ndarray) -> np.ndarray:
     if rc:
         raise ValueError(f"oracle_hadamard128 failed ({rc})")
     return y
+
+
+def _signs_words(signs) -> np.ndarray:
+    """128 sign bits as four uint32 words (bit k of word k // 32: negate feature k)."""
+    w = np.ascontiguousarray(signs, dtype=np.uint32)
+    if w.shape != (4,):
+        raise ValueError("signs: four uint32 words")
+    return w
+
+
+def hadamard128_rht(x: np.ndarray, signs) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    w = _signs_words(signs)
+    y = np.empty(x.shape, dtype=np.float32)
+    rc = lib().oracle_hadamard128_rht(_ptr(x), dt, x.size // 128, _ptr(w), _ptr(y))
+    if rc:
+        raise ValueError(f"oracle_hadamard128_rht failed ({rc})")
+    return y
+
+
+def quantize_rht(x: np.ndarray, signs, f_lo: int = -8, f_hi: int = 8, gscale: float | None = None,
+                 nthreads: int | None = None):
+    x = np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    w = _signs_words(signs)
+    K = x.shape[-1]
+    R = x.size // K
+    codes = np.empty((R, K // 2), dtype=np.uint8)
+    scales = np.empty((R, K // 16), dtype=np.uint8)
+    g = np.array([0.0 if gscale is None else gscale], dtype=np.float32)
+    rc = lib().oracle_quantize_rht(_ptr(x), dt, R, K, _ptr(w), f_lo, f_hi, int(gscale is not None),
+                                   _ptr(g), _ptr(codes), _ptr(scales), _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_quantize_rht failed ({rc})")
+    shp = x.shape[:-1]
+    return codes.reshape(*shp, K // 2), scales.reshape(*shp, K // 16), np.float32(g[0])

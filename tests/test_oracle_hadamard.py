@@ -51,3 +51,43 @@ def test_hadamard_then_quantize(orc):
     assert g == g2
     np.testing.assert_array_equal(c.reshape(c2.shape), c2)
     np.testing.assert_array_equal(s.reshape(s2.shape), s2)
+
+
+# --- randomized Hadamard (QuIP#-style random sign flips before the transform) ---
+
+def _signs(seed):
+    return np.random.default_rng(seed).integers(0, 2**32, 4, dtype=np.uint64).astype(np.uint32)
+
+
+def test_rht_all_positive_signs_is_plain(orc):
+    x = workloads.workload(5, (1, 1, 16, 128))
+    np.testing.assert_array_equal(orc.hadamard128_rht(x, np.zeros(4, np.uint32)),
+                                  orc.hadamard128(x))
+
+
+def test_rht_matches_library_hadamard_with_signs(orc):
+    x = workloads.workload(5, (1, 2, 32, 128))
+    w = _signs(3)
+    bits = np.array([(w[k // 32] >> (k % 32)) & 1 for k in range(128)])
+    s = np.where(bits == 1, -1.0, 1.0)
+    xf = workloads.bf16_bits_to_f32(x).reshape(-1, 128).astype(np.float64)
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    ref = (((xf * s) @ H) * np.sqrt(1.0 / 128.0)).astype(np.float32)
+    np.testing.assert_array_equal(orc.hadamard128_rht(x, w).reshape(-1, 128), ref)
+
+
+def test_rht_inverse_and_quantize(orc):
+    x = workloads.workload(5, (1, 1, 64, 128))
+    w = _signs(4)
+    bits = np.array([(w[k // 32] >> (k % 32)) & 1 for k in range(128)])
+    y = orc.hadamard128_rht(x, w).reshape(-1, 128).astype(np.float64)
+    # inverse: x = (y H / sqrt(128)) o s
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    back = (y @ H) * np.sqrt(1.0 / 128.0) * np.where(bits == 1, -1.0, 1.0)
+    xf = workloads.bf16_bits_to_f32(x).reshape(-1, 128)
+    np.testing.assert_allclose(back, xf, rtol=0, atol=1e-6 * np.abs(xf).max())
+    c, s, g = orc.quantize_rht(x, w, -8, 8)
+    c2, s2, g2 = orc.quantize(orc.hadamard128_rht(x, w).reshape(-1, 128), -8, 8)
+    assert g == g2
+    np.testing.assert_array_equal(c.reshape(c2.shape), c2)
+    np.testing.assert_array_equal(s.reshape(s2.shape), s2)
