@@ -170,6 +170,45 @@ NVFP4_API nvfp4_status nvfp4_kv_append(const void *kv_new, nvfp4_dtype dt, int64
 NVFP4_API nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,
                                void *stream);
 
+/* Randomized Hadamard transform (QuIP#-style incoherence processing, ScaleSearch
+ * summary page, ScaleSearchAttention section: a transform pair Q' = Q R^-T,
+ * K' = K R that keeps Q K^T while lowering the mean-square absolute value).
+ * Reading: R = diag(s) H / sqrt(128) per 128-vector with random signs s; R is
+ * orthogonal, so R^-T = R and Q and K take the same transform (the same signs):
+ * (Q R)(K R)^T = Q K^T. signs: host pointer to four uint32 words (read during
+ * the call only); bit k % 32 of signs[k / 32] set negates feature k of every
+ * 128-vector before H. The caller draws the signs (once per model or layer) and
+ * must use the same words for Q and K. Each *_rht call is its namesake with
+ * NVFP4_HADAMARD128 implied (other flags as there, bf16 input, cols % 128 == 0)
+ * and x replaced by x o s; signs == NULL is NVFP4_EINVAL. All-zero signs give
+ * exactly the plain-transform results. */
+NVFP4_API nvfp4_status nvfp4_quantize_rht(const void *x, nvfp4_dtype xdt, int64_t rows,
+                                          int64_t cols, int block, int f_lo, int f_hi,
+                                          uint32_t flags, const uint32_t *signs, uint8_t *codes,
+                                          uint8_t *scales, float *global_scale, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+NVFP4_API nvfp4_status nvfp4_global_scale_rht(const void *x, nvfp4_dtype xdt, int64_t rows,
+                                              int64_t cols, uint32_t flags, const uint32_t *signs,
+                                              float *global_scale, void *workspace,
+                                              size_t workspace_bytes, void *stream);
+NVFP4_API nvfp4_status nvfp4_quantize_kv_sink_rht(const void *kv, nvfp4_dtype dt, int64_t B,
+                                                  int64_t H, int64_t T, int64_t D,
+                                                  int64_t n_first, int64_t n_last, int block,
+                                                  int f_lo, int f_hi, uint32_t flags,
+                                                  const uint32_t *signs, uint8_t *codes,
+                                                  uint8_t *scales, float *global_scale,
+                                                  void *sink, void *workspace,
+                                                  size_t workspace_bytes, void *stream);
+NVFP4_API nvfp4_status nvfp4_kv_append_rht(const void *kv_new, nvfp4_dtype dt, int64_t B,
+                                           int64_t H, int64_t T, int64_t t_new, int64_t D,
+                                           int64_t n_first, int64_t n_last, int64_t cap,
+                                           int block, int f_lo, int f_hi, uint32_t flags,
+                                           const uint32_t *signs, const float *global_scale,
+                                           void *head, void *tail, uint8_t *codes,
+                                           uint8_t *scales, void *stream);
+NVFP4_API nvfp4_status nvfp4_hadamard128_rht(const void *x, nvfp4_dtype xdt, int64_t rows,
+                                             const uint32_t *signs, float *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,9 +42,9 @@ RegionMap plain_map(int64_t rows, int64_t cols) {
 
 // Global amax pass: one partial maximum per workgroup into the workspace.
 // Returns the number of partials (0 on a launch error).
-int run_amax(const void *x, bool bf16, bool hadamard, const RegionMap &m, void *ws,
-             hipStream_t s) {
-  AmaxArgs a{x, (uint32_t *)ws, m};
+int run_amax(const void *x, bool bf16, bool hadamard, const HadamardSigns &hs, const RegionMap &m,
+             void *ws, hipStream_t s) {
+  AmaxArgs a{x, (uint32_t *)ws, m, hs};
   int groups;
   hipError_t e;
   if (hadamard) {
@@ -58,9 +58,9 @@ int run_amax(const void *x, bool bf16, bool hadamard, const RegionMap &m, void *
 }
 
 // Global amax + finalize into gscale (the tensor scale alone).
-nvfp4_status run_global_scale(const void *x, bool bf16, bool hadamard, const RegionMap &m,
-                              float *gscale, void *ws, hipStream_t s) {
-  const int groups = run_amax(x, bf16, hadamard, m, ws, s);
+nvfp4_status run_global_scale(const void *x, bool bf16, bool hadamard, const HadamardSigns &hs,
+                              const RegionMap &m, float *gscale, void *ws, hipStream_t s) {
+  const int groups = run_amax(x, bf16, hadamard, hs, m, ws, s);
   if (groups == 0) return NVFP4_EHIP;
   return hip_status(launch_finalize((const uint32_t *)ws, groups, gscale, s));
 }
@@ -72,20 +72,30 @@ hipError_t run_quantize(const QuantArgs &q, bool bf16, bool hadamard, hipStream_
 // Quantize a region: the amax pass (unless the tensor scale is given), then the
 // search kernel, which reduces the partials to S_g in its prologue. An empty
 // region still gets its tensor scale.
-nvfp4_status run_quantize_region(const void *x, bool bf16, bool had, bool given,
-                                 const RegionMap &m, int f_lo, int f_hi, uint8_t *codes,
-                                 uint8_t *scales, float *gscale, void *ws, hipStream_t s) {
+nvfp4_status run_quantize_region(const void *x, bool bf16, bool had, const HadamardSigns &hs,
+                                 bool given, const RegionMap &m, int f_lo, int f_hi,
+                                 uint8_t *codes, uint8_t *scales, float *gscale, void *ws,
+                                 hipStream_t s) {
   if (m.nblocks == 0)
-    return given ? NVFP4_OK : run_global_scale(x, bf16, had, m, gscale, ws, s);
+    return given ? NVFP4_OK : run_global_scale(x, bf16, had, hs, m, gscale, ws, s);
   int np = 0;
   if (!given) {
-    np = run_amax(x, bf16, had, m, ws, s);
+    np = run_amax(x, bf16, had, hs, m, ws, s);
     if (np == 0) return NVFP4_EHIP;
   }
-  QuantArgs q{x, codes, scales, gscale, (const uint32_t *)ws, np, m, f_lo, f_hi};
+  QuantArgs q{x, codes, scales, gscale, (const uint32_t *)ws, np, m, f_lo, f_hi, hs};
   return hip_status(run_quantize(q, bf16, had, s));
 }
 
+
+HadamardSigns make_signs(const uint32_t *signs) {
+  HadamardSigns h{};
+  if (signs) {
+    h.on = 1;
+    for (int i = 0; i < 4; ++i) h.w[i] = signs[i];
+  }
+  return h;
+}
 
 nvfp4_status check_offsets(int block, int f_lo, int f_hi) {
   if (block != 16) return NVFP4_EINVAL;
@@ -129,9 +139,16 @@ size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags) {
   return workspace_needed();
 }
 
-nvfp4_status nvfp4_global_scale(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
-                                uint32_t flags, float *global_scale, void *workspace,
-                                size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The entry points below with signs == nullptr (plain transform or none), and
+// the *_rht entry points with the caller's signs and the transform forced on.
+
+nvfp4_status global_scale_impl(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                               uint32_t flags, const uint32_t *signs, float *global_scale,
+                               void *workspace, size_t workspace_bytes, void *stream) {
   if (!global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
   nvfp4_status st = check_shape(rows, cols, flags & ~NVFP4_GSCALE_GIVEN, xdt);
   if (st) return st;
@@ -139,14 +156,14 @@ nvfp4_status nvfp4_global_scale(const void *x, nvfp4_dtype xdt, int64_t rows, in
   if (!aligned(x, 16)) return NVFP4_EALIGN;
   if (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4))
     return NVFP4_EWORKSPACE;
-  return run_global_scale(x, xdt == NVFP4_BF16, flags & NVFP4_HADAMARD128, plain_map(rows, cols),
-                          global_scale, workspace, (hipStream_t)stream);
+  return run_global_scale(x, xdt == NVFP4_BF16, flags & NVFP4_HADAMARD128, make_signs(signs),
+                          plain_map(rows, cols), global_scale, workspace, (hipStream_t)stream);
 }
 
-nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
-                            int block, int f_lo, int f_hi, uint32_t flags, uint8_t *codes,
-                            uint8_t *scales, float *global_scale, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+nvfp4_status quantize_impl(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols, int block,
+                           int f_lo, int f_hi, uint32_t flags, const uint32_t *signs,
+                           uint8_t *codes, uint8_t *scales, float *global_scale, void *workspace,
+                           size_t workspace_bytes, void *stream) {
   if (!global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
   nvfp4_status st = check_offsets(block, f_lo, f_hi);
   if (st) return st;
@@ -160,8 +177,45 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = xdt == NVFP4_BF16;
   const bool had = flags & NVFP4_HADAMARD128;
-  return run_quantize_region(x, bf16, had, given, plain_map(rows, cols), f_lo, f_hi, codes,
-                             scales, global_scale, workspace, s);
+  return run_quantize_region(x, bf16, had, make_signs(signs), given, plain_map(rows, cols), f_lo,
+                             f_hi, codes, scales, global_scale, workspace, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_global_scale(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                                uint32_t flags, float *global_scale, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  return global_scale_impl(x, xdt, rows, cols, flags, nullptr, global_scale, workspace,
+                           workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_global_scale_rht(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                                    uint32_t flags, const uint32_t *signs, float *global_scale,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  if (!signs) return NVFP4_EINVAL;
+  return global_scale_impl(x, xdt, rows, cols, flags | NVFP4_HADAMARD128, signs, global_scale,
+                           workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                            int block, int f_lo, int f_hi, uint32_t flags, uint8_t *codes,
+                            uint8_t *scales, float *global_scale, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  return quantize_impl(x, xdt, rows, cols, block, f_lo, f_hi, flags, nullptr, codes, scales,
+                       global_scale, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_quantize_rht(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                                int block, int f_lo, int f_hi, uint32_t flags,
+                                const uint32_t *signs, uint8_t *codes, uint8_t *scales,
+                                float *global_scale, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  if (!signs) return NVFP4_EINVAL;
+  return quantize_impl(x, xdt, rows, cols, block, f_lo, f_hi, flags | NVFP4_HADAMARD128, signs,
+                       codes, scales, global_scale, workspace, workspace_bytes, stream);
 }
 
 nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
@@ -178,12 +232,15 @@ nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
   return hip_status(launch_dequantize(a, ydt == NVFP4_BF16, (hipStream_t)stream));
 }
 
-nvfp4_status nvfp4_quantize_kv_sink(const void *kv, nvfp4_dtype dt, int64_t B, int64_t H,
-                                    int64_t T, int64_t D, int64_t n_first, int64_t n_last,
-                                    int block, int f_lo, int f_hi, uint32_t flags,
-                                    uint8_t *codes, uint8_t *scales, float *global_scale,
-                                    void *sink, void *workspace, size_t workspace_bytes,
-                                    void *stream) {
+}  // extern "C"
+
+namespace {
+
+nvfp4_status kv_sink_impl(const void *kv, nvfp4_dtype dt, int64_t B, int64_t H, int64_t T,
+                          int64_t D, int64_t n_first, int64_t n_last, int block, int f_lo,
+                          int f_hi, uint32_t flags, const uint32_t *signs, uint8_t *codes,
+                          uint8_t *scales, float *global_scale, void *sink, void *workspace,
+                          size_t workspace_bytes, void *stream) {
   if (!global_scale || !dtype_ok(dt)) return NVFP4_EINVAL;
   nvfp4_status st = check_offsets(block, f_lo, f_hi);
   if (st) return st;
@@ -232,8 +289,34 @@ nvfp4_status nvfp4_quantize_kv_sink(const void *kv, nvfp4_dtype dt, int64_t B, i
   m.seg_tokens = (uint32_t)T;
   m.n_first = (uint32_t)n_first;
   m.cols = (uint32_t)D;
-  return run_quantize_region(kv, bf16, had, given, m, f_lo, f_hi, codes, scales, global_scale,
-                             workspace, s);
+  return run_quantize_region(kv, bf16, had, make_signs(signs), given, m, f_lo, f_hi, codes, scales,
+                             global_scale, workspace, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_quantize_kv_sink(const void *kv, nvfp4_dtype dt, int64_t B, int64_t H,
+                                    int64_t T, int64_t D, int64_t n_first, int64_t n_last,
+                                    int block, int f_lo, int f_hi, uint32_t flags,
+                                    uint8_t *codes, uint8_t *scales, float *global_scale,
+                                    void *sink, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  return kv_sink_impl(kv, dt, B, H, T, D, n_first, n_last, block, f_lo, f_hi, flags, nullptr,
+                      codes, scales, global_scale, sink, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_quantize_kv_sink_rht(const void *kv, nvfp4_dtype dt, int64_t B, int64_t H,
+                                        int64_t T, int64_t D, int64_t n_first, int64_t n_last,
+                                        int block, int f_lo, int f_hi, uint32_t flags,
+                                        const uint32_t *signs, uint8_t *codes, uint8_t *scales,
+                                        float *global_scale, void *sink, void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+  if (!signs) return NVFP4_EINVAL;
+  return kv_sink_impl(kv, dt, B, H, T, D, n_first, n_last, block, f_lo, f_hi,
+                      flags | NVFP4_HADAMARD128, signs, codes, scales, global_scale, sink,
+                      workspace, workspace_bytes, stream);
 }
 
 nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scales,
@@ -272,11 +355,15 @@ nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scale
       launch_dequantize_kv(a, sink_dt == NVFP4_BF16, ydt == NVFP4_BF16, (hipStream_t)stream));
 }
 
-nvfp4_status nvfp4_kv_append(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H,
-                             int64_t T, int64_t t_new, int64_t D, int64_t n_first,
-                             int64_t n_last, int64_t cap, int block, int f_lo, int f_hi,
-                             uint32_t flags, const float *global_scale, void *head, void *tail,
-                             uint8_t *codes, uint8_t *scales, void *stream) {
+}  // extern "C"
+
+namespace {
+
+nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H, int64_t T,
+                            int64_t t_new, int64_t D, int64_t n_first, int64_t n_last,
+                            int64_t cap, int block, int f_lo, int f_hi, uint32_t flags,
+                            const uint32_t *signs, const float *global_scale, void *head,
+                            void *tail, uint8_t *codes, uint8_t *scales, void *stream) {
   if (!global_scale || !dtype_ok(dt)) return NVFP4_EINVAL;
   nvfp4_status st = check_offsets(block, f_lo, f_hi);
   if (st) return st;
@@ -327,7 +414,8 @@ nvfp4_status nvfp4_kv_append(const void *kv_new, nvfp4_dtype dt, int64_t B, int6
     m.cap = (uint32_t)cap;
     m.div_nlast = make_fastdiv((uint32_t)(n_last > 0 ? n_last : 1));
     m.ring = tail;
-    QuantArgs q{kv_new, codes, scales, (float *)global_scale, nullptr, 0, m, f_lo, f_hi};
+    QuantArgs q{kv_new, codes, scales, (float *)global_scale, nullptr, 0, m, f_lo, f_hi,
+                make_signs(signs)};
     if (run_quantize(q, bf16, had, s) != hipSuccess) return NVFP4_EHIP;
   }
   // 2. store the new tokens that stay in full precision
@@ -350,14 +438,51 @@ nvfp4_status nvfp4_kv_append(const void *kv_new, nvfp4_dtype dt, int64_t B, int6
   return NVFP4_OK;
 }
 
-nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,
-                               void *stream) {
+nvfp4_status hadamard_impl(const void *x, nvfp4_dtype xdt, int64_t rows, const uint32_t *signs,
+                           float *y, void *stream) {
   if (xdt != NVFP4_BF16) return NVFP4_EINVAL;
   if (rows < 0 || rows > kMaxBlocks / 8) return NVFP4_ESHAPE;
   if (rows == 0) return NVFP4_OK;
   if (!x || !y) return NVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_EALIGN;
-  return hip_status(launch_hadamard((const uint16_t *)x, y, (uint32_t)rows, (hipStream_t)stream));
+  return hip_status(launch_hadamard((const uint16_t *)x, y, (uint32_t)rows, make_signs(signs),
+                                    (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_kv_append(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H,
+                             int64_t T, int64_t t_new, int64_t D, int64_t n_first,
+                             int64_t n_last, int64_t cap, int block, int f_lo, int f_hi,
+                             uint32_t flags, const float *global_scale, void *head, void *tail,
+                             uint8_t *codes, uint8_t *scales, void *stream) {
+  return kv_append_impl(kv_new, dt, B, H, T, t_new, D, n_first, n_last, cap, block, f_lo, f_hi,
+                        flags, nullptr, global_scale, head, tail, codes, scales, stream);
+}
+
+nvfp4_status nvfp4_kv_append_rht(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H,
+                                 int64_t T, int64_t t_new, int64_t D, int64_t n_first,
+                                 int64_t n_last, int64_t cap, int block, int f_lo, int f_hi,
+                                 uint32_t flags, const uint32_t *signs, const float *global_scale,
+                                 void *head, void *tail, uint8_t *codes, uint8_t *scales,
+                                 void *stream) {
+  if (!signs) return NVFP4_EINVAL;
+  return kv_append_impl(kv_new, dt, B, H, T, t_new, D, n_first, n_last, cap, block, f_lo, f_hi,
+                        flags | NVFP4_HADAMARD128, signs, global_scale, head, tail, codes, scales,
+                        stream);
+}
+
+nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,
+                               void *stream) {
+  return hadamard_impl(x, xdt, rows, nullptr, y, stream);
+}
+
+nvfp4_status nvfp4_hadamard128_rht(const void *x, nvfp4_dtype xdt, int64_t rows,
+                                   const uint32_t *signs, float *y, void *stream) {
+  if (!signs) return NVFP4_EINVAL;
+  return hadamard_impl(x, xdt, rows, signs, y, stream);
 }
 
 }  // extern "C"

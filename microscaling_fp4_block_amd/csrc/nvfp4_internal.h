@@ -53,6 +53,13 @@ struct RegionMap {
   const void *ring;
 };
 
+// Random sign flips of the randomized Hadamard transform: bit k of w[k / 32]
+// set negates input feature k of every 128-vector before H is applied.
+struct HadamardSigns {
+  uint32_t on;    // 0: plain transform (w ignored)
+  uint32_t w[4];
+};
+
 struct QuantArgs {
   const void *x;
   uint8_t *codes;
@@ -62,12 +69,14 @@ struct QuantArgs {
   int npartials;              // 0: the tensor scale is given
   RegionMap map;
   int f_lo, f_hi;
+  HadamardSigns hs;           // Hadamard kernels only
 };
 
 struct AmaxArgs {
   const void *x;
   uint32_t *partials;
   RegionMap map;
+  HadamardSigns hs;           // Hadamard kernels only
 };
 
 struct DequantArgs {
@@ -121,7 +130,8 @@ hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s);
 int amax_hadamard_groups(uint32_t nblocks);
 hipError_t launch_amax_hadamard(const AmaxArgs &a, int groups, hipStream_t s);
 hipError_t launch_quantize_hadamard(const QuantArgs &a, hipStream_t s);
-hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, hipStream_t s);
+hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, const HadamardSigns &hs,
+                           hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s);
 hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_admit(const AdmitArgs &a, bool bf16, hipStream_t s);

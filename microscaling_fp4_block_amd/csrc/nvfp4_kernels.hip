@@ -619,6 +619,11 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
 // per 32-feature tile t. The products are exact; the FP32 accumulation may
 // round, so the transform is within a few FP32 ulps of the exact one. The sum
 // is scaled in FP64 by the double nearest 2^-3.5 and rounded once to FP32.
+//
+// Randomized variant (random +-1 signs before H, as in QuIP#'s incoherence
+// processing): y = (x o s) H / sqrt(128). The signs flip the sign bits of the
+// bf16 B operand as it is loaded, so the products stay exact and the result
+// is that of the plain transform of x o s.
 // ---------------------------------------------------------------------------
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -663,12 +668,29 @@ __device__ __forceinline__ bf16x8 hadamard_a(const HadamardLane &h, uint32_t t, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Load this lane's B slices of one 128-vector: elements 16 ks + 8 g .. +7.
-__device__ __forceinline__ void hadamard_load(const uint16_t *x, uint64_t off, bool valid,
-                                              uint32_t g, uint4 (&b)[8]) {
+// bf16 sign-bit mask of elements 16 ks + 8 g .. +7 (two per word, low first).
+__device__ __forceinline__ uint4 hadamard_sign_mask(const HadamardSigns &hs, int ks, uint32_t g) {
+  const uint32_t bits = (hs.w[ks >> 1] >> (16u * (ks & 1) + 8u * g)) & 0xFFu;
+  uint32_t m[4];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
+  for (int q = 0; q < 4; ++q)
+    m[q] = (((bits >> (2 * q)) & 1u) << 15) | (((bits >> (2 * q + 1)) & 1u) << 31);
+  return make_uint4(m[0], m[1], m[2], m[3]);
+}
+
+// Load this lane's B slices of one 128-vector: elements 16 ks + 8 g .. +7,
+// with the random signs applied when SIGNS.
+template <bool SIGNS>
+__device__ __forceinline__ void hadamard_load(const uint16_t *x, uint64_t off, bool valid,
+                                              uint32_t g, const HadamardSigns &hs, uint4 (&b)[8]) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
     b[ks] = valid ? *(const uint4 *)(x + off + 16u * ks + 8u * g) : make_uint4(0, 0, 0, 0);
+    if (SIGNS) {
+      const uint4 m = hadamard_sign_mask(hs, ks, g);
+      b[ks] = make_uint4(b[ks].x ^ m.x, b[ks].y ^ m.y, b[ks].z ^ m.z, b[ks].w ^ m.w);
+    }
+  }
 }
 
 // Tile t of the transform: y[v] = feature 32 t + 16 g + v of this lane's vector.
@@ -685,6 +707,7 @@ __device__ __forceinline__ void hadamard_tile(const HadamardLane &h, const uint4
 
 // Quantize with the Hadamard pre-transform (bf16 input, cols % 128 == 0). One
 // wave per 32 vectors; each lane codes four blocks of its vector.
+template <bool SIGNS>
 __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a) {
   __shared__ f32x2 tbl[128];
   const float sg = resolve_tensor_scale(a);
@@ -701,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
     const bool valid = vec < nvec;
     uint4 b[8];
     const BlockIO io = block_io(a.x, a.map, valid ? vec * 8u : 0u, 2u);
-    hadamard_load((const uint16_t *)io.src, 0, valid, h.g, b);
+    hadamard_load<SIGNS>((const uint16_t *)io.src, 0, valid, h.g, a.hs, b);
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
@@ -718,6 +741,7 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
 }
 
 // Global amax of the transformed values.
+template <bool SIGNS>
 __global__ __launch_bounds__(kThreads) void amax_hadamard_kernel(AmaxArgs a) {
   const HadamardLane h = hadamard_lane_setup();
   const uint32_t nvec = a.map.nblocks / 8u;
@@ -729,7 +753,8 @@ __global__ __launch_bounds__(kThreads) void amax_hadamard_kernel(AmaxArgs a) {
     const uint32_t vec = tile * 32u + (lane & 31u);
     const bool valid = vec < nvec;
     uint4 b[8];
-    hadamard_load((const uint16_t *)a.x, valid ? block_offset(a.map, vec * 8u) : 0, valid, h.g, b);
+    hadamard_load<SIGNS>((const uint16_t *)a.x, valid ? block_offset(a.map, vec * 8u) : 0, valid,
+                         h.g, a.hs, b);
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
@@ -743,8 +768,9 @@ __global__ __launch_bounds__(kThreads) void amax_hadamard_kernel(AmaxArgs a) {
 }
 
 // The transform alone: y[nvec][128] FP32.
+template <bool SIGNS>
 __global__ __launch_bounds__(kThreads) void hadamard_kernel(const uint16_t *x, float *out,
-                                                            uint32_t nvec) {
+                                                            uint32_t nvec, HadamardSigns hs) {
   const HadamardLane h = hadamard_lane_setup();
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
@@ -753,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void hadamard_kernel(const uint16_t *x, f
     const uint32_t vec = tile * 32u + (lane & 31u);
     const bool valid = vec < nvec;
     uint4 b[8];
-    hadamard_load(x, (uint64_t)(valid ? vec : 0) * 128u, valid, h.g, b);
+    hadamard_load<SIGNS>(x, (uint64_t)(valid ? vec : 0) * 128u, valid, h.g, hs, b);
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
@@ -983,19 +1009,29 @@ static int hadamard_groups(uint32_t nvec, int cap) {
 int amax_hadamard_groups(uint32_t nblocks) { return hadamard_groups(nblocks / 8u, kMaxAmaxGroups); }
 
 hipError_t launch_amax_hadamard(const AmaxArgs &a, int groups, hipStream_t s) {
-  hipLaunchKernelGGL(amax_hadamard_kernel, dim3(groups), dim3(kThreads), 0, s, a);
+  if (a.hs.on)
+    hipLaunchKernelGGL(amax_hadamard_kernel<true>, dim3(groups), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(amax_hadamard_kernel<false>, dim3(groups), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_hadamard(const QuantArgs &a, hipStream_t s) {
   const int g = hadamard_groups(a.map.nblocks / 8u, kMaxQuantGroups);
-  hipLaunchKernelGGL(quantize_hadamard_kernel, dim3(g), dim3(kThreads), 0, s, a);
+  if (a.hs.on)
+    hipLaunchKernelGGL(quantize_hadamard_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(quantize_hadamard_kernel<false>, dim3(g), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, hipStream_t s) {
+hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, const HadamardSigns &hs,
+                           hipStream_t s) {
   const int g = hadamard_groups(nvec, kMaxQuantGroups);
-  hipLaunchKernelGGL(hadamard_kernel, dim3(g), dim3(kThreads), 0, s, x, y, nvec);
+  if (hs.on)
+    hipLaunchKernelGGL(hadamard_kernel<true>, dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs);
+  else
+    hipLaunchKernelGGL(hadamard_kernel<false>, dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs);
   return hipGetLastError();
 }
 

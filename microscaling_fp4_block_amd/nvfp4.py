@@ -39,6 +39,14 @@ SIGNATURES = {
     "nvfp4_hadamard128": ([_vp, _i32, _i64, _vp, _vp], _i32),
     "nvfp4_kv_append": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32,
                          _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "nvfp4_quantize_rht": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp,
+                            _vp, _sz, _vp], _i32),
+    "nvfp4_global_scale_rht": ([_vp, _i32, _i64, _i64, _u32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "nvfp4_quantize_kv_sink_rht": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32,
+                                    _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "nvfp4_kv_append_rht": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32,
+                             _i32, _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "nvfp4_hadamard128_rht": ([_vp, _i32, _i64, _vp, _vp, _vp], _i32),
 }
 
 _lock = threading.Lock()
@@ -100,17 +108,32 @@ def workspace_bytes(rows: int, cols: int, flags: int = 0) -> int:
     return int(load().nvfp4_workspace_bytes(rows, cols, flags))
 
 
+def _signs(signs):
+    """Random signs of the randomized Hadamard transform as a host uint32[4]
+    (bit k % 32 of word k // 32 negates feature k); None for the plain transform."""
+    if signs is None:
+        return None
+    if isinstance(signs, torch.Tensor):
+        signs = signs.cpu().tolist()
+    w = [int(v) for v in signs]
+    if len(w) != 4 or any(v < 0 or v >= 1 << 32 for v in w):
+        raise ValueError("signs: four uint32 words")
+    return (ctypes.c_uint32 * 4)(*w)
+
+
 def _offsets(offsets):
     lo, hi = int(offsets[0]), int(offsets[1])
     return lo, hi
 
 
 def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
-             global_scale: torch.Tensor | None = None, block: int = 16, workspace=None):
+             global_scale: torch.Tensor | None = None, block: int = 16, workspace=None,
+             signs=None):
     """ScaleSearch NVFP4 quantize of x (last dim in blocks of 16).
 
     Returns (codes uint8[..., K/2], scales uint8[..., K/16], global_scale float32[1]).
     If ``global_scale`` (a device float32[1]) is given it is used as S_g.
+    ``signs`` (four uint32 words) selects the randomized Hadamard transform.
     """
     L = load()
     dev = _dev(x)
@@ -130,14 +153,21 @@ def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
         g = torch.empty(1, dtype=torch.float32, device=dev)
     wsb = int(L.nvfp4_workspace_bytes(R, K, flags))
     ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
-    st = L.nvfp4_quantize(x.data_ptr(), _dtype(x), R, K, block, f_lo, f_hi, flags,
-                          codes.data_ptr(), scales.data_ptr(), g.data_ptr(), ws.data_ptr(),
-                          ws.numel(), _stream(dev))
+    sw = _signs(signs)
+    if sw is None:
+        st = L.nvfp4_quantize(x.data_ptr(), _dtype(x), R, K, block, f_lo, f_hi, flags,
+                              codes.data_ptr(), scales.data_ptr(), g.data_ptr(), ws.data_ptr(),
+                              ws.numel(), _stream(dev))
+    else:
+        st = L.nvfp4_quantize_rht(x.data_ptr(), _dtype(x), R, K, block, f_lo, f_hi, flags,
+                                  ctypes.addressof(sw), codes.data_ptr(), scales.data_ptr(),
+                                  g.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     _check("nvfp4_quantize", st)
     return codes, scales, g
 
 
-def global_scale(x: torch.Tensor, hadamard: bool = False, workspace=None) -> torch.Tensor:
+def global_scale(x: torch.Tensor, hadamard: bool = False, workspace=None,
+                 signs=None) -> torch.Tensor:
     """Tensor scale S_g = fl(max|x| / 2688) (1 if that is 0) as a device float32[1]."""
     L = load()
     dev = _dev(x)
@@ -147,8 +177,13 @@ def global_scale(x: torch.Tensor, hadamard: bool = False, workspace=None) -> tor
     g = torch.empty(1, dtype=torch.float32, device=dev)
     wsb = int(L.nvfp4_workspace_bytes(R, K, flags))
     ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
-    st = L.nvfp4_global_scale(x.data_ptr(), _dtype(x), R, K, flags, g.data_ptr(), ws.data_ptr(),
-                              ws.numel(), _stream(dev))
+    sw = _signs(signs)
+    if sw is None:
+        st = L.nvfp4_global_scale(x.data_ptr(), _dtype(x), R, K, flags, g.data_ptr(),
+                                  ws.data_ptr(), ws.numel(), _stream(dev))
+    else:
+        st = L.nvfp4_global_scale_rht(x.data_ptr(), _dtype(x), R, K, flags, ctypes.addressof(sw),
+                                      g.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     _check("nvfp4_global_scale", st)
     return g
 
@@ -172,7 +207,7 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, global_scale: torch.Te
 
 def quantize_kv_sink(kv: torch.Tensor, n_first: int = 128, n_last: int = 128, offsets=(-2, 6),
                      hadamard: bool = False, global_scale: torch.Tensor | None = None,
-                     block: int = 16, workspace=None):
+                     block: int = 16, workspace=None, signs=None):
     """Attention-sink KV mode on kv[B, H, T, D].
 
     Returns (codes[B,H,Tm,D/2], scales[B,H,Tm,D/16], global_scale[1], sink[B,H,nf+nl,D]).
@@ -197,10 +232,18 @@ def quantize_kv_sink(kv: torch.Tensor, n_first: int = 128, n_last: int = 128, of
         g = torch.empty(1, dtype=torch.float32, device=dev)
     wsb = int(L.nvfp4_workspace_bytes(B * H * Tm, D, flags))
     ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
-    st = L.nvfp4_quantize_kv_sink(kv.data_ptr(), _dtype(kv), B, H, T, D, n_first, n_last, block,
-                                  f_lo, f_hi, flags, codes.data_ptr(), scales.data_ptr(),
-                                  g.data_ptr(), sink.data_ptr(), ws.data_ptr(), ws.numel(),
-                                  _stream(dev))
+    sw = _signs(signs)
+    if sw is None:
+        st = L.nvfp4_quantize_kv_sink(kv.data_ptr(), _dtype(kv), B, H, T, D, n_first, n_last,
+                                      block, f_lo, f_hi, flags, codes.data_ptr(),
+                                      scales.data_ptr(), g.data_ptr(), sink.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), _stream(dev))
+    else:
+        st = L.nvfp4_quantize_kv_sink_rht(kv.data_ptr(), _dtype(kv), B, H, T, D, n_first, n_last,
+                                          block, f_lo, f_hi, flags, ctypes.addressof(sw),
+                                          codes.data_ptr(), scales.data_ptr(), g.data_ptr(),
+                                          sink.data_ptr(), ws.data_ptr(), ws.numel(),
+                                          _stream(dev))
     _check("nvfp4_quantize_kv_sink", st)
     return codes, scales, g, sink
 
@@ -222,15 +265,21 @@ def dequantize_kv_sink(codes, scales, global_scale, sink, T: int, n_first: int, 
     return y
 
 
-def hadamard128(x: torch.Tensor) -> torch.Tensor:
-    """FP32 y = x H / sqrt(128) per 128-vector (x bf16), as the quantizer computes it."""
+def hadamard128(x: torch.Tensor, signs=None) -> torch.Tensor:
+    """FP32 y = x H / sqrt(128) per 128-vector (x bf16), as the quantizer computes it;
+    with ``signs``, y = (x o s) H / sqrt(128)."""
     L = load()
     dev = _dev(x)
     if x.shape[-1] % 128:
         raise ValueError("last dimension must be a multiple of 128")
     y = torch.empty(x.shape, dtype=torch.float32, device=dev)
-    st = L.nvfp4_hadamard128(x.data_ptr(), _dtype(x), x.numel() // 128, y.data_ptr(),
-                             _stream(dev))
+    sw = _signs(signs)
+    if sw is None:
+        st = L.nvfp4_hadamard128(x.data_ptr(), _dtype(x), x.numel() // 128, y.data_ptr(),
+                                 _stream(dev))
+    else:
+        st = L.nvfp4_hadamard128_rht(x.data_ptr(), _dtype(x), x.numel() // 128,
+                                     ctypes.addressof(sw), y.data_ptr(), _stream(dev))
     _check("nvfp4_hadamard128", st)
     return y
 
@@ -250,7 +299,7 @@ def kv_cache_alloc(B: int, H: int, D: int, capacity: int, n_first: int = 128, n_
 
 
 def kv_append(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor, offsets=(-2, 6),
-              hadamard: bool = False, block: int = 16):
+              hadamard: bool = False, block: int = 16, signs=None):
     """Append kv_new [B, H, t_new, D] to a cache made by kv_cache_alloc (in place)."""
     L = load()
     dev = _dev(kv_new)
@@ -262,10 +311,18 @@ def kv_append(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor, off
     f_lo, f_hi = _offsets(offsets)
     flags = HADAMARD128 if hadamard else 0
     T = cache["length"]
-    st = L.nvfp4_kv_append(kv_new.data_ptr(), _dtype(kv_new), B, H, T, t_new, D,
-                           cache["n_first"], cache["n_last"], codes.shape[2], block, f_lo, f_hi,
-                           flags, global_scale.data_ptr(), head.data_ptr(), tail.data_ptr(),
-                           codes.data_ptr(), scales.data_ptr(), _stream(dev))
+    sw = _signs(signs)
+    if sw is None:
+        st = L.nvfp4_kv_append(kv_new.data_ptr(), _dtype(kv_new), B, H, T, t_new, D,
+                               cache["n_first"], cache["n_last"], codes.shape[2], block, f_lo,
+                               f_hi, flags, global_scale.data_ptr(), head.data_ptr(),
+                               tail.data_ptr(), codes.data_ptr(), scales.data_ptr(), _stream(dev))
+    else:
+        st = L.nvfp4_kv_append_rht(kv_new.data_ptr(), _dtype(kv_new), B, H, T, t_new, D,
+                                   cache["n_first"], cache["n_last"], codes.shape[2], block, f_lo,
+                                   f_hi, flags, ctypes.addressof(sw), global_scale.data_ptr(),
+                                   head.data_ptr(), tail.data_ptr(), codes.data_ptr(),
+                                   scales.data_ptr(), _stream(dev))
     _check("nvfp4_kv_append", st)
     cache["length"] = T + t_new
     return cache

@@ -110,3 +110,16 @@ def test_binding_refuses_cpu_tensors(lib):
 
     with pytest.raises(ValueError):
         nv.quantize(torch.zeros(4, 64))
+
+
+def test_rht_argument_checks(lib):
+    w = (ctypes.c_uint32 * 4)(1, 2, 3, 4)
+    sp = ctypes.addressof(w)
+    assert lib.nvfp4_hadamard128_rht(P, 1, 4, None, P, None) == 1   # signs required
+    assert lib.nvfp4_hadamard128_rht(P, 0, 4, sp, P, None) == 1     # bf16 only
+    assert lib.nvfp4_hadamard128_rht(P, 1, -1, sp, P, None) == 2
+    q = lib.nvfp4_quantize_rht
+    assert q(P, 1, 4, 256, 16, -2, 6, 0, None, P, P, P, P, 1 << 20, None) == 1
+    assert q(P, 0, 4, 256, 16, -2, 6, 0, sp, P, P, P, P, 1 << 20, None) == 1   # FP32 input
+    assert q(P, 1, 4, 192, 16, -2, 6, 0, sp, P, P, P, P, 1 << 20, None) == 2   # cols % 128
+    assert lib.nvfp4_global_scale_rht(P, 1, 4, 256, 0, None, P, P, 1 << 20, None) == 1
