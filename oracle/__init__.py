@@ -20,4 +20,7 @@ from .oracle import (  # noqa: F401
     hadamard128,
     hadamard128_rht,
     quantize_rht,
+    quantize_mxfp4,
+    dequantize_mxfp4,
+    mx_block_sse,
 )

@@ -720,3 +720,184 @@ void oracle_e4m3_encode_batch(const float *t, int64_t n, int16_t *out)
     for (int64_t i = 0; i < n; ++i)
         out[i] = (int16_t)oracle_e4m3_encode(t[i]);
 }
+
+/* ======================================================================== */
+/* MXFP4, the power-of-two contrast format ([NV]: NVFP4's E4M3 block scale   */
+/* and FP32 tensor scale are set against MXFP4's plain power-of-two          */
+/* scaling). The pages define MXFP4 no further; reading (the published OCP   */
+/* Microscaling v1.0 format): blocks of 32 consecutive elements share one    */
+/* E8M0 scale byte b = X + 127 standing for 2^X (X in -127..127; 255 is     */
+/* NaN); elements are E2M1 codes as above; there is no tensor scale. The     */
+/* spec's scale rule is X = floor(log2 amax) - 2 (2 = the exponent of E2M1's */
+/* largest value, 6 = 1.5 * 2^2), clamped to -127; an all-zero block takes   */
+/* X = -127. Elements are coded as y = |x| * 2^-X, nearest-even, saturating  */
+/* at 6 (so a block amax in (6, 8) * 2^X clips). ScaleSearch carried over:   */
+/* candidates X + f, f in [f_lo, f_hi] (an E8M0 pattern step doubles the     */
+/* scale), ranked by the same left-to-right FP32 squared error over the 32   */
+/* elements, f = 0 first, first strictly smaller wins; X + f outside         */
+/* -127..127 is skipped. [0, 0] is the plain OCP conversion.                 */
+/* ======================================================================== */
+
+/* floor(log2 a) for finite a > 0: a = m * 2^e with m in [0.5, 1). */
+static int floor_log2(float a)
+{
+    int e;
+    frexpf(a, &e);
+    return e - 1;
+}
+
+/* Squared error of coding the 32 magnitudes ax[] with scale 2^X. Both 2^X and
+ * 2^-X are exact binary32 values for X in -127..127, and every reconstruction
+ * V * 2^X (V an E2M1 value, at least 0.5 unless 0) is exact. */
+static float mx_block_sse(const float ax[32], int X, uint8_t mag_codes[32])
+{
+    float d = ldexpf(1.0f, X);
+    float r = ldexpf(1.0f, -X);
+    float sse = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        float y = ax[i] * r;
+        int c = oracle_e2m1_code(y);
+        float xhat = E2M1_MAG[c] * d;
+        float e = ax[i] - xhat;
+        float q = e * e;
+        sse = (i == 0) ? q : sse + q;
+        if (mag_codes)
+            mag_codes[i] = (uint8_t)c;
+    }
+    return sse;
+}
+
+/* One block: 16 code bytes, returns the scale byte (255 for a non-finite block). */
+static int mx_search_block(const float x[32], int f_lo, int f_hi, uint8_t out[16])
+{
+    float ax[32], amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        if (!isfinite(x[i])) {
+            memset(out, 0, 16);
+            return 255;
+        }
+        ax[i] = fabsf(x[i]);
+        if (ax[i] > amax)
+            amax = ax[i];
+    }
+    int X0 = amax > 0.0f ? floor_log2(amax) - 2 : -127;
+    if (X0 < -127)
+        X0 = -127;
+    uint8_t best_codes[32];
+    int best_X = X0;
+    float best = mx_block_sse(ax, X0, best_codes);
+    for (int f = f_lo; f <= f_hi; ++f) {
+        int X = X0 + f;
+        if (f == 0 || X < -127 || X > 127)
+            continue;
+        uint8_t c[32];
+        float e = mx_block_sse(ax, X, c);
+        if (e < best) {
+            best = e;
+            best_X = X;
+            memcpy(best_codes, c, 32);
+        }
+    }
+    for (int i = 0; i < 16; ++i) {
+        int lo = best_codes[2 * i] | (signbit(x[2 * i]) ? 8 : 0);
+        int hi = best_codes[2 * i + 1] | (signbit(x[2 * i + 1]) ? 8 : 0);
+        out[i] = (uint8_t)(lo | (hi << 4));
+    }
+    return best_X + 127;
+}
+
+typedef struct {
+    const void *x;
+    int dtype;
+    int64_t cols, r0, r1;
+    int f_lo, f_hi;
+    uint8_t *codes, *scales;
+} mxjob_t;
+
+static void *mx_rows(void *arg)
+{
+    const mxjob_t *J = (const mxjob_t *)arg;
+    int64_t nb = J->cols / 32;
+    for (int64_t r = J->r0; r < J->r1; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            float x[32];
+            for (int i = 0; i < 32; ++i)
+                x[i] = load_elem(J->x, J->dtype, r * J->cols + b * 32 + i);
+            J->scales[r * nb + b] =
+                (uint8_t)mx_search_block(x, J->f_lo, J->f_hi, J->codes + r * (J->cols / 2) + b * 16);
+        }
+    return NULL;
+}
+
+/* MXFP4 quantize of x[rows][cols] (cols % 32 == 0): codes[rows][cols/2] (even
+ * element in the low nibble), scales[rows][cols/32] (E8M0 bytes). */
+int oracle_quantize_mxfp4(const void *x, int dtype, int64_t rows, int64_t cols, int f_lo, int f_hi,
+                          uint8_t *codes, uint8_t *scales, int nthreads)
+{
+    if (rows < 0 || cols <= 0 || cols % 32 || f_lo > 0 || f_hi < 0 ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    if (rows == 0)
+        return ORACLE_OK;
+    if (!x || !codes || !scales)
+        return ORACLE_EINVAL;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nthreads > rows)
+        nthreads = (int)rows;
+    pthread_t th[256];
+    int running[256];
+    mxjob_t jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (mxjob_t){x, dtype, cols, rows * t / nthreads, rows * (t + 1) / nthreads,
+                            f_lo, f_hi, codes, scales};
+        running[t] = nthreads > 1 && pthread_create(&th[t], NULL, mx_rows, &jobs[t]) == 0;
+        if (!running[t])
+            mx_rows(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (running[t])
+            pthread_join(th[t], NULL);
+    return ORACLE_OK;
+}
+
+/* Inverse: y = V * 2^(b - 127) in FP32 (exact), NaN for scale byte 255;
+ * out_dtype BF16 rounds that value to nearest-even. */
+int oracle_dequantize_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                            int64_t cols, int out_dtype, void *y)
+{
+    if (rows < 0 || cols <= 0 || cols % 32 || (out_dtype != ORACLE_F32 && out_dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    if (rows == 0)
+        return ORACLE_OK;
+    if (!codes || !scales || !y)
+        return ORACLE_EINVAL;
+    for (int64_t e = 0; e < rows * cols; ++e) {
+        int nib = (codes[e / 2] >> ((e & 1) * 4)) & 0xF;
+        int b = scales[e / 32];
+        float v;
+        if (b == 255)
+            v = NAN;
+        else {
+            v = E2M1_MAG[nib & 7] * ldexpf(1.0f, b - 127);
+            if (nib & 8)
+                v = -v;
+        }
+        if (out_dtype == ORACLE_F32)
+            ((float *)y)[e] = v;
+        else
+            ((uint16_t *)y)[e] = float_to_bf16_rne(v);
+    }
+    return ORACLE_OK;
+}
+
+/* Squared error of one 32-element block at scale 2^X (for the pins). */
+float oracle_mx_block_sse(const float x[32], int X)
+{
+    float ax[32];
+    for (int i = 0; i < 32; ++i)
+        ax[i] = fabsf(x[i]);
+    return mx_block_sse(ax, X, NULL);
+}

@@ -78,6 +78,12 @@ def lib() -> ctypes.CDLL:
             L.oracle_hadamard128_rht.restype = i32
             L.oracle_quantize_rht.argtypes = [vp, i32, i64, i64, vp, i32, i32, i32, vp, vp, vp, i32]
             L.oracle_quantize_rht.restype = i32
+            L.oracle_quantize_mxfp4.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, i32]
+            L.oracle_quantize_mxfp4.restype = i32
+            L.oracle_dequantize_mxfp4.argtypes = [vp, vp, i64, i64, i32, vp]
+            L.oracle_dequantize_mxfp4.restype = i32
+            L.oracle_mx_block_sse.argtypes = [vp, i32]
+            L.oracle_mx_block_sse.restype = f32
             _lib = L
     return _lib
 
@@ -241,3 +247,37 @@ def quantize_rht(x: np.ndarray, signs, f_lo: int = -8, f_hi: int = 8, gscale: fl
         raise ValueError(f"oracle_quantize_rht failed ({rc})")
     shp = x.shape[:-1]
     return codes.reshape(*shp, K // 2), scales.reshape(*shp, K // 16), np.float32(g[0])
+
+
+def quantize_mxfp4(x: np.ndarray, f_lo: int = 0, f_hi: int = 0, nthreads: int | None = None):
+    """MXFP4 (32-element blocks, E8M0 scales): (codes[R, K/2] u8, scales[R, K/32] u8)."""
+    x = np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    K = x.shape[-1]
+    R = x.size // K
+    codes = np.empty((R, K // 2), dtype=np.uint8)
+    scales = np.empty((R, K // 32), dtype=np.uint8)
+    rc = lib().oracle_quantize_mxfp4(_ptr(x), dt, R, K, f_lo, f_hi, _ptr(codes), _ptr(scales),
+                                     _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_quantize_mxfp4 failed ({rc})")
+    shp = x.shape[:-1]
+    return codes.reshape(*shp, K // 2), scales.reshape(*shp, K // 32)
+
+
+def dequantize_mxfp4(codes: np.ndarray, scales: np.ndarray, out: str = "f32"):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    K = codes.shape[-1] * 2
+    R = codes.size * 2 // K
+    odt = F32 if out == "f32" else BF16
+    y = np.empty(codes.shape[:-1] + (K,), dtype=np.float32 if odt == F32 else np.uint16)
+    rc = lib().oracle_dequantize_mxfp4(_ptr(codes), _ptr(scales), R, K, odt, _ptr(y))
+    if rc:
+        raise ValueError(f"oracle_dequantize_mxfp4 failed ({rc})")
+    return y
+
+
+def mx_block_sse(x32, X: int) -> float:
+    x = np.ascontiguousarray(x32, dtype=np.float32).reshape(32)
+    return float(np.float32(lib().oracle_mx_block_sse(_ptr(x), int(X))))

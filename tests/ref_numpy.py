@@ -195,3 +195,62 @@ def quantize_ref_search(x: np.ndarray, f_lo: int, f_hi: int, sg=None):
     nib = (best_c.astype(np.uint8) | sign).reshape(-1)
     codes = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8).reshape(R, K // 2)
     return codes, best_p.astype(np.uint8).reshape(R, K // 16), sg, best_f.reshape(R, K // 16)
+
+
+# --- MXFP4 contrast format (32-element blocks, E8M0 power-of-two scales) ---
+
+def mx_sse_all_exponents(ax: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """ax [nb, 32] float32 magnitudes -> (sse [nb, 255] float32 for X = -127..127,
+    codes [nb, 255, 32])."""
+    ax = np.asarray(ax, dtype=np.float32)
+    nb = ax.shape[0]
+    sse = np.empty((nb, 255), dtype=np.float32)
+    codes = np.empty((nb, 255, 32), dtype=np.int8)
+    G32 = _G.astype(np.float32)
+    with np.errstate(over="ignore", under="ignore"):
+        for k, X in enumerate(range(-127, 128)):
+            d = np.float32(2.0 ** X)
+            r = np.float32(2.0 ** -X)
+            y = (ax * r).astype(np.float32)
+            c = e2m1_nearest(y)
+            xh = (G32[c] * d).astype(np.float32)
+            e = (ax - xh).astype(np.float32)
+            q = (e * e).astype(np.float32)
+            s = q[:, 0].copy()
+            for i in range(1, 32):
+                s = (s + q[:, i]).astype(np.float32)
+            sse[:, k] = s
+            codes[:, k, :] = c
+    return sse, codes
+
+
+def mx_quantize_ref(x: np.ndarray, f_lo: int, f_hi: int):
+    """x [R, K] float32 (finite) -> (codes [R, K/2], scales [R, K/32] E8M0 bytes):
+    every exponent scored, then the first strictly smaller SSE in the visiting
+    order f = 0, f_lo..f_hi around X0 = floor(log2 amax) - 2."""
+    x = np.asarray(x, dtype=np.float32)
+    R, K = x.shape
+    blocks = x.reshape(-1, 32)
+    ax = np.abs(blocks)
+    amax = ax.max(axis=1).astype(np.float64)
+    with np.errstate(divide="ignore"):
+        X0 = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    X0 = np.maximum(X0, -127).astype(np.int64)
+    sse, allc = mx_sse_all_exponents(ax)
+    nb = blocks.shape[0]
+    rows = np.arange(nb)
+    best_X = X0.copy()
+    best_s = sse[rows, X0 + 127]
+    for f in [f for f in range(f_lo, f_hi + 1) if f != 0]:
+        X = X0 + f
+        ok = (X >= -127) & (X <= 127)
+        Xc = np.clip(X, -127, 127)
+        s = sse[rows, Xc + 127]
+        win = ok & (s < best_s)
+        best_X = np.where(win, Xc, best_X)
+        best_s = np.where(win, s, best_s)
+    mag = allc[rows, best_X + 127, :].astype(np.uint8)
+    sign = np.signbit(blocks).astype(np.uint8) << 3
+    nib = (mag | sign).reshape(-1)
+    codes = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8).reshape(R, K // 2)
+    return codes, (best_X + 127).astype(np.uint8).reshape(R, K // 32)
