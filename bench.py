@@ -281,6 +281,85 @@ def kv_append_table(torch, nv, workloads, iters: int = 200):
               f"{nbytes / (ms * 1e-3) / 1e9:.1f} |", flush=True)
 
 
+def formats_table(torch, nv, workloads, iters: int = 50):
+    """Markdown tables: relative quantization error (sum (x - x^)^2 / sum x^2) of NVFP4
+    max scaling, NVFP4 ScaleSearch and MXFP4 (OCP rule and exponent search) on every
+    workload (whole tensor, no sinks), the Hadamard variants on the 128-wide ones, and
+    the MXFP4 kernels' times."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    signs = np.random.default_rng(12345).integers(0, 2**32, 4, dtype=np.uint64).astype(np.uint32)
+
+    def rel(yhat, ref, den):
+        return float(((yhat.double() - ref.double()) ** 2).sum().item()) / den
+
+    rows, times = [], []
+    for idx in (1, 2, 3, 4, 5):
+        w = workloads.WORKLOADS[idx]
+        xh = workloads.workload(idx)
+        if xh.dtype == np.uint16:
+            x = torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16).to(dev)
+            esz = 2
+        else:
+            x = torch.from_numpy(xh).to(dev)
+            esz = 4
+        x = x.reshape(-1, x.shape[-1])
+        xf = x.float()
+        den = float((xf.double() ** 2).sum().item())
+        e = {}
+        for offs in ((0, 0), (-2, 6), (-8, 8)):
+            c, s, g = nv.quantize(x, offs)
+            e[f"nv{offs}"] = rel(nv.dequantize(c, s, g), xf, den)
+        for offs in ((0, 0), (-1, 1)):
+            c, s = nv.mxfp4_quantize(x, offs)
+            e[f"mx{offs}"] = rel(nv.mxfp4_dequantize(c, s), xf, den)
+        if esz == 2 and x.shape[-1] % 128 == 0:
+            for name, kw in (("had", {}), ("rht", {"signs": signs})):
+                yr = nv.hadamard128(x, **kw)
+                dy = float((yr.double() ** 2).sum().item())
+                c, s, g = nv.quantize(x, (-8, 8), hadamard=not kw, **kw)
+                e[f"nv_{name}"] = rel(nv.dequantize(c, s, g), yr, dy)
+                c, s = nv.mxfp4_quantize(yr, (0, 0))
+                e[f"mx_{name}"] = rel(nv.mxfp4_dequantize(c, s), yr, dy)
+        rows.append((idx, w["name"], e))
+        n = x.numel()
+        qb = n * esz + n // 2 + n // 32
+        db = n // 2 + n // 32 + n * 4
+        c, s = nv.mxfp4_quantize(x, (0, 0))
+        t = {"q0": event_time_ms(torch, lambda: nv.mxfp4_quantize(x, (0, 0)), iters, stream),
+             "q1": event_time_ms(torch, lambda: nv.mxfp4_quantize(x, (-1, 1)), iters, stream),
+             "d": event_time_ms(torch, lambda: nv.mxfp4_dequantize(c, s), iters, stream)}
+        times.append((idx, w["name"], t, qb, db))
+        del xf
+
+    f = lambda v: f"{v:.3e}" if v is not None else "—"
+    print("| # | workload | NVFP4 max scaling | NVFP4 ScaleSearch [-2,6] | NVFP4 SS [-8,8] | "
+          "MXFP4 (OCP rule) | MXFP4 search [-1,1] | NVFP4 SS [-2,6] error below MXFP4 OCP |")
+    print("|---|---|---|---|---|---|---|---|")
+    for idx, name, e in rows:
+        red = 1.0 - e["nv(-2, 6)"] / e["mx(0, 0)"]
+        print(f"| {idx} | {name} | {f(e['nv(0, 0)'])} | {f(e['nv(-2, 6)'])} | "
+              f"{f(e['nv(-8, 8)'])} | {f(e['mx(0, 0)'])} | {f(e['mx(-1, 1)'])} | "
+              f"{100 * red:.1f}% |")
+    print()
+    print("| # | NVFP4 SS [-8,8] after Hadamard | after randomized Hadamard | "
+          "MXFP4 after Hadamard | after randomized Hadamard |")
+    print("|---|---|---|---|---|")
+    for idx, name, e in rows:
+        if "nv_had" in e:
+            print(f"| {idx} | {f(e['nv_had'])} | {f(e['nv_rht'])} | {f(e['mx_had'])} | "
+                  f"{f(e['mx_rht'])} |")
+    print()
+    gbs = lambda b, m: b / (m * 1e-3) / 1e9
+    print("| # | MXFP4 quantize [0,0] us (GB/s) | MXFP4 quantize [-1,1] us (GB/s) | "
+          "MXFP4 dequantize to FP32 us (GB/s) |")
+    print("|---|---|---|---|")
+    for idx, name, t, qb, db in times:
+        print(f"| {idx} | {t['q0'] * 1e3:.1f} ({gbs(qb, t['q0']):.0f}) | "
+              f"{t['q1'] * 1e3:.1f} ({gbs(qb, t['q1']):.0f}) | "
+              f"{t['d'] * 1e3:.1f} ({gbs(db, t['d']):.0f}) |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,6 +375,9 @@ def main():
                     help="print a markdown table timing KV-cache appends (no JSON line)")
     ap.add_argument("--workloads", action="store_true",
                     help="print a markdown table timing all five workloads (no JSON line)")
+    ap.add_argument("--formats", action="store_true",
+                    help="print markdown tables of NVFP4 vs MXFP4 quantization error and the "
+                         "MXFP4 kernel times (no JSON line)")
     ap.add_argument("--rocpd-summary", nargs="+", metavar="DB",
                     help="print a text summary of rocprofv3 databases of a --profile run")
     args = ap.parse_args()
@@ -319,6 +401,9 @@ def main():
         return
     if args.kv_append:
         kv_append_table(torch, nv, workloads)
+        return
+    if args.formats:
+        formats_table(torch, nv, workloads)
         return
     dev = torch.device("cuda:0")
     print(f"[bench] generating workload 4 ({ROWS}x{COLS} bf16)", file=sys.stderr, flush=True)

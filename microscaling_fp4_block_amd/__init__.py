@@ -13,6 +13,8 @@ from .nvfp4 import (  # noqa: F401
     kv_append,
     kv_cache_alloc,
     load,
+    mxfp4_dequantize,
+    mxfp4_quantize,
     quantize,
     quantize_kv_sink,
     workspace_bytes,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/mxfp4.h"
 #include "../../include/nvfp4.h"
 #include "nvfp4_internal.h"
 
@@ -483,6 +484,32 @@ nvfp4_status nvfp4_hadamard128_rht(const void *x, nvfp4_dtype xdt, int64_t rows,
                                    const uint32_t *signs, float *y, void *stream) {
   if (!signs) return NVFP4_EINVAL;
   return hadamard_impl(x, xdt, rows, signs, y, stream);
+}
+
+nvfp4_status mxfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                            int block, int f_lo, int f_hi, uint8_t *codes, uint8_t *scales,
+                            void *stream) {
+  if (!dtype_ok(xdt) || block != 32) return NVFP4_EINVAL;
+  if (f_lo > 0 || f_hi < 0 || f_lo < -8 || f_hi > 8) return NVFP4_EINVAL;
+  if (rows < 0 || cols <= 0 || cols % 32) return NVFP4_ESHAPE;
+  if (cols > (1ll << 30) || (rows > 0 && rows > kMaxBlocks / (cols / 16))) return NVFP4_ESHAPE;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !codes || !scales) return NVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return NVFP4_EALIGN;
+  MxArgs a{x, codes, scales, (uint32_t)(rows * (cols / 32)), f_lo, f_hi};
+  return hip_status(launch_mx_quantize(a, xdt == NVFP4_BF16, (hipStream_t)stream));
+}
+
+nvfp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                              int64_t cols, int block, void *y, nvfp4_dtype ydt, void *stream) {
+  if (!dtype_ok(ydt) || block != 32) return NVFP4_EINVAL;
+  if (rows < 0 || cols <= 0 || cols % 32) return NVFP4_ESHAPE;
+  if (cols > (1ll << 30) || (rows > 0 && rows > kMaxBlocks / (cols / 16))) return NVFP4_ESHAPE;
+  if (rows == 0) return NVFP4_OK;
+  if (!codes || !scales || !y) return NVFP4_EINVAL;
+  if (!aligned(codes, 16) || !aligned(y, 16)) return NVFP4_EALIGN;
+  MxDequantArgs a{codes, scales, y, (uint32_t)(rows * (cols / 32))};
+  return hip_status(launch_mx_dequantize(a, ydt == NVFP4_BF16, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -130,6 +130,25 @@ hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s);
 int amax_hadamard_groups(uint32_t nblocks);
 hipError_t launch_amax_hadamard(const AmaxArgs &a, int groups, hipStream_t s);
 hipError_t launch_quantize_hadamard(const QuantArgs &a, hipStream_t s);
+// MXFP4 contrast format: 32-element blocks, E8M0 scale bytes.
+struct MxArgs {
+  const void *x;
+  uint8_t *codes;
+  uint8_t *scales;
+  uint32_t nblocks;
+  int f_lo, f_hi;
+};
+
+struct MxDequantArgs {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  void *y;
+  uint32_t nblocks;
+};
+
+hipError_t launch_mx_quantize(const MxArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_mx_dequantize(const MxDequantArgs &a, bool out_bf16, hipStream_t s);
+
 hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, const HadamardSigns &hs,
                            hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s);

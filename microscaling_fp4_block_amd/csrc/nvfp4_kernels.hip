@@ -960,6 +960,179 @@ __global__ __launch_bounds__(kThreads) void dequantize_kv_kernel(DequantKvArgs a
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 contrast format (power-of-two block scaling, set against NVFP4 on
+// "NVIDIAのFP4推論が50倍の効率を実現", 超低精度推論を支えるアーキテクチャ). Read as
+// the OCP Microscaling format: 32 elements share one E8M0 byte b = X + 127
+// (2^X, 255 = NaN); X0 = floor(log2 amax) - 2, at least -127 (-127 for an
+// all-zero block); elements are E2M1 of x * 2^-X, nearest-even, saturating.
+// With a non-trivial offset range the ScaleSearch rule runs over exponents:
+// X0 + f, f = 0 first, least left-to-right FP32 squared error, first strictly
+// smaller wins. One lane per block; 2^X and 2^-X are exact (2^-127 is
+// subnormal) and so is every reconstruction V * 2^X.
+// ---------------------------------------------------------------------------
+
+// 2^k for k in -127..127, exact.
+__device__ __forceinline__ float pow2_exact(int k) {
+  return k >= -126 ? __uint_as_float((uint32_t)(k + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Codes of the 32 signed elements at scale 2^X; returns the squared error
+// when SSE (sum of fl(fl(|x| - |x^|)^2), left to right).
+template <bool SSE>
+__device__ __forceinline__ float mx_candidate(const float (&x)[32], int X, uint32_t (&cw)[4]) {
+  const float r = pow2_exact(-X), d = pow2_exact(X);
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 8 * q + 2 * j;
+      w = fp4_encode_pair(w, x[i] * r, x[i + 1] * r, j);
+      if (SSE) {
+        const f32x2 v = fp4_decode_pair(w, j);
+        const float e0 = fabsf(x[i]) - fabsf(v.x * d);
+        const float e1 = fabsf(x[i + 1]) - fabsf(v.y * d);
+        const float q0 = e0 * e0;
+        s = s + q0;
+        const float q1 = e1 * e1;
+        s = s + q1;
+      }
+    }
+    cw[q] = w;
+  }
+  return s;
+}
+
+template <bool BF16, bool SEARCH>
+__global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxArgs a) {
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.nblocks; b += stride) {
+    float x[32];
+    uint32_t amb = 0u;
+    if (BF16) {
+      const uint4 *p = (const uint4 *)((const uint16_t *)a.x + (uint64_t)b * 32u);
+      uint4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = load_stream(p + q);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[8 * q + 2 * k] = __uint_as_float(w[k] << 16);
+          x[8 * q + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+          amb = max(amb, (w[k] << 16) & 0x7FFFFFFFu);
+          amb = max(amb, w[k] & 0x7FFF0000u);
+        }
+      }
+    } else {
+      const uint4 *p = (const uint4 *)((const float *)a.x + (uint64_t)b * 32u);
+      uint4 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = load_stream(p + q);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[4 * q + k] = __uint_as_float(w[k]);
+          amb = max(amb, w[k] & 0x7FFFFFFFu);
+        }
+      }
+    }
+    uint32_t cw[4];
+    uint32_t byte;
+    if (amb >= 0x7F800000u) {  // NaN or Inf in the block
+      cw[0] = cw[1] = cw[2] = cw[3] = 0u;
+      byte = 255u;
+    } else {
+      int X0 = -127;
+      if (amb != 0u) {
+        const int e = amb >= 0x00800000u ? (int)(amb >> 23) - 127 : (31 - (int)__clz(amb)) - 149;
+        X0 = max(e - 2, -127);
+      }
+      int bestX = X0;
+      if (SEARCH) {
+        float best = mx_candidate<true>(x, X0, cw);
+        for (int f = a.f_lo; f <= a.f_hi; ++f) {
+          const int X = X0 + f;
+          if (f == 0 || X < -127 || X > 127) continue;
+          uint32_t c[4];
+          const float e = mx_candidate<true>(x, X, c);
+          if (e < best) {
+            best = e;
+            bestX = X;
+            cw[0] = c[0];
+            cw[1] = c[1];
+            cw[2] = c[2];
+            cw[3] = c[3];
+          }
+        }
+      } else {
+        mx_candidate<false>(x, X0, cw);
+      }
+      byte = (uint32_t)(bestX + 127);
+    }
+    store_stream(a.codes + (uint64_t)b * 16u, cw[0], cw[1], cw[2], cw[3]);
+    a.scales[b] = (uint8_t)byte;
+  }
+}
+
+// One lane per 16-byte output chunk (8 bf16 or 4 FP32), as the NVFP4 inverse.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void mx_dequantize_kernel(MxDequantArgs a) {
+  constexpr uint32_t EPU = OUT_BF16 ? 8u : 4u;
+  constexpr uint32_t SHIFT = OUT_BF16 ? 2u : 3u;  // log2(chunks per 32-element block)
+  constexpr int UNROLL = 4;
+  const uint32_t nunits = a.nblocks << SHIFT;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < nunits; u0 += UNROLL * stride) {
+    uint32_t cw[UNROLL];
+    uint32_t sb[UNROLL];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+      const uint32_t u = u0 + k * stride;
+      cw[k] = 0u;
+      sb[k] = 0u;
+      if (u < nunits) {
+        const uint32_t b = u >> SHIFT, part = u & ((1u << SHIFT) - 1u);
+        if (OUT_BF16)
+          cw[k] = *(const uint32_t *)(a.codes + (uint64_t)b * 16u + part * 4u);
+        else
+          cw[k] = *(const uint16_t *)(a.codes + (uint64_t)b * 16u + part * 2u);
+        sb[k] = a.scales[b];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+      const uint32_t u = u0 + k * stride;
+      if (u < nunits) {
+        const float d = sb[k] == 255u ? __uint_as_float(0x7FC00000u) : pow2_exact((int)sb[k] - 127);
+        float o[EPU];
+#pragma unroll
+        for (int j = 0; j < (int)EPU / 2; ++j) {
+          const f32x2 v = fp4_decode_pair(cw[k], j);
+          o[2 * j] = v.x * d;
+          o[2 * j + 1] = v.y * d;
+        }
+        if (OUT_BF16) {
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w[j] = __builtin_bit_cast(uint32_t,
+                                      __builtin_convertvector((f32x2{o[2 * j], o[2 * j + 1]}), bf16x2));
+          store_stream((uint16_t *)a.y + (uint64_t)u * EPU, w[0], w[1], w[2], w[3]);
+        } else {
+          store_stream((float *)a.y + (uint64_t)u * EPU, __float_as_uint(o[0]), __float_as_uint(o[1]),
+                       __float_as_uint(o[2]), __float_as_uint(o[3]));
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
 
@@ -1032,6 +1205,33 @@ hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, const Had
     hipLaunchKernelGGL(hadamard_kernel<true>, dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs);
   else
     hipLaunchKernelGGL(hadamard_kernel<false>, dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize(const MxArgs &a, bool bf16, hipStream_t s) {
+  const int g = grid_for(a.nblocks, kMaxQuantGroups);
+  const bool search = a.f_lo != 0 || a.f_hi != 0;
+  if (bf16) {
+    if (search)
+      hipLaunchKernelGGL((mx_quantize_kernel<true, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((mx_quantize_kernel<true, false>), dim3(g), dim3(kThreads), 0, s, a);
+  } else {
+    if (search)
+      hipLaunchKernelGGL((mx_quantize_kernel<false, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((mx_quantize_kernel<false, false>), dim3(g), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_dequantize(const MxDequantArgs &a, bool out_bf16, hipStream_t s) {
+  const uint64_t units = (uint64_t)a.nblocks << (out_bf16 ? 2 : 3);
+  const int g = grid_for(units / 4u, kMaxStreamGroups);  // four chunks in flight per lane
+  if (out_bf16)
+    hipLaunchKernelGGL(mx_dequantize_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(mx_dequantize_kernel<false>, dim3(g), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -47,6 +47,8 @@ SIGNATURES = {
     "nvfp4_kv_append_rht": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32,
                              _i32, _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "nvfp4_hadamard128_rht": ([_vp, _i32, _i64, _vp, _vp, _vp], _i32),
+    "mxfp4_quantize": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
+    "mxfp4_dequantize": ([_vp, _vp, _i64, _i64, _i32, _vp, _i32, _vp], _i32),
 }
 
 _lock = threading.Lock()
@@ -326,3 +328,35 @@ def kv_append(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor, off
     _check("nvfp4_kv_append", st)
     cache["length"] = T + t_new
     return cache
+
+
+def mxfp4_quantize(x: torch.Tensor, offsets=(0, 0), block: int = 32):
+    """MXFP4 (32-element blocks, E8M0 power-of-two scales) of x: returns
+    (codes uint8[..., K/2], scales uint8[..., K/32]); offsets search the exponent."""
+    L = load()
+    dev = _dev(x)
+    K = x.shape[-1]
+    R = x.numel() // K if K else 0
+    f_lo, f_hi = _offsets(offsets)
+    codes = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(*x.shape[:-1], K // 32, dtype=torch.uint8, device=dev)
+    st = L.mxfp4_quantize(x.data_ptr(), _dtype(x), R, K, block, f_lo, f_hi, codes.data_ptr(),
+                          scales.data_ptr(), _stream(dev))
+    _check("mxfp4_quantize", st)
+    return codes, scales
+
+
+def mxfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.float32,
+                     block: int = 32, out: torch.Tensor | None = None):
+    L = load()
+    dev = _dev(codes)
+    _dev(scales)
+    K = codes.shape[-1] * 2
+    R = codes.numel() * 2 // K if K else 0
+    if scales.numel() * 32 != R * K:
+        raise ValueError("codes and scales sizes disagree")
+    y = out if out is not None else torch.empty(*codes.shape[:-1], K, dtype=out_dtype, device=dev)
+    st = L.mxfp4_dequantize(codes.data_ptr(), scales.data_ptr(), R, K, block, y.data_ptr(),
+                            _dtype(y), _stream(dev))
+    _check("mxfp4_dequantize", st)
+    return y

@@ -1,13 +1,14 @@
-"""The C-ABI library loads and exports every symbol include/nvfp4.h declares, and
+"""The C-ABI library loads and exports every symbol include/*.h declares, and
 rejects bad arguments on the host (no GPU needed: checks run before any launch)."""
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -20,15 +21,19 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        names |= set(re.findall(r"NVFP4_API\s+[^;(]*?\b((?:nvfp4|mxfp4)_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_quantize_kv_sink",
               "nvfp4_dequantize_kv_sink", "nvfp4_hadamard128", "nvfp4_workspace_bytes",
-              "nvfp4_status_str", "nvfp4_abi_version", "nvfp4_global_scale"]:
+              "nvfp4_status_str", "nvfp4_abi_version", "nvfp4_global_scale",
+              "nvfp4_kv_append", "nvfp4_quantize_rht", "mxfp4_quantize", "mxfp4_dequantize"]:
         assert n in names
 
 
@@ -123,3 +128,19 @@ def test_rht_argument_checks(lib):
     assert q(P, 0, 4, 256, 16, -2, 6, 0, sp, P, P, P, P, 1 << 20, None) == 1   # FP32 input
     assert q(P, 1, 4, 192, 16, -2, 6, 0, sp, P, P, P, P, 1 << 20, None) == 2   # cols % 128
     assert lib.nvfp4_global_scale_rht(P, 1, 4, 256, 0, None, P, P, 1 << 20, None) == 1
+
+
+def test_mxfp4_argument_checks(lib):
+    q = lib.mxfp4_quantize
+    assert q(P, 1, 4, 256, 16, 0, 0, P, P, None) == 1    # block must be 32
+    assert q(P, 1, 4, 256, 32, -9, 0, P, P, None) == 1   # offsets within +-8
+    assert q(P, 1, 4, 256, 32, 1, 2, P, P, None) == 1    # 0 inside the range
+    assert q(P, 1, 4, 240, 32, 0, 0, P, P, None) == 2    # cols % 32
+    assert q(P, 1, -1, 256, 32, 0, 0, P, P, None) == 2
+    assert q(None, 1, 4, 256, 32, 0, 0, P, P, None) == 1
+    assert q(P + 8, 1, 4, 256, 32, 0, 0, P, P, None) == 3
+    assert q(P, 1, 0, 256, 32, 0, 0, None, None, None) == 0   # empty: nothing to do
+    d = lib.mxfp4_dequantize
+    assert d(P, P, 4, 256, 16, P, 0, None) == 1
+    assert d(P, P, 4, 250, 32, P, 0, None) == 2
+    assert d(P, P, 4, 256, 32, P + 4, 0, None) == 3
