@@ -23,4 +23,5 @@ from .oracle import (  # noqa: F401
     quantize_mxfp4,
     dequantize_mxfp4,
     mx_block_sse,
+    attention_nvfp4,
 )

@@ -901,3 +901,247 @@ float oracle_mx_block_sse(const float x[32], int X)
         ax[i] = fabsf(x[i]);
     return mx_block_sse(ax, X, NULL);
 }
+
+/* ======================================================================== */
+/* Attention on NVFP4 operands ([SSA]: ScaleSearchAttention computes QK^T    */
+/* and PV with NVFP4 operands and FP32 accumulation; IP and the sink cache   */
+/* are applied to the operands beforehand).                                  */
+/*                                                                           */
+/* Readings (the pages give no kernel): Q, K, V are NVFP4 tensors           */
+/* [B][H][N][D] with 16-element blocks along D, each with its own tensor     */
+/* scale; K and V heads may be shared by Hq / Hkv query heads. Operand       */
+/* values are V[code] * s_block (exact in binary32), the tensor scales are   */
+/* applied to the products. Online softmax over key tiles of `tile` keys in  */
+/* order: s_j = tau * Sq * Sk * (q . k_j), tau = 1/sqrt(D); m' = max(m,      */
+/* max_j s_j); p_j = exp(s_j - m') rounded to binary32; l = e^(m-m') l +     */
+/* sum_j p_j. P is quantized to NVFP4 per 16 keys of the tile with max      */
+/* scaling (offset 0) under the fixed tensor scale S_P = fl(1/2688) (the    */
+/* largest possible p is 1), exactly as the quantizer codes a block, and     */
+/* acc = e^(m-m') acc + sum_j P^_j v_j, with P^_j = V[code] * s_block. The   */
+/* output is O = acc * S_P * Sv / l. Keys past Nk are masked; with causal,   */
+/* query i sees keys j <= i + Nk - Nq.                                       */
+/*                                                                           */
+/* Besides O the oracle returns, per output element, the magnitude sum       */
+/* mag = S_P Sv / l * sum |P^_j v_jd| (rescaled like acc) and an allowance    */
+/* `bound` for P codes that a binary32 implementation may round the other    */
+/* way: an element whose y = p_j * r lies within the relative error that     */
+/* binary32 scores and exp can put on p_j of an E2M1 rounding midpoint may   */
+/* take the neighbouring code, and a block whose scale argument lies that    */
+/* close to an E4M3 midpoint may take the neighbouring scale; bound sums the */
+/* largest such changes of P^_j times |v_jd|.                                */
+/* ======================================================================== */
+
+static void decode_row(const uint8_t *codes, const uint8_t *scales, int64_t D, float *out)
+{
+    for (int64_t d = 0; d < D; ++d) {
+        int nib = (codes[d / 2] >> ((d & 1) * 4)) & 0xF;
+        float v = E2M1_MAG[nib & 7] * oracle_e4m3_value(scales[d / 16]);
+        out[d] = (nib & 8) ? -v : v;
+    }
+}
+
+/* Relative distance of y from the nearest E2M1 rounding midpoint, and the
+ * gap between the two grid values on either side of it. */
+static double e2m1_mid_distance(float y, float *gap)
+{
+    static const float MID[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+    static const float GAP[7] = {0.5f, 0.5f, 0.5f, 0.5f, 1.0f, 1.0f, 2.0f};
+    double best = INFINITY;
+    for (int k = 0; k < 7; ++k) {
+        double dd = fabs((double)y - MID[k]) / MID[k];
+        if (dd < best) {
+            best = dd;
+            *gap = GAP[k];
+        }
+    }
+    return best;
+}
+
+typedef struct {
+    const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
+    float qg, kg, vg;
+    int64_t B, Hq, Hkv, Nq, Nk, D, tile;
+    int causal;
+    double *O, *mag, *bound;
+    int64_t r0, r1; /* rows (b, h, i) of this job */
+} ajob_t;
+
+static void *attention_rows(void *arg)
+{
+    const ajob_t *J = (const ajob_t *)arg;
+    const int64_t D = J->D, Nk = J->Nk, T = J->tile;
+    const float SP = 1.0f / 2688.0f;
+    const double c = (1.0 / sqrt((double)D)) * (double)J->qg * (double)J->kg;
+    float *q = malloc(sizeof(float) * D);
+    float *kv = malloc(sizeof(float) * D * (size_t)(Nk > 0 ? Nk : 1));
+    float *vv = malloc(sizeof(float) * D * (size_t)(Nk > 0 ? Nk : 1));
+    double *acc = malloc(sizeof(double) * D), *mg = malloc(sizeof(double) * D);
+    double *bd = malloc(sizeof(double) * D);
+    double *s = malloc(sizeof(double) * T), *A = malloc(sizeof(double) * T);
+    float *pf = malloc(sizeof(float) * T), *ph = malloc(sizeof(float) * T);
+    double *dl = malloc(sizeof(double) * T);
+    int64_t cached_head = -1;
+    for (int64_t r = J->r0; r < J->r1; ++r) {
+        int64_t i = r % J->Nq, bh = r / J->Nq;
+        int64_t b = bh / J->Hq, h = bh % J->Hq;
+        int64_t kvh = b * J->Hkv + h / (J->Hq / J->Hkv);
+        if (kvh != cached_head) {
+            for (int64_t j = 0; j < Nk; ++j) {
+                int64_t row = kvh * Nk + j;
+                decode_row(J->kc + row * (D / 2), J->ks + row * (D / 16), D, kv + j * D);
+                decode_row(J->vc + row * (D / 2), J->vs + row * (D / 16), D, vv + j * D);
+            }
+            cached_head = kvh;
+        }
+        decode_row(J->qc + r * (D / 2), J->qs + r * (D / 16), D, q);
+        int64_t jmax = J->causal ? i + Nk - J->Nq : Nk - 1; /* last visible key */
+        double m = -INFINITY, l = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            acc[d] = mg[d] = bd[d] = 0.0;
+        for (int64_t t0 = 0; t0 < Nk; t0 += T) {
+            double mt = -INFINITY, amax_abs = 0.0;
+            for (int64_t u = 0; u < T; ++u) {
+                int64_t j = t0 + u;
+                s[u] = -INFINITY;
+                A[u] = 0.0;
+                if (j < Nk && j <= jmax) {
+                    double dot = 0.0, ab = 0.0;
+                    for (int64_t d = 0; d < D; ++d) {
+                        double pr = (double)q[d] * (double)kv[j * D + d];
+                        dot += pr;
+                        ab += fabs(pr);
+                    }
+                    s[u] = c * dot;
+                    A[u] = c * ab;
+                    if (s[u] > mt)
+                        mt = s[u];
+                    if (A[u] > amax_abs)
+                        amax_abs = A[u];
+                }
+            }
+            double mn = m > mt ? m : mt;
+            if (mn == -INFINITY)
+                continue; /* nothing visible yet */
+            double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
+            double psum = 0.0;
+            for (int64_t u = 0; u < T; ++u) {
+                pf[u] = (s[u] == -INFINITY) ? 0.0f : (float)exp(s[u] - mn);
+                psum += pf[u];
+                /* relative error a binary32 score and exp can put on p */
+                dl[u] = amax_abs * (double)(D + 2) * 0x1p-24 + (fabs(s[u]) + fabs(mn)) * 0x1p-21 +
+                        0x1p-20;
+                if (s[u] == -INFINITY)
+                    dl[u] = 0.0;
+            }
+            l = alpha * l + psum;
+            for (int64_t d = 0; d < D; ++d) {
+                acc[d] *= alpha;
+                mg[d] *= alpha;
+                bd[d] *= alpha;
+            }
+            for (int64_t u0 = 0; u0 < T; u0 += 16) {
+                uint8_t cb[8];
+                int p = search_block(pf + u0, SP, 0, 0, cb, NULL);
+                float sp = oracle_e4m3_value(p);
+                float r = 1.0f / (sp * SP);
+                float amax_b = 0.0f;
+                double dmax = 0.0;
+                for (int e = 0; e < 16; ++e) {
+                    int nib = (cb[e / 2] >> ((e & 1) * 4)) & 0xF;
+                    ph[u0 + e] = E2M1_MAG[nib & 7] * sp;
+                    if (pf[u0 + e] > amax_b)
+                        amax_b = pf[u0 + e];
+                    if (dl[u0 + e] > dmax)
+                        dmax = dl[u0 + e];
+                }
+                /* allowance per element */
+                double flip[16];
+                for (int e = 0; e < 16; ++e) {
+                    flip[e] = 0.0;
+                    float gap = 0.0f;
+                    float y = pf[u0 + e] * r;
+                    if (pf[u0 + e] > 0.0f && e2m1_mid_distance(y, &gap) <= dl[u0 + e] + 0x1p-22)
+                        flip[e] = (double)gap * sp;
+                }
+                /* the block scale: t within reach of an E4M3 midpoint */
+                float tb = (amax_b / 6.0f) / SP;
+                if (amax_b > 0.0f) {
+                    for (int nb = -1; nb <= 1; nb += 2) {
+                        int p2 = p + nb;
+                        if (p2 < 0 || p2 > 126)
+                            continue;
+                        double mid = 0.5 * ((double)oracle_e4m3_value(p) + oracle_e4m3_value(p2));
+                        if (fabs((double)tb - mid) <= (dmax + 0x1p-21) * mid) {
+                            float sp2 = oracle_e4m3_value(p2);
+                            float r2 = 1.0f / (sp2 * SP);
+                            for (int e = 0; e < 16; ++e) {
+                                int c2 = oracle_e2m1_code(pf[u0 + e] * r2);
+                                double alt = (double)E2M1_MAG[c2] * sp2;
+                                double dv = fabs(alt - ph[u0 + e]) + 2.0 * sp2; /* and its own flips */
+                                if (dv > flip[e])
+                                    flip[e] = dv;
+                            }
+                        }
+                    }
+                }
+                for (int e = 0; e < 16; ++e) {
+                    int64_t j = t0 + u0 + e;
+                    if (j >= Nk || pf[u0 + e] == 0.0f)
+                        continue;
+                    for (int64_t d = 0; d < D; ++d) {
+                        double v = vv[j * D + d];
+                        acc[d] += (double)ph[u0 + e] * v;
+                        mg[d] += (double)ph[u0 + e] * fabs(v);
+                        bd[d] += flip[e] * fabs(v);
+                    }
+                }
+            }
+            m = mn;
+        }
+        double f = (l > 0.0) ? (double)SP * (double)J->vg / l : 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            J->O[r * D + d] = acc[d] * f;
+            if (J->mag)
+                J->mag[r * D + d] = mg[d] * f;
+            if (J->bound)
+                J->bound[r * D + d] = bd[d] * f;
+        }
+    }
+    free(q); free(kv); free(vv); free(acc); free(mg); free(bd);
+    free(s); free(A); free(pf); free(ph); free(dl);
+    return NULL;
+}
+
+int oracle_attention_nvfp4(const uint8_t *qc, const uint8_t *qs, float qg, const uint8_t *kc,
+                           const uint8_t *ks, float kg, const uint8_t *vc, const uint8_t *vs,
+                           float vg, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                           int64_t D, int64_t tile, int causal, double *O, double *mag,
+                           double *bound, int nthreads)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || Nk < 0 || D <= 0 || D % 16 ||
+        tile <= 0 || tile % 16 || !O)
+        return ORACLE_EINVAL;
+    int64_t rows = B * Hq * Nq;
+    if (rows == 0)
+        return ORACLE_OK;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nthreads > rows)
+        nthreads = (int)rows;
+    pthread_t th[256];
+    int running[256];
+    ajob_t jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (ajob_t){qc, qs, kc, ks, vc, vs, qg, kg, vg, B, Hq, Hkv, Nq, Nk, D, tile,
+                           causal, O, mag, bound, rows * t / nthreads, rows * (t + 1) / nthreads};
+        running[t] = nthreads > 1 && pthread_create(&th[t], NULL, attention_rows, &jobs[t]) == 0;
+        if (!running[t])
+            attention_rows(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (running[t])
+            pthread_join(th[t], NULL);
+    return ORACLE_OK;
+}

@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
             L.oracle_dequantize_mxfp4.restype = i32
             L.oracle_mx_block_sse.argtypes = [vp, i32]
             L.oracle_mx_block_sse.restype = f32
+            L.oracle_attention_nvfp4.argtypes = [vp, vp, f32, vp, vp, f32, vp, vp, f32, i64, i64,
+                                                 i64, i64, i64, i64, i64, i32, vp, vp, vp, i32]
+            L.oracle_attention_nvfp4.restype = i32
             _lib = L
     return _lib
 
@@ -281,3 +284,27 @@ def dequantize_mxfp4(codes: np.ndarray, scales: np.ndarray, out: str = "f32"):
 def mx_block_sse(x32, X: int) -> float:
     x = np.ascontiguousarray(x32, dtype=np.float32).reshape(32)
     return float(np.float32(lib().oracle_mx_block_sse(_ptr(x), int(X))))
+
+
+def attention_nvfp4(q, k, v, tile: int = 32, causal: bool = False, nthreads: int | None = None):
+    """Attention on NVFP4 operands. q, k, v: (codes [B,H,N,D/2] u8, scales [B,H,N,D/16] u8,
+    tensor scale); k and v may have fewer heads (shared by groups of query heads).
+    Returns (O, mag, bound) as float64 [B, Hq, Nq, D]."""
+    qc, qs, qg = q
+    kc, ks, kg = k
+    vc, vs, vg = v
+    qc, qs, kc, ks, vc, vs = (np.ascontiguousarray(a, dtype=np.uint8)
+                              for a in (qc, qs, kc, ks, vc, vs))
+    B, Hq, Nq, D2 = qc.shape
+    Hkv, Nk = kc.shape[1], kc.shape[2]
+    D = D2 * 2
+    O = np.empty((B, Hq, Nq, D), np.float64)
+    mag = np.empty_like(O)
+    bound = np.empty_like(O)
+    rc = lib().oracle_attention_nvfp4(_ptr(qc), _ptr(qs), float(qg), _ptr(kc), _ptr(ks), float(kg),
+                                      _ptr(vc), _ptr(vs), float(vg), B, Hq, Hkv, Nq, Nk, D, tile,
+                                      int(causal), _ptr(O), _ptr(mag), _ptr(bound),
+                                      _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_attention_nvfp4 failed ({rc})")
+    return O, mag, bound

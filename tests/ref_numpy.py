@@ -254,3 +254,60 @@ def mx_quantize_ref(x: np.ndarray, f_lo: int, f_hi: int):
     nib = (mag | sign).reshape(-1)
     codes = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8).reshape(R, K // 2)
     return codes, (best_X + 127).astype(np.uint8).reshape(R, K // 32)
+
+
+# --- attention on NVFP4 operands ---
+
+def nvfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """codes [..., D/2], scales [..., D/16] -> float64 values V[code] * s (no tensor scale)."""
+    c = np.asarray(codes, np.uint8)
+    nib = np.stack([c & 0xF, c >> 4], axis=-1).reshape(*c.shape[:-1], c.shape[-1] * 2)
+    mag = _G[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    s = _S[np.minimum(np.asarray(scales, np.int64), 126)]
+    return mag * np.repeat(s, 16, axis=-1)
+
+
+def attention_ref(q, k, v, tile: int = 32, causal: bool = False):
+    """Same readings as the oracle's attention, written with NumPy: online softmax over
+    key tiles, P coded per 16 keys by quantize_ref_search with S_P = fl(1/2688) and
+    offsets [0, 0]. Returns O float64 [B, Hq, Nq, D]."""
+    qd, kd, vd = (nvfp4_decode(t[0], t[1]) for t in (q, k, v))
+    qg, kg, vg = (float(t[2]) for t in (q, k, v))
+    B, Hq, Nq, D = qd.shape
+    Hkv, Nk = kd.shape[1], kd.shape[2]
+    SP = np.float32(1.0) / np.float32(2688.0)
+    c = qg * kg / np.sqrt(D)
+    O = np.zeros((B, Hq, Nq, D))
+    for b in range(B):
+        for h in range(Hq):
+            Q = qd[b, h]
+            K = kd[b, h // (Hq // Hkv)]
+            V = vd[b, h // (Hq // Hkv)]
+            S = (Q @ K.T) * c
+            if causal:
+                vis = np.arange(Nk)[None, :] <= (np.arange(Nq)[:, None] + Nk - Nq)
+                S = np.where(vis, S, -np.inf)
+            m = np.full(Nq, -np.inf)
+            l = np.zeros(Nq)
+            acc = np.zeros((Nq, D))
+            for t0 in range(0, Nk, tile):
+                St = np.full((Nq, tile), -np.inf)
+                w = min(tile, Nk - t0)
+                St[:, :w] = S[:, t0:t0 + w]
+                mn = np.maximum(m, St.max(axis=1))
+                live = mn > -np.inf
+                with np.errstate(invalid="ignore"):
+                    alpha = np.where(np.isfinite(m), np.exp(m - mn), 0.0)
+                    P = np.where(np.isfinite(St), np.exp(St - mn[:, None]), 0.0).astype(np.float32)
+                alpha = np.where(live, alpha, 1.0)
+                P = np.where(live[:, None], P, np.float32(0))
+                l = alpha * l + P.astype(np.float64).sum(axis=1)
+                codes, scales, _, _ = quantize_ref_search(P, 0, 0, sg=SP)
+                Ph = nvfp4_decode(codes, scales)
+                Vt = np.zeros((tile, D))
+                Vt[:w] = V[t0:t0 + w]
+                acc = alpha[:, None] * acc + Ph @ Vt
+                m = np.where(live, mn, m)
+            with np.errstate(invalid="ignore", divide="ignore"):
+                O[b, h] = np.where(l[:, None] > 0, acc * (float(SP) * vg) / l[:, None], 0.0)
+    return O

@@ -1,0 +1,107 @@
+"""Pins of the oracle's attention on NVFP4 operands (ScaleSearch summary page,
+ScaleSearchAttention: QK^T and PV on NVFP4 operands with FP32 accumulation).
+
+The oracle follows the readings stated in its source: operands V[code] * s with
+the tensor scales applied to the products, online softmax over key tiles, P coded
+per 16 keys by max scaling under S_P = fl(1/2688)."""
+import numpy as np
+import pytest
+
+import ref_numpy
+import workloads
+
+
+def quant(orc, x, offsets=(-2, 6)):
+    c, s, g = orc.quantize(x, *offsets)
+    shp = x.shape[:-1]
+    return c.reshape(*shp, -1), s.reshape(*shp, -1), g
+
+
+def operands(orc, B, Hq, Hkv, Nq, Nk, D=128, seed=0):
+    rng = np.random.default_rng(seed)
+    q = workloads.to_bf16_bits(rng.standard_normal((B, Hq, Nq, D)).astype(np.float32))
+    k = workloads.workload(3, (B, Hkv, Nk, D))
+    v = workloads.to_bf16_bits(rng.standard_normal((B, Hkv, Nk, D)).astype(np.float32))
+    return quant(orc, q), quant(orc, k), quant(orc, v)
+
+
+def dequant(t):
+    return ref_numpy.nvfp4_decode(t[0], t[1]) * float(t[2])
+
+
+def test_uniform_scores_give_the_mean(orc):
+    """Q = 0: every score is 0 and every p is 1, which codes as 6 at scale 448
+    under S_P = fl(1/2688); so O is the mean of the dequantized V times
+    2688 * fl(1/2688) (the tensor scale of P is a rounded reciprocal)."""
+    _, k, v = operands(orc, 1, 1, 1, 8, 100)
+    q = quant(orc, np.zeros((1, 1, 8, 128), np.float32))
+    O, mag, bound = orc.attention_nvfp4(q, k, v)
+    ref = dequant(v)[0, 0].mean(axis=0) * (2688.0 * float(np.float32(1) / np.float32(2688)))
+    np.testing.assert_allclose(O[0, 0], np.broadcast_to(ref, (8, 128)), rtol=1e-12, atol=1e-15)
+    assert np.all(bound == 0)
+
+
+def test_dominant_key(orc):
+    """One key aligned with the query and far above the others: O = its value row."""
+    D = 128
+    rng = np.random.default_rng(1)
+    kx = rng.standard_normal((1, 1, 64, D)).astype(np.float32) * 0.01
+    kx[0, 0, 37] = 8.0
+    qx = np.full((1, 1, 1, D), 8.0, np.float32)
+    q, k = quant(orc, qx), quant(orc, kx)
+    _, _, v = operands(orc, 1, 1, 1, 1, 64)
+    O, _, _ = orc.attention_nvfp4(q, k, v)
+    f = 2688.0 * float(np.float32(1) / np.float32(2688))
+    np.testing.assert_allclose(O[0, 0, 0], dequant(v)[0, 0, 37] * f, rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("Nq,Nk,tile,causal", [(40, 100, 32, False), (64, 64, 16, True),
+                                               (33, 130, 64, False), (20, 50, 32, True)])
+def test_matches_numpy_reference(orc, Nq, Nk, tile, causal):
+    q, k, v = operands(orc, 1, 2, 1, Nq, Nk, seed=Nq)
+    O, _, _ = orc.attention_nvfp4(q, k, v, tile=tile, causal=causal)
+    ref = ref_numpy.attention_ref(q, k, v, tile=tile, causal=causal)
+    np.testing.assert_allclose(O, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_causal_equals_truncated(orc):
+    q, k, v = operands(orc, 1, 1, 1, 48, 48, seed=5)
+    O, _, _ = orc.attention_nvfp4(q, k, v, causal=True)
+    for i in (0, 15, 16, 31, 47):
+        qi = tuple(a[:, :, i:i + 1] if a.ndim else a for a in q)
+        ki = tuple(a[:, :, :i + 1] if a.ndim else a for a in k)
+        vi = tuple(a[:, :, :i + 1] if a.ndim else a for a in v)
+        Oi, _, _ = orc.attention_nvfp4(qi, ki, vi)
+        np.testing.assert_array_equal(O[0, 0, i], Oi[0, 0, 0])
+
+
+def test_grouped_heads(orc):
+    q, k, v = operands(orc, 1, 4, 2, 24, 70, seed=7)
+    O, _, _ = orc.attention_nvfp4(q, k, v)
+    for h in range(4):
+        sel = lambda t, hh: (t[0][:, hh:hh + 1], t[1][:, hh:hh + 1], t[2])
+        Oh, _, _ = orc.attention_nvfp4(sel(q, h), sel(k, h // 2), sel(v, h // 2))
+        np.testing.assert_array_equal(O[:, h:h + 1], Oh)
+
+
+def test_close_to_exact_attention(orc):
+    """Against FP64 softmax attention of the dequantized operands (P unquantized): the
+    only difference is P's coding, a few percent of the output's scale."""
+    q, k, v = operands(orc, 1, 1, 1, 64, 256, seed=9)
+    O, _, _ = orc.attention_nvfp4(q, k, v)
+    Q, K, V = dequant(q)[0, 0], dequant(k)[0, 0], dequant(v)[0, 0]
+    S = Q @ K.T / np.sqrt(128)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    ref = (P @ V) / P.sum(axis=1, keepdims=True)
+    err = np.abs(O[0, 0] - ref).max() / np.abs(ref).max()
+    assert err < 0.1, err
+
+
+def test_flip_allowance_is_small_and_present(orc):
+    """The allowance covers only P codes near a rounding midpoint: present on some
+    outputs of a realistic case, and a small part of the magnitude sum."""
+    q, k, v = operands(orc, 1, 2, 1, 64, 512, seed=11)
+    O, mag, bound = orc.attention_nvfp4(q, k, v)
+    assert np.all(bound >= 0) and np.any(bound > 0)
+    assert np.all(bound <= 0.25 * mag + 1e-300)
+    assert np.median(bound / mag) < 0.02
