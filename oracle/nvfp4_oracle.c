@@ -1075,9 +1075,14 @@ static void *attention_rows(void *arg)
                             float sp2 = oracle_e4m3_value(p2);
                             float r2 = 1.0f / (sp2 * SP);
                             for (int e = 0; e < 16; ++e) {
-                                int c2 = oracle_e2m1_code(pf[u0 + e] * r2);
+                                float y2 = pf[u0 + e] * r2, gap2 = 0.0f;
+                                int c2 = oracle_e2m1_code(y2);
                                 double alt = (double)E2M1_MAG[c2] * sp2;
-                                double dv = fabs(alt - ph[u0 + e]) + 2.0 * sp2; /* and its own flips */
+                                double dv = fabs(alt - ph[u0 + e]);
+                                /* and the element's own flip under that scale */
+                                if (pf[u0 + e] > 0.0f &&
+                                    e2m1_mid_distance(y2, &gap2) <= dl[u0 + e] + 0x1p-22)
+                                    dv += (double)gap2 * sp2;
                                 if (dv > flip[e])
                                     flip[e] = dv;
                             }
