@@ -41,7 +41,8 @@ OPS_PER_ELEMENT_CANDIDATE = 5
 SEARCH_KERNEL = "quantize_certified_kernel<-2, 6, true>"
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "quantize_search_bf16_8192x28672.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "microscaling_fp4_block_amd", "csrc", f)
-                  for f in ("nvfp4_kernels.hip", "nvfp4_api.hip", "nvfp4_internal.h")]
+                  for f in ("nvfp4_kernels.hip", "nvfp4_api.hip", "nvfp4_internal.h",
+                            "nvfp4_device.h")]
 
 
 def kernel_source_hash() -> str:

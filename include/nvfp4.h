@@ -170,6 +170,29 @@ NVFP4_API nvfp4_status nvfp4_kv_append(const void *kv_new, nvfp4_dtype dt, int64
 NVFP4_API nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,
                                void *stream);
 
+/* Attention on NVFP4 operands (ScaleSearch summary page, ScaleSearchAttention:
+ * QK^T and PV with NVFP4 operands and FP32 accumulation). q: codes
+ * [B][Hq][Nq][64], scales [B][Hq][Nq][8], tensor scale q_gscale[1]; k and v the
+ * same with Hkv heads and Nk keys (Hq % Hkv == 0: query head h reads K/V head
+ * h / (Hq / Hkv)), as nvfp4_quantize writes them for rows of 128 elements (the
+ * head dimension must be 128). Computes, per query row i,
+ *   s_j = (q_i . k_j) * Sq * Sk / sqrt(128) with q, k the values V[code] * s_block,
+ * an online softmax over tiles of 32 keys (p_j = exp(s_j - m), m the running max),
+ * P coded to NVFP4 per 16 keys of a tile by max scaling under the fixed tensor
+ * scale fl(1/2688), and O_i = (sum_j P^_j v_j) * fl(1/2688) * Sv / l_i, l_i the
+ * sum of the unrounded p_j. causal != 0 masks keys j > i + Nk - Nq (a query with
+ * no visible key gets 0). out: [B][Hq][Nq][128] FP32 or bf16. Products are
+ * exact; sums are FP32 in the matrix units' order, so results agree with an
+ * exact evaluation to FP32 accumulation error plus P codes that round the other
+ * way near a midpoint. All arrays device memory; codes 16-byte aligned. */
+NVFP4_API nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_scales,
+                                       const float *q_gscale, const uint8_t *k_codes,
+                                       const uint8_t *k_scales, const float *k_gscale,
+                                       const uint8_t *v_codes, const uint8_t *v_scales,
+                                       const float *v_gscale, int64_t B, int64_t Hq, int64_t Hkv,
+                                       int64_t Nq, int64_t Nk, int64_t D, int causal, void *out,
+                                       nvfp4_dtype out_dt, void *stream);
+
 /* Randomized Hadamard transform (QuIP#-style incoherence processing, ScaleSearch
  * summary page, ScaleSearchAttention section: a transform pair Q' = Q R^-T,
  * K' = K R that keeps Q K^T while lowering the mean-square absolute value).

@@ -6,6 +6,7 @@ The compute path is the HIP library ``libnvfp4.so`` (C ABI in
 from .nvfp4 import (  # noqa: F401
     LIB_PATH,
     NVFP4Error,
+    attention,
     dequantize,
     dequantize_kv_sink,
     global_scale,

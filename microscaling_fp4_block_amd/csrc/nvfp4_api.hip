@@ -512,4 +512,42 @@ nvfp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64
   return hip_status(launch_mx_dequantize(a, ydt == NVFP4_BF16, (hipStream_t)stream));
 }
 
+nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_scales,
+                             const float *q_gscale, const uint8_t *k_codes,
+                             const uint8_t *k_scales, const float *k_gscale,
+                             const uint8_t *v_codes, const uint8_t *v_scales,
+                             const float *v_gscale, int64_t B, int64_t Hq, int64_t Hkv,
+                             int64_t Nq, int64_t Nk, int64_t D, int causal, void *out,
+                             nvfp4_dtype out_dt, void *stream) {
+  if (!dtype_ok(out_dt)) return NVFP4_EINVAL;
+  if (D != 128) return NVFP4_ESHAPE;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || Nk < 0) return NVFP4_ESHAPE;
+  if (B * Hq > 65535 || Nq > (1ll << 30) || Nk > (1ll << 30)) return NVFP4_ESHAPE;
+  if (B * Hq * Nq > kMaxBlocks / 8 || B * Hkv * Nk > kMaxBlocks / 8) return NVFP4_ESHAPE;
+  if (B * Nq == 0) return NVFP4_OK;
+  if (!q_codes || !q_scales || !q_gscale || !k_gscale || !v_gscale || !out) return NVFP4_EINVAL;
+  if (Nk > 0 && (!k_codes || !k_scales || !v_codes || !v_scales)) return NVFP4_EINVAL;
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(out, 16))
+    return NVFP4_EALIGN;
+  AttnArgs a{};
+  a.qc = q_codes;
+  a.qs = q_scales;
+  a.kc = k_codes;
+  a.ks = k_scales;
+  a.vc = v_codes;
+  a.vs = v_scales;
+  a.qg = q_gscale;
+  a.kg = k_gscale;
+  a.vg = v_gscale;
+  a.o = out;
+  a.B = (uint32_t)B;
+  a.Hq = (uint32_t)Hq;
+  a.Hkv = (uint32_t)Hkv;
+  a.Nq = (uint32_t)Nq;
+  a.Nk = (uint32_t)Nk;
+  a.causal = causal ? 1u : 0u;
+  a.tau_log2e = (float)(1.4426950408889634 / sqrt(128.0));
+  return hip_status(launch_attention(a, out_dt == NVFP4_BF16, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,246 @@
+// nvfp4_attention.hip -- attention whose QK^T and PV products take NVFP4
+// operands (ScaleSearch summary page, ScaleSearchAttention: both products on
+// NVFP4 data with FP32 accumulation; Q and K prepared by incoherence
+// processing, K and V from the sink-aware cache).
+//
+// gfx950's scaled MFMAs take power-of-two (E8M0) block scales only, so the
+// E4M3 block scales cannot ride inside the matrix instruction. Instead every
+// operand element V[code] * s_block is formed exactly in bf16 (a 2-bit by
+// 4-bit significand product), the products run on v_mfma_f32_32x32x16_bf16
+// with FP32 accumulation, and the tensor scales multiply the FP32 results.
+//
+// Per workgroup: 128 queries of one head (4 waves x 32), looping over tiles
+// of 32 keys. Each tile of K (row-major) and V (transposed, key columns
+// swizzled by d >> 4 against bank conflicts) is decoded once into LDS. A wave
+// computes S^T = K Q^T, so each lane holds 16 keys of one query (its lane-pair
+// partner the other 16): the softmax statistics of a query live in one lane
+// pair. Online softmax in base 2 (log2 e folded into the score scale); P is
+// coded to NVFP4 per 16 keys by max scaling under the fixed tensor scale
+// fl(1/2688) and decoded again to exact bf16 values, and O^T += V^T P^T keeps
+// each query's 128 outputs in its lane pair, so the rescale by
+// exp(m - m') is a per-lane multiply. The K index of both PV operands runs
+// over the keys in the order the S^T accumulator holds them.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr uint32_t kAttnD = 128;
+constexpr uint32_t kKeyTile = 32;
+constexpr uint32_t kAttnWaves = 4;
+constexpr uint32_t kQueriesPerGroup = 32 * kAttnWaves;
+constexpr uint32_t kKsStride = kAttnD + 8;     // bf16 per K row in LDS (16-byte pad)
+constexpr uint32_t kVtStride = kKeyTile + 4;   // bf16 per V^T row in LDS (18 dwords)
+
+__device__ __forceinline__ float scale_value(uint32_t p) { return p >= 127u ? NAN : e4m3_value(p); }
+
+// Eight codes of one 32-bit word (element 2j in the low nibble of byte j)
+// times the block scale s, as bf16 (exact: at most 6 significant bits).
+__device__ __forceinline__ bf16x8 decode8(uint32_t w, float s) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x2 v = fp4_decode_pair(w, j);
+    const bf16x2 b = __builtin_convertvector((f32x2{v.x * s, v.y * s}), bf16x2);
+    r[2 * j] = b.x;
+    r[2 * j + 1] = b.y;
+  }
+  return r;
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[kKeyTile * kKsStride];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[kAttnD * kVtStride];
+  __shared__ f32x2 ptbl[128];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6, g = lane >> 5;
+  const uint32_t col = lane & 31u;
+  const uint32_t bh = blockIdx.y;
+  const uint32_t b = bh / a.Hq, h = bh - b * a.Hq;
+  const uint32_t kvh = b * a.Hkv + h / (a.Hq / a.Hkv);
+  const uint32_t q0 = blockIdx.x * kQueriesPerGroup;
+  const uint32_t qi = q0 + wave * 32u + col;
+  const bool qvalid = qi < a.Nq;
+
+  // P's scale table under S_P = fl(1/2688): pattern -> (encode r = fl(1/fl(s * S_P)), s);
+  // a pattern whose r is not finite codes everything as 0 (r = 0).
+  const float SP = 1.0f / 2688.0f;
+  if (tid < 127u) {
+    const float s = e4m3_value(tid);
+    float r = 1.0f / (s * SP);
+    if (!(r < INFINITY)) r = 0.0f;
+    ptbl[tid] = f32x2{r, s};
+  }
+
+  const float c2 = (*a.qg * *a.kg) * a.tau_log2e;  // score scale, base 2
+  const float fo = SP * *a.vg;
+
+  // This lane's B operand of S^T: query qi, elements 16 ks + 8 g .. +7.
+  bf16x8 qf[8];
+  {
+    const uint64_t row = (uint64_t)bh * a.Nq + (qvalid ? qi : 0u);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint32_t w = 0u;
+      float s = 0.0f;
+      if (qvalid) {
+        w = *(const uint32_t *)(a.qc + row * 64u + 8u * ks + 4u * g);
+        s = scale_value(a.qs[row * 8u + ks]);
+      }
+      qf[ks] = decode8(w, s);
+    }
+  }
+
+  uint32_t kend = a.Nk;
+  if (a.causal) {
+    const int64_t qlast = (int64_t)min(q0 + kQueriesPerGroup, a.Nq) - 1;
+    const int64_t last = qlast + (int64_t)a.Nk - (int64_t)a.Nq;
+    kend = last < 0 ? 0u : (uint32_t)min<int64_t>(last + 1, a.Nk);
+  }
+  const int64_t lim = a.causal ? (int64_t)qi + (int64_t)a.Nk - (int64_t)a.Nq : (int64_t)a.Nk - 1;
+  const uint64_t kvrow0 = (uint64_t)kvh * a.Nk;
+
+  f32x16 o[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) o[t] = f32x16{};
+  float m = -INFINITY, l = 0.0f;
+
+  for (uint32_t t0 = 0; t0 < kend; t0 += kKeyTile) {
+    __syncthreads();
+    {
+      // decode the K and V tiles: thread -> key tid >> 3, 16 elements 16c .. 16c + 15
+      const uint32_t key = tid >> 3, c = tid & 7u, j = t0 + key;
+      uint2 kw = make_uint2(0u, 0u), vw = make_uint2(0u, 0u);
+      float ksc = 0.0f, vsc = 0.0f;
+      if (j < a.Nk) {
+        const uint64_t r = kvrow0 + j;
+        kw = *(const uint2 *)(a.kc + r * 64u + 8u * c);
+        vw = *(const uint2 *)(a.vc + r * 64u + 8u * c);
+        ksc = scale_value(a.ks[r * 8u + c]);
+        vsc = scale_value(a.vs[r * 8u + c]);
+      }
+      *(bf16x8 *)&Ks[key * kKsStride + 16u * c] = decode8(kw.x, ksc);
+      *(bf16x8 *)&Ks[key * kKsStride + 16u * c + 8u] = decode8(kw.y, ksc);
+      const bf16x8 v0 = decode8(vw.x, vsc), v1 = decode8(vw.y, vsc);
+      const uint32_t pk = key ^ (c << 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        Vt[(16u * c + e) * kVtStride + pk] = v0[e];
+        Vt[(16u * c + 8u + e) * kVtStride + pk] = v1[e];
+      }
+    }
+    __syncthreads();
+
+    // S^T = K Q^T: sacc[v] = key 8 (v >> 2) + 4 g + (v & 3) of the tile, query qi.
+    f32x16 sacc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 ka = *(const bf16x8 *)&Ks[col * kKsStride + 16u * ks + 8u * g];
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sacc, 0, 0, 0);
+    }
+
+    float p[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const uint32_t key = t0 + 8u * (v >> 2) + 4u * g + (v & 3);
+      const bool vis = key < a.Nk && (int64_t)key <= lim;
+      p[v] = vis ? sacc[v] * c2 : -INFINITY;
+      mt = fmaxf(mt, p[v]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    float alpha = 1.0f;
+    if (mn == -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[v] = 0.0f;
+    } else {
+      alpha = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[v] = exp2f(p[v] - mn);
+    }
+    float ps = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ps += p[v];
+    l = l * alpha + ps;
+    m = mn;
+
+    // P to NVFP4 per 16 keys (keys 16 blk .. +15: 8 in this lane, 8 in its partner),
+    // max scaling, then back to exact bf16 values V[code] * s.
+    bf16x8 pb[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      float am = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, p[8 * blk + e]);
+      am = fmaxf(am, __shfl_xor(am, 32));
+      // p <= 1, so the pattern is at most 126; the clamp only keeps a NaN score
+      // (from a NaN operand scale) inside the table
+      const uint32_t pat = min(e4m3_rne_sat((am / 6.0f) / SP), 126u);
+      const f32x2 rs = ptbl[pat];
+      uint32_t cw = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        cw = fp4_encode_pair(cw, p[8 * blk + 2 * j] * rs.x, p[8 * blk + 2 * j + 1] * rs.x, j);
+      pb[blk] = decode8(cw, rs.y);
+    }
+
+    // O^T = alpha O^T + V^T P^T; o[t][v] = output d = 32 t + 8 (v >> 2) + 4 g + (v & 3).
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+      const uint32_t d = 32u * t + col;
+      const uint32_t sw = (d >> 4) << 2;
+      const __bf16 *vrow = &Vt[d * kVtStride];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const uint2 x0 = *(const uint2 *)(vrow + ((16u * blk + 4u * g) ^ sw));
+        const uint2 x1 = *(const uint2 *)(vrow + ((16u * blk + 8u + 4u * g) ^ sw));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk], o[t], 0, 0, 0);
+      }
+    }
+  }
+
+  l = l + __shfl_xor(l, 32);
+  if (!qvalid) return;
+  const float f = l > 0.0f ? fo / l : 0.0f;
+  const uint64_t row = (uint64_t)bh * a.Nq + qi;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint32_t d0 = 32u * t + 8u * q4 + 4u * g;
+      const float y0 = o[t][4 * q4] * f, y1 = o[t][4 * q4 + 1] * f;
+      const float y2 = o[t][4 * q4 + 2] * f, y3 = o[t][4 * q4 + 3] * f;
+      if (OUT_BF16) {
+        const bf16x2 lo = __builtin_convertvector((f32x2{y0, y1}), bf16x2);
+        const bf16x2 hi = __builtin_convertvector((f32x2{y2, y3}), bf16x2);
+        *(uint2 *)((uint16_t *)a.o + row * kAttnD + d0) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      } else {
+        *(float4 *)((float *)a.o + row * kAttnD + d0) = make_float4(y0, y1, y2, y3);
+      }
+    }
+  }
+}
+
+hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s) {
+  const dim3 grid((a.Nq + kQueriesPerGroup - 1) / kQueriesPerGroup, a.B * a.Hq);
+  if (out_bf16)
+    hipLaunchKernelGGL(attention_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attention_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

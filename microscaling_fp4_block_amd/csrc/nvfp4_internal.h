@@ -146,6 +146,18 @@ struct MxDequantArgs {
   uint32_t nblocks;
 };
 
+// Attention on NVFP4 operands (head dimension 128).
+struct AttnArgs {
+  const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;  // codes [rows][64], scales [rows][8]
+  const float *qg, *kg, *vg;                   // device tensor scales
+  void *o;                                     // [B][Hq][Nq][128] FP32 or bf16
+  uint32_t B, Hq, Hkv, Nq, Nk;
+  uint32_t causal;
+  float tau_log2e;                             // log2(e) / sqrt(128)
+};
+
+hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s);
+
 hipError_t launch_mx_quantize(const MxArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_mx_dequantize(const MxDequantArgs &a, bool out_bf16, hipStream_t s);
 

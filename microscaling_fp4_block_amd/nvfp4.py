@@ -47,6 +47,8 @@ SIGNATURES = {
     "nvfp4_kv_append_rht": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32,
                              _i32, _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "nvfp4_hadamard128_rht": ([_vp, _i32, _i64, _vp, _vp, _vp], _i32),
+    "nvfp4_attention": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                         _i64, _i64, _i32, _vp, _i32, _vp], _i32),
     "mxfp4_quantize": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "mxfp4_dequantize": ([_vp, _vp, _i64, _i64, _i32, _vp, _i32, _vp], _i32),
 }
@@ -359,4 +361,28 @@ def mxfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.
     st = L.mxfp4_dequantize(codes.data_ptr(), scales.data_ptr(), R, K, block, y.data_ptr(),
                             _dtype(y), _stream(dev))
     _check("mxfp4_dequantize", st)
+    return y
+
+
+def attention(q, k, v, causal: bool = False, out_dtype=torch.float32):
+    """Attention on NVFP4 operands. q, k, v: (codes [B, H, N, 64], scales [B, H, N, 8],
+    global_scale float32[1]) as ``quantize`` returns them for [B, H, N, 128] tensors;
+    k and v may have fewer heads than q. Returns O [B, Hq, Nq, 128]."""
+    L = load()
+    qc, qs, qg = q
+    kc, ks, kg = k
+    vc, vs, vg = v
+    dev = _dev(qc)
+    for t in (qs, qg, kc, ks, kg, vc, vs, vg):
+        _dev(t)
+    if qc.dim() != 4 or kc.dim() != 4 or vc.shape != kc.shape:
+        raise ValueError("q, k, v codes must be [B, H, N, 64] with matching k and v")
+    B, Hq, Nq, D2 = qc.shape
+    Hkv, Nk = kc.shape[1], kc.shape[2]
+    y = torch.empty(B, Hq, Nq, D2 * 2, dtype=out_dtype, device=dev)
+    st = L.nvfp4_attention(qc.data_ptr(), qs.data_ptr(), qg.data_ptr(), kc.data_ptr(),
+                           ks.data_ptr(), kg.data_ptr(), vc.data_ptr(), vs.data_ptr(),
+                           vg.data_ptr(), B, Hq, Hkv, Nq, Nk, D2 * 2, int(causal), y.data_ptr(),
+                           _dtype(y), _stream(dev))
+    _check("nvfp4_attention", st)
     return y

@@ -144,3 +144,15 @@ def test_mxfp4_argument_checks(lib):
     assert d(P, P, 4, 256, 16, P, 0, None) == 1
     assert d(P, P, 4, 250, 32, P, 0, None) == 2
     assert d(P, P, 4, 256, 32, P + 4, 0, None) == 3
+
+
+def test_attention_argument_checks(lib):
+    f = lib.nvfp4_attention
+    base = [P] * 9
+    assert f(*base, 1, 2, 1, 64, 64, 64, 0, P, 0, None) == 2     # head dimension must be 128
+    assert f(*base, 1, 3, 2, 64, 64, 128, 0, P, 0, None) == 2    # Hq % Hkv
+    assert f(*base, 1, 2, 1, -1, 64, 128, 0, P, 0, None) == 2
+    assert f(*base, 1, 2, 1, 64, 64, 128, 0, P, 7, None) == 1    # output dtype
+    assert f(*([None] + [P] * 8), 1, 2, 1, 64, 64, 128, 0, P, 0, None) == 1
+    assert f(*base, 1, 2, 1, 64, 64, 128, 0, P + 8, 0, None) == 3
+    assert f(*base, 1, 2, 1, 0, 64, 128, 0, P, 0, None) == 0     # no queries: nothing to do

@@ -1,0 +1,149 @@
+"""GPU parity of attention on NVFP4 operands (ScaleSearch summary page,
+ScaleSearchAttention: QK^T and PV with NVFP4 operands and FP32 accumulation).
+
+The operands are coded by the oracle (so no input comes from the HIP path) and
+uploaded. The kernel's products are exact but its sums run in FP32 in the
+matrix units' order, and its P codes come from binary32 scores and exp, so the
+bar is a per-element bound derived from that arithmetic (u = 2^-24):
+
+  |O_gpu - O| <= mag * (Nk + 8 * tiles + 64) u        (FP32 sums of P^ v, rescales)
+               + |O| * (delta + (Nk + 64) u)          (the softmax sum l)
+               + bound                                (P codes that may round the other way)
+
+with O, mag and bound from the oracle and delta the relative error the scores
+and exp can put on a p (the oracle's own allowance formula)."""
+import numpy as np
+import pytest
+import torch
+
+import ref_numpy
+import workloads
+from gpu_util import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def coded(orc, x):
+    c, s, g = orc.quantize(x, -2, 6)
+    shp = x.shape[:-1]
+    return c.reshape(*shp, 64), s.reshape(*shp, 8), g
+
+
+def make_ops(orc, B, Hq, Hkv, Nq, Nk, seed):
+    rng = np.random.default_rng(seed)
+    q = workloads.to_bf16_bits(rng.standard_normal((B, Hq, Nq, 128)).astype(np.float32))
+    k = workloads.workload(3, (B, Hkv, Nk, 128))
+    v = workloads.to_bf16_bits(rng.standard_normal((B, Hkv, Nk, 128)).astype(np.float32))
+    return coded(orc, q), coded(orc, k), coded(orc, v)
+
+
+def upload(t):
+    c, s, g = t
+    return (torch.from_numpy(np.ascontiguousarray(c)).cuda(),
+            torch.from_numpy(np.ascontiguousarray(s)).cuda(),
+            torch.tensor([g], dtype=torch.float32, device="cuda:0"))
+
+
+def score_delta(q, k):
+    """Largest relative error binary32 scores and exp can put on a p (the oracle's formula)."""
+    Q = ref_numpy.nvfp4_decode(q[0], q[1])
+    K = ref_numpy.nvfp4_decode(k[0], k[1])
+    c = float(q[2]) * float(k[2]) / np.sqrt(128.0)
+    Hq, Hkv = Q.shape[1], K.shape[1]
+    worst = 0.0
+    for h in range(Hq):
+        Qh, Kh = Q[:, h], K[:, h // (Hq // Hkv)]
+        A = np.einsum("bid,bjd->bij", np.abs(Qh), np.abs(Kh)) * c
+        S = np.einsum("bid,bjd->bij", Qh, Kh) * c
+        worst = max(worst, float(A.max(initial=0.0)) * 130 * U + 2 * float(np.abs(S).max(initial=0.0))
+                    * 2.0 ** -21 + 2.0 ** -20)
+    return worst
+
+
+def check(gpu, orc, q, k, v, causal=False, out_dtype=torch.float32):
+    Nk = k[0].shape[2]
+    print(f"[case] attention q={q[0].shape} k={k[0].shape} causal={causal} out={out_dtype}",
+          flush=True)
+    O = gpu.attention(upload(q), upload(k), upload(v), causal=causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    got = to_host(O.float()).astype(np.float64)
+    ref, mag, bound = orc.attention_nvfp4(q, k, v, tile=32, causal=causal)
+    tiles = -(-Nk // 32)
+    delta = score_delta(q, k)
+    tol = mag * (Nk + 8 * tiles + 64) * U + np.abs(ref) * (delta + (Nk + 64) * U) + bound
+    if out_dtype == torch.bfloat16:
+        tol = tol + np.abs(ref) * 2.0 ** -8
+    err = np.abs(got - ref)
+    ratio = float(np.max(err / np.maximum(tol, 1e-300)))
+    print(f"[attention] max err/tol {ratio:.3f}, max err {err.max():.3e}, "
+          f"elements with a flip allowance {np.mean(bound > 0):.4f}")
+    bad = err > tol
+    assert not bad.any(), f"{bad.sum()} elements outside the bound; first at {np.argwhere(bad)[0]}"
+    return got, ref
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk", [(1, 2, 1, 300, 1000), (2, 1, 1, 128, 32),
+                                             (1, 4, 2, 77, 513), (1, 1, 1, 1, 5)])
+def test_parity(gpu, orc, B, Hq, Hkv, Nq, Nk):
+    check(gpu, orc, *make_ops(orc, B, Hq, Hkv, Nq, Nk, seed=Nq + Nk))
+
+
+@pytest.mark.parametrize("Nq,Nk", [(257, 257), (100, 300), (300, 100)])
+def test_causal(gpu, orc, Nq, Nk):
+    check(gpu, orc, *make_ops(orc, 1, 2, 2, Nq, Nk, seed=Nq * 3 + Nk), causal=True)
+
+
+def test_bf16_output(gpu, orc):
+    check(gpu, orc, *make_ops(orc, 1, 1, 1, 200, 400, seed=3), out_dtype=torch.bfloat16)
+
+
+def test_hadamard_operands(gpu, orc):
+    """Q and K coded after the same randomized Hadamard transform (their product is
+    unchanged): the attention of the transformed operands, same bar."""
+    rng = np.random.default_rng(8)
+    signs = rng.integers(0, 2**32, 4, dtype=np.uint64).astype(np.uint32)
+    qx = workloads.workload(5, (1, 4, 200, 128))
+    kx = workloads.workload(3, (1, 1, 700, 128))
+    vx = workloads.to_bf16_bits(rng.standard_normal((1, 1, 700, 128)).astype(np.float32))
+
+    def rht(x):
+        c, s, g = orc.quantize_rht(x, signs, -8, 8)
+        return c.reshape(*x.shape[:-1], 64), s.reshape(*x.shape[:-1], 8), g
+
+    check(gpu, orc, rht(qx), rht(kx), coded(orc, vx))
+
+
+def test_no_keys_and_no_queries(gpu, orc):
+    q, k, v = make_ops(orc, 1, 1, 1, 40, 0, seed=1)
+    O = gpu.attention(upload(q), upload(k), upload(v))
+    torch.cuda.synchronize()
+    assert torch.all(O == 0)
+    q, k, v = make_ops(orc, 1, 1, 1, 0, 64, seed=2)
+    O = gpu.attention(upload(q), upload(k), upload(v))
+    assert O.shape == (1, 1, 0, 128)
+
+
+def test_full_size_sampled_rows(gpu, orc):
+    """Q [1, 32, 32768, 128] against K, V [1, 8, 32768, 128] (grouped heads), non-causal,
+    the benchmark's launch; the oracle evaluates 4 sampled query rows of every head."""
+    rng = np.random.default_rng(17)
+    qx = workloads.workload(5)
+    kx = workloads.workload(3)
+    vx = workloads.to_bf16_bits(rng.standard_normal(kx.shape).astype(np.float32))
+    q, k, v = coded(orc, qx), coded(orc, kx), coded(orc, vx)
+    O = gpu.attention(upload(q), upload(k), upload(v))
+    torch.cuda.synchronize()
+    got_all = to_host(O)
+    rows = np.sort(rng.choice(32768, 4, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, 32767]]))
+    qs = (q[0][:, :, rows], q[1][:, :, rows], q[2])
+    ref, mag, bound = orc.attention_nvfp4(qs, k, v)
+    got = got_all[:, :, rows].astype(np.float64)
+    Nk = 32768
+    delta = score_delta(qs, k)
+    tol = mag * (Nk + 8 * 1024 + 64) * U + np.abs(ref) * (delta + (Nk + 64) * U) + bound
+    err = np.abs(got - ref)
+    print(f"[attention] full size: max err/tol {float(np.max(err / tol)):.3f}")
+    assert np.all(err <= tol)
