@@ -361,6 +361,56 @@ def formats_table(torch, nv, workloads, iters: int = 50):
               f"{t['d'] * 1e3:.1f} ({gbs(db, t['d']):.0f}) |", flush=True)
 
 
+def attention_table(torch, nv, workloads, iters: int = 5):
+    """Markdown table: attention on NVFP4 operands at 32K, Q [1, 32, 32768, 128] (workload 5
+    recipe) against K [1, 8, 32768, 128] (workload 3 recipe) and V [1, 8, 32768, 128]
+    N(0, 1), grouped heads; against PyTorch's bf16 scaled_dot_product_attention on the
+    unquantized tensors."""
+    import torch.nn.functional as F
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rng = np.random.default_rng(17)
+    qh = workloads.workload(5)
+    kh = workloads.workload(3)
+    vh = workloads.to_bf16_bits(rng.standard_normal(kh.shape).astype(np.float32))
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = bf(qh), bf(kh), bf(vh)
+    signs = rng.integers(0, 2**32, 4, dtype=np.uint64).astype(np.uint32)
+    B, Hq, N, D = q.shape
+    flops = 4.0 * B * Hq * N * N * D
+    quant = {
+        "ScaleSearch, randomized Hadamard on Q and K": lambda: (
+            nv.quantize(q, (-8, 8), signs=signs), nv.quantize(k, (-2, 6), signs=signs),
+            nv.quantize(v, (-2, 6))),
+        "max scaling, no transform": lambda: (
+            nv.quantize(q, (0, 0)), nv.quantize(k, (0, 0)), nv.quantize(v, (0, 0))),
+    }
+    print("| operands | quantize Q, K, V ms | attention ms | attention TFLOP/s | "
+          "fraction of bf16 MFMA peak | causal attention ms |")
+    print("|---|---|---|---|---|---|")
+    for name, fn in quant.items():
+        ops = fn()
+        torch.cuda.synchronize()
+        tq = event_time_ms(torch, fn, iters, stream)
+        attn = lambda: nv.attention(*ops)
+        attn()
+        torch.cuda.synchronize()
+        ta = event_time_ms(torch, attn, iters, stream)
+        tc = event_time_ms(torch, lambda: nv.attention(*ops, causal=True), iters, stream)
+        print(f"| {name} | {tq:.3f} | {ta:.2f} | {flops / (ta * 1e-3) / 1e12:.0f} | "
+              f"{flops / (ta * 1e-3) / 2.5e15:.3f} | {tc:.2f} |", flush=True)
+    try:
+        sdpa = lambda: F.scaled_dot_product_attention(q, k, v, enable_gqa=True)
+        sdpa()
+        torch.cuda.synchronize()
+        ts = event_time_ms(torch, sdpa, iters, stream)
+        print(f"| PyTorch bf16 scaled_dot_product_attention (unquantized) | — | {ts:.2f} | "
+              f"{flops / (ts * 1e-3) / 1e12:.0f} | {flops / (ts * 1e-3) / 2.5e15:.3f} | — |")
+    except Exception as e:  # noqa: BLE001 - report, do not fail the table
+        print(f"| PyTorch bf16 scaled_dot_product_attention | failed: {type(e).__name__} | | | | |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -379,6 +429,9 @@ def main():
     ap.add_argument("--formats", action="store_true",
                     help="print markdown tables of NVFP4 vs MXFP4 quantization error and the "
                          "MXFP4 kernel times (no JSON line)")
+    ap.add_argument("--attention", action="store_true",
+                    help="print a markdown table timing attention on NVFP4 operands at 32K "
+                         "(no JSON line)")
     ap.add_argument("--rocpd-summary", nargs="+", metavar="DB",
                     help="print a text summary of rocprofv3 databases of a --profile run")
     args = ap.parse_args()
@@ -405,6 +458,9 @@ def main():
         return
     if args.formats:
         formats_table(torch, nv, workloads)
+        return
+    if args.attention:
+        attention_table(torch, nv, workloads)
         return
     dev = torch.device("cuda:0")
     print(f"[bench] generating workload 4 ({ROWS}x{COLS} bf16)", file=sys.stderr, flush=True)

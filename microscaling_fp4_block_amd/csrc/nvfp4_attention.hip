@@ -5,9 +5,11 @@
 //
 // gfx950's scaled MFMAs take power-of-two (E8M0) block scales only, so the
 // E4M3 block scales cannot ride inside the matrix instruction. Instead every
-// operand element V[code] * s_block is formed exactly in bf16 (a 2-bit by
-// 4-bit significand product), the products run on v_mfma_f32_32x32x16_bf16
-// with FP32 accumulation, and the tensor scales multiply the FP32 results.
+// operand element V[code] * s_block is formed exactly in fp16 (a 2-bit by
+// 4-bit significand product between 2^-10 and 2688: always a normal fp16),
+// two at a time by the hardware FP4 -> fp16 convert and a packed fp16
+// multiply; the products run on v_mfma_f32_32x32x16_f16 with FP32
+// accumulation, and the tensor scales multiply the FP32 results.
 //
 // Per workgroup: 128 queries of one head (4 waves x 32), looping over tiles
 // of 32 keys. Each tile of K (row-major) and V (transposed, key columns
@@ -16,7 +18,7 @@
 // partner the other 16): the softmax statistics of a query live in one lane
 // pair. Online softmax in base 2 (log2 e folded into the score scale); P is
 // coded to NVFP4 per 16 keys by max scaling under the fixed tensor scale
-// fl(1/2688) and decoded again to exact bf16 values, and O^T += V^T P^T keeps
+// fl(1/2688) and decoded again to exact fp16 values, and O^T += V^T P^T keeps
 // each query's 128 outputs in its lane pair, so the rescale by
 // exp(m - m') is a per-lane multiply. The K index of both PV operands runs
 // over the keys in the order the S^T accumulator holds them.
@@ -29,37 +31,91 @@
 
 namespace nvfp4 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr uint32_t kAttnD = 128;
 constexpr uint32_t kKeyTile = 32;
 constexpr uint32_t kAttnWaves = 4;
 constexpr uint32_t kQueriesPerGroup = 32 * kAttnWaves;
-constexpr uint32_t kKsStride = kAttnD + 8;     // bf16 per K row in LDS (16-byte pad)
-constexpr uint32_t kVtStride = kKeyTile + 4;   // bf16 per V^T row in LDS (18 dwords)
+constexpr uint32_t kKsStride = kAttnD + 8;     // fp16 per K row in LDS (16-byte pad)
+constexpr uint32_t kVtStride = kKeyTile + 4;   // fp16 per V^T row in LDS (18 dwords)
 
 __device__ __forceinline__ float scale_value(uint32_t p) { return p >= 127u ? NAN : e4m3_value(p); }
 
+// Two codes of byte sel of w as fp16 (the byte selector must be a constant).
+__device__ __forceinline__ f16x2 fp4_pair_f16(uint32_t w, int sel) {
+  switch (sel & 3) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
+}
+
 // Eight codes of one 32-bit word (element 2j in the low nibble of byte j)
-// times the block scale s, as bf16 (exact: at most 6 significant bits).
-__device__ __forceinline__ bf16x8 decode8(uint32_t w, float s) {
-  bf16x8 r;
+// times the block scale s, as fp16 (exact: at most 6 significant bits).
+__device__ __forceinline__ f16x8 decode8(uint32_t w, float s) {
+  const _Float16 sh = (_Float16)s;  // E4M3 values are exact in fp16
+  const f16x2 s2 = {sh, sh};
+  f16x8 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const f32x2 v = fp4_decode_pair(w, j);
-    const bf16x2 b = __builtin_convertvector((f32x2{v.x * s, v.y * s}), bf16x2);
-    r[2 * j] = b.x;
-    r[2 * j + 1] = b.y;
+    const f16x2 v = fp4_pair_f16(w, j) * s2;
+    r[2 * j] = v.x;
+    r[2 * j + 1] = v.y;
   }
   return r;
 }
 
+// One tile's raw K and V codes and scales as this thread loads them from
+// memory: key tid >> 3 of the tile, elements 16 c .. 16 c + 15, c = tid & 7.
+struct TileRegs {
+  uint2 kw, vw;
+  uint32_t ksb, vsb;
+};
+
+__device__ __forceinline__ TileRegs load_tile(const AttnArgs &a, uint64_t kvrow0, uint32_t t0,
+                                              uint32_t tid) {
+  TileRegs r{make_uint2(0u, 0u), make_uint2(0u, 0u), 0u, 0u};
+  const uint32_t key = tid >> 3, c = tid & 7u, j = t0 + key;
+  if (j < a.Nk) {
+    const uint64_t row = kvrow0 + j;
+    r.kw = *(const uint2 *)(a.kc + row * 64u + 8u * c);
+    r.vw = *(const uint2 *)(a.vc + row * 64u + 8u * c);
+    r.ksb = a.ks[row * 8u + c];
+    r.vsb = a.vs[row * 8u + c];
+  }
+  return r;
+}
+
+// Decode a loaded tile into LDS: K row-major, V transposed with the key column
+// swizzled by d >> 4.
+__device__ __forceinline__ void store_tile(const TileRegs &r, bool live, uint32_t tid, _Float16 *Ks,
+                                           _Float16 *Vt) {
+  const uint32_t key = tid >> 3, c = tid & 7u;
+  const float ksc = live ? scale_value(r.ksb) : 0.0f;
+  const float vsc = live ? scale_value(r.vsb) : 0.0f;
+  *(f16x8 *)&Ks[key * kKsStride + 16u * c] = decode8(r.kw.x, ksc);
+  *(f16x8 *)&Ks[key * kKsStride + 16u * c + 8u] = decode8(r.kw.y, ksc);
+  const f16x8 v0 = decode8(r.vw.x, vsc), v1 = decode8(r.vw.y, vsc);
+  const uint32_t pk = key ^ (c << 2);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    Vt[(16u * c + e) * kVtStride + pk] = v0[e];
+    Vt[(16u * c + 8u + e) * kVtStride + pk] = v1[e];
+  }
+}
+
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kKeyTile * kKsStride];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[kAttnD * kVtStride];
+__global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
+  // two buffers: tile i is decoded into buffer i & 1 while the codes of tile
+  // i + 1 are in flight, so one barrier per tile suffices
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][kKeyTile * kKsStride];
+  __shared__ __attribute__((aligned(16))) _Float16 Vt[2][kAttnD * kVtStride];
   __shared__ f32x2 ptbl[128];
+  __shared__ float pthr[128];
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6, g = lane >> 5;
   const uint32_t col = lane & 31u;
@@ -79,12 +135,49 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
     if (!(r < INFINITY)) r = 0.0f;
     ptbl[tid] = f32x2{r, s};
   }
+  // The block pattern E4M3(fl(fl(a / 6) / S_P)) is non-decreasing in a, so it is
+  // the number of thresholds pthr[k] <= a, pthr[k] = the least binary32 a whose
+  // pattern is at least k (found by bisection over the bit patterns of a in [0, 1];
+  // p <= 1 puts every block amax there). In the loop a one-multiply estimate
+  // E4M3(fl(a * 448)) is never more than one pattern off (checked over every
+  // binary32 in [0, 1]) and one comparison each way corrects it.
+  if (tid < 128u) {
+    float thr = INFINITY;
+    if (tid == 0u) {
+      thr = 0.0f;
+    } else if (tid < 127u) {
+      uint32_t lo = 0u, hi = 0x3F800000u;
+      while (lo < hi) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        if (e4m3_rne_sat((__uint_as_float(mid) / 6.0f) / SP) >= tid)
+          hi = mid;
+        else
+          lo = mid + 1u;
+      }
+      thr = __uint_as_float(lo);
+    }
+    pthr[tid] = thr;
+  }
 
   const float c2 = (*a.qg * *a.kg) * a.tau_log2e;  // score scale, base 2
   const float fo = SP * *a.vg;
 
+  uint32_t kend = a.Nk;
+  if (a.causal) {
+    const int64_t qlast = (int64_t)min(q0 + kQueriesPerGroup, a.Nq) - 1;
+    const int64_t last = qlast + (int64_t)a.Nk - (int64_t)a.Nq;
+    kend = last < 0 ? 0u : (uint32_t)min<int64_t>(last + 1, a.Nk);
+  }
+  const int64_t lim = a.causal ? (int64_t)qi + (int64_t)a.Nk - (int64_t)a.Nq : (int64_t)a.Nk - 1;
+  // the smallest lim of the wave (its first query), for the unmasked fast path
+  const int64_t lim_wave =
+      a.causal ? (int64_t)(q0 + wave * 32u) + (int64_t)a.Nk - (int64_t)a.Nq : (int64_t)a.Nk - 1;
+  const uint64_t kvrow0 = (uint64_t)kvh * a.Nk;
+
+  TileRegs nxt = load_tile(a, kvrow0, 0u, tid);
+
   // This lane's B operand of S^T: query qi, elements 16 ks + 8 g .. +7.
-  bf16x8 qf[8];
+  f16x8 qf[8];
   {
     const uint64_t row = (uint64_t)bh * a.Nq + (qvalid ? qi : 0u);
 #pragma unroll
@@ -99,73 +192,57 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
     }
   }
 
-  uint32_t kend = a.Nk;
-  if (a.causal) {
-    const int64_t qlast = (int64_t)min(q0 + kQueriesPerGroup, a.Nq) - 1;
-    const int64_t last = qlast + (int64_t)a.Nk - (int64_t)a.Nq;
-    kend = last < 0 ? 0u : (uint32_t)min<int64_t>(last + 1, a.Nk);
-  }
-  const int64_t lim = a.causal ? (int64_t)qi + (int64_t)a.Nk - (int64_t)a.Nq : (int64_t)a.Nk - 1;
-  const uint64_t kvrow0 = (uint64_t)kvh * a.Nk;
-
   f32x16 o[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) o[t] = f32x16{};
   float m = -INFINITY, l = 0.0f;
 
-  for (uint32_t t0 = 0; t0 < kend; t0 += kKeyTile) {
+  uint32_t buf = 0;
+  for (uint32_t t0 = 0; t0 < kend; t0 += kKeyTile, buf ^= 1u) {
+    store_tile(nxt, t0 + (tid >> 3) < a.Nk, tid, Ks[buf], Vt[buf]);
+    if (t0 + kKeyTile < kend) nxt = load_tile(a, kvrow0, t0 + kKeyTile, tid);
     __syncthreads();
-    {
-      // decode the K and V tiles: thread -> key tid >> 3, 16 elements 16c .. 16c + 15
-      const uint32_t key = tid >> 3, c = tid & 7u, j = t0 + key;
-      uint2 kw = make_uint2(0u, 0u), vw = make_uint2(0u, 0u);
-      float ksc = 0.0f, vsc = 0.0f;
-      if (j < a.Nk) {
-        const uint64_t r = kvrow0 + j;
-        kw = *(const uint2 *)(a.kc + r * 64u + 8u * c);
-        vw = *(const uint2 *)(a.vc + r * 64u + 8u * c);
-        ksc = scale_value(a.ks[r * 8u + c]);
-        vsc = scale_value(a.vs[r * 8u + c]);
-      }
-      *(bf16x8 *)&Ks[key * kKsStride + 16u * c] = decode8(kw.x, ksc);
-      *(bf16x8 *)&Ks[key * kKsStride + 16u * c + 8u] = decode8(kw.y, ksc);
-      const bf16x8 v0 = decode8(vw.x, vsc), v1 = decode8(vw.y, vsc);
-      const uint32_t pk = key ^ (c << 2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Vt[(16u * c + e) * kVtStride + pk] = v0[e];
-        Vt[(16u * c + 8u + e) * kVtStride + pk] = v1[e];
-      }
-    }
-    __syncthreads();
+    const _Float16 *K = Ks[buf];
+    const _Float16 *V = Vt[buf];
 
     // S^T = K Q^T: sacc[v] = key 8 (v >> 2) + 4 g + (v & 3) of the tile, query qi.
     f32x16 sacc = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 ka = *(const bf16x8 *)&Ks[col * kKsStride + 16u * ks + 8u * g];
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sacc, 0, 0, 0);
+      const f16x8 ka = *(const f16x8 *)&K[col * kKsStride + 16u * ks + 8u * g];
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], sacc, 0, 0, 0);
     }
 
+    // Base-2 scores s = acc * c2 (c2 > 0, so the max is taken on acc). Full tiles
+    // (every key present and visible to every query of the wave) skip the masks.
     float p[16];
     float mt = -INFINITY;
+    const bool full = t0 + kKeyTile <= a.Nk && (int64_t)(t0 + kKeyTile - 1u) <= lim_wave;
+    if (full) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const uint32_t key = t0 + 8u * (v >> 2) + 4u * g + (v & 3);
-      const bool vis = key < a.Nk && (int64_t)key <= lim;
-      p[v] = vis ? sacc[v] * c2 : -INFINITY;
-      mt = fmaxf(mt, p[v]);
+      for (int v = 0; v < 16; ++v) {
+        p[v] = sacc[v];
+        mt = fmaxf(mt, p[v]);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t key = t0 + 8u * (v >> 2) + 4u * g + (v & 3);
+        const bool vis = key < a.Nk && (int64_t)key <= lim;
+        p[v] = vis ? sacc[v] : -INFINITY;
+        mt = fmaxf(mt, p[v]);
+      }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
     const float mn = fmaxf(m, mt);
     float alpha = 1.0f;
     if (mn == -INFINITY) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) p[v] = 0.0f;
     } else {
-      alpha = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
+      alpha = __builtin_amdgcn_exp2f(m - mn);  // m = -inf gives 0
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = exp2f(p[v] - mn);
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[v], c2, -mn));
     }
     float ps = 0.0f;
 #pragma unroll
@@ -174,8 +251,8 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
     m = mn;
 
     // P to NVFP4 per 16 keys (keys 16 blk .. +15: 8 in this lane, 8 in its partner),
-    // max scaling, then back to exact bf16 values V[code] * s.
-    bf16x8 pb[2];
+    // max scaling, then back to exact fp16 values V[code] * s.
+    f16x8 pb[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       float am = 0.0f;
@@ -184,7 +261,8 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
       am = fmaxf(am, __shfl_xor(am, 32));
       // p <= 1, so the pattern is at most 126; the clamp only keeps a NaN score
       // (from a NaN operand scale) inside the table
-      const uint32_t pat = min(e4m3_rne_sat((am / 6.0f) / SP), 126u);
+      uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
+      pat = am >= pthr[pat + 1u] ? pat + 1u : (am < pthr[pat] ? pat - 1u : pat);
       const f32x2 rs = ptbl[pat];
       uint32_t cw = 0u;
 #pragma unroll
@@ -194,19 +272,24 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
     }
 
     // O^T = alpha O^T + V^T P^T; o[t][v] = output d = 32 t + 8 (v >> 2) + 4 g + (v & 3).
+    // Multiplying by alpha = 1 changes nothing, so the wave skips it when no lane needs it.
+    if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
       const uint32_t d = 32u * t + col;
       const uint32_t sw = (d >> 4) << 2;
-      const __bf16 *vrow = &Vt[d * kVtStride];
+      const _Float16 *vrow = &V[d * kVtStride];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const uint2 x0 = *(const uint2 *)(vrow + ((16u * blk + 4u * g) ^ sw));
         const uint2 x1 = *(const uint2 *)(vrow + ((16u * blk + 8u + 4u * g) ^ sw));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk], o[t], 0, 0, 0);
+        const f16x8 va = __builtin_bit_cast(f16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[blk], o[t], 0, 0, 0);
       }
     }
   }
