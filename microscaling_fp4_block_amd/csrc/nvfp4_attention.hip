@@ -11,9 +11,10 @@
 // multiply; the products run on v_mfma_f32_32x32x16_f16 with FP32
 // accumulation, and the tensor scales multiply the FP32 results.
 //
-// Per workgroup: 128 queries of one head (4 waves x 32), looping over tiles
-// of 32 keys. Each tile of K (row-major) and V (transposed, key columns
-// swizzled by d >> 4 against bank conflicts) is decoded once into LDS. A wave
+// Per workgroup: 128 queries of one head (4 waves x 32), looping over chunks
+// of 64 keys, each decoded once into LDS (K row-major, V transposed with its
+// key columns swizzled against bank conflicts) and consumed as two tiles of
+// 32 keys. A wave
 // computes S^T = K Q^T, so each lane holds 16 keys of one query (its lane-pair
 // partner the other 16): the softmax statistics of a query live in one lane
 // pair. Online softmax in base 2 (log2 e folded into the score scale); P is
@@ -36,11 +37,12 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr uint32_t kAttnD = 128;
-constexpr uint32_t kKeyTile = 32;
+constexpr uint32_t kKeyTile = 32;                // softmax / P-coding tile
+constexpr uint32_t kChunk = 2 * kKeyTile;        // keys decoded into LDS per barrier
 constexpr uint32_t kAttnWaves = 4;
 constexpr uint32_t kQueriesPerGroup = 32 * kAttnWaves;
 constexpr uint32_t kKsStride = kAttnD + 8;     // fp16 per K row in LDS (16-byte pad)
-constexpr uint32_t kVtStride = kKeyTile + 4;   // fp16 per V^T row in LDS (18 dwords)
+constexpr uint32_t kVtStride = kChunk + 4;     // fp16 per V^T row in LDS (34 dwords)
 
 __device__ __forceinline__ float scale_value(uint32_t p) { return p >= 127u ? NAN : e4m3_value(p); }
 
@@ -69,50 +71,56 @@ __device__ __forceinline__ f16x8 decode8(uint32_t w, float s) {
   return r;
 }
 
-// One tile's raw K and V codes and scales as this thread loads them from
-// memory: key tid >> 3 of the tile, elements 16 c .. 16 c + 15, c = tid & 7.
+// One chunk's raw K and V codes and scales as this thread loads them from
+// memory: key tid >> 2 of the chunk, elements 32 c .. 32 c + 31, c = tid & 3.
 struct TileRegs {
-  uint2 kw, vw;
-  uint32_t ksb, vsb;
+  uint4 kw, vw;
+  uint32_t ksb, vsb;  // two scale bytes each
 };
 
-__device__ __forceinline__ TileRegs load_tile(const AttnArgs &a, uint64_t kvrow0, uint32_t t0,
-                                              uint32_t tid) {
-  TileRegs r{make_uint2(0u, 0u), make_uint2(0u, 0u), 0u, 0u};
-  const uint32_t key = tid >> 3, c = tid & 7u, j = t0 + key;
+__device__ __forceinline__ TileRegs load_chunk(const AttnArgs &a, uint64_t kvrow0, uint32_t c0,
+                                               uint32_t tid) {
+  TileRegs r{make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u), 0u, 0u};
+  const uint32_t key = tid >> 2, c = tid & 3u, j = c0 + key;
   if (j < a.Nk) {
     const uint64_t row = kvrow0 + j;
-    r.kw = *(const uint2 *)(a.kc + row * 64u + 8u * c);
-    r.vw = *(const uint2 *)(a.vc + row * 64u + 8u * c);
-    r.ksb = a.ks[row * 8u + c];
-    r.vsb = a.vs[row * 8u + c];
+    r.kw = *(const uint4 *)(a.kc + row * 64u + 16u * c);
+    r.vw = *(const uint4 *)(a.vc + row * 64u + 16u * c);
+    r.ksb = *(const uint16_t *)(a.ks + row * 8u + 2u * c);
+    r.vsb = *(const uint16_t *)(a.vs + row * 8u + 2u * c);
   }
   return r;
 }
 
-// Decode a loaded tile into LDS: K row-major, V transposed with the key column
-// swizzled by d >> 4.
-__device__ __forceinline__ void store_tile(const TileRegs &r, bool live, uint32_t tid, _Float16 *Ks,
-                                           _Float16 *Vt) {
-  const uint32_t key = tid >> 3, c = tid & 7u;
-  const float ksc = live ? scale_value(r.ksb) : 0.0f;
-  const float vsc = live ? scale_value(r.vsb) : 0.0f;
-  *(f16x8 *)&Ks[key * kKsStride + 16u * c] = decode8(r.kw.x, ksc);
-  *(f16x8 *)&Ks[key * kKsStride + 16u * c + 8u] = decode8(r.kw.y, ksc);
-  const f16x8 v0 = decode8(r.vw.x, vsc), v1 = decode8(r.vw.y, vsc);
-  const uint32_t pk = key ^ (c << 2);
+// Decode a loaded chunk into LDS: K row-major [key][d]; V transposed [d][key]
+// with the key column XOR-ed with 16 (d >> 5), which spreads the four lanes
+// that share a key over different banks and keeps 4-key groups contiguous.
+__device__ __forceinline__ void store_chunk(const TileRegs &r, bool live, uint32_t tid,
+                                            _Float16 *Ks, _Float16 *Vt) {
+  const uint32_t key = tid >> 2, c = tid & 3u;
+  const float k0 = live ? scale_value(r.ksb & 0xFFu) : 0.0f;
+  const float k1 = live ? scale_value((r.ksb >> 8) & 0xFFu) : 0.0f;
+  _Float16 *kd = &Ks[key * kKsStride + 32u * c];
+  *(f16x8 *)(kd) = decode8(r.kw.x, k0);
+  *(f16x8 *)(kd + 8) = decode8(r.kw.y, k0);
+  *(f16x8 *)(kd + 16) = decode8(r.kw.z, k1);
+  *(f16x8 *)(kd + 24) = decode8(r.kw.w, k1);
+  const float v0 = live ? scale_value(r.vsb & 0xFFu) : 0.0f;
+  const float v1 = live ? scale_value((r.vsb >> 8) & 0xFFu) : 0.0f;
+  const f16x8 x[4] = {decode8(r.vw.x, v0), decode8(r.vw.y, v0), decode8(r.vw.z, v1),
+                      decode8(r.vw.w, v1)};
+  const uint32_t pk = key ^ (16u * c);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    Vt[(16u * c + e) * kVtStride + pk] = v0[e];
-    Vt[(16u * c + 8u + e) * kVtStride + pk] = v1[e];
-  }
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Vt[(32u * c + 8u * i + e) * kVtStride + pk] = x[i][e];
 }
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // two buffers: tile i is decoded into buffer i & 1 while the codes of tile
   // i + 1 are in flight, so one barrier per tile suffices
-  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][kKeyTile * kKsStride];
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][kChunk * kKsStride];
   __shared__ __attribute__((aligned(16))) _Float16 Vt[2][kAttnD * kVtStride];
   __shared__ f32x2 ptbl[128];
   __shared__ float pthr[128];
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       a.causal ? (int64_t)(q0 + wave * 32u) + (int64_t)a.Nk - (int64_t)a.Nq : (int64_t)a.Nk - 1;
   const uint64_t kvrow0 = (uint64_t)kvh * a.Nk;
 
-  TileRegs nxt = load_tile(a, kvrow0, 0u, tid);
+  TileRegs nxt = load_chunk(a, kvrow0, 0u, tid);
 
   // This lane's B operand of S^T: query qi, elements 16 ks + 8 g .. +7.
   f16x8 qf[8];
@@ -198,11 +206,15 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   float m = -INFINITY, l = 0.0f;
 
   uint32_t buf = 0;
-  for (uint32_t t0 = 0; t0 < kend; t0 += kKeyTile, buf ^= 1u) {
-    store_tile(nxt, t0 + (tid >> 3) < a.Nk, tid, Ks[buf], Vt[buf]);
-    if (t0 + kKeyTile < kend) nxt = load_tile(a, kvrow0, t0 + kKeyTile, tid);
+  for (uint32_t c0 = 0; c0 < kend; c0 += kChunk, buf ^= 1u) {
+    store_chunk(nxt, c0 + (tid >> 2) < a.Nk, tid, Ks[buf], Vt[buf]);
+    if (c0 + kChunk < kend) nxt = load_chunk(a, kvrow0, c0 + kChunk, tid);
     __syncthreads();
-    const _Float16 *K = Ks[buf];
+#pragma unroll 1
+  for (uint32_t sub = 0; sub < 2; ++sub) {
+    const uint32_t t0 = c0 + sub * kKeyTile;
+    if (t0 >= kend) break;
+    const _Float16 *K = Ks[buf] + sub * kKeyTile * kKsStride;
     const _Float16 *V = Vt[buf];
 
     // S^T = K Q^T: sacc[v] = key 8 (v >> 2) + 4 g + (v & 3) of the tile, query qi.
@@ -281,17 +293,18 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint32_t d = 32u * t + col;
-      const uint32_t sw = (d >> 4) << 2;
-      const _Float16 *vrow = &V[d * kVtStride];
+      // row d = 32 t + col of V^T; its key columns are XOR-ed with 16 t
+      const _Float16 *vrow = &V[(32u * t + col) * kVtStride];
+      const uint32_t kb = sub * kKeyTile;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const uint2 x0 = *(const uint2 *)(vrow + ((16u * blk + 4u * g) ^ sw));
-        const uint2 x1 = *(const uint2 *)(vrow + ((16u * blk + 8u + 4u * g) ^ sw));
+        const uint2 x0 = *(const uint2 *)(vrow + ((kb + 16u * blk + 4u * g) ^ (16u * t)));
+        const uint2 x1 = *(const uint2 *)(vrow + ((kb + 16u * blk + 8u + 4u * g) ^ (16u * t)));
         const f16x8 va = __builtin_bit_cast(f16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[blk], o[t], 0, 0, 0);
       }
     }
+  }
   }
 
   l = l + __shfl_xor(l, 32);
