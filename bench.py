@@ -361,6 +361,30 @@ def formats_table(torch, nv, workloads, iters: int = 50):
               f"{t['d'] * 1e3:.1f} ({gbs(db, t['d']):.0f}) |", flush=True)
 
 
+def attention_operands(torch, nv, workloads):
+    """Q [1, 32, 32768, 128] (workload 5 recipe), K [1, 8, 32768, 128] (workload 3 recipe),
+    V [1, 8, 32768, 128] N(0, 1), all bf16, and random signs for the Hadamard transform."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(17)
+    qh = workloads.workload(5)
+    kh = workloads.workload(3)
+    vh = workloads.to_bf16_bits(rng.standard_normal(kh.shape).astype(np.float32))
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    signs = rng.integers(0, 2**32, 4, dtype=np.uint64).astype(np.uint32)
+    return bf(qh), bf(kh), bf(vh), signs
+
+
+def attention_profile(torch, nv, workloads, launches: int = 5):
+    """Short run for rocprofv3: code Q, K, V once (ScaleSearch, randomized Hadamard on
+    Q and K), then `launches` non-causal attention launches at 32K."""
+    q, k, v, signs = attention_operands(torch, nv, workloads)
+    ops = (nv.quantize(q, (-8, 8), signs=signs), nv.quantize(k, (-2, 6), signs=signs),
+           nv.quantize(v, (-2, 6)))
+    for _ in range(launches):
+        nv.attention(*ops)
+    torch.cuda.synchronize()
+
+
 def attention_table(torch, nv, workloads, iters: int = 5):
     """Markdown table: attention on NVFP4 operands at 32K, Q [1, 32, 32768, 128] (workload 5
     recipe) against K [1, 8, 32768, 128] (workload 3 recipe) and V [1, 8, 32768, 128]
@@ -370,13 +394,7 @@ def attention_table(torch, nv, workloads, iters: int = 5):
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    rng = np.random.default_rng(17)
-    qh = workloads.workload(5)
-    kh = workloads.workload(3)
-    vh = workloads.to_bf16_bits(rng.standard_normal(kh.shape).astype(np.float32))
-    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-    q, k, v = bf(qh), bf(kh), bf(vh)
-    signs = rng.integers(0, 2**32, 4, dtype=np.uint64).astype(np.uint32)
+    q, k, v, signs = attention_operands(torch, nv, workloads)
     B, Hq, N, D = q.shape
     flops = 4.0 * B * Hq * N * N * D
     quant = {
@@ -432,6 +450,8 @@ def main():
     ap.add_argument("--attention", action="store_true",
                     help="print a markdown table timing attention on NVFP4 operands at 32K "
                          "(no JSON line)")
+    ap.add_argument("--attention-profile", action="store_true",
+                    help="short run for rocprofv3: five non-causal attention launches at 32K")
     ap.add_argument("--rocpd-summary", nargs="+", metavar="DB",
                     help="print a text summary of rocprofv3 databases of a --profile run")
     args = ap.parse_args()
@@ -461,6 +481,9 @@ def main():
         return
     if args.attention:
         attention_table(torch, nv, workloads)
+        return
+    if args.attention_profile:
+        attention_profile(torch, nv, workloads)
         return
     dev = torch.device("cuda:0")
     print(f"[bench] generating workload 4 ({ROWS}x{COLS} bf16)", file=sys.stderr, flush=True)
