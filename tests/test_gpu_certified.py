@@ -1,5 +1,5 @@
-"""The certified bf16 search must give the contract's result on blocks where the
-certificate cannot decide: candidates whose SSEs tie exactly or differ by a few
+"""The certified search (bf16 input, and FP32 values through three exact bf16
+parts) must give the contract's result on blocks where the certificate cannot decide: candidates whose SSEs tie exactly or differ by a few
 parts per million. Inputs are chosen on the CPU with the independent NumPy
 reference (no GPU output is used to build them); results are compared bit for
 bit with the oracle under the same tensor scale."""
@@ -90,3 +90,66 @@ def test_magnitude_edges(gpu, orc):
         xf = workloads.bf16_bits_to_f32(xh)
         sg = np.float32(np.abs(xf).max() / np.float32(2688))
         check_given(gpu, orc, xh, sg, (-2, 6))
+
+
+# --- FP32 values: the certified search on three exact bf16 parts of each value ---
+
+def test_mined_near_ties_f32(gpu, orc):
+    """The 1024 closest-call blocks out of 2^17 FP32 Gaussian blocks (full 24-bit
+    significands), offsets [-8, 8] and [-2, 6]."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((128, 16384)).astype(np.float32)
+    xf = x.reshape(-1, 16)
+    sg = np.float32(np.abs(xf).max() / np.float32(2688))
+    for offsets in [(-2, 6), (-8, 8)]:
+        gaps = _relative_gaps(xf, sg, *offsets)
+        pick = np.argsort(gaps, kind="stable")[:1024]
+        print(f"[near-ties f32] {offsets}: gaps min {gaps[pick].min():.2e} max {gaps[pick].max():.2e}")
+        sel = np.ascontiguousarray(xf[pick].reshape(64, 256))
+        check_given(gpu, orc, sel, sg, offsets)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_identical_reconstructions(gpu, orc, dt):
+    """Blocks whose values are V * s_p with V in {0, 1, 2, 3} and amax = 3 s_p: the
+    default pattern is p - 8, and candidates p - 8 and p reconstruct every element
+    alike (values doubled at half the scale), an exact tie the visiting order
+    decides; half of the blocks nudged by a few ulps in one element."""
+    rng = np.random.default_rng(31)
+    n = 4096
+    vals = R.e4m3_values()
+    p = rng.integers(40, 110, n)
+    V = np.array([0, 1, 2, 3], np.float32)[rng.integers(0, 4, (n, 16))]
+    V[:, 0] = 3
+    sign = rng.integers(0, 2, (n, 16)) * 2 - 1
+    x = (sign * V * vals[p][:, None]).astype(np.float32)
+    bits = x.view(np.uint32)
+    idx = rng.integers(1, 16, n)
+    bump = np.where(np.arange(n) % 2 == 0, 0, rng.integers(1, 4, n)).astype(np.uint32)
+    nz = (bits[np.arange(n), idx] & 0x7FFFFFFF) != 0
+    if dt == "bf16":
+        xh = workloads.to_bf16_bits(x)
+        xh[np.arange(n)[nz], idx[nz]] += bump[nz].astype(np.uint16)
+        xin = xh.reshape(-1, 256)
+    else:
+        bits[np.arange(n)[nz], idx[nz]] += bump[nz]
+        xin = bits.view(np.float32).reshape(-1, 256)
+    for offsets in [(-8, 8), (0, 8), (-8, 0)]:
+        check_given(gpu, orc, np.ascontiguousarray(xin), np.float32(1.0), offsets)
+
+
+@pytest.mark.parametrize("offsets", [(0, 0), (-1, 1), (-3, 2), (-8, 0), (0, 8), (-8, 8)])
+def test_offset_subranges_f32(gpu, orc, offsets):
+    x = workloads.bf16_bits_to_f32(workloads.workload(2, (96, 4096)))
+    x = (x * np.float32(1.0 + 2.0 ** -9)).astype(np.float32)  # full FP32 significands
+    sg = np.float32(np.abs(x).max() / np.float32(2688))
+    check_given(gpu, orc, x, sg, offsets)
+
+
+def test_magnitude_edges_f32(gpu, orc):
+    base = np.random.default_rng(41).standard_normal((8, 1024)).astype(np.float32)
+    for e in (-45, -40, -39, 59, 60, 61):
+        x = (base * np.float32(2.0 ** e)).astype(np.float32)
+        sg = np.float32(np.abs(x).max() / np.float32(2688))
+        check_given(gpu, orc, x, sg, (-2, 6))
+        check_given(gpu, orc, x, sg, (-8, 8))
