@@ -246,10 +246,22 @@ __device__ __forceinline__ void build_scale_table(f32x2 *tbl, float sg) {
   __syncthreads();
 }
 
+// The contract's squared-error term of the block's largest element a under
+// candidate (d, r): fl(fl(a - fl(V d))^2), V the E2M1 value of fl(a r).
+__device__ __forceinline__ float amax_term(float a, float d, float r) {
+  const uint32_t c = fp4_encode_pair(0u, a * r, 0.0f, 0);
+  const float e = a - fp4_decode_pair(c, 0).x * d;
+  return e * e;
+}
+
 // ScaleSearch on one block held in registers: default pattern p0 from the
 // block amax, then f = 0, f_lo..f_hi; first strictly smaller SSE wins.
 // Writes the chosen pattern (0x7F and zero codes under the non-finite
-// contract) and the two code words.
+// contract) and the two code words. A candidate's SSE is a running sum of
+// non-negative terms, so it is at least its term for the block's largest
+// element; a candidate whose amax term already exceeds the best SSE so far
+// cannot win and is skipped when no lane of the wave needs it (exact: the
+// result is unchanged).
 __device__ __forceinline__ void search_block(const float (&x)[16], float sg, bool sg_ok,
                                              const f32x2 *tbl, int f_lo, int f_hi,
                                              uint32_t &best_p, uint32_t &bc0, uint32_t &bc1) {
@@ -271,6 +283,8 @@ __device__ __forceinline__ void search_block(const float (&x)[16], float sg, boo
       const int p = (int)p0 + f;
       const bool valid = (unsigned)p <= 126u;
       dr = tbl[valid ? p : (int)p0];
+      const bool live = valid && !(amax_term(amax, dr.x, dr.y) > best);
+      if (__ballot(live) == 0ull) continue;
       uint32_t c0, c1;
       const float s = candidate_sse(x, dr.x, dr.y, c0, c1);
       const bool win = valid && (s < best);
