@@ -130,7 +130,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const uint32_t bh = blockIdx.y;
   const uint32_t b = bh / a.Hq, h = bh - b * a.Hq;
   const uint32_t kvh = b * a.Hkv + h / (a.Hq / a.Hkv);
-  const uint32_t q0 = blockIdx.x * kQueriesPerGroup;
+  // causal: the last query blocks see the most keys; dispatch them first
+  const uint32_t qb = a.causal ? gridDim.x - 1u - blockIdx.x : blockIdx.x;
+  const uint32_t q0 = qb * kQueriesPerGroup;
   const uint32_t qi = q0 + wave * 32u + col;
   const bool qvalid = qi < a.Nq;
 
