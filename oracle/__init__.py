@@ -24,4 +24,5 @@ from .oracle import (  # noqa: F401
     dequantize_mxfp4,
     mx_block_sse,
     attention_nvfp4,
+    attention_kv_cache,
 )

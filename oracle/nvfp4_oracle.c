@@ -1150,3 +1150,233 @@ int oracle_attention_nvfp4(const uint8_t *qc, const uint8_t *qs, float qg, const
             pthread_join(th[t], NULL);
     return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Attention over the attention-sink KV cache ([SSA]: the first and last KV  */
+/* blocks stay in full precision, the middle is NVFP4). The cache holds T    */
+/* tokens: token t < n_first in head[t], t >= max(n_first, T - n_last) in    */
+/* the ring tail[t mod n_last] (bf16), the rest coded at middle row          */
+/* t - n_first under the tensor scale. Reading: keys are visited segment by  */
+/* segment (head, middle, tail, each in token order) in tiles of `tile`      */
+/* keys that never straddle two segments (a segment's last tile may be       */
+/* short); everything else is the attention above. All T keys are visible.  */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const uint8_t *qc, *qs;
+    float qg;
+    const uint16_t *kh, *kt, *vh, *vt;
+    const uint8_t *kc, *ks, *vc, *vs;
+    float kg, vg;
+    int64_t B, Hq, Hkv, Nq, T, D, nf, nl, cap, tile;
+    double *O, *mag, *bound;
+    int64_t r0, r1;
+} cjob_t;
+
+static void *attention_cache_rows(void *arg)
+{
+    const cjob_t *J = (const cjob_t *)arg;
+    const int64_t D = J->D, T = J->T, tile = J->tile;
+    const float SP = 1.0f / 2688.0f;
+    const double tau = 1.0 / sqrt((double)D);
+    float *q = malloc(sizeof(float) * D);
+    double *kv = malloc(sizeof(double) * D * (size_t)(T > 0 ? T : 1));
+    float *vv = malloc(sizeof(float) * D * (size_t)(T > 0 ? T : 1));
+    double *vfac = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    double *acc = malloc(sizeof(double) * D), *mg = malloc(sizeof(double) * D);
+    double *bd = malloc(sizeof(double) * D);
+    double *s = malloc(sizeof(double) * tile);
+    float *pf = malloc(sizeof(float) * tile), *ph = malloc(sizeof(float) * tile);
+    double *dl = malloc(sizeof(double) * tile);
+    int64_t cached = -1;
+    const int64_t mid_lo = J->nf, mid_hi = T - J->nl > J->nf ? T - J->nl : J->nf;
+    for (int64_t r = J->r0; r < J->r1; ++r) {
+        int64_t bh = r / J->Nq;
+        int64_t b = bh / J->Hq, h = bh % J->Hq;
+        int64_t kvh = b * J->Hkv + h / (J->Hq / J->Hkv);
+        if (kvh != cached) {
+            /* key t: kv = its value in units of the factor kfac (head/tail 1, middle Sk);
+               the score scale folds the factor in, as the kernel does */
+            for (int64_t t = 0; t < T; ++t) {
+                double *kd = kv + t * D;
+                float *vd = vv + t * D;
+                if (t < J->nf || t >= mid_hi) {
+                    const uint16_t *kr, *vr;
+                    if (t < J->nf) {
+                        kr = J->kh + (kvh * J->nf + t) * D;
+                        vr = J->vh + (kvh * J->nf + t) * D;
+                    } else {
+                        kr = J->kt + (kvh * J->nl + t % J->nl) * D;
+                        vr = J->vt + (kvh * J->nl + t % J->nl) * D;
+                    }
+                    for (int64_t d = 0; d < D; ++d) {
+                        kd[d] = (double)bf16_bits_to_float(kr[d]) * (double)J->qg;
+                        vd[d] = bf16_bits_to_float(vr[d]);
+                    }
+                    vfac[t] = 1.0;
+                } else {
+                    int64_t row = kvh * J->cap + (t - J->nf);
+                    float tmp[1024];
+                    decode_row(J->kc + row * (D / 2), J->ks + row * (D / 16), D, tmp);
+                    for (int64_t d = 0; d < D; ++d)
+                        kd[d] = (double)tmp[d] * (double)J->kg * (double)J->qg;
+                    decode_row(J->vc + row * (D / 2), J->vs + row * (D / 16), D, vd);
+                    vfac[t] = (double)J->vg;
+                }
+            }
+            cached = kvh;
+        }
+        decode_row(J->qc + r * (D / 2), J->qs + r * (D / 16), D, q);
+        double m = -INFINITY, l = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            acc[d] = mg[d] = bd[d] = 0.0;
+        const int64_t seg[3][2] = {{0, J->nf < T ? J->nf : T}, {mid_lo, mid_hi}, {mid_hi > J->nf ? mid_hi : J->nf, T}};
+        for (int sg = 0; sg < 3; ++sg) {
+            for (int64_t t0 = seg[sg][0]; t0 < seg[sg][1]; t0 += tile) {
+                double mt = -INFINITY, amax_abs = 0.0;
+                for (int64_t u = 0; u < tile; ++u) {
+                    int64_t j = t0 + u;
+                    s[u] = -INFINITY;
+                    if (j < seg[sg][1]) {
+                        double dot = 0.0, ab = 0.0;
+                        for (int64_t d = 0; d < D; ++d) {
+                            double pr = (double)q[d] * kv[j * D + d];
+                            dot += pr;
+                            ab += fabs(pr);
+                        }
+                        s[u] = tau * dot;
+                        if (s[u] > mt)
+                            mt = s[u];
+                        if (tau * ab > amax_abs)
+                            amax_abs = tau * ab;
+                    }
+                }
+                double mn = m > mt ? m : mt;
+                if (mn == -INFINITY)
+                    continue;
+                double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
+                double psum = 0.0;
+                for (int64_t u = 0; u < tile; ++u) {
+                    pf[u] = (s[u] == -INFINITY) ? 0.0f : (float)exp(s[u] - mn);
+                    psum += pf[u];
+                    dl[u] = (s[u] == -INFINITY) ? 0.0
+                                                : amax_abs * (double)(D + 2) * 0x1p-24 +
+                                                      (fabs(s[u]) + fabs(mn)) * 0x1p-21 + 0x1p-20;
+                }
+                l = alpha * l + psum;
+                for (int64_t d = 0; d < D; ++d) {
+                    acc[d] *= alpha;
+                    mg[d] *= alpha;
+                    bd[d] *= alpha;
+                }
+                for (int64_t u0 = 0; u0 < tile; u0 += 16) {
+                    uint8_t cb[8];
+                    int p = search_block(pf + u0, SP, 0, 0, cb, NULL);
+                    float sp = oracle_e4m3_value(p);
+                    float rr = 1.0f / (sp * SP);
+                    float amax_b = 0.0f;
+                    double dmax = 0.0, flip[16];
+                    for (int e = 0; e < 16; ++e) {
+                        int nib = (cb[e / 2] >> ((e & 1) * 4)) & 0xF;
+                        ph[u0 + e] = E2M1_MAG[nib & 7] * sp;
+                        if (pf[u0 + e] > amax_b)
+                            amax_b = pf[u0 + e];
+                        if (dl[u0 + e] > dmax)
+                            dmax = dl[u0 + e];
+                    }
+                    for (int e = 0; e < 16; ++e) {
+                        float gap = 0.0f;
+                        flip[e] = 0.0;
+                        if (pf[u0 + e] > 0.0f &&
+                            e2m1_mid_distance(pf[u0 + e] * rr, &gap) <= dl[u0 + e] + 0x1p-22)
+                            flip[e] = (double)gap * sp;
+                    }
+                    float tb = (amax_b / 6.0f) / SP;
+                    if (amax_b > 0.0f) {
+                        for (int nb = -1; nb <= 1; nb += 2) {
+                            int p2 = p + nb;
+                            if (p2 < 0 || p2 > 126)
+                                continue;
+                            double mid = 0.5 * ((double)oracle_e4m3_value(p) + oracle_e4m3_value(p2));
+                            if (fabs((double)tb - mid) <= (dmax + 0x1p-21) * mid) {
+                                float sp2 = oracle_e4m3_value(p2);
+                                float r2 = 1.0f / (sp2 * SP);
+                                for (int e = 0; e < 16; ++e) {
+                                    float y2 = pf[u0 + e] * r2, gap2 = 0.0f;
+                                    int c2 = oracle_e2m1_code(y2);
+                                    double dv = fabs((double)E2M1_MAG[c2] * sp2 - ph[u0 + e]);
+                                    if (pf[u0 + e] > 0.0f &&
+                                        e2m1_mid_distance(y2, &gap2) <= dl[u0 + e] + 0x1p-22)
+                                        dv += (double)gap2 * sp2;
+                                    if (dv > flip[e])
+                                        flip[e] = dv;
+                                }
+                            }
+                        }
+                    }
+                    for (int e = 0; e < 16; ++e) {
+                        int64_t j = t0 + u0 + e;
+                        if (j >= seg[sg][1] || pf[u0 + e] == 0.0f)
+                            continue;
+                        for (int64_t d = 0; d < D; ++d) {
+                            double v = (double)vv[j * D + d] * vfac[j];
+                            acc[d] += (double)ph[u0 + e] * v;
+                            mg[d] += (double)ph[u0 + e] * fabs(v);
+                            bd[d] += flip[e] * fabs(v);
+                        }
+                    }
+                }
+                m = mn;
+            }
+        }
+        double f = (l > 0.0) ? (double)SP / l : 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            J->O[r * D + d] = acc[d] * f;
+            if (J->mag)
+                J->mag[r * D + d] = mg[d] * f;
+            if (J->bound)
+                J->bound[r * D + d] = bd[d] * f;
+        }
+    }
+    free(q); free(kv); free(vv); free(vfac); free(acc); free(mg); free(bd);
+    free(s); free(pf); free(ph); free(dl);
+    return NULL;
+}
+
+int oracle_attention_kv_cache(const uint8_t *qc, const uint8_t *qs, float qg, const uint16_t *kh,
+                              const uint16_t *kt, const uint8_t *kc, const uint8_t *ks, float kg,
+                              const uint16_t *vh, const uint16_t *vt, const uint8_t *vc,
+                              const uint8_t *vs, float vg, int64_t B, int64_t Hq, int64_t Hkv,
+                              int64_t Nq, int64_t T, int64_t D, int64_t nf, int64_t nl, int64_t cap,
+                              int64_t tile, double *O, double *mag, double *bound, int nthreads)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || T < 0 || D <= 0 || D % 16 ||
+        D > 1024 || nf < 0 || nl < 0 || cap < 0 || tile <= 0 || tile % 16 || !O)
+        return ORACLE_EINVAL;
+    int64_t mid = T - nf - nl;
+    if (mid > cap)
+        return ORACLE_EINVAL;
+    int64_t rows = B * Hq * Nq;
+    if (rows == 0)
+        return ORACLE_OK;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nthreads > rows)
+        nthreads = (int)rows;
+    pthread_t th[256];
+    int running[256];
+    cjob_t jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (cjob_t){qc, qs, qg, kh, kt, vh, vt, kc, ks, vc, vs, kg, vg, B, Hq, Hkv, Nq, T,
+                           D, nf, nl, cap, tile, O, mag, bound, rows * t / nthreads,
+                           rows * (t + 1) / nthreads};
+        running[t] = nthreads > 1 && pthread_create(&th[t], NULL, attention_cache_rows, &jobs[t]) == 0;
+        if (!running[t])
+            attention_cache_rows(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (running[t])
+            pthread_join(th[t], NULL);
+    return ORACLE_OK;
+}

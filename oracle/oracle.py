@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
             L.oracle_attention_nvfp4.argtypes = [vp, vp, f32, vp, vp, f32, vp, vp, f32, i64, i64,
                                                  i64, i64, i64, i64, i64, i32, vp, vp, vp, i32]
             L.oracle_attention_nvfp4.restype = i32
+            L.oracle_attention_kv_cache.argtypes = [vp, vp, f32, vp, vp, vp, vp, f32, vp, vp, vp,
+                                                    vp, f32, i64, i64, i64, i64, i64, i64, i64,
+                                                    i64, i64, i64, vp, vp, vp, i32]
+            L.oracle_attention_kv_cache.restype = i32
             _lib = L
     return _lib
 
@@ -307,4 +311,32 @@ def attention_nvfp4(q, k, v, tile: int = 32, causal: bool = False, nthreads: int
                                       _threads(nthreads))
     if rc:
         raise ValueError(f"oracle_attention_nvfp4 failed ({rc})")
+    return O, mag, bound
+
+
+def attention_kv_cache(q, k, v, T: int, n_first: int, n_last: int, tile: int = 32,
+                       nthreads: int | None = None):
+    """Attention over the attention-sink KV cache. q: (codes, scales, tensor scale) of
+    [B, Hq, Nq, D]; k, v: dicts with head [B,H,nf,D], tail [B,H,nl,D] (bf16 bits, ring by
+    token mod nl), codes [B,H,cap,D/2], scales [B,H,cap,D/16], gscale. Returns (O, mag, bound)."""
+    qc, qs, qg = q
+    qc = np.ascontiguousarray(qc, dtype=np.uint8)
+    qs = np.ascontiguousarray(qs, dtype=np.uint8)
+    B, Hq, Nq, D2 = qc.shape
+    D = D2 * 2
+    Hkv = k["codes"].shape[1]
+    cap = k["codes"].shape[2]
+    arr = lambda a, dt: np.ascontiguousarray(a, dtype=dt)
+    kh, kt, vh, vt = (arr(x, np.uint16) for x in (k["head"], k["tail"], v["head"], v["tail"]))
+    kc, ks, vc, vs = (arr(x, np.uint8) for x in (k["codes"], k["scales"], v["codes"], v["scales"]))
+    O = np.empty((B, Hq, Nq, D), np.float64)
+    mag = np.empty_like(O)
+    bound = np.empty_like(O)
+    rc = lib().oracle_attention_kv_cache(_ptr(qc), _ptr(qs), float(qg), _ptr(kh), _ptr(kt),
+                                         _ptr(kc), _ptr(ks), float(k["gscale"]), _ptr(vh),
+                                         _ptr(vt), _ptr(vc), _ptr(vs), float(v["gscale"]), B, Hq,
+                                         Hkv, Nq, T, D, n_first, n_last, cap, tile, _ptr(O),
+                                         _ptr(mag), _ptr(bound), _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_attention_kv_cache failed ({rc})")
     return O, mag, bound

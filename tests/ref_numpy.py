@@ -311,3 +311,57 @@ def attention_ref(q, k, v, tile: int = 32, causal: bool = False):
             with np.errstate(invalid="ignore", divide="ignore"):
                 O[b, h] = np.where(l[:, None] > 0, acc * (float(SP) * vg) / l[:, None], 0.0)
     return O
+
+
+def attention_cache_ref(q, k, v, T: int, nf: int, nl: int, tile: int = 32):
+    """Attention over the sink KV cache with NumPy: key values assembled from the head
+    (t < nf), the ring (t >= max(nf, T - nl), slot t mod nl) and the coded middle; keys
+    visited segment by segment in tiles of `tile` that stay inside a segment; P coded
+    per 16 keys as in attention_ref."""
+    def bf(a):
+        return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    qd = nvfp4_decode(q[0], q[1]) * float(q[2])
+    B, Hq, Nq, D = qd.shape
+    Hkv = k["codes"].shape[1]
+    mid_hi = max(T - nl, nf)
+    SP = np.float32(1.0) / np.float32(2688.0)
+
+    def values(c, b, hk):
+        out = np.zeros((T, D))
+        for t in range(T):
+            if t < nf:
+                out[t] = bf(c["head"][b, hk, t])
+            elif t >= mid_hi:
+                out[t] = bf(c["tail"][b, hk, t % nl])
+            else:
+                dec = nvfp4_decode(c["codes"][b, hk, t - nf], c["scales"][b, hk, t - nf])
+                out[t] = dec * float(c["gscale"])
+        return out
+
+    segs = [(0, min(nf, T)), (nf, mid_hi), (max(mid_hi, nf), T)]
+    O = np.zeros((B, Hq, Nq, D))
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            K, V = values(k, b, hk), values(v, b, hk)
+            S = (qd[b, h] @ K.T) / np.sqrt(D)
+            m = np.full(Nq, -np.inf)
+            l = np.zeros(Nq)
+            acc = np.zeros((Nq, D))
+            for lo, hi in segs:
+                for t0 in range(lo, hi, tile):
+                    w = min(tile, hi - t0)
+                    St = np.full((Nq, tile), -np.inf)
+                    St[:, :w] = S[:, t0:t0 + w]
+                    mn = np.maximum(m, St.max(axis=1))
+                    with np.errstate(invalid="ignore"):
+                        alpha = np.where(np.isfinite(m), np.exp(m - mn), 0.0)
+                        P = np.where(np.isfinite(St), np.exp(St - mn[:, None]), 0.0).astype(np.float32)
+                    l = alpha * l + P.astype(np.float64).sum(axis=1)
+                    codes, scales, _, _ = quantize_ref_search(P, 0, 0, sg=SP)
+                    Vt = np.zeros((tile, D))
+                    Vt[:w] = V[t0:t0 + w]
+                    acc = alpha[:, None] * acc + nvfp4_decode(codes, scales) @ Vt
+                    m = mn
+            O[b, h] = acc * float(SP) / l[:, None]
+    return O

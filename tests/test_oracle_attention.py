@@ -105,3 +105,47 @@ def test_flip_allowance_is_small_and_present(orc):
     assert np.all(bound >= 0) and np.any(bound > 0)
     assert np.all(bound <= 0.25 * mag + 1e-300)
     assert np.median(bound / mag) < 0.02
+
+
+# --- attention over the sink KV cache ---
+
+def cache_of(orc, x, nf, nl, T, cap):
+    """Sink-cache buffers of a [B, H, T, D] bf16 tensor, as the KV append builds them."""
+    B, H, _, D = x.shape
+    mid = max(T - nf - nl, 0)
+    g = np.float32(np.abs(workloads.bf16_bits_to_f32(x[:, :, nf:T - nl])).max() / 2688) if mid else np.float32(1)
+    c, s, _ = orc.quantize(np.ascontiguousarray(x[:, :, nf:nf + mid]).reshape(-1, D) if mid else
+                           np.zeros((0, D), np.uint16), -2, 6, gscale=float(g))
+    codes = np.zeros((B, H, cap, D // 2), np.uint8)
+    scales = np.zeros((B, H, cap, D // 16), np.uint8)
+    codes[:, :, :mid] = c.reshape(B, H, mid, D // 2)
+    scales[:, :, :mid] = s.reshape(B, H, mid, D // 16)
+    head = np.zeros((B, H, nf, D), np.uint16)
+    head[:, :, :min(nf, T)] = x[:, :, :min(nf, T)]
+    tail = np.zeros((B, H, nl, D), np.uint16)
+    for t in range(max(nf, T - nl), T):
+        tail[:, :, t % nl] = x[:, :, t]
+    return dict(head=head, tail=tail, codes=codes, scales=scales, gscale=g)
+
+
+@pytest.mark.parametrize("T,nf,nl", [(200, 32, 48), (90, 64, 64), (300, 0, 0), (130, 16, 0)])
+def test_cache_matches_numpy_reference(orc, T, nf, nl):
+    rng = np.random.default_rng(T + nf)
+    qx = workloads.to_bf16_bits(rng.standard_normal((1, 2, 20, 128)).astype(np.float32))
+    kx = workloads.workload(3, (1, 1, T, 128))
+    vx = workloads.to_bf16_bits(rng.standard_normal((1, 1, T, 128)).astype(np.float32))
+    q = quant(orc, qx)
+    k, v = cache_of(orc, kx, nf, nl, T, T), cache_of(orc, vx, nf, nl, T, T)
+    O, _, _ = orc.attention_kv_cache(q, k, v, T, nf, nl)
+    ref = ref_numpy.attention_cache_ref(q, k, v, T, nf, nl)
+    np.testing.assert_allclose(O, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_cache_without_sinks_is_plain_attention(orc):
+    q, k, v = operands(orc, 1, 2, 1, 30, 150, seed=3)
+    mk = lambda t: dict(head=np.zeros((1, 1, 0, 128), np.uint16), tail=np.zeros((1, 1, 0, 128), np.uint16),
+                        codes=t[0], scales=t[1], gscale=t[2])
+    O, _, _ = orc.attention_kv_cache(q, mk(k), mk(v), 150, 0, 0)
+    O2, _, _ = orc.attention_nvfp4(q, k, v)
+    # the two apply the tensor scales at different points in double precision
+    np.testing.assert_allclose(O, O2, rtol=1e-9, atol=1e-15)
