@@ -418,6 +418,23 @@ def attention_table(torch, nv, workloads, iters: int = 5):
         tc = event_time_ms(torch, lambda: nv.attention(*ops, causal=True), iters, stream)
         print(f"| {name} | {tq:.3f} | {ta:.2f} | {flops / (ta * 1e-3) / 1e12:.0f} | "
               f"{flops / (ta * 1e-3) / 2.5e15:.3f} | {tc:.2f} |", flush=True)
+    # the same operands through the sink cache (first and last 128 tokens in bf16)
+    nf = nl = 128
+    B, Hkv, T, D = k.shape
+    qops = nv.quantize(q, (-8, 8), signs=signs)
+    kg = nv.global_scale(k[:, :, nf:T - nl].contiguous(), signs=signs)
+    vg = nv.global_scale(v[:, :, nf:T - nl].contiguous())
+    kc = nv.kv_cache_alloc(B, Hkv, D, T, nf, nl, torch.bfloat16, dev)
+    vc = nv.kv_cache_alloc(B, Hkv, D, T, nf, nl, torch.bfloat16, dev)
+    nv.kv_append(kc, k, kg, (-2, 6), signs=signs)
+    nv.kv_append(vc, v, vg, (-2, 6))
+    cache_attn = lambda: nv.attention_kv_cache(qops, kc, kg, vc, vg)
+    cache_attn()
+    torch.cuda.synchronize()
+    tk = event_time_ms(torch, cache_attn, iters, stream)
+    print(f"| sink cache 128 + 128 bf16, middle ScaleSearch (K randomized Hadamard) | — | "
+          f"{tk:.2f} | {flops / (tk * 1e-3) / 1e12:.0f} | {flops / (tk * 1e-3) / 2.5e15:.3f} | — |",
+          flush=True)
     try:
         sdpa = lambda: F.scaled_dot_product_attention(q, k, v, enable_gqa=True)
         sdpa()

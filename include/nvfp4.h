@@ -193,6 +193,26 @@ NVFP4_API nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_
                                        int64_t Nq, int64_t Nk, int64_t D, int causal, void *out,
                                        nvfp4_dtype out_dt, void *stream);
 
+/* Attention over the attention-sink KV cache that nvfp4_kv_append maintains
+ * (ScaleSearch summary page, ScaleSearchAttention: mixed-precision KV cache with
+ * the first and last tokens in full precision). q as for nvfp4_attention. The K
+ * and V caches each hold T tokens: token t < n_first in head[b][h][t] (bf16),
+ * token t >= max(n_first, T - n_last) in the ring tail[b][h][t mod n_last]
+ * (bf16), every other token coded at row t - n_first of codes[b][h][cap][64] /
+ * scales[b][h][cap][8] under the tensor scale k_gscale / v_gscale. cache_dt must
+ * be NVFP4_BF16; T - n_first - n_last <= cap. Every token is visible (no causal
+ * mask). Keys are visited segment by segment (head, middle, tail, each in token
+ * order) in tiles of 32 keys that never straddle two segments; otherwise as
+ * nvfp4_attention: sink keys enter the products as their exact bf16 values, coded
+ * keys as V[code] * s_block times the tensor scale. out: [B][Hq][Nq][128]. */
+NVFP4_API nvfp4_status nvfp4_attention_kv_cache(
+    const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
+    const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
+    const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
+    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    int64_t T, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, void *out,
+    nvfp4_dtype out_dt, void *stream);
+
 /* Randomized Hadamard transform (QuIP#-style incoherence processing, ScaleSearch
  * summary page, ScaleSearchAttention section: a transform pair Q' = Q R^-T,
  * K' = K R that keeps Q K^T while lowering the mean-square absolute value).

@@ -7,6 +7,7 @@ from .nvfp4 import (  # noqa: F401
     LIB_PATH,
     NVFP4Error,
     attention,
+    attention_kv_cache,
     dequantize,
     dequantize_kv_sink,
     global_scale,

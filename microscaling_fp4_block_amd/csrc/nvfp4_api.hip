@@ -550,4 +550,59 @@ nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_scales,
   return hip_status(launch_attention(a, out_dt == NVFP4_BF16, (hipStream_t)stream));
 }
 
+nvfp4_status nvfp4_attention_kv_cache(
+    const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
+    const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
+    const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
+    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    int64_t T, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, void *out,
+    nvfp4_dtype out_dt, void *stream) {
+  if (!dtype_ok(out_dt) || cache_dt != NVFP4_BF16) return NVFP4_EINVAL;
+  if (D != 128) return NVFP4_ESHAPE;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || T < 0 || n_first < 0 || n_last < 0 ||
+      cap < 0)
+    return NVFP4_ESHAPE;
+  if (B * Hq > 65535 || Nq > (1ll << 30) || T > (1ll << 30) || cap > (1ll << 30))
+    return NVFP4_ESHAPE;
+  const int64_t mid = T - n_first - n_last;
+  if (mid > cap) return NVFP4_ESHAPE;
+  if (B * Hq * Nq > kMaxBlocks / 8 || B * Hkv * cap > kMaxBlocks / 8) return NVFP4_ESHAPE;
+  if (B * Nq == 0) return NVFP4_OK;
+  if (!q_codes || !q_scales || !q_gscale || !k_gscale || !v_gscale || !out) return NVFP4_EINVAL;
+  if (n_first > 0 && T > 0 && (!k_head || !v_head)) return NVFP4_EINVAL;
+  if (n_last > 0 && T > n_first && (!k_tail || !v_tail)) return NVFP4_EINVAL;
+  if (mid > 0 && (!k_codes || !k_scales || !v_codes || !v_scales)) return NVFP4_EINVAL;
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_head, 16) || !aligned(k_tail, 16) || !aligned(v_head, 16) ||
+      !aligned(v_tail, 16) || !aligned(out, 16))
+    return NVFP4_EALIGN;
+  AttnArgs a{};
+  a.qc = q_codes;
+  a.qs = q_scales;
+  a.kc = k_codes;
+  a.ks = k_scales;
+  a.vc = v_codes;
+  a.vs = v_scales;
+  a.qg = q_gscale;
+  a.kg = k_gscale;
+  a.vg = v_gscale;
+  a.o = out;
+  a.B = (uint32_t)B;
+  a.Hq = (uint32_t)Hq;
+  a.Hkv = (uint32_t)Hkv;
+  a.Nq = (uint32_t)Nq;
+  a.Nk = (uint32_t)T;
+  a.causal = 0u;
+  a.tau_log2e = (float)(1.4426950408889634 / sqrt(128.0));
+  a.cache = 1u;
+  a.kh = (const uint16_t *)k_head;
+  a.kt = (const uint16_t *)k_tail;
+  a.vh = (const uint16_t *)v_head;
+  a.vt = (const uint16_t *)v_tail;
+  a.nf = (uint32_t)n_first;
+  a.nl = (uint32_t)n_last;
+  a.cap = (uint32_t)cap;
+  return hip_status(launch_attention(a, out_dt == NVFP4_BF16, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -27,12 +27,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -78,12 +81,13 @@ struct TileRegs {
   uint32_t ksb, vsb;  // two scale bytes each
 };
 
-__device__ __forceinline__ TileRegs load_chunk(const AttnArgs &a, uint64_t kvrow0, uint32_t c0,
+__device__ __forceinline__ TileRegs load_chunk(const AttnArgs &a, uint64_t row_base,
+                                               uint32_t row_off, uint32_t c0, uint32_t hi,
                                                uint32_t tid) {
   TileRegs r{make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u), 0u, 0u};
   const uint32_t key = tid >> 2, c = tid & 3u, j = c0 + key;
-  if (j < a.Nk) {
-    const uint64_t row = kvrow0 + j;
+  if (j < hi) {
+    const uint64_t row = row_base + (j - row_off);
     r.kw = *(const uint4 *)(a.kc + row * 64u + 16u * c);
     r.vw = *(const uint4 *)(a.vc + row * 64u + 16u * c);
     r.ksb = *(const uint16_t *)(a.ks + row * 8u + 2u * c);
@@ -116,7 +120,55 @@ __device__ __forceinline__ void store_chunk(const TileRegs &r, bool live, uint32
     for (int e = 0; e < 8; ++e) Vt[(32u * c + 8u * i + e) * kVtStride + pk] = x[i][e];
 }
 
-template <bool OUT_BF16>
+// A chunk of sink keys (bf16 rows of the cache head, or of the tail ring at
+// slot t mod n_last) copied into LDS as bf16 bits in the same layouts; keys
+// past the segment end are zeros. Loaded directly: sink chunks are few.
+__device__ __forceinline__ void store_sink_chunk(const AttnArgs &a, uint32_t kvh, bool head,
+                                                 uint32_t c0, uint32_t hi, uint32_t tid,
+                                                 _Float16 *Ks, _Float16 *Vt) {
+  const uint32_t key = tid >> 2, c = tid & 3u, j = c0 + key;
+  uint4 kq[4], vq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kq[i] = vq[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (j < hi) {
+    const uint64_t row = head ? (uint64_t)kvh * a.nf + j : (uint64_t)kvh * a.nl + j % a.nl;
+    const uint4 *kr = (const uint4 *)((head ? a.kh : a.kt) + row * kAttnD + 32u * c);
+    const uint4 *vr = (const uint4 *)((head ? a.vh : a.vt) + row * kAttnD + 32u * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kq[i] = kr[i];
+      vq[i] = vr[i];
+    }
+  }
+  uint4 *kd = (uint4 *)&Ks[key * kKsStride + 32u * c];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kd[i] = kq[i];
+  const uint32_t pk = key ^ (16u * c);
+  uint16_t *vt = (uint16_t *)Vt;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {vq[i].x, vq[i].y, vq[i].z, vq[i].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vt[(32u * c + 8u * i + e) * kVtStride + pk] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
+// fp16 values that are exact in bf16 too (at most 8 significant bits) as bf16.
+__device__ __forceinline__ bf16x8 to_bf16x8(f16x8 h) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x2 b =
+        __builtin_convertvector((f32x2{(float)h[2 * j], (float)h[2 * j + 1]}), bf16x2);
+    r[2 * j] = b.x;
+    r[2 * j + 1] = b.y;
+  }
+  return r;
+}
+
+// CACHE: keys from the sink cache's three segments (else one coded segment).
+template <bool OUT_BF16, bool CACHE>
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // two buffers: tile i is decoded into buffer i & 1 while the codes of tile
   // i + 1 are in flight, so one barrier per tile suffices
@@ -169,8 +221,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     pthr[tid] = thr;
   }
 
-  const float c2 = (*a.qg * *a.kg) * a.tau_log2e;  // score scale, base 2
-  const float fo = SP * *a.vg;
+  const float qg = *a.qg;
+  const float c2_coded = (qg * *a.kg) * a.tau_log2e;  // score scale, base 2
+  const float c2_sink = qg * a.tau_log2e;
+  const float vg = *a.vg;
 
   uint32_t kend = a.Nk;
   if (a.causal) {
@@ -182,9 +236,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // the smallest lim of the wave (its first query), for the unmasked fast path
   const int64_t lim_wave =
       a.causal ? (int64_t)(q0 + wave * 32u) + (int64_t)a.Nk - (int64_t)a.Nq : (int64_t)a.Nk - 1;
-  const uint64_t kvrow0 = (uint64_t)kvh * a.Nk;
 
-  TileRegs nxt = load_chunk(a, kvrow0, 0u, tid);
+  const uint64_t coded_base = CACHE ? (uint64_t)kvh * a.cap : (uint64_t)kvh * a.Nk;
+  const uint32_t coded_off = CACHE ? a.nf : 0u;
 
   // This lane's B operand of S^T: query qi, elements 16 ks + 8 g .. +7.
   f16x8 qf[8];
@@ -201,117 +255,161 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       qf[ks] = decode8(w, s);
     }
   }
+  __syncthreads();  // the P tables
 
   f32x16 o[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) o[t] = f32x16{};
   float m = -INFINITY, l = 0.0f;
-
+  float unit = vg;  // the factor (tensor scale of V) the accumulator o is counted in
   uint32_t buf = 0;
-  for (uint32_t c0 = 0; c0 < kend; c0 += kChunk, buf ^= 1u) {
-    store_chunk(nxt, c0 + (tid >> 2) < a.Nk, tid, Ks[buf], Vt[buf]);
-    if (c0 + kChunk < kend) nxt = load_chunk(a, kvrow0, c0 + kChunk, tid);
-    __syncthreads();
-#pragma unroll 1
-  for (uint32_t sub = 0; sub < 2; ++sub) {
-    const uint32_t t0 = c0 + sub * kKeyTile;
-    if (t0 >= kend) break;
-    const _Float16 *K = Ks[buf] + sub * kKeyTile * kKsStride;
-    const _Float16 *V = Vt[buf];
 
-    // S^T = K Q^T: sacc[v] = key 8 (v >> 2) + 4 g + (v & 3) of the tile, query qi.
-    f32x16 sacc = {};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const f16x8 ka = *(const f16x8 *)&K[col * kKsStride + 16u * ks + 8u * g];
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], sacc, 0, 0, 0);
-    }
-
-    // Base-2 scores s = acc * c2 (c2 > 0, so the max is taken on acc). Full tiles
-    // (every key present and visible to every query of the wave) skip the masks.
-    float p[16];
-    float mt = -INFINITY;
-    const bool full = t0 + kKeyTile <= a.Nk && (int64_t)(t0 + kKeyTile - 1u) <= lim_wave;
-    if (full) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        p[v] = sacc[v];
-        mt = fmaxf(mt, p[v]);
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint32_t key = t0 + 8u * (v >> 2) + 4u * g + (v & 3);
-        const bool vis = key < a.Nk && (int64_t)key <= lim;
-        p[v] = vis ? sacc[v] : -INFINITY;
-        mt = fmaxf(mt, p[v]);
-      }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
-    const float mn = fmaxf(m, mt);
-    float alpha = 1.0f;
-    if (mn == -INFINITY) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = 0.0f;
-    } else {
-      alpha = __builtin_amdgcn_exp2f(m - mn);  // m = -inf gives 0
-#pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[v], c2, -mn));
-    }
-    float ps = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ps += p[v];
-    l = l * alpha + ps;
-    m = mn;
-
-    // P to NVFP4 per 16 keys (keys 16 blk .. +15: 8 in this lane, 8 in its partner),
-    // max scaling, then back to exact fp16 values V[code] * s.
-    f16x8 pb[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      float am = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) am = fmaxf(am, p[8 * blk + e]);
-      am = fmaxf(am, __shfl_xor(am, 32));
-      // p <= 1, so the pattern is at most 126; the clamp only keeps a NaN score
-      // (from a NaN operand scale) inside the table
-      uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
-      pat = am >= pthr[pat + 1u] ? pat + 1u : (am < pthr[pat] ? pat - 1u : pat);
-      const f32x2 rs = ptbl[pat];
-      uint32_t cw = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        cw = fp4_encode_pair(cw, p[8 * blk + 2 * j] * rs.x, p[8 * blk + 2 * j + 1] * rs.x, j);
-      pb[blk] = decode8(cw, rs.y);
-    }
-
-    // O^T = alpha O^T + V^T P^T; o[t][v] = output d = 32 t + 8 (v >> 2) + 4 g + (v & 3).
-    // Multiplying by alpha = 1 changes nothing, so the wave skips it when no lane needs it.
-    if (__ballot(alpha != 1.0f) != 0ull) {
+  // Keys [lo, hi) of one segment, coded (SINK false) or bf16 sink rows of the
+  // cache head or tail ring, in chunks that stay inside the segment. Each chunk
+  // is decoded into LDS buffer buf while the next coded chunk's codes are in
+  // flight; one barrier per chunk publishes it and retires the reads of the
+  // other buffer.
+  auto run_segment = [&](auto sink_tag, uint32_t lo, uint32_t hi, bool head) {
+    constexpr bool SINK = decltype(sink_tag)::value;
+    if (lo >= hi) return;
+    const float c2 = SINK ? c2_sink : c2_coded;
+    const float cunit = SINK ? 1.0f : vg;
+    if (cunit != unit) {  // at most twice per launch, uniform
+      const float ratio = unit / cunit;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+        for (int v = 0; v < 16; ++v) o[t][v] *= ratio;
+      unit = cunit;
     }
+    TileRegs nxt{make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u), 0u, 0u};
+    if (!SINK) nxt = load_chunk(a, coded_base, coded_off, lo, hi, tid);
+    for (uint32_t c0 = lo; c0 < hi; c0 += kChunk, buf ^= 1u) {
+      if (SINK)
+        store_sink_chunk(a, kvh, head, c0, hi, tid, Ks[buf], Vt[buf]);
+      else
+        store_chunk(nxt, c0 + (tid >> 2) < hi, tid, Ks[buf], Vt[buf]);
+      if (!SINK && c0 + kChunk < hi) nxt = load_chunk(a, coded_base, coded_off, c0 + kChunk, hi, tid);
+      __syncthreads();
+#pragma unroll 1
+      for (uint32_t sub = 0; sub < 2; ++sub) {
+        const uint32_t t0 = c0 + sub * kKeyTile;
+        if (t0 >= hi) break;
+        const _Float16 *K = Ks[buf] + sub * kKeyTile * kKsStride;
+        const _Float16 *V = Vt[buf];
+
+        // S^T = K Q^T: sacc[v] = key 8 (v >> 2) + 4 g + (v & 3) of the tile, query qi.
+        f32x16 sacc = {};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      // row d = 32 t + col of V^T; its key columns are XOR-ed with 16 t
-      const _Float16 *vrow = &V[(32u * t + col) * kVtStride];
-      const uint32_t kb = sub * kKeyTile;
+        for (int ks = 0; ks < 8; ++ks) {
+          if (!SINK) {
+            const f16x8 ka = *(const f16x8 *)&K[col * kKsStride + 16u * ks + 8u * g];
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], sacc, 0, 0, 0);
+          } else {
+            const bf16x8 ka = *(const bf16x8 *)&K[col * kKsStride + 16u * ks + 8u * g];
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, to_bf16x8(qf[ks]), sacc, 0, 0, 0);
+          }
+        }
+
+        // Base-2 scores s = acc * c2 (c2 > 0, so the max is taken on acc). Full tiles
+        // (every key present and visible to every query of the wave) skip the masks.
+        float p[16];
+        float mt = -INFINITY;
+        const bool full = t0 + kKeyTile <= hi && (int64_t)(t0 + kKeyTile - 1u) <= lim_wave;
+        if (full) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const uint2 x0 = *(const uint2 *)(vrow + ((kb + 16u * blk + 4u * g) ^ (16u * t)));
-        const uint2 x1 = *(const uint2 *)(vrow + ((kb + 16u * blk + 8u + 4u * g) ^ (16u * t)));
-        const f16x8 va = __builtin_bit_cast(f16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[blk], o[t], 0, 0, 0);
+          for (int v = 0; v < 16; ++v) {
+            p[v] = sacc[v];
+            mt = fmaxf(mt, p[v]);
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t key = t0 + 8u * (v >> 2) + 4u * g + (v & 3);
+            const bool vis = key < hi && (int64_t)key <= lim;
+            p[v] = vis ? sacc[v] : -INFINITY;
+            mt = fmaxf(mt, p[v]);
+          }
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+        const float mn = fmaxf(m, mt);
+        float alpha = 1.0f;
+        if (mn == -INFINITY) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) p[v] = 0.0f;
+        } else {
+          alpha = __builtin_amdgcn_exp2f(m - mn);  // m = -inf gives 0
+#pragma unroll
+          for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[v], c2, -mn));
+        }
+        float ps = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ps += p[v];
+        l = l * alpha + ps;
+        m = mn;
+
+        // P to NVFP4 per 16 keys (keys 16 blk .. +15: 8 in this lane, 8 in its
+        // partner), max scaling, then back to exact fp16 values V[code] * s.
+        f16x8 pb[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          float am = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) am = fmaxf(am, p[8 * blk + e]);
+          am = fmaxf(am, __shfl_xor(am, 32));
+          uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
+          pat = am >= pthr[pat + 1u] ? pat + 1u : (am < pthr[pat] ? pat - 1u : pat);
+          const f32x2 rs = ptbl[pat];
+          uint32_t cw = 0u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            cw = fp4_encode_pair(cw, p[8 * blk + 2 * j] * rs.x, p[8 * blk + 2 * j + 1] * rs.x, j);
+          pb[blk] = decode8(cw, rs.y);
+        }
+
+        // O^T = alpha O^T + V^T P^T; o[t][v] = output d = 32 t + 8 (v >> 2) + 4 g + (v & 3).
+        // Multiplying by alpha = 1 changes nothing: the wave skips it when no lane needs it.
+        if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // row d = 32 t + col of V^T; its key columns are XOR-ed with 16 t
+          const _Float16 *vrow = &V[(32u * t + col) * kVtStride];
+          const uint32_t kb = sub * kKeyTile;
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            const uint2 x0 = *(const uint2 *)(vrow + ((kb + 16u * blk + 4u * g) ^ (16u * t)));
+            const uint2 x1 = *(const uint2 *)(vrow + ((kb + 16u * blk + 8u + 4u * g) ^ (16u * t)));
+            const uint4 vv = make_uint4(x0.x, x0.y, x1.x, x1.y);
+            if (!SINK)
+              o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv),
+                                                            pb[blk], o[t], 0, 0, 0);
+            else
+              o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                             to_bf16x8(pb[blk]), o[t], 0, 0, 0);
+          }
+        }
       }
     }
-  }
+  };
+
+  if (CACHE) {
+    // head sinks, coded middle, tail ring: tiles never straddle two segments
+    const uint32_t mid_hi = max(a.Nk > a.nl ? a.Nk - a.nl : 0u, a.nf);
+    run_segment(std::true_type{}, 0u, min(a.nf, a.Nk), true);
+    run_segment(std::false_type{}, a.nf, mid_hi, false);
+    run_segment(std::true_type{}, max(mid_hi, a.nf), a.Nk, false);
+  } else {
+    run_segment(std::false_type{}, 0u, kend, false);
   }
 
   l = l + __shfl_xor(l, 32);
   if (!qvalid) return;
-  const float f = l > 0.0f ? fo / l : 0.0f;
+  const float f = l > 0.0f ? (SP * unit) / l : 0.0f;
   const uint64_t row = (uint64_t)bh * a.Nq + qi;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -334,10 +432,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
 hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s) {
   const dim3 grid((a.Nq + kQueriesPerGroup - 1) / kQueriesPerGroup, a.B * a.Hq);
-  if (out_bf16)
-    hipLaunchKernelGGL(attention_kernel<true>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(attention_kernel<false>, grid, dim3(256), 0, s, a);
+  if (a.cache) {
+    if (out_bf16)
+      hipLaunchKernelGGL((attention_kernel<true, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attention_kernel<false, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((attention_kernel<true, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attention_kernel<false, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

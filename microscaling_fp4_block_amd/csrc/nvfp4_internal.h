@@ -151,9 +151,14 @@ struct AttnArgs {
   const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;  // codes [rows][64], scales [rows][8]
   const float *qg, *kg, *vg;                   // device tensor scales
   void *o;                                     // [B][Hq][Nq][128] FP32 or bf16
-  uint32_t B, Hq, Hkv, Nq, Nk;
+  uint32_t B, Hq, Hkv, Nq, Nk;                 // Nk: keys (tokens in the cache)
   uint32_t causal;
   float tau_log2e;                             // log2(e) / sqrt(128)
+  // sink-cache mode: bf16 head [BHkv][nf][128] and tail ring [BHkv][nl][128];
+  // coded middle rows [BHkv][cap] (token t at row t - nf)
+  uint32_t cache;
+  const uint16_t *kh, *kt, *vh, *vt;
+  uint32_t nf, nl, cap;
 };
 
 hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s);

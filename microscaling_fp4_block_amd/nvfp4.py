@@ -49,6 +49,9 @@ SIGNATURES = {
     "nvfp4_hadamard128_rht": ([_vp, _i32, _i64, _vp, _vp, _vp], _i32),
     "nvfp4_attention": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                          _i64, _i64, _i32, _vp, _i32, _vp], _i32),
+    "nvfp4_attention_kv_cache": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  _vp, _i32, _vp], _i32),
     "mxfp4_quantize": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "mxfp4_dequantize": ([_vp, _vp, _i64, _i64, _i32, _vp, _i32, _vp], _i32),
 }
@@ -385,4 +388,31 @@ def attention(q, k, v, causal: bool = False, out_dtype=torch.float32):
                            vg.data_ptr(), B, Hq, Hkv, Nq, Nk, D2 * 2, int(causal), y.data_ptr(),
                            _dtype(y), _stream(dev))
     _check("nvfp4_attention", st)
+    return y
+
+
+def attention_kv_cache(q, k_cache: dict, k_gscale: torch.Tensor, v_cache: dict,
+                       v_gscale: torch.Tensor, out_dtype=torch.float32):
+    """Attention of q (codes, scales, global_scale of [B, Hq, Nq, 128]) over K and V
+    sink caches made by kv_cache_alloc and filled by kv_append (bf16). Returns O."""
+    L = load()
+    qc, qs, qg = q
+    dev = _dev(qc)
+    for t in (qs, qg, k_gscale, v_gscale):
+        _dev(t)
+    if k_cache["length"] != v_cache["length"]:
+        raise ValueError("the K and V caches hold different numbers of tokens")
+    if k_cache["head"].dtype != torch.bfloat16 or v_cache["head"].dtype != torch.bfloat16:
+        raise ValueError("attention over the cache needs bf16 caches")
+    B, Hq, Nq, D2 = qc.shape
+    Hkv, cap = k_cache["codes"].shape[1], k_cache["codes"].shape[2]
+    y = torch.empty(B, Hq, Nq, D2 * 2, dtype=out_dtype, device=dev)
+    st = L.nvfp4_attention_kv_cache(
+        qc.data_ptr(), qs.data_ptr(), qg.data_ptr(), k_cache["head"].data_ptr(),
+        k_cache["tail"].data_ptr(), k_cache["codes"].data_ptr(), k_cache["scales"].data_ptr(),
+        k_gscale.data_ptr(), v_cache["head"].data_ptr(), v_cache["tail"].data_ptr(),
+        v_cache["codes"].data_ptr(), v_cache["scales"].data_ptr(), v_gscale.data_ptr(), BF16, B,
+        Hq, Hkv, Nq, k_cache["length"], D2 * 2, k_cache["n_first"], k_cache["n_last"], cap,
+        y.data_ptr(), _dtype(y), _stream(dev))
+    _check("nvfp4_attention_kv_cache", st)
     return y

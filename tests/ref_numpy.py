@@ -313,6 +313,25 @@ def attention_ref(q, k, v, tile: int = 32, causal: bool = False):
     return O
 
 
+def cache_values(c, T: int, nf: int, nl: int) -> np.ndarray:
+    """[B, H, T, D] float64 values of the tokens a sink cache holds."""
+    B, H = c["codes"].shape[:2]
+    D = c["codes"].shape[3] * 2
+    mid_hi = max(T - nl, nf)
+    out = np.zeros((B, H, T, D))
+    for t in range(T):
+        if t < nf:
+            w = np.asarray(c["head"][:, :, t], np.uint16)
+        elif t >= mid_hi:
+            w = np.asarray(c["tail"][:, :, t % nl], np.uint16)
+        else:
+            out[:, :, t] = nvfp4_decode(c["codes"][:, :, t - nf], c["scales"][:, :, t - nf]) * \
+                float(c["gscale"])
+            continue
+        out[:, :, t] = (w.astype(np.uint32) << 16).view(np.float32)
+    return out
+
+
 def attention_cache_ref(q, k, v, T: int, nf: int, nl: int, tile: int = 32):
     """Attention over the sink KV cache with NumPy: key values assembled from the head
     (t < nf), the ring (t >= max(nf, T - nl), slot t mod nl) and the coded middle; keys

@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import ref_numpy
+import ref_numpy as R
 import workloads
 from gpu_util import to_dev, to_host
 
@@ -146,4 +147,51 @@ def test_full_size_sampled_rows(gpu, orc):
     tol = mag * (Nk + 8 * 1024 + 64) * U + np.abs(ref) * (delta + (Nk + 64) * U) + bound
     err = np.abs(got - ref)
     print(f"[attention] full size: max err/tol {float(np.max(err / tol)):.3f}")
+    assert np.all(err <= tol)
+
+
+# --- attention over the sink KV cache (the cache is built by the oracle) ---
+
+def upload_cache(c, T, nf, nl):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    bf = lambda a: t(a.view(np.int16)).view(torch.bfloat16)
+    return dict(head=bf(c["head"]), tail=bf(c["tail"]), codes=t(c["codes"]), scales=t(c["scales"]),
+                n_first=nf, n_last=nl, length=T), \
+        torch.tensor([c["gscale"]], dtype=torch.float32, device="cuda:0")
+
+
+@pytest.mark.parametrize("Hq,Hkv,Nq,T,nf,nl", [(2, 1, 77, 1000, 128, 128), (4, 2, 40, 300, 64, 0),
+                                                (1, 1, 33, 90, 64, 64), (1, 1, 20, 50, 64, 16),
+                                                (2, 2, 64, 200, 0, 0), (1, 1, 5, 520, 32, 96)])
+def test_kv_cache_attention(gpu, orc, Hq, Hkv, Nq, T, nf, nl):
+    from test_oracle_attention import cache_of
+
+    rng = np.random.default_rng(T + 7 * nf + nl)
+    qx = workloads.to_bf16_bits(rng.standard_normal((1, Hq, Nq, 128)).astype(np.float32))
+    kx = workloads.workload(3, (1, Hkv, T, 128))
+    vx = workloads.to_bf16_bits(rng.standard_normal((1, Hkv, T, 128)).astype(np.float32))
+    q = coded(orc, qx)
+    cap = max(T - nf - nl, 0) + 8
+    k, v = cache_of(orc, kx, nf, nl, T, cap), cache_of(orc, vx, nf, nl, T, cap)
+    print(f"[case] kv-cache attention Hq={Hq} Hkv={Hkv} Nq={Nq} T={T} nf={nf} nl={nl}", flush=True)
+    kc, kg = upload_cache(k, T, nf, nl)
+    vc, vg = upload_cache(v, T, nf, nl)
+    O = gpu.attention_kv_cache(upload(q), kc, kg, vc, vg)
+    torch.cuda.synchronize()
+    got = to_host(O).astype(np.float64)
+    ref, mag, bound = orc.attention_kv_cache(q, k, v, T, nf, nl)
+    tiles = -(-T // 32) + 3
+    # the relative error binary32 scores and exp can put on a p (the oracle's formula)
+    Qd = R.nvfp4_decode(q[0], q[1]) * float(q[2])
+    Kd = R.cache_values(k, T, nf, nl)
+    delta = 0.0
+    for h in range(Hq):
+        Kh = Kd[:, h // (Hq // Hkv)]
+        A = np.einsum("bid,bjd->bij", np.abs(Qd[:, h]), np.abs(Kh)) / np.sqrt(128.0)
+        S = np.einsum("bid,bjd->bij", Qd[:, h], Kh) / np.sqrt(128.0)
+        delta = max(delta, float(A.max(initial=0.0)) * 130 * U +
+                    2 * float(np.abs(S).max(initial=0.0)) * 2.0 ** -21 + 2.0 ** -20)
+    tol = mag * (T + 8 * tiles + 64) * U + np.abs(ref) * (delta + (T + 64) * U) + bound
+    err = np.abs(got - ref)
+    print(f"[attention] kv cache: max err/tol {float(np.max(err / np.maximum(tol, 1e-300))):.3f}")
     assert np.all(err <= tol)
