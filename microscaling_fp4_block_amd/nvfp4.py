@@ -400,6 +400,12 @@ def attention_kv_cache(q, k_cache: dict, k_gscale: torch.Tensor, v_cache: dict,
     dev = _dev(qc)
     for t in (qs, qg, k_gscale, v_gscale):
         _dev(t)
+    for c in (k_cache, v_cache):
+        for key in ("head", "tail", "codes", "scales"):
+            _dev(c[key])
+    if (k_cache["n_first"], k_cache["n_last"], k_cache["codes"].shape) != \
+            (v_cache["n_first"], v_cache["n_last"], v_cache["codes"].shape):
+        raise ValueError("the K and V caches have different layouts")
     if k_cache["length"] != v_cache["length"]:
         raise ValueError("the K and V caches hold different numbers of tokens")
     if k_cache["head"].dtype != torch.bfloat16 or v_cache["head"].dtype != torch.bfloat16:

@@ -156,3 +156,14 @@ def test_attention_argument_checks(lib):
     assert f(*([None] + [P] * 8), 1, 2, 1, 64, 64, 128, 0, P, 0, None) == 1
     assert f(*base, 1, 2, 1, 64, 64, 128, 0, P + 8, 0, None) == 3
     assert f(*base, 1, 2, 1, 0, 64, 128, 0, P, 0, None) == 0     # no queries: nothing to do
+
+
+def test_attention_kv_cache_argument_checks(lib):
+    f = lib.nvfp4_attention_kv_cache
+    ptrs = [P] * 13
+    # cache dtype must be bf16; head dimension 128; middle rows must fit cap
+    assert f(*ptrs, 0, 1, 2, 1, 8, 300, 128, 16, 16, 64, P, 0, None) == 1
+    assert f(*ptrs, 1, 1, 2, 1, 8, 300, 64, 16, 16, 300, P, 0, None) == 2
+    assert f(*ptrs, 1, 1, 2, 1, 8, 300, 128, 16, 16, 100, P, 0, None) == 2
+    assert f(*ptrs, 1, 1, 3, 2, 8, 300, 128, 16, 16, 300, P, 0, None) == 2
+    assert f(*ptrs, 1, 1, 2, 1, 0, 300, 128, 16, 16, 300, P, 0, None) == 0
