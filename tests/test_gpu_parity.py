@@ -194,3 +194,44 @@ def test_dequantize_every_code_and_scale(gpu, orc):
 
 def to_dev_u8(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def test_e2m1_convert_strided_sweep(gpu, orc):
+    """Every 97th binary32 bit pattern in [0, 6] (about 11 million values: every exponent,
+    mantissa patterns in steps of 97 ulps), both signs, through the quantizer as above."""
+    top = int(np.array([6.0], np.float32).view(np.uint32)[0])
+    v = np.arange(0, top + 1, 97, dtype=np.uint32).view(np.float32)
+    v = np.concatenate([v, -v])
+    n = -(-v.size // 15) * 15
+    v = np.concatenate([v, np.zeros(n - v.size, np.float32)]).reshape(-1, 15)
+    blocks = np.concatenate([np.full((v.shape[0], 1), 6.0, np.float32), v], axis=1)
+    pad = (-blocks.shape[0]) % 64
+    blocks = np.concatenate([blocks, np.zeros((pad, 16), np.float32)])
+    x = np.ascontiguousarray(blocks.reshape(-1, 1024))
+    check_quantize(gpu, orc, x, (0, 0), gscale=1.0, deq=False)
+
+
+def test_random_shapes_and_values(gpu, orc):
+    """Seeded random shapes (rows 1..257, cols 16..4096), dtypes, magnitudes, offset ranges
+    (the certified ranges and, every sixth case, one beyond +-8 for the exact search) and
+    special values: zero blocks, signed zeros, an outlier, a subnormal block."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        rows, cols = int(rng.integers(1, 258)), 16 * int(rng.integers(1, 257))
+        x = (rng.standard_normal((rows, cols)) * np.float32(np.exp(rng.uniform(-20, 20))))
+        x = x.astype(np.float32)
+        r, c = int(rng.integers(0, rows)), 16 * int(rng.integers(0, cols // 16))
+        kind = case % 5
+        if kind == 0:
+            x[r, c:c + 16] = 0.0
+        elif kind == 1:
+            x[r, c:c + 16] = -0.0
+        elif kind == 2:
+            x[r, c] *= np.float32(1e6)
+        elif kind == 3:
+            x[r, c:c + 16] = np.float32(1e-40) * np.arange(16, dtype=np.float32)
+        lo, hi = -int(rng.integers(0, 9)), int(rng.integers(0, 9))
+        if case % 6 == 5:
+            lo, hi = -12, 10
+        xin = workloads.to_bf16_bits(x) if case % 2 == 0 else x
+        check_quantize(gpu, orc, xin, (lo, hi))
