@@ -333,8 +333,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 //    it) a_i > amax/128: every nonzero product and partial sum is a multiple
 //    of 2^(E-15) below 2^(E+8), E the exponent of amax (23 bits). S2 is a
 //    multiple of 1/4 below 577.
-//  * K_f is formed in FP64: d S2 - 2 S1 is exact (< 40 significant bits),
-//    the product with d is rounded once (relative 2^-53).
+//  * K_f = d^2 S2 - 2d S1 is formed in FP64 with one rounding (relative
+//    2^-53): d has at most 24 significant bits, so d^2 and 2d S1 (at most
+//    48 bits each) are exact and one fused multiply-add forms the rest.
 //  * The contract's FP32 SSE differs from E_f by at most
 //    delta_f <= 2u (sum x^_i^2 / 8 + 14 E_f) (u = 2^-24): per element the
 //    rounding of x^, e and e^2 moves e^2 by <= 2u(V_i d |t_i| + t_i^2) to
@@ -343,9 +344,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 //    E_f <= |K_f - K_0| + E_0 this gives a per-candidate margin
 //    M_f = 2^-18 |D_f| + 2^-23 (0.3 A2 + 15 E_0) (+ FP64/FP32 rounding),
 //    D_f = K_f - K_0 (candidate 0 = offset 0 as reference).
-//  * Winner w = first candidate with least U_f = D_f + M_f. If every other
-//    candidate has L_f = D_f - M_f > U_w, its SSE is certainly larger and w is
-//    the contract's choice. Otherwise (near-ties, or a block outside the
+//  * Winner w = first candidate with least D_f; U_f = D_f + M_f and
+//    L_f = D_f - M_f are both increasing in D_f, so w also has the least U.
+//    If every other candidate has L_f > U_w (it suffices to test the
+//    runner-up in D), its SSE is certainly larger and w is the contract's
+//    choice. Otherwise (near-ties, or a block outside the
 //    range where the argument holds: non-normal candidate patterns, amax
 //    outside [2^-40, 2^60]) the lane evaluates the contract's FP32 SSE
 //    exactly for the candidates that could win and applies the visiting-order
@@ -415,10 +418,16 @@ __device__ __forceinline__ constexpr int slot_offset(int s) {
   return s == 0 ? 0 : (FLO + s - 1 < 0 ? FLO + s - 1 : FLO + s);
 }
 
-struct CertEntry {  // per pattern: decode d, encode r = 1/d, d in FP64
-  float d, r;
-  double dd;
+// Per pattern: d^2 and -2d in FP64 (both exact: d has at most 24 significant
+// bits) and the encode scale r = 1/d. Rows past pattern 126 are zero: a
+// candidate there codes every element to 0 and scores K = 0, i.e. the block's
+// full energy, which no eligible block's leader or contender can reach (the
+// offset-0 candidate already removes more than 0.99 amax^2 of it).
+struct CertEntry {
+  double dd2, ntw;
+  float r, pad0, pad1, pad2;
 };
+constexpr int kCertRows = 136;
 
 // Max of |x| bit patterns of 16 bf16 values packed in 8 words (packed 16-bit max).
 __device__ __forceinline__ uint32_t bf16_block_absmax_bits(const uint32_t (&w)[8]) {
@@ -435,13 +444,14 @@ template <int FLO, int FHI, bool RANGE_FIXED>
 __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs a) {
   constexpr int NC = FHI - FLO + 1;  // visiting slots (offset 0 included)
   __shared__ f32x2 tbl[128];
-  __shared__ CertEntry ctbl[128];
+  __shared__ CertEntry ctbl[kCertRows];
   const float sg = resolve_tensor_scale(a);
   const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
   build_scale_table(tbl, sg);
-  if (threadIdx.x < 127) {
-    const f32x2 dr = tbl[threadIdx.x];
-    ctbl[threadIdx.x] = CertEntry{dr.x, dr.y, (double)dr.x};
+  if (threadIdx.x < kCertRows) {
+    const f32x2 dr = threadIdx.x < 127 ? tbl[threadIdx.x] : f32x2{0.0f, 0.0f};
+    const double dd = (double)dr.x;
+    ctbl[threadIdx.x] = CertEntry{dd * dd, -2.0 * dd, dr.y, 0.0f, 0.0f, 0.0f};
   }
   __syncthreads();
 
@@ -468,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
       } else {
         // certificate applies: every candidate pattern normal, amax in
         // [2^-40, 2^60]; other blocks take the exact path below. Candidates
-        // above pattern 126 are skipped (scored +inf).
+        // above pattern 126 read the zero rows of the table.
         const bool eligible = ((int)p0 + FLO >= 8) && am >= 0x2B800000u && am <= 0x5D800000u;
         const int p0b = max((int)p0, -FLO);  // keeps table indices >= 0
         float a2 = dot2_first(__builtin_bit_cast(bf16x2, w[0]), __builtin_bit_cast(bf16x2, w[0]));
@@ -478,48 +488,57 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
                                                __builtin_bit_cast(bf16x2, w[k]), a2, false);
         const double a2ub = (double)a2 * (1.0 + 0x1p-18) + 0x1p-120;
 
-        float D[NC], M[NC];
+        // Leader = first candidate with the least D (the margin is monotone in
+        // D, so this is also a candidate with the least U = D + M); only the
+        // runner-up's D is needed to decide whether any other candidate's
+        // L = D - M reaches the leader's U.
+        float D[NC];
         double k0 = 0.0;
         float cst = 0.0f;  // block part of the margin
-        float best_u = INFINITY;
+        float best_d = 0.0f, second_d = INFINITY;
         uint32_t cw[2] = {0u, 0u};
 #pragma unroll
         for (int sl = 0; sl < NC; ++sl) {
           const int f = slot_offset<FLO>(sl);
           const int p = p0b + f;
-          const bool valid = (RANGE_FIXED || (f >= a.f_lo && f <= a.f_hi)) && p <= 126;
-          const CertEntry ce = ctbl[min(p, 126)];
+          const CertEntry ce = ctbl[p];
           float s1, s2;
           candidate_stats(x, w, ce.r, cw, s1, s2);
-          const double kf = ce.dd * __builtin_fma(ce.dd, (double)s2, -2.0 * (double)s1);
+          // K_f = d^2 S2 - 2 d S1: both products exact, one rounding.
+          const double kf = __builtin_fma(ce.dd2, (double)s2, ce.ntw * (double)s1);
+          float df;
           if (sl == 0) {
             k0 = kf;
+            df = 0.0f;
             const double e0ub = kf + a2ub + __builtin_fabs(kf) * 0x1p-50;
             cst = (float)((0.3 * a2ub + 15.0 * (e0ub > 0.0 ? e0ub : 0.0)) * 0x1p-23 +
                           (__builtin_fabs(kf) + a2ub) * 0x1p-50) * (1.0f + 0x1p-20f) +
                   0x1p-120f;
+          } else {
+            df = (float)(kf - k0);
           }
-          float df = (float)(kf - k0);
-          float mf = __builtin_fmaf(__builtin_fabsf(df), 0x1p-18f, cst);
-          if (!valid) {
-            df = INFINITY;
-            mf = 0.0f;
-          }
+          if (!RANGE_FIXED && (f < a.f_lo || f > a.f_hi)) df = INFINITY;
           D[sl] = df;
-          M[sl] = mf;
-          const float u = df + mf;
-          if (sl == 0 || u < best_u) {
-            best_u = u;
+          if (sl == 0) {
+            best_d = df;
             best_p = (uint32_t)p;
             bc0 = cw[0];
             bc1 = cw[1];
+          } else {
+            const bool lt = df < best_d;
+            second_d = lt ? best_d : fminf(second_d, df);
+            if (lt) {
+              best_d = df;
+              best_p = (uint32_t)p;
+              bc0 = cw[0];
+              bc1 = cw[1];
+            }
           }
         }
-        // Candidates that might tie or beat the leader (which always counts once).
-        int contenders = 0;
-#pragma unroll
-        for (int sl = 0; sl < NC; ++sl) contenders += (D[sl] - M[sl] <= best_u) ? 1 : 0;
-        if (!eligible || contenders > 1) {
+        const float best_u = best_d + __builtin_fmaf(__builtin_fabsf(best_d), 0x1p-18f, cst);
+        const bool contested =
+            second_d - __builtin_fmaf(__builtin_fabsf(second_d), 0x1p-18f, cst) <= best_u;
+        if (!eligible || best_p > 126u || contested) {
           // Exact contract evaluation over the candidates that could win,
           // in visiting order.
           const uint32_t lead = best_p;
@@ -530,7 +549,8 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
             const int f = slot_offset<FLO>(sl);
             const int p = (int)p0 + f;
             const bool valid = (RANGE_FIXED || (f >= a.f_lo && f <= a.f_hi)) && p >= 0 && p <= 126;
-            const bool need = valid && (!eligible || (uint32_t)p == lead || D[sl] - M[sl] <= best_u);
+            const float lf = D[sl] - __builtin_fmaf(__builtin_fabsf(D[sl]), 0x1p-18f, cst);
+            const bool need = valid && (!eligible || (uint32_t)p == lead || lf <= best_u);
             if (need) {
               const f32x2 dr = tbl[p];
               uint32_t c0, c1;
