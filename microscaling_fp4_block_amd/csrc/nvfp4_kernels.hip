@@ -333,9 +333,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 //    it) a_i > amax/128: every nonzero product and partial sum is a multiple
 //    of 2^(E-15) below 2^(E+8), E the exponent of amax (23 bits). S2 is a
 //    multiple of 1/4 below 577.
-//  * K_f = d^2 S2 - 2d S1 is formed in FP64 with one rounding (relative
-//    2^-53): d has at most 24 significant bits, so d^2 and 2d S1 (at most
-//    48 bits each) are exact and one fused multiply-add forms the rest.
+//  * K_f = d^2 S2 - 2d S1 is formed in FP64: d has at most 24 significant
+//    bits, so d^2 and 2d S1 (at most 48 bits each) are exact; K_0 takes one
+//    rounding, D_f = K_f - K_0 two (-2d S1 - K_0, then + d^2 S2), each
+//    relative 2^-53 of terms below 3 A2.
 //  * The contract's FP32 SSE differs from E_f by at most
 //    delta_f <= 2u (sum x^_i^2 / 8 + 14 E_f) (u = 2^-24): per element the
 //    rounding of x^, e and e^2 moves e^2 by <= 2u(V_i d |t_i| + t_i^2) to
@@ -454,6 +455,16 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
     ctbl[threadIdx.x] = CertEntry{dd * dd, -2.0 * dd, dr.y, 0.0f, 0.0f, 0.0f};
   }
   __syncthreads();
+  // Default pattern in one multiply: q = fl(am * c6), c6 = 1/(6 S_g) rounded
+  // once, and the contract's t = fl(fl(am / 6) / S_g) are each within
+  // 2^-23 (relative) of am / (6 S_g), so they differ by at most 4 ulps of q.
+  // RNE to E4M3 changes only at midpoints (low 20 bits of the binary32
+  // pattern 0x80000 in E4M3's normal range), so when q is more than 8 ulps
+  // from a midpoint, q and t give the same pattern. Otherwise (or for q in
+  // E4M3's subnormal range, or S_g outside [2^-100, 2^100]) t is formed as
+  // the contract does.
+  const float c6 = (float)(1.0 / (6.0 * (double)sg));
+  const bool c6_ok = sg_ok && sg >= 0x1p-100f && sg <= 0x1p100f;
 
   const uint32_t stride = gridDim.x * kThreads;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
@@ -470,7 +481,10 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
 
     uint32_t best_p = 0x7Fu, bc0 = 0u, bc1 = 0u;
     if (sg_ok && am < 0x7F800000u) {
-      const float t = (__uint_as_float(am) / 6.0f) / sg;
+      float t = __uint_as_float(am) * c6;
+      const bool near_mid = ((__float_as_uint(t) - 0x80000u + 8u) & 0xFFFFFu) <= 16u;
+      if (!c6_ok || near_mid || !(t >= 0x1p-6f || am == 0u))
+        t = (__uint_as_float(am) / 6.0f) / sg;
       const uint32_t p0 = e4m3_rne_sat(t);
       if (NC == 1) {
         best_p = p0;
@@ -504,10 +518,10 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
           const CertEntry ce = ctbl[p];
           float s1, s2;
           candidate_stats(x, w, ce.r, cw, s1, s2);
-          // K_f = d^2 S2 - 2 d S1: both products exact, one rounding.
-          const double kf = __builtin_fma(ce.dd2, (double)s2, ce.ntw * (double)s1);
           float df;
           if (sl == 0) {
+            // K_0 = d^2 S2 - 2d S1: both products exact, one rounding.
+            const double kf = __builtin_fma(ce.dd2, (double)s2, ce.ntw * (double)s1);
             k0 = kf;
             df = 0.0f;
             const double e0ub = kf + a2ub + __builtin_fabs(kf) * 0x1p-50;
@@ -515,7 +529,8 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
                           (__builtin_fabs(kf) + a2ub) * 0x1p-50) * (1.0f + 0x1p-20f) +
                   0x1p-120f;
           } else {
-            df = (float)(kf - k0);
+            // D_f = K_f - K_0 = d^2 S2 + (-2d S1 - K_0): two FP64 roundings.
+            df = (float)__builtin_fma(ce.dd2, (double)s2, __builtin_fma(ce.ntw, (double)s1, -k0));
           }
           if (!RANGE_FIXED && (f < a.f_lo || f > a.f_hi)) df = INFINITY;
           D[sl] = df;

@@ -153,3 +153,30 @@ def test_magnitude_edges_f32(gpu, orc):
         sg = np.float32(np.abs(x).max() / np.float32(2688))
         check_given(gpu, orc, x, sg, (-2, 6))
         check_given(gpu, orc, x, sg, (-8, 8))
+
+
+def test_default_pattern_near_e4m3_midpoints(gpu, orc):
+    """The default pattern p0 = E4M3(fl(fl(amax / 6) / S_g)) where that quotient sits on or
+    within a few ulps of an E4M3 rounding midpoint: block maxima on every bf16 significand
+    over 18 binades, S_g = fl(2^j / 6) moved by -10..10 ulps, so the quotient is amax 2^-j
+    up to a few ulps and every midpoint with five significant bits is met."""
+    rng = np.random.default_rng(31)
+    sig = np.arange(128, 256, dtype=np.float32) / np.float32(128)
+    am = np.concatenate([sig * np.float32(2.0 ** e) for e in range(-8, 10)]).astype(np.float32)
+    rest = (rng.uniform(-1, 1, (am.size, 15)) * am[:, None]).astype(np.float32)
+    xh = workloads.to_bf16_bits(np.concatenate([am[:, None], rest], 1)).reshape(-1, 1024)
+    amax = np.abs(workloads.bf16_bits_to_f32(xh)).reshape(-1, 16).max(1)
+    near = ties = 0
+    for j in (0, 3):
+        base = int(np.array([2.0 ** j / 6], np.float32).view(np.uint32)[0])
+        for k in range(-10, 11):
+            sg = np.array([base + k], np.uint32).view(np.float32)[0]
+            t = ((amax / np.float32(6)).astype(np.float32) / sg).astype(np.float32)
+            tb = t.view(np.uint32).astype(np.int64)
+            normal = (t >= 2.0 ** -6) & (t < 448)
+            near += int(np.sum(normal & (((tb - 0x80000 + 8) & 0xFFFFF) <= 16)))
+            ties += int(np.sum(normal & ((tb & 0xFFFFF) == 0x80000)))
+            for offsets in [(0, 0), (-2, 6)]:
+                check_given(gpu, orc, xh, sg, offsets)
+    print(f"[p0] blocks within 8 ulps of an E4M3 midpoint: {near}, exactly on one: {ties}")
+    assert near > 1000 and ties > 100
