@@ -95,6 +95,71 @@ def event_time_ms(torch, fn, iters: int, stream) -> float:
     return start.elapsed_time(end) / iters
 
 
+def launch_times_ms(torch, fn, iters: int, stream, between=None) -> np.ndarray:
+    """GPU time of each of `iters` calls of fn, from an event pair around each call;
+    `between` (if given) runs after each pair, outside the timed interval."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+        if between is not None:
+            between()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def percentiles(t: np.ndarray):
+    p10, p50, p90 = np.percentile(t, [10, 50, 90])
+    return float(p10), float(p50), float(p90)
+
+
+def graph_time_ms(torch, fn, reps: int, stream, replays: int = 5) -> float:
+    """Per-call GPU time with the host out of the loop: `reps` calls of fn captured in
+    one HIP graph, replayed `replays` times."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    t = event_time_ms(torch, graph.replay, replays, stream) / reps
+    del graph
+    return t
+
+
+class CacheFlush:
+    """Evicts the 256 MB Infinity Cache between timed launches: a 512 MiB device copy
+    (1 GiB of traffic through the cache)."""
+
+    def __init__(self, torch, dev):
+        self.src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        self.dst = torch.empty_like(self.src)
+
+    def __call__(self):
+        self.dst.copy_(self.src)
+
+
+def copy_gbs(torch, dev, stream, nbytes: int = 1 << 30, iters: int = 10) -> float:
+    """A plain device-to-device copy (torch's copy_, which the HIP runtime serves with its
+    own blit kernel) in read + write GB/s: a streaming rate measured on the box, beside
+    the published peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = event_time_ms(torch, lambda: dst.copy_(src), iters, stream)
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(x_host: np.ndarray, budget_s: float = 10.0) -> dict:
     """The oracle, as it stands, on a row sample of the same tensor (quantize + dequantize)."""
     import oracle
@@ -185,17 +250,22 @@ def rocpd_summary(dbs):
 
 
 def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
-    """Markdown table of every workload: passes timed with HIP events, oracle beside."""
+    """Markdown table of every workload, passes timed with HIP events: per-call GPU time
+    of calls captured in a HIP graph (host out of the loop), the eager call rate, the
+    search pass's per-launch p50 with p10 and p90, and its p50 with the Infinity Cache
+    flushed before every launch; the oracle beside."""
     import oracle
 
     oracle.build(force=False)
     threads = min(16, os.cpu_count() or 1)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    print("| # | workload | quantize call GB/s | search pass us (GB/s) | amax pass us | "
+    flush = CacheFlush(torch, dev)
+    print("| # | workload | quantize call GB/s (eager; graph) | search pass us, graph (GB/s) | "
+          "search pass us per launch: p50 [p10, p90] warm; p50 cold | amax pass us | "
           "max-scaling control us | SS / control | dequantize us (GB/s) | oracle quantize s "
           f"({threads} threads) |")
-    print("|---|---|---|---|---|---|---|---|---|")
+    print("|---|---|---|---|---|---|---|---|---|---|")
     for idx in (1, 2, 3, 4, 5):
         w = workloads.WORKLOADS[idx]
         xh = workloads.workload(idx)
@@ -240,9 +310,13 @@ def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
         while time.perf_counter() - t0 < warm_s:
             call()
         torch.cuda.synchronize()
-        ms = {k: event_time_ms(torch, f, iters, stream)
+        reps = 20 if n >= (1 << 24) else 100
+        ms = {k: graph_time_ms(torch, f, reps, stream)
               for k, f in (("call", call), ("search", search), ("amax", amax),
                            ("control", control), ("deq", deq))}
+        ms["call_eager"] = event_time_ms(torch, call, iters, stream)
+        warm = percentiles(launch_times_ms(torch, search, iters, stream))
+        cold = percentiles(launch_times_ms(torch, search, 30, stream, between=flush))
         t1 = time.perf_counter()
         if sink:
             oracle.quantize_kv_sink(xh, nf, nl, *offs, hadamard=had, nthreads=threads)
@@ -250,8 +324,11 @@ def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
             oracle.quantize(xh, *offs, hadamard=had, nthreads=threads)
         t_or = time.perf_counter() - t1
         gbs = lambda b, m: b / (m * 1e-3) / 1e9
-        print(f"| {idx} | {w['name']} | {gbs(qbytes, ms['call']):.0f} | "
+        print(f"| {idx} | {w['name']} | {gbs(qbytes, ms['call_eager']):.0f}; "
+              f"{gbs(qbytes, ms['call']):.0f} | "
               f"{ms['search'] * 1e3:.1f} ({gbs(qbytes, ms['search']):.0f}) | "
+              f"{warm[1] * 1e3:.1f} [{warm[0] * 1e3:.1f}, {warm[2] * 1e3:.1f}]; "
+              f"{cold[1] * 1e3:.1f} | "
               f"{ms['amax'] * 1e3:.1f} | {ms['control'] * 1e3:.1f} | "
               f"{ms['search'] / ms['control']:.2f} | {ms['deq'] * 1e3:.1f} "
               f"({gbs(dbytes, ms['deq']):.0f}) | {t_or:.2f} |", flush=True)
@@ -570,6 +647,8 @@ def main():
     ms_amax = event_time_ms(torch, amax_only, iters, stream)
     ms_ctrl = event_time_ms(torch, control_only, iters, stream)
     ms_deq = event_time_ms(torch, dequant_only, iters, stream)
+    s10, s50, s90 = percentiles(launch_times_ms(torch, search_only, iters, stream))
+    copy_rate = copy_gbs(torch, dev, stream)
     qbytes = quantize_bytes(n, 2)
     search_gbs = search_pass_bytes(n, 2) / (ms_search * 1e-3) / 1e9
     ncand = OFFSETS[1] - OFFSETS[0] + 1
@@ -613,6 +692,7 @@ def main():
         "breakdown": {
             "search_pass_ms": round(ms_search, 4),
             "search_pass_gbs": round(search_gbs, 2),
+            "search_pass_per_launch_ms_p10_p50_p90": [round(s10, 4), round(s50, 4), round(s90, 4)],
             "amax_pass_ms": round(ms_amax, 4),
             "amax_pass_gbs": round(n * 2 / (ms_amax * 1e-3) / 1e9, 2),
             "quantize_call_ms": round(quant_call_ms, 4),
@@ -621,6 +701,8 @@ def main():
             "scalesearch_over_max_scaling": round(ms_search / ms_ctrl, 3),
             "dequantize_bf16_ms": round(ms_deq, 4),
             "dequantize_bf16_gbs": round(dequantize_bytes(n, 2) / (ms_deq * 1e-3) / 1e9, 2),
+            "hip_d2d_copy_gbs": round(copy_rate, 1),
+            "step_frac_of_d2d_copy": round(value / copy_rate, 4),
             "wall_s_timed_region": round(wall, 3),
         },
     }
