@@ -66,6 +66,21 @@ def committed_traffic(kernel: str):
         if line.startswith("traffic_bytes_per_launch") and kernel in line:
             traffic = int(line.rsplit("|", 1)[1].strip())
     return traffic if src_hash == kernel_source_hash() else None
+
+
+def committed_valu_issue(kernel: str):
+    """Fraction of the kernel's cycles in which its CUs issued VALU, from the committed
+    counter summary (SQ_INSTS_VALU per CU over GRBM_GUI_ACTIVE per XCD), if that summary
+    was taken on the current kernel sources (else None)."""
+    if not os.path.exists(PROFILE_SUMMARY):
+        return None
+    src_hash, frac = None, None
+    for line in open(PROFILE_SUMMARY):
+        if line.startswith("source_hash:"):
+            src_hash = line.split(":", 1)[1].strip()
+        if line.startswith("valu_issue_frac") and kernel in line:
+            frac = float(line.rsplit("|", 1)[1].strip())
+    return frac if src_hash == kernel_source_hash() else None
 ROWS, COLS = 8192, 28672
 OFFSETS = (-2, 6)
 
@@ -682,6 +697,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(alg_tflops / VALU_PEAK_TFLOPS, 4),
             "traffic": committed_traffic(SEARCH_KERNEL),
+            "valu_issue_frac_counters": committed_valu_issue(SEARCH_KERNEL),
             "kernel": SEARCH_KERNEL,
             "kernel_ms": round(ms_search, 4),
             "flops_per_launch": alg_flops,

@@ -375,19 +375,27 @@ __device__ __forceinline__ float dot2_first(bf16x2 a, bf16x2 b) {
   return r;
 }
 
-// Codes of one candidate (encode scale r) and the exact sums S1 = sum x V,
-// S2 = sum V^2 (x and V carry the same sign, so S1 = sum |x| |V|). Each code
-// word starts from the bits of its first product, a value that dies there:
-// the four byte-selected converts overwrite all of it, and the convert can
-// write in place without a copy.
-__device__ __forceinline__ void candidate_stats(const float (&x)[16], const uint32_t (&w)[8],
-                                                float r, uint32_t (&cw)[2], float &s1,
-                                                float &s2) {
+// Codes of one candidate and its exact sums S1 = sum x V, S2 = sum V^2 (x and
+// V carry the same sign, so S1 = sum |x| |V|; hardware E2M1 decode to bf16,
+// which is exact, and v_dot2_f32_bf16), from products y formed with the
+// candidate's own encode scale (SC_LOG2 = 0) or with that of the candidate
+// eight patterns below (+1) or above (-1): patterns p and p + 8 (both normal)
+// have d_{p+8} = 2 d_p and r_{p+8} = r_p / 2 exactly, so y_{p+8} = y_p / 2, and
+// the convert's power-of-two scale operand divides by 2^SC_LOG2 exactly before
+// rounding. Each code word is converted in place over the candidate's
+// previous word (all four byte selects overwrite it).
+template <int SC_LOG2>
+__device__ __forceinline__ void candidate_stats_y(const float (&y)[16], const uint32_t (&w)[8],
+                                                  uint32_t (&cw)[2], float &s1, float &s2) {
+  constexpr float sc = SC_LOG2 == 0 ? 1.0f : (SC_LOG2 > 0 ? 2.0f : 0.5f);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float y0 = x[2 * j] * r, y1 = x[2 * j + 1] * r;
-    const uint32_t old = (j & 3) == 0 ? __float_as_uint(y0) : cw[j >> 2];
-    cw[j >> 2] = fp4_encode_pair(old, y0, y1, j);
+    switch (j & 3) {
+      case 0: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw[j >> 2], y[2 * j], y[2 * j + 1], sc, 0); break;
+      case 1: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw[j >> 2], y[2 * j], y[2 * j + 1], sc, 1); break;
+      case 2: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw[j >> 2], y[2 * j], y[2 * j + 1], sc, 2); break;
+      default: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw[j >> 2], y[2 * j], y[2 * j + 1], sc, 3); break;
+    }
   }
   bf16x2 v = fp4_decode_pair_bf16(cw[0], 0);
   float a = dot2_first(__builtin_bit_cast(bf16x2, w[0]), v);
@@ -418,6 +426,37 @@ template <int FLO>
 __device__ __forceinline__ constexpr int slot_offset(int s) {
   return s == 0 ? 0 : (FLO + s - 1 < 0 ? FLO + s - 1 : FLO + s);
 }
+
+// Evaluation order of the certified search: candidates in visiting order,
+// each followed at once by its in-range twins eight patterns up and down,
+// which reuse its products (shift +1: scale 2, -1: scale 1/2, 0: own
+// products). slot_of maps an evaluation position back to the visiting slot.
+template <int FLO, int FHI>
+struct EvalOrder {
+  static constexpr int NC = FHI - FLO + 1;
+  int off[NC];
+  int shift[NC];
+  int slot_of[NC];
+  constexpr EvalOrder() : off(), shift(), slot_of() {
+    bool used[NC] = {};
+    int k = 0;
+    for (int sl = 0; sl < NC; ++sl) {
+      const int f = slot_offset<FLO>(sl);
+      if (used[f - FLO]) continue;
+      const int grp[3] = {f, f + 8, f - 8};
+      const int sh[3] = {0, 1, -1};
+      for (int g = 0; g < 3; ++g) {
+        const int h = grp[g];
+        if (h < FLO || h > FHI || used[h - FLO]) continue;
+        used[h - FLO] = true;
+        off[k] = h;
+        shift[k] = sh[g];
+        slot_of[k] = h == 0 ? 0 : (h < 0 ? h - FLO + 1 : h - FLO);
+        ++k;
+      }
+    }
+  }
+};
 
 // Per pattern: d^2 and -2d in FP64 (both exact: d has at most 24 significant
 // bits) and the encode scale r = 1/d. Rows past pattern 126 are zero: a
@@ -506,20 +545,32 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
         // D, so this is also a candidate with the least U = D + M); only the
         // runner-up's D is needed to decide whether any other candidate's
         // L = D - M reaches the leader's U.
-        float D[NC];
+        constexpr EvalOrder<FLO, FHI> ord;
+        float D[NC];  // by visiting slot
         double k0 = 0.0;
         float cst = 0.0f;  // block part of the margin
         float best_d = 0.0f, second_d = INFINITY;
         uint32_t cw[2] = {0u, 0u};
+        float y[16];
 #pragma unroll
-        for (int sl = 0; sl < NC; ++sl) {
-          const int f = slot_offset<FLO>(sl);
+        for (int k = 0; k < NC; ++k) {
+          const int f = ord.off[k];
+          const int sl = ord.slot_of[k];
           const int p = p0b + f;
           const CertEntry ce = ctbl[p];
+          if (ord.shift[k] == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y[i] = x[i] * ce.r;
+          }
           float s1, s2;
-          candidate_stats(x, w, ce.r, cw, s1, s2);
+          if (ord.shift[k] == 0)
+            candidate_stats_y<0>(y, w, cw, s1, s2);
+          else if (ord.shift[k] > 0)
+            candidate_stats_y<1>(y, w, cw, s1, s2);
+          else
+            candidate_stats_y<-1>(y, w, cw, s1, s2);
           float df;
-          if (sl == 0) {
+          if (k == 0) {
             // K_0 = d^2 S2 - 2d S1: both products exact, one rounding.
             const double kf = __builtin_fma(ce.dd2, (double)s2, ce.ntw * (double)s1);
             k0 = kf;
@@ -534,7 +585,7 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
           }
           if (!RANGE_FIXED && (f < a.f_lo || f > a.f_hi)) df = INFINITY;
           D[sl] = df;
-          if (sl == 0) {
+          if (k == 0) {
             best_d = df;
             best_p = (uint32_t)p;
             bc0 = cw[0];
