@@ -99,18 +99,20 @@ __device__ __forceinline__ TileRegs load_chunk(const AttnArgs &a, uint64_t row_b
 // Decode a loaded chunk into LDS: K row-major [key][d]; V transposed [d][key]
 // with the key column XOR-ed with 16 (d >> 5), which spreads the four lanes
 // that share a key over different banks and keeps 4-key groups contiguous.
-__device__ __forceinline__ void store_chunk(const TileRegs &r, bool live, uint32_t tid,
-                                            _Float16 *Ks, _Float16 *Vt) {
+// Keys past the segment end were loaded as zero codes and scale bytes, so
+// they decode to zeros.
+__device__ __forceinline__ void store_chunk(const TileRegs &r, uint32_t tid, _Float16 *Ks,
+                                            _Float16 *Vt) {
   const uint32_t key = tid >> 2, c = tid & 3u;
-  const float k0 = live ? scale_value(r.ksb & 0xFFu) : 0.0f;
-  const float k1 = live ? scale_value((r.ksb >> 8) & 0xFFu) : 0.0f;
+  const float k0 = scale_value(r.ksb & 0xFFu);
+  const float k1 = scale_value((r.ksb >> 8) & 0xFFu);
   _Float16 *kd = &Ks[key * kKsStride + 32u * c];
   *(f16x8 *)(kd) = decode8(r.kw.x, k0);
   *(f16x8 *)(kd + 8) = decode8(r.kw.y, k0);
   *(f16x8 *)(kd + 16) = decode8(r.kw.z, k1);
   *(f16x8 *)(kd + 24) = decode8(r.kw.w, k1);
-  const float v0 = live ? scale_value(r.vsb & 0xFFu) : 0.0f;
-  const float v1 = live ? scale_value((r.vsb >> 8) & 0xFFu) : 0.0f;
+  const float v0 = scale_value(r.vsb & 0xFFu);
+  const float v1 = scale_value((r.vsb >> 8) & 0xFFu);
   const f16x8 x[4] = {decode8(r.vw.x, v0), decode8(r.vw.y, v0), decode8(r.vw.z, v1),
                       decode8(r.vw.w, v1)};
   const uint32_t pk = key ^ (16u * c);
@@ -176,6 +178,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 Vt[2][kAttnD * kVtStride];
   __shared__ f32x2 ptbl[128];
   __shared__ float pthr[128];
+  __shared__ f32x2 pthr2[127];  // (pthr[k], pthr[k + 1]): both bounds in one read
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6, g = lane >> 5;
   const uint32_t col = lane & 31u;
@@ -256,6 +259,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     }
   }
   __syncthreads();  // the P tables
+  // published by the barrier that ends the first segment's prologue, before any use
+  if (tid < 127u) pthr2[tid] = f32x2{pthr[tid], pthr[tid + 1u]};
 
   f32x16 o[4];
 #pragma unroll
@@ -264,11 +269,122 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   float unit = vg;  // the factor (tensor scale of V) the accumulator o is counted in
   uint32_t buf = 0;
 
+  // S^T = K Q^T for one tile of 32 keys: sacc[v] = key 8 (v >> 2) + 4 g + (v & 3)
+  // of the tile, query qi.
+  auto s_tile = [&](auto sink_tag, const _Float16 *K) {
+    constexpr bool SINK = decltype(sink_tag)::value;
+    f32x16 sacc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (!SINK) {
+        const f16x8 ka = *(const f16x8 *)&K[col * kKsStride + 16u * ks + 8u * g];
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], sacc, 0, 0, 0);
+      } else {
+        const bf16x8 ka = *(const bf16x8 *)&K[col * kKsStride + 16u * ks + 8u * g];
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, to_bf16x8(qf[ks]), sacc, 0, 0, 0);
+      }
+    }
+    return sacc;
+  };
+
+  // Keys that are absent (past hi) or not visible to this lane's query score
+  // -inf. Full tiles (every key present and visible to every query of the
+  // wave) are left as they are.
+  auto mask_tile = [&](f32x16 &sacc, uint32_t t0, uint32_t hi) {
+    const bool full = t0 + kKeyTile <= hi && (int64_t)(t0 + kKeyTile - 1u) <= lim_wave;
+    if (!full) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t key = t0 + 8u * (v >> 2) + 4u * g + (v & 3);
+        const bool vis = key < hi && (int64_t)key <= lim;
+        sacc[v] = vis ? sacc[v] : -INFINITY;
+      }
+    }
+  };
+
+  // Online softmax of one tile (base-2 scores s = acc * c2, c2 > 0, so the max
+  // is taken on acc), then P to NVFP4 per 16 keys (keys 16 blk .. +15: 8 in this
+  // lane, 8 in its partner), max scaling, and back to exact fp16 values
+  // V[code] * s. Branch-free, so the matrix instructions issued around it can
+  // run while it executes. Returns the rescale factor of the accumulator.
+  auto softmax_code = [&](const f32x16 &sacc, float c2, f16x8 (&pb)[2]) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+    const float mn = fmaxf(m, mt);
+    // with every score -inf so far, the exponent base 0 gives p = 0 and
+    // alpha = 0 on an accumulator and sum that are still 0
+    const float mb = mn == -INFINITY ? 0.0f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - mb);
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c2, -mb));
+    float ps = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ps += p[v];
+    l = l * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      float am = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, p[8 * blk + e]);
+      am = fmaxf(am, __shfl_xor(am, 32));
+      uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
+      const f32x2 th = pthr2[pat];
+      pat = am >= th.y ? pat + 1u : (am < th.x ? pat - 1u : pat);
+      const f32x2 rs = ptbl[pat];
+      uint32_t cw = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        cw = fp4_encode_pair(cw, p[8 * blk + 2 * j] * rs.x, p[8 * blk + 2 * j + 1] * rs.x, j);
+      pb[blk] = decode8(cw, rs.y);
+    }
+    return alpha;
+  };
+
+  // O^T = alpha O^T: multiplying by alpha = 1 changes nothing, so the wave
+  // skips it when no lane needs it.
+  auto rescale = [&](float alpha) {
+    if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+    }
+  };
+
+  // O^T += V^T P^T for the tile at key offset kb of the chunk; o[t][v] =
+  // output d = 32 t + 8 (v >> 2) + 4 g + (v & 3). Row d = 32 t + col of V^T;
+  // its key columns are XOR-ed with 16 t.
+  auto pv_tile = [&](auto sink_tag, const _Float16 *V, uint32_t kb, const f16x8 (&pb)[2]) {
+    constexpr bool SINK = decltype(sink_tag)::value;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const _Float16 *vrow = &V[(32u * t + col) * kVtStride];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const uint2 x0 = *(const uint2 *)(vrow + ((kb + 16u * blk + 4u * g) ^ (16u * t)));
+        const uint2 x1 = *(const uint2 *)(vrow + ((kb + 16u * blk + 8u + 4u * g) ^ (16u * t)));
+        const uint4 vv = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        if (!SINK)
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[blk],
+                                                        o[t], 0, 0, 0);
+        else
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                         to_bf16x8(pb[blk]), o[t], 0, 0, 0);
+      }
+    }
+  };
+
   // Keys [lo, hi) of one segment, coded (SINK false) or bf16 sink rows of the
-  // cache head or tail ring, in chunks that stay inside the segment. Each chunk
-  // is decoded into LDS buffer buf while the next coded chunk's codes are in
-  // flight; one barrier per chunk publishes it and retires the reads of the
-  // other buffer.
+  // cache head or tail ring, in chunks of 64 keys that stay inside the segment.
+  // Software-pipelined per chunk: tile 1's scores are issued to the matrix
+  // units before tile 0's softmax, tile 0's P V^T before tile 1's softmax, and
+  // tile 1's P V^T before the next chunk is decoded into the other LDS buffer;
+  // one barrier per chunk publishes that buffer and retires the reads of this
+  // one. A chunk's second tile past hi is all masked and adds nothing.
   auto run_segment = [&](auto sink_tag, uint32_t lo, uint32_t hi, bool head) {
     constexpr bool SINK = decltype(sink_tag)::value;
     if (lo >= hi) return;
@@ -283,117 +399,38 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       unit = cunit;
     }
     TileRegs nxt{make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u), 0u, 0u};
-    if (!SINK) nxt = load_chunk(a, coded_base, coded_off, lo, hi, tid);
+    if (SINK) {
+      store_sink_chunk(a, kvh, head, lo, hi, tid, Ks[buf], Vt[buf]);
+    } else {
+      nxt = load_chunk(a, coded_base, coded_off, lo, hi, tid);
+      store_chunk(nxt, tid, Ks[buf], Vt[buf]);
+      if (lo + kChunk < hi) nxt = load_chunk(a, coded_base, coded_off, lo + kChunk, hi, tid);
+    }
+    __syncthreads();
     for (uint32_t c0 = lo; c0 < hi; c0 += kChunk, buf ^= 1u) {
-      if (SINK)
-        store_sink_chunk(a, kvh, head, c0, hi, tid, Ks[buf], Vt[buf]);
-      else
-        store_chunk(nxt, c0 + (tid >> 2) < hi, tid, Ks[buf], Vt[buf]);
-      if (!SINK && c0 + kChunk < hi) nxt = load_chunk(a, coded_base, coded_off, c0 + kChunk, hi, tid);
-      __syncthreads();
-#pragma unroll 1
-      for (uint32_t sub = 0; sub < 2; ++sub) {
-        const uint32_t t0 = c0 + sub * kKeyTile;
-        if (t0 >= hi) break;
-        const _Float16 *K = Ks[buf] + sub * kKeyTile * kKsStride;
-        const _Float16 *V = Vt[buf];
-
-        // S^T = K Q^T: sacc[v] = key 8 (v >> 2) + 4 g + (v & 3) of the tile, query qi.
-        f32x16 sacc = {};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          if (!SINK) {
-            const f16x8 ka = *(const f16x8 *)&K[col * kKsStride + 16u * ks + 8u * g];
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], sacc, 0, 0, 0);
-          } else {
-            const bf16x8 ka = *(const bf16x8 *)&K[col * kKsStride + 16u * ks + 8u * g];
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, to_bf16x8(qf[ks]), sacc, 0, 0, 0);
-          }
-        }
-
-        // Base-2 scores s = acc * c2 (c2 > 0, so the max is taken on acc). Full tiles
-        // (every key present and visible to every query of the wave) skip the masks.
-        float p[16];
-        float mt = -INFINITY;
-        const bool full = t0 + kKeyTile <= hi && (int64_t)(t0 + kKeyTile - 1u) <= lim_wave;
-        if (full) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            p[v] = sacc[v];
-            mt = fmaxf(mt, p[v]);
-          }
+      const _Float16 *K = Ks[buf];
+      const _Float16 *V = Vt[buf];
+      f32x16 sa0 = s_tile(sink_tag, K);
+      mask_tile(sa0, c0, hi);
+      f32x16 sa1 = s_tile(sink_tag, K + kKeyTile * kKsStride);
+      f16x8 pb0[2], pb1[2];
+      const float a0 = softmax_code(sa0, c2, pb0);
+      rescale(a0);
+      mask_tile(sa1, c0 + kKeyTile, hi);
+      pv_tile(sink_tag, V, 0u, pb0);
+      const float a1 = softmax_code(sa1, c2, pb1);
+      rescale(a1);
+      pv_tile(sink_tag, V, kKeyTile, pb1);
+      const uint32_t c1 = c0 + kChunk;
+      if (c1 < hi) {
+        if (SINK) {
+          store_sink_chunk(a, kvh, head, c1, hi, tid, Ks[buf ^ 1u], Vt[buf ^ 1u]);
         } else {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const uint32_t key = t0 + 8u * (v >> 2) + 4u * g + (v & 3);
-            const bool vis = key < hi && (int64_t)key <= lim;
-            p[v] = vis ? sacc[v] : -INFINITY;
-            mt = fmaxf(mt, p[v]);
-          }
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
-        const float mn = fmaxf(m, mt);
-        float alpha = 1.0f;
-        if (mn == -INFINITY) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) p[v] = 0.0f;
-        } else {
-          alpha = __builtin_amdgcn_exp2f(m - mn);  // m = -inf gives 0
-#pragma unroll
-          for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[v], c2, -mn));
-        }
-        float ps = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) ps += p[v];
-        l = l * alpha + ps;
-        m = mn;
-
-        // P to NVFP4 per 16 keys (keys 16 blk .. +15: 8 in this lane, 8 in its
-        // partner), max scaling, then back to exact fp16 values V[code] * s.
-        f16x8 pb[2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          float am = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) am = fmaxf(am, p[8 * blk + e]);
-          am = fmaxf(am, __shfl_xor(am, 32));
-          uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
-          pat = am >= pthr[pat + 1u] ? pat + 1u : (am < pthr[pat] ? pat - 1u : pat);
-          const f32x2 rs = ptbl[pat];
-          uint32_t cw = 0u;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            cw = fp4_encode_pair(cw, p[8 * blk + 2 * j] * rs.x, p[8 * blk + 2 * j + 1] * rs.x, j);
-          pb[blk] = decode8(cw, rs.y);
-        }
-
-        // O^T = alpha O^T + V^T P^T; o[t][v] = output d = 32 t + 8 (v >> 2) + 4 g + (v & 3).
-        // Multiplying by alpha = 1 changes nothing: the wave skips it when no lane needs it.
-        if (__ballot(alpha != 1.0f) != 0ull) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // row d = 32 t + col of V^T; its key columns are XOR-ed with 16 t
-          const _Float16 *vrow = &V[(32u * t + col) * kVtStride];
-          const uint32_t kb = sub * kKeyTile;
-#pragma unroll
-          for (int blk = 0; blk < 2; ++blk) {
-            const uint2 x0 = *(const uint2 *)(vrow + ((kb + 16u * blk + 4u * g) ^ (16u * t)));
-            const uint2 x1 = *(const uint2 *)(vrow + ((kb + 16u * blk + 8u + 4u * g) ^ (16u * t)));
-            const uint4 vv = make_uint4(x0.x, x0.y, x1.x, x1.y);
-            if (!SINK)
-              o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv),
-                                                            pb[blk], o[t], 0, 0, 0);
-            else
-              o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                             to_bf16x8(pb[blk]), o[t], 0, 0, 0);
-          }
+          store_chunk(nxt, tid, Ks[buf ^ 1u], Vt[buf ^ 1u]);
+          if (c1 + kChunk < hi) nxt = load_chunk(a, coded_base, coded_off, c1 + kChunk, hi, tid);
         }
       }
+      __syncthreads();
     }
   };
 
