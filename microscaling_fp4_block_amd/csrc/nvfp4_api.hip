@@ -15,6 +15,9 @@ namespace {
 constexpr int64_t kMaxBlocks = 1ll << 29;  // 32-bit chunk and block indices never overflow
 
 bool dtype_ok(nvfp4_dtype d) { return d == NVFP4_F32 || d == NVFP4_BF16; }
+// a * b <= lim for a, b >= 0, decided without forming a product that could overflow
+bool prod_le(int64_t a, int64_t b, int64_t lim) { return a == 0 || b <= lim / a; }
+constexpr int64_t k2p31 = 1ll << 31;
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t workspace_needed() { return (size_t)kMaxAmaxGroups * sizeof(uint32_t); }
@@ -245,9 +248,9 @@ nvfp4_status kv_sink_impl(const void *kv, nvfp4_dtype dt, int64_t B, int64_t H, 
   if (!global_scale || !dtype_ok(dt)) return NVFP4_EINVAL;
   nvfp4_status st = check_offsets(block, f_lo, f_hi);
   if (st) return st;
-  if (B < 0 || H < 0 || T < 0 || D <= 0 || n_first < 0 || n_last < 0 || n_first + n_last > T)
-    return NVFP4_ESHAPE;
-  if (T > (1ll << 31) || B * H > (1ll << 31)) return NVFP4_ESHAPE;
+  if (B < 0 || H < 0 || T < 0 || D <= 0 || n_first < 0 || n_last < 0) return NVFP4_ESHAPE;
+  if (T > k2p31 || n_first > T || n_last > T || !prod_le(B, H, k2p31)) return NVFP4_ESHAPE;
+  if (n_first + n_last > T) return NVFP4_ESHAPE;
   const int64_t BH = B * H, NS = n_first + n_last, Tm = T - NS;
   if (BH * T > 0 && !kv) return NVFP4_EINVAL;
   if (BH * NS > 0 && !sink) return NVFP4_EINVAL;
@@ -327,10 +330,10 @@ nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scale
                                       void *y, nvfp4_dtype ydt, void *stream) {
   if (!global_scale || !dtype_ok(sink_dt) || !dtype_ok(ydt)) return NVFP4_EINVAL;
   if (block != 16) return NVFP4_EINVAL;
-  if (B < 0 || H < 0 || T < 0 || D <= 0 || D % 16 || n_first < 0 || n_last < 0 ||
-      n_first + n_last > T)
+  if (B < 0 || H < 0 || T < 0 || D <= 0 || D % 16 || n_first < 0 || n_last < 0)
     return NVFP4_ESHAPE;
-  if (T > (1ll << 31) || B * H > (1ll << 31)) return NVFP4_ESHAPE;
+  if (T > k2p31 || n_first > T || n_last > T || !prod_le(B, H, k2p31)) return NVFP4_ESHAPE;
+  if (n_first + n_last > T) return NVFP4_ESHAPE;
   const int64_t BH = B * H, NS = n_first + n_last, Tm = T - NS;
   nvfp4_status st = check_shape(BH * T, D, 0, ydt);
   if (st) return st;
@@ -372,7 +375,10 @@ nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64
   if (B < 0 || H < 0 || T < 0 || t_new < 0 || D <= 0 || D % 16 || n_first < 0 || n_last < 0 ||
       cap < 0)
     return NVFP4_ESHAPE;
-  if (T + t_new > (1ll << 31) || B * H > (1ll << 31) || cap > (1ll << 31)) return NVFP4_ESHAPE;
+  if (T > k2p31 || t_new > k2p31 || n_first > k2p31 || n_last > k2p31 || cap > k2p31 ||
+      !prod_le(B, H, k2p31))
+    return NVFP4_ESHAPE;
+  if (T + t_new > k2p31) return NVFP4_ESHAPE;
   const bool had = flags & NVFP4_HADAMARD128;
   if (had && (dt != NVFP4_BF16)) return NVFP4_EINVAL;
   if (had && D % 128) return NVFP4_ESHAPE;
@@ -522,7 +528,7 @@ nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_scales,
   if (!dtype_ok(out_dt)) return NVFP4_EINVAL;
   if (D != 128) return NVFP4_ESHAPE;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || Nk < 0) return NVFP4_ESHAPE;
-  if (B * Hq > 65535 || Nq > (1ll << 30) || Nk > (1ll << 30)) return NVFP4_ESHAPE;
+  if (!prod_le(B, Hq, 65535) || Nq > (1ll << 30) || Nk > (1ll << 30)) return NVFP4_ESHAPE;
   if (B * Hq * Nq > kMaxBlocks / 8 || B * Hkv * Nk > kMaxBlocks / 8) return NVFP4_ESHAPE;
   if (B * Nq == 0) return NVFP4_OK;
   if (!q_codes || !q_scales || !q_gscale || !k_gscale || !v_gscale || !out) return NVFP4_EINVAL;
@@ -562,7 +568,8 @@ nvfp4_status nvfp4_attention_kv_cache(
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || T < 0 || n_first < 0 || n_last < 0 ||
       cap < 0)
     return NVFP4_ESHAPE;
-  if (B * Hq > 65535 || Nq > (1ll << 30) || T > (1ll << 30) || cap > (1ll << 30))
+  if (!prod_le(B, Hq, 65535) || Nq > (1ll << 30) || T > (1ll << 30) || cap > (1ll << 30) ||
+      n_first > (1ll << 30) || n_last > (1ll << 30))
     return NVFP4_ESHAPE;
   const int64_t mid = T - n_first - n_last;
   if (mid > cap) return NVFP4_ESHAPE;

@@ -167,3 +167,24 @@ def test_attention_kv_cache_argument_checks(lib):
     assert f(*ptrs, 1, 1, 2, 1, 8, 300, 128, 16, 16, 100, P, 0, None) == 2
     assert f(*ptrs, 1, 1, 3, 2, 8, 300, 128, 16, 16, 300, P, 0, None) == 2
     assert f(*ptrs, 1, 1, 2, 1, 0, 300, 128, 16, 16, 300, P, 0, None) == 0
+
+
+def test_huge_dimensions_are_refused_without_overflow(lib):
+    """Dimensions whose products or sums would overflow 64 bits are refused as shapes
+    (the checks bound each factor before multiplying)."""
+    big = 1 << 40
+    q = lib.nvfp4_quantize_kv_sink
+    assert q(P, 1, big, big, 8, 128, 0, 0, 16, -2, 6, 0, P, P, P, P, P, 1 << 20, None) == 2
+    assert q(P, 1, 1, 1, 8, 128, 1 << 62, 1 << 62, 16, -2, 6, 0, P, P, P, P, P, 1 << 20, None) == 2
+    d = lib.nvfp4_dequantize_kv_sink
+    assert d(P, P, P, P, 1, big, big, 300, 128, 128, 128, 16, P, 0, None) == 2
+    assert d(P, P, P, P, 1, 1, 1, 300, 128, 1 << 62, 1 << 62, 16, P, 0, None) == 2
+    a = lib.nvfp4_kv_append
+    assert a(P, 1, big, big, 8, 1, 128, 4, 4, 64, 16, -2, 6, 0, P, P, P, P, P, None) == 2
+    assert a(P, 1, 1, 1, 1 << 62, 1 << 62, 128, 4, 4, 64, 16, -2, 6, 0, P, P, P, P, P, None) == 2
+    assert a(P, 1, 1, 1, 8, 1, 128, 1 << 62, 4, 64, 16, -2, 6, 0, P, P, P, P, P, None) == 2
+    f = lib.nvfp4_attention
+    assert f(*([P] * 9), big, big, 1, 64, 64, 128, 0, P, 0, None) == 2
+    c = lib.nvfp4_attention_kv_cache
+    assert c(*([P] * 13), 1, big, big, 1, 8, 300, 128, 16, 16, 300, P, 0, None) == 2
+    assert c(*([P] * 13), 1, 1, 2, 1, 8, 300, 128, 1 << 62, 1 << 62, 300, P, 0, None) == 2
