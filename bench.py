@@ -202,9 +202,6 @@ def cpu_baseline(x_host: np.ndarray, budget_s: float = 10.0) -> dict:
                       f"quantize [-2,6] + bf16 dequantize, {t:.2f} s wall on {threads} threads"}
 
 
-# quantize_kernel dispatches of a --profile run, in launch order
-PROFILE_PHASES = ["search [-2,6] in the warm-up step"] + ["search [-2,6], S_g given"] * 5 + \
-    ["max-scaling control [0,0], S_g given"] * 5
 COPY_BYTES = 1 << 30
 
 
@@ -231,15 +228,6 @@ def rocpd_summary(dbs):
                 gx, wx, vg, ag, sg, lds = info[name]
                 print(f"{name} | {len(ds)} | {sum(ds) / len(ds):.2f} | {min(ds):.2f} | "
                       f"{max(ds):.2f} | {gx} x {wx} | {vg}/{ag}/{sg} | {lds}")
-            q = [d for n, d in ((n, d / 1000.0) for n, d, *_ in rows)
-                 if n.startswith("void nvfp4::quantize_kernel<true>")]
-            if len(q) >= len(PROFILE_PHASES):
-                by = defaultdict(list)
-                for ph, d in zip(PROFILE_PHASES, q):
-                    by[ph].append(d)
-                print("quantize_kernel<true> by phase:")
-                for ph, ds in by.items():
-                    print(f"  {ph}: n={len(ds)} avg {sum(ds) / len(ds):.2f} us")
         crow = db.execute("select kernel_name, counter_name, value from counters_collection "
                           "order by start").fetchall()
         if crow:
@@ -625,8 +613,8 @@ def main():
         nv.dequantize(codes, scales, g, torch.bfloat16, out=y)
 
     if args.profile:
-        # Fixed launch order, so a profile can be split by phase (see PROFILE_PHASES):
-        # warm-up step, then 5 launches of each phase, then the 1 GiB copy.
+        # Fixed launch order: a warm-up step, then 5 launches of each pass, then the
+        # 1 GiB copies that calibrate the byte counters.
         step()
         gfix = g.clone()
         torch.cuda.synchronize()

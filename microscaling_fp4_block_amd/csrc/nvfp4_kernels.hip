@@ -208,13 +208,21 @@ __device__ __forceinline__ float resolve_tensor_scale(const QuantArgs &a) {
 // +-V[c]. Element pairs go through one convert each way.
 __device__ __forceinline__ float candidate_sse(const float (&x)[16], float d, float r,
                                                uint32_t &c0, uint32_t &c1) {
-  uint32_t cw[2] = {0u, 0u};
-  float s = 0.0f;
+  // all four pairs of a code word are encoded before any is decoded, so the
+  // in-place converts chain without copies; each word starts from the bits of
+  // its first product, a value that dies there (the four byte selects
+  // overwrite all of it)
+  uint32_t cw[2];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float y0 = x[2 * j] * r;
     const float y1 = x[2 * j + 1] * r;
-    cw[j >> 2] = fp4_encode_pair(cw[j >> 2], y0, y1, j);
+    const uint32_t old = (j & 3) == 0 ? __float_as_uint(y0) : cw[j >> 2];
+    cw[j >> 2] = fp4_encode_pair(old, y0, y1, j);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
     const f32x2 v = fp4_decode_pair(cw[j >> 2], j);
     const float xh0 = v.x * d;
     const float xh1 = v.y * d;
@@ -248,11 +256,85 @@ __device__ __forceinline__ void build_scale_table(f32x2 *tbl, float sg) {
 
 // The contract's squared-error term of the block's largest element a under
 // candidate (d, r): fl(fl(a - fl(V d))^2), V the E2M1 value of fl(a r).
+// The contract's SSE of one candidate from products y formed with its own
+// encode scale (SC_LOG2 = 0) or with that of the candidate eight patterns
+// below (+1: y / 2) or above (-1: y * 2); the convert's power-of-two scale
+// operand applies the factor exactly before rounding.
+template <int SC_LOG2>
+__device__ __forceinline__ float sse_from_y(const float (&x)[16], const float (&y)[16], float d,
+                                            uint32_t &c0, uint32_t &c1) {
+  constexpr float sc = SC_LOG2 == 0 ? 1.0f : (SC_LOG2 > 0 ? 2.0f : 0.5f);
+  uint32_t cw[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t old = (j & 3) == 0 ? 0u : cw[j >> 2];
+    switch (j & 3) {
+      case 0: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y[2 * j], y[2 * j + 1], sc, 0); break;
+      case 1: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y[2 * j], y[2 * j + 1], sc, 1); break;
+      case 2: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y[2 * j], y[2 * j + 1], sc, 2); break;
+      default: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y[2 * j], y[2 * j + 1], sc, 3); break;
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f32x2 v = fp4_decode_pair(cw[j >> 2], j);
+    const float xh0 = v.x * d;
+    const float xh1 = v.y * d;
+    const float e0 = fabsf(x[2 * j]) - fabsf(xh0);
+    const float e1 = fabsf(x[2 * j + 1]) - fabsf(xh1);
+    const float q0 = e0 * e0;
+    s = s + q0;
+    const float q1 = e1 * e1;
+    s = s + q1;
+  }
+  c0 = cw[0];
+  c1 = cw[1];
+  return s;
+}
+
 __device__ __forceinline__ float amax_term(float a, float d, float r) {
   const uint32_t c = fp4_encode_pair(0u, a * r, 0.0f, 0);
   const float e = a - fp4_decode_pair(c, 0).x * d;
   return e * e;
 }
+
+// Offset of visiting slot s: slot 0 is f = 0, then FLO, FLO+1, ... without 0.
+template <int FLO>
+__device__ __forceinline__ constexpr int slot_offset(int s) {
+  return s == 0 ? 0 : (FLO + s - 1 < 0 ? FLO + s - 1 : FLO + s);
+}
+
+// Evaluation order of the fixed-range searches: candidates in visiting order,
+// each followed at once by its in-range twins eight patterns up and down,
+// which reuse its products (shift +1: scale 2, -1: scale 1/2, 0: own
+// products). slot_of maps an evaluation position back to the visiting slot.
+template <int FLO, int FHI>
+struct EvalOrder {
+  static constexpr int NC = FHI - FLO + 1;
+  int off[NC];
+  int shift[NC];
+  int slot_of[NC];
+  constexpr EvalOrder() : off(), shift(), slot_of() {
+    bool used[NC] = {};
+    int k = 0;
+    for (int sl = 0; sl < NC; ++sl) {
+      const int f = slot_offset<FLO>(sl);
+      if (used[f - FLO]) continue;
+      const int grp[3] = {f, f + 8, f - 8};
+      const int sh[3] = {0, 1, -1};
+      for (int g = 0; g < 3; ++g) {
+        const int h = grp[g];
+        if (h < FLO || h > FHI || used[h - FLO]) continue;
+        used[h - FLO] = true;
+        off[k] = h;
+        shift[k] = sh[g];
+        slot_of[k] = h == 0 ? 0 : (h < 0 ? h - FLO + 1 : h - FLO);
+        ++k;
+      }
+    }
+  }
+};
 
 // ScaleSearch on one block held in registers: default pattern p0 from the
 // block amax, then f = 0, f_lo..f_hi; first strictly smaller SSE wins.
@@ -296,7 +378,75 @@ __device__ __forceinline__ void search_block(const float (&x)[16], float sg, boo
   }
 }
 
-template <bool BF16>
+// The same exact search for a fixed offset range, in the evaluation order of
+// EvalOrder: a candidate eight patterns from an earlier one takes that one's
+// products through the convert's power-of-two scale (exact when the table
+// shows d and 1/d differing by exactly 2 between the two patterns, checked
+// per lane; a wave with any lane outside that case forms its own products).
+// The winner is the least SSE, ties to the earliest visiting slot, which is
+// the contract's first strictly smaller SSE in visiting order.
+template <int FLO, int FHI>
+__device__ __forceinline__ void search_block_twins(const float (&x)[16], float sg, bool sg_ok,
+                                                   const f32x2 *tbl, uint32_t &best_p,
+                                                   uint32_t &bc0, uint32_t &bc1) {
+  constexpr int NC = FHI - FLO + 1;
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  best_p = 0x7Fu;
+  bc0 = 0u;
+  bc1 = 0u;
+  if (!(sg_ok && am < 0x7F800000u)) return;
+  const float amax = __uint_as_float(am);
+  const float t = (amax / 6.0f) / sg;
+  const uint32_t p0 = e4m3_rne_sat(t);
+  constexpr EvalOrder<FLO, FHI> ord;
+  float best = INFINITY;
+  int best_slot = NC;
+  float y[16];
+  f32x2 db = f32x2{0.0f, 0.0f};  // table entry of the current group's first candidate
+  bool have_y = false;           // y holds that candidate's products (wave-uniform)
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int f = ord.off[k], sl = ord.slot_of[k], sh = ord.shift[k];
+    const int p = (int)p0 + f;
+    const bool valid = p >= 0 && p <= 126;
+    const f32x2 dr = tbl[valid ? p : (int)p0];
+    const bool live = valid && (k == 0 || !(amax_term(amax, dr.x, dr.y) > best));
+    if (sh == 0) {
+      db = valid ? dr : f32x2{0.0f, 0.0f};
+      have_y = false;
+    }
+    if (__ballot(live) == 0ull) continue;
+    uint32_t c0, c1;
+    float sse;
+    bool twin = false;
+    if (sh != 0 && have_y) {
+      const bool rel = sh > 0 ? (dr.x == 2.0f * db.x && dr.y == 0.5f * db.y && db.y != 0.0f)
+                              : (db.x == 2.0f * dr.x && db.y == 0.5f * dr.y && dr.y != 0.0f);
+      twin = __ballot(live && !rel) == 0ull;
+    }
+    if (twin) {
+      sse = sh > 0 ? sse_from_y<1>(x, y, dr.x, c0, c1) : sse_from_y<-1>(x, y, dr.x, c0, c1);
+    } else if (sh == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = x[i] * dr.y;
+      have_y = true;
+      sse = sse_from_y<0>(x, y, dr.x, c0, c1);
+    } else {
+      sse = candidate_sse(x, dr.x, dr.y, c0, c1);
+    }
+    const bool win = valid && (sse < best || (sse == best && sl < best_slot));
+    best = win ? sse : best;
+    best_slot = win ? sl : best_slot;
+    best_p = win ? (uint32_t)p : best_p;
+    bc0 = win ? c0 : bc0;
+    bc1 = win ? c1 : bc1;
+  }
+}
+
+// FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI] (twin-sharing search).
+template <bool BF16, int FLO, int FHI, bool FIXED>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   __shared__ f32x2 tbl[128];
   const float sg = resolve_tensor_scale(a);
@@ -309,7 +459,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     const BlockIO io = block_io(a.x, a.map, b, BF16 ? 2u : 4u);
     load_block_at<BF16>(io.src, x);
     uint32_t best_p, bc0, bc1;
-    search_block(x, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
+    if (FIXED)
+      search_block_twins<FLO, FHI>(x, sg, sg_ok, tbl, best_p, bc0, bc1);
+    else
+      search_block(x, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
     *(uint2 *)(a.codes + io.dst * 8u) = make_uint2(bc0, bc1);
     a.scales[io.dst] = (uint8_t)best_p;
   }
@@ -421,42 +574,6 @@ __device__ __forceinline__ void candidate_codes(const float (&x)[16], float r, u
   c1 = cw[1];
 }
 
-// Offset of visiting slot s: slot 0 is f = 0, then FLO, FLO+1, ... without 0.
-template <int FLO>
-__device__ __forceinline__ constexpr int slot_offset(int s) {
-  return s == 0 ? 0 : (FLO + s - 1 < 0 ? FLO + s - 1 : FLO + s);
-}
-
-// Evaluation order of the certified search: candidates in visiting order,
-// each followed at once by its in-range twins eight patterns up and down,
-// which reuse its products (shift +1: scale 2, -1: scale 1/2, 0: own
-// products). slot_of maps an evaluation position back to the visiting slot.
-template <int FLO, int FHI>
-struct EvalOrder {
-  static constexpr int NC = FHI - FLO + 1;
-  int off[NC];
-  int shift[NC];
-  int slot_of[NC];
-  constexpr EvalOrder() : off(), shift(), slot_of() {
-    bool used[NC] = {};
-    int k = 0;
-    for (int sl = 0; sl < NC; ++sl) {
-      const int f = slot_offset<FLO>(sl);
-      if (used[f - FLO]) continue;
-      const int grp[3] = {f, f + 8, f - 8};
-      const int sh[3] = {0, 1, -1};
-      for (int g = 0; g < 3; ++g) {
-        const int h = grp[g];
-        if (h < FLO || h > FHI || used[h - FLO]) continue;
-        used[h - FLO] = true;
-        off[k] = h;
-        shift[k] = sh[g];
-        slot_of[k] = h == 0 ? 0 : (h < 0 ? h - FLO + 1 : h - FLO);
-        ++k;
-      }
-    }
-  }
-};
 
 // Per pattern: d^2 and -2d in FP64 (both exact: d has at most 24 significant
 // bits) and the encode scale r = 1/d. Rows past pattern 126 are zero: a
@@ -742,7 +859,7 @@ __device__ __forceinline__ void hadamard_tile(const HadamardLane &h, const uint4
 
 // Quantize with the Hadamard pre-transform (bf16 input, cols % 128 == 0). One
 // wave per 32 vectors; each lane codes four blocks of its vector.
-template <bool SIGNS>
+template <bool SIGNS, int FLO, int FHI, bool FIXED>
 __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a) {
   __shared__ f32x2 tbl[128];
   const float sg = resolve_tensor_scale(a);
@@ -766,7 +883,10 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
       hadamard_tile(h, b, t, y);
       if (valid) {
         uint32_t best_p, bc0, bc1;
-        search_block(y, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
+        if (FIXED)
+          search_block_twins<FLO, FHI>(y, sg, sg_ok, tbl, best_p, bc0, bc1);
+        else
+          search_block(y, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
         const uint64_t blk = io.dst + 2u * t + h.g;
         *(uint2 *)(a.codes + blk * 8u) = make_uint2(bc0, bc1);
         a.scales[blk] = (uint8_t)best_p;
@@ -1201,9 +1321,13 @@ hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
   else if (bf16 && a.f_lo >= -8 && a.f_hi <= 8)
     hipLaunchKernelGGL((quantize_certified_kernel<-8, 8, false>), dim3(g), dim3(kThreads), 0, s, a);
   else if (bf16)
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<true, 0, 0, false>), dim3(g), dim3(kThreads), 0, s, a);
+  else if (a.f_lo == -2 && a.f_hi == 6)
+    hipLaunchKernelGGL((quantize_kernel<false, -2, 6, true>), dim3(g), dim3(kThreads), 0, s, a);
+  else if (a.f_lo == -8 && a.f_hi == 8)
+    hipLaunchKernelGGL((quantize_kernel<false, -8, 8, true>), dim3(g), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<false, 0, 0, false>), dim3(g), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1226,10 +1350,22 @@ hipError_t launch_amax_hadamard(const AmaxArgs &a, int groups, hipStream_t s) {
 
 hipError_t launch_quantize_hadamard(const QuantArgs &a, hipStream_t s) {
   const int g = hadamard_groups(a.map.nblocks / 8u, kMaxQuantGroups);
-  if (a.hs.on)
-    hipLaunchKernelGGL(quantize_hadamard_kernel<true>, dim3(g), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(quantize_hadamard_kernel<false>, dim3(g), dim3(kThreads), 0, s, a);
+  const int range = (a.f_lo == -2 && a.f_hi == 6) ? 1 : (a.f_lo == -8 && a.f_hi == 8) ? 2 : 0;
+  if (a.hs.on) {
+    if (range == 1)
+      hipLaunchKernelGGL((quantize_hadamard_kernel<true, -2, 6, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else if (range == 2)
+      hipLaunchKernelGGL((quantize_hadamard_kernel<true, -8, 8, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((quantize_hadamard_kernel<true, 0, 0, false>), dim3(g), dim3(kThreads), 0, s, a);
+  } else {
+    if (range == 1)
+      hipLaunchKernelGGL((quantize_hadamard_kernel<false, -2, 6, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else if (range == 2)
+      hipLaunchKernelGGL((quantize_hadamard_kernel<false, -8, 8, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((quantize_hadamard_kernel<false, 0, 0, false>), dim3(g), dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
