@@ -468,6 +468,58 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   }
 }
 
+// Max scaling alone (offsets [0, 0]: one candidate, nothing to score) with two
+// lanes per 16-element block: each lane loads 8 consecutive elements (16 B of
+// bf16 or 32 B of FP32, so a wave's loads are contiguous), the pair exchanges
+// its amax over DPP (a block's two lanes are always active together), and
+// each lane codes its 8 elements into one 32-bit word.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void quantize_rule_kernel(QuantArgs a) {
+  __shared__ f32x2 tbl[128];
+  const float sg = resolve_tensor_scale(a);
+  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+  build_scale_table(tbl, sg);
+
+  const uint32_t nunits = a.map.nblocks * 2u;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < nunits; u += stride) {
+    const uint32_t half = u & 1u;
+    const BlockIO io = block_io(a.x, a.map, u >> 1, BF16 ? 2u : 4u);
+    float x[8];
+    uint32_t am = 0u;
+    if (BF16) {
+      const uint4 v = load_stream((const uint4 *)(io.src + 16u * half));
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(w[k] << 16);
+        x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        am = max(am, (w[k] << 16) & 0x7FFFFFFFu);
+        am = max(am, w[k] & 0x7FFF0000u);
+      }
+    } else {
+      const uint4 *p = (const uint4 *)(io.src + 32u * half);
+      const uint4 v0 = load_stream(p), v1 = load_stream(p + 1);
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        x[k] = __uint_as_float(w[k]);
+        am = max(am, w[k] & 0x7FFFFFFFu);
+      }
+    }
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp((int)am, (int)am, 0xB1, 0xF, 0xF, false));
+    uint32_t w = 0u, pat = 0x7Fu;
+    if (sg_ok && am < 0x7F800000u) {
+      pat = e4m3_rne_sat((__uint_as_float(am) / 6.0f) / sg);
+      const float r = tbl[pat].y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w = fp4_encode_pair(w, x[2 * j] * r, x[2 * j + 1] * r, j);
+    }
+    *(uint32_t *)(a.codes + io.dst * 8u + 4u * half) = w;
+    if (half == 0u) a.scales[io.dst] = (uint8_t)pat;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Certified search for bf16 inputs.
 //
@@ -508,7 +560,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 //    exactly for the candidates that could win and applies the visiting-order
 //    rule among them.
 //
-// Offsets with one candidate ([0, 0], max scaling) need no search at all.
+// Offsets with one candidate ([0, 0], max scaling) need no search at all (the
+// launcher sends them to quantize_rule_kernel; the kernel still codes them if
+// instantiated so).
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ bf16x2 fp4_decode_pair_bf16(uint32_t w, int sel) {
@@ -1234,6 +1288,58 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(MxArgs a) {
   }
 }
 
+// The OCP rule alone (offsets [0, 0]) with four lanes per 32-element block:
+// each lane loads 8 consecutive elements (16 B of bf16 or 32 B of FP32, so a
+// wave's loads are contiguous), the block amax is the maximum over the lane
+// quad (DPP quad permutes; a block's four lanes are always active together),
+// and each lane codes its 8 elements into one 32-bit word with the same
+// arithmetic as the one-lane kernel.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void mx_rule_kernel(MxArgs a) {
+  const uint32_t nunits = a.nblocks * 4u;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < nunits; u += stride) {
+    float x[8];
+    uint32_t amb = 0u;
+    if (BF16) {
+      const uint4 v = load_stream((const uint4 *)((const uint16_t *)a.x + (uint64_t)u * 8u));
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(w[k] << 16);
+        x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        amb = max(amb, (w[k] << 16) & 0x7FFFFFFFu);
+        amb = max(amb, w[k] & 0x7FFF0000u);
+      }
+    } else {
+      const uint4 *p = (const uint4 *)((const float *)a.x + (uint64_t)u * 8u);
+      const uint4 v0 = load_stream(p), v1 = load_stream(p + 1);
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        x[k] = __uint_as_float(w[k]);
+        amb = max(amb, w[k] & 0x7FFFFFFFu);
+      }
+    }
+    amb = max(amb, (uint32_t)__builtin_amdgcn_update_dpp((int)amb, (int)amb, 0xB1, 0xF, 0xF, false));
+    amb = max(amb, (uint32_t)__builtin_amdgcn_update_dpp((int)amb, (int)amb, 0x4E, 0xF, 0xF, false));
+    uint32_t w = 0u, byte = 255u;
+    if (amb < 0x7F800000u) {
+      int X = -127;
+      if (amb != 0u) {
+        const int e = amb >= 0x00800000u ? (int)(amb >> 23) - 127 : (31 - (int)__clz(amb)) - 149;
+        X = max(e - 2, -127);
+      }
+      const float r = pow2_exact(-X);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w = fp4_encode_pair(w, x[2 * j] * r, x[2 * j + 1] * r, j);
+      byte = (uint32_t)(X + 127);
+    }
+    *(uint32_t *)(a.codes + (uint64_t)u * 4u) = w;
+    if ((u & 3u) == 0u) a.scales[u >> 2] = (uint8_t)byte;
+  }
+}
+
 // One lane per 16-byte output chunk (8 bf16 or 4 FP32), as the NVFP4 inverse.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void mx_dequantize_kernel(MxDequantArgs a) {
@@ -1312,9 +1418,13 @@ hipError_t launch_finalize(const uint32_t *partials, int n, float *gscale, hipSt
 
 hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.map.nblocks, kMaxQuantGroups);
-  if (bf16 && a.f_lo == 0 && a.f_hi == 0)
-    hipLaunchKernelGGL((quantize_certified_kernel<0, 0, true>), dim3(g), dim3(kThreads), 0, s, a);
-  else if (bf16 && a.f_lo == -2 && a.f_hi == 6)
+  if (a.f_lo == 0 && a.f_hi == 0) {
+    const int gr = grid_for((uint64_t)a.map.nblocks * 2u, kMaxQuantGroups);
+    if (bf16)
+      hipLaunchKernelGGL(quantize_rule_kernel<true>, dim3(gr), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(quantize_rule_kernel<false>, dim3(gr), dim3(kThreads), 0, s, a);
+  } else if (bf16 && a.f_lo == -2 && a.f_hi == 6)
     hipLaunchKernelGGL((quantize_certified_kernel<-2, 6, true>), dim3(g), dim3(kThreads), 0, s, a);
   else if (bf16 && a.f_lo == -8 && a.f_hi == 8)
     hipLaunchKernelGGL((quantize_certified_kernel<-8, 8, true>), dim3(g), dim3(kThreads), 0, s, a);
@@ -1382,16 +1492,16 @@ hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, const Had
 hipError_t launch_mx_quantize(const MxArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.nblocks, kMaxQuantGroups);
   const bool search = a.f_lo != 0 || a.f_hi != 0;
-  if (bf16) {
-    if (search)
-      hipLaunchKernelGGL((mx_quantize_kernel<true, true>), dim3(g), dim3(kThreads), 0, s, a);
+  if (!search) {
+    const int gr = grid_for((uint64_t)a.nblocks * 4u, kMaxQuantGroups);
+    if (bf16)
+      hipLaunchKernelGGL(mx_rule_kernel<true>, dim3(gr), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((mx_quantize_kernel<true, false>), dim3(g), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL(mx_rule_kernel<false>, dim3(gr), dim3(kThreads), 0, s, a);
+  } else if (bf16) {
+    hipLaunchKernelGGL((mx_quantize_kernel<true, true>), dim3(g), dim3(kThreads), 0, s, a);
   } else {
-    if (search)
-      hipLaunchKernelGGL((mx_quantize_kernel<false, true>), dim3(g), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((mx_quantize_kernel<false, false>), dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((mx_quantize_kernel<false, true>), dim3(g), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
