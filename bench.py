@@ -374,7 +374,22 @@ def formats_table(torch, nv, workloads, iters: int = 50):
     def rel(yhat, ref, den):
         return float(((yhat.double() - ref.double()) ** 2).sum().item()) / den
 
-    rows, times = [], []
+    def chosen_offsets(x2d, scales, g):
+        """Histogram of the chosen offset (scale pattern minus the max-scaling pattern
+        E4M3(fl(fl(amax / 6) / S_g)), formed here with the same rounding rule) over the
+        blocks with a finite amax and a normal default pattern."""
+        am = x2d.float().abs().reshape(-1, 16).amax(1)
+        t = (am / 6.0) / g.float()
+        b = t.view(torch.int32)
+        nrm = ((b + 0x7FFFF + ((b >> 20) & 1)) >> 20) - 960
+        sub = torch.round(t * 512.0).to(torch.int32)
+        p0 = torch.where(t < 2.0 ** -6, sub, nrm)
+        p0 = torch.where(t >= 448.0, torch.full_like(p0, 126), p0)
+        ok = torch.isfinite(am) & (p0 >= 8)
+        f = scales.reshape(-1).to(torch.int32)[ok] - p0[ok]
+        return torch.bincount(f + 8, minlength=17).cpu().numpy(), int(ok.sum().item())
+
+    rows, times, hists = [], [], []
     for idx in (1, 2, 3, 4, 5):
         w = workloads.WORKLOADS[idx]
         xh = workloads.workload(idx)
@@ -391,6 +406,8 @@ def formats_table(torch, nv, workloads, iters: int = 50):
         for offs in ((0, 0), (-2, 6), (-8, 8)):
             c, s, g = nv.quantize(x, offs)
             e[f"nv{offs}"] = rel(nv.dequantize(c, s, g), xf, den)
+            if offs == (-2, 6):
+                hists.append((idx,) + chosen_offsets(x, s, g))
         for offs in ((0, 0), (-1, 1)):
             c, s = nv.mxfp4_quantize(x, offs)
             e[f"mx{offs}"] = rel(nv.mxfp4_dequantize(c, s), xf, den)
@@ -430,6 +447,13 @@ def formats_table(torch, nv, workloads, iters: int = 50):
         if "nv_had" in e:
             print(f"| {idx} | {f(e['nv_had'])} | {f(e['nv_rht'])} | {f(e['mx_had'])} | "
                   f"{f(e['mx_rht'])} |")
+    print()
+    print("| # | blocks | chosen offset of NVFP4 ScaleSearch [-2,6], share of blocks: "
+          "-2 | -1 | 0 | 1 | 2 | 3 | 4 | 5 | 6 |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for idx, h, nb in hists:
+        print(f"| {idx} | {nb} | " + " | ".join(f"{h[f + 8] / max(nb, 1):.3f}"
+                                                 for f in range(-2, 7)) + " |")
     print()
     gbs = lambda b, m: b / (m * 1e-3) / 1e9
     print("| # | MXFP4 quantize [0,0] us (GB/s) | MXFP4 quantize [-1,1] us (GB/s) | "
