@@ -111,6 +111,39 @@ def _dev(t: torch.Tensor):
     return t.device
 
 
+def _expect(t: torch.Tensor, name: str, shape, dtype, dev):
+    """A caller-supplied tensor the kernels read or write: on the same device,
+    contiguous, of this dtype and exactly this shape (so no access leaves it)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    return t
+
+
+def _scale_arg(g: torch.Tensor, name: str, dev):
+    """A device float32 tensor scale of one element."""
+    _expect(g, name, None, torch.float32, dev)
+    if g.numel() != 1:
+        raise ValueError(f"{name} must hold one element")
+    return g
+
+
+def _workspace(ws, nbytes: int, dev):
+    """The caller's workspace (any contiguous device tensor of at least nbytes bytes)
+    or a new one; returns (tensor, its size in bytes)."""
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _expect(ws, "workspace", None, None, dev)
+    return ws, ws.numel() * ws.element_size()
+
+
 def workspace_bytes(rows: int, cols: int, flags: int = 0) -> int:
     return int(load().nvfp4_workspace_bytes(rows, cols, flags))
 
@@ -152,23 +185,19 @@ def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
     scales = torch.empty(*x.shape[:-1], K // 16, dtype=torch.uint8, device=dev)
     if global_scale is not None:
         flags |= GSCALE_GIVEN
-        g = global_scale
-        _dev(g)
-        if g.dtype != torch.float32 or g.numel() != 1:
-            raise ValueError("global_scale must be a device float32 tensor of one element")
+        g = _scale_arg(global_scale, "global_scale", dev)
     else:
         g = torch.empty(1, dtype=torch.float32, device=dev)
-    wsb = int(L.nvfp4_workspace_bytes(R, K, flags))
-    ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws, wsb = _workspace(workspace, int(L.nvfp4_workspace_bytes(R, K, flags)), dev)
     sw = _signs(signs)
     if sw is None:
         st = L.nvfp4_quantize(x.data_ptr(), _dtype(x), R, K, block, f_lo, f_hi, flags,
                               codes.data_ptr(), scales.data_ptr(), g.data_ptr(), ws.data_ptr(),
-                              ws.numel(), _stream(dev))
+                              wsb, _stream(dev))
     else:
         st = L.nvfp4_quantize_rht(x.data_ptr(), _dtype(x), R, K, block, f_lo, f_hi, flags,
                                   ctypes.addressof(sw), codes.data_ptr(), scales.data_ptr(),
-                                  g.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+                                  g.data_ptr(), ws.data_ptr(), wsb, _stream(dev))
     _check("nvfp4_quantize", st)
     return codes, scales, g
 
@@ -182,15 +211,14 @@ def global_scale(x: torch.Tensor, hadamard: bool = False, workspace=None,
     R = x.numel() // K if K else 0
     flags = HADAMARD128 if hadamard else 0
     g = torch.empty(1, dtype=torch.float32, device=dev)
-    wsb = int(L.nvfp4_workspace_bytes(R, K, flags))
-    ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws, wsb = _workspace(workspace, int(L.nvfp4_workspace_bytes(R, K, flags)), dev)
     sw = _signs(signs)
     if sw is None:
         st = L.nvfp4_global_scale(x.data_ptr(), _dtype(x), R, K, flags, g.data_ptr(),
-                                  ws.data_ptr(), ws.numel(), _stream(dev))
+                                  ws.data_ptr(), wsb, _stream(dev))
     else:
         st = L.nvfp4_global_scale_rht(x.data_ptr(), _dtype(x), R, K, flags, ctypes.addressof(sw),
-                                      g.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+                                      g.data_ptr(), ws.data_ptr(), wsb, _stream(dev))
     _check("nvfp4_global_scale", st)
     return g
 
@@ -199,13 +227,15 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, global_scale: torch.Te
                out_dtype=torch.float32, block: int = 16, out: torch.Tensor | None = None):
     L = load()
     dev = _dev(codes)
-    _dev(scales)
-    _dev(global_scale)
+    _expect(codes, "codes", None, torch.uint8, dev)
     K = codes.shape[-1] * 2
     R = codes.numel() * 2 // K if K else 0
-    if scales.numel() * 16 != R * K:
-        raise ValueError("codes and scales sizes disagree")
-    y = out if out is not None else torch.empty(*codes.shape[:-1], K, dtype=out_dtype, device=dev)
+    _expect(scales, "scales", (*codes.shape[:-1], K // 16), torch.uint8, dev)
+    _scale_arg(global_scale, "global_scale", dev)
+    if out is not None:
+        y = _expect(out, "out", (*codes.shape[:-1], K), None, dev)
+    else:
+        y = torch.empty(*codes.shape[:-1], K, dtype=out_dtype, device=dev)
     st = L.nvfp4_dequantize(codes.data_ptr(), scales.data_ptr(), global_scale.data_ptr(), R, K,
                             block, y.data_ptr(), _dtype(y), _stream(dev))
     _check("nvfp4_dequantize", st)
@@ -234,23 +264,21 @@ def quantize_kv_sink(kv: torch.Tensor, n_first: int = 128, n_last: int = 128, of
     sink = torch.empty(B, H, n_first + n_last, D, dtype=kv.dtype, device=dev)
     if global_scale is not None:
         flags |= GSCALE_GIVEN
-        g = global_scale
+        g = _scale_arg(global_scale, "global_scale", dev)
     else:
         g = torch.empty(1, dtype=torch.float32, device=dev)
-    wsb = int(L.nvfp4_workspace_bytes(B * H * Tm, D, flags))
-    ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws, wsb = _workspace(workspace, int(L.nvfp4_workspace_bytes(B * H * Tm, D, flags)), dev)
     sw = _signs(signs)
     if sw is None:
         st = L.nvfp4_quantize_kv_sink(kv.data_ptr(), _dtype(kv), B, H, T, D, n_first, n_last,
                                       block, f_lo, f_hi, flags, codes.data_ptr(),
                                       scales.data_ptr(), g.data_ptr(), sink.data_ptr(),
-                                      ws.data_ptr(), ws.numel(), _stream(dev))
+                                      ws.data_ptr(), wsb, _stream(dev))
     else:
         st = L.nvfp4_quantize_kv_sink_rht(kv.data_ptr(), _dtype(kv), B, H, T, D, n_first, n_last,
                                           block, f_lo, f_hi, flags, ctypes.addressof(sw),
                                           codes.data_ptr(), scales.data_ptr(), g.data_ptr(),
-                                          sink.data_ptr(), ws.data_ptr(), ws.numel(),
-                                          _stream(dev))
+                                          sink.data_ptr(), ws.data_ptr(), wsb, _stream(dev))
     _check("nvfp4_quantize_kv_sink", st)
     return codes, scales, g, sink
 
@@ -259,11 +287,16 @@ def dequantize_kv_sink(codes, scales, global_scale, sink, T: int, n_first: int, 
                        out_dtype=torch.float32, block: int = 16):
     L = load()
     dev = _dev(codes)
-    _dev(scales)
     _dev(sink)
+    if sink.dim() != 4:
+        raise ValueError("sink must be [B, H, n_first + n_last, D]")
     B, H, NS, D = sink.shape
-    if NS != n_first + n_last:
-        raise ValueError("sink holds n_first + n_last tokens")
+    if NS != n_first + n_last or T < NS:
+        raise ValueError("sink holds n_first + n_last tokens, at most T")
+    Tm = T - NS
+    _expect(codes, "codes", (B, H, Tm, D // 2), torch.uint8, dev)
+    _expect(scales, "scales", (B, H, Tm, D // 16), torch.uint8, dev)
+    _scale_arg(global_scale, "global_scale", dev)
     y = torch.empty(B, H, T, D, dtype=out_dtype, device=dev)
     st = L.nvfp4_dequantize_kv_sink(codes.data_ptr(), scales.data_ptr(), global_scale.data_ptr(),
                                     sink.data_ptr(), _dtype(sink), B, H, T, D, n_first, n_last,
@@ -310,11 +343,16 @@ def kv_append(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor, off
     """Append kv_new [B, H, t_new, D] to a cache made by kv_cache_alloc (in place)."""
     L = load()
     dev = _dev(kv_new)
-    _dev(global_scale)
+    _scale_arg(global_scale, "global_scale", dev)
+    if kv_new.dim() != 4:
+        raise ValueError("kv_new must be [B, H, t_new, D]")
     B, H, t_new, D = kv_new.shape
-    head, tail, codes, scales = cache["head"], cache["tail"], cache["codes"], cache["scales"]
-    if kv_new.dtype != head.dtype:
-        raise ValueError("kv_new must have the cache dtype")
+    nf, nl = cache["n_first"], cache["n_last"]
+    cap = cache["codes"].shape[2] if cache["codes"].dim() == 4 else -1
+    head = _expect(cache["head"], "cache head", (B, H, nf, D), kv_new.dtype, dev)
+    tail = _expect(cache["tail"], "cache tail", (B, H, nl, D), kv_new.dtype, dev)
+    codes = _expect(cache["codes"], "cache codes", (B, H, cap, D // 2), torch.uint8, dev)
+    scales = _expect(cache["scales"], "cache scales", (B, H, cap, D // 16), torch.uint8, dev)
     f_lo, f_hi = _offsets(offsets)
     flags = HADAMARD128 if hadamard else 0
     T = cache["length"]
@@ -355,12 +393,14 @@ def mxfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.
                      block: int = 32, out: torch.Tensor | None = None):
     L = load()
     dev = _dev(codes)
-    _dev(scales)
+    _expect(codes, "codes", None, torch.uint8, dev)
     K = codes.shape[-1] * 2
     R = codes.numel() * 2 // K if K else 0
-    if scales.numel() * 32 != R * K:
-        raise ValueError("codes and scales sizes disagree")
-    y = out if out is not None else torch.empty(*codes.shape[:-1], K, dtype=out_dtype, device=dev)
+    _expect(scales, "scales", (*codes.shape[:-1], K // 32), torch.uint8, dev)
+    if out is not None:
+        y = _expect(out, "out", (*codes.shape[:-1], K), None, dev)
+    else:
+        y = torch.empty(*codes.shape[:-1], K, dtype=out_dtype, device=dev)
     st = L.mxfp4_dequantize(codes.data_ptr(), scales.data_ptr(), R, K, block, y.data_ptr(),
                             _dtype(y), _stream(dev))
     _check("mxfp4_dequantize", st)
@@ -376,12 +416,17 @@ def attention(q, k, v, causal: bool = False, out_dtype=torch.float32):
     kc, ks, kg = k
     vc, vs, vg = v
     dev = _dev(qc)
-    for t in (qs, qg, kc, ks, kg, vc, vs, vg):
-        _dev(t)
     if qc.dim() != 4 or kc.dim() != 4 or vc.shape != kc.shape:
         raise ValueError("q, k, v codes must be [B, H, N, 64] with matching k and v")
     B, Hq, Nq, D2 = qc.shape
     Hkv, Nk = kc.shape[1], kc.shape[2]
+    _expect(qc, "q codes", None, torch.uint8, dev)
+    _expect(qs, "q scales", (B, Hq, Nq, D2 // 8), torch.uint8, dev)
+    for name, c, sc in (("k", kc, ks), ("v", vc, vs)):
+        _expect(c, f"{name} codes", (B, Hkv, Nk, D2), torch.uint8, dev)
+        _expect(sc, f"{name} scales", (B, Hkv, Nk, D2 // 8), torch.uint8, dev)
+    for name, g in (("q", qg), ("k", kg), ("v", vg)):
+        _scale_arg(g, f"{name} global_scale", dev)
     y = torch.empty(B, Hq, Nq, D2 * 2, dtype=out_dtype, device=dev)
     st = L.nvfp4_attention(qc.data_ptr(), qs.data_ptr(), qg.data_ptr(), kc.data_ptr(),
                            ks.data_ptr(), kg.data_ptr(), vc.data_ptr(), vs.data_ptr(),
@@ -398,20 +443,25 @@ def attention_kv_cache(q, k_cache: dict, k_gscale: torch.Tensor, v_cache: dict,
     L = load()
     qc, qs, qg = q
     dev = _dev(qc)
-    for t in (qs, qg, k_gscale, v_gscale):
-        _dev(t)
-    for c in (k_cache, v_cache):
-        for key in ("head", "tail", "codes", "scales"):
-            _dev(c[key])
+    if qc.dim() != 4 or k_cache["codes"].dim() != 4:
+        raise ValueError("q codes must be [B, Hq, Nq, 64]; cache codes [B, Hkv, cap, 64]")
     if (k_cache["n_first"], k_cache["n_last"], k_cache["codes"].shape) != \
             (v_cache["n_first"], v_cache["n_last"], v_cache["codes"].shape):
         raise ValueError("the K and V caches have different layouts")
     if k_cache["length"] != v_cache["length"]:
         raise ValueError("the K and V caches hold different numbers of tokens")
-    if k_cache["head"].dtype != torch.bfloat16 or v_cache["head"].dtype != torch.bfloat16:
-        raise ValueError("attention over the cache needs bf16 caches")
     B, Hq, Nq, D2 = qc.shape
     Hkv, cap = k_cache["codes"].shape[1], k_cache["codes"].shape[2]
+    nf, nl, D = k_cache["n_first"], k_cache["n_last"], 2 * D2
+    _expect(qc, "q codes", None, torch.uint8, dev)
+    _expect(qs, "q scales", (B, Hq, Nq, D2 // 8), torch.uint8, dev)
+    for name, g in (("q", qg), ("k", k_gscale), ("v", v_gscale)):
+        _scale_arg(g, f"{name} global_scale", dev)
+    for which, c in (("k", k_cache), ("v", v_cache)):
+        _expect(c["head"], f"{which} cache head", (B, Hkv, nf, D), torch.bfloat16, dev)
+        _expect(c["tail"], f"{which} cache tail", (B, Hkv, nl, D), torch.bfloat16, dev)
+        _expect(c["codes"], f"{which} cache codes", (B, Hkv, cap, D2), torch.uint8, dev)
+        _expect(c["scales"], f"{which} cache scales", (B, Hkv, cap, D2 // 8), torch.uint8, dev)
     y = torch.empty(B, Hq, Nq, D2 * 2, dtype=out_dtype, device=dev)
     st = L.nvfp4_attention_kv_cache(
         qc.data_ptr(), qs.data_ptr(), qg.data_ptr(), k_cache["head"].data_ptr(),
