@@ -164,6 +164,24 @@ NVFP4_API nvfp4_status nvfp4_kv_append(const void *kv_new, nvfp4_dtype dt, int64
                                        uint32_t flags, const float *global_scale, void *head,
                                        void *tail, uint8_t *codes, uint8_t *scales, void *stream);
 
+/* nvfp4_kv_append with the token count T held in device memory, so a decode
+ * step can be captured once in a HIP graph and replayed token after token (the
+ * caller refills kv_new in place between replays). length: device int64[1],
+ * 8-byte aligned; the kernels read T = *length when they run and the call ends
+ * by setting *length = T + t_new, all in stream order. An append that does not
+ * fit the cache (T + t_new > n_first + cap + n_last) changes neither the cache
+ * nor *length (check the length to detect it: nothing is reported at call time,
+ * T being on the device). signs: NULL, or four uint32 words for the randomized
+ * Hadamard transform as in nvfp4_kv_append_rht (read during the call only).
+ * Everything else, including the result, is as nvfp4_kv_append with T = *length. */
+NVFP4_API nvfp4_status nvfp4_kv_append_dev(const void *kv_new, nvfp4_dtype dt, int64_t B,
+                                           int64_t H, int64_t t_new, int64_t D, int64_t n_first,
+                                           int64_t n_last, int64_t cap, int block, int f_lo,
+                                           int f_hi, uint32_t flags, const uint32_t *signs,
+                                           const float *global_scale, void *head, void *tail,
+                                           uint8_t *codes, uint8_t *scales, int64_t *length,
+                                           void *stream);
+
 /* The FP32 Hadamard pre-transform alone: y[rows][128] = x[rows][128] H/sqrt(128)
  * (x bf16), as the quantizer computes it on the fly. For inspection and split
  * parity checks; the quantize path never writes it to memory. */
@@ -211,6 +229,19 @@ NVFP4_API nvfp4_status nvfp4_attention_kv_cache(
     const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
     const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
     int64_t T, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, void *out,
+    nvfp4_dtype out_dt, void *stream);
+
+/* nvfp4_attention_kv_cache with the token count read from device memory
+ * (length: device int64[1], 8-byte aligned, as nvfp4_kv_append_dev keeps it)
+ * when the kernel runs, clamped to n_first + cap + n_last; for a decode step
+ * captured in a HIP graph. The host checks that need T use the capacity
+ * instead (head, tail, codes and scales must cover n_first + cap + n_last). */
+NVFP4_API nvfp4_status nvfp4_attention_kv_cache_dev(
+    const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
+    const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
+    const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
+    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    const int64_t *length, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, void *out,
     nvfp4_dtype out_dt, void *stream);
 
 /* Randomized Hadamard transform (QuIP#-style incoherence processing, ScaleSearch

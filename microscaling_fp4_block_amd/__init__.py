@@ -13,7 +13,9 @@ from .nvfp4 import (  # noqa: F401
     global_scale,
     hadamard128,
     kv_append,
+    kv_append_dev,
     kv_cache_alloc,
+    kv_length,
     load,
     mxfp4_dequantize,
     mxfp4_quantize,

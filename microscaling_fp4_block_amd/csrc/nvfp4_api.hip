@@ -445,6 +445,88 @@ nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64
   return NVFP4_OK;
 }
 
+// The append at a device-resident length: the kernels read t_old from *length
+// when they run and the last one advances it; an append that would overflow
+// the cache (t_old + t_new > n_first + cap + n_last) leaves cache and length
+// unchanged. Host checks cover everything that does not depend on t_old.
+nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H,
+                                int64_t t_new, int64_t D, int64_t n_first, int64_t n_last,
+                                int64_t cap, int block, int f_lo, int f_hi, uint32_t flags,
+                                const uint32_t *signs, const float *global_scale, void *head,
+                                void *tail, uint8_t *codes, uint8_t *scales, int64_t *length,
+                                void *stream) {
+  if (!global_scale || !length || !dtype_ok(dt)) return NVFP4_EINVAL;
+  nvfp4_status st = check_offsets(block, f_lo, f_hi);
+  if (st) return st;
+  if (flags & ~(NVFP4_HADAMARD128 | NVFP4_GSCALE_GIVEN)) return NVFP4_EINVAL;
+  if (B < 0 || H < 0 || t_new < 0 || D <= 0 || D % 16 || n_first < 0 || n_last < 0 || cap < 0)
+    return NVFP4_ESHAPE;
+  if (t_new > k2p31 || n_first > k2p31 || n_last > k2p31 || cap > k2p31 || !prod_le(B, H, k2p31))
+    return NVFP4_ESHAPE;
+  const int64_t total = n_first + cap + n_last;
+  if (total > k2p31) return NVFP4_ESHAPE;
+  const bool had = flags & NVFP4_HADAMARD128;
+  if (had && (dt != NVFP4_BF16)) return NVFP4_EINVAL;
+  if (had && D % 128) return NVFP4_ESHAPE;
+  const int64_t BH = B * H;
+  st = check_shape(BH * t_new, D, 0, dt);
+  if (st) return st;
+  st = check_shape(BH * cap, D, 0, dt);
+  if (st) return st;
+  if (BH * t_new > 0 && !kv_new) return NVFP4_EINVAL;
+  if (BH * n_first > 0 && !head) return NVFP4_EINVAL;
+  if (BH * n_last > 0 && !tail) return NVFP4_EINVAL;
+  if (BH * cap > 0 && (!codes || !scales)) return NVFP4_EINVAL;
+  if (!aligned(kv_new, 16) || !aligned(head, 16) || !aligned(tail, 16) || !aligned(codes, 8) ||
+      !aligned(length, 8))
+    return NVFP4_EALIGN;
+  if (t_new == 0) return NVFP4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dt == NVFP4_BF16;
+  const uint32_t es = bf16 ? 2u : 4u;
+  if (BH > 0) {
+    // 1. code the tokens that leave the recent window: at most t_new rows per segment
+    RegionMap m{};
+    m.bpr = (uint32_t)(D / 16);
+    m.nblocks = (uint32_t)(BH * t_new) * m.bpr;
+    m.div_bpr = make_fastdiv(m.bpr);
+    m.segments = (uint32_t)BH;
+    m.tm = (uint32_t)t_new;
+    m.div_tm = make_fastdiv(m.tm);
+    m.cols = (uint32_t)D;
+    m.n_first = (uint32_t)n_first;
+    m.append = 1;
+    m.n_last = (uint32_t)n_last;
+    m.t_new = (uint32_t)t_new;
+    m.cap = (uint32_t)cap;
+    m.div_nlast = make_fastdiv((uint32_t)(n_last > 0 ? n_last : 1));
+    m.ring = tail;
+    m.len_dev = length;
+    m.total = (uint32_t)total;
+    QuantArgs q{kv_new, codes, scales, (float *)global_scale, nullptr, 0, m, f_lo, f_hi,
+                make_signs(signs)};
+    if (run_quantize(q, bf16, had, s) != hipSuccess) return NVFP4_EHIP;
+    // 2. store the new tokens that stay in full precision
+    AdmitArgs c{};
+    c.src = kv_new;
+    c.head = head;
+    c.tail = tail;
+    c.t_new = (uint32_t)t_new;
+    c.n_first = (uint32_t)n_first;
+    c.n_last = (uint32_t)n_last;
+    c.chunks_per_row = (uint32_t)(D * es / 16);
+    c.nchunks = (uint32_t)(BH * t_new) * c.chunks_per_row;
+    c.div_cpr = make_fastdiv(c.chunks_per_row);
+    c.div_tnew = make_fastdiv((uint32_t)t_new);
+    c.div_nlast = make_fastdiv((uint32_t)(n_last > 0 ? n_last : 1));
+    c.len_dev = length;
+    c.total = (uint32_t)total;
+    if (launch_admit(c, bf16, s) != hipSuccess) return NVFP4_EHIP;
+  }
+  // 3. advance the length (after both kernels read it)
+  return hip_status(launch_advance_length(length, (uint32_t)t_new, (uint32_t)total, s));
+}
+
 nvfp4_status hadamard_impl(const void *x, nvfp4_dtype xdt, int64_t rows, const uint32_t *signs,
                            float *y, void *stream) {
   if (xdt != NVFP4_BF16) return NVFP4_EINVAL;
@@ -479,6 +561,17 @@ nvfp4_status nvfp4_kv_append_rht(const void *kv_new, nvfp4_dtype dt, int64_t B, 
   return kv_append_impl(kv_new, dt, B, H, T, t_new, D, n_first, n_last, cap, block, f_lo, f_hi,
                         flags | NVFP4_HADAMARD128, signs, global_scale, head, tail, codes, scales,
                         stream);
+}
+
+nvfp4_status nvfp4_kv_append_dev(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H,
+                                 int64_t t_new, int64_t D, int64_t n_first, int64_t n_last,
+                                 int64_t cap, int block, int f_lo, int f_hi, uint32_t flags,
+                                 const uint32_t *signs, const float *global_scale, void *head,
+                                 void *tail, uint8_t *codes, uint8_t *scales, int64_t *length,
+                                 void *stream) {
+  return kv_append_dev_impl(kv_new, dt, B, H, t_new, D, n_first, n_last, cap, block, f_lo, f_hi,
+                            signs ? (flags | NVFP4_HADAMARD128) : flags, signs, global_scale,
+                            head, tail, codes, scales, length, stream);
 }
 
 nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,
@@ -556,13 +649,21 @@ nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_scales,
   return hip_status(launch_attention(a, out_dt == NVFP4_BF16, (hipStream_t)stream));
 }
 
-nvfp4_status nvfp4_attention_kv_cache(
+}  // extern "C"
+
+namespace {
+
+// Attention over the sink cache with T tokens, or (len_dev set) with the token
+// count read from that device word when the kernel runs (clamped to the
+// cache's n_first + cap + n_last); checks that need T are then made on the
+// cache's capacity instead.
+nvfp4_status attention_kv_cache_impl(
     const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
     const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
     const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
     const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
-    int64_t T, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, void *out,
-    nvfp4_dtype out_dt, void *stream) {
+    int64_t T, const int64_t *len_dev, int64_t D, int64_t n_first, int64_t n_last, int64_t cap,
+    void *out, nvfp4_dtype out_dt, void *stream) {
   if (!dtype_ok(out_dt) || cache_dt != NVFP4_BF16) return NVFP4_EINVAL;
   if (D != 128) return NVFP4_ESHAPE;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || T < 0 || n_first < 0 || n_last < 0 ||
@@ -571,17 +672,18 @@ nvfp4_status nvfp4_attention_kv_cache(
   if (!prod_le(B, Hq, 65535) || Nq > (1ll << 30) || T > (1ll << 30) || cap > (1ll << 30) ||
       n_first > (1ll << 30) || n_last > (1ll << 30))
     return NVFP4_ESHAPE;
-  const int64_t mid = T - n_first - n_last;
+  const int64_t mid = len_dev ? cap : T - n_first - n_last;
   if (mid > cap) return NVFP4_ESHAPE;
   if (B * Hq * Nq > kMaxBlocks / 8 || B * Hkv * cap > kMaxBlocks / 8) return NVFP4_ESHAPE;
   if (B * Nq == 0) return NVFP4_OK;
   if (!q_codes || !q_scales || !q_gscale || !k_gscale || !v_gscale || !out) return NVFP4_EINVAL;
-  if (n_first > 0 && T > 0 && (!k_head || !v_head)) return NVFP4_EINVAL;
-  if (n_last > 0 && T > n_first && (!k_tail || !v_tail)) return NVFP4_EINVAL;
+  const int64_t span = len_dev ? n_first + cap + n_last : T;  // tokens that may be read
+  if (n_first > 0 && span > 0 && (!k_head || !v_head)) return NVFP4_EINVAL;
+  if (n_last > 0 && span > n_first && (!k_tail || !v_tail)) return NVFP4_EINVAL;
   if (mid > 0 && (!k_codes || !k_scales || !v_codes || !v_scales)) return NVFP4_EINVAL;
   if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
       !aligned(k_head, 16) || !aligned(k_tail, 16) || !aligned(v_head, 16) ||
-      !aligned(v_tail, 16) || !aligned(out, 16))
+      !aligned(v_tail, 16) || !aligned(out, 16) || !aligned(len_dev, 8))
     return NVFP4_EALIGN;
   AttnArgs a{};
   a.qc = q_codes;
@@ -609,7 +711,39 @@ nvfp4_status nvfp4_attention_kv_cache(
   a.nf = (uint32_t)n_first;
   a.nl = (uint32_t)n_last;
   a.cap = (uint32_t)cap;
+  a.nk_dev = len_dev;
   return hip_status(launch_attention(a, out_dt == NVFP4_BF16, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_attention_kv_cache(
+    const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
+    const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
+    const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
+    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    int64_t T, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, void *out,
+    nvfp4_dtype out_dt, void *stream) {
+  return attention_kv_cache_impl(q_codes, q_scales, q_gscale, k_head, k_tail, k_codes, k_scales,
+                                 k_gscale, v_head, v_tail, v_codes, v_scales, v_gscale, cache_dt,
+                                 B, Hq, Hkv, Nq, T, nullptr, D, n_first, n_last, cap, out, out_dt,
+                                 stream);
+}
+
+nvfp4_status nvfp4_attention_kv_cache_dev(
+    const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
+    const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
+    const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
+    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    const int64_t *length, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, void *out,
+    nvfp4_dtype out_dt, void *stream) {
+  if (!length) return NVFP4_EINVAL;
+  return attention_kv_cache_impl(q_codes, q_scales, q_gscale, k_head, k_tail, k_codes, k_scales,
+                                 k_gscale, v_head, v_tail, v_codes, v_scales, v_gscale, cache_dt,
+                                 B, Hq, Hkv, Nq, 0, length, D, n_first, n_last, cap, out, out_dt,
+                                 stream);
 }
 
 }  // extern "C"

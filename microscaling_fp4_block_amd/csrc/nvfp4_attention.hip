@@ -229,18 +229,22 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const float c2_sink = qg * a.tau_log2e;
   const float vg = *a.vg;
 
-  uint32_t kend = a.Nk;
+  // keys: a.Nk, or in cache mode with a device-resident length, that length
+  // (at most the cache's n_first + cap + n_last tokens)
+  const uint32_t Nk = (CACHE && a.nk_dev) ? (uint32_t)min<int64_t>(*a.nk_dev, (int64_t)a.nf + a.cap + a.nl)
+                                          : a.Nk;
+  uint32_t kend = Nk;
   if (a.causal) {
     const int64_t qlast = (int64_t)min(q0 + kQueriesPerGroup, a.Nq) - 1;
-    const int64_t last = qlast + (int64_t)a.Nk - (int64_t)a.Nq;
-    kend = last < 0 ? 0u : (uint32_t)min<int64_t>(last + 1, a.Nk);
+    const int64_t last = qlast + (int64_t)Nk - (int64_t)a.Nq;
+    kend = last < 0 ? 0u : (uint32_t)min<int64_t>(last + 1, Nk);
   }
-  const int64_t lim = a.causal ? (int64_t)qi + (int64_t)a.Nk - (int64_t)a.Nq : (int64_t)a.Nk - 1;
+  const int64_t lim = a.causal ? (int64_t)qi + (int64_t)Nk - (int64_t)a.Nq : (int64_t)Nk - 1;
   // the smallest lim of the wave (its first query), for the unmasked fast path
   const int64_t lim_wave =
-      a.causal ? (int64_t)(q0 + wave * 32u) + (int64_t)a.Nk - (int64_t)a.Nq : (int64_t)a.Nk - 1;
+      a.causal ? (int64_t)(q0 + wave * 32u) + (int64_t)Nk - (int64_t)a.Nq : (int64_t)Nk - 1;
 
-  const uint64_t coded_base = CACHE ? (uint64_t)kvh * a.cap : (uint64_t)kvh * a.Nk;
+  const uint64_t coded_base = CACHE ? (uint64_t)kvh * a.cap : (uint64_t)kvh * Nk;
   const uint32_t coded_off = CACHE ? a.nf : 0u;
 
   // This lane's B operand of S^T: query qi, elements 16 ks + 8 g .. +7.
@@ -436,10 +440,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
   if (CACHE) {
     // head sinks, coded middle, tail ring: tiles never straddle two segments
-    const uint32_t mid_hi = max(a.Nk > a.nl ? a.Nk - a.nl : 0u, a.nf);
-    run_segment(std::true_type{}, 0u, min(a.nf, a.Nk), true);
+    const uint32_t mid_hi = max(Nk > a.nl ? Nk - a.nl : 0u, a.nf);
+    run_segment(std::true_type{}, 0u, min(a.nf, Nk), true);
     run_segment(std::false_type{}, a.nf, mid_hi, false);
-    run_segment(std::true_type{}, max(mid_hi, a.nf), a.Nk, false);
+    run_segment(std::true_type{}, max(mid_hi, a.nf), Nk, false);
   } else {
     run_segment(std::false_type{}, 0u, kend, false);
   }

@@ -37,6 +37,10 @@ inline FastDiv make_fastdiv(uint32_t d) {
 // g = r / tm; a token below t_old comes from the ring [segments][n_last][cols]
 // (slot pos mod n_last), a later one from x [segments][t_new][cols] (row
 // pos - t_old); its codes go to row g * cap + pos - n_first of the cache.
+// With len_dev set, t_old is read from that device word when the kernel runs,
+// tm is t_new (an upper bound on the positions that leave the window), lo and
+// the end of the window follow from t_old, rows past the end are skipped, and
+// an append that would not fit (t_old + t_new > total) skips every row.
 struct RegionMap {
   uint32_t nblocks;     // 16-element blocks in the region
   uint32_t bpr;         // blocks per row (cols / 16)
@@ -51,6 +55,8 @@ struct RegionMap {
   uint32_t lo, t_old, n_last, t_new, cap;
   FastDiv div_nlast;
   const void *ring;
+  const int64_t *len_dev;  // device-resident t_old (append mode), or null
+  uint32_t total;          // n_first + cap + n_last: tokens the cache holds
 };
 
 // Random sign flips of the randomized Hadamard transform: bit k of w[k / 32]
@@ -96,6 +102,8 @@ struct AdmitArgs {
   uint32_t t_old, t_new, n_first, n_last;
   uint32_t chunks_per_row, nchunks;
   FastDiv div_cpr, div_tnew, div_nlast;
+  const int64_t *len_dev;  // device-resident t_old, or null
+  uint32_t total;          // tokens the cache holds (with len_dev)
 };
 
 // Sink copy / reassembly: BH segments of T tokens of D elements; tokens
@@ -159,6 +167,7 @@ struct AttnArgs {
   uint32_t cache;
   const uint16_t *kh, *kt, *vh, *vt;
   uint32_t nf, nl, cap;
+  const int64_t *nk_dev;  // cache mode: device-resident token count (replaces Nk), or null
 };
 
 hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s);
@@ -171,6 +180,7 @@ hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, const Had
 hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s);
 hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_admit(const AdmitArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_advance_length(int64_t *len, uint32_t t_new, uint32_t total, hipStream_t s);
 hipError_t launch_dequantize_kv(const DequantKvArgs &a, bool sink_bf16, bool out_bf16,
                                 hipStream_t s);
 

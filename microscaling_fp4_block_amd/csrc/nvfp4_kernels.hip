@@ -36,31 +36,43 @@ __device__ __forceinline__ uint64_t block_offset(const RegionMap &m, uint32_t b)
   return row * m.cols + (uint64_t)j * 16u;
 }
 
-// Source address and destination block of block b of a quantize region.
+// Source address and destination block of block b of a quantize region;
+// valid is false for a row past the end of a device-length append.
 struct BlockIO {
   const char *src;
   uint64_t dst;
+  bool valid;
 };
 
 __device__ __forceinline__ BlockIO block_io(const void *x, const RegionMap &m, uint32_t b,
                                             uint32_t esize) {
-  if (!m.append) return BlockIO{(const char *)x + block_offset(m, b) * esize, b};
+  if (!m.append) return BlockIO{(const char *)x + block_offset(m, b) * esize, b, true};
   const uint32_t r = fastdiv(b, m.div_bpr);
   const uint32_t j = b - r * m.bpr;
   const uint32_t g = fastdiv(r, m.div_tm);
-  const uint32_t pos = m.lo + (r - g * m.tm);
+  uint32_t t_old = m.t_old, lo = m.lo;
+  bool valid = true;
+  if (m.len_dev) {
+    t_old = (uint32_t)*m.len_dev;
+    const uint32_t t2 = t_old + m.t_new;
+    lo = max(m.n_first, t_old > m.n_last ? t_old - m.n_last : 0u);
+    const uint32_t hi = max(m.n_first, t2 > m.n_last ? t2 - m.n_last : 0u);
+    valid = t2 <= m.total && lo + (r - g * m.tm) < hi;
+  }
+  const uint32_t pos = lo + (r - g * m.tm);
+  if (!valid) return BlockIO{(const char *)x, 0, false};
   uint64_t row;
   const char *base;
-  if (pos < m.t_old) {
+  if (pos < t_old) {
     const uint32_t q = fastdiv(pos, m.div_nlast);
     row = (uint64_t)g * m.n_last + (pos - q * m.n_last);
     base = (const char *)m.ring;
   } else {
-    row = (uint64_t)g * m.t_new + (pos - m.t_old);
+    row = (uint64_t)g * m.t_new + (pos - t_old);
     base = (const char *)x;
   }
   const uint64_t dst = ((uint64_t)g * m.cap + (pos - m.n_first)) * m.bpr + j;
-  return BlockIO{base + (row * m.cols + (uint64_t)j * 16u) * esize, dst};
+  return BlockIO{base + (row * m.cols + (uint64_t)j * 16u) * esize, dst, true};
 }
 
 // Wave64 max with DPP: xor-1 and xor-2 quad permutes, half-row and row
@@ -457,6 +469,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
     float x[16];
     const BlockIO io = block_io(a.x, a.map, b, BF16 ? 2u : 4u);
+    if (!io.valid) continue;
     load_block_at<BF16>(io.src, x);
     uint32_t best_p, bc0, bc1;
     if (FIXED)
@@ -485,6 +498,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rule_kernel(QuantArgs a) {
   for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < nunits; u += stride) {
     const uint32_t half = u & 1u;
     const BlockIO io = block_io(a.x, a.map, u >> 1, BF16 ? 2u : 4u);
+    if (!io.valid) continue;  // both lanes of the block skip together
     float x[8];
     uint32_t am = 0u;
     if (BF16) {
@@ -679,6 +693,7 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
   const uint32_t stride = gridDim.x * kThreads;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
     const BlockIO io = block_io(a.x, a.map, b, 2u);
+    if (!io.valid) continue;
     const uint4 q0 = load_stream(io.src), q1 = load_stream(io.src + 16);
     const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     float x[16];
@@ -930,12 +945,13 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
     const bool valid = vec < nvec;
     uint4 b[8];
     const BlockIO io = block_io(a.x, a.map, valid ? vec * 8u : 0u, 2u);
-    hadamard_load<SIGNS>((const uint16_t *)io.src, 0, valid, h.g, a.hs, b);
+    const bool live = valid && io.valid;  // the 8 blocks of a vector share one row
+    hadamard_load<SIGNS>((const uint16_t *)io.src, 0, live, h.g, a.hs, b);
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
-      hadamard_tile(h, b, t, y);
-      if (valid) {
+      hadamard_tile(h, b, t, y);  // every lane takes part in the matrix instructions
+      if (live) {
         uint32_t best_p, bc0, bc1;
         if (FIXED)
           search_block_twins<FLO, FHI>(y, sg, sg_ok, tbl, best_p, bc0, bc1);
@@ -1121,6 +1137,10 @@ __global__ __launch_bounds__(kThreads) void sink_copy_kernel(SinkArgs a, uint32_
 // (tokens bound for the middle are coded by the quantize kernel instead).
 __global__ __launch_bounds__(kThreads) void admit_kernel(AdmitArgs a, uint32_t row_bytes) {
   const uint32_t stride = gridDim.x * kThreads;
+  if (a.len_dev) {  // device-resident length: skip an append that does not fit
+    a.t_old = (uint32_t)*a.len_dev;
+    if (a.t_old + a.t_new > a.total) return;
+  }
   const uint32_t tail_from = a.t_old + a.t_new - min(a.n_last, a.t_old + a.t_new);
   for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < a.nchunks; c += stride) {
     const uint32_t row = fastdiv(c, a.div_cpr);  // g * t_new + k
@@ -1138,6 +1158,15 @@ __global__ __launch_bounds__(kThreads) void admit_kernel(AdmitArgs a, uint32_t r
     }
     *(uint4 *)(dst + (uint64_t)k * 16u) =
         *(const uint4 *)((const char *)a.src + (uint64_t)row * row_bytes + (uint64_t)k * 16u);
+  }
+}
+
+// The device-resident length after an append: t_old + t_new when that fits the
+// cache (the append kernels ran), else unchanged (they skipped). One lane.
+__global__ void advance_length_kernel(int64_t *len, uint32_t t_new, uint32_t total) {
+  if (threadIdx.x == 0) {
+    const int64_t t = *len;
+    if (t + (int64_t)t_new <= (int64_t)total) *len = t + (int64_t)t_new;
   }
 }
 
@@ -1528,6 +1557,11 @@ hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s)
 hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.nchunks, kMaxQuantGroups);
   hipLaunchKernelGGL(sink_copy_kernel, dim3(g), dim3(kThreads), 0, s, a, bf16 ? 2u : 4u);
+  return hipGetLastError();
+}
+
+hipError_t launch_advance_length(int64_t *len, uint32_t t_new, uint32_t total, hipStream_t s) {
+  hipLaunchKernelGGL(advance_length_kernel, dim3(1), dim3(64), 0, s, len, t_new, total);
   return hipGetLastError();
 }
 

@@ -39,6 +39,8 @@ SIGNATURES = {
     "nvfp4_hadamard128": ([_vp, _i32, _i64, _vp, _vp], _i32),
     "nvfp4_kv_append": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32,
                          _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "nvfp4_kv_append_dev": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32,
+                             _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "nvfp4_quantize_rht": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp,
                             _vp, _sz, _vp], _i32),
     "nvfp4_global_scale_rht": ([_vp, _i32, _i64, _i64, _u32, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -52,6 +54,9 @@ SIGNATURES = {
     "nvfp4_attention_kv_cache": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _vp, _i32, _vp], _i32),
+    "nvfp4_attention_kv_cache_dev": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _i32, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                                      _i64, _vp, _i32, _vp], _i32),
     "mxfp4_quantize": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "mxfp4_dequantize": ([_vp, _vp, _i64, _i64, _i32, _vp, _i32, _vp], _i32),
 }
@@ -328,20 +333,20 @@ def kv_cache_alloc(B: int, H: int, D: int, capacity: int, n_first: int = 128, n_
                    dtype=torch.bfloat16, device="cuda"):
     """Buffers of an attention-sink NVFP4 KV cache for up to `capacity` tokens per (b, h):
     head [B, H, n_first, D], tail ring [B, H, n_last, D], codes [B, H, cap, D/2],
-    scales [B, H, cap, D/16] with cap = capacity - n_first - n_last middle rows."""
+    scales [B, H, cap, D/16] with cap = capacity - n_first - n_last middle rows; the
+    token count as a host int ("length", kv_append) and as a device int64[1]
+    ("length_dev", kv_append_dev and attention_kv_cache_dev)."""
     cap = max(capacity - n_first - n_last, 0)
     return dict(
         head=torch.empty(B, H, n_first, D, dtype=dtype, device=device),
         tail=torch.empty(B, H, n_last, D, dtype=dtype, device=device),
         codes=torch.empty(B, H, cap, D // 2, dtype=torch.uint8, device=device),
         scales=torch.empty(B, H, cap, D // 16, dtype=torch.uint8, device=device),
+        length_dev=torch.zeros(1, dtype=torch.int64, device=device),
         n_first=n_first, n_last=n_last, length=0)
 
 
-def kv_append(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor, offsets=(-2, 6),
-              hadamard: bool = False, block: int = 16, signs=None):
-    """Append kv_new [B, H, t_new, D] to a cache made by kv_cache_alloc (in place)."""
-    L = load()
+def _cache_args(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor):
     dev = _dev(kv_new)
     _scale_arg(global_scale, "global_scale", dev)
     if kv_new.dim() != 4:
@@ -353,6 +358,43 @@ def kv_append(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor, off
     tail = _expect(cache["tail"], "cache tail", (B, H, nl, D), kv_new.dtype, dev)
     codes = _expect(cache["codes"], "cache codes", (B, H, cap, D // 2), torch.uint8, dev)
     scales = _expect(cache["scales"], "cache scales", (B, H, cap, D // 16), torch.uint8, dev)
+    return dev, B, H, t_new, D, nf, nl, cap, head, tail, codes, scales
+
+
+def kv_append_dev(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor, offsets=(-2, 6),
+                  hadamard: bool = False, block: int = 16, signs=None):
+    """kv_append at the device-resident length cache["length_dev"] (read and advanced on
+    the device, so the call can be captured in a HIP graph and replayed per token; an
+    append that would not fit leaves cache and length unchanged). cache["length"] (the
+    host count) is not touched; kv_length reads the device one."""
+    L = load()
+    dev, B, H, t_new, D, nf, nl, cap, head, tail, codes, scales = _cache_args(cache, kv_new,
+                                                                             global_scale)
+    length = _expect(cache["length_dev"], "cache length_dev", (1,), torch.int64, dev)
+    f_lo, f_hi = _offsets(offsets)
+    flags = HADAMARD128 if hadamard else 0
+    sw = _signs(signs)
+    st = L.nvfp4_kv_append_dev(kv_new.data_ptr(), _dtype(kv_new), B, H, t_new, D, nf, nl, cap,
+                               block, f_lo, f_hi, flags,
+                               ctypes.addressof(sw) if sw is not None else None,
+                               global_scale.data_ptr(), head.data_ptr(), tail.data_ptr(),
+                               codes.data_ptr(), scales.data_ptr(), length.data_ptr(),
+                               _stream(dev))
+    _check("nvfp4_kv_append_dev", st)
+    return cache
+
+
+def kv_length(cache: dict) -> int:
+    """The device-resident token count of a cache (synchronizes with the device)."""
+    return int(cache["length_dev"].item())
+
+
+def kv_append(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor, offsets=(-2, 6),
+              hadamard: bool = False, block: int = 16, signs=None):
+    """Append kv_new [B, H, t_new, D] to a cache made by kv_cache_alloc (in place)."""
+    L = load()
+    dev, B, H, t_new, D, nf, nl, cap, head, tail, codes, scales = _cache_args(cache, kv_new,
+                                                                             global_scale)
     f_lo, f_hi = _offsets(offsets)
     flags = HADAMARD128 if hadamard else 0
     T = cache["length"]
@@ -437,9 +479,11 @@ def attention(q, k, v, causal: bool = False, out_dtype=torch.float32):
 
 
 def attention_kv_cache(q, k_cache: dict, k_gscale: torch.Tensor, v_cache: dict,
-                       v_gscale: torch.Tensor, out_dtype=torch.float32):
+                       v_gscale: torch.Tensor, out_dtype=torch.float32, device_length: bool = False):
     """Attention of q (codes, scales, global_scale of [B, Hq, Nq, 128]) over K and V
-    sink caches made by kv_cache_alloc and filled by kv_append (bf16). Returns O."""
+    sink caches made by kv_cache_alloc and filled by kv_append (bf16). Returns O.
+    With device_length, the token count is k_cache["length_dev"], read on the device
+    (for caches filled by kv_append_dev; capturable in a HIP graph)."""
     L = load()
     qc, qs, qg = q
     dev = _dev(qc)
@@ -448,7 +492,7 @@ def attention_kv_cache(q, k_cache: dict, k_gscale: torch.Tensor, v_cache: dict,
     if (k_cache["n_first"], k_cache["n_last"], k_cache["codes"].shape) != \
             (v_cache["n_first"], v_cache["n_last"], v_cache["codes"].shape):
         raise ValueError("the K and V caches have different layouts")
-    if k_cache["length"] != v_cache["length"]:
+    if not device_length and k_cache["length"] != v_cache["length"]:
         raise ValueError("the K and V caches hold different numbers of tokens")
     B, Hq, Nq, D2 = qc.shape
     Hkv, cap = k_cache["codes"].shape[1], k_cache["codes"].shape[2]
@@ -463,6 +507,17 @@ def attention_kv_cache(q, k_cache: dict, k_gscale: torch.Tensor, v_cache: dict,
         _expect(c["codes"], f"{which} cache codes", (B, Hkv, cap, D2), torch.uint8, dev)
         _expect(c["scales"], f"{which} cache scales", (B, Hkv, cap, D2 // 8), torch.uint8, dev)
     y = torch.empty(B, Hq, Nq, D2 * 2, dtype=out_dtype, device=dev)
+    if device_length:
+        length = _expect(k_cache["length_dev"], "cache length_dev", (1,), torch.int64, dev)
+        st = L.nvfp4_attention_kv_cache_dev(
+            qc.data_ptr(), qs.data_ptr(), qg.data_ptr(), k_cache["head"].data_ptr(),
+            k_cache["tail"].data_ptr(), k_cache["codes"].data_ptr(), k_cache["scales"].data_ptr(),
+            k_gscale.data_ptr(), v_cache["head"].data_ptr(), v_cache["tail"].data_ptr(),
+            v_cache["codes"].data_ptr(), v_cache["scales"].data_ptr(), v_gscale.data_ptr(), BF16,
+            B, Hq, Hkv, Nq, length.data_ptr(), D2 * 2, k_cache["n_first"], k_cache["n_last"],
+            cap, y.data_ptr(), _dtype(y), _stream(dev))
+        _check("nvfp4_attention_kv_cache_dev", st)
+        return y
     st = L.nvfp4_attention_kv_cache(
         qc.data_ptr(), qs.data_ptr(), qg.data_ptr(), k_cache["head"].data_ptr(),
         k_cache["tail"].data_ptr(), k_cache["codes"].data_ptr(), k_cache["scales"].data_ptr(),

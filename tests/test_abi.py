@@ -188,3 +188,20 @@ def test_huge_dimensions_are_refused_without_overflow(lib):
     c = lib.nvfp4_attention_kv_cache
     assert c(*([P] * 13), 1, big, big, 1, 8, 300, 128, 16, 16, 300, P, 0, None) == 2
     assert c(*([P] * 13), 1, 1, 2, 1, 8, 300, 128, 1 << 62, 1 << 62, 300, P, 0, None) == 2
+
+
+def test_device_length_argument_checks(lib):
+    a = lib.nvfp4_kv_append_dev
+    base = [P, 1, 1, 2, 1, 128, 4, 4, 64, 16, -2, 6, 0, None, P, P, P, P, P, P, None]
+    x = list(base); x[19] = None          # length missing
+    assert a(*x) == 1
+    x = list(base); x[19] = P + 4         # length not 8-byte aligned
+    assert a(*x) == 3
+    x = list(base); x[2] = 1 << 40; x[3] = 1 << 40
+    assert a(*x) == 2
+    x = list(base); x[4] = 0              # nothing to append: nothing enqueued
+    assert a(*x) == 0
+    c = lib.nvfp4_attention_kv_cache_dev
+    assert c(*([P] * 13), 1, 1, 2, 1, 8, None, 128, 16, 16, 300, P, 0, None) == 1
+    assert c(*([P] * 13), 1, 1, 2, 1, 8, P + 4, 128, 16, 16, 300, P, 0, None) == 3
+    assert c(*([P] * 13), 1, 1, 2, 1, 0, P, 128, 16, 16, 300, P, 0, None) == 0

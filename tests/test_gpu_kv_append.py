@@ -68,3 +68,104 @@ def test_append_capacity_check(gpu):
     x = torch.zeros(1, 1, 301, 128, dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(ValueError):
         gpu.kv_append(cache, x, g)
+
+
+# --- the device-resident length (capturable decode steps) ---
+
+def _same_cache(a, b, tm):
+    for key in ("head", "tail"):
+        assert torch.equal(a[key], b[key]), key
+    assert torch.equal(a["codes"][:, :, :tm], b["codes"][:, :, :tm])
+    assert torch.equal(a["scales"][:, :, :tm], b["scales"][:, :, :tm])
+
+
+@pytest.mark.parametrize("dtype,signs", [(torch.bfloat16, None), (torch.float32, None),
+                                         (torch.bfloat16, (5, 6, 7, 8))])
+def test_device_length_matches_host_length(gpu, dtype, signs):
+    B, H, D, nf, nl = 1, 2, 128, 32, 48
+    steps = [150, 1, 1, 40, 1, 7, 0, 3]
+    kv_all = workloads.workload(3, (B, H, sum(steps), D))
+    xall = to_dev(kv_all)
+    if dtype == torch.float32:
+        xall = xall.float()
+    g = gpu.global_scale(xall[:, :, :150].contiguous())
+    host = gpu.kv_cache_alloc(B, H, D, 300, nf, nl, dtype)
+    devc = gpu.kv_cache_alloc(B, H, D, 300, nf, nl, dtype)
+    had = signs is not None
+    t = 0
+    for k in steps:
+        print(f"[case] device-length append {k} tokens at {t} ({dtype}, signs={signs})", flush=True)
+        chunk = xall[:, :, t:t + k].contiguous()
+        gpu.kv_append(host, chunk, g, (-2, 6), signs=signs)
+        gpu.kv_append_dev(devc, chunk, g, (-2, 6), signs=signs)
+        t += k
+        torch.cuda.synchronize()
+        assert gpu.kv_length(devc) == host["length"] == t
+        _same_cache(host, devc, max(t - nf - nl, 0))
+
+
+def test_device_length_overflow_is_a_noop(gpu):
+    B, H, D, nf, nl = 1, 1, 128, 16, 16
+    kv = to_dev(workloads.workload(3, (B, H, 120, D)))
+    g = gpu.global_scale(kv)
+    c = gpu.kv_cache_alloc(B, H, D, 100, nf, nl)  # holds 100 tokens
+    gpu.kv_append_dev(c, kv[:, :, :90].contiguous(), g)
+    torch.cuda.synchronize()
+    before = {k: v.clone() for k, v in c.items() if isinstance(v, torch.Tensor)}
+    gpu.kv_append_dev(c, kv[:, :, 90:120].contiguous(), g)  # 90 + 30 > 100
+    torch.cuda.synchronize()
+    assert gpu.kv_length(c) == 90
+    for k, v in before.items():
+        assert torch.equal(c[k], v), k
+
+
+def test_graph_replayed_decode_step(gpu):
+    """One decode step (append a K and a V token at the device length, attention of one
+    query over the caches) captured once and replayed token after token; every replay is
+    checked against the host-length calls made eagerly on a second pair of caches."""
+    B, H, D, nf, nl = 1, 2, 128, 32, 32
+    n_pre, n_dec = 100, 12
+    rng = np.random.default_rng(5)
+    kall = to_dev(workloads.workload(3, (B, H, n_pre + n_dec, D)))
+    vall = to_dev(workloads.to_bf16_bits(rng.standard_normal((B, H, n_pre + n_dec, D))
+                                         .astype(np.float32)))
+    qx = to_dev(workloads.to_bf16_bits(rng.standard_normal((B, 2 * H, 1, D)).astype(np.float32)))
+    q = gpu.quantize(qx)
+    kg = gpu.global_scale(kall[:, :, :n_pre].contiguous())
+    vg = gpu.global_scale(vall[:, :, :n_pre].contiguous())
+    kd, vd = (gpu.kv_cache_alloc(B, H, D, 256, nf, nl) for _ in range(2))
+    kh, vh = (gpu.kv_cache_alloc(B, H, D, 256, nf, nl) for _ in range(2))
+    for c, x, gs in ((kd, kall, kg), (vd, vall, vg)):
+        gpu.kv_append_dev(c, x[:, :, :n_pre].contiguous(), gs)
+    for c, x, gs in ((kh, kall, kg), (vh, vall, vg)):
+        gpu.kv_append(c, x[:, :, :n_pre].contiguous(), gs)
+    knew = torch.empty(B, H, 1, D, dtype=torch.bfloat16, device="cuda")
+    vnew = torch.empty_like(knew)
+
+    def step():
+        gpu.kv_append_dev(kd, knew, kg)
+        gpu.kv_append_dev(vd, vnew, vg)
+        return gpu.attention_kv_cache(q, kd, kg, vd, vg, device_length=True)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        out = step()
+    torch.cuda.synchronize()
+    assert gpu.kv_length(kd) == n_pre  # capture launched nothing
+    for i in range(n_dec):
+        t = n_pre + i
+        print(f"[case] graph replay {i}: token {t}", flush=True)
+        knew.copy_(kall[:, :, t:t + 1])
+        vnew.copy_(vall[:, :, t:t + 1])
+        graph.replay()
+        gpu.kv_append(kh, kall[:, :, t:t + 1].contiguous(), kg)
+        gpu.kv_append(vh, vall[:, :, t:t + 1].contiguous(), vg)
+        ref = gpu.attention_kv_cache(q, kh, kg, vh, vg)
+        torch.cuda.synchronize()
+        assert gpu.kv_length(kd) == gpu.kv_length(vd) == t + 1
+        assert torch.equal(out, ref), f"replay {i}"
+        _same_cache(kh, kd, t + 1 - nf - nl)
+        _same_cache(vh, vd, t + 1 - nf - nl)
