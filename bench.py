@@ -361,6 +361,40 @@ def kv_append_table(torch, nv, workloads, iters: int = 200):
         print(f"| {t_new} | {ms * 1e3:.1f} | {t_new / (ms * 1e-3):.0f} | "
               f"{nbytes / (ms * 1e-3) / 1e9:.1f} |", flush=True)
 
+    # A decode step at the device-resident length, captured once and replayed: append
+    # one K and one V token to 32K-token caches, then attention of one query per head
+    # (32 query heads over the 8 K/V heads) over the caches.
+    steps = 200
+    kc = nv.kv_cache_alloc(B, H, D, 32768 + steps + 8, nf, nl, torch.bfloat16, dev)
+    vc = nv.kv_cache_alloc(B, H, D, 32768 + steps + 8, nf, nl, torch.bfloat16, dev)
+    nv.kv_append_dev(kc, x, g)
+    nv.kv_append_dev(vc, x, g)
+    knew = x[:, :, :1].contiguous()
+    vnew = x[:, :, 1:2].contiguous()
+    q = nv.quantize(torch.from_numpy(workloads.workload(5, (1, 32, 1, 128)).view(np.int16))
+                    .view(torch.bfloat16).to(dev))
+    torch.cuda.synchronize()
+    graphs = []
+    for parts in (("append",), ("append", "attention")):
+        gph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.graph(gph, stream=side):
+            nv.kv_append_dev(kc, knew, g)
+            nv.kv_append_dev(vc, vnew, g)
+            if "attention" in parts:
+                nv.attention_kv_cache(q, kc, g, vc, g, device_length=True)
+        graphs.append((parts, gph))
+    torch.cuda.synchronize()
+    print()
+    print("| captured decode step (graph replay, device-resident length) | us per step |")
+    print("|---|---|")
+    for parts, gph in graphs:
+        ms = event_time_ms(torch, gph.replay, steps // 2, stream)
+        name = "append 1 K + 1 V token" + (
+            ", then attention of 32 query heads over the 32K caches" if len(parts) > 1 else "")
+        print(f"| {name} | {ms * 1e3:.1f} |", flush=True)
+
 
 def formats_table(torch, nv, workloads, iters: int = 50):
     """Markdown tables: relative quantization error (sum (x - x^)^2 / sum x^2) of NVFP4
