@@ -1160,6 +1160,16 @@ int oracle_attention_nvfp4(const uint8_t *qc, const uint8_t *qs, float qg, const
 /* segment (head, middle, tail, each in token order) in tiles of `tile`      */
 /* keys that never straddle two segments (a segment's last tile may be       */
 /* short); everything else is the attention above. All T keys are visible.  */
+/*                                                                          */
+/* Split keys (split > 0, a multiple of the tile). The pages describe the   */
+/* attention's online softmax but not how a kernel spreads one query's keys */
+/* over parallel workers; this reading lets a decode step with few queries  */
+/* do so. The keys fall into units: the head, the tail, and the middle cut  */
+/* into pieces of `split` tokens from n_first (the last may be short). Each */
+/* unit runs the online softmax and the coding of P above from its own      */
+/* running max, alone; the unit states (m_u, l_u, acc_u) then combine       */
+/* exactly: with M = max m_u and w_u = exp(m_u - M), O = S_P sum w_u acc_u  */
+/* / sum w_u l_u. split = 0 folds the three segments into one state.        */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     const uint8_t *qc, *qs;
@@ -1167,28 +1177,164 @@ typedef struct {
     const uint16_t *kh, *kt, *vh, *vt;
     const uint8_t *kc, *ks, *vc, *vs;
     float kg, vg;
-    int64_t B, Hq, Hkv, Nq, T, D, nf, nl, cap, tile;
+    int64_t B, Hq, Hkv, Nq, T, D, nf, nl, cap, tile, split;
     double *O, *mag, *bound;
     int64_t r0, r1;
 } cjob_t;
+
+/* Online-softmax state of one query: running max m, sum l, and per output
+ * element the unnormalized sum acc, its magnitude sum mg and allowance bd. */
+typedef struct {
+    double m, l;
+    double *acc, *mg, *bd;
+} sstate_t;
+
+typedef struct {
+    double *s, *dl;
+    float *pf, *ph;
+} stile_t;
+
+/* Keys [lo, hi) of the cache in tiles of `tile` keys from lo (a last tile may
+ * be short), folded into the state st: the attention of the oracle above, with
+ * kv[t] the key in units that fold the query scale (and for coded keys the K
+ * tensor scale) in, and vv[t] * vfac[t] the value. */
+static void cache_tiles(const cjob_t *J, const float *q, const double *kv, const float *vv,
+                        const double *vfac, int64_t lo, int64_t hi, sstate_t *st, stile_t *w)
+{
+    const int64_t D = J->D, tile = J->tile;
+    const float SP = 1.0f / 2688.0f;
+    const double tau = 1.0 / sqrt((double)D);
+    double *s = w->s, *dl = w->dl;
+    float *pf = w->pf, *ph = w->ph;
+    for (int64_t t0 = lo; t0 < hi; t0 += tile) {
+        double mt = -INFINITY, amax_abs = 0.0;
+        for (int64_t u = 0; u < tile; ++u) {
+            int64_t j = t0 + u;
+            s[u] = -INFINITY;
+            if (j < hi) {
+                double dot = 0.0, ab = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    double pr = (double)q[d] * kv[j * D + d];
+                    dot += pr;
+                    ab += fabs(pr);
+                }
+                s[u] = tau * dot;
+                if (s[u] > mt)
+                    mt = s[u];
+                if (tau * ab > amax_abs)
+                    amax_abs = tau * ab;
+            }
+        }
+        double mn = st->m > mt ? st->m : mt;
+        if (mn == -INFINITY)
+            continue;
+        double alpha = (st->m == -INFINITY) ? 0.0 : exp(st->m - mn);
+        double psum = 0.0;
+        for (int64_t u = 0; u < tile; ++u) {
+            pf[u] = (s[u] == -INFINITY) ? 0.0f : (float)exp(s[u] - mn);
+            psum += pf[u];
+            dl[u] = (s[u] == -INFINITY) ? 0.0
+                                        : amax_abs * (double)(D + 2) * 0x1p-24 +
+                                              (fabs(s[u]) + fabs(mn)) * 0x1p-21 + 0x1p-20;
+        }
+        st->l = alpha * st->l + psum;
+        for (int64_t d = 0; d < D; ++d) {
+            st->acc[d] *= alpha;
+            st->mg[d] *= alpha;
+            st->bd[d] *= alpha;
+        }
+        for (int64_t u0 = 0; u0 < tile; u0 += 16) {
+            uint8_t cb[8];
+            int p = search_block(pf + u0, SP, 0, 0, cb, NULL);
+            float sp = oracle_e4m3_value(p);
+            float rr = 1.0f / (sp * SP);
+            float amax_b = 0.0f;
+            double dmax = 0.0, flip[16];
+            for (int e = 0; e < 16; ++e) {
+                int nib = (cb[e / 2] >> ((e & 1) * 4)) & 0xF;
+                ph[u0 + e] = E2M1_MAG[nib & 7] * sp;
+                if (pf[u0 + e] > amax_b)
+                    amax_b = pf[u0 + e];
+                if (dl[u0 + e] > dmax)
+                    dmax = dl[u0 + e];
+            }
+            for (int e = 0; e < 16; ++e) {
+                float gap = 0.0f;
+                flip[e] = 0.0;
+                if (pf[u0 + e] > 0.0f &&
+                    e2m1_mid_distance(pf[u0 + e] * rr, &gap) <= dl[u0 + e] + 0x1p-22)
+                    flip[e] = (double)gap * sp;
+            }
+            float tb = (amax_b / 6.0f) / SP;
+            if (amax_b > 0.0f) {
+                for (int nb = -1; nb <= 1; nb += 2) {
+                    int p2 = p + nb;
+                    if (p2 < 0 || p2 > 126)
+                        continue;
+                    double mid = 0.5 * ((double)oracle_e4m3_value(p) + oracle_e4m3_value(p2));
+                    if (fabs((double)tb - mid) <= (dmax + 0x1p-21) * mid) {
+                        float sp2 = oracle_e4m3_value(p2);
+                        float r2 = 1.0f / (sp2 * SP);
+                        for (int e = 0; e < 16; ++e) {
+                            float y2 = pf[u0 + e] * r2, gap2 = 0.0f;
+                            int c2 = oracle_e2m1_code(y2);
+                            double dv = fabs((double)E2M1_MAG[c2] * sp2 - ph[u0 + e]);
+                            if (pf[u0 + e] > 0.0f &&
+                                e2m1_mid_distance(y2, &gap2) <= dl[u0 + e] + 0x1p-22)
+                                dv += (double)gap2 * sp2;
+                            if (dv > flip[e])
+                                flip[e] = dv;
+                        }
+                    }
+                }
+            }
+            for (int e = 0; e < 16; ++e) {
+                int64_t j = t0 + u0 + e;
+                if (j >= hi || pf[u0 + e] == 0.0f)
+                    continue;
+                for (int64_t d = 0; d < D; ++d) {
+                    double v = (double)vv[j * D + d] * vfac[j];
+                    st->acc[d] += (double)ph[u0 + e] * v;
+                    st->mg[d] += (double)ph[u0 + e] * fabs(v);
+                    st->bd[d] += flip[e] * fabs(v);
+                }
+            }
+        }
+        st->m = mn;
+    }
+}
+
+static void state_clear(sstate_t *st, int64_t D)
+{
+    st->m = -INFINITY;
+    st->l = 0.0;
+    for (int64_t d = 0; d < D; ++d)
+        st->acc[d] = st->mg[d] = st->bd[d] = 0.0;
+}
 
 static void *attention_cache_rows(void *arg)
 {
     const cjob_t *J = (const cjob_t *)arg;
     const int64_t D = J->D, T = J->T, tile = J->tile;
-    const float SP = 1.0f / 2688.0f;
-    const double tau = 1.0 / sqrt((double)D);
+    const double SP = (double)(1.0f / 2688.0f);
     float *q = malloc(sizeof(float) * D);
     double *kv = malloc(sizeof(double) * D * (size_t)(T > 0 ? T : 1));
     float *vv = malloc(sizeof(float) * D * (size_t)(T > 0 ? T : 1));
     double *vfac = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
-    double *acc = malloc(sizeof(double) * D), *mg = malloc(sizeof(double) * D);
-    double *bd = malloc(sizeof(double) * D);
-    double *s = malloc(sizeof(double) * tile);
-    float *pf = malloc(sizeof(float) * tile), *ph = malloc(sizeof(float) * tile);
-    double *dl = malloc(sizeof(double) * tile);
-    int64_t cached = -1;
+    stile_t w = {malloc(sizeof(double) * tile), malloc(sizeof(double) * tile),
+                 malloc(sizeof(float) * tile), malloc(sizeof(float) * tile)};
     const int64_t mid_lo = J->nf, mid_hi = T - J->nl > J->nf ? T - J->nl : J->nf;
+    /* the units whose softmax states are combined: the three segments folded
+       into one state (no split), or head, each piece of `split` middle keys and
+       tail each with its own state */
+    const int64_t npieces = J->split > 0 ? (mid_hi - mid_lo + J->split - 1) / J->split : 0;
+    const int64_t nunits = J->split > 0 ? 2 + npieces : 1;
+    double *ubuf = malloc(sizeof(double) * (size_t)(3 * D * nunits + 1));
+    sstate_t *us = malloc(sizeof(sstate_t) * (size_t)nunits);
+    for (int64_t u = 0; u < nunits; ++u)
+        us[u] = (sstate_t){-INFINITY, 0.0, ubuf + 3 * D * u, ubuf + 3 * D * u + D,
+                           ubuf + 3 * D * u + 2 * D};
+    int64_t cached = -1;
     for (int64_t r = J->r0; r < J->r1; ++r) {
         int64_t bh = r / J->Nq;
         int64_t b = bh / J->Hq, h = bh % J->Hq;
@@ -1226,119 +1372,53 @@ static void *attention_cache_rows(void *arg)
             cached = kvh;
         }
         decode_row(J->qc + r * (D / 2), J->qs + r * (D / 16), D, q);
-        double m = -INFINITY, l = 0.0;
-        for (int64_t d = 0; d < D; ++d)
-            acc[d] = mg[d] = bd[d] = 0.0;
-        const int64_t seg[3][2] = {{0, J->nf < T ? J->nf : T}, {mid_lo, mid_hi}, {mid_hi > J->nf ? mid_hi : J->nf, T}};
-        for (int sg = 0; sg < 3; ++sg) {
-            for (int64_t t0 = seg[sg][0]; t0 < seg[sg][1]; t0 += tile) {
-                double mt = -INFINITY, amax_abs = 0.0;
-                for (int64_t u = 0; u < tile; ++u) {
-                    int64_t j = t0 + u;
-                    s[u] = -INFINITY;
-                    if (j < seg[sg][1]) {
-                        double dot = 0.0, ab = 0.0;
-                        for (int64_t d = 0; d < D; ++d) {
-                            double pr = (double)q[d] * kv[j * D + d];
-                            dot += pr;
-                            ab += fabs(pr);
-                        }
-                        s[u] = tau * dot;
-                        if (s[u] > mt)
-                            mt = s[u];
-                        if (tau * ab > amax_abs)
-                            amax_abs = tau * ab;
-                    }
-                }
-                double mn = m > mt ? m : mt;
-                if (mn == -INFINITY)
-                    continue;
-                double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
-                double psum = 0.0;
-                for (int64_t u = 0; u < tile; ++u) {
-                    pf[u] = (s[u] == -INFINITY) ? 0.0f : (float)exp(s[u] - mn);
-                    psum += pf[u];
-                    dl[u] = (s[u] == -INFINITY) ? 0.0
-                                                : amax_abs * (double)(D + 2) * 0x1p-24 +
-                                                      (fabs(s[u]) + fabs(mn)) * 0x1p-21 + 0x1p-20;
-                }
-                l = alpha * l + psum;
-                for (int64_t d = 0; d < D; ++d) {
-                    acc[d] *= alpha;
-                    mg[d] *= alpha;
-                    bd[d] *= alpha;
-                }
-                for (int64_t u0 = 0; u0 < tile; u0 += 16) {
-                    uint8_t cb[8];
-                    int p = search_block(pf + u0, SP, 0, 0, cb, NULL);
-                    float sp = oracle_e4m3_value(p);
-                    float rr = 1.0f / (sp * SP);
-                    float amax_b = 0.0f;
-                    double dmax = 0.0, flip[16];
-                    for (int e = 0; e < 16; ++e) {
-                        int nib = (cb[e / 2] >> ((e & 1) * 4)) & 0xF;
-                        ph[u0 + e] = E2M1_MAG[nib & 7] * sp;
-                        if (pf[u0 + e] > amax_b)
-                            amax_b = pf[u0 + e];
-                        if (dl[u0 + e] > dmax)
-                            dmax = dl[u0 + e];
-                    }
-                    for (int e = 0; e < 16; ++e) {
-                        float gap = 0.0f;
-                        flip[e] = 0.0;
-                        if (pf[u0 + e] > 0.0f &&
-                            e2m1_mid_distance(pf[u0 + e] * rr, &gap) <= dl[u0 + e] + 0x1p-22)
-                            flip[e] = (double)gap * sp;
-                    }
-                    float tb = (amax_b / 6.0f) / SP;
-                    if (amax_b > 0.0f) {
-                        for (int nb = -1; nb <= 1; nb += 2) {
-                            int p2 = p + nb;
-                            if (p2 < 0 || p2 > 126)
-                                continue;
-                            double mid = 0.5 * ((double)oracle_e4m3_value(p) + oracle_e4m3_value(p2));
-                            if (fabs((double)tb - mid) <= (dmax + 0x1p-21) * mid) {
-                                float sp2 = oracle_e4m3_value(p2);
-                                float r2 = 1.0f / (sp2 * SP);
-                                for (int e = 0; e < 16; ++e) {
-                                    float y2 = pf[u0 + e] * r2, gap2 = 0.0f;
-                                    int c2 = oracle_e2m1_code(y2);
-                                    double dv = fabs((double)E2M1_MAG[c2] * sp2 - ph[u0 + e]);
-                                    if (pf[u0 + e] > 0.0f &&
-                                        e2m1_mid_distance(y2, &gap2) <= dl[u0 + e] + 0x1p-22)
-                                        dv += (double)gap2 * sp2;
-                                    if (dv > flip[e])
-                                        flip[e] = dv;
-                                }
-                            }
-                        }
-                    }
-                    for (int e = 0; e < 16; ++e) {
-                        int64_t j = t0 + u0 + e;
-                        if (j >= seg[sg][1] || pf[u0 + e] == 0.0f)
-                            continue;
-                        for (int64_t d = 0; d < D; ++d) {
-                            double v = (double)vv[j * D + d] * vfac[j];
-                            acc[d] += (double)ph[u0 + e] * v;
-                            mg[d] += (double)ph[u0 + e] * fabs(v);
-                            bd[d] += flip[e] * fabs(v);
-                        }
-                    }
-                }
-                m = mn;
+        const int64_t head_hi = J->nf < T ? J->nf : T;
+        const int64_t tail_lo = mid_hi > J->nf ? mid_hi : J->nf;
+        if (J->split <= 0) {
+            state_clear(&us[0], D);
+            cache_tiles(J, q, kv, vv, vfac, 0, head_hi, &us[0], &w);
+            cache_tiles(J, q, kv, vv, vfac, mid_lo, mid_hi, &us[0], &w);
+            cache_tiles(J, q, kv, vv, vfac, tail_lo, T, &us[0], &w);
+        } else {
+            state_clear(&us[0], D);
+            cache_tiles(J, q, kv, vv, vfac, 0, head_hi, &us[0], &w);
+            state_clear(&us[1], D);
+            cache_tiles(J, q, kv, vv, vfac, tail_lo, T, &us[1], &w);
+            for (int64_t k = 0; k < npieces; ++k) {
+                int64_t lo = mid_lo + k * J->split, hi = lo + J->split;
+                state_clear(&us[2 + k], D);
+                cache_tiles(J, q, kv, vv, vfac, lo, hi < mid_hi ? hi : mid_hi, &us[2 + k], &w);
             }
         }
-        double f = (l > 0.0) ? (double)SP / l : 0.0;
+        /* combine: weights exp(m_u - M); a unit with no key has m_u = -inf */
+        double M = -INFINITY;
+        for (int64_t u = 0; u < nunits; ++u)
+            if (us[u].m > M)
+                M = us[u].m;
+        double L = 0.0;
+        for (int64_t u = 0; u < nunits; ++u)
+            if (us[u].m > -INFINITY)
+                L += exp(us[u].m - M) * us[u].l;
+        double f = (L > 0.0) ? SP / L : 0.0;
         for (int64_t d = 0; d < D; ++d) {
-            J->O[r * D + d] = acc[d] * f;
+            double o = 0.0, mg = 0.0, bd = 0.0;
+            for (int64_t u = 0; u < nunits; ++u) {
+                if (us[u].m == -INFINITY)
+                    continue;
+                double wu = exp(us[u].m - M);
+                o += wu * us[u].acc[d];
+                mg += wu * us[u].mg[d];
+                bd += wu * us[u].bd[d];
+            }
+            J->O[r * D + d] = o * f;
             if (J->mag)
-                J->mag[r * D + d] = mg[d] * f;
+                J->mag[r * D + d] = mg * f;
             if (J->bound)
-                J->bound[r * D + d] = bd[d] * f;
+                J->bound[r * D + d] = bd * f;
         }
     }
-    free(q); free(kv); free(vv); free(vfac); free(acc); free(mg); free(bd);
-    free(s); free(pf); free(ph); free(dl);
+    free(q); free(kv); free(vv); free(vfac); free(ubuf); free(us);
+    free(w.s); free(w.dl); free(w.pf); free(w.ph);
     return NULL;
 }
 
@@ -1347,10 +1427,12 @@ int oracle_attention_kv_cache(const uint8_t *qc, const uint8_t *qs, float qg, co
                               const uint16_t *vh, const uint16_t *vt, const uint8_t *vc,
                               const uint8_t *vs, float vg, int64_t B, int64_t Hq, int64_t Hkv,
                               int64_t Nq, int64_t T, int64_t D, int64_t nf, int64_t nl, int64_t cap,
-                              int64_t tile, double *O, double *mag, double *bound, int nthreads)
+                              int64_t tile, int64_t split, double *O, double *mag, double *bound,
+                              int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || T < 0 || D <= 0 || D % 16 ||
-        D > 1024 || nf < 0 || nl < 0 || cap < 0 || tile <= 0 || tile % 16 || !O)
+        D > 1024 || nf < 0 || nl < 0 || cap < 0 || tile <= 0 || tile % 16 || split < 0 ||
+        (split > 0 && split % tile) || !O)
         return ORACLE_EINVAL;
     int64_t mid = T - nf - nl;
     if (mid > cap)
@@ -1369,7 +1451,7 @@ int oracle_attention_kv_cache(const uint8_t *qc, const uint8_t *qs, float qg, co
     cjob_t jobs[256];
     for (int t = 0; t < nthreads; ++t) {
         jobs[t] = (cjob_t){qc, qs, qg, kh, kt, vh, vt, kc, ks, vc, vs, kg, vg, B, Hq, Hkv, Nq, T,
-                           D, nf, nl, cap, tile, O, mag, bound, rows * t / nthreads,
+                           D, nf, nl, cap, tile, split, O, mag, bound, rows * t / nthreads,
                            rows * (t + 1) / nthreads};
         running[t] = nthreads > 1 && pthread_create(&th[t], NULL, attention_cache_rows, &jobs[t]) == 0;
         if (!running[t])

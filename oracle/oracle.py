@@ -89,7 +89,7 @@ def lib() -> ctypes.CDLL:
             L.oracle_attention_nvfp4.restype = i32
             L.oracle_attention_kv_cache.argtypes = [vp, vp, f32, vp, vp, vp, vp, f32, vp, vp, vp,
                                                     vp, f32, i64, i64, i64, i64, i64, i64, i64,
-                                                    i64, i64, i64, vp, vp, vp, i32]
+                                                    i64, i64, i64, i64, vp, vp, vp, i32]
             L.oracle_attention_kv_cache.restype = i32
             _lib = L
     return _lib
@@ -315,10 +315,12 @@ def attention_nvfp4(q, k, v, tile: int = 32, causal: bool = False, nthreads: int
 
 
 def attention_kv_cache(q, k, v, T: int, n_first: int, n_last: int, tile: int = 32,
-                       nthreads: int | None = None):
+                       split: int = 0, nthreads: int | None = None):
     """Attention over the attention-sink KV cache. q: (codes, scales, tensor scale) of
     [B, Hq, Nq, D]; k, v: dicts with head [B,H,nf,D], tail [B,H,nl,D] (bf16 bits, ring by
-    token mod nl), codes [B,H,cap,D/2], scales [B,H,cap,D/16], gscale. Returns (O, mag, bound)."""
+    token mod nl), codes [B,H,cap,D/2], scales [B,H,cap,D/16], gscale. split > 0 (a
+    multiple of tile): head, tail and each piece of `split` middle tokens run their
+    softmax alone and are combined. Returns (O, mag, bound)."""
     qc, qs, qg = q
     qc = np.ascontiguousarray(qc, dtype=np.uint8)
     qs = np.ascontiguousarray(qs, dtype=np.uint8)
@@ -335,7 +337,8 @@ def attention_kv_cache(q, k, v, T: int, n_first: int, n_last: int, tile: int = 3
     rc = lib().oracle_attention_kv_cache(_ptr(qc), _ptr(qs), float(qg), _ptr(kh), _ptr(kt),
                                          _ptr(kc), _ptr(ks), float(k["gscale"]), _ptr(vh),
                                          _ptr(vt), _ptr(vc), _ptr(vs), float(v["gscale"]), B, Hq,
-                                         Hkv, Nq, T, D, n_first, n_last, cap, tile, _ptr(O),
+                                         Hkv, Nq, T, D, n_first, n_last, cap, tile, split,
+                                         _ptr(O),
                                          _ptr(mag), _ptr(bound), _threads(nthreads))
     if rc:
         raise ValueError(f"oracle_attention_kv_cache failed ({rc})")

@@ -31,8 +31,8 @@ int oracle_attention_kv_cache(const uint8_t *, const uint8_t *, float, const uin
                               const uint16_t *, const uint8_t *, const uint8_t *, float,
                               const uint16_t *, const uint16_t *, const uint8_t *,
                               const uint8_t *, float, int64_t, int64_t, int64_t, int64_t, int64_t,
-                              int64_t, int64_t, int64_t, int64_t, int64_t, double *, double *,
-                              double *, int);
+                              int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, double *,
+                              double *, double *, int);
 
 static uint64_t state = 88172645463325252ull;
 static double uniform(void) { /* xorshift64 */
@@ -104,8 +104,13 @@ int main(void) {
     /* the sink cache: head NF, tail ring NL, middle rows = the coded middle */
     CHECK(oracle_attention_kv_cache(qc, qs, qg, sink, sink + B * H * NF * D, kc, ks, kg, sink,
                                     sink + B * H * NF * D, kc, ks, kg, B, H, 1, NQ, NF + TM + NL, D,
-                                    NF, NL, TM, 32, O, O + B * H * NQ * D, O + 2 * B * H * NQ * D,
-                                    2));
+                                    NF, NL, TM, 32, 0, O, O + B * H * NQ * D,
+                                    O + 2 * B * H * NQ * D, 2));
+    /* the same with the middle split into pieces of 64 tokens */
+    CHECK(oracle_attention_kv_cache(qc, qs, qg, sink, sink + B * H * NF * D, kc, ks, kg, sink,
+                                    sink + B * H * NF * D, kc, ks, kg, B, H, 1, NQ, NF + TM + NL, D,
+                                    NF, NL, TM, 32, 64, O, O + B * H * NQ * D,
+                                    O + 2 * B * H * NQ * D, 2));
     free(x); free(xb); free(codes); free(scales); free(fsel); free(y); free(kv); free(kc);
     free(ks); free(sink); free(yk); free(qc); free(qs); free(O);
     puts("oracle sanitizer run: ok");

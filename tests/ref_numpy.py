@@ -332,11 +332,13 @@ def cache_values(c, T: int, nf: int, nl: int) -> np.ndarray:
     return out
 
 
-def attention_cache_ref(q, k, v, T: int, nf: int, nl: int, tile: int = 32):
+def attention_cache_ref(q, k, v, T: int, nf: int, nl: int, tile: int = 32, split: int = 0):
     """Attention over the sink KV cache with NumPy: key values assembled from the head
     (t < nf), the ring (t >= max(nf, T - nl), slot t mod nl) and the coded middle; keys
     visited segment by segment in tiles of `tile` that stay inside a segment; P coded
-    per 16 keys as in attention_ref."""
+    per 16 keys as in attention_ref. split > 0: the head, the tail and each piece of
+    `split` middle tokens keep separate softmax states, merged at the end by the
+    weights exp(m_u - max m)."""
     def bf(a):
         return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     qd = nvfp4_decode(q[0], q[1]) * float(q[2])
@@ -358,29 +360,45 @@ def attention_cache_ref(q, k, v, T: int, nf: int, nl: int, tile: int = 32):
         return out
 
     segs = [(0, min(nf, T)), (nf, mid_hi), (max(mid_hi, nf), T)]
+    if split:
+        units = [[segs[0]], [segs[2]]] + [[(a, min(a + split, mid_hi))]
+                                          for a in range(nf, mid_hi, split)]
+    else:
+        units = [segs]
     O = np.zeros((B, Hq, Nq, D))
     for b in range(B):
         for h in range(Hq):
             hk = h // (Hq // Hkv)
             K, V = values(k, b, hk), values(v, b, hk)
             S = (qd[b, h] @ K.T) / np.sqrt(D)
-            m = np.full(Nq, -np.inf)
-            l = np.zeros(Nq)
-            acc = np.zeros((Nq, D))
-            for lo, hi in segs:
-                for t0 in range(lo, hi, tile):
-                    w = min(tile, hi - t0)
-                    St = np.full((Nq, tile), -np.inf)
-                    St[:, :w] = S[:, t0:t0 + w]
-                    mn = np.maximum(m, St.max(axis=1))
-                    with np.errstate(invalid="ignore"):
-                        alpha = np.where(np.isfinite(m), np.exp(m - mn), 0.0)
-                        P = np.where(np.isfinite(St), np.exp(St - mn[:, None]), 0.0).astype(np.float32)
-                    l = alpha * l + P.astype(np.float64).sum(axis=1)
-                    codes, scales, _, _ = quantize_ref_search(P, 0, 0, sg=SP)
-                    Vt = np.zeros((tile, D))
-                    Vt[:w] = V[t0:t0 + w]
-                    acc = alpha[:, None] * acc + nvfp4_decode(codes, scales) @ Vt
-                    m = mn
-            O[b, h] = acc * float(SP) / l[:, None]
+            states = []
+            for unit in units:
+                m = np.full(Nq, -np.inf)
+                l = np.zeros(Nq)
+                acc = np.zeros((Nq, D))
+                for lo, hi in unit:
+                    for t0 in range(lo, hi, tile):
+                        w = min(tile, hi - t0)
+                        St = np.full((Nq, tile), -np.inf)
+                        St[:, :w] = S[:, t0:t0 + w]
+                        mn = np.maximum(m, St.max(axis=1))
+                        with np.errstate(invalid="ignore"):
+                            alpha = np.where(np.isfinite(m), np.exp(m - mn), 0.0)
+                            P = np.where(np.isfinite(St), np.exp(St - mn[:, None]), 0.0).astype(np.float32)
+                        l = alpha * l + P.astype(np.float64).sum(axis=1)
+                        codes, scales, _, _ = quantize_ref_search(P, 0, 0, sg=SP)
+                        Vt = np.zeros((tile, D))
+                        Vt[:w] = V[t0:t0 + w]
+                        acc = alpha[:, None] * acc + nvfp4_decode(codes, scales) @ Vt
+                        m = mn
+                states.append((m, l, acc))
+            M = np.max([st[0] for st in states], axis=0)
+            num = np.zeros((Nq, D))
+            den = np.zeros(Nq)
+            for m, l, acc in states:
+                with np.errstate(invalid="ignore"):
+                    wgt = np.where(np.isfinite(m), np.exp(m - M), 0.0)
+                num += wgt[:, None] * acc
+                den += wgt * l
+            O[b, h] = num * float(SP) / den[:, None]
     return O

@@ -149,3 +149,81 @@ def test_cache_without_sinks_is_plain_attention(orc):
     O2, _, _ = orc.attention_nvfp4(q, k, v)
     # the two apply the tensor scales at different points in double precision
     np.testing.assert_allclose(O, O2, rtol=1e-9, atol=1e-15)
+
+
+# --- split keys: units with separate softmax states, merged ---
+
+def _cache_case(orc, T, nf, nl, Nq=3, Hq=4, Hkv=2, seed=0):
+    rng = np.random.default_rng(seed)
+    qx = workloads.to_bf16_bits(rng.standard_normal((1, Hq, Nq, 128)).astype(np.float32))
+    kx = workloads.workload(3, (1, Hkv, T, 128))
+    vx = workloads.to_bf16_bits(rng.standard_normal((1, Hkv, T, 128)).astype(np.float32))
+    q = quant(orc, qx)
+    return q, cache_of(orc, kx, nf, nl, T, T), cache_of(orc, vx, nf, nl, T, T)
+
+
+@pytest.mark.parametrize("T,nf,nl,split", [(300, 32, 48, 64), (300, 32, 48, 96), (90, 64, 64, 32),
+                                           (260, 0, 0, 64), (200, 16, 0, 32), (40, 64, 64, 64),
+                                           (500, 128, 128, 512)])
+def test_cache_split_matches_numpy_reference(orc, T, nf, nl, split):
+    q, k, v = _cache_case(orc, T, nf, nl, seed=T + split)
+    O, _, _ = orc.attention_kv_cache(q, k, v, T, nf, nl, split=split)
+    ref = ref_numpy.attention_cache_ref(q, k, v, T, nf, nl, split=split)
+    np.testing.assert_allclose(O, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_cache_split_one_unit_is_the_unsplit_attention(orc):
+    """No sinks and one middle piece: a single unit, whose merge weight is 1."""
+    q, k, v = _cache_case(orc, 200, 0, 0, seed=5)
+    O, _, _ = orc.attention_kv_cache(q, k, v, 200, 0, 0, split=256)
+    O0, _, _ = orc.attention_kv_cache(q, k, v, 200, 0, 0)
+    assert np.array_equal(O, O0)
+
+
+def test_cache_split_is_the_mass_weighted_mean_of_unit_attentions(orc):
+    """The merged output equals sum_u Z_u O_u / sum_u Z_u, where O_u is the unsplit
+    oracle's attention over unit u's keys alone (as a cache of its own) and Z_u the
+    softmax mass exp(s) of those keys, computed here in float64 from the decoded
+    operands. Equal up to the rounding of the probabilities to binary32 in l."""
+    T, nf, nl, split = 330, 32, 48, 96
+    q, k, v = _cache_case(orc, T, nf, nl, Nq=2, Hq=2, Hkv=1, seed=11)
+    O, _, _ = orc.attention_kv_cache(q, k, v, T, nf, nl, split=split)
+    D = 128
+    qd = ref_numpy.nvfp4_decode(q[0], q[1]) * float(q[2])
+    bf = lambda a: (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    mid_hi = max(T - nl, nf)
+    empty = np.zeros((1, 1, 0, D), np.uint16)
+
+    def sub_sink(c, rows):  # bf16 rows as the head of a cache with nothing else
+        return dict(head=rows, tail=empty, codes=np.zeros((1, 1, 0, D // 2), np.uint8),
+                    scales=np.zeros((1, 1, 0, D // 16), np.uint8), gscale=c["gscale"])
+
+    def sub_mid(c, a, b):
+        return dict(head=empty, tail=empty, codes=c["codes"][:, :, a - nf:b - nf],
+                    scales=c["scales"][:, :, a - nf:b - nf], gscale=c["gscale"])
+
+    tail_rows = lambda c: np.stack([c["tail"][:, :, t % nl] for t in range(mid_hi, T)], axis=2)
+    units = [(sub_sink(k, k["head"]), sub_sink(v, v["head"]), nf, nf,
+              bf(k["head"][0, 0])),
+             (sub_sink(k, tail_rows(k)), sub_sink(v, tail_rows(v)), T - mid_hi, T - mid_hi,
+              bf(tail_rows(k)[0, 0]))]
+    for a in range(nf, mid_hi, split):
+        b = min(a + split, mid_hi)
+        kd = ref_numpy.nvfp4_decode(k["codes"][0, 0, a - nf:b - nf],
+                                    k["scales"][0, 0, a - nf:b - nf]) * float(k["gscale"])
+        units.append((sub_mid(k, a, b), sub_mid(v, a, b), b - a, 0, kd))
+    num = np.zeros_like(O)
+    den = np.zeros(O.shape[:3] + (1,))
+    for ku, vu, Tu, nfu, kvals in units:
+        Ou, _, _ = orc.attention_kv_cache(q, ku, vu, Tu, nfu, 0)
+        s = np.einsum("hqd,kd->hqk", qd[0], kvals) / np.sqrt(D)
+        Z = np.exp(s - 40.0).sum(axis=-1)[None, :, :, None]
+        num += Z * Ou
+        den += Z
+    np.testing.assert_allclose(O, num / den, rtol=1e-6, atol=1e-7 * np.abs(O).max())
+
+
+def test_cache_split_must_be_whole_tiles(orc):
+    q, k, v = _cache_case(orc, 100, 16, 16, seed=2)
+    with pytest.raises(ValueError):
+        orc.attention_kv_cache(q, k, v, 100, 16, 16, split=48)
