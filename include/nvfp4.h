@@ -244,6 +244,48 @@ NVFP4_API nvfp4_status nvfp4_attention_kv_cache_dev(
     const int64_t *length, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, void *out,
     nvfp4_dtype out_dt, void *stream);
 
+/* Cache attention with the keys split over workgroups, for decode steps with few
+ * queries (ScaleSearch summary page, ScaleSearchAttention: the online softmax of
+ * the attention on NVFP4 operands; the split is a reading of this library, as the
+ * pages do not say how one query's keys are spread over parallel workers). The
+ * keys fall into units: the head, the tail, and the middle cut into pieces of
+ * `split` tokens from n_first (the last may be short). Each unit runs the online
+ * softmax and the P coding of nvfp4_attention_kv_cache over its own keys, from its
+ * own running max (P codes therefore differ from the unsplit call's); a second
+ * kernel merges the unit states exactly: with M the largest running max and
+ * w_u = exp(m_u - M), O = fl(1/2688) * sum w_u acc_u / sum w_u l_u. split > 0 and a
+ * multiple of 32; at most 65535 units. workspace: device memory of at least
+ * nvfp4_attention_split_workspace_bytes(B, Hq, Nq, cap, split) bytes, 16-byte
+ * aligned, owned by the caller, overwritten by the call (calls sharing a workspace
+ * must not overlap). Other arguments and errors as nvfp4_attention_kv_cache;
+ * NVFP4_EWORKSPACE for a missing or short workspace. */
+NVFP4_API nvfp4_status nvfp4_attention_kv_cache_split(
+    const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
+    const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
+    const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
+    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    int64_t T, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, int64_t split,
+    void *workspace, size_t workspace_bytes, void *out, nvfp4_dtype out_dt, void *stream);
+
+/* nvfp4_attention_kv_cache_split with the token count read from device memory,
+ * as nvfp4_attention_kv_cache_dev: the grid covers every unit of a full cache and
+ * units past the tokens present contribute nothing, so one captured launch serves
+ * every length. */
+NVFP4_API nvfp4_status nvfp4_attention_kv_cache_split_dev(
+    const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
+    const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
+    const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
+    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    const int64_t *length, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, int64_t split,
+    void *workspace, size_t workspace_bytes, void *out, nvfp4_dtype out_dt, void *stream);
+
+/* Workspace bytes of the split cache attention for a cache of `cap` middle rows:
+ * (2 + ceil(cap / split)) units x B * Hq * Nq rows x (128 + 2) FP32 values. 0 for
+ * arguments the split calls reject (split not a positive multiple of 32, too many
+ * units, sizes out of range). */
+NVFP4_API size_t nvfp4_attention_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq,
+                                                       int64_t cap, int64_t split);
+
 /* Randomized Hadamard transform (QuIP#-style incoherence processing, ScaleSearch
  * summary page, ScaleSearchAttention section: a transform pair Q' = Q R^-T,
  * K' = K R that keeps Q K^T while lowering the mean-square absolute value).

@@ -8,6 +8,7 @@ from .nvfp4 import (  # noqa: F401
     NVFP4Error,
     attention,
     attention_kv_cache,
+    attention_split_workspace_bytes,
     dequantize,
     dequantize_kv_sink,
     global_scale,

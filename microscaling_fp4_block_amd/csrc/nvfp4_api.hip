@@ -657,14 +657,20 @@ namespace {
 // count read from that device word when the kernel runs (clamped to the
 // cache's n_first + cap + n_last); checks that need T are then made on the
 // cache's capacity instead.
+// Units of a split cache attention sized for a middle of `cap` tokens: the
+// head, the tail and ceil(cap / split) pieces.
+int64_t split_units(int64_t cap, int64_t split) { return 2 + (cap + split - 1) / split; }
+
 nvfp4_status attention_kv_cache_impl(
     const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
     const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
     const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
     const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
     int64_t T, const int64_t *len_dev, int64_t D, int64_t n_first, int64_t n_last, int64_t cap,
-    void *out, nvfp4_dtype out_dt, void *stream) {
+    int64_t split, void *workspace, size_t workspace_bytes, void *out, nvfp4_dtype out_dt,
+    void *stream) {
   if (!dtype_ok(out_dt) || cache_dt != NVFP4_BF16) return NVFP4_EINVAL;
+  if (split < 0 || split % 32 || split > (1ll << 30)) return NVFP4_EINVAL;
   if (D != 128) return NVFP4_ESHAPE;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || T < 0 || n_first < 0 || n_last < 0 ||
       cap < 0)
@@ -685,6 +691,12 @@ nvfp4_status attention_kv_cache_impl(
       !aligned(k_head, 16) || !aligned(k_tail, 16) || !aligned(v_head, 16) ||
       !aligned(v_tail, 16) || !aligned(out, 16) || !aligned(len_dev, 8))
     return NVFP4_EALIGN;
+  if (split > 0) {
+    if (split_units(cap, split) > 65535) return NVFP4_ESHAPE;
+    const size_t need = nvfp4_attention_split_workspace_bytes(B, Hq, Nq, cap, split);
+    if (!workspace || need == 0 || workspace_bytes < need) return NVFP4_EWORKSPACE;
+    if (!aligned(workspace, 16)) return NVFP4_EALIGN;
+  }
   AttnArgs a{};
   a.qc = q_codes;
   a.qs = q_scales;
@@ -712,6 +724,12 @@ nvfp4_status attention_kv_cache_impl(
   a.nl = (uint32_t)n_last;
   a.cap = (uint32_t)cap;
   a.nk_dev = len_dev;
+  if (split > 0) {
+    const int64_t part = split_units(cap, split) * B * Hq * Nq * 128;
+    a.split = (uint32_t)split;
+    a.part = (float *)workspace;
+    a.ml = (float2 *)((float *)workspace + part);
+  }
   return hip_status(launch_attention(a, out_dt == NVFP4_BF16, (hipStream_t)stream));
 }
 
@@ -728,8 +746,8 @@ nvfp4_status nvfp4_attention_kv_cache(
     nvfp4_dtype out_dt, void *stream) {
   return attention_kv_cache_impl(q_codes, q_scales, q_gscale, k_head, k_tail, k_codes, k_scales,
                                  k_gscale, v_head, v_tail, v_codes, v_scales, v_gscale, cache_dt,
-                                 B, Hq, Hkv, Nq, T, nullptr, D, n_first, n_last, cap, out, out_dt,
-                                 stream);
+                                 B, Hq, Hkv, Nq, T, nullptr, D, n_first, n_last, cap, 0, nullptr,
+                                 0, out, out_dt, stream);
 }
 
 nvfp4_status nvfp4_attention_kv_cache_dev(
@@ -742,8 +760,47 @@ nvfp4_status nvfp4_attention_kv_cache_dev(
   if (!length) return NVFP4_EINVAL;
   return attention_kv_cache_impl(q_codes, q_scales, q_gscale, k_head, k_tail, k_codes, k_scales,
                                  k_gscale, v_head, v_tail, v_codes, v_scales, v_gscale, cache_dt,
-                                 B, Hq, Hkv, Nq, 0, length, D, n_first, n_last, cap, out, out_dt,
-                                 stream);
+                                 B, Hq, Hkv, Nq, 0, length, D, n_first, n_last, cap, 0, nullptr,
+                                 0, out, out_dt, stream);
+}
+
+size_t nvfp4_attention_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t cap,
+                                             int64_t split) {
+  if (B < 0 || Hq <= 0 || Nq < 0 || cap < 0 || cap > (1ll << 30) || split <= 0 || split % 32 ||
+      split > (1ll << 30) || !prod_le(B, Hq, 65535) || Nq > (1ll << 30))
+    return 0;
+  const int64_t units = split_units(cap, split), rows = B * Hq * Nq;
+  if (units > 65535 || rows > kMaxBlocks / 8) return 0;
+  // per unit and row: 128 FP32 accumulator values, then (max, sum)
+  return (size_t)(units * rows) * (128 * sizeof(float) + 2 * sizeof(float));
+}
+
+nvfp4_status nvfp4_attention_kv_cache_split(
+    const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
+    const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
+    const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
+    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    int64_t T, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, int64_t split,
+    void *workspace, size_t workspace_bytes, void *out, nvfp4_dtype out_dt, void *stream) {
+  if (split <= 0) return NVFP4_EINVAL;
+  return attention_kv_cache_impl(q_codes, q_scales, q_gscale, k_head, k_tail, k_codes, k_scales,
+                                 k_gscale, v_head, v_tail, v_codes, v_scales, v_gscale, cache_dt,
+                                 B, Hq, Hkv, Nq, T, nullptr, D, n_first, n_last, cap, split,
+                                 workspace, workspace_bytes, out, out_dt, stream);
+}
+
+nvfp4_status nvfp4_attention_kv_cache_split_dev(
+    const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
+    const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
+    const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
+    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    const int64_t *length, int64_t D, int64_t n_first, int64_t n_last, int64_t cap, int64_t split,
+    void *workspace, size_t workspace_bytes, void *out, nvfp4_dtype out_dt, void *stream) {
+  if (!length || split <= 0) return NVFP4_EINVAL;
+  return attention_kv_cache_impl(q_codes, q_scales, q_gscale, k_head, k_tail, k_codes, k_scales,
+                                 k_gscale, v_head, v_tail, v_codes, v_scales, v_gscale, cache_dt,
+                                 B, Hq, Hkv, Nq, 0, length, D, n_first, n_last, cap, split,
+                                 workspace, workspace_bytes, out, out_dt, stream);
 }
 
 }  // extern "C"

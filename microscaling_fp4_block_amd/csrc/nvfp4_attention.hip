@@ -170,7 +170,13 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f16x8 h) {
 }
 
 // CACHE: keys from the sink cache's three segments (else one coded segment).
-template <bool OUT_BF16, bool CACHE>
+// The query heads that share a KV head are adjacent rows of Q, so in cache
+// mode (never causal) a workgroup takes 128 consecutive rows of those G * Nq
+// and the cache is read once per KV head, not once per query head.
+// SPLIT (cache mode): this workgroup runs one unit of keys (blockIdx.z: 0 the
+// head, 1 the tail, 2 + k the k-th piece of `split` middle tokens) and writes
+// its softmax state for attention_merge_kernel instead of the output.
+template <bool OUT_BF16, bool CACHE, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // two buffers: tile i is decoded into buffer i & 1 while the codes of tile
   // i + 1 are in flight, so one barrier per tile suffices
@@ -182,14 +188,18 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6, g = lane >> 5;
   const uint32_t col = lane & 31u;
+  // rows of Q this grid row covers: one head's Nq queries, or in cache mode the
+  // G * Nq queries of the G heads of KV head blockIdx.y
   const uint32_t bh = blockIdx.y;
-  const uint32_t b = bh / a.Hq, h = bh - b * a.Hq;
-  const uint32_t kvh = b * a.Hkv + h / (a.Hq / a.Hkv);
+  const uint32_t rows = CACHE ? a.Nq * (a.Hq / a.Hkv) : a.Nq;
+  const uint32_t kvh = CACHE ? bh : (bh / a.Hq) * a.Hkv + (bh % a.Hq) / (a.Hq / a.Hkv);
   // causal: the last query blocks see the most keys; dispatch them first
   const uint32_t qb = a.causal ? gridDim.x - 1u - blockIdx.x : blockIdx.x;
   const uint32_t q0 = qb * kQueriesPerGroup;
   const uint32_t qi = q0 + wave * 32u + col;
-  const bool qvalid = qi < a.Nq;
+  const bool qvalid = qi < rows;
+  // a wave without a valid query only helps load and decode the chunks
+  const bool wave_live = q0 + wave * 32u < rows;
 
   // P's scale table under S_P = fl(1/2688): pattern -> (encode r = fl(1/fl(s * S_P)), s);
   // a pattern whose r is not finite codes everything as 0 (r = 0).
@@ -250,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // This lane's B operand of S^T: query qi, elements 16 ks + 8 g .. +7.
   f16x8 qf[8];
   {
-    const uint64_t row = (uint64_t)bh * a.Nq + (qvalid ? qi : 0u);
+    const uint64_t row = (uint64_t)bh * rows + (qvalid ? qi : 0u);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       uint32_t w = 0u;
@@ -414,17 +424,19 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     for (uint32_t c0 = lo; c0 < hi; c0 += kChunk, buf ^= 1u) {
       const _Float16 *K = Ks[buf];
       const _Float16 *V = Vt[buf];
-      f32x16 sa0 = s_tile(sink_tag, K);
-      mask_tile(sa0, c0, hi);
-      f32x16 sa1 = s_tile(sink_tag, K + kKeyTile * kKsStride);
-      f16x8 pb0[2], pb1[2];
-      const float a0 = softmax_code(sa0, c2, pb0);
-      rescale(a0);
-      mask_tile(sa1, c0 + kKeyTile, hi);
-      pv_tile(sink_tag, V, 0u, pb0);
-      const float a1 = softmax_code(sa1, c2, pb1);
-      rescale(a1);
-      pv_tile(sink_tag, V, kKeyTile, pb1);
+      if (wave_live) {
+        f32x16 sa0 = s_tile(sink_tag, K);
+        mask_tile(sa0, c0, hi);
+        f32x16 sa1 = s_tile(sink_tag, K + kKeyTile * kKsStride);
+        f16x8 pb0[2], pb1[2];
+        const float a0 = softmax_code(sa0, c2, pb0);
+        rescale(a0);
+        mask_tile(sa1, c0 + kKeyTile, hi);
+        pv_tile(sink_tag, V, 0u, pb0);
+        const float a1 = softmax_code(sa1, c2, pb1);
+        rescale(a1);
+        pv_tile(sink_tag, V, kKeyTile, pb1);
+      }
       const uint32_t c1 = c0 + kChunk;
       if (c1 < hi) {
         if (SINK) {
@@ -438,7 +450,22 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     }
   };
 
-  if (CACHE) {
+  if (SPLIT) {
+    // one unit; units past the keys present run nothing and write an empty state
+    const uint32_t mid_hi = max(Nk > a.nl ? Nk - a.nl : 0u, a.nf);
+    const uint32_t z = blockIdx.z;
+    if (z < 2u) {
+      if (z == 0u)
+        run_segment(std::true_type{}, 0u, min(a.nf, Nk), true);
+      else
+        run_segment(std::true_type{}, max(mid_hi, a.nf), Nk, false);
+    } else {
+      const uint64_t lo = (uint64_t)a.nf + (uint64_t)(z - 2u) * a.split;
+      if (lo < mid_hi)
+        run_segment(std::false_type{}, (uint32_t)lo,
+                    (uint32_t)min<uint64_t>(lo + a.split, mid_hi), false);
+    }
+  } else if (CACHE) {
     // head sinks, coded middle, tail ring: tiles never straddle two segments
     const uint32_t mid_hi = max(Nk > a.nl ? Nk - a.nl : 0u, a.nf);
     run_segment(std::true_type{}, 0u, min(a.nf, Nk), true);
@@ -450,8 +477,23 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
   l = l + __shfl_xor(l, 32);
   if (!qvalid) return;
+  const uint64_t row = (uint64_t)bh * rows + qi;
+  if (SPLIT) {
+    // the unit's state: accumulator in absolute units, base-2 max, sum
+    const uint64_t urow = (uint64_t)blockIdx.z * ((uint64_t)gridDim.y * rows) + row;
+    float *dst = a.part + urow * kAttnD;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint32_t d0 = 32u * t + 8u * q4 + 4u * g;
+        *(float4 *)(dst + d0) = make_float4(o[t][4 * q4] * unit, o[t][4 * q4 + 1] * unit,
+                                            o[t][4 * q4 + 2] * unit, o[t][4 * q4 + 3] * unit);
+      }
+    if (g == 0u) a.ml[urow] = make_float2(m, l);
+    return;
+  }
   const float f = l > 0.0f ? (SP * unit) / l : 0.0f;
-  const uint64_t row = (uint64_t)bh * a.Nq + qi;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -471,19 +513,79 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   }
 }
 
-hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s) {
-  const dim3 grid((a.Nq + kQueriesPerGroup - 1) / kQueriesPerGroup, a.B * a.Hq);
-  if (a.cache) {
-    if (out_bf16)
-      hipLaunchKernelGGL((attention_kernel<true, true>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((attention_kernel<false, true>), grid, dim3(256), 0, s, a);
-  } else {
-    if (out_bf16)
-      hipLaunchKernelGGL((attention_kernel<true, false>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((attention_kernel<false, false>), grid, dim3(256), 0, s, a);
+// The units' states of one output row merged: with M the largest base-2 max,
+// w_u = 2^(m_u - M), O = S_P sum_u w_u acc_u / sum_u w_u l_u (0 with no key).
+// 32 lanes per row, four outputs each; a unit with m_u = -inf saw no key.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs a, uint32_t units,
+                                                              uint32_t nrows) {
+  const uint32_t row = blockIdx.x * 8u + (threadIdx.x >> 5);
+  const uint32_t d0 = 4u * (threadIdx.x & 31u);
+  if (row >= nrows) return;
+  float M = -INFINITY;
+  for (uint32_t u = 0; u < units; ++u) M = fmaxf(M, a.ml[(uint64_t)u * nrows + row].x);
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float L = 0.0f;
+  if (M != -INFINITY) {
+    for (uint32_t u = 0; u < units; ++u) {
+      const float2 st = a.ml[(uint64_t)u * nrows + row];
+      if (st.x == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(st.x - M);
+      const float4 p = *(const float4 *)(a.part + ((uint64_t)u * nrows + row) * kAttnD + d0);
+      acc.x += w * p.x;
+      acc.y += w * p.y;
+      acc.z += w * p.z;
+      acc.w += w * p.w;
+      L += w * st.y;
+    }
   }
+  const float f = L > 0.0f ? (1.0f / 2688.0f) / L : 0.0f;
+  const float y0 = acc.x * f, y1 = acc.y * f, y2 = acc.z * f, y3 = acc.w * f;
+  if (OUT_BF16) {
+    const bf16x2 lo = __builtin_convertvector((f32x2{y0, y1}), bf16x2);
+    const bf16x2 hi = __builtin_convertvector((f32x2{y2, y3}), bf16x2);
+    *(uint2 *)((uint16_t *)a.o + (uint64_t)row * kAttnD + d0) =
+        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+  } else {
+    *(float4 *)((float *)a.o + (uint64_t)row * kAttnD + d0) = make_float4(y0, y1, y2, y3);
+  }
+}
+
+hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s) {
+  if (a.cache) {
+    // rows of one KV head's query heads per grid row
+    const uint32_t rows = a.Nq * (a.Hq / a.Hkv);
+    const uint32_t cap_mid = a.nk_dev ? a.cap : (a.Nk > a.nf + a.nl ? a.Nk - a.nf - a.nl : 0u);
+    const uint32_t units = a.split ? 2u + (cap_mid + a.split - 1u) / a.split : 1u;
+    const dim3 grid((rows + kQueriesPerGroup - 1) / kQueriesPerGroup, a.B * a.Hkv, units);
+    if (a.split) {
+      hipLaunchKernelGGL((attention_kernel<false, true, true>), grid, dim3(256), 0, s, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_attention_merge(a, units, out_bf16, s);
+    }
+    if (out_bf16)
+      hipLaunchKernelGGL((attention_kernel<true, true, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attention_kernel<false, true, false>), grid, dim3(256), 0, s, a);
+  } else {
+    const dim3 grid((a.Nq + kQueriesPerGroup - 1) / kQueriesPerGroup, a.B * a.Hq);
+    if (out_bf16)
+      hipLaunchKernelGGL((attention_kernel<true, false, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attention_kernel<false, false, false>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_merge(const AttnArgs &a, uint32_t units, bool out_bf16,
+                                  hipStream_t s) {
+  const uint32_t nrows = a.B * a.Hq * a.Nq;
+  const dim3 grid((nrows + 7u) / 8u);
+  if (out_bf16)
+    hipLaunchKernelGGL((attention_merge_kernel<true>), grid, dim3(256), 0, s, a, units, nrows);
+  else
+    hipLaunchKernelGGL((attention_merge_kernel<false>), grid, dim3(256), 0, s, a, units, nrows);
   return hipGetLastError();
 }
 

@@ -168,7 +168,17 @@ struct AttnArgs {
   const uint16_t *kh, *kt, *vh, *vt;
   uint32_t nf, nl, cap;
   const int64_t *nk_dev;  // cache mode: device-resident token count (replaces Nk), or null
+  // cache mode with split keys (split > 0 tokens per middle piece): unit z of the grid
+  // (0 head, 1 tail, 2 + k middle piece k) writes its softmax state to part
+  // [units][rows][128] (accumulator times the unit's value factor) and ml [units][rows]
+  // (running max in base 2, sum); attention_merge combines them into o
+  uint32_t split;
+  float *part;
+  float2 *ml;
 };
+
+hipError_t launch_attention_merge(const AttnArgs &a, uint32_t units, bool out_bf16,
+                                  hipStream_t s);
 
 hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s);
 

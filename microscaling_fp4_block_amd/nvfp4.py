@@ -57,6 +57,12 @@ SIGNATURES = {
     "nvfp4_attention_kv_cache_dev": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _i32, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                                       _i64, _vp, _i32, _vp], _i32),
+    "nvfp4_attention_kv_cache_split": ([_vp] * 13 + [_i32, _i64, _i64, _i64, _i64, _i64, _i64,
+                                        _i64, _i64, _i64, _i64, _vp, _sz, _vp, _i32, _vp], _i32),
+    "nvfp4_attention_kv_cache_split_dev": ([_vp] * 13 + [_i32, _i64, _i64, _i64, _i64, _vp, _i64,
+                                            _i64, _i64, _i64, _i64, _vp, _sz, _vp, _i32, _vp],
+                                           _i32),
+    "nvfp4_attention_split_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64], _sz),
     "mxfp4_quantize": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "mxfp4_dequantize": ([_vp, _vp, _i64, _i64, _i32, _vp, _i32, _vp], _i32),
 }
@@ -478,12 +484,23 @@ def attention(q, k, v, causal: bool = False, out_dtype=torch.float32):
     return y
 
 
+def attention_split_workspace_bytes(B: int, Hq: int, Nq: int, cap: int, split: int) -> int:
+    """Workspace bytes of attention_kv_cache(..., split=split) for a cache of `cap`
+    middle rows (0 if the split calls would reject these sizes)."""
+    return int(load().nvfp4_attention_split_workspace_bytes(B, Hq, Nq, cap, split))
+
+
 def attention_kv_cache(q, k_cache: dict, k_gscale: torch.Tensor, v_cache: dict,
-                       v_gscale: torch.Tensor, out_dtype=torch.float32, device_length: bool = False):
+                       v_gscale: torch.Tensor, out_dtype=torch.float32, device_length: bool = False,
+                       split: int = 0, workspace: torch.Tensor | None = None):
     """Attention of q (codes, scales, global_scale of [B, Hq, Nq, 128]) over K and V
     sink caches made by kv_cache_alloc and filled by kv_append (bf16). Returns O.
     With device_length, the token count is k_cache["length_dev"], read on the device
-    (for caches filled by kv_append_dev; capturable in a HIP graph)."""
+    (for caches filled by kv_append_dev; capturable in a HIP graph). split > 0 (a
+    multiple of 32): the head, the tail and each piece of `split` middle tokens run
+    on their own workgroups and are merged (for decode steps with few queries);
+    workspace: a device tensor of attention_split_workspace_bytes bytes, else one
+    is allocated."""
     L = load()
     qc, qs, qg = q
     dev = _dev(qc)
@@ -507,23 +524,23 @@ def attention_kv_cache(q, k_cache: dict, k_gscale: torch.Tensor, v_cache: dict,
         _expect(c["codes"], f"{which} cache codes", (B, Hkv, cap, D2), torch.uint8, dev)
         _expect(c["scales"], f"{which} cache scales", (B, Hkv, cap, D2 // 8), torch.uint8, dev)
     y = torch.empty(B, Hq, Nq, D2 * 2, dtype=out_dtype, device=dev)
-    if device_length:
-        length = _expect(k_cache["length_dev"], "cache length_dev", (1,), torch.int64, dev)
-        st = L.nvfp4_attention_kv_cache_dev(
-            qc.data_ptr(), qs.data_ptr(), qg.data_ptr(), k_cache["head"].data_ptr(),
+    ptrs = (qc.data_ptr(), qs.data_ptr(), qg.data_ptr(), k_cache["head"].data_ptr(),
             k_cache["tail"].data_ptr(), k_cache["codes"].data_ptr(), k_cache["scales"].data_ptr(),
             k_gscale.data_ptr(), v_cache["head"].data_ptr(), v_cache["tail"].data_ptr(),
-            v_cache["codes"].data_ptr(), v_cache["scales"].data_ptr(), v_gscale.data_ptr(), BF16,
-            B, Hq, Hkv, Nq, length.data_ptr(), D2 * 2, k_cache["n_first"], k_cache["n_last"],
-            cap, y.data_ptr(), _dtype(y), _stream(dev))
-        _check("nvfp4_attention_kv_cache_dev", st)
-        return y
-    st = L.nvfp4_attention_kv_cache(
-        qc.data_ptr(), qs.data_ptr(), qg.data_ptr(), k_cache["head"].data_ptr(),
-        k_cache["tail"].data_ptr(), k_cache["codes"].data_ptr(), k_cache["scales"].data_ptr(),
-        k_gscale.data_ptr(), v_cache["head"].data_ptr(), v_cache["tail"].data_ptr(),
-        v_cache["codes"].data_ptr(), v_cache["scales"].data_ptr(), v_gscale.data_ptr(), BF16, B,
-        Hq, Hkv, Nq, k_cache["length"], D2 * 2, k_cache["n_first"], k_cache["n_last"], cap,
-        y.data_ptr(), _dtype(y), _stream(dev))
-    _check("nvfp4_attention_kv_cache", st)
+            v_cache["codes"].data_ptr(), v_cache["scales"].data_ptr(), v_gscale.data_ptr())
+    if device_length:
+        length = _expect(k_cache["length_dev"], "cache length_dev", (1,), torch.int64, dev)
+        tokens, fn = length.data_ptr(), "nvfp4_attention_kv_cache_dev"
+    else:
+        tokens, fn = k_cache["length"], "nvfp4_attention_kv_cache"
+    if split:
+        ws, nbytes = _workspace(workspace, attention_split_workspace_bytes(B, Hq, Nq, cap, split),
+                                dev)
+        fn = fn.replace("kv_cache", "kv_cache_split")
+        st = getattr(L, fn)(*ptrs, BF16, B, Hq, Hkv, Nq, tokens, D, nf, nl, cap, split,
+                            ws.data_ptr(), nbytes, y.data_ptr(), _dtype(y), _stream(dev))
+    else:
+        st = getattr(L, fn)(*ptrs, BF16, B, Hq, Hkv, Nq, tokens, D, nf, nl, cap, y.data_ptr(),
+                            _dtype(y), _stream(dev))
+    _check(fn, st)
     return y

@@ -205,3 +205,27 @@ def test_device_length_argument_checks(lib):
     assert c(*([P] * 13), 1, 1, 2, 1, 8, None, 128, 16, 16, 300, P, 0, None) == 1
     assert c(*([P] * 13), 1, 1, 2, 1, 8, P + 4, 128, 16, 16, 300, P, 0, None) == 3
     assert c(*([P] * 13), 1, 1, 2, 1, 0, P, 128, 16, 16, 300, P, 0, None) == 0
+
+
+def test_split_attention_argument_checks(lib):
+    w = lib.nvfp4_attention_split_workspace_bytes
+    # (2 + ceil(cap / split)) units x B * Hq * Nq rows x 130 FP32 values
+    assert w(1, 32, 1, 32768, 512) == (2 + 64) * 32 * 130 * 4
+    assert w(2, 8, 3, 1000, 96) == (2 + 11) * 48 * 130 * 4
+    assert w(1, 32, 1, 32768, 48) == 0          # split not a multiple of 32
+    assert w(1, 32, 1, 32768, 0) == 0
+    assert w(1, 32, 1, 1 << 30, 32) == 0        # more than 65535 units
+    assert w(1, 1 << 40, 1, 100, 32) == 0
+    need = w(1, 2, 8, 300, 64)
+    for f, tokens in ((lib.nvfp4_attention_kv_cache_split, 300),
+                      (lib.nvfp4_attention_kv_cache_split_dev, P)):
+        args = lambda split, ws, nbytes, Nq=8: [*([P] * 13), 1, 1, 2, 1, Nq, tokens, 128, 16, 16,
+                                                300, split, ws, nbytes, P, 0, None]
+        assert f(*args(48, P, need)) == 1        # split must be a multiple of 32
+        assert f(*args(0, P, need)) == 1         # and positive
+        assert f(*args(64, None, need)) == 4     # workspace missing
+        assert f(*args(64, P, need - 1)) == 4    # workspace too small
+        assert f(*args(64, P + 4, need)) == 3    # workspace not 16-byte aligned
+        assert f(*args(32, P, 1 << 40, Nq=0)) == 0   # no queries: nothing to do
+    d = lib.nvfp4_attention_kv_cache_split_dev
+    assert d(*([P] * 13), 1, 1, 2, 1, 8, None, 128, 16, 16, 300, 64, P, need, P, 0, None) == 1

@@ -160,28 +160,25 @@ def upload_cache(c, T, nf, nl):
         torch.tensor([c["gscale"]], dtype=torch.float32, device="cuda:0")
 
 
-@pytest.mark.parametrize("Hq,Hkv,Nq,T,nf,nl", [(2, 1, 77, 1000, 128, 128), (4, 2, 40, 300, 64, 0),
-                                                (1, 1, 33, 90, 64, 64), (1, 1, 20, 50, 64, 16),
-                                                (2, 2, 64, 200, 0, 0), (1, 1, 5, 520, 32, 96)])
-def test_kv_cache_attention(gpu, orc, Hq, Hkv, Nq, T, nf, nl):
+def cache_case(orc, Hq, Hkv, Nq, T, nf, nl, seed):
+    """Q coded by the oracle and K, V sink caches built by the oracle (cap = middle + 8)."""
     from test_oracle_attention import cache_of
 
-    rng = np.random.default_rng(T + 7 * nf + nl)
+    rng = np.random.default_rng(seed)
     qx = workloads.to_bf16_bits(rng.standard_normal((1, Hq, Nq, 128)).astype(np.float32))
     kx = workloads.workload(3, (1, Hkv, T, 128))
     vx = workloads.to_bf16_bits(rng.standard_normal((1, Hkv, T, 128)).astype(np.float32))
     q = coded(orc, qx)
     cap = max(T - nf - nl, 0) + 8
-    k, v = cache_of(orc, kx, nf, nl, T, cap), cache_of(orc, vx, nf, nl, T, cap)
-    print(f"[case] kv-cache attention Hq={Hq} Hkv={Hkv} Nq={Nq} T={T} nf={nf} nl={nl}", flush=True)
-    kc, kg = upload_cache(k, T, nf, nl)
-    vc, vg = upload_cache(v, T, nf, nl)
-    O = gpu.attention_kv_cache(upload(q), kc, kg, vc, vg)
-    torch.cuda.synchronize()
-    got = to_host(O).astype(np.float64)
-    ref, mag, bound = orc.attention_kv_cache(q, k, v, T, nf, nl)
+    return q, cache_of(orc, kx, nf, nl, T, cap), cache_of(orc, vx, nf, nl, T, cap)
+
+
+def cache_tol(q, k, T, nf, nl, ref, mag, bound, units=1):
+    """The bound of the module docstring over the cache's T keys; with split keys,
+    plus the merge: units weights 2^(m_u - M) in binary32 (a few u each) and the
+    FP32 sums over the units, on the numerator (mag) and on l (|O|)."""
+    Hq, Hkv = q[0].shape[1], k["codes"].shape[1]
     tiles = -(-T // 32) + 3
-    # the relative error binary32 scores and exp can put on a p (the oracle's formula)
     Qd = R.nvfp4_decode(q[0], q[1]) * float(q[2])
     Kd = R.cache_values(k, T, nf, nl)
     delta = 0.0
@@ -191,7 +188,79 @@ def test_kv_cache_attention(gpu, orc, Hq, Hkv, Nq, T, nf, nl):
         S = np.einsum("bid,bjd->bij", Qd[:, h], Kh) / np.sqrt(128.0)
         delta = max(delta, float(A.max(initial=0.0)) * 130 * U +
                     2 * float(np.abs(S).max(initial=0.0)) * 2.0 ** -21 + 2.0 ** -20)
-    tol = mag * (T + 8 * tiles + 64) * U + np.abs(ref) * (delta + (T + 64) * U) + bound
+    merge = (units + 16) * U if units > 1 else 0.0
+    return (mag * ((T + 8 * tiles + 64) * U + merge) +
+            np.abs(ref) * (delta + (T + 64) * U + merge) + bound)
+
+
+@pytest.mark.parametrize("Hq,Hkv,Nq,T,nf,nl", [(2, 1, 77, 1000, 128, 128), (4, 2, 40, 300, 64, 0),
+                                                (1, 1, 33, 90, 64, 64), (1, 1, 20, 50, 64, 16),
+                                                (2, 2, 64, 200, 0, 0), (1, 1, 5, 520, 32, 96),
+                                                (8, 1, 17, 300, 16, 16)])
+def test_kv_cache_attention(gpu, orc, Hq, Hkv, Nq, T, nf, nl):
+    q, k, v = cache_case(orc, Hq, Hkv, Nq, T, nf, nl, T + 7 * nf + nl)
+    print(f"[case] kv-cache attention Hq={Hq} Hkv={Hkv} Nq={Nq} T={T} nf={nf} nl={nl}", flush=True)
+    kc, kg = upload_cache(k, T, nf, nl)
+    vc, vg = upload_cache(v, T, nf, nl)
+    O = gpu.attention_kv_cache(upload(q), kc, kg, vc, vg)
+    torch.cuda.synchronize()
+    got = to_host(O).astype(np.float64)
+    ref, mag, bound = orc.attention_kv_cache(q, k, v, T, nf, nl)
+    tol = cache_tol(q, k, T, nf, nl, ref, mag, bound)
     err = np.abs(got - ref)
     print(f"[attention] kv cache: max err/tol {float(np.max(err / np.maximum(tol, 1e-300))):.3f}")
+    assert np.all(err <= tol)
+
+
+@pytest.mark.parametrize("Hq,Hkv,Nq,T,nf,nl,split", [
+    (32, 8, 1, 3000, 128, 128, 256),   # decode, grouped heads, a short last piece
+    (4, 2, 40, 300, 64, 0, 64),
+    (1, 1, 5, 520, 32, 96, 96),        # pieces of one and a half chunks
+    (2, 1, 3, 50, 64, 16, 32),         # fewer tokens than the head: empty middle and tail
+    (2, 2, 1, 200, 0, 0, 32),          # no sinks: empty head and tail units
+    (8, 1, 16, 700, 16, 16, 128),      # 8 heads x 16 queries: one full workgroup
+    (8, 1, 17, 700, 16, 16, 128),      # 136 rows: a second workgroup across two heads
+])
+def test_kv_cache_attention_split(gpu, orc, Hq, Hkv, Nq, T, nf, nl, split):
+    q, k, v = cache_case(orc, Hq, Hkv, Nq, T, nf, nl, T + split + Nq)
+    print(f"[case] split kv-cache attention Hq={Hq} Hkv={Hkv} Nq={Nq} T={T} nf={nf} nl={nl} "
+          f"split={split}", flush=True)
+    kc, kg = upload_cache(k, T, nf, nl)
+    vc, vg = upload_cache(v, T, nf, nl)
+    cap = kc["codes"].shape[2]
+    units = 2 + -(-cap // split)
+    ws = torch.full((gpu.attention_split_workspace_bytes(1, Hq, Nq, cap, split),), 0xFF,
+                    dtype=torch.uint8, device="cuda:0")   # NaN patterns: every read slot is written
+    for dt in (torch.float32, torch.bfloat16):
+        O = gpu.attention_kv_cache(upload(q), kc, kg, vc, vg, out_dtype=dt, split=split,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        got = to_host(O.float()).astype(np.float64)
+        ref, mag, bound = orc.attention_kv_cache(q, k, v, T, nf, nl, split=split)
+        tol = cache_tol(q, k, T, nf, nl, ref, mag, bound, units)
+        if dt == torch.bfloat16:
+            tol = tol + np.abs(ref) * 2.0 ** -8
+        err = np.abs(got - ref)
+        print(f"[attention] split kv cache {dt}: max err/tol "
+              f"{float(np.max(err / np.maximum(tol, 1e-300))):.3f}")
+        assert np.all(err <= tol)
+
+
+def test_kv_cache_attention_split_full_size_decode(gpu, orc):
+    """One decode query per head, Hq = 32 over Hkv = 8, a cache of 128 + 32768 + 128
+    tokens, split into pieces of 512: every row against the oracle."""
+    Hq, Hkv, Nq, nf, nl, split = 32, 8, 1, 128, 128, 512
+    T = nf + 32768 + nl
+    q, k, v = cache_case(orc, Hq, Hkv, Nq, T, nf, nl, 2024)
+    print("[case] split kv-cache attention, full-size decode", flush=True)
+    kc, kg = upload_cache(k, T, nf, nl)
+    vc, vg = upload_cache(v, T, nf, nl)
+    cap = kc["codes"].shape[2]
+    O = gpu.attention_kv_cache(upload(q), kc, kg, vc, vg, split=split)
+    torch.cuda.synchronize()
+    got = to_host(O).astype(np.float64)
+    ref, mag, bound = orc.attention_kv_cache(q, k, v, T, nf, nl, split=split)
+    tol = cache_tol(q, k, T, nf, nl, ref, mag, bound, 2 + -(-cap // split))
+    err = np.abs(got - ref)
+    print(f"[attention] full-size decode: max err/tol {float(np.max(err / tol)):.3f}")
     assert np.all(err <= tol)

@@ -119,10 +119,14 @@ def test_device_length_overflow_is_a_noop(gpu):
         assert torch.equal(c[k], v), k
 
 
-def test_graph_replayed_decode_step(gpu):
+@pytest.mark.parametrize("split", [0, 64])
+def test_graph_replayed_decode_step(gpu, split):
     """One decode step (append a K and a V token at the device length, attention of one
     query over the caches) captured once and replayed token after token; every replay is
-    checked against the host-length calls made eagerly on a second pair of caches."""
+    checked against the host-length calls made eagerly on a second pair of caches. With
+    split keys the captured grid covers every unit of a full cache and the units past
+    the tokens present add nothing, so the result equals the host-length call's bit for
+    bit."""
     B, H, D, nf, nl = 1, 2, 128, 32, 32
     n_pre, n_dec = 100, 12
     rng = np.random.default_rng(5)
@@ -141,11 +145,15 @@ def test_graph_replayed_decode_step(gpu):
         gpu.kv_append(c, x[:, :, :n_pre].contiguous(), gs)
     knew = torch.empty(B, H, 1, D, dtype=torch.bfloat16, device="cuda")
     vnew = torch.empty_like(knew)
+    nws = gpu.attention_split_workspace_bytes(B, 2 * H, 1, 256, split) if split else 0
+    ws_dev = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ws_host = torch.empty(nws, dtype=torch.uint8, device="cuda")
 
     def step():
         gpu.kv_append_dev(kd, knew, kg)
         gpu.kv_append_dev(vd, vnew, vg)
-        return gpu.attention_kv_cache(q, kd, kg, vd, vg, device_length=True)
+        return gpu.attention_kv_cache(q, kd, kg, vd, vg, device_length=True, split=split,
+                                      workspace=ws_dev if split else None)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -163,7 +171,8 @@ def test_graph_replayed_decode_step(gpu):
         graph.replay()
         gpu.kv_append(kh, kall[:, :, t:t + 1].contiguous(), kg)
         gpu.kv_append(vh, vall[:, :, t:t + 1].contiguous(), vg)
-        ref = gpu.attention_kv_cache(q, kh, kg, vh, vg)
+        ref = gpu.attention_kv_cache(q, kh, kg, vh, vg, split=split,
+                                     workspace=ws_host if split else None)
         torch.cuda.synchronize()
         assert gpu.kv_length(kd) == gpu.kv_length(vd) == t + 1
         assert torch.equal(out, ref), f"replay {i}"
