@@ -727,6 +727,7 @@ nvfp4_status attention_kv_cache_impl(
   if (split > 0) {
     const int64_t part = split_units(cap, split) * B * Hq * Nq * 128;
     a.split = (uint32_t)split;
+    a.ustride = (uint32_t)split_units(cap, split);
     a.part = (float *)workspace;
     a.ml = (float2 *)((float *)workspace + part);
   }

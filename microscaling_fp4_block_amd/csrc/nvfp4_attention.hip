@@ -49,6 +49,64 @@ constexpr uint32_t kVtStride = kChunk + 4;     // fp16 per V^T row in LDS (34 dw
 
 __device__ __forceinline__ float scale_value(uint32_t p) { return p >= 127u ? NAN : e4m3_value(p); }
 
+// P's scale tables under S_P = fl(1/2688), evaluated by the compiler in IEEE
+// binary32 (round to nearest even: the rounding of the device's own float
+// multiply and correctly rounded divide), so a workgroup copies them instead
+// of deriving them. For pattern k: s[k] its value, r[k] = fl(1/fl(s * S_P))
+// (0 where that is not finite: everything codes as 0), and thr[k] the least
+// binary32 a with E4M3(fl(fl(a / 6) / S_P)) >= k. That pattern is
+// non-decreasing in a, so thr is found by bisection over the bit patterns of
+// a in [0, 1] (p <= 1 puts every block amax there); thr[0] = 0, thr[127] = inf.
+struct PTables {
+  float s[128], r[128], thr[128];
+};
+
+constexpr float ce_e4m3_value(uint32_t p) {
+  const uint32_t e = p >> 3, m = p & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+}
+
+// e4m3_rne_sat for the compiler: the same steps, with the subnormal rounding
+// (t * 2^9 < 8, exact) done by hand.
+constexpr uint32_t ce_e4m3_rne_sat(float t) {
+  if (t >= 448.0f) return 126u;
+  if (t < 0x1p-6f) {
+    const float x = t * 512.0f;
+    const uint32_t i = (uint32_t)x;
+    const float f = x - (float)i;
+    return f > 0.5f || (f == 0.5f && (i & 1u)) ? i + 1u : i;
+  }
+  const uint32_t b = __builtin_bit_cast(uint32_t, t);
+  return ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u;
+}
+
+constexpr PTables make_ptables() {
+  PTables t{};
+  const float SP = 1.0f / 2688.0f;
+  for (uint32_t k = 0; k < 128; ++k) {
+    t.s[k] = k < 127u ? ce_e4m3_value(k) : 0.0f;
+    t.r[k] = t.s[k] > 0.0f ? 1.0f / (t.s[k] * SP) : 0.0f;
+    if (k == 0u) {
+      t.thr[k] = 0.0f;
+    } else if (k == 127u) {
+      t.thr[k] = __builtin_inff();
+    } else {
+      uint32_t lo = 0u, hi = 0x3F800000u;
+      while (lo < hi) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        if (ce_e4m3_rne_sat((__builtin_bit_cast(float, mid) / 6.0f) / SP) >= k)
+          hi = mid;
+        else
+          lo = mid + 1u;
+      }
+      t.thr[k] = __builtin_bit_cast(float, lo);
+    }
+  }
+  return t;
+}
+
+__constant__ PTables kPTables = make_ptables();
+
 // Two codes of byte sel of w as fp16 (the byte selector must be a constant).
 __device__ __forceinline__ f16x2 fp4_pair_f16(uint32_t w, int sel) {
   switch (sel & 3) {
@@ -201,37 +259,14 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // a wave without a valid query only helps load and decode the chunks
   const bool wave_live = q0 + wave * 32u < rows;
 
-  // P's scale table under S_P = fl(1/2688): pattern -> (encode r = fl(1/fl(s * S_P)), s);
-  // a pattern whose r is not finite codes everything as 0 (r = 0).
+  // P's tables (see PTables); in the loop a one-multiply estimate
+  // E4M3(fl(a * 448)) of the block pattern is never more than one pattern off
+  // (checked over every binary32 in [0, 1]) and one comparison each way against
+  // the thresholds corrects it.
   const float SP = 1.0f / 2688.0f;
-  if (tid < 127u) {
-    const float s = e4m3_value(tid);
-    float r = 1.0f / (s * SP);
-    if (!(r < INFINITY)) r = 0.0f;
-    ptbl[tid] = f32x2{r, s};
-  }
-  // The block pattern E4M3(fl(fl(a / 6) / S_P)) is non-decreasing in a, so it is
-  // the number of thresholds pthr[k] <= a, pthr[k] = the least binary32 a whose
-  // pattern is at least k (found by bisection over the bit patterns of a in [0, 1];
-  // p <= 1 puts every block amax there). In the loop a one-multiply estimate
-  // E4M3(fl(a * 448)) is never more than one pattern off (checked over every
-  // binary32 in [0, 1]) and one comparison each way corrects it.
   if (tid < 128u) {
-    float thr = INFINITY;
-    if (tid == 0u) {
-      thr = 0.0f;
-    } else if (tid < 127u) {
-      uint32_t lo = 0u, hi = 0x3F800000u;
-      while (lo < hi) {
-        const uint32_t mid = lo + ((hi - lo) >> 1);
-        if (e4m3_rne_sat((__uint_as_float(mid) / 6.0f) / SP) >= tid)
-          hi = mid;
-        else
-          lo = mid + 1u;
-      }
-      thr = __uint_as_float(lo);
-    }
-    pthr[tid] = thr;
+    ptbl[tid] = f32x2{kPTables.r[tid], kPTables.s[tid]};
+    pthr[tid] = kPTables.thr[tid];
   }
 
   const float qg = *a.qg;
@@ -480,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const uint64_t row = (uint64_t)bh * rows + qi;
   if (SPLIT) {
     // the unit's state: accumulator in absolute units, base-2 max, sum
-    const uint64_t urow = (uint64_t)blockIdx.z * ((uint64_t)gridDim.y * rows) + row;
+    const uint64_t urow = row * a.ustride + blockIdx.z;
     float *dst = a.part + urow * kAttnD;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -515,23 +550,34 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
 // The units' states of one output row merged: with M the largest base-2 max,
 // w_u = 2^(m_u - M), O = S_P sum_u w_u acc_u / sum_u w_u l_u (0 with no key).
-// 32 lanes per row, four outputs each; a unit with m_u = -inf saw no key.
+// One workgroup per row: eight groups of 32 lanes take every eighth unit (four
+// outputs per lane) with their loads independent of one another, and the
+// groups' sums are added in a fixed order. A unit that saw no key holds
+// m_u = -inf, l_u = 0 and a zero accumulator, so its weight and terms are 0.
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs a, uint32_t units,
-                                                              uint32_t nrows) {
-  const uint32_t row = blockIdx.x * 8u + (threadIdx.x >> 5);
-  const uint32_t d0 = 4u * (threadIdx.x & 31u);
-  if (row >= nrows) return;
-  float M = -INFINITY;
-  for (uint32_t u = 0; u < units; ++u) M = fmaxf(M, a.ml[(uint64_t)u * nrows + row].x);
+__global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs a, uint32_t units) {
+  __shared__ float wmax[4];
+  __shared__ float4 sacc[8][32];
+  __shared__ float sl[8];
+  const uint32_t row = blockIdx.x, tid = threadIdx.x;
+  const float2 *ml = a.ml + (uint64_t)row * a.ustride;
+  const float *part = a.part + (uint64_t)row * a.ustride * kAttnD;
+  float mx = -INFINITY;
+  for (uint32_t u = tid; u < units; u += 256u) mx = fmaxf(mx, ml[u].x);
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
+  if ((tid & 63u) == 0u) wmax[tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const uint32_t grp = tid >> 5, d0 = 4u * (tid & 31u);
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float L = 0.0f;
   if (M != -INFINITY) {
-    for (uint32_t u = 0; u < units; ++u) {
-      const float2 st = a.ml[(uint64_t)u * nrows + row];
-      if (st.x == -INFINITY) continue;
+#pragma unroll 4
+    for (uint32_t u = grp; u < units; u += 8u) {
+      const float2 st = ml[u];
+      const float4 p = *(const float4 *)(part + (uint64_t)u * kAttnD + d0);
       const float w = __builtin_amdgcn_exp2f(st.x - M);
-      const float4 p = *(const float4 *)(a.part + ((uint64_t)u * nrows + row) * kAttnD + d0);
       acc.x += w * p.x;
       acc.y += w * p.y;
       acc.z += w * p.z;
@@ -539,8 +585,23 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs a, uint32
       L += w * st.y;
     }
   }
-  const float f = L > 0.0f ? (1.0f / 2688.0f) / L : 0.0f;
-  const float y0 = acc.x * f, y1 = acc.y * f, y2 = acc.z * f, y3 = acc.w * f;
+  sacc[grp][tid & 31u] = acc;
+  if ((tid & 31u) == 0u) sl[grp] = L;
+  __syncthreads();
+  if (tid >= 32u) return;
+  float4 t = sacc[0][tid];
+  float lt = sl[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) {
+    const float4 v = sacc[j][tid];
+    t.x += v.x;
+    t.y += v.y;
+    t.z += v.z;
+    t.w += v.w;
+    lt += sl[j];
+  }
+  const float f = lt > 0.0f ? (1.0f / 2688.0f) / lt : 0.0f;
+  const float y0 = t.x * f, y1 = t.y * f, y2 = t.z * f, y3 = t.w * f;
   if (OUT_BF16) {
     const bf16x2 lo = __builtin_convertvector((f32x2{y0, y1}), bf16x2);
     const bf16x2 hi = __builtin_convertvector((f32x2{y2, y3}), bf16x2);
@@ -580,12 +641,11 @@ hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s) {
 
 hipError_t launch_attention_merge(const AttnArgs &a, uint32_t units, bool out_bf16,
                                   hipStream_t s) {
-  const uint32_t nrows = a.B * a.Hq * a.Nq;
-  const dim3 grid((nrows + 7u) / 8u);
+  const dim3 grid(a.B * a.Hq * a.Nq);
   if (out_bf16)
-    hipLaunchKernelGGL((attention_merge_kernel<true>), grid, dim3(256), 0, s, a, units, nrows);
+    hipLaunchKernelGGL((attention_merge_kernel<true>), grid, dim3(256), 0, s, a, units);
   else
-    hipLaunchKernelGGL((attention_merge_kernel<false>), grid, dim3(256), 0, s, a, units, nrows);
+    hipLaunchKernelGGL((attention_merge_kernel<false>), grid, dim3(256), 0, s, a, units);
   return hipGetLastError();
 }
 

@@ -170,9 +170,9 @@ struct AttnArgs {
   const int64_t *nk_dev;  // cache mode: device-resident token count (replaces Nk), or null
   // cache mode with split keys (split > 0 tokens per middle piece): unit z of the grid
   // (0 head, 1 tail, 2 + k middle piece k) writes its softmax state to part
-  // [units][rows][128] (accumulator times the unit's value factor) and ml [units][rows]
-  // (running max in base 2, sum); attention_merge combines them into o
-  uint32_t split;
+  // [rows][ustride][128] (accumulator times the unit's value factor) and
+  // ml [rows][ustride] (running max in base 2, sum); attention_merge combines them
+  uint32_t split, ustride;
   float *part;
   float2 *ml;
 };
