@@ -363,36 +363,48 @@ def kv_append_table(torch, nv, workloads, iters: int = 200):
 
     # A decode step at the device-resident length, captured once and replayed: append
     # one K and one V token to 32K-token caches, then attention of one query per head
-    # (32 query heads over the 8 K/V heads) over the caches.
-    steps = 200
-    kc = nv.kv_cache_alloc(B, H, D, 32768 + steps + 8, nf, nl, torch.bfloat16, dev)
-    vc = nv.kv_cache_alloc(B, H, D, 32768 + steps + 8, nf, nl, torch.bfloat16, dev)
+    # (32 query heads over the 8 K/V heads) over the caches, unsplit or with the keys
+    # split into pieces of S tokens (each piece on its own workgroups, then merged).
+    steps = 100
+    variants = [("append", 0)] + [("append+attention", s) for s in (0, 256, 512, 1024)] + \
+        [("attention", s) for s in (0, 256, 384, 512, 768, 1024)]
+    cap = 32768 + steps * len(variants) + 8
+    kc = nv.kv_cache_alloc(B, H, D, cap, nf, nl, torch.bfloat16, dev)
+    vc = nv.kv_cache_alloc(B, H, D, cap, nf, nl, torch.bfloat16, dev)
     nv.kv_append_dev(kc, x, g)
     nv.kv_append_dev(vc, x, g)
     knew = x[:, :, :1].contiguous()
     vnew = x[:, :, 1:2].contiguous()
     q = nv.quantize(torch.from_numpy(workloads.workload(5, (1, 32, 1, 128)).view(np.int16))
                     .view(torch.bfloat16).to(dev))
+    ws = torch.empty(max(nv.attention_split_workspace_bytes(1, 32, 1, cap, s)
+                         for s in (256, 384)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     graphs = []
-    for parts in (("append",), ("append", "attention")):
+    for parts, split in variants:
         gph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.graph(gph, stream=side):
-            nv.kv_append_dev(kc, knew, g)
-            nv.kv_append_dev(vc, vnew, g)
+            if "append" in parts:
+                nv.kv_append_dev(kc, knew, g)
+                nv.kv_append_dev(vc, vnew, g)
             if "attention" in parts:
-                nv.attention_kv_cache(q, kc, g, vc, g, device_length=True)
-        graphs.append((parts, gph))
+                nv.attention_kv_cache(q, kc, g, vc, g, device_length=True, split=split,
+                                      workspace=ws if split else None)
+        graphs.append((parts, split, gph))
     torch.cuda.synchronize()
     print()
-    print("| captured decode step (graph replay, device-resident length) | us per step |")
+    print("| captured decode step (graph replay, device-resident length, ~32.9K tokens) "
+          "| us per step |")
     print("|---|---|")
-    for parts, gph in graphs:
-        ms = event_time_ms(torch, gph.replay, steps // 2, stream)
-        name = "append 1 K + 1 V token" + (
-            ", then attention of 32 query heads over the 32K caches" if len(parts) > 1 else "")
+    for parts, split, gph in graphs:
+        ms = event_time_ms(torch, gph.replay, steps, stream)
+        name = {"append": "append 1 K + 1 V token",
+                "append+attention": "append 1 K + 1 V token, then attention of 32 query heads",
+                "attention": "attention of 32 query heads alone"}[parts]
+        if "attention" in parts:
+            name += f", keys split into pieces of {split}" if split else ", keys unsplit"
         print(f"| {name} | {ms * 1e3:.1f} |", flush=True)
 
 

@@ -254,10 +254,14 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // causal: the last query blocks see the most keys; dispatch them first
   const uint32_t qb = a.causal ? gridDim.x - 1u - blockIdx.x : blockIdx.x;
   const uint32_t q0 = qb * kQueriesPerGroup;
-  const uint32_t qi = q0 + wave * 32u + col;
+  // with split keys the waves take the 32-row slices in an order rotated by the
+  // unit, so that when few rows are valid (decode) the live waves of the
+  // workgroups that share a compute unit tend to sit on different SIMDs
+  const uint32_t wslot = SPLIT ? (wave + blockIdx.z) & 3u : wave;
+  const uint32_t qi = q0 + wslot * 32u + col;
   const bool qvalid = qi < rows;
   // a wave without a valid query only helps load and decode the chunks
-  const bool wave_live = q0 + wave * 32u < rows;
+  const bool wave_live = q0 + wslot * 32u < rows;
 
   // P's tables (see PTables); in the loop a one-multiply estimate
   // E4M3(fl(a * 448)) of the block pattern is never more than one pattern off
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const int64_t lim = a.causal ? (int64_t)qi + (int64_t)Nk - (int64_t)a.Nq : (int64_t)Nk - 1;
   // the smallest lim of the wave (its first query), for the unmasked fast path
   const int64_t lim_wave =
-      a.causal ? (int64_t)(q0 + wave * 32u) + (int64_t)Nk - (int64_t)a.Nq : (int64_t)Nk - 1;
+      a.causal ? (int64_t)(q0 + wslot * 32u) + (int64_t)Nk - (int64_t)a.Nq : (int64_t)Nk - 1;
 
   const uint64_t coded_base = CACHE ? (uint64_t)kvh * a.cap : (uint64_t)kvh * Nk;
   const uint32_t coded_off = CACHE ? a.nf : 0u;
