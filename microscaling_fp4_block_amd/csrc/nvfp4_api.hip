@@ -403,6 +403,7 @@ nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64
   const uint32_t es = bf16 ? 2u : 4u;
 
   // 1. code the tokens that leave the recent window (before the ring is overwritten)
+  QuantArgs q{};
   if (BH > 0 && npos > 0) {
     RegionMap m{};
     m.bpr = (uint32_t)(D / 16);
@@ -421,13 +422,12 @@ nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64
     m.cap = (uint32_t)cap;
     m.div_nlast = make_fastdiv((uint32_t)(n_last > 0 ? n_last : 1));
     m.ring = tail;
-    QuantArgs q{kv_new, codes, scales, (float *)global_scale, nullptr, 0, m, f_lo, f_hi,
-                make_signs(signs)};
-    if (run_quantize(q, bf16, had, s) != hipSuccess) return NVFP4_EHIP;
+    q = QuantArgs{kv_new, codes, scales, (float *)global_scale, nullptr, 0, m, f_lo, f_hi,
+                  make_signs(signs)};
   }
   // 2. store the new tokens that stay in full precision
+  AdmitArgs c{};
   if (BH > 0 && t_new > 0) {
-    AdmitArgs c{};
     c.src = kv_new;
     c.head = head;
     c.tail = tail;
@@ -440,8 +440,14 @@ nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64
     c.div_cpr = make_fastdiv(c.chunks_per_row);
     c.div_tnew = make_fastdiv((uint32_t)t_new);
     c.div_nlast = make_fastdiv((uint32_t)(n_last > 0 ? n_last : 1));
-    if (launch_admit(c, bf16, s) != hipSuccess) return NVFP4_EHIP;
   }
+  if (q.map.nblocks == 0 && c.nchunks == 0) return NVFP4_OK;
+  if (!had && q.map.nblocks <= kSmallAppendBlocks && c.nchunks <= kSmallAppendChunks) {
+    q.gscale = (float *)global_scale;
+    return hip_status(launch_kv_append_small(q, c, nullptr, bf16, s));
+  }
+  if (q.map.nblocks > 0 && run_quantize(q, bf16, had, s) != hipSuccess) return NVFP4_EHIP;
+  if (c.nchunks > 0 && launch_admit(c, bf16, s) != hipSuccess) return NVFP4_EHIP;
   return NVFP4_OK;
 }
 
@@ -484,6 +490,12 @@ nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, i
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dt == NVFP4_BF16;
   const uint32_t es = bf16 ? 2u : 4u;
+  QuantArgs q{};
+  q.gscale = (float *)global_scale;
+  AdmitArgs c{};
+  c.len_dev = length;
+  c.t_new = (uint32_t)t_new;
+  c.total = (uint32_t)total;
   if (BH > 0) {
     // 1. code the tokens that leave the recent window: at most t_new rows per segment
     RegionMap m{};
@@ -503,11 +515,9 @@ nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, i
     m.ring = tail;
     m.len_dev = length;
     m.total = (uint32_t)total;
-    QuantArgs q{kv_new, codes, scales, (float *)global_scale, nullptr, 0, m, f_lo, f_hi,
-                make_signs(signs)};
-    if (run_quantize(q, bf16, had, s) != hipSuccess) return NVFP4_EHIP;
+    q = QuantArgs{kv_new, codes, scales, (float *)global_scale, nullptr, 0, m, f_lo, f_hi,
+                  make_signs(signs)};
     // 2. store the new tokens that stay in full precision
-    AdmitArgs c{};
     c.src = kv_new;
     c.head = head;
     c.tail = tail;
@@ -519,8 +529,12 @@ nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, i
     c.div_cpr = make_fastdiv(c.chunks_per_row);
     c.div_tnew = make_fastdiv((uint32_t)t_new);
     c.div_nlast = make_fastdiv((uint32_t)(n_last > 0 ? n_last : 1));
-    c.len_dev = length;
-    c.total = (uint32_t)total;
+  }
+  // small appends (a decode step's): all three steps in one workgroup
+  if (!had && q.map.nblocks <= kSmallAppendBlocks && c.nchunks <= kSmallAppendChunks)
+    return hip_status(launch_kv_append_small(q, c, length, bf16, s));
+  if (BH > 0) {
+    if (run_quantize(q, bf16, had, s) != hipSuccess) return NVFP4_EHIP;
     if (launch_admit(c, bf16, s) != hipSuccess) return NVFP4_EHIP;
   }
   // 3. advance the length (after both kernels read it)

@@ -191,6 +191,13 @@ hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s)
 hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_admit(const AdmitArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_advance_length(int64_t *len, uint32_t t_new, uint32_t total, hipStream_t s);
+// The coding, admit and (with len, the device-resident length, else null) length
+// advance of one append in a single workgroup: for appends of at most
+// kSmallAppendBlocks coded blocks and kSmallAppendChunks admitted 16-byte chunks,
+// without the Hadamard transform.
+constexpr uint32_t kSmallAppendBlocks = 256, kSmallAppendChunks = 1024;
+hipError_t launch_kv_append_small(const QuantArgs &q, const AdmitArgs &c, int64_t *len,
+                                  bool bf16, hipStream_t s);
 hipError_t launch_dequantize_kv(const DequantKvArgs &a, bool sink_bf16, bool out_bf16,
                                 hipStream_t s);
 

@@ -44,8 +44,9 @@ struct BlockIO {
   bool valid;
 };
 
+// t_dev: the value of *m.len_dev when the map has one (read once by the caller).
 __device__ __forceinline__ BlockIO block_io(const void *x, const RegionMap &m, uint32_t b,
-                                            uint32_t esize) {
+                                            uint32_t esize, uint32_t t_dev) {
   if (!m.append) return BlockIO{(const char *)x + block_offset(m, b) * esize, b, true};
   const uint32_t r = fastdiv(b, m.div_bpr);
   const uint32_t j = b - r * m.bpr;
@@ -53,7 +54,7 @@ __device__ __forceinline__ BlockIO block_io(const void *x, const RegionMap &m, u
   uint32_t t_old = m.t_old, lo = m.lo;
   bool valid = true;
   if (m.len_dev) {
-    t_old = (uint32_t)*m.len_dev;
+    t_old = t_dev;
     const uint32_t t2 = t_old + m.t_new;
     lo = max(m.n_first, t_old > m.n_last ? t_old - m.n_last : 0u);
     const uint32_t hi = max(m.n_first, t2 > m.n_last ? t2 - m.n_last : 0u);
@@ -73,6 +74,11 @@ __device__ __forceinline__ BlockIO block_io(const void *x, const RegionMap &m, u
   }
   const uint64_t dst = ((uint64_t)g * m.cap + (pos - m.n_first)) * m.bpr + j;
   return BlockIO{base + (row * m.cols + (uint64_t)j * 16u) * esize, dst, true};
+}
+
+// The device-resident token count of an append map (0 when there is none).
+__device__ __forceinline__ uint32_t map_length(const RegionMap &m) {
+  return m.len_dev ? (uint32_t)*m.len_dev : 0u;
 }
 
 // Wave64 max with DPP: xor-1 and xor-2 quad permutes, half-row and row
@@ -457,18 +463,15 @@ __device__ __forceinline__ void search_block_twins(const float (&x)[16], float s
   }
 }
 
+// Blocks first, first + stride, ... of the region with the exact search.
 // FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI] (twin-sharing search).
 template <bool BF16, int FLO, int FHI, bool FIXED>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  __shared__ f32x2 tbl[128];
-  const float sg = resolve_tensor_scale(a);
-  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
-  build_scale_table(tbl, sg);
-
-  const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
+__device__ __forceinline__ void quantize_blocks(const QuantArgs &a, const f32x2 *tbl, float sg,
+                                                bool sg_ok, uint32_t first, uint32_t stride,
+                                                uint32_t t_dev) {
+  for (uint32_t b = first; b < a.map.nblocks; b += stride) {
     float x[16];
-    const BlockIO io = block_io(a.x, a.map, b, BF16 ? 2u : 4u);
+    const BlockIO io = block_io(a.x, a.map, b, BF16 ? 2u : 4u, t_dev);
     if (!io.valid) continue;
     load_block_at<BF16>(io.src, x);
     uint32_t best_p, bc0, bc1;
@@ -479,6 +482,16 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
     *(uint2 *)(a.codes + io.dst * 8u) = make_uint2(bc0, bc1);
     a.scales[io.dst] = (uint8_t)best_p;
   }
+}
+
+template <bool BF16, int FLO, int FHI, bool FIXED>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  __shared__ f32x2 tbl[128];
+  const float sg = resolve_tensor_scale(a);
+  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+  build_scale_table(tbl, sg);
+  quantize_blocks<BF16, FLO, FHI, FIXED>(a, tbl, sg, sg_ok, blockIdx.x * kThreads + threadIdx.x,
+                                         gridDim.x * kThreads, map_length(a.map));
 }
 
 // Max scaling alone (offsets [0, 0]: one candidate, nothing to score) with two
@@ -495,9 +508,10 @@ __global__ __launch_bounds__(kThreads) void quantize_rule_kernel(QuantArgs a) {
 
   const uint32_t nunits = a.map.nblocks * 2u;
   const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t t_dev = map_length(a.map);
   for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < nunits; u += stride) {
     const uint32_t half = u & 1u;
-    const BlockIO io = block_io(a.x, a.map, u >> 1, BF16 ? 2u : 4u);
+    const BlockIO io = block_io(a.x, a.map, u >> 1, BF16 ? 2u : 4u, t_dev);
     if (!io.valid) continue;  // both lanes of the block skip together
     float x[8];
     uint32_t am = 0u;
@@ -691,8 +705,9 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
   const bool c6_ok = sg_ok && sg >= 0x1p-100f && sg <= 0x1p100f;
 
   const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t t_dev = map_length(a.map);
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < a.map.nblocks; b += stride) {
-    const BlockIO io = block_io(a.x, a.map, b, 2u);
+    const BlockIO io = block_io(a.x, a.map, b, 2u, t_dev);
     if (!io.valid) continue;
     const uint4 q0 = load_stream(io.src), q1 = load_stream(io.src + 16);
     const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
@@ -939,12 +954,13 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
   const uint32_t nvec = a.map.nblocks / 8u;
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
+  const uint32_t t_dev = map_length(a.map);
   for (uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile * 32u < nvec;
        tile += nwaves) {
     const uint32_t vec = tile * 32u + (lane & 31u);
     const bool valid = vec < nvec;
     uint4 b[8];
-    const BlockIO io = block_io(a.x, a.map, valid ? vec * 8u : 0u, 2u);
+    const BlockIO io = block_io(a.x, a.map, valid ? vec * 8u : 0u, 2u, t_dev);
     const bool live = valid && io.valid;  // the 8 blocks of a vector share one row
     hadamard_load<SIGNS>((const uint16_t *)io.src, 0, live, h.g, a.hs, b);
 #pragma unroll 1
@@ -1135,29 +1151,35 @@ __global__ __launch_bounds__(kThreads) void sink_copy_kernel(SinkArgs a, uint32_
 
 // New tokens of a KV append into the cache head or tail ring, 16 bytes a lane
 // (tokens bound for the middle are coded by the quantize kernel instead).
-__global__ __launch_bounds__(kThreads) void admit_kernel(AdmitArgs a, uint32_t row_bytes) {
-  const uint32_t stride = gridDim.x * kThreads;
-  if (a.len_dev) {  // device-resident length: skip an append that does not fit
-    a.t_old = (uint32_t)*a.len_dev;
-    if (a.t_old + a.t_new > a.total) return;
+// Destination of admit chunk c when the cache held t_old tokens before the
+// append, or null when its token goes to the coded middle; src is its source.
+__device__ __forceinline__ char *admit_dst(const AdmitArgs &a, uint32_t row_bytes,
+                                           uint32_t t_old, uint32_t c, const char *&src) {
+  const uint32_t tail_from = t_old + a.t_new - min(a.n_last, t_old + a.t_new);
+  const uint32_t row = fastdiv(c, a.div_cpr);  // g * t_new + k
+  const uint32_t k = c - row * a.chunks_per_row;
+  const uint32_t g = fastdiv(row, a.div_tnew);
+  const uint32_t pos = t_old + (row - g * a.t_new);
+  src = (const char *)a.src + (uint64_t)row * row_bytes + (uint64_t)k * 16u;
+  if (pos < a.n_first) return (char *)a.head + ((uint64_t)g * a.n_first + pos) * row_bytes + k * 16u;
+  if (pos >= tail_from) {
+    const uint32_t q = fastdiv(pos, a.div_nlast);
+    return (char *)a.tail + ((uint64_t)g * a.n_last + (pos - q * a.n_last)) * row_bytes + k * 16u;
   }
-  const uint32_t tail_from = a.t_old + a.t_new - min(a.n_last, a.t_old + a.t_new);
+  return nullptr;
+}
+
+__global__ __launch_bounds__(kThreads) void admit_kernel(AdmitArgs a, uint32_t row_bytes) {
+  uint32_t t_old = a.t_old;
+  if (a.len_dev) {  // device-resident length: skip an append that does not fit
+    t_old = (uint32_t)*a.len_dev;
+    if (t_old + a.t_new > a.total) return;
+  }
+  const uint32_t stride = gridDim.x * kThreads;
   for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < a.nchunks; c += stride) {
-    const uint32_t row = fastdiv(c, a.div_cpr);  // g * t_new + k
-    const uint32_t k = c - row * a.chunks_per_row;
-    const uint32_t g = fastdiv(row, a.div_tnew);
-    const uint32_t pos = a.t_old + (row - g * a.t_new);
-    char *dst;
-    if (pos < a.n_first) {
-      dst = (char *)a.head + ((uint64_t)g * a.n_first + pos) * row_bytes;
-    } else if (pos >= tail_from) {
-      const uint32_t q = fastdiv(pos, a.div_nlast);
-      dst = (char *)a.tail + ((uint64_t)g * a.n_last + (pos - q * a.n_last)) * row_bytes;
-    } else {
-      continue;
-    }
-    *(uint4 *)(dst + (uint64_t)k * 16u) =
-        *(const uint4 *)((const char *)a.src + (uint64_t)row * row_bytes + (uint64_t)k * 16u);
+    const char *src;
+    char *dst = admit_dst(a, row_bytes, t_old, c, src);
+    if (dst) *(uint4 *)dst = *(const uint4 *)src;
   }
 }
 
@@ -1167,6 +1189,52 @@ __global__ void advance_length_kernel(int64_t *len, uint32_t t_new, uint32_t tot
   if (threadIdx.x == 0) {
     const int64_t t = *len;
     if (t + (int64_t)t_new <= (int64_t)total) *len = t + (int64_t)t_new;
+  }
+}
+
+// A KV append small enough for one workgroup, in one launch (a decode step's
+// append would otherwise be two or three launches of a few lanes each). The
+// device-resident length (len, the same as c.len_dev and q.map.len_dev; null
+// for a host-held one) is read once, and the admit's sources, which do not
+// depend on it, are loaded at once; after the scale table's barrier every lane
+// has its copy of the length, so it is advanced there; the tokens that leave
+// the recent window are coded with the exact search; a barrier (the admit
+// overwrites ring slots the coding reads); the new full-precision tokens are
+// stored. The tensor scale is the caller's.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void kv_append_small_kernel(QuantArgs q, AdmitArgs c,
+                                                                   uint32_t row_bytes,
+                                                                   int64_t *len) {
+  __shared__ f32x2 tbl[128];
+  constexpr uint32_t kPer = kSmallAppendChunks / kThreads;
+  const uint32_t t_old = len ? (uint32_t)*len : c.t_old;
+  const bool fits = !len || (uint64_t)t_old + c.t_new <= c.total;
+  uint4 v[kPer];
+#pragma unroll
+  for (uint32_t i = 0; i < kPer; ++i) {
+    const uint32_t ch = threadIdx.x + i * kThreads;
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (ch < c.nchunks) {
+      const uint32_t row = fastdiv(ch, c.div_cpr);
+      v[i] = *(const uint4 *)((const char *)c.src + (uint64_t)row * row_bytes +
+                              (uint64_t)(ch - row * c.chunks_per_row) * 16u);
+    }
+  }
+  const float sg = *q.gscale;
+  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+  build_scale_table(tbl, sg);
+  if (len && fits && threadIdx.x == 0) *len = (int64_t)t_old + c.t_new;
+  quantize_blocks<BF16, 0, 0, false>(q, tbl, sg, sg_ok, threadIdx.x, kThreads, t_old);
+  __syncthreads();
+  if (!fits) return;
+#pragma unroll
+  for (uint32_t i = 0; i < kPer; ++i) {
+    const uint32_t ch = threadIdx.x + i * kThreads;
+    if (ch < c.nchunks) {
+      const char *src;
+      char *dst = admit_dst(c, row_bytes, t_old, ch, src);
+      if (dst) *(uint4 *)dst = v[i];
+    }
   }
 }
 
@@ -1562,6 +1630,17 @@ hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s) {
 
 hipError_t launch_advance_length(int64_t *len, uint32_t t_new, uint32_t total, hipStream_t s) {
   hipLaunchKernelGGL(advance_length_kernel, dim3(1), dim3(64), 0, s, len, t_new, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_small(const QuantArgs &q, const AdmitArgs &c, int64_t *len,
+                                  bool bf16, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL((kv_append_small_kernel<true>), dim3(1), dim3(kThreads), 0, s, q, c,
+                       c.chunks_per_row * 16u, len);
+  else
+    hipLaunchKernelGGL((kv_append_small_kernel<false>), dim3(1), dim3(kThreads), 0, s, q, c,
+                       c.chunks_per_row * 16u, len);
   return hipGetLastError();
 }
 
