@@ -366,8 +366,8 @@ def kv_append_table(torch, nv, workloads, iters: int = 200):
     # (32 query heads over the 8 K/V heads) over the caches, unsplit or with the keys
     # split into pieces of S tokens (each piece on its own workgroups, then merged).
     steps, warm = 100, 5
-    variants = [("append", 0)] + [("append+attention", s) for s in (0, 256, 512, 1024)] + \
-        [("attention", s) for s in (0, 256, 384, 512, 768, 1024)]
+    variants = [("append", 0)] + [("append+attention", s) for s in (0, 128, 256, 512)] + \
+        [("attention", s) for s in (0, 64, 128, 256, 512, 1024)]
     cap = 32768 + (steps + warm) * len(variants) + 8
     kc = nv.kv_cache_alloc(B, H, D, cap, nf, nl, torch.bfloat16, dev)
     vc = nv.kv_cache_alloc(B, H, D, cap, nf, nl, torch.bfloat16, dev)
@@ -378,7 +378,7 @@ def kv_append_table(torch, nv, workloads, iters: int = 200):
     q = nv.quantize(torch.from_numpy(workloads.workload(5, (1, 32, 1, 128)).view(np.int16))
                     .view(torch.bfloat16).to(dev))
     ws = torch.empty(max(nv.attention_split_workspace_bytes(1, 32, 1, cap, s)
-                         for s in (256, 384)), dtype=torch.uint8, device=dev)
+                         for s in (64, 128)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     graphs = []
     for parts, split in variants:
@@ -537,6 +537,26 @@ def attention_profile(torch, nv, workloads, launches: int = 5):
     torch.cuda.synchronize()
 
 
+def decode_profile(torch, nv, workloads, split: int = 256, launches: int = 5):
+    """Short run for rocprofv3: K and V sink caches of 128 + 32768 + 128 tokens
+    ([1, 8, *, 128], workload-3 recipe, ScaleSearch [-2, 6]), one query per head for 32
+    query heads, then `launches` split-key cache attention calls (pieces of `split`)."""
+    dev = torch.device("cuda:0")
+    B, H, D, nf, nl, T = 1, 8, 128, 128, 128, 32768 + 256
+    x = torch.from_numpy(workloads.workload(3, (B, H, T, D)).view(np.int16)) \
+        .view(torch.bfloat16).to(dev)
+    g = nv.global_scale(x[:, :, nf:T - nl].contiguous())
+    kc = nv.kv_cache_alloc(B, H, D, T, nf, nl, torch.bfloat16, dev)
+    vc = nv.kv_cache_alloc(B, H, D, T, nf, nl, torch.bfloat16, dev)
+    nv.kv_append(kc, x, g)
+    nv.kv_append(vc, x, g)
+    q = nv.quantize(torch.from_numpy(workloads.workload(5, (1, 32, 1, 128)).view(np.int16))
+                    .view(torch.bfloat16).to(dev))
+    for _ in range(launches):
+        nv.attention_kv_cache(q, kc, g, vc, g, split=split)
+    torch.cuda.synchronize()
+
+
 def attention_table(torch, nv, workloads, iters: int = 5):
     """Markdown table: attention on NVFP4 operands at 32K, Q [1, 32, 32768, 128] (workload 5
     recipe) against K [1, 8, 32768, 128] (workload 3 recipe) and V [1, 8, 32768, 128]
@@ -619,6 +639,9 @@ def main():
     ap.add_argument("--attention", action="store_true",
                     help="print a markdown table timing attention on NVFP4 operands at 32K "
                          "(no JSON line)")
+    ap.add_argument("--decode-profile", action="store_true",
+                    help="short run for rocprofv3: split-key cache attention, one query per "
+                         "head over 32K-token caches")
     ap.add_argument("--attention-profile", action="store_true",
                     help="short run for rocprofv3: five non-causal attention launches at 32K")
     ap.add_argument("--rocpd-summary", nargs="+", metavar="DB",
@@ -650,6 +673,9 @@ def main():
         return
     if args.attention:
         attention_table(torch, nv, workloads)
+        return
+    if args.decode_profile:
+        decode_profile(torch, nv, workloads)
         return
     if args.attention_profile:
         attention_profile(torch, nv, workloads)

@@ -227,14 +227,61 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f16x8 h) {
   return r;
 }
 
+// Online softmax of one 32-key tile held as an Sᵀ accumulator (sacc[v] = key
+// 8 (v >> 2) + 4 g + (v & 3) of the tile; this lane's query; base-2 scores
+// s = acc * c2, c2 > 0, so the max is taken on acc), then P to NVFP4 per 16
+// keys (keys 16 blk .. +15: 8 in this lane, 8 in its partner lane ^ 32), max
+// scaling under S_P = fl(1/2688), and back to exact fp16 values V[code] * s.
+// Branch-free, so matrix instructions issued around it can run while it
+// executes. Updates the running max m and sum l; returns the factor exp2(m_old
+// - m_new) the accumulator must be rescaled by. pthr2 / ptbl: the PTables
+// thresholds as pairs (thr[k], thr[k + 1]) and (r, s) per pattern, in LDS.
+__device__ __forceinline__ float softmax_code_tile(const f32x16 &sacc, float c2, float &m,
+                                                   float &l, const f32x2 *pthr2,
+                                                   const f32x2 *ptbl, f16x8 (&pb)[2]) {
+  float mt = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+  const float mn = fmaxf(m, mt);
+  // with every score -inf so far, the exponent base 0 gives p = 0 and
+  // alpha = 0 on an accumulator and sum that are still 0
+  const float mb = mn == -INFINITY ? 0.0f : mn;
+  const float alpha = __builtin_amdgcn_exp2f(m - mb);
+  float p[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c2, -mb));
+  float ps = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) ps += p[v];
+  l = l * alpha + ps;
+  m = mn;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am = fmaxf(am, p[8 * blk + e]);
+    am = fmaxf(am, __shfl_xor(am, 32));
+    // a one-multiply estimate of the pattern E4M3(fl(fl(am / 6) / S_P)), never
+    // more than one pattern off, corrected against the thresholds
+    uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
+    const f32x2 th = pthr2[pat];
+    pat = am >= th.y ? pat + 1u : (am < th.x ? pat - 1u : pat);
+    const f32x2 rs = ptbl[pat];
+    uint32_t cw = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      cw = fp4_encode_pair(cw, p[8 * blk + 2 * j] * rs.x, p[8 * blk + 2 * j + 1] * rs.x, j);
+    pb[blk] = decode8(cw, rs.y);
+  }
+  return alpha;
+}
+
 // CACHE: keys from the sink cache's three segments (else one coded segment).
 // The query heads that share a KV head are adjacent rows of Q, so in cache
 // mode (never causal) a workgroup takes 128 consecutive rows of those G * Nq
 // and the cache is read once per KV head, not once per query head.
-// SPLIT (cache mode): this workgroup runs one unit of keys (blockIdx.z: 0 the
-// head, 1 the tail, 2 + k the k-th piece of `split` middle tokens) and writes
-// its softmax state for attention_merge_kernel instead of the output.
-template <bool OUT_BF16, bool CACHE, bool SPLIT>
+template <bool OUT_BF16, bool CACHE>
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // two buffers: tile i is decoded into buffer i & 1 while the codes of tile
   // i + 1 are in flight, so one barrier per tile suffices
@@ -254,14 +301,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // causal: the last query blocks see the most keys; dispatch them first
   const uint32_t qb = a.causal ? gridDim.x - 1u - blockIdx.x : blockIdx.x;
   const uint32_t q0 = qb * kQueriesPerGroup;
-  // with split keys the waves take the 32-row slices in an order rotated by the
-  // unit, so that when few rows are valid (decode) the live waves of the
-  // workgroups that share a compute unit tend to sit on different SIMDs
-  const uint32_t wslot = SPLIT ? (wave + blockIdx.z) & 3u : wave;
-  const uint32_t qi = q0 + wslot * 32u + col;
+  const uint32_t qi = q0 + wave * 32u + col;
   const bool qvalid = qi < rows;
   // a wave without a valid query only helps load and decode the chunks
-  const bool wave_live = q0 + wslot * 32u < rows;
+  const bool wave_live = q0 + wave * 32u < rows;
 
   // P's tables (see PTables); in the loop a one-multiply estimate
   // E4M3(fl(a * 448)) of the block pattern is never more than one pattern off
@@ -291,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const int64_t lim = a.causal ? (int64_t)qi + (int64_t)Nk - (int64_t)a.Nq : (int64_t)Nk - 1;
   // the smallest lim of the wave (its first query), for the unmasked fast path
   const int64_t lim_wave =
-      a.causal ? (int64_t)(q0 + wslot * 32u) + (int64_t)Nk - (int64_t)a.Nq : (int64_t)Nk - 1;
+      a.causal ? (int64_t)(q0 + wave * 32u) + (int64_t)Nk - (int64_t)a.Nq : (int64_t)Nk - 1;
 
   const uint64_t coded_base = CACHE ? (uint64_t)kvh * a.cap : (uint64_t)kvh * Nk;
   const uint32_t coded_off = CACHE ? a.nf : 0u;
@@ -355,46 +398,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     }
   };
 
-  // Online softmax of one tile (base-2 scores s = acc * c2, c2 > 0, so the max
-  // is taken on acc), then P to NVFP4 per 16 keys (keys 16 blk .. +15: 8 in this
-  // lane, 8 in its partner), max scaling, and back to exact fp16 values
-  // V[code] * s. Branch-free, so the matrix instructions issued around it can
-  // run while it executes. Returns the rescale factor of the accumulator.
   auto softmax_code = [&](const f32x16 &sacc, float c2, f16x8 (&pb)[2]) {
-    float mt = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
-    const float mn = fmaxf(m, mt);
-    // with every score -inf so far, the exponent base 0 gives p = 0 and
-    // alpha = 0 on an accumulator and sum that are still 0
-    const float mb = mn == -INFINITY ? 0.0f : mn;
-    const float alpha = __builtin_amdgcn_exp2f(m - mb);
-    float p[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], c2, -mb));
-    float ps = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ps += p[v];
-    l = l * alpha + ps;
-    m = mn;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      float am = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) am = fmaxf(am, p[8 * blk + e]);
-      am = fmaxf(am, __shfl_xor(am, 32));
-      uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
-      const f32x2 th = pthr2[pat];
-      pat = am >= th.y ? pat + 1u : (am < th.x ? pat - 1u : pat);
-      const f32x2 rs = ptbl[pat];
-      uint32_t cw = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        cw = fp4_encode_pair(cw, p[8 * blk + 2 * j] * rs.x, p[8 * blk + 2 * j + 1] * rs.x, j);
-      pb[blk] = decode8(cw, rs.y);
-    }
-    return alpha;
+    return softmax_code_tile(sacc, c2, m, l, pthr2, ptbl, pb);
   };
 
   // O^T = alpha O^T: multiplying by alpha = 1 changes nothing, so the wave
@@ -489,22 +494,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     }
   };
 
-  if (SPLIT) {
-    // one unit; units past the keys present run nothing and write an empty state
-    const uint32_t mid_hi = max(Nk > a.nl ? Nk - a.nl : 0u, a.nf);
-    const uint32_t z = blockIdx.z;
-    if (z < 2u) {
-      if (z == 0u)
-        run_segment(std::true_type{}, 0u, min(a.nf, Nk), true);
-      else
-        run_segment(std::true_type{}, max(mid_hi, a.nf), Nk, false);
-    } else {
-      const uint64_t lo = (uint64_t)a.nf + (uint64_t)(z - 2u) * a.split;
-      if (lo < mid_hi)
-        run_segment(std::false_type{}, (uint32_t)lo,
-                    (uint32_t)min<uint64_t>(lo + a.split, mid_hi), false);
-    }
-  } else if (CACHE) {
+  if (CACHE) {
     // head sinks, coded middle, tail ring: tiles never straddle two segments
     const uint32_t mid_hi = max(Nk > a.nl ? Nk - a.nl : 0u, a.nf);
     run_segment(std::true_type{}, 0u, min(a.nf, Nk), true);
@@ -517,21 +507,6 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   l = l + __shfl_xor(l, 32);
   if (!qvalid) return;
   const uint64_t row = (uint64_t)bh * rows + qi;
-  if (SPLIT) {
-    // the unit's state: accumulator in absolute units, base-2 max, sum
-    const uint64_t urow = row * a.ustride + blockIdx.z;
-    float *dst = a.part + urow * kAttnD;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const uint32_t d0 = 32u * t + 8u * q4 + 4u * g;
-        *(float4 *)(dst + d0) = make_float4(o[t][4 * q4] * unit, o[t][4 * q4 + 1] * unit,
-                                            o[t][4 * q4 + 2] * unit, o[t][4 * q4 + 3] * unit);
-      }
-    if (g == 0u) a.ml[urow] = make_float2(m, l);
-    return;
-  }
   const float f = l > 0.0f ? (SP * unit) / l : 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -550,6 +525,252 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Split keys for decode steps: one wave per workgroup takes 32 query rows and
+// one unit of keys (blockIdx.z: 0 the head, 1 the tail, 2 + k the k-th piece
+// of `split` middle tokens), in chunks of 32 keys, one softmax tile each. With
+// few valid rows (one query per head), the 4-wave kernel above keeps one wave
+// in four busy and two workgroups per compute unit; here each workgroup is one
+// wave with 20 KB of LDS, so up to seven share a compute unit and each of them
+// has work. A single wave needs no barrier: its LDS accesses run in order, so
+// the next chunk is decoded into the same buffer once this one's reads are
+// issued, while the codes of the chunk after are in flight in registers.
+// Writes the unit's state for attention_merge_kernel.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kDecKeys = 32;                // keys per chunk = one softmax tile
+constexpr uint32_t kDecVtStride = kDecKeys + 4;  // fp16 per V^T row (18 dwords)
+
+// This lane's share of one coded chunk: key t >> 1 of the chunk, elements
+// 64 (t & 1) .. +63 of its K and V rows (two 16-byte code words and four
+// scale bytes each).
+struct DecRegs {
+  uint4 k0, k1, v0, v1;
+  uint32_t ks, vs;
+};
+
+__device__ __forceinline__ DecRegs dec_load(const AttnArgs &a, uint64_t row_base, uint32_t c0,
+                                            uint32_t hi, uint32_t t) {
+  DecRegs r{};
+  const uint32_t j = c0 + (t >> 1), h = t & 1u;
+  if (j < hi) {
+    const uint64_t row = row_base + (j - a.nf);
+    const uint8_t *kc = a.kc + row * 64u + 32u * h, *vc = a.vc + row * 64u + 32u * h;
+    r.k0 = *(const uint4 *)kc;
+    r.k1 = *(const uint4 *)(kc + 16);
+    r.v0 = *(const uint4 *)vc;
+    r.v1 = *(const uint4 *)(vc + 16);
+    r.ks = *(const uint32_t *)(a.ks + row * 8u + 4u * h);
+    r.vs = *(const uint32_t *)(a.vs + row * 8u + 4u * h);
+  }
+  return r;
+}
+
+// V^T [d][key] in LDS: row d, the key column XOR-ed with 16 (d >> 6), so the
+// two lanes of a key (d below and above 64) write different banks; 4-key
+// groups stay contiguous for the products' reads.
+__device__ __forceinline__ uint32_t dec_vt_index(uint32_t d, uint32_t key) {
+  return d * kDecVtStride + (key ^ (16u * (d >> 6)));
+}
+
+// A loaded coded chunk decoded into LDS: K row-major [key][d], V transposed.
+// Keys past the unit's end were loaded as zero codes and scales (zeros).
+__device__ __forceinline__ void dec_store(const DecRegs &r, uint32_t t, _Float16 *Ks,
+                                          _Float16 *Vt) {
+  const uint32_t key = t >> 1, d0 = 64u * (t & 1u);
+  _Float16 *kd = &Ks[key * kKsStride + d0];
+  const uint32_t kw[8] = {r.k0.x, r.k0.y, r.k0.z, r.k0.w, r.k1.x, r.k1.y, r.k1.z, r.k1.w};
+  const uint32_t vw[8] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *(f16x8 *)(kd + 8 * i) = decode8(kw[i], scale_value((r.ks >> (8 * (i >> 1))) & 0xFFu));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f16x8 x = decode8(vw[i], scale_value((r.vs >> (8 * (i >> 1))) & 0xFFu));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Vt[dec_vt_index(d0 + 8u * i + e, key)] = x[e];
+  }
+}
+
+// A chunk of sink keys (bf16 rows of the head, or of the tail ring at slot
+// t mod n_last) into LDS as bf16 bits in the same layouts; keys past hi are zeros.
+__device__ __forceinline__ void dec_store_sink(const AttnArgs &a, uint32_t kvh, bool head,
+                                               uint32_t c0, uint32_t hi, uint32_t t,
+                                               _Float16 *Ks, _Float16 *Vt) {
+  const uint32_t key = t >> 1, d0 = 64u * (t & 1u), j = c0 + key;
+  uint4 kq[8], vq[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kq[i] = vq[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (j < hi) {
+    const uint64_t row = head ? (uint64_t)kvh * a.nf + j : (uint64_t)kvh * a.nl + j % a.nl;
+    const uint4 *kr = (const uint4 *)((head ? a.kh : a.kt) + row * kAttnD + d0);
+    const uint4 *vr = (const uint4 *)((head ? a.vh : a.vt) + row * kAttnD + d0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      kq[i] = kr[i];
+      vq[i] = vr[i];
+    }
+  }
+  uint4 *kd = (uint4 *)&Ks[key * kKsStride + d0];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kd[i] = kq[i];
+  uint16_t *vt = (uint16_t *)Vt;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w[4] = {vq[i].x, vq[i].y, vq[i].z, vq[i].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vt[dec_vt_index(d0 + 8u * i + e, key)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
+__global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[kDecKeys * kKsStride];
+  __shared__ __attribute__((aligned(16))) _Float16 Vt[kAttnD * kDecVtStride];
+  __shared__ f32x2 ptbl[128];
+  __shared__ f32x2 pthr2[127];
+
+  const uint32_t t = threadIdx.x, g = t >> 5, col = t & 31u;
+  const uint32_t kvh = blockIdx.y;
+  const uint32_t rows = a.Nq * (a.Hq / a.Hkv);
+  const uint32_t qi = blockIdx.x * 32u + col;
+  const bool qvalid = qi < rows;
+  const uint64_t row = (uint64_t)kvh * rows + (qvalid ? qi : 0u);
+
+  for (uint32_t k = t; k < 128u; k += 64u) {
+    ptbl[k] = f32x2{kPTables.r[k], kPTables.s[k]};
+    if (k < 127u) pthr2[k] = f32x2{kPTables.thr[k], kPTables.thr[k + 1u]};
+  }
+
+  // keys present (the device-resident count if there is one) and this unit's range
+  const uint32_t Nk = a.nk_dev ? (uint32_t)min<int64_t>(*a.nk_dev, (int64_t)a.nf + a.cap + a.nl)
+                               : a.Nk;
+  const uint32_t mid_hi = max(Nk > a.nl ? Nk - a.nl : 0u, a.nf);
+  const uint32_t z = blockIdx.z;
+  const bool sink = z < 2u;
+  uint32_t lo, hi;
+  if (z == 0u) {
+    lo = 0u;
+    hi = min(a.nf, Nk);
+  } else if (z == 1u) {
+    lo = max(mid_hi, a.nf);
+    hi = Nk;
+  } else {
+    const uint64_t l64 = (uint64_t)a.nf + (uint64_t)(z - 2u) * a.split;
+    lo = (uint32_t)min<uint64_t>(l64, mid_hi);
+    hi = (uint32_t)min<uint64_t>(l64 + a.split, mid_hi);
+  }
+
+  // this lane's B operand of Sᵀ: query qi, elements 16 ks + 8 g .. +7
+  f16x8 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    uint32_t w = 0u;
+    float sq = 0.0f;
+    if (qvalid) {
+      w = *(const uint32_t *)(a.qc + row * 64u + 8u * ks + 4u * g);
+      sq = scale_value(a.qs[row * 8u + ks]);
+    }
+    qf[ks] = decode8(w, sq);
+  }
+  // a sink unit multiplies bf16 keys: its Q values (exact in bf16 too) are
+  // converted once, in place, and read back as bf16 bits
+  if (sink) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(f16x8, to_bf16x8(qf[ks]));
+  }
+
+  const float qg = *a.qg;
+  const float c2 = sink ? qg * a.tau_log2e : (qg * *a.kg) * a.tau_log2e;
+  const float unit = sink ? 1.0f : *a.vg;  // the factor the accumulator is counted in
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+  float m = -INFINITY, l = 0.0f;
+
+  const uint64_t coded_base = (uint64_t)kvh * a.cap;
+  DecRegs nxt{};
+  if (lo < hi) {
+    if (sink) {
+      dec_store_sink(a, kvh, z == 0u, lo, hi, t, Ks, Vt);
+    } else {
+      dec_store(dec_load(a, coded_base, lo, hi, t), t, Ks, Vt);
+      if (lo + kDecKeys < hi) nxt = dec_load(a, coded_base, lo + kDecKeys, hi, t);
+    }
+  }
+  for (uint32_t c0 = lo; c0 < hi; c0 += kDecKeys) {
+    f32x16 sacc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const f16x8 qk = qf[ks];
+      if (!sink) {
+        const f16x8 ka = *(const f16x8 *)&Ks[col * kKsStride + 16u * ks + 8u * g];
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qk, sacc, 0, 0, 0);
+      } else {
+        const bf16x8 ka = *(const bf16x8 *)&Ks[col * kKsStride + 16u * ks + 8u * g];
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, __builtin_bit_cast(bf16x8, qk), sacc,
+                                                       0, 0, 0);
+      }
+    }
+    if (c0 + kDecKeys > hi) {  // keys past the unit's end score -inf
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t key = c0 + 8u * (v >> 2) + 4u * g + (v & 3);
+        sacc[v] = key < hi ? sacc[v] : -INFINITY;
+      }
+    }
+    f16x8 pb[2];
+    const float alpha = softmax_code_tile(sacc, c2, m, l, pthr2, ptbl, pb);
+    if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+    }
+    // Oᵀ += Vᵀ Pᵀ: o[i][v] = output d = 32 i + 8 (v >> 2) + 4 g + (v & 3)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t d = 32u * i + col;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const uint2 x0 = *(const uint2 *)&Vt[dec_vt_index(d, 16u * blk + 4u * g)];
+        const uint2 x1 = *(const uint2 *)&Vt[dec_vt_index(d, 16u * blk + 8u + 4u * g)];
+        const uint4 vv = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        if (!sink)
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[blk],
+                                                        o[i], 0, 0, 0);
+        else
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                         to_bf16x8(pb[blk]), o[i], 0, 0, 0);
+      }
+    }
+    // the next chunk into the same buffer (this one's reads are issued and LDS
+    // runs one wave's accesses in order), the codes of the one after in flight
+    const uint32_t c1 = c0 + kDecKeys;
+    if (c1 < hi) {
+      if (sink) {
+        dec_store_sink(a, kvh, z == 0u, c1, hi, t, Ks, Vt);
+      } else {
+        dec_store(nxt, t, Ks, Vt);
+        if (c1 + kDecKeys < hi) nxt = dec_load(a, coded_base, c1 + kDecKeys, hi, t);
+      }
+    }
+  }
+
+  l = l + __shfl_xor(l, 32);
+  if (!qvalid) return;
+  const uint64_t urow = row * a.ustride + z;
+  float *dst = a.part + urow * kAttnD;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint32_t d0 = 32u * i + 8u * q4 + 4u * g;
+      *(float4 *)(dst + d0) = make_float4(o[i][4 * q4] * unit, o[i][4 * q4 + 1] * unit,
+                                          o[i][4 * q4 + 2] * unit, o[i][4 * q4 + 3] * unit);
+    }
+  if (g == 0u) a.ml[urow] = make_float2(m, l);
 }
 
 // The units' states of one output row merged: with M the largest base-2 max,
@@ -621,24 +842,25 @@ hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s) {
     // rows of one KV head's query heads per grid row
     const uint32_t rows = a.Nq * (a.Hq / a.Hkv);
     const uint32_t cap_mid = a.nk_dev ? a.cap : (a.Nk > a.nf + a.nl ? a.Nk - a.nf - a.nl : 0u);
-    const uint32_t units = a.split ? 2u + (cap_mid + a.split - 1u) / a.split : 1u;
-    const dim3 grid((rows + kQueriesPerGroup - 1) / kQueriesPerGroup, a.B * a.Hkv, units);
-    if (a.split) {
-      hipLaunchKernelGGL((attention_kernel<false, true, true>), grid, dim3(256), 0, s, a);
+    if (a.split) {  // units: head, tail, middle pieces
+      const uint32_t units = 2u + (cap_mid + a.split - 1u) / a.split;
+      const dim3 dgrid((rows + 31u) / 32u, a.B * a.Hkv, units);
+      hipLaunchKernelGGL(attention_decode_kernel, dgrid, dim3(64), 0, s, a);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       return launch_attention_merge(a, units, out_bf16, s);
     }
+    const dim3 grid((rows + kQueriesPerGroup - 1) / kQueriesPerGroup, a.B * a.Hkv);
     if (out_bf16)
-      hipLaunchKernelGGL((attention_kernel<true, true, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attention_kernel<true, true>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((attention_kernel<false, true, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attention_kernel<false, true>), grid, dim3(256), 0, s, a);
   } else {
     const dim3 grid((a.Nq + kQueriesPerGroup - 1) / kQueriesPerGroup, a.B * a.Hq);
     if (out_bf16)
-      hipLaunchKernelGGL((attention_kernel<true, false, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attention_kernel<true, false>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((attention_kernel<false, false, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attention_kernel<false, false>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
