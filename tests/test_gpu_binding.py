@@ -80,6 +80,18 @@ def test_attention_operand_checks(gpu, orc):
     o = nv.attention_kv_cache(q, cache, g, cache, g)
     torch.cuda.synchronize()
     assert o.shape == (1, 2, 64, 128) and torch.isfinite(o).all()
+    # split keys: a piece size that is not a whole number of 32-key tiles, and a
+    # workspace one byte short, are refused before any launch
+    with pytest.raises(ValueError):
+        nv.attention_kv_cache(q, cache, g, cache, g, split=48)
+    need = nv.attention_split_workspace_bytes(1, 2, 64, cache["codes"].shape[2], 32)
+    short = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        nv.attention_kv_cache(q, cache, g, cache, g, split=32, workspace=short)
+    o2 = nv.attention_kv_cache(q, cache, g, cache, g, split=32,
+                               workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert o2.shape == (1, 2, 64, 128) and torch.isfinite(o2).all()
 
 
 def test_mxfp4_out_checks(gpu):
