@@ -793,7 +793,7 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
             bc1 = cw[1];
           } else {
             const bool lt = df < best_d;
-            second_d = lt ? best_d : fminf(second_d, df);
+            second_d = lt ? best_d : (df < second_d ? df : second_d);
             if (lt) {
               best_d = df;
               best_p = (uint32_t)p;
