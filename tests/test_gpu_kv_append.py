@@ -38,6 +38,10 @@ def check_against_oracle(orc, cache, kv_all, sg, offsets, hadamard):
     (32, 0, [50, 2, 1], True, False, (-2, 6)),
     (0, 24, [10, 30, 1, 5], False, False, (-2, 6)),
     (64, 64, [200, 1, 9], True, True, (-8, 8)),
+    # 3 heads x 8 blocks a token: 10 tokens (240 blocks) take the one-workgroup
+    # append, 11 (264) the multi-kernel one
+    (16, 16, [40, 10, 11, 10, 11, 1], True, False, (-2, 6)),
+    (16, 16, [40, 10, 11, 10, 11, 1], False, False, (-8, 8)),
 ])
 def test_append_sequence_matches_one_shot(gpu, orc, nf, nl, steps, dtype_bf16, hadamard, offsets):
     B, H, D = 1, 3, 128
