@@ -533,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 // of `split` middle tokens), in chunks of 32 keys, one softmax tile each. With
 // few valid rows (one query per head), the 4-wave kernel above keeps one wave
 // in four busy and two workgroups per compute unit; here each workgroup is one
-// wave with 20 KB of LDS, so up to seven share a compute unit and each of them
+// wave with 20 KB of LDS, so up to eight share a compute unit and each of them
 // has work. A single wave needs no barrier: its LDS accesses run in order, so
 // the next chunk is decoded into the same buffer once this one's reads are
 // issued, while the codes of the chunk after are in flight in registers.
