@@ -132,7 +132,7 @@ def test_graph_replayed_decode_step(gpu, split):
     the tokens present add nothing, so the result equals the host-length call's bit for
     bit."""
     B, H, D, nf, nl = 1, 2, 128, 32, 32
-    n_pre, n_dec = 100, 12
+    n_pre, n_dec = 120, 12  # the middle grows from 56 to 68 tokens: across a 64-token piece
     rng = np.random.default_rng(5)
     kall = to_dev(workloads.workload(3, (B, H, n_pre + n_dec, D)))
     vall = to_dev(workloads.to_bf16_bits(rng.standard_normal((B, H, n_pre + n_dec, D))
