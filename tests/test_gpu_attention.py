@@ -264,3 +264,25 @@ def test_kv_cache_attention_split_full_size_decode(gpu, orc):
     err = np.abs(got - ref)
     print(f"[attention] full-size decode: max err/tol {float(np.max(err / tol)):.3f}")
     assert np.all(err <= tol)
+
+
+def test_kv_cache_attention_empty_cache(gpu, orc):
+    """A cache that holds no token: every unit of the split call is empty (its state
+    max -inf, sum 0) and the output is 0, as the unsplit call and the oracle give; the
+    same through the device-held length."""
+    q = coded(orc, workloads.to_bf16_bits(
+        np.random.default_rng(9).standard_normal((1, 4, 3, 128)).astype(np.float32)))
+    empty = dict(head=np.zeros((1, 2, 16, 128), np.uint16), tail=np.zeros((1, 2, 16, 128), np.uint16),
+                 codes=np.zeros((1, 2, 64, 64), np.uint8), scales=np.zeros((1, 2, 64, 8), np.uint8),
+                 gscale=np.float32(1))
+    ref, _, _ = orc.attention_kv_cache(q, empty, empty, 0, 16, 16, split=32)
+    assert np.all(ref == 0)
+    kc, g = upload_cache(empty, 0, 16, 16)
+    kc["length_dev"] = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    qd = upload(q)
+    for kw in (dict(), dict(split=32), dict(split=32, device_length=True),
+               dict(device_length=True)):
+        print(f"[case] empty cache {kw}", flush=True)
+        O = gpu.attention_kv_cache(qd, kc, g, kc, g, **kw)
+        torch.cuda.synchronize()
+        assert O.shape == (1, 4, 3, 128) and torch.all(O == 0), kw
