@@ -38,6 +38,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kAttnD = 128;
 constexpr uint32_t kKeyTile = 32;                // softmax / P-coding tile
@@ -107,6 +108,22 @@ constexpr PTables make_ptables() {
 
 __constant__ PTables kPTables = make_ptables();
 
+// UE4M3 scale byte -> its value in fp16 bits (exact: at most 4 significant bits
+// between 2^-9 and 448), NaN for bytes 127..255, evaluated by the compiler. The
+// decode kernel looks its block scales up here instead of forming them.
+struct ScaleF16Table {
+  uint16_t v[256];
+};
+
+constexpr ScaleF16Table make_scale_f16_table() {
+  ScaleF16Table t{};
+  for (uint32_t p = 0; p < 256u; ++p)
+    t.v[p] = p < 127u ? __builtin_bit_cast(uint16_t, (_Float16)ce_e4m3_value(p)) : (uint16_t)0x7E00u;
+  return t;
+}
+
+__constant__ ScaleF16Table kScaleF16 = make_scale_f16_table();
+
 // Two codes of byte sel of w as fp16 (the byte selector must be a constant).
 __device__ __forceinline__ f16x2 fp4_pair_f16(uint32_t w, int sel) {
   switch (sel & 3) {
@@ -121,6 +138,20 @@ __device__ __forceinline__ f16x2 fp4_pair_f16(uint32_t w, int sel) {
 // times the block scale s, as fp16 (exact: at most 6 significant bits).
 __device__ __forceinline__ f16x8 decode8(uint32_t w, float s) {
   const _Float16 sh = (_Float16)s;  // E4M3 values are exact in fp16
+  const f16x2 s2 = {sh, sh};
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f16x2 v = fp4_pair_f16(w, j) * s2;
+    r[2 * j] = v.x;
+    r[2 * j + 1] = v.y;
+  }
+  return r;
+}
+
+// decode8 with the scale given as fp16 bits.
+__device__ __forceinline__ f16x8 decode8_h(uint32_t w, uint16_t sbits) {
+  const _Float16 sh = __builtin_bit_cast(_Float16, sbits);
   const f16x2 s2 = {sh, sh};
   f16x8 r;
 #pragma unroll
@@ -576,18 +607,23 @@ __device__ __forceinline__ uint32_t dec_vt_index(uint32_t d, uint32_t key) {
 
 // A loaded coded chunk decoded into LDS: K row-major [key][d], V transposed.
 // Keys past the unit's end were loaded as zero codes and scales (zeros).
-__device__ __forceinline__ void dec_store(const DecRegs &r, uint32_t t, _Float16 *Ks,
-                                          _Float16 *Vt) {
+__device__ __forceinline__ void dec_store(const DecRegs &r, uint32_t t, const uint16_t *sf16,
+                                          _Float16 *Ks, _Float16 *Vt) {
   const uint32_t key = t >> 1, d0 = 64u * (t & 1u);
   _Float16 *kd = &Ks[key * kKsStride + d0];
   const uint32_t kw[8] = {r.k0.x, r.k0.y, r.k0.z, r.k0.w, r.k1.x, r.k1.y, r.k1.z, r.k1.w};
   const uint32_t vw[8] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w};
+  uint16_t ksf[4], vsf[4];  // the block scales in fp16, from the table
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *(f16x8 *)(kd + 8 * i) = decode8(kw[i], scale_value((r.ks >> (8 * (i >> 1))) & 0xFFu));
+  for (int b = 0; b < 4; ++b) {
+    ksf[b] = sf16[(r.ks >> (8 * b)) & 0xFFu];
+    vsf[b] = sf16[(r.vs >> (8 * b)) & 0xFFu];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *(f16x8 *)(kd + 8 * i) = decode8_h(kw[i], ksf[i >> 1]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const f16x8 x = decode8(vw[i], scale_value((r.vs >> (8 * (i >> 1))) & 0xFFu));
+    const f16x8 x = decode8_h(vw[i], vsf[i >> 1]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) Vt[dec_vt_index(d0 + 8u * i + e, key)] = x[e];
   }
@@ -625,16 +661,98 @@ __device__ __forceinline__ void dec_store_sink(const AttnArgs &a, uint32_t kvh, 
   }
 }
 
+// Reductions over the lanes l, l ^ 32 (and l ^ 16) with the gfx950 permlane
+// swaps, which exchange rows of lanes in the VALU (a lane shuffle would take an
+// LDS round trip): after a swap of v with itself the two results hold the value
+// of each lane and of its partner, the same pair on both lanes.
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Online softmax and P coding of one 32-key tile in the 16 x 16 layout of the
+// decode kernel: lane l holds, for query l & 15, the scores of keys 4 g + v
+// (s0[v]) and 16 + 4 g + v (s1[v]), g = l >> 4, so each 16-key block of P is
+// spread over the four lanes l, l ^ 16, l ^ 32, l ^ 48. The arithmetic is that
+// of softmax_code_tile: base-2 scores s = acc * c2, running max m and sum l
+// (this lane's share), P per 16 keys by max scaling under S_P = fl(1/2688),
+// back to exact fp16 values; returns the accumulator's rescale factor. pb
+// holds the lane's P values in the order of its scores (s0, then s1).
+__device__ __forceinline__ float softmax_code_tile16(const f32x4 &s0, const f32x4 &s1, float c2,
+                                                     float &m, float &l, const f32x2 *pthr2,
+                                                     const f32x2 *ptbl, f16x8 &pb) {
+  float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                   fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+  mt = pair_max32(pair_max16(mt)) * c2;
+  const float mn = fmaxf(m, mt);
+  const float mb = mn == -INFINITY ? 0.0f : mn;  // every score -inf so far: p = 0
+  const float alpha = __builtin_amdgcn_exp2f(m - mb);
+  float p[8];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[v], c2, -mb));
+    p[4 + v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[v], c2, -mb));
+  }
+  float ps = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) ps += p[v];
+  l = l * alpha + ps;
+  m = mn;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const float am = pair_max32(pair_max16(
+        fmaxf(fmaxf(p[4 * blk], p[4 * blk + 1]), fmaxf(p[4 * blk + 2], p[4 * blk + 3]))));
+    uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
+    const f32x2 th = pthr2[pat];
+    pat = am >= th.y ? pat + 1u : (am < th.x ? pat - 1u : pat);
+    const f32x2 rs = ptbl[pat];
+    uint32_t cw = fp4_encode_pair(0u, p[4 * blk] * rs.x, p[4 * blk + 1] * rs.x, 0);
+    cw = fp4_encode_pair(cw, p[4 * blk + 2] * rs.x, p[4 * blk + 3] * rs.x, 1);
+    const _Float16 sh = (_Float16)rs.y;
+    const f16x2 s2 = {sh, sh};
+    const f16x2 lo = fp4_pair_f16(cw, 0) * s2, hi = fp4_pair_f16(cw, 1) * s2;
+    pb[4 * blk] = lo.x;
+    pb[4 * blk + 1] = lo.y;
+    pb[4 * blk + 2] = hi.x;
+    pb[4 * blk + 3] = hi.y;
+  }
+  return alpha;
+}
+
+// 16 query rows per wave in the 16 x 16 x 32 matrix layout: with one query
+// per head only a few rows are valid, and the narrower layout halves both the
+// softmax work per lane and the accumulator registers against 32 x 32.
+// Sᵀ = K Qᵀ per 16-key half h: A = key 16 h + (l & 15), d slice 32 s + 8 g
+// .. +7; B = query l & 15, same slice; the result holds keys 16 h + 4 g + v.
+// Oᵀ += Vᵀ Pᵀ per 16-row slice of d: the K index 8 g + e runs over keys
+// 4 g + e (e < 4) and 16 + 4 g + e - 4, the order the lane holds its P in.
 __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 Ks[kDecKeys * kKsStride];
   __shared__ __attribute__((aligned(16))) _Float16 Vt[kAttnD * kDecVtStride];
   __shared__ f32x2 ptbl[128];
   __shared__ f32x2 pthr2[127];
+  __shared__ uint16_t sf16[256];
 
-  const uint32_t t = threadIdx.x, g = t >> 5, col = t & 31u;
+  const uint32_t t = threadIdx.x, g = t >> 4, qc = t & 15u;
   const uint32_t kvh = blockIdx.y;
   const uint32_t rows = a.Nq * (a.Hq / a.Hkv);
-  const uint32_t qi = blockIdx.x * 32u + col;
+  const uint32_t qi = blockIdx.x * 16u + qc;
   const bool qvalid = qi < rows;
   const uint64_t row = (uint64_t)kvh * rows + (qvalid ? qi : 0u);
 
@@ -642,6 +760,7 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
     ptbl[k] = f32x2{kPTables.r[k], kPTables.s[k]};
     if (k < 127u) pthr2[k] = f32x2{kPTables.thr[k], kPTables.thr[k + 1u]};
   }
+  for (uint32_t k = t; k < 256u; k += 64u) sf16[k] = kScaleF16.v[k];
 
   // keys present (the device-resident count if there is one) and this unit's range
   const uint32_t Nk = a.nk_dev ? (uint32_t)min<int64_t>(*a.nk_dev, (int64_t)a.nf + a.cap + a.nl)
@@ -662,114 +781,113 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
     hi = (uint32_t)min<uint64_t>(l64 + a.split, mid_hi);
   }
 
-  // this lane's B operand of Sᵀ: query qi, elements 16 ks + 8 g .. +7
-  f16x8 qf[8];
+  // this lane's B operand of Sᵀ: query qi, elements 32 s + 8 g .. +7 (block 2 s + g / 2)
+  f16x8 qf[4];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int s4 = 0; s4 < 4; ++s4) {
     uint32_t w = 0u;
     float sq = 0.0f;
     if (qvalid) {
-      w = *(const uint32_t *)(a.qc + row * 64u + 8u * ks + 4u * g);
-      sq = scale_value(a.qs[row * 8u + ks]);
+      w = *(const uint32_t *)(a.qc + row * 64u + 16u * s4 + 4u * g);
+      sq = scale_value(a.qs[row * 8u + 2u * s4 + (g >> 1)]);
     }
-    qf[ks] = decode8(w, sq);
+    qf[s4] = decode8(w, sq);
   }
   // a sink unit multiplies bf16 keys: its Q values (exact in bf16 too) are
   // converted once, in place, and read back as bf16 bits
   if (sink) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(f16x8, to_bf16x8(qf[ks]));
+    for (int s4 = 0; s4 < 4; ++s4) qf[s4] = __builtin_bit_cast(f16x8, to_bf16x8(qf[s4]));
   }
 
   const float qg = *a.qg;
   const float c2 = sink ? qg * a.tau_log2e : (qg * *a.kg) * a.tau_log2e;
   const float unit = sink ? 1.0f : *a.vg;  // the factor the accumulator is counted in
-  f32x16 o[4];
+  f32x4 o[8];  // o[i][v]: output d = 16 i + 4 g + v of query qi
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{};
   float m = -INFINITY, l = 0.0f;
 
   const uint64_t coded_base = (uint64_t)kvh * a.cap;
-  DecRegs nxt{};
-  if (lo < hi) {
-    if (sink) {
-      dec_store_sink(a, kvh, z == 0u, lo, hi, t, Ks, Vt);
-    } else {
-      dec_store(dec_load(a, coded_base, lo, hi, t), t, Ks, Vt);
-      if (lo + kDecKeys < hi) nxt = dec_load(a, coded_base, lo + kDecKeys, hi, t);
-    }
-  }
-  for (uint32_t c0 = lo; c0 < hi; c0 += kDecKeys) {
-    f32x16 sacc = {};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const f16x8 qk = qf[ks];
-      if (!sink) {
-        const f16x8 ka = *(const f16x8 *)&Ks[col * kKsStride + 16u * ks + 8u * g];
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qk, sacc, 0, 0, 0);
+  // the chunk loop, compiled once for sink units (bf16 keys) and once for coded
+  // ones, so that no branch separates its LDS reads from the matrix instructions
+  auto run = [&](auto sink_tag) {
+    constexpr bool SINK = decltype(sink_tag)::value;
+    DecRegs nxt{};
+    if (lo < hi) {
+      if (SINK) {
+        dec_store_sink(a, kvh, z == 0u, lo, hi, t, Ks, Vt);
       } else {
-        const bf16x8 ka = *(const bf16x8 *)&Ks[col * kKsStride + 16u * ks + 8u * g];
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, __builtin_bit_cast(bf16x8, qk), sacc,
-                                                       0, 0, 0);
+        dec_store(dec_load(a, coded_base, lo, hi, t), t, sf16, Ks, Vt);
+        if (lo + kDecKeys < hi) nxt = dec_load(a, coded_base, lo + kDecKeys, hi, t);
       }
     }
-    if (c0 + kDecKeys > hi) {  // keys past the unit's end score -inf
+    for (uint32_t c0 = lo; c0 < hi; c0 += kDecKeys) {
+      f32x4 sacc[2] = {{}, {}};
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint32_t key = c0 + 8u * (v >> 2) + 4u * g + (v & 3);
-        sacc[v] = key < hi ? sacc[v] : -INFINITY;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const _Float16 *kp = &Ks[(16u * h + qc) * kKsStride + 32u * s4 + 8u * g];
+          if (!SINK)
+            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const f16x8 *)kp, qf[s4],
+                                                             sacc[h], 0, 0, 0);
+          else
+            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *(const bf16x8 *)kp, __builtin_bit_cast(bf16x8, qf[s4]), sacc[h], 0, 0, 0);
+        }
+      if (c0 + kDecKeys > hi) {  // keys past the unit's end score -inf
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            sacc[h][v] = c0 + 16u * h + 4u * g + v < hi ? sacc[h][v] : -INFINITY;
       }
-    }
-    f16x8 pb[2];
-    const float alpha = softmax_code_tile(sacc, c2, m, l, pthr2, ptbl, pb);
-    if (__ballot(alpha != 1.0f) != 0ull) {
+      f16x8 pb;
+      const float alpha = softmax_code_tile16(sacc[0], sacc[1], c2, m, l, pthr2, ptbl, pb);
+      if (__ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i) o[i] *= alpha;
+      }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-    }
-    // Oᵀ += Vᵀ Pᵀ: o[i][v] = output d = 32 i + 8 (v >> 2) + 4 g + (v & 3)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t d = 32u * i + col;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const uint2 x0 = *(const uint2 *)&Vt[dec_vt_index(d, 16u * blk + 4u * g)];
-        const uint2 x1 = *(const uint2 *)&Vt[dec_vt_index(d, 16u * blk + 8u + 4u * g)];
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t d = 16u * i + qc;
+        const uint2 x0 = *(const uint2 *)&Vt[dec_vt_index(d, 4u * g)];
+        const uint2 x1 = *(const uint2 *)&Vt[dec_vt_index(d, 16u + 4u * g)];
         const uint4 vv = make_uint4(x0.x, x0.y, x1.x, x1.y);
-        if (!sink)
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[blk],
-                                                        o[i], 0, 0, 0);
+        if (!SINK)
+          o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vv), pb, o[i],
+                                                        0, 0, 0);
         else
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                         to_bf16x8(pb[blk]), o[i], 0, 0, 0);
+          o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                         to_bf16x8(pb), o[i], 0, 0, 0);
+      }
+      // the next chunk into the same buffer (this one's reads are issued and LDS
+      // runs one wave's accesses in order), the codes of the one after in flight
+      const uint32_t c1 = c0 + kDecKeys;
+      if (c1 < hi) {
+        if (SINK) {
+          dec_store_sink(a, kvh, z == 0u, c1, hi, t, Ks, Vt);
+        } else {
+          dec_store(nxt, t, sf16, Ks, Vt);
+          if (c1 + kDecKeys < hi) nxt = dec_load(a, coded_base, c1 + kDecKeys, hi, t);
+        }
       }
     }
-    // the next chunk into the same buffer (this one's reads are issued and LDS
-    // runs one wave's accesses in order), the codes of the one after in flight
-    const uint32_t c1 = c0 + kDecKeys;
-    if (c1 < hi) {
-      if (sink) {
-        dec_store_sink(a, kvh, z == 0u, c1, hi, t, Ks, Vt);
-      } else {
-        dec_store(nxt, t, Ks, Vt);
-        if (c1 + kDecKeys < hi) nxt = dec_load(a, coded_base, c1 + kDecKeys, hi, t);
-      }
-    }
-  }
+  };
+  if (sink)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
-  l = l + __shfl_xor(l, 32);
+  l = pair_sum32(pair_sum16(l));
   if (!qvalid) return;
   const uint64_t urow = row * a.ustride + z;
   float *dst = a.part + urow * kAttnD;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const uint32_t d0 = 32u * i + 8u * q4 + 4u * g;
-      *(float4 *)(dst + d0) = make_float4(o[i][4 * q4] * unit, o[i][4 * q4 + 1] * unit,
-                                          o[i][4 * q4 + 2] * unit, o[i][4 * q4 + 3] * unit);
-    }
+  for (int i = 0; i < 8; ++i)
+    *(float4 *)(dst + 16u * i + 4u * g) =
+        make_float4(o[i][0] * unit, o[i][1] * unit, o[i][2] * unit, o[i][3] * unit);
   if (g == 0u) a.ml[urow] = make_float2(m, l);
 }
 
@@ -844,7 +962,7 @@ hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s) {
     const uint32_t cap_mid = a.nk_dev ? a.cap : (a.Nk > a.nf + a.nl ? a.Nk - a.nf - a.nl : 0u);
     if (a.split) {  // units: head, tail, middle pieces
       const uint32_t units = 2u + (cap_mid + a.split - 1u) / a.split;
-      const dim3 dgrid((rows + 31u) / 32u, a.B * a.Hkv, units);
+      const dim3 dgrid((rows + 15u) / 16u, a.B * a.Hkv, units);
       hipLaunchKernelGGL(attention_decode_kernel, dgrid, dim3(64), 0, s, a);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
