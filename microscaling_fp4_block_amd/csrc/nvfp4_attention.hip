@@ -756,12 +756,6 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
   const bool qvalid = qi < rows;
   const uint64_t row = (uint64_t)kvh * rows + (qvalid ? qi : 0u);
 
-  for (uint32_t k = t; k < 128u; k += 64u) {
-    ptbl[k] = f32x2{kPTables.r[k], kPTables.s[k]};
-    if (k < 127u) pthr2[k] = f32x2{kPTables.thr[k], kPTables.thr[k + 1u]};
-  }
-  for (uint32_t k = t; k < 256u; k += 64u) sf16[k] = kScaleF16.v[k];
-
   // keys present (the device-resident count if there is one) and this unit's range
   const uint32_t Nk = a.nk_dev ? (uint32_t)min<int64_t>(*a.nk_dev, (int64_t)a.nf + a.cap + a.nl)
                                : a.Nk;
@@ -781,18 +775,48 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
     hi = (uint32_t)min<uint64_t>(l64 + a.split, mid_hi);
   }
 
+  // Set-up loads in the order they are needed, so that each wait leaves the
+  // later ones in flight: the tables, this lane's Q codes, then (coded units)
+  // the codes of the first two chunks, which arrive while the tables and Q are
+  // stored and decoded.
+  f32x2 tb_r[2], tb_t[2];
+  uint16_t tb_s[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t k = t + 64u * i;
+    tb_r[i] = f32x2{kPTables.r[k], kPTables.s[k]};
+    tb_t[i] = f32x2{kPTables.thr[k], k < 127u ? kPTables.thr[k + 1u] : 0.0f};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tb_s[i] = kScaleF16.v[t + 64u * i];
+  uint32_t qw[4] = {0u, 0u, 0u, 0u}, qsb[4] = {0u, 0u, 0u, 0u};
+  if (qvalid) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      qw[s4] = *(const uint32_t *)(a.qc + row * 64u + 16u * s4 + 4u * g);
+      qsb[s4] = a.qs[row * 8u + 2u * s4 + (g >> 1)];
+    }
+  }
+  const uint64_t coded_base = (uint64_t)kvh * a.cap;
+  DecRegs first{}, nxt{};
+  if (!sink && lo < hi) {
+    first = dec_load(a, coded_base, lo, hi, t);
+    if (lo + kDecKeys < hi) nxt = dec_load(a, coded_base, lo + kDecKeys, hi, t);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t k = t + 64u * i;
+    ptbl[k] = tb_r[i];
+    if (k < 127u) pthr2[k] = tb_t[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sf16[t + 64u * i] = tb_s[i];
+
   // this lane's B operand of Sᵀ: query qi, elements 32 s + 8 g .. +7 (block 2 s + g / 2)
   f16x8 qf[4];
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) {
-    uint32_t w = 0u;
-    float sq = 0.0f;
-    if (qvalid) {
-      w = *(const uint32_t *)(a.qc + row * 64u + 16u * s4 + 4u * g);
-      sq = scale_value(a.qs[row * 8u + 2u * s4 + (g >> 1)]);
-    }
-    qf[s4] = decode8(w, sq);
-  }
+  for (int s4 = 0; s4 < 4; ++s4) qf[s4] = decode8(qw[s4], qvalid ? scale_value(qsb[s4]) : 0.0f);
   // a sink unit multiplies bf16 keys: its Q values (exact in bf16 too) are
   // converted once, in place, and read back as bf16 bits
   if (sink) {
@@ -808,19 +832,15 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
   for (int i = 0; i < 8; ++i) o[i] = f32x4{};
   float m = -INFINITY, l = 0.0f;
 
-  const uint64_t coded_base = (uint64_t)kvh * a.cap;
   // the chunk loop, compiled once for sink units (bf16 keys) and once for coded
   // ones, so that no branch separates its LDS reads from the matrix instructions
   auto run = [&](auto sink_tag) {
     constexpr bool SINK = decltype(sink_tag)::value;
-    DecRegs nxt{};
     if (lo < hi) {
-      if (SINK) {
+      if (SINK)
         dec_store_sink(a, kvh, z == 0u, lo, hi, t, Ks, Vt);
-      } else {
-        dec_store(dec_load(a, coded_base, lo, hi, t), t, sf16, Ks, Vt);
-        if (lo + kDecKeys < hi) nxt = dec_load(a, coded_base, lo + kDecKeys, hi, t);
-      }
+      else
+        dec_store(first, t, sf16, Ks, Vt);
     }
     for (uint32_t c0 = lo; c0 < hi; c0 += kDecKeys) {
       f32x4 sacc[2] = {{}, {}};
