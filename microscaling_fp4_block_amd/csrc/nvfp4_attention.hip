@@ -913,31 +913,38 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
 
 // The units' states of one output row merged: with M the largest base-2 max,
 // w_u = 2^(m_u - M), O = S_P sum_u w_u acc_u / sum_u w_u l_u (0 with no key).
-// One workgroup per row: eight groups of 32 lanes take every eighth unit (four
-// outputs per lane) with their loads independent of one another, and the
-// groups' sums are added in a fixed order. A unit that saw no key holds
-// m_u = -inf, l_u = 0 and a zero accumulator, so its weight and terms are 0.
+// One workgroup of kMergeGroups x 32 lanes per row: group j takes the units
+// u = j mod kMergeGroups (four outputs per lane) with its loads independent of
+// one another, and the groups' sums are added in a fixed order, so a grid that
+// covers more units (all empty) gives the same sums. A unit that saw no key
+// holds m_u = -inf, l_u = 0 and a zero accumulator: its weight and terms are 0.
+constexpr uint32_t kMergeGroups = 32;
+constexpr uint32_t kMergeThreads = 32 * kMergeGroups;
+
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs a, uint32_t units) {
-  __shared__ float wmax[4];
-  __shared__ float4 sacc[8][32];
-  __shared__ float sl[8];
+__global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs a,
+                                                                        uint32_t units) {
+  __shared__ float wmax[kMergeThreads / 64];
+  __shared__ float4 sacc[kMergeGroups][32];
+  __shared__ float sl[kMergeGroups];
   const uint32_t row = blockIdx.x, tid = threadIdx.x;
   const float2 *ml = a.ml + (uint64_t)row * a.ustride;
   const float *part = a.part + (uint64_t)row * a.ustride * kAttnD;
   float mx = -INFINITY;
-  for (uint32_t u = tid; u < units; u += 256u) mx = fmaxf(mx, ml[u].x);
+  for (uint32_t u = tid; u < units; u += kMergeThreads) mx = fmaxf(mx, ml[u].x);
 #pragma unroll
   for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
   if ((tid & 63u) == 0u) wmax[tid >> 6] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  float M = wmax[0];
+#pragma unroll
+  for (uint32_t w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, wmax[w]);
   const uint32_t grp = tid >> 5, d0 = 4u * (tid & 31u);
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float L = 0.0f;
   if (M != -INFINITY) {
 #pragma unroll 4
-    for (uint32_t u = grp; u < units; u += 8u) {
+    for (uint32_t u = grp; u < units; u += kMergeGroups) {
       const float2 st = ml[u];
       const float4 p = *(const float4 *)(part + (uint64_t)u * kAttnD + d0);
       const float w = __builtin_amdgcn_exp2f(st.x - M);
@@ -954,8 +961,8 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs a, uint32
   if (tid >= 32u) return;
   float4 t = sacc[0][tid];
   float lt = sl[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) {
+#pragma unroll 8
+  for (uint32_t j = 1; j < kMergeGroups; ++j) {
     const float4 v = sacc[j][tid];
     t.x += v.x;
     t.y += v.y;
@@ -1007,9 +1014,9 @@ hipError_t launch_attention_merge(const AttnArgs &a, uint32_t units, bool out_bf
                                   hipStream_t s) {
   const dim3 grid(a.B * a.Hq * a.Nq);
   if (out_bf16)
-    hipLaunchKernelGGL((attention_merge_kernel<true>), grid, dim3(256), 0, s, a, units);
+    hipLaunchKernelGGL((attention_merge_kernel<true>), grid, dim3(kMergeThreads), 0, s, a, units);
   else
-    hipLaunchKernelGGL((attention_merge_kernel<false>), grid, dim3(256), 0, s, a, units);
+    hipLaunchKernelGGL((attention_merge_kernel<false>), grid, dim3(kMergeThreads), 0, s, a, units);
   return hipGetLastError();
 }
 
