@@ -630,31 +630,36 @@ __device__ __forceinline__ void dec_store(const DecRegs &r, uint32_t t, const ui
 }
 
 // A chunk of sink keys (bf16 rows of the head, or of the tail ring at slot
-// t mod n_last) into LDS as bf16 bits in the same layouts; keys past hi are zeros.
+// t mod n_last) into LDS as bf16 bits in the same layouts; keys past hi are
+// zeros. K first, then V, so that only one row half is held in registers.
 __device__ __forceinline__ void dec_store_sink(const AttnArgs &a, uint32_t kvh, bool head,
                                                uint32_t c0, uint32_t hi, uint32_t t,
                                                _Float16 *Ks, _Float16 *Vt) {
   const uint32_t key = t >> 1, d0 = 64u * (t & 1u), j = c0 + key;
-  uint4 kq[8], vq[8];
+  const uint64_t row = j < hi ? (head ? (uint64_t)kvh * a.nf + j : (uint64_t)kvh * a.nl + j % a.nl)
+                              : 0u;
+  uint4 q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) kq[i] = vq[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < 8; ++i) q[i] = make_uint4(0u, 0u, 0u, 0u);
   if (j < hi) {
-    const uint64_t row = head ? (uint64_t)kvh * a.nf + j : (uint64_t)kvh * a.nl + j % a.nl;
     const uint4 *kr = (const uint4 *)((head ? a.kh : a.kt) + row * kAttnD + d0);
-    const uint4 *vr = (const uint4 *)((head ? a.vh : a.vt) + row * kAttnD + d0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      kq[i] = kr[i];
-      vq[i] = vr[i];
-    }
+    for (int i = 0; i < 8; ++i) q[i] = kr[i];
   }
   uint4 *kd = (uint4 *)&Ks[key * kKsStride + d0];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) kd[i] = kq[i];
+  for (int i = 0; i < 8; ++i) kd[i] = q[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (j < hi) {
+    const uint4 *vr = (const uint4 *)((head ? a.vh : a.vt) + row * kAttnD + d0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = vr[i];
+  }
   uint16_t *vt = (uint16_t *)Vt;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t w[4] = {vq[i].x, vq[i].y, vq[i].z, vq[i].w};
+    const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       vt[dec_vt_index(d0 + 8u * i + e, key)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
