@@ -537,7 +537,7 @@ def attention_profile(torch, nv, workloads, launches: int = 5):
     torch.cuda.synchronize()
 
 
-def decode_profile(torch, nv, workloads, split: int = 256, launches: int = 5):
+def decode_profile(torch, nv, workloads, split: int = 160, launches: int = 5):
     """Short run for rocprofv3: K and V sink caches of 128 + 32768 + 128 tokens
     ([1, 8, *, 128], workload-3 recipe, ScaleSearch [-2, 6]), one query per head for 32
     query heads, then `launches` split-key cache attention calls (pieces of `split`)."""
@@ -642,6 +642,8 @@ def main():
     ap.add_argument("--decode-profile", action="store_true",
                     help="short run for rocprofv3: split-key cache attention, one query per "
                          "head over 32K-token caches")
+    ap.add_argument("--decode-split", type=int, default=160,
+                    help="piece size of --decode-profile (middle tokens per unit)")
     ap.add_argument("--attention-profile", action="store_true",
                     help="short run for rocprofv3: five non-causal attention launches at 32K")
     ap.add_argument("--rocpd-summary", nargs="+", metavar="DB",
@@ -675,7 +677,7 @@ def main():
         attention_table(torch, nv, workloads)
         return
     if args.decode_profile:
-        decode_profile(torch, nv, workloads)
+        decode_profile(torch, nv, workloads, split=args.decode_split)
         return
     if args.attention_profile:
         attention_profile(torch, nv, workloads)

@@ -202,7 +202,8 @@ NVFP4_API nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t
  * no visible key gets 0). out: [B][Hq][Nq][128] FP32 or bf16. Products are
  * exact; sums are FP32 in the matrix units' order, so results agree with an
  * exact evaluation to FP32 accumulation error plus P codes that round the other
- * way near a midpoint. All arrays device memory; codes 16-byte aligned. */
+ * way near a midpoint. All arrays device memory; codes and out 16-byte aligned,
+ * scales 8-byte aligned (NVFP4_EALIGN otherwise). */
 NVFP4_API nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_scales,
                                        const float *q_gscale, const uint8_t *k_codes,
                                        const uint8_t *k_scales, const float *k_gscale,
@@ -222,7 +223,8 @@ NVFP4_API nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_
  * mask). Keys are visited segment by segment (head, middle, tail, each in token
  * order) in tiles of 32 keys that never straddle two segments; otherwise as
  * nvfp4_attention: sink keys enter the products as their exact bf16 values, coded
- * keys as V[code] * s_block times the tensor scale. out: [B][Hq][Nq][128]. */
+ * keys as V[code] * s_block times the tensor scale. out: [B][Hq][Nq][128].
+ * Codes, head, tail and out 16-byte aligned, scales 8-byte aligned. */
 NVFP4_API nvfp4_status nvfp4_attention_kv_cache(
     const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
     const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,

@@ -640,7 +640,8 @@ nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_scales,
   if (B * Nq == 0) return NVFP4_OK;
   if (!q_codes || !q_scales || !q_gscale || !k_gscale || !v_gscale || !out) return NVFP4_EINVAL;
   if (Nk > 0 && (!k_codes || !k_scales || !v_codes || !v_scales)) return NVFP4_EINVAL;
-  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(out, 16))
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(out, 16) ||
+      !aligned(q_scales, 8) || !aligned(k_scales, 8) || !aligned(v_scales, 8))
     return NVFP4_EALIGN;
   AttnArgs a{};
   a.qc = q_codes;
@@ -703,7 +704,8 @@ nvfp4_status attention_kv_cache_impl(
   if (mid > 0 && (!k_codes || !k_scales || !v_codes || !v_scales)) return NVFP4_EINVAL;
   if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
       !aligned(k_head, 16) || !aligned(k_tail, 16) || !aligned(v_head, 16) ||
-      !aligned(v_tail, 16) || !aligned(out, 16) || !aligned(len_dev, 8))
+      !aligned(v_tail, 16) || !aligned(out, 16) || !aligned(len_dev, 8) ||
+      !aligned(q_scales, 8) || !aligned(k_scales, 8) || !aligned(v_scales, 8))
     return NVFP4_EALIGN;
   if (split > 0) {
     if (split_units(cap, split) > 65535) return NVFP4_ESHAPE;

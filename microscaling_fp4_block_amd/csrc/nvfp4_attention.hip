@@ -559,41 +559,55 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split keys for decode steps: one wave per workgroup takes 32 query rows and
+// Split keys for decode steps: one wave per workgroup takes 16 query rows and
 // one unit of keys (blockIdx.z: 0 the head, 1 the tail, 2 + k the k-th piece
 // of `split` middle tokens), in chunks of 32 keys, one softmax tile each. With
-// few valid rows (one query per head), the 4-wave kernel above keeps one wave
-// in four busy and two workgroups per compute unit; here each workgroup is one
-// wave with 20 KB of LDS, so up to eight share a compute unit and each of them
-// has work. A single wave needs no barrier: its LDS accesses run in order, so
-// the next chunk is decoded into the same buffer once this one's reads are
-// issued, while the codes of the chunk after are in flight in registers.
-// Writes the unit's state for attention_merge_kernel.
+// few valid rows (one query per head) the 4-wave kernel above keeps one wave in
+// four busy; here each workgroup is one wave. Its K operands go from registers
+// to the matrix instructions (each lane loads and decodes the code words of its
+// own operand slices), so only V, transposed, passes through LDS: 12 KB a
+// workgroup, and three waves share each SIMD. A single wave needs no barrier:
+// its LDS accesses run in order, so the next chunk's V is stored into the same
+// buffer once this one's reads are issued, while the codes of the chunk after
+// are in flight in registers. Writes the unit's state for attention_merge_kernel.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kDecKeys = 32;                // keys per chunk = one softmax tile
 constexpr uint32_t kDecVtStride = kDecKeys + 4;  // fp16 per V^T row (18 dwords)
 
-// This lane's share of one coded chunk: key t >> 1 of the chunk, elements
-// 64 (t & 1) .. +63 of its K and V rows (two 16-byte code words and four
-// scale bytes each).
+// This lane's share of one coded chunk. K, as its A operands of Sᵀ: key
+// 16 h + (t & 15) of the chunk (h = 0, 1), elements 32 (t >> 4) .. +31 (one
+// 16-byte code word, slice s = 0..3 of it feeding the s-th product, since the
+// sum over d may run in any order as long as Q's slices follow the same one)
+// and their two block scales. V, to be transposed into LDS: key t >> 1,
+// elements 64 (t & 1) .. +63 (two 16-byte code words, four scale bytes). Keys
+// past the unit's end stay zero.
 struct DecRegs {
-  uint4 k0, k1, v0, v1;
-  uint32_t ks, vs;
+  uint4 kw[2];
+  uint32_t ks[2];
+  uint4 v0, v1;
+  uint32_t vs;
 };
 
 __device__ __forceinline__ DecRegs dec_load(const AttnArgs &a, uint64_t row_base, uint32_t c0,
                                             uint32_t hi, uint32_t t) {
   DecRegs r{};
-  const uint32_t j = c0 + (t >> 1), h = t & 1u;
-  if (j < hi) {
-    const uint64_t row = row_base + (j - a.nf);
-    const uint8_t *kc = a.kc + row * 64u + 32u * h, *vc = a.vc + row * 64u + 32u * h;
-    r.k0 = *(const uint4 *)kc;
-    r.k1 = *(const uint4 *)(kc + 16);
+  const uint32_t g = t >> 4, qc = t & 15u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t j = c0 + 16u * h + qc;
+    if (j < hi) {
+      const uint64_t row = row_base + (j - a.nf);
+      r.kw[h] = *(const uint4 *)(a.kc + row * 64u + 16u * g);
+      r.ks[h] = *(const uint16_t *)(a.ks + row * 8u + 2u * g);
+    }
+  }
+  const uint32_t jv = c0 + (t >> 1), hv = t & 1u;
+  if (jv < hi) {
+    const uint64_t row = row_base + (jv - a.nf);
+    const uint8_t *vc = a.vc + row * 64u + 32u * hv;
     r.v0 = *(const uint4 *)vc;
     r.v1 = *(const uint4 *)(vc + 16);
-    r.ks = *(const uint32_t *)(a.ks + row * 8u + 4u * h);
-    r.vs = *(const uint32_t *)(a.vs + row * 8u + 4u * h);
+    r.vs = *(const uint32_t *)(a.vs + row * 8u + 4u * hv);
   }
   return r;
 }
@@ -605,22 +619,15 @@ __device__ __forceinline__ uint32_t dec_vt_index(uint32_t d, uint32_t key) {
   return d * kDecVtStride + (key ^ (16u * (d >> 6)));
 }
 
-// A loaded coded chunk decoded into LDS: K row-major [key][d], V transposed.
-// Keys past the unit's end were loaded as zero codes and scales (zeros).
-__device__ __forceinline__ void dec_store(const DecRegs &r, uint32_t t, const uint16_t *sf16,
-                                          _Float16 *Ks, _Float16 *Vt) {
+// V of a loaded coded chunk decoded (block scales from the fp16 table) and
+// transposed into LDS.
+__device__ __forceinline__ void dec_store_v(const DecRegs &r, uint32_t t, const uint16_t *sf16,
+                                            _Float16 *Vt) {
   const uint32_t key = t >> 1, d0 = 64u * (t & 1u);
-  _Float16 *kd = &Ks[key * kKsStride + d0];
-  const uint32_t kw[8] = {r.k0.x, r.k0.y, r.k0.z, r.k0.w, r.k1.x, r.k1.y, r.k1.z, r.k1.w};
   const uint32_t vw[8] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w};
-  uint16_t ksf[4], vsf[4];  // the block scales in fp16, from the table
+  uint16_t vsf[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    ksf[b] = sf16[(r.ks >> (8 * b)) & 0xFFu];
-    vsf[b] = sf16[(r.vs >> (8 * b)) & 0xFFu];
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *(f16x8 *)(kd + 8 * i) = decode8_h(kw[i], ksf[i >> 1]);
+  for (int b = 0; b < 4; ++b) vsf[b] = sf16[(r.vs >> (8 * b)) & 0xFFu];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const f16x8 x = decode8_h(vw[i], vsf[i >> 1]);
@@ -629,30 +636,30 @@ __device__ __forceinline__ void dec_store(const DecRegs &r, uint32_t t, const ui
   }
 }
 
-// A chunk of sink keys (bf16 rows of the head, or of the tail ring at slot
-// t mod n_last) into LDS as bf16 bits in the same layouts; keys past hi are
-// zeros. K first, then V, so that only one row half is held in registers.
-__device__ __forceinline__ void dec_store_sink(const AttnArgs &a, uint32_t kvh, bool head,
-                                               uint32_t c0, uint32_t hi, uint32_t t,
-                                               _Float16 *Ks, _Float16 *Vt) {
+// The K operand slice s of half h from loaded codes: elements 32 (t >> 4) + 8 s
+// .. +7, in block 2 (t >> 4) + s / 2 of the key.
+__device__ __forceinline__ f16x8 dec_k_operand(const DecRegs &r, int h, int s4,
+                                               const uint16_t *sf16) {
+  const uint32_t w[4] = {r.kw[h].x, r.kw[h].y, r.kw[h].z, r.kw[h].w};
+  return decode8_h(w[s4], sf16[(r.ks[h] >> (8 * (s4 >> 1))) & 0xFFu]);
+}
+
+// Row of sink key j (bf16): the head, or the tail ring at slot j mod n_last.
+__device__ __forceinline__ uint64_t sink_row(const AttnArgs &a, uint32_t kvh, bool head,
+                                             uint32_t j) {
+  return head ? (uint64_t)kvh * a.nf + j : (uint64_t)kvh * a.nl + j % a.nl;
+}
+
+// V of a chunk of sink keys transposed into LDS as bf16 bits; keys past hi are zeros.
+__device__ __forceinline__ void dec_store_sink_v(const AttnArgs &a, uint32_t kvh, bool head,
+                                                 uint32_t c0, uint32_t hi, uint32_t t,
+                                                 _Float16 *Vt) {
   const uint32_t key = t >> 1, d0 = 64u * (t & 1u), j = c0 + key;
-  const uint64_t row = j < hi ? (head ? (uint64_t)kvh * a.nf + j : (uint64_t)kvh * a.nl + j % a.nl)
-                              : 0u;
   uint4 q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) q[i] = make_uint4(0u, 0u, 0u, 0u);
   if (j < hi) {
-    const uint4 *kr = (const uint4 *)((head ? a.kh : a.kt) + row * kAttnD + d0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = kr[i];
-  }
-  uint4 *kd = (uint4 *)&Ks[key * kKsStride + d0];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) kd[i] = q[i];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (j < hi) {
-    const uint4 *vr = (const uint4 *)((head ? a.vh : a.vt) + row * kAttnD + d0);
+    const uint4 *vr = (const uint4 *)((head ? a.vh : a.vt) + sink_row(a, kvh, head, j) * kAttnD + d0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) q[i] = vr[i];
   }
@@ -743,12 +750,12 @@ __device__ __forceinline__ float softmax_code_tile16(const f32x4 &s0, const f32x
 // 16 query rows per wave in the 16 x 16 x 32 matrix layout: with one query
 // per head only a few rows are valid, and the narrower layout halves both the
 // softmax work per lane and the accumulator registers against 32 x 32.
-// Sᵀ = K Qᵀ per 16-key half h: A = key 16 h + (l & 15), d slice 32 s + 8 g
-// .. +7; B = query l & 15, same slice; the result holds keys 16 h + 4 g + v.
+// Sᵀ = K Qᵀ per 16-key half h, in four products s: A = key 16 h + (l & 15),
+// d = 32 g + 8 s .. +7; B = query l & 15, the same d; the result holds keys
+// 16 h + 4 g + v.
 // Oᵀ += Vᵀ Pᵀ per 16-row slice of d: the K index 8 g + e runs over keys
 // 4 g + e (e < 4) and 16 + 4 g + e - 4, the order the lane holds its P in.
-__global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 Ks[kDecKeys * kKsStride];
+__global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 Vt[kAttnD * kDecVtStride];
   __shared__ f32x2 ptbl[128];
   __shared__ f32x2 pthr2[127];
@@ -794,18 +801,16 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) tb_s[i] = kScaleF16.v[t + 64u * i];
-  uint32_t qw[4] = {0u, 0u, 0u, 0u}, qsb[4] = {0u, 0u, 0u, 0u};
+  uint4 qw = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t qsb = 0u;
   if (qvalid) {
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      qw[s4] = *(const uint32_t *)(a.qc + row * 64u + 16u * s4 + 4u * g);
-      qsb[s4] = a.qs[row * 8u + 2u * s4 + (g >> 1)];
-    }
+    qw = *(const uint4 *)(a.qc + row * 64u + 16u * g);
+    qsb = *(const uint16_t *)(a.qs + row * 8u + 2u * g);
   }
   const uint64_t coded_base = (uint64_t)kvh * a.cap;
-  DecRegs first{}, nxt{};
+  DecRegs cur{}, nxt{};
   if (!sink && lo < hi) {
-    first = dec_load(a, coded_base, lo, hi, t);
+    cur = dec_load(a, coded_base, lo, hi, t);
     if (lo + kDecKeys < hi) nxt = dec_load(a, coded_base, lo + kDecKeys, hi, t);
   }
 
@@ -818,10 +823,14 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) sf16[t + 64u * i] = tb_s[i];
 
-  // this lane's B operand of Sᵀ: query qi, elements 32 s + 8 g .. +7 (block 2 s + g / 2)
+  // this lane's B operands of Sᵀ: query qi, elements 32 g + 8 s .. +7 (block 2 g + s / 2)
   f16x8 qf[4];
+  {
+    const uint32_t w[4] = {qw.x, qw.y, qw.z, qw.w};
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) qf[s4] = decode8(qw[s4], qvalid ? scale_value(qsb[s4]) : 0.0f);
+    for (int s4 = 0; s4 < 4; ++s4)
+      qf[s4] = decode8(w[s4], qvalid ? scale_value((qsb >> (8 * (s4 >> 1))) & 0xFFu) : 0.0f);
+  }
   // a sink unit multiplies bf16 keys: its Q values (exact in bf16 too) are
   // converted once, in place, and read back as bf16 bits
   if (sink) {
@@ -838,29 +847,39 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
   float m = -INFINITY, l = 0.0f;
 
   // the chunk loop, compiled once for sink units (bf16 keys) and once for coded
-  // ones, so that no branch separates its LDS reads from the matrix instructions
+  // ones, so that no branch separates its loads from the matrix instructions
   auto run = [&](auto sink_tag) {
     constexpr bool SINK = decltype(sink_tag)::value;
+    const bool head = z == 0u;
     if (lo < hi) {
       if (SINK)
-        dec_store_sink(a, kvh, z == 0u, lo, hi, t, Ks, Vt);
+        dec_store_sink_v(a, kvh, head, lo, hi, t, Vt);
       else
-        dec_store(first, t, sf16, Ks, Vt);
+        dec_store_v(cur, t, sf16, Vt);
     }
     for (uint32_t c0 = lo; c0 < hi; c0 += kDecKeys) {
       f32x4 sacc[2] = {{}, {}};
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        if (!SINK) {
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const _Float16 *kp = &Ks[(16u * h + qc) * kKsStride + 32u * s4 + 8u * g];
-          if (!SINK)
-            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const f16x8 *)kp, qf[s4],
-                                                             sacc[h], 0, 0, 0);
-          else
+          for (int s4 = 0; s4 < 4; ++s4)
+            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dec_k_operand(cur, h, s4, sf16),
+                                                             qf[s4], sacc[h], 0, 0, 0);
+        } else {
+          const uint32_t j = c0 + 16u * h + qc;
+          const uint4 *kr = (const uint4 *)((head ? a.kh : a.kt) +
+                                            sink_row(a, kvh, head, j < hi ? j : c0) * kAttnD +
+                                            32u * g);
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const uint4 kq = j < hi ? kr[s4] : make_uint4(0u, 0u, 0u, 0u);
             sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                *(const bf16x8 *)kp, __builtin_bit_cast(bf16x8, qf[s4]), sacc[h], 0, 0, 0);
+                __builtin_bit_cast(bf16x8, kq), __builtin_bit_cast(bf16x8, qf[s4]), sacc[h], 0,
+                0, 0);
+          }
         }
+      }
       if (c0 + kDecKeys > hi) {  // keys past the unit's end score -inf
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -887,14 +906,15 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
           o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv),
                                                          to_bf16x8(pb), o[i], 0, 0, 0);
       }
-      // the next chunk into the same buffer (this one's reads are issued and LDS
-      // runs one wave's accesses in order), the codes of the one after in flight
+      // the next chunk's V into the same buffer (this one's reads are issued and
+      // LDS runs one wave's accesses in order), the codes of the one after in flight
       const uint32_t c1 = c0 + kDecKeys;
       if (c1 < hi) {
         if (SINK) {
-          dec_store_sink(a, kvh, z == 0u, c1, hi, t, Ks, Vt);
+          dec_store_sink_v(a, kvh, head, c1, hi, t, Vt);
         } else {
-          dec_store(nxt, t, sf16, Ks, Vt);
+          cur = nxt;
+          dec_store_v(cur, t, sf16, Vt);
           if (c1 + kDecKeys < hi) nxt = dec_load(a, coded_base, c1 + kDecKeys, hi, t);
         }
       }

@@ -155,6 +155,10 @@ def test_attention_argument_checks(lib):
     assert f(*base, 1, 2, 1, 64, 64, 128, 0, P, 7, None) == 1    # output dtype
     assert f(*([None] + [P] * 8), 1, 2, 1, 64, 64, 128, 0, P, 0, None) == 1
     assert f(*base, 1, 2, 1, 64, 64, 128, 0, P + 8, 0, None) == 3
+    for i in (1, 4, 7):                                           # q, k, v scales: 8-byte words
+        ptrs = list(base)
+        ptrs[i] = P + 4
+        assert f(*ptrs, 1, 2, 1, 64, 64, 128, 0, P, 0, None) == 3
     assert f(*base, 1, 2, 1, 0, 64, 128, 0, P, 0, None) == 0     # no queries: nothing to do
 
 
@@ -167,6 +171,10 @@ def test_attention_kv_cache_argument_checks(lib):
     assert f(*ptrs, 1, 1, 2, 1, 8, 300, 128, 16, 16, 100, P, 0, None) == 2
     assert f(*ptrs, 1, 1, 3, 2, 8, 300, 128, 16, 16, 300, P, 0, None) == 2
     assert f(*ptrs, 1, 1, 2, 1, 0, 300, 128, 16, 16, 300, P, 0, None) == 0
+    for i in (1, 6, 11):                                          # q, k, v scales: 8-byte words
+        bad = list(ptrs)
+        bad[i] = P + 4
+        assert f(*bad, 1, 1, 2, 1, 8, 300, 128, 16, 16, 300, P, 0, None) == 3
 
 
 def test_huge_dimensions_are_refused_without_overflow(lib):
