@@ -239,8 +239,12 @@ def rocpd_summary(dbs):
                 print(f"{name} | {cn} | {len(vs)} | {sum(vs) / len(vs):.1f}")
             factors = {}
             for (name, cn), vs in agg.items():
-                if "copyBuffer" in name and cn in ("FETCH_SIZE", "WRITE_SIZE") and max(vs) > 0:
-                    big = [v for v in vs if v >= 0.5 * max(vs)]  # the 1 GiB copies only
+                # the calibration copies only: a run's own small copies (a few KiB) are no
+                # measure of the counter's unit
+                floor = COPY_BYTES / 1024.0 / 16.0
+                if "copyBuffer" in name and cn in ("FETCH_SIZE", "WRITE_SIZE") and \
+                        max(vs) >= floor:
+                    big = [v for v in vs if v >= floor]
                     avg = sum(big) / len(big)
                     f = (COPY_BYTES / 1024.0) / avg
                     factors[cn] = f
