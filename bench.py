@@ -30,13 +30,13 @@ if ROOT not in sys.path:
 
 METRIC = "NVFP4 ScaleSearch quantize GB/s (in+out) and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
-# VALU issue rate for plain (unfused, unpacked) FP32 operations: 256 CUs x 4 SIMDs x
-# 16 lanes x 2.4 GHz. The scored arithmetic may not use FMA and packed FP32 is
-# not used, so this is the applicable peak (the published 157.3 TFLOP/s counts
-# packed FMAs).
-VALU_PEAK_TFLOPS = 256 * 64 * 2.4e9 / 1e12
-# Algorithmic FP32 operations of the search per element and candidate:
-# y = x * r, xhat = V * d, e = |x| - xhat, e * e, running sum.
+# VALU issue ceiling in lane-instructions: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# (one wave-instruction of 64 lanes per SIMD every four cycles).
+VALU_PEAK_TLANE = 256 * 64 * 2.4e9 / 1e12
+# FP32 operations of the exact search per element and candidate, as the scoring
+# rule defines them: y = x * r, xhat = V * d, e = |x| - xhat, e * e, running sum.
+# The certified kernel reaches the same argmin with fewer instructions, so this is
+# a work count for comparison, not a roofline.
 OPS_PER_ELEMENT_CANDIDATE = 5
 SEARCH_KERNEL = "quantize_certified_kernel<-2, 6, true>"
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "quantize_search_bf16_8192x28672.md")
@@ -68,19 +68,24 @@ def committed_traffic(kernel: str):
     return traffic if src_hash == kernel_source_hash() else None
 
 
-def committed_valu_issue(kernel: str):
-    """Fraction of the kernel's cycles in which its CUs issued VALU, from the committed
-    counter summary (SQ_INSTS_VALU per CU over GRBM_GUI_ACTIVE per XCD), if that summary
+def committed_figure(key: str, kernel: str):
+    """A `key | kernel | value` line of the committed counter summary, if that summary
     was taken on the current kernel sources (else None)."""
     if not os.path.exists(PROFILE_SUMMARY):
         return None
-    src_hash, frac = None, None
+    src_hash, val = None, None
     for line in open(PROFILE_SUMMARY):
         if line.startswith("source_hash:"):
             src_hash = line.split(":", 1)[1].strip()
-        if line.startswith("valu_issue_frac") and kernel in line:
-            frac = float(line.rsplit("|", 1)[1].strip())
-    return frac if src_hash == kernel_source_hash() else None
+        if line.startswith(key + " ") and kernel in line:
+            val = float(line.rsplit("|", 1)[1].strip())
+    return val if src_hash == kernel_source_hash() else None
+
+
+def committed_valu_issue(kernel: str):
+    """Fraction of the kernel's cycles in which its CUs issued VALU, from the committed
+    counter summary (SQ_INSTS_VALU per CU over GRBM_GUI_ACTIVE per XCD)."""
+    return committed_figure("valu_issue_frac", kernel)
 ROWS, COLS = 8192, 28672
 OFFSETS = (-2, 6)
 
@@ -761,6 +766,10 @@ def main():
     ncand = OFFSETS[1] - OFFSETS[0] + 1
     alg_flops = OPS_PER_ELEMENT_CANDIDATE * ncand * n
     alg_tflops = alg_flops / (ms_search * 1e-3) / 1e12
+    # VALU check: the kernel's own wave-instructions per launch (committed counters,
+    # fixed for given sources and input) x 64 lanes over the live launch time
+    valu_waves = committed_figure("valu_wave_instructions_per_launch", SEARCH_KERNEL)
+    lane_rate = None if valu_waves is None else valu_waves * 64 / (ms_search * 1e-3) / 1e12
     quant_call_ms = ms_amax + ms_search
     out = {
         "metric": METRIC,
@@ -783,19 +792,27 @@ def main():
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {
-            "bound": "alu",
-            "achieved": round(alg_tflops, 2),
-            "peak": round(VALU_PEAK_TFLOPS, 2),
-            "unit": "TFLOP/s",
-            "frac": round(alg_tflops / VALU_PEAK_TFLOPS, 4),
+            "bound": "hbm",
+            "achieved": round(search_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(search_gbs / HBM_PEAK_GBS, 4),
             "traffic": committed_traffic(SEARCH_KERNEL),
-            "valu_issue_frac_counters": committed_valu_issue(SEARCH_KERNEL),
             "kernel": SEARCH_KERNEL,
             "kernel_ms": round(ms_search, 4),
-            "flops_per_launch": alg_flops,
-            "hbm_gbs": round(search_gbs, 2),
-            "hbm_frac": round(search_gbs / HBM_PEAK_GBS, 4),
             "bytes_per_launch": search_pass_bytes(n, 2),
+            "valu_check": {
+                "limit": "VALU issue (the kernel's binding limit)",
+                "lane_instructions_per_launch": None if valu_waves is None
+                else int(valu_waves * 64),
+                "achieved": None if lane_rate is None else round(lane_rate, 2),
+                "peak": round(VALU_PEAK_TLANE, 2),
+                "unit": "T lane-instructions/s",
+                "frac": None if lane_rate is None else round(lane_rate / VALU_PEAK_TLANE, 4),
+                "issue_frac_counters": committed_valu_issue(SEARCH_KERNEL),
+            },
+            "exact_search_fp32_ops_per_launch": alg_flops,
+            "exact_search_fp32_tops": round(alg_tflops, 2),
         },
         "breakdown": {
             "search_pass_ms": round(ms_search, 4),
