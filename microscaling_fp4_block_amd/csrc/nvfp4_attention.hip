@@ -846,49 +846,67 @@ __global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
   for (int i = 0; i < 8; ++i) o[i] = f32x4{};
   float m = -INFINITY, l = 0.0f;
 
-  // the chunk loop, compiled once for sink units (bf16 keys) and once for coded
-  // ones, so that no branch separates its loads from the matrix instructions
+  // Scores Sᵀ of the chunk at c0: coded keys from loaded codes r, sink keys read
+  // here (rows past hi read as zeros).
+  struct Scores {
+    f32x4 h[2];
+  };
+  auto scores = [&](auto sink_tag, uint32_t c0, const DecRegs &r) {
+    constexpr bool SINK = decltype(sink_tag)::value;
+    Scores sc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sc.h[h] = f32x4{};
+      if (!SINK) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          sc.h[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dec_k_operand(r, h, s4, sf16), qf[s4],
+                                                           sc.h[h], 0, 0, 0);
+      } else {
+        const bool head = z == 0u;
+        const uint32_t j = c0 + 16u * h + qc;
+        const uint4 *kr = (const uint4 *)((head ? a.kh : a.kt) +
+                                          sink_row(a, kvh, head, j < hi ? j : c0) * kAttnD +
+                                          32u * g);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const uint4 kq = j < hi ? kr[s4] : make_uint4(0u, 0u, 0u, 0u);
+          sc.h[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, kq), __builtin_bit_cast(bf16x8, qf[s4]), sc.h[h], 0, 0,
+              0);
+        }
+      }
+    }
+    return sc;
+  };
+
+  // The chunk loop, compiled once for sink units (bf16 keys) and once for coded
+  // ones, so that no branch separates its loads from the matrix instructions.
+  // Software-pipelined by one chunk: the next chunk's scores depend only on its
+  // keys and Q, so their products are issued before this chunk's softmax, P
+  // coding and PV products, which hold the dependent chain.
   auto run = [&](auto sink_tag) {
     constexpr bool SINK = decltype(sink_tag)::value;
     const bool head = z == 0u;
-    if (lo < hi) {
-      if (SINK)
-        dec_store_sink_v(a, kvh, head, lo, hi, t, Vt);
-      else
-        dec_store_v(cur, t, sf16, Vt);
-    }
+    if (lo >= hi) return;
+    if (SINK)
+      dec_store_sink_v(a, kvh, head, lo, hi, t, Vt);
+    else
+      dec_store_v(cur, t, sf16, Vt);
+    Scores sc = scores(sink_tag, lo, cur);
     for (uint32_t c0 = lo; c0 < hi; c0 += kDecKeys) {
-      f32x4 sacc[2] = {{}, {}};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (!SINK) {
-#pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4)
-            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dec_k_operand(cur, h, s4, sf16),
-                                                             qf[s4], sacc[h], 0, 0, 0);
-        } else {
-          const uint32_t j = c0 + 16u * h + qc;
-          const uint4 *kr = (const uint4 *)((head ? a.kh : a.kt) +
-                                            sink_row(a, kvh, head, j < hi ? j : c0) * kAttnD +
-                                            32u * g);
-#pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4) {
-            const uint4 kq = j < hi ? kr[s4] : make_uint4(0u, 0u, 0u, 0u);
-            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, kq), __builtin_bit_cast(bf16x8, qf[s4]), sacc[h], 0,
-                0, 0);
-          }
-        }
-      }
-      if (c0 + kDecKeys > hi) {  // keys past the unit's end score -inf
+      const uint32_t c1 = c0 + kDecKeys;
+      Scores sn;
+      if (c1 < hi) sn = scores(sink_tag, c1, nxt);
+      if (c1 > hi) {  // keys past the unit's end score -inf
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            sacc[h][v] = c0 + 16u * h + 4u * g + v < hi ? sacc[h][v] : -INFINITY;
+            sc.h[h][v] = c0 + 16u * h + 4u * g + v < hi ? sc.h[h][v] : -INFINITY;
       }
       f16x8 pb;
-      const float alpha = softmax_code_tile16(sacc[0], sacc[1], c2, m, l, pthr2, ptbl, pb);
+      const float alpha = softmax_code_tile16(sc.h[0], sc.h[1], c2, m, l, pthr2, ptbl, pb);
       if (__ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] *= alpha;
@@ -908,15 +926,14 @@ __global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
       }
       // the next chunk's V into the same buffer (this one's reads are issued and
       // LDS runs one wave's accesses in order), the codes of the one after in flight
-      const uint32_t c1 = c0 + kDecKeys;
       if (c1 < hi) {
         if (SINK) {
           dec_store_sink_v(a, kvh, head, c1, hi, t, Vt);
         } else {
-          cur = nxt;
-          dec_store_v(cur, t, sf16, Vt);
+          dec_store_v(nxt, t, sf16, Vt);
           if (c1 + kDecKeys < hi) nxt = dec_load(a, coded_base, c1 + kDecKeys, hi, t);
         }
+        sc = sn;
       }
     }
   };

@@ -246,13 +246,15 @@ def test_kv_cache_attention_split(gpu, orc, Hq, Hkv, Nq, T, nf, nl, split):
         assert np.all(err <= tol)
 
 
-def test_kv_cache_attention_split_full_size_decode(gpu, orc):
+@pytest.mark.parametrize("split", [160, 512])
+def test_kv_cache_attention_split_full_size_decode(gpu, orc, split):
     """One decode query per head, Hq = 32 over Hkv = 8, a cache of 128 + 32768 + 128
-    tokens, split into pieces of 512: every row against the oracle."""
-    Hq, Hkv, Nq, nf, nl, split = 32, 8, 1, 128, 128, 512
+    tokens, split into pieces of 160 (the benchmark's decode step) and of 512: every
+    row against the oracle."""
+    Hq, Hkv, Nq, nf, nl = 32, 8, 1, 128, 128
     T = nf + 32768 + nl
     q, k, v = cache_case(orc, Hq, Hkv, Nq, T, nf, nl, 2024)
-    print("[case] split kv-cache attention, full-size decode", flush=True)
+    print(f"[case] split kv-cache attention, full-size decode, pieces of {split}", flush=True)
     kc, kg = upload_cache(k, T, nf, nl)
     vc, vg = upload_cache(v, T, nf, nl)
     cap = kc["codes"].shape[2]
