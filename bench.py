@@ -375,7 +375,8 @@ def kv_append_table(torch, nv, workloads, iters: int = 200):
     # (32 query heads over the 8 K/V heads) over the caches, unsplit or with the keys
     # split into pieces of S tokens (each piece on its own workgroups, then merged).
     steps, warm = 100, 5
-    variants = [("append", 0)] + [("append+attention", s) for s in (0, 128, 160, 256)] + \
+    variants = [("append", 0), ("append2", 0)] + \
+        [("append+attention", s) for s in (0, 128, 160, 256)] + [("append2+attention", 160)] + \
         [("attention", s) for s in (0, 64, 128, 160, 192, 256, 512, 1024)]
     cap = 32768 + (steps + warm) * len(variants) + 8
     kc = nv.kv_cache_alloc(B, H, D, cap, nf, nl, torch.bfloat16, dev)
@@ -395,7 +396,9 @@ def kv_append_table(torch, nv, workloads, iters: int = 200):
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.graph(gph, stream=side):
-            if "append" in parts:
+            if parts.startswith("append2"):  # both appends in one call (one launch)
+                nv.kv_append2_dev(kc, knew, g, vc, vnew, g)
+            elif parts.startswith("append"):
                 nv.kv_append_dev(kc, knew, g)
                 nv.kv_append_dev(vc, vnew, g)
             if "attention" in parts:
@@ -412,7 +415,10 @@ def kv_append_table(torch, nv, workloads, iters: int = 200):
             gph.replay()
         ms = event_time_ms(torch, gph.replay, steps, stream)
         name = {"append": "append 1 K + 1 V token",
+                "append2": "append 1 K + 1 V token in one call",
                 "append+attention": "append 1 K + 1 V token, then attention of 32 query heads",
+                "append2+attention": "append 1 K + 1 V token in one call, then attention of "
+                                     "32 query heads",
                 "attention": "attention of 32 query heads alone"}[parts]
         if "attention" in parts:
             name += f", keys split into pieces of {split}" if split else ", keys unsplit"

@@ -182,6 +182,36 @@ NVFP4_API nvfp4_status nvfp4_kv_append_dev(const void *kv_new, nvfp4_dtype dt, i
                                            uint8_t *codes, uint8_t *scales, int64_t *length,
                                            void *stream);
 
+/* One KV cache of nvfp4_kv_append2_dev: the new tokens and the cache arrays
+ * with their meaning in nvfp4_kv_append_dev (flags and signs likewise, per
+ * cache, so that K may take the randomized Hadamard transform and V not). */
+typedef struct {
+  const void *kv_new;
+  uint32_t flags;
+  const uint32_t *signs;
+  const float *global_scale;
+  void *head;
+  void *tail;
+  uint8_t *codes;
+  uint8_t *scales;
+  int64_t *length;
+} nvfp4_kv_cache_ref;
+
+/* The K and the V append of one decode step (ScaleSearch summary page,
+ * ScaleSearchAttention: the mixed-precision KV cache, extended token by token)
+ * in one call: exactly nvfp4_kv_append_dev on *k, then on *v, with the shared
+ * shape and offset arguments. k and v: host pointers to the two caches' refs,
+ * read during the call only. The two caches must not overlap and must keep
+ * their own length words (k->length == v->length is NVFP4_EINVAL). Both are
+ * checked before anything is enqueued. When both appends are small (at most 256
+ * coded blocks and 1024 admitted 16-byte chunks each, no Hadamard: a decode
+ * step's) they run as one launch of two workgroups; otherwise as the two calls. */
+NVFP4_API nvfp4_status nvfp4_kv_append2_dev(const nvfp4_kv_cache_ref *k,
+                                            const nvfp4_kv_cache_ref *v, nvfp4_dtype dt,
+                                            int64_t B, int64_t H, int64_t t_new, int64_t D,
+                                            int64_t n_first, int64_t n_last, int64_t cap,
+                                            int block, int f_lo, int f_hi, void *stream);
+
 /* The FP32 Hadamard pre-transform alone: y[rows][128] = x[rows][128] H/sqrt(128)
  * (x bf16), as the quantizer computes it on the fly. For inspection and split
  * parity checks; the quantize path never writes it to memory. */

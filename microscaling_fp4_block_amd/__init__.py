@@ -15,6 +15,7 @@ from .nvfp4 import (  # noqa: F401
     hadamard128,
     kv_append,
     kv_append_dev,
+    kv_append2_dev,
     kv_cache_alloc,
     kv_length,
     load,

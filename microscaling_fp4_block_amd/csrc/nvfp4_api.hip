@@ -455,12 +455,20 @@ nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64
 // when they run and the last one advances it; an append that would overflow
 // the cache (t_old + t_new > n_first + cap + n_last) leaves cache and length
 // unchanged. Host checks cover everything that does not depend on t_old.
+// With `plan` given, the checks run and the launch arguments are returned
+// there instead of being launched (the paired K and V append).
+struct KvAppendPlan {
+  QuantArgs q;
+  AdmitArgs c;
+  bool empty, small;
+};
+
 nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H,
                                 int64_t t_new, int64_t D, int64_t n_first, int64_t n_last,
                                 int64_t cap, int block, int f_lo, int f_hi, uint32_t flags,
                                 const uint32_t *signs, const float *global_scale, void *head,
                                 void *tail, uint8_t *codes, uint8_t *scales, int64_t *length,
-                                void *stream) {
+                                void *stream, KvAppendPlan *plan = nullptr) {
   if (!global_scale || !length || !dtype_ok(dt)) return NVFP4_EINVAL;
   nvfp4_status st = check_offsets(block, f_lo, f_hi);
   if (st) return st;
@@ -486,6 +494,7 @@ nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, i
   if (!aligned(kv_new, 16) || !aligned(head, 16) || !aligned(tail, 16) || !aligned(codes, 8) ||
       !aligned(length, 8))
     return NVFP4_EALIGN;
+  if (plan) plan->empty = t_new == 0;
   if (t_new == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dt == NVFP4_BF16;
@@ -531,8 +540,15 @@ nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, i
     c.div_nlast = make_fastdiv((uint32_t)(n_last > 0 ? n_last : 1));
   }
   // small appends (a decode step's): all three steps in one workgroup
-  if (!had && q.map.nblocks <= kSmallAppendBlocks && c.nchunks <= kSmallAppendChunks)
-    return hip_status(launch_kv_append_small(q, c, length, bf16, s));
+  const bool small =
+      !had && q.map.nblocks <= kSmallAppendBlocks && c.nchunks <= kSmallAppendChunks;
+  if (plan) {  // checked, nothing launched
+    plan->q = q;
+    plan->c = c;
+    plan->small = small;
+    return NVFP4_OK;
+  }
+  if (small) return hip_status(launch_kv_append_small(q, c, length, bf16, s));
   if (BH > 0) {
     if (run_quantize(q, bf16, had, s) != hipSuccess) return NVFP4_EHIP;
     if (launch_admit(c, bf16, s) != hipSuccess) return NVFP4_EHIP;
@@ -586,6 +602,44 @@ nvfp4_status nvfp4_kv_append_dev(const void *kv_new, nvfp4_dtype dt, int64_t B, 
   return kv_append_dev_impl(kv_new, dt, B, H, t_new, D, n_first, n_last, cap, block, f_lo, f_hi,
                             signs ? (flags | NVFP4_HADAMARD128) : flags, signs, global_scale,
                             head, tail, codes, scales, length, stream);
+}
+
+nvfp4_status nvfp4_kv_append2_dev(const nvfp4_kv_cache_ref *k, const nvfp4_kv_cache_ref *v,
+                                  nvfp4_dtype dt, int64_t B, int64_t H, int64_t t_new, int64_t D,
+                                  int64_t n_first, int64_t n_last, int64_t cap, int block,
+                                  int f_lo, int f_hi, void *stream) {
+  if (!k || !v) return NVFP4_EINVAL;
+  if (k->length && k->length == v->length) return NVFP4_EINVAL;  // one length each
+  const nvfp4_kv_cache_ref *r[2] = {k, v};
+  KvAppendPlan plan[2];
+  for (int i = 0; i < 2; ++i) {  // every check first: nothing runs unless both pass
+    const nvfp4_kv_cache_ref &c = *r[i];
+    const nvfp4_status st = kv_append_dev_impl(
+        c.kv_new, dt, B, H, t_new, D, n_first, n_last, cap, block, f_lo, f_hi,
+        c.signs ? (c.flags | NVFP4_HADAMARD128) : c.flags, c.signs, c.global_scale, c.head,
+        c.tail, c.codes, c.scales, c.length, stream, &plan[i]);
+    if (st) return st;
+  }
+  if (plan[0].empty) return NVFP4_OK;
+  if (plan[0].small && plan[1].small) {
+    KvAppendPair p{};
+    for (int i = 0; i < 2; ++i) {
+      p.q[i] = plan[i].q;
+      p.c[i] = plan[i].c;
+      p.len[i] = r[i]->length;
+    }
+    p.row_bytes = plan[0].c.chunks_per_row * 16u;
+    return hip_status(launch_kv_append_small_pair(p, dt == NVFP4_BF16, (hipStream_t)stream));
+  }
+  for (int i = 0; i < 2; ++i) {
+    const nvfp4_kv_cache_ref &c = *r[i];
+    const nvfp4_status st = kv_append_dev_impl(
+        c.kv_new, dt, B, H, t_new, D, n_first, n_last, cap, block, f_lo, f_hi,
+        c.signs ? (c.flags | NVFP4_HADAMARD128) : c.flags, c.signs, c.global_scale, c.head,
+        c.tail, c.codes, c.scales, c.length, stream);
+    if (st) return st;
+  }
+  return NVFP4_OK;
 }
 
 nvfp4_status nvfp4_hadamard128(const void *x, nvfp4_dtype xdt, int64_t rows, float *y,

@@ -198,6 +198,14 @@ hipError_t launch_advance_length(int64_t *len, uint32_t t_new, uint32_t total, h
 constexpr uint32_t kSmallAppendBlocks = 256, kSmallAppendChunks = 1024;
 hipError_t launch_kv_append_small(const QuantArgs &q, const AdmitArgs &c, int64_t *len,
                                   bool bf16, hipStream_t s);
+// The K and V appends of a decode step: two small appends, one workgroup each.
+struct KvAppendPair {
+  QuantArgs q[2];
+  AdmitArgs c[2];
+  int64_t *len[2];
+  uint32_t row_bytes;
+};
+hipError_t launch_kv_append_small_pair(const KvAppendPair &p, bool bf16, hipStream_t s);
 hipError_t launch_dequantize_kv(const DequantKvArgs &a, bool sink_bf16, bool out_bf16,
                                 hipStream_t s);
 

@@ -1202,10 +1202,9 @@ __global__ void advance_length_kernel(int64_t *len, uint32_t t_new, uint32_t tot
 // overwrites ring slots the coding reads); the new full-precision tokens are
 // stored. The tensor scale is the caller's.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void kv_append_small_kernel(QuantArgs q, AdmitArgs c,
-                                                                   uint32_t row_bytes,
-                                                                   int64_t *len) {
-  __shared__ f32x2 tbl[128];
+__device__ __forceinline__ void kv_append_small(const QuantArgs &q, const AdmitArgs &c,
+                                                uint32_t row_bytes, int64_t *len,
+                                                f32x2 *tbl) {
   constexpr uint32_t kPer = kSmallAppendChunks / kThreads;
   const uint32_t t_old = len ? (uint32_t)*len : c.t_old;
   const bool fits = !len || (uint64_t)t_old + c.t_new <= c.total;
@@ -1236,6 +1235,26 @@ __global__ __launch_bounds__(kThreads) void kv_append_small_kernel(QuantArgs q, 
       if (dst) *(uint4 *)dst = v[i];
     }
   }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void kv_append_small_kernel(QuantArgs q, AdmitArgs c,
+                                                                   uint32_t row_bytes,
+                                                                   int64_t *len) {
+  __shared__ f32x2 tbl[128];
+  kv_append_small<BF16>(q, c, row_bytes, len, tbl);
+}
+
+// Two small appends in one launch, one workgroup each (the K and V caches of a
+// decode step: distinct caches with their own lengths, so the workgroups share
+// nothing).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void kv_append_small_pair_kernel(KvAppendPair p) {
+  __shared__ f32x2 tbl[128];
+  if (blockIdx.x == 0)
+    kv_append_small<BF16>(p.q[0], p.c[0], p.row_bytes, p.len[0], tbl);
+  else
+    kv_append_small<BF16>(p.q[1], p.c[1], p.row_bytes, p.len[1], tbl);
 }
 
 // y[BH][T][D] from the sink tokens and the dequantized middle, one 16-element
@@ -1641,6 +1660,14 @@ hipError_t launch_kv_append_small(const QuantArgs &q, const AdmitArgs &c, int64_
   else
     hipLaunchKernelGGL((kv_append_small_kernel<false>), dim3(1), dim3(kThreads), 0, s, q, c,
                        c.chunks_per_row * 16u, len);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_small_pair(const KvAppendPair &p, bool bf16, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL((kv_append_small_pair_kernel<true>), dim3(2), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((kv_append_small_pair_kernel<false>), dim3(2), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -41,6 +41,8 @@ SIGNATURES = {
                          _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "nvfp4_kv_append_dev": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32,
                              _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "nvfp4_kv_append2_dev": ([_vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32,
+                              _i32, _i32, _vp], _i32),
     "nvfp4_quantize_rht": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp,
                             _vp, _sz, _vp], _i32),
     "nvfp4_global_scale_rht": ([_vp, _i32, _i64, _i64, _u32, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -388,6 +390,42 @@ def kv_append_dev(cache: dict, kv_new: torch.Tensor, global_scale: torch.Tensor,
                                _stream(dev))
     _check("nvfp4_kv_append_dev", st)
     return cache
+
+
+class _KvCacheRef(ctypes.Structure):
+    """nvfp4_kv_cache_ref: one cache of nvfp4_kv_append2_dev."""
+    _fields_ = [("kv_new", _vp), ("flags", _u32), ("signs", _vp), ("global_scale", _vp),
+                ("head", _vp), ("tail", _vp), ("codes", _vp), ("scales", _vp), ("length", _vp)]
+
+
+def kv_append2_dev(k_cache: dict, k_new: torch.Tensor, k_gscale: torch.Tensor, v_cache: dict,
+                   v_new: torch.Tensor, v_gscale: torch.Tensor, offsets=(-2, 6),
+                   k_hadamard: bool = False, v_hadamard: bool = False, k_signs=None,
+                   v_signs=None, block: int = 16):
+    """kv_append_dev on k_cache, then on v_cache, in one call: a decode step's two
+    appends (small, no Hadamard) run as one launch. Both caches hold the same
+    geometry and each its own device-resident length."""
+    L = load()
+    refs, keep, geo = [], [], []
+    for cache, new, gs, had, signs in ((k_cache, k_new, k_gscale, k_hadamard, k_signs),
+                                       (v_cache, v_new, v_gscale, v_hadamard, v_signs)):
+        dev, B, H, t_new, D, nf, nl, cap, head, tail, codes, scales = _cache_args(cache, new, gs)
+        length = _expect(cache["length_dev"], "cache length_dev", (1,), torch.int64, dev)
+        sw = _signs(signs)
+        keep.append(sw)
+        refs.append(_KvCacheRef(new.data_ptr(), HADAMARD128 if had else 0,
+                                ctypes.addressof(sw) if sw is not None else None, gs.data_ptr(),
+                                head.data_ptr(), tail.data_ptr(), codes.data_ptr(),
+                                scales.data_ptr(), length.data_ptr()))
+        geo.append((dev, B, H, t_new, D, nf, nl, cap, _dtype(new)))
+    if geo[0] != geo[1]:
+        raise ValueError(f"kv_append2_dev: K and V differ in device, shape or dtype: {geo}")
+    dev, B, H, t_new, D, nf, nl, cap, dt = geo[0]
+    f_lo, f_hi = _offsets(offsets)
+    st = L.nvfp4_kv_append2_dev(ctypes.addressof(refs[0]), ctypes.addressof(refs[1]), dt, B, H,
+                                t_new, D, nf, nl, cap, block, f_lo, f_hi, _stream(dev))
+    _check("nvfp4_kv_append2_dev", st)
+    return k_cache, v_cache
 
 
 def kv_length(cache: dict) -> int:

@@ -237,3 +237,21 @@ def test_split_attention_argument_checks(lib):
         assert f(*args(32, P, 1 << 40, Nq=0)) == 0   # no queries: nothing to do
     d = lib.nvfp4_attention_kv_cache_split_dev
     assert d(*([P] * 13), 1, 1, 2, 1, 8, None, 128, 16, 16, 300, 64, P, need, P, 0, None) == 1
+
+
+def test_kv_append2_argument_checks(lib):
+    """The paired K and V append checks both caches before it enqueues anything."""
+    from microscaling_fp4_block_amd import nvfp4
+
+    f = lib.nvfp4_kv_append2_dev
+    ref = lambda length, scales=P: nvfp4._KvCacheRef(P, 0, None, P, P, P, P, scales, length)
+    addr = ctypes.addressof
+    shape = lambda t_new=1, D=128: [1, 1, 2, t_new, D, 16, 16, 64, 16, -2, 6, None]
+    k, v = ref(P), ref(P + 64)
+    assert f(None, addr(v), *shape()) == 1               # a cache missing
+    same = ref(P)
+    assert f(addr(k), addr(same), *shape()) == 1         # one length word for both
+    assert f(addr(k), addr(v), *shape(D=100)) == 2       # D % 16
+    bad = ref(P + 68)
+    assert f(addr(k), addr(bad), *shape()) == 3          # V's length not 8-byte aligned
+    assert f(addr(k), addr(v), *shape(t_new=0)) == 0     # nothing to append: no launch

@@ -108,6 +108,42 @@ def test_device_length_matches_host_length(gpu, dtype, signs):
         _same_cache(host, devc, max(t - nf - nl, 0))
 
 
+@pytest.mark.parametrize("dtype,k_signs", [(torch.bfloat16, None), (torch.float32, None),
+                                           (torch.bfloat16, (5, 6, 7, 8))])
+def test_paired_append_matches_two_appends(gpu, dtype, k_signs):
+    """kv_append2_dev (the K and V appends of a step in one call: one launch of two
+    workgroups when both are small) leaves both caches and both lengths exactly as two
+    kv_append_dev calls do: prefill chunks (the multi-kernel path), single tokens, an
+    empty append, an append that does not fit, and K with the randomized Hadamard
+    transform (V without, so the call takes the two-call path)."""
+    B, H, D, nf, nl, cap = 1, 2, 128, 32, 48, 220
+    steps = [150, 1, 1, 40, 1, 7, 0, 3, 100]  # the last: 203 + 100 > 32 + 220 + 48
+    kv_all = workloads.workload(3, (B, H, sum(steps), D))
+    xk = to_dev(kv_all)
+    xv = to_dev(np.ascontiguousarray(kv_all[..., ::-1]))
+    if dtype == torch.float32:
+        xk, xv = xk.float(), xv.float()
+    gk = gpu.global_scale(xk[:, :, :150].contiguous())
+    gv = gpu.global_scale(xv[:, :, :150].contiguous())
+    one_k, one_v, pair_k, pair_v = (gpu.kv_cache_alloc(B, H, D, cap, nf, nl, dtype)
+                                    for _ in range(4))
+    t = 0
+    for k in steps:
+        print(f"[case] paired append {k} tokens at {t} ({dtype}, k_signs={k_signs})", flush=True)
+        kc = xk[:, :, t:t + k].contiguous()
+        vc = xv[:, :, t:t + k].contiguous()
+        gpu.kv_append_dev(one_k, kc, gk, (-2, 6), signs=k_signs)
+        gpu.kv_append_dev(one_v, vc, gv, (-2, 6))
+        gpu.kv_append2_dev(pair_k, kc, gk, pair_v, vc, gv, (-2, 6), k_signs=k_signs)
+        torch.cuda.synchronize()
+        t += k
+        n = gpu.kv_length(one_k)
+        assert n == min(t, 203)
+        assert gpu.kv_length(pair_k) == gpu.kv_length(pair_v) == gpu.kv_length(one_v) == n
+        _same_cache(one_k, pair_k, max(n - nf - nl, 0))
+        _same_cache(one_v, pair_v, max(n - nf - nl, 0))
+
+
 def test_device_length_overflow_is_a_noop(gpu):
     B, H, D, nf, nl = 1, 1, 128, 16, 16
     kv = to_dev(workloads.workload(3, (B, H, 120, D)))
