@@ -159,14 +159,14 @@ def test_device_length_overflow_is_a_noop(gpu):
         assert torch.equal(c[k], v), k
 
 
-@pytest.mark.parametrize("split", [0, 64])
-def test_graph_replayed_decode_step(gpu, split):
+@pytest.mark.parametrize("split,paired", [(0, False), (64, False), (64, True)])
+def test_graph_replayed_decode_step(gpu, split, paired):
     """One decode step (append a K and a V token at the device length, attention of one
     query over the caches) captured once and replayed token after token; every replay is
     checked against the host-length calls made eagerly on a second pair of caches. With
     split keys the captured grid covers every unit of a full cache and the units past
     the tokens present add nothing, so the result equals the host-length call's bit for
-    bit."""
+    bit. paired: the two appends as one kv_append2_dev call (one launch)."""
     B, H, D, nf, nl = 1, 2, 128, 32, 32
     n_pre, n_dec = 120, 12  # the middle grows from 56 to 68 tokens: across a 64-token piece
     rng = np.random.default_rng(5)
@@ -190,8 +190,11 @@ def test_graph_replayed_decode_step(gpu, split):
     ws_host = torch.empty(nws, dtype=torch.uint8, device="cuda")
 
     def step():
-        gpu.kv_append_dev(kd, knew, kg)
-        gpu.kv_append_dev(vd, vnew, vg)
+        if paired:
+            gpu.kv_append2_dev(kd, knew, kg, vd, vnew, vg)
+        else:
+            gpu.kv_append_dev(kd, knew, kg)
+            gpu.kv_append_dev(vd, vnew, vg)
         return gpu.attention_kv_cache(q, kd, kg, vd, vg, device_length=True, split=split,
                                       workspace=ws_dev if split else None)
 
