@@ -960,7 +960,7 @@ __global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
 // one another, and the groups' sums are added in a fixed order, so a grid that
 // covers more units (all empty) gives the same sums. A unit that saw no key
 // holds m_u = -inf, l_u = 0 and a zero accumulator: its weight and terms are 0.
-constexpr uint32_t kMergeGroups = 32;
+constexpr uint32_t kMergeGroups = 16;
 constexpr uint32_t kMergeThreads = 32 * kMergeGroups;
 
 template <bool OUT_BF16>
