@@ -1,18 +1,19 @@
 """Benchmark: NVFP4 ScaleSearch quantize GB/s (in+out) on MI355X.
 
-Workload (one step): the bf16 weight 8192 x 28672 ~ N(0, 0.02^2) (seeded,
-synthetic), ScaleSearch quantize with offsets [-2, 6] -- global amax pass,
-tensor scale, candidate search, packed codes and scales -- then dequantize
-back to bf16. value = algorithmic bytes of the step (each kernel's input
-read once plus its output written once) / time of the step, inputs resident
-in HBM.
+Workload (one step): the whole nvfp4_quantize call on the bf16 weight
+8192 x 28672 ~ N(0, 0.02^2) (seeded, synthetic) with ScaleSearch offsets
+[-2, 6] -- global amax pass, tensor scale, candidate search, packed codes and
+scales. value = algorithmic bytes of the call (input read once, codes, scales
+and the tensor scale written once) / time of the step, inputs resident in HBM.
 
 Also printed (same JSON line): the dominant kernel's roofline (the search
 kernel alone, timed with HIP events on its stream over its own launches), a
-per-pass breakdown, and the CPU oracle timed on a bounded sample.
+per-pass breakdown (amax pass, search pass given the tensor scale, max-scaling
+control, dequantize, quantize then dequantize), and the CPU oracle timed on a
+bounded sample, on all the host threads this process may use and on one.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--profile]
-       python bench.py --rocpd-summary DB [DB ...]
+       python bench.py --rocpd-summary DB [DB ...] [--sources quantize|attention]
 """
 from __future__ import annotations
 
@@ -39,19 +40,49 @@ VALU_PEAK_TLANE = 256 * 64 * 2.4e9 / 1e12
 # a work count for comparison, not a roofline.
 OPS_PER_ELEMENT_CANDIDATE = 5
 SEARCH_KERNEL = "quantize_certified_kernel<-2, 6, true>"
+CSRC = os.path.join(ROOT, "microscaling_fp4_block_amd", "csrc")
+# the sources each committed profile's kernels are built from: a profile whose recorded
+# hash differs from the current one was taken on other code
+SOURCE_GROUPS = {
+    "quantize": ("nvfp4_kernels.hip", "nvfp4_api.hip", "nvfp4_internal.h", "nvfp4_device.h"),
+    "attention": ("nvfp4_attention.hip", "nvfp4_api.hip", "nvfp4_internal.h", "nvfp4_device.h"),
+}
+PROFILES = {
+    "quantize_search_bf16_8192x28672.md": "quantize",
+    "quantize_hadamard_bf16_q32x32768x128.md": "quantize",
+    "attention_nvfp4_q32x32768_kv8.md": "attention",
+    "attention_decode_split160_q32_kv8_32k.md": "attention",
+}
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "quantize_search_bf16_8192x28672.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "microscaling_fp4_block_amd", "csrc", f)
-                  for f in ("nvfp4_kernels.hip", "nvfp4_api.hip", "nvfp4_internal.h",
-                            "nvfp4_device.h")]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(group: str = "quantize") -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+    for f in SOURCE_GROUPS[group]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def recorded_hash(path: str):
+    for line in open(path):
+        if line.startswith("source_hash:"):
+            return line.split(":", 1)[1].split()[0].strip()
+    return None
+
+
+def profile_status() -> dict:
+    """Each committed profile summary: "current" when its recorded source hash is that of
+    the sources its kernels come from, else "stale" (or "missing")."""
+    out = {}
+    for name, group in PROFILES.items():
+        path = os.path.join(ROOT, "profiles", name)
+        if not os.path.exists(path):
+            out[name] = "missing"
+        else:
+            out[name] = "current" if recorded_hash(path) == kernel_source_hash(group) else "stale"
+    return out
 
 
 def committed_traffic(kernel: str):
@@ -62,7 +93,7 @@ def committed_traffic(kernel: str):
     src_hash, traffic = None, None
     for line in open(PROFILE_SUMMARY):
         if line.startswith("source_hash:"):
-            src_hash = line.split(":", 1)[1].strip()
+            src_hash = line.split(":", 1)[1].split()[0].strip()
         if line.startswith("traffic_bytes_per_launch") and kernel in line:
             traffic = int(line.rsplit("|", 1)[1].strip())
     return traffic if src_hash == kernel_source_hash() else None
@@ -76,7 +107,7 @@ def committed_figure(key: str, kernel: str):
     src_hash, val = None, None
     for line in open(PROFILE_SUMMARY):
         if line.startswith("source_hash:"):
-            src_hash = line.split(":", 1)[1].strip()
+            src_hash = line.split(":", 1)[1].split()[0].strip()
         if line.startswith(key + " ") and kernel in line:
             val = float(line.rsplit("|", 1)[1].strip())
     return val if src_hash == kernel_source_hash() else None
@@ -180,31 +211,59 @@ def copy_gbs(torch, dev, stream, nbytes: int = 1 << 30, iters: int = 10) -> floa
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(x_host: np.ndarray, budget_s: float = 10.0) -> dict:
-    """The oracle, as it stands, on a row sample of the same tensor (quantize + dequantize)."""
+def host_cpus() -> dict:
+    """The host this process runs on: CPU model, CPUs it may run on, CPUs the OS reports,
+    and the threads the oracle uses (the CPUs it may run on, capped by OMP_NUM_THREADS
+    where that is set: the share of the host given to one GPU's jobs)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    allowed = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    threads = min(allowed, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else allowed
+    return {"model": model, "nproc": allowed, "cpu_count": os.cpu_count(), "threads": threads,
+            "omp_num_threads": cap}
+
+
+def cpu_baseline(x_host: np.ndarray, budget_s: float = 8.0) -> dict:
+    """The oracle, as it stands, on a row sample of the same tensor: the whole quantize
+    (amax, tensor scale, tables, search, pack), on every host thread this process may use
+    and on one thread."""
     import oracle
 
     oracle.build(force=False)
-    threads = min(16, os.cpu_count() or 1)
+    cpu = host_cpus()
 
-    def run(rows):
+    def run(rows, threads):
         xs = x_host[:rows]
         t0 = time.perf_counter()
-        c, s, g = oracle.quantize(xs, *OFFSETS, nthreads=threads)
-        oracle.dequantize(c, s, g, "bf16")
+        oracle.quantize(xs, *OFFSETS, nthreads=threads)
         return time.perf_counter() - t0
 
-    rows = 256
-    t = run(rows)
-    rows = int(min(ROWS, max(256, rows * budget_s / max(t, 1e-3))))
-    rows -= rows % 64
-    t = run(rows)
-    n = rows * COLS
-    nbytes = quantize_bytes(n, 2) + dequantize_bytes(n, 2)
-    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the 8192x28672 bf16 tensor ({n} elements): "
-                      f"quantize [-2,6] + bf16 dequantize, {t:.2f} s wall on {threads} threads"}
+    def sample(threads):
+        rows = 64
+        t = run(rows, threads)
+        rows = int(min(ROWS, max(64, rows * budget_s / max(t, 1e-3))))
+        rows -= rows % 64
+        t = run(rows, threads)
+        n = rows * COLS
+        return quantize_bytes(n, 2) / t / 1e9, rows, n, t
+
+    gbs, rows, n, t = sample(cpu["threads"])
+    gbs1, rows1, n1, t1 = sample(1)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cpu["threads"], "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the 8192x28672 bf16 tensor ({n} elements): the whole "
+                      f"quantize [-2,6], {t:.2f} s wall on {cpu['threads']} threads",
+            "single_thread": {"value": round(gbs1, 4), "unit": "GB/s",
+                              "sample": f"rows 0..{rows1 - 1} ({n1} elements), {t1:.2f} s wall "
+                                        "on 1 thread"},
+            "host": {"cpu_model": cpu["model"], "nproc": cpu["nproc"],
+                     "os_cpu_count": cpu["cpu_count"], "omp_num_threads": cpu["omp_num_threads"]}}
 
 
 COPY_BYTES = 1 << 30
@@ -269,7 +328,7 @@ def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
     import oracle
 
     oracle.build(force=False)
-    threads = min(16, os.cpu_count() or 1)
+    threads = host_cpus()["threads"]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     flush = CacheFlush(torch, dev)
@@ -661,11 +720,14 @@ def main():
                     help="piece size of --decode-profile (middle tokens per unit)")
     ap.add_argument("--attention-profile", action="store_true",
                     help="short run for rocprofv3: five non-causal attention launches at 32K")
+    ap.add_argument("--sources", choices=sorted(SOURCE_GROUPS), default="quantize",
+                    help="with --rocpd-summary: the source group whose hash the summary records")
     ap.add_argument("--rocpd-summary", nargs="+", metavar="DB",
                     help="print a text summary of rocprofv3 databases of a --profile run")
     args = ap.parse_args()
     if args.rocpd_summary:
-        print(f"source_hash: {kernel_source_hash()}")
+        print(f"source_hash: {kernel_source_hash(args.sources)} (sources: "
+              f"{', '.join(SOURCE_GROUPS[args.sources])})")
         rocpd_summary(args.rocpd_summary)
         return
     if args.gpus != 1:
@@ -704,35 +766,38 @@ def main():
     n = x.numel()
     ws = torch.empty(nv.workspace_bytes(ROWS, COLS), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    codes = scales = g = None
+    codes = torch.empty(ROWS, COLS // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(ROWS, COLS // 16, dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
+    out = (codes, scales, g)
 
-    def step():
-        nonlocal codes, scales, g
-        codes, scales, g = nv.quantize(x, OFFSETS, workspace=ws)
-        nv.dequantize(codes, scales, g, torch.bfloat16, out=y)
+    def step():  # the whole quantize call: amax pass, tensor scale, search, pack
+        nv.quantize(x, OFFSETS, workspace=ws, out=out)
 
-    gfix = None
+    step()
+    torch.cuda.synchronize()
+    gfix = g.clone()
 
     def search_only():
-        nv.quantize(x, OFFSETS, global_scale=gfix, workspace=ws)
+        nv.quantize(x, OFFSETS, global_scale=gfix, workspace=ws, out=out)
 
     def amax_only():
         nv.global_scale(x, workspace=ws)
 
     def control_only():
-        nv.quantize(x, (0, 0), global_scale=gfix, workspace=ws)
+        nv.quantize(x, (0, 0), global_scale=gfix, workspace=ws, out=out)
 
     def dequant_only():
         nv.dequantize(codes, scales, g, torch.bfloat16, out=y)
 
+    def quant_dequant():
+        step()
+        dequant_only()
+
     if args.profile:
         # Fixed launch order: a warm-up step, then 5 launches of each pass, then the
         # 1 GiB copies that calibrate the byte counters.
-        step()
-        gfix = g.clone()
-        torch.cuda.synchronize()
         for fn in (search_only, control_only, amax_only, dequant_only):
             for _ in range(5):
                 fn()
@@ -744,11 +809,25 @@ def main():
         print("[bench] profile run done", file=sys.stderr, flush=True)
         return
 
+    # Per-pass breakdown first, each pass timed over its own launches on the same stream
+    # (kernel durations settle over the first ~20 ms of GPU work of a process).
+    print("[bench] timing the passes", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.1:
+        step()
+    torch.cuda.synchronize()
+    iters = max(args.steps, 20)
+    ms_search = event_time_ms(torch, search_only, iters, stream)
+    ms_amax = event_time_ms(torch, amax_only, iters, stream)
+    ms_ctrl = event_time_ms(torch, control_only, iters, stream)
+    ms_deq = event_time_ms(torch, dequant_only, iters, stream)
+    ms_qdq = event_time_ms(torch, quant_dequant, iters, stream)
+    s10, s50, s90 = percentiles(launch_times_ms(torch, search_only, iters, stream))
+    copy_rate = copy_gbs(torch, dev, stream)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    gfix = g.clone()
-
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -756,18 +835,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    step_bytes = quantize_bytes(n, 2) + dequantize_bytes(n, 2)
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-
-    # per-pass breakdown, each timed over its own launches on the same stream
-    iters = max(args.steps, 10)
-    ms_search = event_time_ms(torch, search_only, iters, stream)
-    ms_amax = event_time_ms(torch, amax_only, iters, stream)
-    ms_ctrl = event_time_ms(torch, control_only, iters, stream)
-    ms_deq = event_time_ms(torch, dequant_only, iters, stream)
-    s10, s50, s90 = percentiles(launch_times_ms(torch, search_only, iters, stream))
-    copy_rate = copy_gbs(torch, dev, stream)
     qbytes = quantize_bytes(n, 2)
+    value = qbytes / (ms_step * 1e-3) / 1e9
+    amax_bytes = n * 2
+    # the whole call reads the input twice (amax pass, then search pass): at the HBM peak
+    # it could reach qbytes / (qbytes + amax_bytes) of the peak in qbytes-per-second terms
+    two_pass_ceiling = qbytes / (qbytes + amax_bytes)
     search_gbs = search_pass_bytes(n, 2) / (ms_search * 1e-3) / 1e9
     ncand = OFFSETS[1] - OFFSETS[0] + 1
     alg_flops = OPS_PER_ELEMENT_CANDIDATE * ncand * n
@@ -776,7 +849,7 @@ def main():
     # fixed for given sources and input) x 64 lanes over the live launch time
     valu_waves = committed_figure("valu_wave_instructions_per_launch", SEARCH_KERNEL)
     lane_rate = None if valu_waves is None else valu_waves * 64 / (ms_search * 1e-3) / 1e12
-    quant_call_ms = ms_amax + ms_search
+    qdq_bytes = qbytes + dequantize_bytes(n, 2)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -788,15 +861,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "bf16 weight 8192x28672 N(0,0.02^2) seed 3: ScaleSearch quantize "
-                        "offsets [-2,6] (global amax + search + pack) then bf16 dequantize",
+            "workload": "bf16 weight 8192x28672 N(0,0.02^2) seed 3: the whole nvfp4_quantize "
+                        "call, ScaleSearch offsets [-2,6] (global amax pass, tensor scale, "
+                        "candidate search, pack); inputs resident in HBM",
             "rows": ROWS, "cols": COLS, "block": 16, "offsets": list(OFFSETS),
-            "step_bytes": step_bytes,
+            "bytes_per_step": qbytes,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "two_pass_ceiling_pct_hbm_peak": round(100 * two_pass_ceiling, 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(search_gbs, 2),
@@ -825,17 +900,18 @@ def main():
             "search_pass_gbs": round(search_gbs, 2),
             "search_pass_per_launch_ms_p10_p50_p90": [round(s10, 4), round(s50, 4), round(s90, 4)],
             "amax_pass_ms": round(ms_amax, 4),
-            "amax_pass_gbs": round(n * 2 / (ms_amax * 1e-3) / 1e9, 2),
-            "quantize_call_ms": round(quant_call_ms, 4),
-            "quantize_call_gbs": round(qbytes / (quant_call_ms * 1e-3) / 1e9, 2),
+            "amax_pass_gbs": round(amax_bytes / (ms_amax * 1e-3) / 1e9, 2),
+            "amax_plus_search_ms": round(ms_amax + ms_search, 4),
             "max_scaling_control_ms": round(ms_ctrl, 4),
             "scalesearch_over_max_scaling": round(ms_search / ms_ctrl, 3),
             "dequantize_bf16_ms": round(ms_deq, 4),
             "dequantize_bf16_gbs": round(dequantize_bytes(n, 2) / (ms_deq * 1e-3) / 1e9, 2),
+            "quantize_then_dequantize_ms": round(ms_qdq, 4),
+            "quantize_then_dequantize_gbs": round(qdq_bytes / (ms_qdq * 1e-3) / 1e9, 2),
             "hip_d2d_copy_gbs": round(copy_rate, 1),
-            "step_frac_of_d2d_copy": round(value / copy_rate, 4),
             "wall_s_timed_region": round(wall, 3),
         },
+        "profiles": profile_status(),
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -30,6 +30,9 @@ SIGNATURES = {
     "nvfp4_workspace_bytes": ([_i64, _i64, _u32], _sz),
     "nvfp4_quantize": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp, _sz,
                         _vp], _i32),
+    "nvfp4_quantize_noalloc": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _u32, _vp, _vp, _vp,
+                                _vp], _i32),
+    "nvfp4_noalloc_scratch_bytes": ([], _sz),
     "nvfp4_global_scale": ([_vp, _i32, _i64, _i64, _u32, _vp, _vp, _sz, _vp], _i32),
     "nvfp4_dequantize": ([_vp, _vp, _vp, _i64, _i64, _i32, _vp, _i32, _vp], _i32),
     "nvfp4_quantize_kv_sink": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
@@ -181,12 +184,14 @@ def _offsets(offsets):
 
 def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
              global_scale: torch.Tensor | None = None, block: int = 16, workspace=None,
-             signs=None):
+             signs=None, out=None):
     """ScaleSearch NVFP4 quantize of x (last dim in blocks of 16).
 
     Returns (codes uint8[..., K/2], scales uint8[..., K/16], global_scale float32[1]).
     If ``global_scale`` (a device float32[1]) is given it is used as S_g.
     ``signs`` (four uint32 words) selects the randomized Hadamard transform.
+    ``out`` = (codes, scales, global_scale) tensors to write instead of new ones
+    (the third is ignored when ``global_scale`` is given).
     """
     L = load()
     dev = _dev(x)
@@ -194,11 +199,17 @@ def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
     R = x.numel() // K if K else 0
     f_lo, f_hi = _offsets(offsets)
     flags = HADAMARD128 if hadamard else 0
-    codes = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8, device=dev)
-    scales = torch.empty(*x.shape[:-1], K // 16, dtype=torch.uint8, device=dev)
+    if out is not None:
+        codes = _expect(out[0], "out codes", (*x.shape[:-1], K // 2), torch.uint8, dev)
+        scales = _expect(out[1], "out scales", (*x.shape[:-1], K // 16), torch.uint8, dev)
+    else:
+        codes = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8, device=dev)
+        scales = torch.empty(*x.shape[:-1], K // 16, dtype=torch.uint8, device=dev)
     if global_scale is not None:
         flags |= GSCALE_GIVEN
         g = _scale_arg(global_scale, "global_scale", dev)
+    elif out is not None:
+        g = _scale_arg(out[2], "out global_scale", dev)
     else:
         g = torch.empty(1, dtype=torch.float32, device=dev)
     ws, wsb = _workspace(workspace, int(L.nvfp4_workspace_bytes(R, K, flags)), dev)
@@ -212,6 +223,38 @@ def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
                                   ctypes.addressof(sw), codes.data_ptr(), scales.data_ptr(),
                                   g.data_ptr(), ws.data_ptr(), wsb, _stream(dev))
     _check("nvfp4_quantize", st)
+    return codes, scales, g
+
+
+def quantize_noalloc(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
+                     global_scale: torch.Tensor | None = None, out=None):
+    """``quantize`` through nvfp4_quantize_noalloc: the library keeps the amax pass's
+    partial maxima in its own device array (no workspace). Calls that overlap in time on
+    one GPU share that array and race. ``out`` = (codes, scales, global_scale) to write
+    instead of new tensors (the third is ignored when ``global_scale`` is given)."""
+    L = load()
+    dev = _dev(x)
+    K = x.shape[-1]
+    R = x.numel() // K if K else 0
+    f_lo, f_hi = _offsets(offsets)
+    flags = HADAMARD128 if hadamard else 0
+    if out is not None:
+        codes = _expect(out[0], "out codes", (*x.shape[:-1], K // 2), torch.uint8, dev)
+        scales = _expect(out[1], "out scales", (*x.shape[:-1], K // 16), torch.uint8, dev)
+    else:
+        codes = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8, device=dev)
+        scales = torch.empty(*x.shape[:-1], K // 16, dtype=torch.uint8, device=dev)
+    if global_scale is not None:
+        flags |= GSCALE_GIVEN
+        g = _scale_arg(global_scale, "global_scale", dev)
+    elif out is not None:
+        g = _scale_arg(out[2], "out global_scale", dev)
+    else:
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    st = L.nvfp4_quantize_noalloc(x.data_ptr(), _dtype(x), R, K, 16, f_lo, f_hi, flags,
+                                  codes.data_ptr(), scales.data_ptr(), g.data_ptr(),
+                                  _stream(dev))
+    _check("nvfp4_quantize_noalloc", st)
     return codes, scales, g
 
 

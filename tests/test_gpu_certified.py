@@ -1,8 +1,9 @@
-"""The certified search (bf16 input, and FP32 values through three exact bf16
-parts) must give the contract's result on blocks where the certificate cannot decide: candidates whose SSEs tie exactly or differ by a few
-parts per million. Inputs are chosen on the CPU with the independent NumPy
-reference (no GPU output is used to build them); results are compared bit for
-bit with the oracle under the same tensor scale."""
+"""The certified search (bf16 input; FP32 values take the exact search) must give
+the contract's result on blocks where the certificate cannot decide: candidates
+whose SSEs tie exactly or differ by a few parts per million. Inputs are chosen on
+the CPU with the independent NumPy reference (no GPU output is used to build
+them); results are compared bit for bit with the oracle under the same tensor
+scale."""
 import numpy as np
 import pytest
 import torch
