@@ -107,6 +107,27 @@ NVFP4_API nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t ro
                             uint8_t *scales, float *global_scale, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory or pass a workspace (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * exactly nvfp4_quantize (same arguments, checks, outputs and bytes), with the
+ * partial maxima of the global amax pass kept in a library-owned device array of
+ * nvfp4_noalloc_scratch_bytes() bytes (2 KiB; every tensor size fits, the amax
+ * pass never keeps more than 512 partials) instead of a workspace. Each GPU the
+ * library runs on holds its own copy until the process ends; its address is
+ * looked up on the first call on that GPU (the device of `stream`, or the
+ * current device for the null stream). All calls on one GPU share that array:
+ * calls that overlap in time on one GPU race and must be ordered by the caller
+ * (one stream, or events). The call allocates nothing (no hipMalloc, no
+ * library allocation) and enqueues only kernel launches. NVFP4_EHIP if the
+ * array's address cannot be found. */
+NVFP4_API nvfp4_status nvfp4_quantize_noalloc(const void *x, nvfp4_dtype xdt, int64_t rows,
+                                    int64_t cols, int block, int f_lo, int f_hi,
+                                    uint32_t flags, uint8_t *codes, uint8_t *scales,
+                                    float *global_scale, void *stream);
+
+/* Size in bytes of the device array nvfp4_quantize_noalloc uses on each GPU. */
+NVFP4_API size_t nvfp4_noalloc_scratch_bytes(void);
+
 /* Only the global scale: S_g of x[rows][cols] (after the Hadamard transform
  * with NVFP4_HADAMARD128) into global_scale[1]. The first half of
  * nvfp4_quantize; feed the result back with NVFP4_GSCALE_GIVEN. */

@@ -23,5 +23,6 @@ from .nvfp4 import (  # noqa: F401
     mxfp4_quantize,
     quantize,
     quantize_kv_sink,
+    quantize_noalloc,
     workspace_bytes,
 )

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mxfp4.h"
 #include "../../include/nvfp4.h"
 #include "nvfp4_internal.h"
@@ -210,6 +212,72 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_
                             size_t workspace_bytes, void *stream) {
   return quantize_impl(x, xdt, rows, cols, block, f_lo, f_hi, flags, nullptr, codes, scales,
                        global_scale, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free quantize: the partial maxima of the global amax pass live in a
+// file-scope device array instead of a caller workspace. Each GPU holds its own
+// copy; its address is looked up once per device (with that device current) and
+// only that address is handed to the kernels. All calls on one GPU share it, so
+// calls that overlap in time on one GPU race. Every call writes each partial it
+// later reads (one per amax workgroup), so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kScratchWords = kMaxAmaxGroups;
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxScratchDevices];
+
+// The device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream); nullptr if it cannot be found.
+void *scratch_address(hipStream_t stream) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  if (scratch_dev[dev]) return scratch_dev[dev];
+  if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void *p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (dev != cur) (void)hipSetDevice(cur);
+  if (e != hipSuccess || !p) return nullptr;
+  scratch_dev[dev] = p;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_noalloc_scratch_bytes(void) { return sizeof(scratch); }
+
+nvfp4_status nvfp4_quantize_noalloc(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                                    int block, int f_lo, int f_hi, uint32_t flags,
+                                    uint8_t *codes, uint8_t *scales, float *global_scale,
+                                    void *stream) {
+  if (workspace_needed() > sizeof(scratch)) return NVFP4_EWORKSPACE;
+  // argument checks first, so that an invalid call touches no device state
+  if (!global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
+  nvfp4_status st = check_offsets(block, f_lo, f_hi);
+  if (st) return st;
+  st = check_shape(rows, cols, flags, xdt);
+  if (st) return st;
+  if (rows > 0 && (!x || !codes || !scales)) return NVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 8)) return NVFP4_EALIGN;
+  void *ws = nullptr;
+  if (!(flags & NVFP4_GSCALE_GIVEN)) {
+    ws = scratch_address((hipStream_t)stream);
+    if (!ws) return NVFP4_EHIP;
+  }
+  return quantize_impl(x, xdt, rows, cols, block, f_lo, f_hi, flags, nullptr, codes, scales,
+                       global_scale, ws, ws ? sizeof(scratch) : 0, stream);
 }
 
 nvfp4_status nvfp4_quantize_rht(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,

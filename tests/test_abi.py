@@ -78,6 +78,30 @@ def test_quantize_argument_checks(lib, kw, status):
     assert q(lib, **kw) == status
 
 
+def q_noalloc(lib, **kw):
+    a = dict(x=P, xdt=1, rows=4, cols=64, block=16, f_lo=-2, f_hi=6, flags=0, codes=P,
+             scales=P, gs=P, stream=None)
+    a.update(kw)
+    return lib.nvfp4_quantize_noalloc(a["x"], a["xdt"], a["rows"], a["cols"], a["block"],
+                                      a["f_lo"], a["f_hi"], a["flags"], a["codes"], a["scales"],
+                                      a["gs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(scales=None), 1), (dict(gs=None), 1),
+    (dict(xdt=7), 1), (dict(block=32), 1), (dict(f_lo=1), 1), (dict(f_hi=-1), 1),
+    (dict(f_lo=-127), 1), (dict(f_hi=127), 1), (dict(flags=8), 1),
+    (dict(cols=24), 2), (dict(cols=0), 2), (dict(rows=-1), 2), (dict(rows=1 << 40), 2),
+    (dict(flags=1, xdt=0), 1), (dict(flags=1, cols=64), 2),
+    (dict(x=P + 8), 3), (dict(codes=P + 4), 3),
+])
+def test_quantize_noalloc_argument_checks(lib, kw, status):
+    """The allocation-free quantize makes the same checks as nvfp4_quantize, before it
+    looks up its device array."""
+    assert q_noalloc(lib, **kw) == status
+    assert lib.nvfp4_noalloc_scratch_bytes() == 2048
+
+
 def test_dequantize_argument_checks(lib):
     f = lib.nvfp4_dequantize
     assert f(None, P, P, 4, 64, 16, P, 0, None) == 1
