@@ -903,32 +903,38 @@ float oracle_mx_block_sse(const float x[32], int X)
 }
 
 /* ======================================================================== */
-/* Attention on NVFP4 operands ([SSA]: ScaleSearchAttention computes QK^T    */
-/* and PV with NVFP4 operands and FP32 accumulation; IP and the sink cache   */
-/* are applied to the operands beforehand).                                  */
+/* Attention on NVFP4 operands ([SSA] ネイティブ NVFP4 実行: ScaleSearchAttention */
+/* computes QK^T and PV with NVFP4 operands and FP32 accumulation; the IP    */
+/* transform and the sink cache are applied to the operands beforehand).     */
 /*                                                                           */
 /* Readings (the pages give no kernel): Q, K, V are NVFP4 tensors           */
 /* [B][H][N][D] with 16-element blocks along D, each with its own tensor     */
-/* scale; K and V heads may be shared by Hq / Hkv query heads. Operand       */
-/* values are V[code] * s_block (exact in binary32), the tensor scales are   */
-/* applied to the products. Online softmax over key tiles of `tile` keys in  */
-/* order: s_j = tau * Sq * Sk * (q . k_j), tau = 1/sqrt(D); m' = max(m,      */
-/* max_j s_j); p_j = exp(s_j - m') rounded to binary32; l = e^(m-m') l +     */
-/* sum_j p_j. P is quantized to NVFP4 per 16 keys of the tile with max      */
-/* scaling (offset 0) under the fixed tensor scale S_P = fl(1/2688) (the    */
-/* largest possible p is 1), exactly as the quantizer codes a block, and     */
-/* acc = e^(m-m') acc + sum_j P^_j v_j, with P^_j = V[code] * s_block. The   */
-/* output is O = acc * S_P * Sv / l. Keys past Nk are masked; with causal,   */
-/* query i sees keys j <= i + Nk - Nq.                                       */
+/* scale; K and V heads may be shared by Hq / Hkv query heads. An operand   */
+/* element is V[code] * s_block times its tensor scale. Scores              */
+/* s_j = (q . k_j) / sqrt(D). The softmax runs online over the keys in      */
+/* tiles of `tile` keys, in order: m' = max(m, max of the tile's s_j);      */
+/* p_j = exp(s_j - m') rounded to binary32; l = e^(m - m') l + sum_j p_j.    */
+/* P is coded to NVFP4 per 16 keys of a tile with max scaling (offset 0)    */
+/* under the fixed tensor scale S_P = fl(1/2688) (p <= 1), exactly as the    */
+/* quantizer codes a block, and acc = e^(m - m') acc + sum_j P^_j v_j with   */
+/* P^_j = V[code] * s_block; O = acc * S_P / l. Because each tile's p is    */
+/* taken against the running max, the tile size is part of the definition.  */
+/* Keys past Nk are masked; with causal, query i sees keys j <= i + Nk - Nq. */
+/* Everything is evaluated in double except p (binary32, as stated) and the */
+/* coding of P (the quantizer's binary32 rule).                              */
 /*                                                                           */
-/* Besides O the oracle returns, per output element, the magnitude sum       */
-/* mag = S_P Sv / l * sum |P^_j v_jd| (rescaled like acc) and an allowance    */
-/* `bound` for P codes that a binary32 implementation may round the other    */
-/* way: an element whose y = p_j * r lies within the relative error that     */
-/* binary32 scores and exp can put on p_j of an E2M1 rounding midpoint may   */
-/* take the neighbouring code, and a block whose scale argument lies that    */
-/* close to an E4M3 midpoint may take the neighbouring scale; bound sums the */
-/* largest such changes of P^_j times |v_jd|.                                */
+/* Besides O the oracle returns what a comparison with a binary32           */
+/* implementation needs, per output element (in units of O):               */
+/*   mag   sum_j |P^_j v_jd| * S_P / l: what FP32 sums of the products see; */
+/*   rs    the sum over tiles of |acc_d| as each tile starts (after its      */
+/*         rescale): the partial sums an in-order FP32 accumulation rounds;  */
+/*   us    (split keys) sum over units |w_u acc_u,d|: the merge's terms;     */
+/*   bound the largest change of sum_j P^_j |v_jd| from P codes that a       */
+/*         binary32 score and exp could round the other way;                */
+/* and per query row: the number of tiles whose max may move the running    */
+/* max (each a rescale by a rounded exponential), the most tiles one softmax */
+/* state visits, the largest relative error dl binary32 scores and exp can   */
+/* put on a p, and the number of units merged.                              */
 /* ======================================================================== */
 
 static void decode_row(const uint8_t *codes, const uint8_t *scales, int64_t D, float *out)
@@ -957,12 +963,262 @@ static double e2m1_mid_distance(float y, float *gap)
     return best;
 }
 
+/* The flip allowance of one 16-key block of P. pf: the binary32 p values,
+ * dl: each one's relative error allowance, p: the block's scale pattern,
+ * ph: the coded values P^ (without S_P). flip[e] receives the largest
+ * change of P^_e that a p within its allowance could cause:
+ *  - the element's own code, when y = p * r lies within dl of an E2M1
+ *    rounding midpoint: the grid gap there, times the block scale;
+ *  - the block scale, when t = (amax / 6) / S_P lies within the allowance of
+ *    an E4M3 midpoint: the neighbouring pattern p2 may be taken, and each
+ *    element moves to its code under p2 (plus that code's own flip). */
+static void p_block_allowance(const float pf[16], const double dl[16], int p, const float ph[16],
+                              double flip[16])
+{
+    const float SP = 1.0f / 2688.0f;
+    const float sp = oracle_e4m3_value(p);
+    const float r = 1.0f / (sp * SP);
+    float amax_b = 0.0f;
+    double dmax = 0.0;
+    for (int e = 0; e < 16; ++e) {
+        if (pf[e] > amax_b)
+            amax_b = pf[e];
+        if (dl[e] > dmax)
+            dmax = dl[e];
+    }
+    for (int e = 0; e < 16; ++e) {
+        float gap = 0.0f;
+        flip[e] = 0.0;
+        if (pf[e] > 0.0f && e2m1_mid_distance(pf[e] * r, &gap) <= dl[e] + 0x1p-22)
+            flip[e] = (double)gap * sp;
+    }
+    if (amax_b == 0.0f)
+        return;
+    const float tb = (amax_b / 6.0f) / SP;
+    for (int nb = -1; nb <= 1; nb += 2) {
+        const int p2 = p + nb;
+        if (p2 < 0 || p2 > 126)
+            continue;
+        const double mid = 0.5 * ((double)oracle_e4m3_value(p) + oracle_e4m3_value(p2));
+        if (fabs((double)tb - mid) > (dmax + 0x1p-21) * mid)
+            continue;
+        const float sp2 = oracle_e4m3_value(p2);
+        const float r2 = 1.0f / (sp2 * SP);
+        for (int e = 0; e < 16; ++e) {
+            float y2 = pf[e] * r2, gap2 = 0.0f;
+            double dv = fabs((double)E2M1_MAG[oracle_e2m1_code(y2)] * sp2 - ph[e]);
+            if (pf[e] > 0.0f && e2m1_mid_distance(y2, &gap2) <= dl[e] + 0x1p-22)
+                dv += (double)gap2 * sp2;
+            if (dv > flip[e])
+                flip[e] = dv;
+        }
+    }
+}
+
+/* Online-softmax state of one query over a run of keys: running max m, sum
+ * l, and per output element the unnormalized sum acc, its magnitude sum mg,
+ * the flip allowance bd, rs (the partial sums |acc| at tile starts) and mp
+ * (the magnitude sum of the tiles before the last possible rise of the
+ * running max, whose P was coded against an earlier max). nres
+ * counts tiles that may move the running max, ntiles the tiles visited, dmax
+ * is the largest p allowance, arun the largest score magnitude sum
+ * sum_d |q_d k_d| / sqrt(D) of the keys visited. */
+typedef struct {
+    double m, l, dmax, arun;
+    int64_t nres, ntiles;
+    double *acc, *mg, *bd, *rs, *mp;
+} sstate_t;
+
+typedef struct {
+    double *s, *dl, *A;
+    float *pf, *ph;
+} stile_t;
+
+static void state_clear(sstate_t *st, int64_t D)
+{
+    st->m = -INFINITY;
+    st->l = 0.0;
+    st->dmax = 0.0;
+    st->arun = 0.0;
+    st->nres = st->ntiles = 0;
+    for (int64_t d = 0; d < D; ++d)
+        st->acc[d] = st->mg[d] = st->bd[d] = st->rs[d] = st->mp[d] = 0.0;
+}
+
+/* Keys [lo, hi) in tiles of `tile` keys from lo (a last tile may be short),
+ * folded into the state st. kv[t * D + d]: key t with the query's and its
+ * own tensor scale folded in (score = q . kv / sqrt(D)); vv[t * D + d] * vfac[t]:
+ * value t. */
+static void fold_tiles(int64_t D, int64_t tile, const float *q, const double *kv,
+                       const float *vv, const double *vfac, int64_t lo, int64_t hi,
+                       sstate_t *st, stile_t *w)
+{
+    const float SP = 1.0f / 2688.0f;
+    const double tau = 1.0 / sqrt((double)D);
+    double *s = w->s, *dl = w->dl, *A = w->A;
+    float *pf = w->pf, *ph = w->ph;
+    for (int64_t t0 = lo; t0 < hi; t0 += tile) {
+        double mt = -INFINITY, amax_abs = 0.0;
+        for (int64_t u = 0; u < tile; ++u) {
+            int64_t j = t0 + u;
+            s[u] = -INFINITY;
+            A[u] = 0.0;
+            if (j < hi) {
+                double dot = 0.0, ab = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    double pr = (double)q[d] * kv[j * D + d];
+                    dot += pr;
+                    ab += fabs(pr);
+                }
+                s[u] = tau * dot;
+                A[u] = tau * ab;
+                if (s[u] > mt)
+                    mt = s[u];
+                if (A[u] > amax_abs)
+                    amax_abs = A[u];
+            }
+        }
+        if (amax_abs > st->arun)
+            st->arun = amax_abs;
+        double mn = st->m > mt ? st->m : mt;
+        if (mn == -INFINITY)
+            continue;
+        /* a binary32 score carries up to amax_abs (D + 2) 2^-24 of FP32 sum
+           error and a few roundings of s and the max: a tile whose max comes
+           within twice that of the running max may move it there */
+        const double serr = amax_abs * (double)(D + 2) * 0x1p-24 +
+                            (fabs(st->m == -INFINITY ? mt : st->m) + fabs(mt)) * 0x1p-21;
+        const int rise = st->m != -INFINITY && mt + 2.0 * serr >= st->m;
+        if (rise)
+            st->nres += 1;
+        st->ntiles += 1;
+        double alpha = (st->m == -INFINITY) ? 0.0 : exp(st->m - mn);
+        double psum = 0.0;
+        for (int64_t u = 0; u < tile; ++u) {
+            pf[u] = (s[u] == -INFINITY) ? 0.0f : (float)exp(s[u] - mn);
+            psum += pf[u];
+            /* relative error binary32 scores and exp can put on p = exp(s - m):
+               the FP32 sums of s and of the running max's own score (each at
+               most (D + 2) u times its magnitude sum; the max's is at most
+               arun), the roundings of s, m and their difference, and exp */
+            dl[u] = (s[u] == -INFINITY)
+                        ? 0.0
+                        : (A[u] + st->arun) * (double)(D + 2) * 0x1p-24 +
+                              (fabs(s[u]) + fabs(mn)) * 0x1p-21 + 0x1p-20;
+            if (dl[u] > st->dmax)
+                st->dmax = dl[u];
+        }
+        st->l = alpha * st->l + psum;
+        for (int64_t d = 0; d < D; ++d) {
+            st->acc[d] *= alpha;
+            st->mg[d] *= alpha;
+            st->bd[d] *= alpha;
+            st->rs[d] = st->rs[d] * alpha + fabs(st->acc[d]);
+            /* the tiles before a possible rise of the max: their P was coded
+               against a running max other than the final one */
+            st->mp[d] = rise ? st->mg[d] : st->mp[d] * alpha;
+        }
+        for (int64_t u0 = 0; u0 < tile; u0 += 16) {
+            uint8_t cb[8];
+            double flip[16];
+            int p = search_block(pf + u0, SP, 0, 0, cb, NULL);
+            float sp = oracle_e4m3_value(p);
+            for (int e = 0; e < 16; ++e) {
+                int nib = (cb[e / 2] >> ((e & 1) * 4)) & 0xF;
+                ph[u0 + e] = E2M1_MAG[nib & 7] * sp;
+            }
+            p_block_allowance(pf + u0, dl + u0, p, ph + u0, flip);
+            for (int e = 0; e < 16; ++e) {
+                int64_t j = t0 + u0 + e;
+                if (j >= hi || pf[u0 + e] == 0.0f)
+                    continue;
+                for (int64_t d = 0; d < D; ++d) {
+                    double v = (double)vv[j * D + d] * vfac[j];
+                    st->acc[d] += (double)ph[u0 + e] * v;
+                    st->mg[d] += (double)ph[u0 + e] * fabs(v);
+                    st->bd[d] += flip[e] * fabs(v);
+                }
+            }
+        }
+        st->m = mn;
+    }
+}
+
+/* Combine the units' states (O = S_P sum w_u acc_u / sum w_u l_u, w_u =
+ * exp(m_u - M), M = max m_u; a unit with no key has m_u = -inf) into row r
+ * of the outputs. mpre: the magnitude of the keys whose P was coded against a
+ * running max other than the overall one: the tiles before the last possible
+ * rise in the unit that holds M (when no other unit's max comes within dmax
+ * of it), every key of the other units. */
+static void write_row(const sstate_t *us, int64_t nunits, int64_t D, int64_t r, double *O,
+                      double *mag, double *bound, double *rs, double *usum, double *mpre,
+                      double *rowinfo)
+{
+    const double SP = (double)(1.0f / 2688.0f);
+    double M = -INFINITY;
+    int64_t top = -1;
+    for (int64_t u = 0; u < nunits; ++u)
+        if (us[u].m > M) {
+            M = us[u].m;
+            top = u;
+        }
+    double L = 0.0, dmax = 0.0;
+    int64_t nres = 0, ntiles = 0, live = 0;
+    for (int64_t u = 0; u < nunits; ++u) {
+        if (us[u].m == -INFINITY)
+            continue;
+        L += exp(us[u].m - M) * us[u].l;
+        live += 1;
+        if (us[u].nres > nres)
+            nres = us[u].nres;
+        if (us[u].ntiles > ntiles)
+            ntiles = us[u].ntiles;
+        if (us[u].dmax > dmax)
+            dmax = us[u].dmax;
+    }
+    for (int64_t u = 0; u < nunits; ++u)
+        if (u != top && us[u].m != -INFINITY && us[u].m >= M - 2.0 * dmax)
+            top = -1; /* another unit's max may be the largest in binary32 */
+    double f = (L > 0.0) ? SP / L : 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+        double o = 0.0, mg = 0.0, bd = 0.0, r2 = 0.0, ua = 0.0, mp = 0.0;
+        for (int64_t u = 0; u < nunits; ++u) {
+            if (us[u].m == -INFINITY)
+                continue;
+            double wu = exp(us[u].m - M);
+            o += wu * us[u].acc[d];
+            mg += wu * us[u].mg[d];
+            bd += wu * us[u].bd[d];
+            r2 += wu * us[u].rs[d];
+            ua += fabs(wu * us[u].acc[d]);
+            mp += wu * (u == top ? us[u].mp[d] : us[u].mg[d]);
+        }
+        O[r * D + d] = o * f;
+        if (mag)
+            mag[r * D + d] = mg * f;
+        if (bound)
+            bound[r * D + d] = bd * f;
+        if (rs)
+            rs[r * D + d] = r2 * f;
+        if (usum)
+            usum[r * D + d] = live > 1 ? ua * f : 0.0;
+        if (mpre)
+            mpre[r * D + d] = live > 1 ? mp * f : us[top < 0 ? 0 : top].mp[d] * f;
+    }
+    if (rowinfo) {
+        rowinfo[4 * r + 0] = (double)nres;
+        rowinfo[4 * r + 1] = (double)ntiles;
+        rowinfo[4 * r + 2] = dmax;
+        rowinfo[4 * r + 3] = (double)live;
+    }
+}
+
 typedef struct {
     const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
     float qg, kg, vg;
     int64_t B, Hq, Hkv, Nq, Nk, D, tile;
     int causal;
-    double *O, *mag, *bound;
+    double *O, *mag, *bound, *rs, *usum, *mpre, *rowinfo;
     int64_t r0, r1; /* rows (b, h, i) of this job */
 } ajob_t;
 
@@ -970,16 +1226,16 @@ static void *attention_rows(void *arg)
 {
     const ajob_t *J = (const ajob_t *)arg;
     const int64_t D = J->D, Nk = J->Nk, T = J->tile;
-    const float SP = 1.0f / 2688.0f;
-    const double c = (1.0 / sqrt((double)D)) * (double)J->qg * (double)J->kg;
-    float *q = malloc(sizeof(float) * D);
-    float *kv = malloc(sizeof(float) * D * (size_t)(Nk > 0 ? Nk : 1));
-    float *vv = malloc(sizeof(float) * D * (size_t)(Nk > 0 ? Nk : 1));
-    double *acc = malloc(sizeof(double) * D), *mg = malloc(sizeof(double) * D);
-    double *bd = malloc(sizeof(double) * D);
-    double *s = malloc(sizeof(double) * T), *A = malloc(sizeof(double) * T);
-    float *pf = malloc(sizeof(float) * T), *ph = malloc(sizeof(float) * T);
-    double *dl = malloc(sizeof(double) * T);
+    const double qk = (double)J->qg * (double)J->kg;
+    const size_t nk = (size_t)(Nk > 0 ? Nk : 1);
+    float *q = malloc(sizeof(float) * D), *tmp = malloc(sizeof(float) * D);
+    double *kv = malloc(sizeof(double) * D * nk);
+    float *vv = malloc(sizeof(float) * D * nk);
+    double *vfac = malloc(sizeof(double) * nk);
+    double *sbuf = malloc(sizeof(double) * 5 * D);
+    sstate_t st = {0, 0, 0, 0, 0, 0, sbuf, sbuf + D, sbuf + 2 * D, sbuf + 3 * D, sbuf + 4 * D};
+    stile_t w = {malloc(sizeof(double) * T), malloc(sizeof(double) * T),
+                 malloc(sizeof(double) * T), malloc(sizeof(float) * T), malloc(sizeof(float) * T)};
     int64_t cached_head = -1;
     for (int64_t r = J->r0; r < J->r1; ++r) {
         int64_t i = r % J->Nq, bh = r / J->Nq;
@@ -988,132 +1244,26 @@ static void *attention_rows(void *arg)
         if (kvh != cached_head) {
             for (int64_t j = 0; j < Nk; ++j) {
                 int64_t row = kvh * Nk + j;
-                decode_row(J->kc + row * (D / 2), J->ks + row * (D / 16), D, kv + j * D);
+                decode_row(J->kc + row * (D / 2), J->ks + row * (D / 16), D, tmp);
+                for (int64_t d = 0; d < D; ++d)
+                    kv[j * D + d] = (double)tmp[d] * qk;
                 decode_row(J->vc + row * (D / 2), J->vs + row * (D / 16), D, vv + j * D);
+                vfac[j] = (double)J->vg;
             }
             cached_head = kvh;
         }
         decode_row(J->qc + r * (D / 2), J->qs + r * (D / 16), D, q);
-        int64_t jmax = J->causal ? i + Nk - J->Nq : Nk - 1; /* last visible key */
-        double m = -INFINITY, l = 0.0;
-        for (int64_t d = 0; d < D; ++d)
-            acc[d] = mg[d] = bd[d] = 0.0;
-        for (int64_t t0 = 0; t0 < Nk; t0 += T) {
-            double mt = -INFINITY, amax_abs = 0.0;
-            for (int64_t u = 0; u < T; ++u) {
-                int64_t j = t0 + u;
-                s[u] = -INFINITY;
-                A[u] = 0.0;
-                if (j < Nk && j <= jmax) {
-                    double dot = 0.0, ab = 0.0;
-                    for (int64_t d = 0; d < D; ++d) {
-                        double pr = (double)q[d] * (double)kv[j * D + d];
-                        dot += pr;
-                        ab += fabs(pr);
-                    }
-                    s[u] = c * dot;
-                    A[u] = c * ab;
-                    if (s[u] > mt)
-                        mt = s[u];
-                    if (A[u] > amax_abs)
-                        amax_abs = A[u];
-                }
-            }
-            double mn = m > mt ? m : mt;
-            if (mn == -INFINITY)
-                continue; /* nothing visible yet */
-            double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
-            double psum = 0.0;
-            for (int64_t u = 0; u < T; ++u) {
-                pf[u] = (s[u] == -INFINITY) ? 0.0f : (float)exp(s[u] - mn);
-                psum += pf[u];
-                /* relative error a binary32 score and exp can put on p */
-                dl[u] = amax_abs * (double)(D + 2) * 0x1p-24 + (fabs(s[u]) + fabs(mn)) * 0x1p-21 +
-                        0x1p-20;
-                if (s[u] == -INFINITY)
-                    dl[u] = 0.0;
-            }
-            l = alpha * l + psum;
-            for (int64_t d = 0; d < D; ++d) {
-                acc[d] *= alpha;
-                mg[d] *= alpha;
-                bd[d] *= alpha;
-            }
-            for (int64_t u0 = 0; u0 < T; u0 += 16) {
-                uint8_t cb[8];
-                int p = search_block(pf + u0, SP, 0, 0, cb, NULL);
-                float sp = oracle_e4m3_value(p);
-                float r = 1.0f / (sp * SP);
-                float amax_b = 0.0f;
-                double dmax = 0.0;
-                for (int e = 0; e < 16; ++e) {
-                    int nib = (cb[e / 2] >> ((e & 1) * 4)) & 0xF;
-                    ph[u0 + e] = E2M1_MAG[nib & 7] * sp;
-                    if (pf[u0 + e] > amax_b)
-                        amax_b = pf[u0 + e];
-                    if (dl[u0 + e] > dmax)
-                        dmax = dl[u0 + e];
-                }
-                /* allowance per element */
-                double flip[16];
-                for (int e = 0; e < 16; ++e) {
-                    flip[e] = 0.0;
-                    float gap = 0.0f;
-                    float y = pf[u0 + e] * r;
-                    if (pf[u0 + e] > 0.0f && e2m1_mid_distance(y, &gap) <= dl[u0 + e] + 0x1p-22)
-                        flip[e] = (double)gap * sp;
-                }
-                /* the block scale: t within reach of an E4M3 midpoint */
-                float tb = (amax_b / 6.0f) / SP;
-                if (amax_b > 0.0f) {
-                    for (int nb = -1; nb <= 1; nb += 2) {
-                        int p2 = p + nb;
-                        if (p2 < 0 || p2 > 126)
-                            continue;
-                        double mid = 0.5 * ((double)oracle_e4m3_value(p) + oracle_e4m3_value(p2));
-                        if (fabs((double)tb - mid) <= (dmax + 0x1p-21) * mid) {
-                            float sp2 = oracle_e4m3_value(p2);
-                            float r2 = 1.0f / (sp2 * SP);
-                            for (int e = 0; e < 16; ++e) {
-                                float y2 = pf[u0 + e] * r2, gap2 = 0.0f;
-                                int c2 = oracle_e2m1_code(y2);
-                                double alt = (double)E2M1_MAG[c2] * sp2;
-                                double dv = fabs(alt - ph[u0 + e]);
-                                /* and the element's own flip under that scale */
-                                if (pf[u0 + e] > 0.0f &&
-                                    e2m1_mid_distance(y2, &gap2) <= dl[u0 + e] + 0x1p-22)
-                                    dv += (double)gap2 * sp2;
-                                if (dv > flip[e])
-                                    flip[e] = dv;
-                            }
-                        }
-                    }
-                }
-                for (int e = 0; e < 16; ++e) {
-                    int64_t j = t0 + u0 + e;
-                    if (j >= Nk || pf[u0 + e] == 0.0f)
-                        continue;
-                    for (int64_t d = 0; d < D; ++d) {
-                        double v = vv[j * D + d];
-                        acc[d] += (double)ph[u0 + e] * v;
-                        mg[d] += (double)ph[u0 + e] * fabs(v);
-                        bd[d] += flip[e] * fabs(v);
-                    }
-                }
-            }
-            m = mn;
-        }
-        double f = (l > 0.0) ? (double)SP * (double)J->vg / l : 0.0;
-        for (int64_t d = 0; d < D; ++d) {
-            J->O[r * D + d] = acc[d] * f;
-            if (J->mag)
-                J->mag[r * D + d] = mg[d] * f;
-            if (J->bound)
-                J->bound[r * D + d] = bd[d] * f;
-        }
+        /* visible keys: [0, Nk), or with causal [0, i + Nk - Nq] */
+        int64_t hi = J->causal ? i + Nk - J->Nq + 1 : Nk;
+        if (hi > Nk)
+            hi = Nk;
+        state_clear(&st, D);
+        if (hi > 0)
+            fold_tiles(D, T, q, kv, vv, vfac, 0, hi, &st, &w);
+        write_row(&st, 1, D, r, J->O, J->mag, J->bound, J->rs, J->usum, J->mpre, J->rowinfo);
     }
-    free(q); free(kv); free(vv); free(acc); free(mg); free(bd);
-    free(s); free(A); free(pf); free(ph); free(dl);
+    free(q); free(tmp); free(kv); free(vv); free(vfac); free(sbuf);
+    free(w.s); free(w.dl); free(w.A); free(w.pf); free(w.ph);
     return NULL;
 }
 
@@ -1121,7 +1271,8 @@ int oracle_attention_nvfp4(const uint8_t *qc, const uint8_t *qs, float qg, const
                            const uint8_t *ks, float kg, const uint8_t *vc, const uint8_t *vs,
                            float vg, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                            int64_t D, int64_t tile, int causal, double *O, double *mag,
-                           double *bound, int nthreads)
+                           double *bound, double *rs, double *usum, double *mpre, double *rowinfo,
+                           int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || Nk < 0 || D <= 0 || D % 16 ||
         tile <= 0 || tile % 16 || !O)
@@ -1140,7 +1291,8 @@ int oracle_attention_nvfp4(const uint8_t *qc, const uint8_t *qs, float qg, const
     ajob_t jobs[256];
     for (int t = 0; t < nthreads; ++t) {
         jobs[t] = (ajob_t){qc, qs, kc, ks, vc, vs, qg, kg, vg, B, Hq, Hkv, Nq, Nk, D, tile,
-                           causal, O, mag, bound, rows * t / nthreads, rows * (t + 1) / nthreads};
+                           causal, O, mag, bound, rs, usum, mpre, rowinfo, rows * t / nthreads,
+                           rows * (t + 1) / nthreads};
         running[t] = nthreads > 1 && pthread_create(&th[t], NULL, attention_rows, &jobs[t]) == 0;
         if (!running[t])
             attention_rows(&jobs[t]);
@@ -1152,19 +1304,20 @@ int oracle_attention_nvfp4(const uint8_t *qc, const uint8_t *qs, float qg, const
 }
 
 /* ------------------------------------------------------------------------ */
-/* Attention over the attention-sink KV cache ([SSA]: the first and last KV  */
-/* blocks stay in full precision, the middle is NVFP4). The cache holds T    */
-/* tokens: token t < n_first in head[t], t >= max(n_first, T - n_last) in    */
-/* the ring tail[t mod n_last] (bf16), the rest coded at middle row          */
-/* t - n_first under the tensor scale. Reading: keys are visited segment by  */
-/* segment (head, middle, tail, each in token order) in tiles of `tile`      */
-/* keys that never straddle two segments (a segment's last tile may be       */
-/* short); everything else is the attention above. All T keys are visible.  */
+/* Attention over the attention-sink KV cache ([SSA] アテンション・シンク対応  */
+/* 混合精度キャッシング: the first and last KV blocks stay in full precision, */
+/* the middle is NVFP4). The cache holds T tokens: token t < n_first in      */
+/* head[t], t >= max(n_first, T - n_last) in the ring tail[t mod n_last]     */
+/* (bf16), the rest coded at middle row t - n_first under the tensor scale.  */
+/* Reading: keys are visited segment by segment (head, middle, tail, each in */
+/* token order) in tiles of `tile` keys that never straddle two segments (a */
+/* segment's last tile may be short); everything else is the attention      */
+/* above. All T keys are visible.                                            */
 /*                                                                          */
 /* Split keys (split > 0, a multiple of the tile). The pages describe the   */
-/* attention's online softmax but not how a kernel spreads one query's keys */
-/* over parallel workers; this reading lets a decode step with few queries  */
-/* do so. The keys fall into units: the head, the tail, and the middle cut  */
+/* attention's online softmax but not how one query's keys are spread over  */
+/* parallel workers; this reading lets a decode step with few queries do    */
+/* so. The keys fall into units: the head, the tail, and the middle cut     */
 /* into pieces of `split` tokens from n_first (the last may be short). Each */
 /* unit runs the online softmax and the coding of P above from its own      */
 /* running max, alone; the unit states (m_u, l_u, acc_u) then combine       */
@@ -1178,170 +1331,40 @@ typedef struct {
     const uint8_t *kc, *ks, *vc, *vs;
     float kg, vg;
     int64_t B, Hq, Hkv, Nq, T, D, nf, nl, cap, tile, split;
-    double *O, *mag, *bound;
+    double *O, *mag, *bound, *rs, *usum, *mpre, *rowinfo;
     int64_t r0, r1;
 } cjob_t;
-
-/* Online-softmax state of one query: running max m, sum l, and per output
- * element the unnormalized sum acc, its magnitude sum mg and allowance bd. */
-typedef struct {
-    double m, l;
-    double *acc, *mg, *bd;
-} sstate_t;
-
-typedef struct {
-    double *s, *dl;
-    float *pf, *ph;
-} stile_t;
-
-/* Keys [lo, hi) of the cache in tiles of `tile` keys from lo (a last tile may
- * be short), folded into the state st: the attention of the oracle above, with
- * kv[t] the key in units that fold the query scale (and for coded keys the K
- * tensor scale) in, and vv[t] * vfac[t] the value. */
-static void cache_tiles(const cjob_t *J, const float *q, const double *kv, const float *vv,
-                        const double *vfac, int64_t lo, int64_t hi, sstate_t *st, stile_t *w)
-{
-    const int64_t D = J->D, tile = J->tile;
-    const float SP = 1.0f / 2688.0f;
-    const double tau = 1.0 / sqrt((double)D);
-    double *s = w->s, *dl = w->dl;
-    float *pf = w->pf, *ph = w->ph;
-    for (int64_t t0 = lo; t0 < hi; t0 += tile) {
-        double mt = -INFINITY, amax_abs = 0.0;
-        for (int64_t u = 0; u < tile; ++u) {
-            int64_t j = t0 + u;
-            s[u] = -INFINITY;
-            if (j < hi) {
-                double dot = 0.0, ab = 0.0;
-                for (int64_t d = 0; d < D; ++d) {
-                    double pr = (double)q[d] * kv[j * D + d];
-                    dot += pr;
-                    ab += fabs(pr);
-                }
-                s[u] = tau * dot;
-                if (s[u] > mt)
-                    mt = s[u];
-                if (tau * ab > amax_abs)
-                    amax_abs = tau * ab;
-            }
-        }
-        double mn = st->m > mt ? st->m : mt;
-        if (mn == -INFINITY)
-            continue;
-        double alpha = (st->m == -INFINITY) ? 0.0 : exp(st->m - mn);
-        double psum = 0.0;
-        for (int64_t u = 0; u < tile; ++u) {
-            pf[u] = (s[u] == -INFINITY) ? 0.0f : (float)exp(s[u] - mn);
-            psum += pf[u];
-            dl[u] = (s[u] == -INFINITY) ? 0.0
-                                        : amax_abs * (double)(D + 2) * 0x1p-24 +
-                                              (fabs(s[u]) + fabs(mn)) * 0x1p-21 + 0x1p-20;
-        }
-        st->l = alpha * st->l + psum;
-        for (int64_t d = 0; d < D; ++d) {
-            st->acc[d] *= alpha;
-            st->mg[d] *= alpha;
-            st->bd[d] *= alpha;
-        }
-        for (int64_t u0 = 0; u0 < tile; u0 += 16) {
-            uint8_t cb[8];
-            int p = search_block(pf + u0, SP, 0, 0, cb, NULL);
-            float sp = oracle_e4m3_value(p);
-            float rr = 1.0f / (sp * SP);
-            float amax_b = 0.0f;
-            double dmax = 0.0, flip[16];
-            for (int e = 0; e < 16; ++e) {
-                int nib = (cb[e / 2] >> ((e & 1) * 4)) & 0xF;
-                ph[u0 + e] = E2M1_MAG[nib & 7] * sp;
-                if (pf[u0 + e] > amax_b)
-                    amax_b = pf[u0 + e];
-                if (dl[u0 + e] > dmax)
-                    dmax = dl[u0 + e];
-            }
-            for (int e = 0; e < 16; ++e) {
-                float gap = 0.0f;
-                flip[e] = 0.0;
-                if (pf[u0 + e] > 0.0f &&
-                    e2m1_mid_distance(pf[u0 + e] * rr, &gap) <= dl[u0 + e] + 0x1p-22)
-                    flip[e] = (double)gap * sp;
-            }
-            float tb = (amax_b / 6.0f) / SP;
-            if (amax_b > 0.0f) {
-                for (int nb = -1; nb <= 1; nb += 2) {
-                    int p2 = p + nb;
-                    if (p2 < 0 || p2 > 126)
-                        continue;
-                    double mid = 0.5 * ((double)oracle_e4m3_value(p) + oracle_e4m3_value(p2));
-                    if (fabs((double)tb - mid) <= (dmax + 0x1p-21) * mid) {
-                        float sp2 = oracle_e4m3_value(p2);
-                        float r2 = 1.0f / (sp2 * SP);
-                        for (int e = 0; e < 16; ++e) {
-                            float y2 = pf[u0 + e] * r2, gap2 = 0.0f;
-                            int c2 = oracle_e2m1_code(y2);
-                            double dv = fabs((double)E2M1_MAG[c2] * sp2 - ph[u0 + e]);
-                            if (pf[u0 + e] > 0.0f &&
-                                e2m1_mid_distance(y2, &gap2) <= dl[u0 + e] + 0x1p-22)
-                                dv += (double)gap2 * sp2;
-                            if (dv > flip[e])
-                                flip[e] = dv;
-                        }
-                    }
-                }
-            }
-            for (int e = 0; e < 16; ++e) {
-                int64_t j = t0 + u0 + e;
-                if (j >= hi || pf[u0 + e] == 0.0f)
-                    continue;
-                for (int64_t d = 0; d < D; ++d) {
-                    double v = (double)vv[j * D + d] * vfac[j];
-                    st->acc[d] += (double)ph[u0 + e] * v;
-                    st->mg[d] += (double)ph[u0 + e] * fabs(v);
-                    st->bd[d] += flip[e] * fabs(v);
-                }
-            }
-        }
-        st->m = mn;
-    }
-}
-
-static void state_clear(sstate_t *st, int64_t D)
-{
-    st->m = -INFINITY;
-    st->l = 0.0;
-    for (int64_t d = 0; d < D; ++d)
-        st->acc[d] = st->mg[d] = st->bd[d] = 0.0;
-}
 
 static void *attention_cache_rows(void *arg)
 {
     const cjob_t *J = (const cjob_t *)arg;
     const int64_t D = J->D, T = J->T, tile = J->tile;
-    const double SP = (double)(1.0f / 2688.0f);
-    float *q = malloc(sizeof(float) * D);
+    float *q = malloc(sizeof(float) * D), *tmp = malloc(sizeof(float) * D);
     double *kv = malloc(sizeof(double) * D * (size_t)(T > 0 ? T : 1));
     float *vv = malloc(sizeof(float) * D * (size_t)(T > 0 ? T : 1));
     double *vfac = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
     stile_t w = {malloc(sizeof(double) * tile), malloc(sizeof(double) * tile),
-                 malloc(sizeof(float) * tile), malloc(sizeof(float) * tile)};
+                 malloc(sizeof(double) * tile), malloc(sizeof(float) * tile),
+                 malloc(sizeof(float) * tile)};
     const int64_t mid_lo = J->nf, mid_hi = T - J->nl > J->nf ? T - J->nl : J->nf;
     /* the units whose softmax states are combined: the three segments folded
        into one state (no split), or head, each piece of `split` middle keys and
        tail each with its own state */
     const int64_t npieces = J->split > 0 ? (mid_hi - mid_lo + J->split - 1) / J->split : 0;
     const int64_t nunits = J->split > 0 ? 2 + npieces : 1;
-    double *ubuf = malloc(sizeof(double) * (size_t)(3 * D * nunits + 1));
+    double *ubuf = malloc(sizeof(double) * (size_t)(5 * D * nunits + 1));
     sstate_t *us = malloc(sizeof(sstate_t) * (size_t)nunits);
-    for (int64_t u = 0; u < nunits; ++u)
-        us[u] = (sstate_t){-INFINITY, 0.0, ubuf + 3 * D * u, ubuf + 3 * D * u + D,
-                           ubuf + 3 * D * u + 2 * D};
+    for (int64_t u = 0; u < nunits; ++u) {
+        double *b = ubuf + 5 * D * u;
+        us[u] = (sstate_t){0, 0, 0, 0, 0, 0, b, b + D, b + 2 * D, b + 3 * D, b + 4 * D};
+    }
     int64_t cached = -1;
     for (int64_t r = J->r0; r < J->r1; ++r) {
         int64_t bh = r / J->Nq;
         int64_t b = bh / J->Hq, h = bh % J->Hq;
         int64_t kvh = b * J->Hkv + h / (J->Hq / J->Hkv);
         if (kvh != cached) {
-            /* key t: kv = its value in units of the factor kfac (head/tail 1, middle Sk);
-               the score scale folds the factor in, as the kernel does */
+            /* key t with the query's tensor scale (and a coded key's own) folded in */
             for (int64_t t = 0; t < T; ++t) {
                 double *kd = kv + t * D;
                 float *vd = vv + t * D;
@@ -1361,10 +1384,9 @@ static void *attention_cache_rows(void *arg)
                     vfac[t] = 1.0;
                 } else {
                     int64_t row = kvh * J->cap + (t - J->nf);
-                    float tmp[1024];
                     decode_row(J->kc + row * (D / 2), J->ks + row * (D / 16), D, tmp);
                     for (int64_t d = 0; d < D; ++d)
-                        kd[d] = (double)tmp[d] * (double)J->kg * (double)J->qg;
+                        kd[d] = (double)tmp[d] * ((double)J->kg * (double)J->qg);
                     decode_row(J->vc + row * (D / 2), J->vs + row * (D / 16), D, vd);
                     vfac[t] = (double)J->vg;
                 }
@@ -1374,51 +1396,25 @@ static void *attention_cache_rows(void *arg)
         decode_row(J->qc + r * (D / 2), J->qs + r * (D / 16), D, q);
         const int64_t head_hi = J->nf < T ? J->nf : T;
         const int64_t tail_lo = mid_hi > J->nf ? mid_hi : J->nf;
+        for (int64_t u = 0; u < nunits; ++u)
+            state_clear(&us[u], D);
         if (J->split <= 0) {
-            state_clear(&us[0], D);
-            cache_tiles(J, q, kv, vv, vfac, 0, head_hi, &us[0], &w);
-            cache_tiles(J, q, kv, vv, vfac, mid_lo, mid_hi, &us[0], &w);
-            cache_tiles(J, q, kv, vv, vfac, tail_lo, T, &us[0], &w);
+            fold_tiles(D, tile, q, kv, vv, vfac, 0, head_hi, &us[0], &w);
+            fold_tiles(D, tile, q, kv, vv, vfac, mid_lo, mid_hi, &us[0], &w);
+            fold_tiles(D, tile, q, kv, vv, vfac, tail_lo, T, &us[0], &w);
         } else {
-            state_clear(&us[0], D);
-            cache_tiles(J, q, kv, vv, vfac, 0, head_hi, &us[0], &w);
-            state_clear(&us[1], D);
-            cache_tiles(J, q, kv, vv, vfac, tail_lo, T, &us[1], &w);
+            fold_tiles(D, tile, q, kv, vv, vfac, 0, head_hi, &us[0], &w);
+            fold_tiles(D, tile, q, kv, vv, vfac, tail_lo, T, &us[1], &w);
             for (int64_t k = 0; k < npieces; ++k) {
                 int64_t lo = mid_lo + k * J->split, hi = lo + J->split;
-                state_clear(&us[2 + k], D);
-                cache_tiles(J, q, kv, vv, vfac, lo, hi < mid_hi ? hi : mid_hi, &us[2 + k], &w);
+                fold_tiles(D, tile, q, kv, vv, vfac, lo, hi < mid_hi ? hi : mid_hi, &us[2 + k],
+                           &w);
             }
         }
-        /* combine: weights exp(m_u - M); a unit with no key has m_u = -inf */
-        double M = -INFINITY;
-        for (int64_t u = 0; u < nunits; ++u)
-            if (us[u].m > M)
-                M = us[u].m;
-        double L = 0.0;
-        for (int64_t u = 0; u < nunits; ++u)
-            if (us[u].m > -INFINITY)
-                L += exp(us[u].m - M) * us[u].l;
-        double f = (L > 0.0) ? SP / L : 0.0;
-        for (int64_t d = 0; d < D; ++d) {
-            double o = 0.0, mg = 0.0, bd = 0.0;
-            for (int64_t u = 0; u < nunits; ++u) {
-                if (us[u].m == -INFINITY)
-                    continue;
-                double wu = exp(us[u].m - M);
-                o += wu * us[u].acc[d];
-                mg += wu * us[u].mg[d];
-                bd += wu * us[u].bd[d];
-            }
-            J->O[r * D + d] = o * f;
-            if (J->mag)
-                J->mag[r * D + d] = mg * f;
-            if (J->bound)
-                J->bound[r * D + d] = bd * f;
-        }
+        write_row(us, nunits, D, r, J->O, J->mag, J->bound, J->rs, J->usum, J->mpre, J->rowinfo);
     }
-    free(q); free(kv); free(vv); free(vfac); free(ubuf); free(us);
-    free(w.s); free(w.dl); free(w.pf); free(w.ph);
+    free(q); free(tmp); free(kv); free(vv); free(vfac); free(ubuf); free(us);
+    free(w.s); free(w.dl); free(w.A); free(w.pf); free(w.ph);
     return NULL;
 }
 
@@ -1428,6 +1424,7 @@ int oracle_attention_kv_cache(const uint8_t *qc, const uint8_t *qs, float qg, co
                               const uint8_t *vs, float vg, int64_t B, int64_t Hq, int64_t Hkv,
                               int64_t Nq, int64_t T, int64_t D, int64_t nf, int64_t nl, int64_t cap,
                               int64_t tile, int64_t split, double *O, double *mag, double *bound,
+                              double *rs, double *usum, double *mpre, double *rowinfo,
                               int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || T < 0 || D <= 0 || D % 16 ||
@@ -1451,8 +1448,8 @@ int oracle_attention_kv_cache(const uint8_t *qc, const uint8_t *qs, float qg, co
     cjob_t jobs[256];
     for (int t = 0; t < nthreads; ++t) {
         jobs[t] = (cjob_t){qc, qs, qg, kh, kt, vh, vt, kc, ks, vc, vs, kg, vg, B, Hq, Hkv, Nq, T,
-                           D, nf, nl, cap, tile, split, O, mag, bound, rows * t / nthreads,
-                           rows * (t + 1) / nthreads};
+                           D, nf, nl, cap, tile, split, O, mag, bound, rs, usum, mpre, rowinfo,
+                           rows * t / nthreads, rows * (t + 1) / nthreads};
         running[t] = nthreads > 1 && pthread_create(&th[t], NULL, attention_cache_rows, &jobs[t]) == 0;
         if (!running[t])
             attention_cache_rows(&jobs[t]);

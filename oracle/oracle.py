@@ -85,11 +85,13 @@ def lib() -> ctypes.CDLL:
             L.oracle_mx_block_sse.argtypes = [vp, i32]
             L.oracle_mx_block_sse.restype = f32
             L.oracle_attention_nvfp4.argtypes = [vp, vp, f32, vp, vp, f32, vp, vp, f32, i64, i64,
-                                                 i64, i64, i64, i64, i64, i32, vp, vp, vp, i32]
+                                                 i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp,
+                                                 vp, vp, i32]
             L.oracle_attention_nvfp4.restype = i32
             L.oracle_attention_kv_cache.argtypes = [vp, vp, f32, vp, vp, vp, vp, f32, vp, vp, vp,
                                                     vp, f32, i64, i64, i64, i64, i64, i64, i64,
-                                                    i64, i64, i64, i64, vp, vp, vp, i32]
+                                                    i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                                    vp, i32]
             L.oracle_attention_kv_cache.restype = i32
             _lib = L
     return _lib
@@ -290,10 +292,25 @@ def mx_block_sse(x32, X: int) -> float:
     return float(np.float32(lib().oracle_mx_block_sse(_ptr(x), int(X))))
 
 
-def attention_nvfp4(q, k, v, tile: int = 32, causal: bool = False, nthreads: int | None = None):
+def _attention_terms(O, rs, us, mp, rowinfo):
+    """The comparison terms the attention oracle returns beside O: per element rs (sum
+    over tiles of |acc| at each tile's start), us (split keys: sum over units of
+    |w_u acc_u|) and mp (magnitude sum of the keys whose P was coded against a running
+    max other than the final one), all in units of O; per query row nres (tiles that
+    may move the running max), ntiles (most tiles one softmax state visits), dmax
+    (largest relative error allowance on a p) and units (softmax states merged)."""
+    shp = O.shape[:-1]
+    ri = rowinfo.reshape(*shp, 4)
+    return {"rs": rs, "us": us, "mp": mp, "nres": ri[..., 0], "ntiles": ri[..., 1],
+            "dmax": ri[..., 2], "units": ri[..., 3]}
+
+
+def attention_nvfp4(q, k, v, tile: int = 32, causal: bool = False, nthreads: int | None = None,
+                    terms: bool = False):
     """Attention on NVFP4 operands. q, k, v: (codes [B,H,N,D/2] u8, scales [B,H,N,D/16] u8,
     tensor scale); k and v may have fewer heads (shared by groups of query heads).
-    Returns (O, mag, bound) as float64 [B, Hq, Nq, D]."""
+    Returns (O, mag, bound) as float64 [B, Hq, Nq, D], and with terms=True a fourth item,
+    the dict of _attention_terms."""
     qc, qs, qg = q
     kc, ks, kg = k
     vc, vs, vg = v
@@ -302,25 +319,28 @@ def attention_nvfp4(q, k, v, tile: int = 32, causal: bool = False, nthreads: int
     B, Hq, Nq, D2 = qc.shape
     Hkv, Nk = kc.shape[1], kc.shape[2]
     D = D2 * 2
-    O = np.empty((B, Hq, Nq, D), np.float64)
-    mag = np.empty_like(O)
-    bound = np.empty_like(O)
+    O = np.zeros((B, Hq, Nq, D), np.float64)
+    mag, bound, rs, us, mp = (np.zeros_like(O) for _ in range(5))
+    rowinfo = np.zeros((B, Hq, Nq, 4), np.float64)
     rc = lib().oracle_attention_nvfp4(_ptr(qc), _ptr(qs), float(qg), _ptr(kc), _ptr(ks), float(kg),
                                       _ptr(vc), _ptr(vs), float(vg), B, Hq, Hkv, Nq, Nk, D, tile,
-                                      int(causal), _ptr(O), _ptr(mag), _ptr(bound),
-                                      _threads(nthreads))
+                                      int(causal), _ptr(O), _ptr(mag), _ptr(bound), _ptr(rs),
+                                      _ptr(us), _ptr(mp), _ptr(rowinfo), _threads(nthreads))
     if rc:
         raise ValueError(f"oracle_attention_nvfp4 failed ({rc})")
+    if terms:
+        return O, mag, bound, _attention_terms(O, rs, us, mp, rowinfo)
     return O, mag, bound
 
 
 def attention_kv_cache(q, k, v, T: int, n_first: int, n_last: int, tile: int = 32,
-                       split: int = 0, nthreads: int | None = None):
+                       split: int = 0, nthreads: int | None = None, terms: bool = False):
     """Attention over the attention-sink KV cache. q: (codes, scales, tensor scale) of
     [B, Hq, Nq, D]; k, v: dicts with head [B,H,nf,D], tail [B,H,nl,D] (bf16 bits, ring by
     token mod nl), codes [B,H,cap,D/2], scales [B,H,cap,D/16], gscale. split > 0 (a
     multiple of tile): head, tail and each piece of `split` middle tokens run their
-    softmax alone and are combined. Returns (O, mag, bound)."""
+    softmax alone and are combined. Returns (O, mag, bound), and with terms=True the dict
+    of _attention_terms as a fourth item."""
     qc, qs, qg = q
     qc = np.ascontiguousarray(qc, dtype=np.uint8)
     qs = np.ascontiguousarray(qs, dtype=np.uint8)
@@ -331,15 +351,17 @@ def attention_kv_cache(q, k, v, T: int, n_first: int, n_last: int, tile: int = 3
     arr = lambda a, dt: np.ascontiguousarray(a, dtype=dt)
     kh, kt, vh, vt = (arr(x, np.uint16) for x in (k["head"], k["tail"], v["head"], v["tail"]))
     kc, ks, vc, vs = (arr(x, np.uint8) for x in (k["codes"], k["scales"], v["codes"], v["scales"]))
-    O = np.empty((B, Hq, Nq, D), np.float64)
-    mag = np.empty_like(O)
-    bound = np.empty_like(O)
+    O = np.zeros((B, Hq, Nq, D), np.float64)
+    mag, bound, rs, us, mp = (np.zeros_like(O) for _ in range(5))
+    rowinfo = np.zeros((B, Hq, Nq, 4), np.float64)
     rc = lib().oracle_attention_kv_cache(_ptr(qc), _ptr(qs), float(qg), _ptr(kh), _ptr(kt),
                                          _ptr(kc), _ptr(ks), float(k["gscale"]), _ptr(vh),
                                          _ptr(vt), _ptr(vc), _ptr(vs), float(v["gscale"]), B, Hq,
                                          Hkv, Nq, T, D, n_first, n_last, cap, tile, split,
-                                         _ptr(O),
-                                         _ptr(mag), _ptr(bound), _threads(nthreads))
+                                         _ptr(O), _ptr(mag), _ptr(bound), _ptr(rs), _ptr(us),
+                                         _ptr(mp), _ptr(rowinfo), _threads(nthreads))
     if rc:
         raise ValueError(f"oracle_attention_kv_cache failed ({rc})")
+    if terms:
+        return O, mag, bound, _attention_terms(O, rs, us, mp, rowinfo)
     return O, mag, bound

@@ -26,13 +26,13 @@ int oracle_dequantize_mxfp4(const uint8_t *, const uint8_t *, int64_t, int64_t, 
 int oracle_attention_nvfp4(const uint8_t *, const uint8_t *, float, const uint8_t *,
                            const uint8_t *, float, const uint8_t *, const uint8_t *, float, int64_t,
                            int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int, double *,
-                           double *, double *, int);
+                           double *, double *, double *, double *, double *, double *, int);
 int oracle_attention_kv_cache(const uint8_t *, const uint8_t *, float, const uint16_t *,
                               const uint16_t *, const uint8_t *, const uint8_t *, float,
                               const uint16_t *, const uint16_t *, const uint8_t *,
                               const uint8_t *, float, int64_t, int64_t, int64_t, int64_t, int64_t,
                               int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, double *,
-                              double *, double *, int);
+                              double *, double *, double *, double *, double *, double *, int);
 
 static uint64_t state = 88172645463325252ull;
 static double uniform(void) { /* xorshift64 */
@@ -98,19 +98,21 @@ int main(void) {
     uint8_t *qc = malloc(B * H * NQ * D / 2), *qs = malloc(B * H * NQ * D / 16);
     float qg = 0.0f;
     CHECK(oracle_quantize(kv, 1, B * H * NQ, D, -2, 6, 0, 0, &qg, qc, qs, NULL, 1));
-    double *O = malloc(sizeof(double) * B * H * NQ * D * 3);
+    const int64_t NO = (int64_t)B * H * NQ * D;
+    double *O = malloc(sizeof(double) * (NO * 6 + (int64_t)B * H * NQ * 4));
+    double *RI = O + 6 * NO;
     CHECK(oracle_attention_nvfp4(qc, qs, qg, kc, ks, kg, kc, ks, kg, B, H, 1, NQ, NK, D, 32, 1, O,
-                                 O + B * H * NQ * D, O + 2 * B * H * NQ * D, 2));
+                                 O + NO, O + 2 * NO, O + 3 * NO, O + 4 * NO, O + 5 * NO, RI, 2));
     /* the sink cache: head NF, tail ring NL, middle rows = the coded middle */
     CHECK(oracle_attention_kv_cache(qc, qs, qg, sink, sink + B * H * NF * D, kc, ks, kg, sink,
                                     sink + B * H * NF * D, kc, ks, kg, B, H, 1, NQ, NF + TM + NL, D,
-                                    NF, NL, TM, 32, 0, O, O + B * H * NQ * D,
-                                    O + 2 * B * H * NQ * D, 2));
+                                    NF, NL, TM, 32, 0, O, O + NO, O + 2 * NO, O + 3 * NO,
+                                    O + 4 * NO, O + 5 * NO, RI, 2));
     /* the same with the middle split into pieces of 64 tokens */
     CHECK(oracle_attention_kv_cache(qc, qs, qg, sink, sink + B * H * NF * D, kc, ks, kg, sink,
                                     sink + B * H * NF * D, kc, ks, kg, B, H, 1, NQ, NF + TM + NL, D,
-                                    NF, NL, TM, 32, 64, O, O + B * H * NQ * D,
-                                    O + 2 * B * H * NQ * D, 2));
+                                    NF, NL, TM, 32, 64, O, O + NO, O + 2 * NO, O + 3 * NO,
+                                    O + 4 * NO, O + 5 * NO, RI, 2));
     free(x); free(xb); free(codes); free(scales); free(fsel); free(y); free(kv); free(kc);
     free(ks); free(sink); free(yk); free(qc); free(qs); free(O);
     puts("oracle sanitizer run: ok");

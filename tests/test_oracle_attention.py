@@ -109,23 +109,7 @@ def test_flip_allowance_is_small_and_present(orc):
 
 # --- attention over the sink KV cache ---
 
-def cache_of(orc, x, nf, nl, T, cap):
-    """Sink-cache buffers of a [B, H, T, D] bf16 tensor, as the KV append builds them."""
-    B, H, _, D = x.shape
-    mid = max(T - nf - nl, 0)
-    g = np.float32(np.abs(workloads.bf16_bits_to_f32(x[:, :, nf:T - nl])).max() / 2688) if mid else np.float32(1)
-    c, s, _ = orc.quantize(np.ascontiguousarray(x[:, :, nf:nf + mid]).reshape(-1, D) if mid else
-                           np.zeros((0, D), np.uint16), -2, 6, gscale=float(g))
-    codes = np.zeros((B, H, cap, D // 2), np.uint8)
-    scales = np.zeros((B, H, cap, D // 16), np.uint8)
-    codes[:, :, :mid] = c.reshape(B, H, mid, D // 2)
-    scales[:, :, :mid] = s.reshape(B, H, mid, D // 16)
-    head = np.zeros((B, H, nf, D), np.uint16)
-    head[:, :, :min(nf, T)] = x[:, :, :min(nf, T)]
-    tail = np.zeros((B, H, nl, D), np.uint16)
-    for t in range(max(nf, T - nl), T):
-        tail[:, :, t % nl] = x[:, :, t]
-    return dict(head=head, tail=tail, codes=codes, scales=scales, gscale=g)
+from attn_cases import cache_of  # noqa: E402  (the sink-cache buffers the KV append builds)
 
 
 @pytest.mark.parametrize("T,nf,nl", [(200, 32, 48), (90, 64, 64), (300, 0, 0), (130, 16, 0)])
