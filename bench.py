@@ -552,6 +552,8 @@ def formats_table(torch, nv, workloads, iters: int = 50):
         times.append((idx, w["name"], t, qb, db))
         del xf
 
+    scores = scores_table(torch, nv, workloads, signs)
+
     f = lambda v: f"{v:.3e}" if v is not None else "—"
     print("| # | workload | NVFP4 max scaling | NVFP4 ScaleSearch [-2,6] | NVFP4 SS [-8,8] | "
           "MXFP4 (OCP rule) | MXFP4 search [-1,1] | NVFP4 SS [-2,6] error below MXFP4 OCP |")
@@ -577,6 +579,12 @@ def formats_table(torch, nv, workloads, iters: int = 50):
         print(f"| {idx} | {nb} | " + " | ".join(f"{h[f + 8] / max(nb, 1):.3f}"
                                                  for f in range(-2, 7)) + " |")
     print()
+    print("| Q (workload 5) against K (workload 3), 256 query rows per head x all 32768 keys | "
+          "relative score error sum (S^ - S)^2 / sum S^2 | Q, K quantize ms |")
+    print("|---|---|---|")
+    for name, err, ms in scores:
+        print(f"| {name} | {err:.4e} | {ms:.3f} |")
+    print()
     gbs = lambda b, m: b / (m * 1e-3) / 1e9
     print("| # | MXFP4 quantize [0,0] us (GB/s) | MXFP4 quantize [-1,1] us (GB/s) | "
           "MXFP4 dequantize to FP32 us (GB/s) |")
@@ -585,6 +593,43 @@ def formats_table(torch, nv, workloads, iters: int = 50):
         print(f"| {idx} | {t['q0'] * 1e3:.1f} ({gbs(qb, t['q0']):.0f}) | "
               f"{t['q1'] * 1e3:.1f} ({gbs(qb, t['q1']):.0f}) | "
               f"{t['d'] * 1e3:.1f} ({gbs(db, t['d']):.0f}) |", flush=True)
+
+
+def scores_table(torch, nv, workloads, signs, rows_per_head: int = 256):
+    """Relative error of the attention scores QK^T computed from the coded operands, Q of
+    workload 5 [1, 32, 32768, 128] (offsets [-8, 8]) against K of workload 3
+    [1, 8, 32768, 128] (offsets [-2, 6]), grouped heads: plain ScaleSearch, the
+    randomized Hadamard transform on both, the balancing pair (channel exponents from
+    the calibration of Q against K) with and without the transform. Scores of
+    `rows_per_head` sampled query rows per head against every key, in double."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k = bf(workloads.workload(5)), bf(workloads.workload(3))
+    rows = torch.from_numpy(np.sort(np.random.default_rng(7).choice(32768, rows_per_head,
+                                                                    replace=False))).to(dev)
+    e = nv.balance_exponents(q, k)
+    qs, ks = q.double()[:, :, rows], k.double()
+    ref = torch.matmul(qs.reshape(8, 4 * rows_per_head, 128), ks[0].transpose(1, 2).contiguous())
+    den = float((ref ** 2).sum().item())
+    variants = {
+        "ScaleSearch": (dict(), dict()),
+        "randomized Hadamard + ScaleSearch": (dict(signs=signs), dict(signs=signs)),
+        "balancing pair + randomized Hadamard + ScaleSearch":
+            (dict(signs=signs, balance=(e, "q")), dict(signs=signs, balance=(e, "k"))),
+        "balancing pair + ScaleSearch": (dict(balance=(e, "q")), dict(balance=(e, "k"))),
+    }
+    out = []
+    for name, (kq, kk) in variants.items():
+        fn = lambda: (nv.quantize(q, (-8, 8), **kq), nv.quantize(k, (-2, 6), **kk))
+        (qc, qsc, qg), (kc, ksc, kg) = fn()
+        ms = event_time_ms(torch, fn, 5, stream)
+        qd = nv.dequantize(qc, qsc, qg).double()[:, :, rows]
+        kd = nv.dequantize(kc, ksc, kg).double()
+        got = torch.matmul(qd.reshape(8, 4 * rows_per_head, 128), kd[0].transpose(1, 2).contiguous())
+        out.append((name, float(((got - ref) ** 2).sum().item()) / den, ms))
+        del qd, kd, got
+    return out
 
 
 def attention_operands(torch, nv, workloads):

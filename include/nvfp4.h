@@ -82,6 +82,7 @@ typedef enum {
 /* Flags for the quantize calls. */
 #define NVFP4_HADAMARD128 1u  /* transform each 128-vector by H/sqrt(128) first (bf16 input) */
 #define NVFP4_GSCALE_GIVEN 2u /* *global_scale is an input: skip the global amax pass */
+#define NVFP4_PAIR_Q 4u       /* balancing pair: this tensor is the Q side (2^-e), else K (2^e) */
 
 /* Text for a status code (static storage). */
 NVFP4_API const char *nvfp4_status_str(nvfp4_status s);
@@ -377,6 +378,66 @@ NVFP4_API nvfp4_status nvfp4_kv_append_rht(const void *kv_new, nvfp4_dtype dt, i
                                            uint8_t *scales, void *stream);
 NVFP4_API nvfp4_status nvfp4_hadamard128_rht(const void *x, nvfp4_dtype xdt, int64_t rows,
                                              const uint32_t *signs, float *y, void *stream);
+
+/* ------------------------------------------------------------------------
+ * The balancing pair of incoherence processing (ScaleSearch summary page,
+ * ScaleSearchAttention, 非干渉処理（IP）と絶対値低減: besides the Hadamard
+ * transform, an additional linear pair Q' = Q R^-T, K' = K R that keeps every
+ * attention score and lowers the mean-square magnitude of the projected
+ * tensors). The pages fix neither R nor how it is found. Reading taken:
+ * R = diag(2^e) over the channels (columns), so Q'_tj = Q_tj 2^-e_j and
+ * K'_tj = K_tj 2^e_j: each score term q_j k_j is kept exactly, and bf16 values
+ * stay bf16 values. With the Hadamard transform the pair acts first:
+ * Q' = Q diag(2^-e) H_s, K' = K diag(2^e) H_s (H_s orthogonal), so
+ * Q' K'^T = Q K^T.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes of nvfp4_balance_exponents for `cols` channels (0 if cols
+ * is outside 1..2048). */
+NVFP4_API size_t nvfp4_balance_workspace_bytes(int64_t cols);
+
+/* Calibration: channel exponents chan_exp[cols] (device int8) from a Q tensor
+ * q[rows_q][cols] and a K tensor k[rows_k][cols] (device, dt, 16-byte
+ * aligned; cols % 16 == 0, cols <= 2048). With a_j^2 and b_j^2 the channel's
+ * sums of squares over Q's and K's rows (double), channel j's share of
+ * ||Q'||^2 + ||K'||^2 is a^2 4^-e + b^2 4^e; e_j is the least e in [-16, 16]
+ * with a^2 <= b^2 4^(2e+1) (the minimiser, ties to the smaller e; 16 if none),
+ * 0 when a or b is 0. The sums are taken in a fixed order, so the result is
+ * deterministic; a channel whose a^2 / b^2 lies within double rounding of a
+ * decision boundary may differ from another summation order's choice (either
+ * is a minimiser). Workspace: nvfp4_balance_workspace_bytes(cols), 8-byte
+ * aligned, caller-owned. NVFP4_ESHAPE for a size outside those limits. */
+NVFP4_API nvfp4_status nvfp4_balance_exponents(const void *q, const void *k, nvfp4_dtype dt,
+                                               int64_t rows_q, int64_t rows_k, int64_t cols,
+                                               int8_t *chan_exp, void *workspace,
+                                               size_t workspace_bytes, void *stream);
+
+/* nvfp4_quantize of one side of the pair: x' = x 2^(side e_col) with side -1
+ * under NVFP4_PAIR_Q (the Q side) and +1 otherwise (K), chan_exp[cols] device
+ * int8, 16-byte aligned, each clamped to [-32, 32]. Without
+ * NVFP4_HADAMARD128, x' is formed in binary32 (exact unless it leaves the
+ * normal range) and quantized as FP32 values (the exact search: slower than
+ * the bf16 certified search). With NVFP4_HADAMARD128 (bf16 input, cols ==
+ * 128) the transform is applied to x' (its products stay exact: the factors
+ * 2^e ride in the transform's matrix operand), with the random signs when
+ * `signs` (host uint32[4], as in nvfp4_quantize_rht) is not NULL; `signs`
+ * without the transform flag is NVFP4_EINVAL. Outputs, tensor scale and
+ * workspace as nvfp4_quantize; the codes are those of x' (dequantize returns
+ * x'-domain values, whose products with the other side's keep the scores). */
+NVFP4_API nvfp4_status nvfp4_quantize_balanced(const void *x, nvfp4_dtype xdt, int64_t rows,
+                                               int64_t cols, int block, int f_lo, int f_hi,
+                                               uint32_t flags, const int8_t *chan_exp,
+                                               const uint32_t *signs, uint8_t *codes,
+                                               uint8_t *scales, float *global_scale,
+                                               void *workspace, size_t workspace_bytes,
+                                               void *stream);
+
+/* The transform alone on one side of the pair: y[rows][128] (FP32) =
+ * (x diag(2^(side e)) o s) H / sqrt(128) for bf16 x[rows][128] (side as in
+ * nvfp4_quantize_balanced from NVFP4_PAIR_Q in flags; signs optional). */
+NVFP4_API nvfp4_status nvfp4_hadamard128_balanced(const void *x, nvfp4_dtype xdt, int64_t rows,
+                                                  const int8_t *chan_exp, uint32_t flags,
+                                                  const uint32_t *signs, float *y, void *stream);
 
 #ifdef __cplusplus
 }

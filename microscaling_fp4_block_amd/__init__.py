@@ -9,6 +9,7 @@ from .nvfp4 import (  # noqa: F401
     attention,
     attention_kv_cache,
     attention_split_workspace_bytes,
+    balance_exponents,
     dequantize,
     dequantize_kv_sink,
     global_scale,

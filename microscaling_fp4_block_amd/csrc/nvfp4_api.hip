@@ -49,8 +49,8 @@ RegionMap plain_map(int64_t rows, int64_t cols) {
 // Global amax pass: one partial maximum per workgroup into the workspace.
 // Returns the number of partials (0 on a launch error).
 int run_amax(const void *x, bool bf16, bool hadamard, const HadamardSigns &hs, const RegionMap &m,
-             void *ws, hipStream_t s) {
-  AmaxArgs a{x, (uint32_t *)ws, m, hs};
+             void *ws, hipStream_t s, const Balance &bal = Balance{nullptr, 1}) {
+  AmaxArgs a{x, (uint32_t *)ws, m, hs, bal};
   int groups;
   hipError_t e;
   if (hadamard) {
@@ -65,8 +65,9 @@ int run_amax(const void *x, bool bf16, bool hadamard, const HadamardSigns &hs, c
 
 // Global amax + finalize into gscale (the tensor scale alone).
 nvfp4_status run_global_scale(const void *x, bool bf16, bool hadamard, const HadamardSigns &hs,
-                              const RegionMap &m, float *gscale, void *ws, hipStream_t s) {
-  const int groups = run_amax(x, bf16, hadamard, hs, m, ws, s);
+                              const RegionMap &m, float *gscale, void *ws, hipStream_t s,
+                              const Balance &bal = Balance{nullptr, 1}) {
+  const int groups = run_amax(x, bf16, hadamard, hs, m, ws, s, bal);
   if (groups == 0) return NVFP4_EHIP;
   return hip_status(launch_finalize((const uint32_t *)ws, groups, gscale, s));
 }
@@ -81,15 +82,15 @@ hipError_t run_quantize(const QuantArgs &q, bool bf16, bool hadamard, hipStream_
 nvfp4_status run_quantize_region(const void *x, bool bf16, bool had, const HadamardSigns &hs,
                                  bool given, const RegionMap &m, int f_lo, int f_hi,
                                  uint8_t *codes, uint8_t *scales, float *gscale, void *ws,
-                                 hipStream_t s) {
+                                 hipStream_t s, const Balance &bal = Balance{nullptr, 1}) {
   if (m.nblocks == 0)
-    return given ? NVFP4_OK : run_global_scale(x, bf16, had, hs, m, gscale, ws, s);
+    return given ? NVFP4_OK : run_global_scale(x, bf16, had, hs, m, gscale, ws, s, bal);
   int np = 0;
   if (!given) {
-    np = run_amax(x, bf16, had, hs, m, ws, s);
+    np = run_amax(x, bf16, had, hs, m, ws, s, bal);
     if (np == 0) return NVFP4_EHIP;
   }
-  QuantArgs q{x, codes, scales, gscale, (const uint32_t *)ws, np, m, f_lo, f_hi, hs};
+  QuantArgs q{x, codes, scales, gscale, (const uint32_t *)ws, np, m, f_lo, f_hi, hs, bal};
   return hip_status(run_quantize(q, bf16, had, s));
 }
 
@@ -633,7 +634,7 @@ nvfp4_status hadamard_impl(const void *x, nvfp4_dtype xdt, int64_t rows, const u
   if (!x || !y) return NVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_EALIGN;
   return hip_status(launch_hadamard((const uint16_t *)x, y, (uint32_t)rows, make_signs(signs),
-                                    (hipStream_t)stream));
+                                    Balance{nullptr, 1}, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -940,6 +941,91 @@ nvfp4_status nvfp4_attention_kv_cache_split_dev(
                                  k_gscale, v_head, v_tail, v_codes, v_scales, v_gscale, cache_dt,
                                  B, Hq, Hkv, Nq, 0, length, D, n_first, n_last, cap, split,
                                  workspace, workspace_bytes, out, out_dt, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The balancing pair of incoherence processing (ScaleSearch summary page,
+// ScaleSearchAttention, 非干渉処理（IP）と絶対値低減): Q' = Q diag(2^-e),
+// K' = K diag(2^e), before the Hadamard transform when one is used.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kMaxBalanceCols = 2048;
+
+size_t balance_ws(int64_t cols) {
+  return (size_t)2 * kColSumGroups * (size_t)cols * sizeof(double);
+}
+
+Balance make_balance(const int8_t *e, uint32_t flags) {
+  return Balance{e, (flags & NVFP4_PAIR_Q) ? -1 : 1};
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_balance_workspace_bytes(int64_t cols) {
+  return (cols > 0 && cols <= kMaxBalanceCols) ? balance_ws(cols) : 0;
+}
+
+nvfp4_status nvfp4_balance_exponents(const void *q, const void *k, nvfp4_dtype dt, int64_t rows_q,
+                                     int64_t rows_k, int64_t cols, int8_t *chan_exp,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+  if (!dtype_ok(dt) || !chan_exp) return NVFP4_EINVAL;
+  if (cols <= 0 || cols % 16 || cols > kMaxBalanceCols || rows_q < 0 || rows_k < 0 ||
+      rows_q >= k2p31 || rows_k >= k2p31)
+    return NVFP4_ESHAPE;
+  if ((rows_q > 0 && !q) || (rows_k > 0 && !k)) return NVFP4_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16)) return NVFP4_EALIGN;
+  if (!workspace || workspace_bytes < balance_ws(cols) || !aligned(workspace, 8))
+    return NVFP4_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dt == NVFP4_BF16;
+  double *qp = (double *)workspace, *kp = qp + (size_t)kColSumGroups * (size_t)cols;
+  if (launch_colsumsq(ColSumArgs{q, (uint32_t)rows_q, (uint32_t)cols, qp}, bf16, s) != hipSuccess)
+    return NVFP4_EHIP;
+  if (launch_colsumsq(ColSumArgs{k, (uint32_t)rows_k, (uint32_t)cols, kp}, bf16, s) != hipSuccess)
+    return NVFP4_EHIP;
+  return hip_status(launch_balance_exponents(qp, kp, (uint32_t)cols, chan_exp, s));
+}
+
+nvfp4_status nvfp4_quantize_balanced(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+                                     int block, int f_lo, int f_hi, uint32_t flags,
+                                     const int8_t *chan_exp, const uint32_t *signs,
+                                     uint8_t *codes, uint8_t *scales, float *global_scale,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+  if (!global_scale || !dtype_ok(xdt) || !chan_exp) return NVFP4_EINVAL;
+  if (flags & ~(NVFP4_HADAMARD128 | NVFP4_GSCALE_GIVEN | NVFP4_PAIR_Q)) return NVFP4_EINVAL;
+  const bool had = flags & NVFP4_HADAMARD128;
+  if (signs && !had) return NVFP4_EINVAL;
+  nvfp4_status st = check_offsets(block, f_lo, f_hi);
+  if (st) return st;
+  st = check_shape(rows, cols, flags & ~NVFP4_PAIR_Q, xdt);
+  if (st) return st;
+  if (had && cols != 128) return NVFP4_ESHAPE;
+  if (rows > 0 && (!x || !codes || !scales)) return NVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(chan_exp, 16)) return NVFP4_EALIGN;
+  const bool given = flags & NVFP4_GSCALE_GIVEN;
+  if (!given && (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4)))
+    return NVFP4_EWORKSPACE;
+  return run_quantize_region(x, xdt == NVFP4_BF16, had, make_signs(signs), given,
+                             plain_map(rows, cols), f_lo, f_hi, codes, scales, global_scale,
+                             workspace, (hipStream_t)stream, make_balance(chan_exp, flags));
+}
+
+nvfp4_status nvfp4_hadamard128_balanced(const void *x, nvfp4_dtype xdt, int64_t rows,
+                                        const int8_t *chan_exp, uint32_t flags,
+                                        const uint32_t *signs, float *y, void *stream) {
+  if (xdt != NVFP4_BF16 || !chan_exp || (flags & ~NVFP4_PAIR_Q)) return NVFP4_EINVAL;
+  if (rows < 0 || rows > kMaxBlocks / 8) return NVFP4_ESHAPE;
+  if (!aligned(chan_exp, 16)) return NVFP4_EALIGN;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !y) return NVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_EALIGN;
+  return hip_status(launch_hadamard((const uint16_t *)x, y, (uint32_t)rows, make_signs(signs),
+                                    make_balance(chan_exp, flags), (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -66,6 +66,15 @@ struct HadamardSigns {
   uint32_t w[4];
 };
 
+// The balancing pair Q' = Q diag(2^-e), K' = K diag(2^e): channel exponents
+// e[cols] (device, int8, 16-byte aligned; clamped to [-32, 32]) applied with
+// the sign `side` (+1 or -1) to every row before anything else (before the
+// Hadamard transform, whose kernels then need cols == 128).
+struct Balance {
+  const int8_t *e;  // null: no balancing
+  int32_t side;
+};
+
 struct QuantArgs {
   const void *x;
   uint8_t *codes;
@@ -76,6 +85,7 @@ struct QuantArgs {
   RegionMap map;
   int f_lo, f_hi;
   HadamardSigns hs;           // Hadamard kernels only
+  Balance bal;
 };
 
 struct AmaxArgs {
@@ -83,6 +93,15 @@ struct AmaxArgs {
   uint32_t *partials;
   RegionMap map;
   HadamardSigns hs;           // Hadamard kernels only
+  Balance bal;
+};
+
+// Column sums of squares of the balancing pair's calibration (double): the
+// partial sums of workgroup g over its rows go to part[g][cols].
+struct ColSumArgs {
+  const void *x;
+  uint32_t rows, cols;
+  double *part;
 };
 
 struct DequantArgs {
@@ -186,7 +205,14 @@ hipError_t launch_mx_quantize(const MxArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_mx_dequantize(const MxDequantArgs &a, bool out_bf16, hipStream_t s);
 
 hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, const HadamardSigns &hs,
-                           hipStream_t s);
+                           const Balance &bal, hipStream_t s);
+// Balancing pair calibration: per-workgroup column sums of squares of x (cols
+// % 8 == 0, cols <= 2048) into part[kColSumGroups][cols], then the channel
+// exponents from Q's and K's sums.
+constexpr int kColSumGroups = 256;
+hipError_t launch_colsumsq(const ColSumArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_balance_exponents(const double *qpart, const double *kpart, uint32_t cols,
+                                    int8_t *e, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, bool out_bf16, hipStream_t s);
 hipError_t launch_sink_copy(const SinkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_admit(const AdmitArgs &a, bool bf16, hipStream_t s);

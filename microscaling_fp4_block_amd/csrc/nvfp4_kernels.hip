@@ -156,7 +156,38 @@ __device__ __forceinline__ uint32_t chunk_absmax(uint4 c) {
 // Lanes take consecutive 16-byte chunks (a block is 2 chunks in bf16, 4 in
 // FP32), four independent nontemporal loads in flight per lane; the grid is
 // capped at 512 workgroups (fewer concurrent streams read HBM faster here).
+// Balancing pair: the exponent side * e (clamped to [-32, 32]) of a signed byte.
+__device__ __forceinline__ int bal_exp(uint32_t word, int byte, int side) {
+  const int e = side * (int)(int8_t)(uint8_t)(word >> (8 * byte));
+  return min(32, max(-32, e));
+}
+
+// Max of the absolute-value bit patterns of the scaled values x_i 2^e_i of one
+// 16-byte chunk (exponent bytes in ew, one per element).
 template <bool BF16>
+__device__ __forceinline__ uint32_t chunk_absmax_bal(uint4 c, uint2 ew, int side) {
+  uint32_t m = 0;
+  if (BF16) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t eww = k < 2 ? ew.x : ew.y;
+      const float lo = ldexpf(__uint_as_float(w[k] << 16), bal_exp(eww, 2 * (k & 1), side));
+      const float hi = ldexpf(__uint_as_float(w[k] & 0xFFFF0000u), bal_exp(eww, 2 * (k & 1) + 1, side));
+      m = max(m, max(__float_as_uint(lo) & 0x7FFFFFFFu, __float_as_uint(hi) & 0x7FFFFFFFu));
+    }
+  } else {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      m = max(m, __float_as_uint(ldexpf(__uint_as_float(w[k]), bal_exp(ew.x, k, side))) &
+                     0x7FFFFFFFu);
+  }
+  return m;
+}
+
+// BAL: the values are those of the balancing pair, x 2^(side e_col) in binary32.
+template <bool BF16, bool BAL>
 __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
   constexpr uint32_t CPB = BF16 ? 2 : 4;  // 16-byte chunks per block
   constexpr uint32_t ES = BF16 ? 2 : 4;
@@ -166,19 +197,29 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(AmaxArgs a) {
   constexpr int UNROLL = 4;
   for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += UNROLL * stride) {
     uint4 v[UNROLL];
+    uint2 ew[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       uint32_t c = c0 + u * stride;
+      ew[u] = make_uint2(0, 0);
       if (c < nchunks) {
         uint32_t b = c / CPB, sub = c % CPB;
         const char *p = (const char *)a.x + block_offset(a.map, b) * ES + sub * 16u;
         v[u] = load_stream(p);
+        if (BAL) {
+          // exponents of the chunk's columns (8 in bf16, 4 in FP32)
+          const uint32_t r = fastdiv(b, a.map.div_bpr);
+          const uint32_t col = (b - r * a.map.bpr) * 16u + sub * (16u / CPB);
+          ew[u] = BF16 ? *(const uint2 *)(a.bal.e + col)
+                       : make_uint2(*(const uint32_t *)(a.bal.e + col), 0u);
+        }
       } else {
         v[u] = make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) m = max(m, chunk_absmax<BF16>(v[u]));
+    for (int u = 0; u < UNROLL; ++u)
+      m = max(m, BAL ? chunk_absmax_bal<BF16>(v[u], ew[u], a.bal.side) : chunk_absmax<BF16>(v[u]));
   }
   m = group_max_u32(m);
   if (threadIdx.x == 0) a.partials[blockIdx.x] = m;
@@ -465,7 +506,17 @@ __device__ __forceinline__ void search_block_twins(const float (&x)[16], float s
 
 // Blocks first, first + stride, ... of the region with the exact search.
 // FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI] (twin-sharing search).
-template <bool BF16, int FLO, int FHI, bool FIXED>
+// Balancing pair: x_i 2^(side e_i) in binary32 for the block's 16 columns.
+__device__ __forceinline__ void balance_block(const Balance &bal, const RegionMap &m, uint32_t b,
+                                              float (&x)[16]) {
+  const uint32_t r = fastdiv(b, m.div_bpr);
+  const uint4 ew = *(const uint4 *)(bal.e + (b - r * m.bpr) * 16u);
+  const uint32_t w[4] = {ew.x, ew.y, ew.z, ew.w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = ldexpf(x[i], bal_exp(w[i >> 2], i & 3, bal.side));
+}
+
+template <bool BF16, int FLO, int FHI, bool FIXED, bool BAL = false>
 __device__ __forceinline__ void quantize_blocks(const QuantArgs &a, const f32x2 *tbl, float sg,
                                                 bool sg_ok, uint32_t first, uint32_t stride,
                                                 uint32_t t_dev) {
@@ -474,6 +525,7 @@ __device__ __forceinline__ void quantize_blocks(const QuantArgs &a, const f32x2 
     const BlockIO io = block_io(a.x, a.map, b, BF16 ? 2u : 4u, t_dev);
     if (!io.valid) continue;
     load_block_at<BF16>(io.src, x);
+    if (BAL) balance_block(a.bal, a.map, b, x);
     uint32_t best_p, bc0, bc1;
     if (FIXED)
       search_block_twins<FLO, FHI>(x, sg, sg_ok, tbl, best_p, bc0, bc1);
@@ -484,14 +536,17 @@ __device__ __forceinline__ void quantize_blocks(const QuantArgs &a, const f32x2 
   }
 }
 
-template <bool BF16, int FLO, int FHI, bool FIXED>
+// BAL: the blocks are those of the balancing pair's scaled values (plain
+// regions only), searched exactly as FP32 values.
+template <bool BF16, int FLO, int FHI, bool FIXED, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   __shared__ f32x2 tbl[128];
   const float sg = resolve_tensor_scale(a);
   const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
   build_scale_table(tbl, sg);
-  quantize_blocks<BF16, FLO, FHI, FIXED>(a, tbl, sg, sg_ok, blockIdx.x * kThreads + threadIdx.x,
-                                         gridDim.x * kThreads, map_length(a.map));
+  quantize_blocks<BF16, FLO, FHI, FIXED, BAL>(a, tbl, sg, sg_ok,
+                                              blockIdx.x * kThreads + threadIdx.x,
+                                              gridDim.x * kThreads, map_length(a.map));
 }
 
 // Max scaling alone (offsets [0, 0]: one candidate, nothing to score) with two
@@ -904,6 +959,33 @@ __device__ __forceinline__ bf16x8 hadamard_a(const HadamardLane &h, uint32_t t, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Balancing pair folded into the transform: y = (x diag(2^e)) H' = x (diag(2^e) H'),
+// so the A operand's entry for input feature k becomes +-2^e_k (still exact in
+// bf16, and every product x_k 2^e_k stays exact in FP32). ew holds, per K slice
+// ks and lane half g, the bf16 exponent fields of elements 16 ks + 8 g .. +7 in
+// pairs (low element in the low half): [ks][g][4] words.
+__device__ __forceinline__ void build_balance_bits(const Balance &bal, uint32_t *ew) {
+  if (threadIdx.x < 64) {
+    const uint32_t ks = threadIdx.x >> 3, g = (threadIdx.x >> 2) & 1u, q = threadIdx.x & 3u;
+    const uint32_t k0 = 16u * ks + 8u * g + 2u * q;
+    const uint32_t w = *(const uint16_t *)(bal.e + k0);
+    const uint32_t lo = (uint32_t)(127 + bal_exp(w, 0, bal.side)) << 7;
+    const uint32_t hi = (uint32_t)(127 + bal_exp(w, 1, bal.side)) << 7;
+    ew[threadIdx.x] = lo | (hi << 16);
+  }
+}
+
+__device__ __forceinline__ bf16x8 hadamard_a_bal(const HadamardLane &h, uint32_t t, uint32_t ks,
+                                                 const uint4 *ew4) {
+  const uint32_t feat = 32u * t + h.lo;
+  const uint32_t neg = __builtin_popcount(feat & (16u * ks + 8u * h.g)) & 1u;
+  const uint32_t m = neg ? 0x80008000u : 0u;
+  const uint4 e = ew4[2u * ks + h.g];
+  uint4 v = make_uint4(((h.base[0] ^ m) & 0x80008000u) | e.x, ((h.base[1] ^ m) & 0x80008000u) | e.y,
+                       ((h.base[2] ^ m) & 0x80008000u) | e.z, ((h.base[3] ^ m) & 0x80008000u) | e.w);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // bf16 sign-bit mask of elements 16 ks + 8 g .. +7 (two per word, low first).
 __device__ __forceinline__ uint4 hadamard_sign_mask(const HadamardSigns &hs, int ks, uint32_t g) {
   const uint32_t bits = (hs.w[ks >> 1] >> (16u * (ks & 1) + 8u * g)) & 0xFFu;
@@ -930,12 +1012,16 @@ __device__ __forceinline__ void hadamard_load(const uint16_t *x, uint64_t off, b
 }
 
 // Tile t of the transform: y[v] = feature 32 t + 16 g + v of this lane's vector.
+// BAL: with the balancing pair's exponents (ew4, the LDS words of
+// build_balance_bits) in the A operand.
+template <bool BAL = false>
 __device__ __forceinline__ void hadamard_tile(const HadamardLane &h, const uint4 (&b)[8], uint32_t t,
-                                              float (&y)[16]) {
+                                              float (&y)[16], const uint4 *ew4 = nullptr) {
   f32x16 acc = {};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hadamard_a(h, t, ks),
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(BAL ? hadamard_a_bal(h, t, ks, ew4)
+                                                      : hadamard_a(h, t, ks),
                                                   __builtin_bit_cast(bf16x8, b[ks]), acc, 0, 0, 0);
 #pragma unroll
   for (int v = 0; v < 16; ++v) y[v] = (float)((double)acc[v] * kInvSqrt128);
@@ -943,9 +1029,11 @@ __device__ __forceinline__ void hadamard_tile(const HadamardLane &h, const uint4
 
 // Quantize with the Hadamard pre-transform (bf16 input, cols % 128 == 0). One
 // wave per 32 vectors; each lane codes four blocks of its vector.
-template <bool SIGNS, int FLO, int FHI, bool FIXED>
+template <bool SIGNS, int FLO, int FHI, bool FIXED, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a) {
   __shared__ f32x2 tbl[128];
+  __shared__ __attribute__((aligned(16))) uint32_t ew[64];
+  if (BAL) build_balance_bits(a.bal, ew);  // the table build below synchronizes
   const float sg = resolve_tensor_scale(a);
   const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
   build_scale_table(tbl, sg);
@@ -966,7 +1054,7 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
-      hadamard_tile(h, b, t, y);  // every lane takes part in the matrix instructions
+      hadamard_tile<BAL>(h, b, t, y, (const uint4 *)ew);  // every lane takes part
       if (live) {
         uint32_t best_p, bc0, bc1;
         if (FIXED)
@@ -982,8 +1070,13 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
 }
 
 // Global amax of the transformed values.
-template <bool SIGNS>
+template <bool SIGNS, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void amax_hadamard_kernel(AmaxArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t ew[64];
+  if (BAL) {
+    build_balance_bits(a.bal, ew);
+    __syncthreads();
+  }
   const HadamardLane h = hadamard_lane_setup();
   const uint32_t nvec = a.map.nblocks / 8u;
   const uint32_t lane = threadIdx.x & 63u;
@@ -999,7 +1092,7 @@ __global__ __launch_bounds__(kThreads) void amax_hadamard_kernel(AmaxArgs a) {
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
-      hadamard_tile(h, b, t, y);
+      hadamard_tile<BAL>(h, b, t, y, (const uint4 *)ew);
 #pragma unroll
       for (int v = 0; v < 16; ++v) m = max(m, __float_as_uint(y[v]) & 0x7FFFFFFFu);
     }
@@ -1009,9 +1102,15 @@ __global__ __launch_bounds__(kThreads) void amax_hadamard_kernel(AmaxArgs a) {
 }
 
 // The transform alone: y[nvec][128] FP32.
-template <bool SIGNS>
+template <bool SIGNS, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void hadamard_kernel(const uint16_t *x, float *out,
-                                                            uint32_t nvec, HadamardSigns hs) {
+                                                            uint32_t nvec, HadamardSigns hs,
+                                                            Balance bal) {
+  __shared__ __attribute__((aligned(16))) uint32_t ew[64];
+  if (BAL) {
+    build_balance_bits(bal, ew);
+    __syncthreads();
+  }
   const HadamardLane h = hadamard_lane_setup();
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
@@ -1024,7 +1123,7 @@ __global__ __launch_bounds__(kThreads) void hadamard_kernel(const uint16_t *x, f
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
-      hadamard_tile(h, b, t, y);
+      hadamard_tile<BAL>(h, b, t, y, (const uint4 *)ew);
       if (valid) {
         float4 *o = (float4 *)(out + (uint64_t)vec * 128u + 32u * t + 16u * h.g);
 #pragma unroll
@@ -1512,6 +1611,84 @@ __global__ __launch_bounds__(kThreads) void mx_dequantize_kernel(MxDequantArgs a
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
+// Balancing pair calibration (ScaleSearch summary page, ScaleSearchAttention,
+// 非干渉処理（IP）と絶対値低減: an additional pair Q' = Q R^-T, K' = K R that keeps
+// the scores and lowers the mean-square magnitude). R = diag(2^e); channel j's
+// share of ||Q'||^2 + ||K'||^2 is a^2 4^-e + b^2 4^e with a^2, b^2 its sums of
+// squares in Q and K; e_j is the least e in [-16, 16] with a^2 <= b^2 4^(2e+1)
+// (16 if none), 0 when a or b is 0.
+// ---------------------------------------------------------------------------
+
+// Workgroup g sums rows [g R / G, (g + 1) R / G): a lane owns 8 consecutive
+// columns (one 16- or 32-byte load per row), cols / 8 lanes cover a row, the
+// workgroup's lanes take kThreads / (cols / 8) rows at a time; double sums,
+// then the lanes of one column group add their sums in a fixed order.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void colsumsq_kernel(ColSumArgs a) {
+  __shared__ double red[kThreads][8];
+  const uint32_t tpr = a.cols / 8u;
+  const uint32_t rpi = kThreads / tpr;
+  const uint32_t cg = threadIdx.x % tpr, rsub = threadIdx.x / tpr;
+  const uint32_t r0 = (uint32_t)((uint64_t)a.rows * blockIdx.x / gridDim.x);
+  const uint32_t r1 = (uint32_t)((uint64_t)a.rows * (blockIdx.x + 1) / gridDim.x);
+  double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (rsub < rpi) {
+    for (uint32_t r = r0 + rsub; r < r1; r += rpi) {
+      float v[8];
+      if (BF16) {
+        const uint4 c = load_stream((const char *)a.x + ((uint64_t)r * a.cols + 8u * cg) * 2u);
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[2 * k] = __uint_as_float(w[k] << 16);
+          v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+      } else {
+        const char *p = (const char *)a.x + ((uint64_t)r * a.cols + 8u * cg) * 4u;
+        const uint4 c0 = load_stream(p), c1 = load_stream(p + 16);
+        const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(w[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s[k] += (double)v[k] * (double)v[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) red[threadIdx.x][k] = s[k];
+  __syncthreads();
+  if (threadIdx.x < tpr) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      double t = 0.0;
+      for (uint32_t i = 0; i < rpi; ++i) t += red[i * tpr + threadIdx.x][k];
+      a.part[(uint64_t)blockIdx.x * a.cols + 8u * threadIdx.x + k] = t;
+    }
+  }
+}
+
+__device__ __forceinline__ int balance_exponent(double a2, double b2) {
+  if (!(a2 > 0.0) || !(b2 > 0.0)) return 0;
+  for (int e = -16; e <= 15; ++e)
+    if (a2 <= ldexp(b2, 2 * (2 * e + 1))) return e;
+  return 16;
+}
+
+// One workgroup: each channel's partial sums in workgroup order, then its exponent.
+__global__ __launch_bounds__(kThreads) void balance_exponents_kernel(const double *qpart,
+                                                                     const double *kpart,
+                                                                     uint32_t cols, int8_t *e) {
+  for (uint32_t j = threadIdx.x; j < cols; j += kThreads) {
+    double a2 = 0.0, b2 = 0.0;
+    for (int g = 0; g < kColSumGroups; ++g) {
+      a2 += qpart[(uint64_t)g * cols + j];
+      b2 += kpart[(uint64_t)g * cols + j];
+    }
+    e[j] = (int8_t)balance_exponent(a2, b2);
+  }
+}
+
+// ---------------------------------------------------------------------------
 
 static int grid_for(uint64_t items, int cap) {
   uint64_t g = (items + kThreads - 1) / kThreads;
@@ -1520,10 +1697,15 @@ static int grid_for(uint64_t items, int cap) {
 }
 
 hipError_t launch_amax(const AmaxArgs &a, bool bf16, int groups, hipStream_t s) {
-  if (bf16)
-    hipLaunchKernelGGL(amax_kernel<true>, dim3(groups), dim3(kThreads), 0, s, a);
+  const bool bal = a.bal.e != nullptr;
+  if (bf16 && bal)
+    hipLaunchKernelGGL((amax_kernel<true, true>), dim3(groups), dim3(kThreads), 0, s, a);
+  else if (bf16)
+    hipLaunchKernelGGL((amax_kernel<true, false>), dim3(groups), dim3(kThreads), 0, s, a);
+  else if (bal)
+    hipLaunchKernelGGL((amax_kernel<false, true>), dim3(groups), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(amax_kernel<false>, dim3(groups), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((amax_kernel<false, false>), dim3(groups), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1532,8 +1714,31 @@ hipError_t launch_finalize(const uint32_t *partials, int n, float *gscale, hipSt
   return hipGetLastError();
 }
 
+// The balancing pair's plain quantize: the exact search on the scaled binary32
+// values (the certified search needs bf16 values).
+static hipError_t launch_quantize_balanced(const QuantArgs &a, bool bf16, int g, hipStream_t s) {
+  const int range = (a.f_lo == -2 && a.f_hi == 6) ? 1 : (a.f_lo == -8 && a.f_hi == 8) ? 2 : 0;
+  if (bf16) {
+    if (range == 1)
+      hipLaunchKernelGGL((quantize_kernel<true, -2, 6, true, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else if (range == 2)
+      hipLaunchKernelGGL((quantize_kernel<true, -8, 8, true, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((quantize_kernel<true, 0, 0, false, true>), dim3(g), dim3(kThreads), 0, s, a);
+  } else {
+    if (range == 1)
+      hipLaunchKernelGGL((quantize_kernel<false, -2, 6, true, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else if (range == 2)
+      hipLaunchKernelGGL((quantize_kernel<false, -8, 8, true, true>), dim3(g), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((quantize_kernel<false, 0, 0, false, true>), dim3(g), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.map.nblocks, kMaxQuantGroups);
+  if (a.bal.e) return launch_quantize_balanced(a, bf16, g, s);
   if (a.f_lo == 0 && a.f_hi == 0) {
     const int gr = grid_for((uint64_t)a.map.nblocks * 2u, kMaxQuantGroups);
     if (bf16)
@@ -1567,16 +1772,39 @@ static int hadamard_groups(uint32_t nvec, int cap) {
 int amax_hadamard_groups(uint32_t nblocks) { return hadamard_groups(nblocks / 8u, kMaxAmaxGroups); }
 
 hipError_t launch_amax_hadamard(const AmaxArgs &a, int groups, hipStream_t s) {
-  if (a.hs.on)
-    hipLaunchKernelGGL(amax_hadamard_kernel<true>, dim3(groups), dim3(kThreads), 0, s, a);
+  const bool bal = a.bal.e != nullptr;
+  if (a.hs.on && bal)
+    hipLaunchKernelGGL((amax_hadamard_kernel<true, true>), dim3(groups), dim3(kThreads), 0, s, a);
+  else if (a.hs.on)
+    hipLaunchKernelGGL((amax_hadamard_kernel<true, false>), dim3(groups), dim3(kThreads), 0, s, a);
+  else if (bal)
+    hipLaunchKernelGGL((amax_hadamard_kernel<false, true>), dim3(groups), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(amax_hadamard_kernel<false>, dim3(groups), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((amax_hadamard_kernel<false, false>), dim3(groups), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// The balancing pair before the transform (the exponents ride in the A operand).
+template <bool SIGNS>
+static void launch_quantize_hadamard_bal(const QuantArgs &a, int g, int range, hipStream_t s) {
+  if (range == 1)
+    hipLaunchKernelGGL((quantize_hadamard_kernel<SIGNS, -2, 6, true, true>), dim3(g), dim3(kThreads), 0, s, a);
+  else if (range == 2)
+    hipLaunchKernelGGL((quantize_hadamard_kernel<SIGNS, -8, 8, true, true>), dim3(g), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((quantize_hadamard_kernel<SIGNS, 0, 0, false, true>), dim3(g), dim3(kThreads), 0, s, a);
 }
 
 hipError_t launch_quantize_hadamard(const QuantArgs &a, hipStream_t s) {
   const int g = hadamard_groups(a.map.nblocks / 8u, kMaxQuantGroups);
   const int range = (a.f_lo == -2 && a.f_hi == 6) ? 1 : (a.f_lo == -8 && a.f_hi == 8) ? 2 : 0;
+  if (a.bal.e) {
+    if (a.hs.on)
+      launch_quantize_hadamard_bal<true>(a, g, range, s);
+    else
+      launch_quantize_hadamard_bal<false>(a, g, range, s);
+    return hipGetLastError();
+  }
   if (a.hs.on) {
     if (range == 1)
       hipLaunchKernelGGL((quantize_hadamard_kernel<true, -2, 6, true>), dim3(g), dim3(kThreads), 0, s, a);
@@ -1596,12 +1824,30 @@ hipError_t launch_quantize_hadamard(const QuantArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_hadamard(const uint16_t *x, float *y, uint32_t nvec, const HadamardSigns &hs,
-                           hipStream_t s) {
+                           const Balance &bal, hipStream_t s) {
   const int g = hadamard_groups(nvec, kMaxQuantGroups);
-  if (hs.on)
-    hipLaunchKernelGGL(hadamard_kernel<true>, dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs);
+  if (hs.on && bal.e)
+    hipLaunchKernelGGL((hadamard_kernel<true, true>), dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs, bal);
+  else if (hs.on)
+    hipLaunchKernelGGL((hadamard_kernel<true, false>), dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs, bal);
+  else if (bal.e)
+    hipLaunchKernelGGL((hadamard_kernel<false, true>), dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs, bal);
   else
-    hipLaunchKernelGGL(hadamard_kernel<false>, dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs);
+    hipLaunchKernelGGL((hadamard_kernel<false, false>), dim3(g), dim3(kThreads), 0, s, x, y, nvec, hs, bal);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsumsq(const ColSumArgs &a, bool bf16, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(colsumsq_kernel<true>, dim3(kColSumGroups), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(colsumsq_kernel<false>, dim3(kColSumGroups), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_balance_exponents(const double *qpart, const double *kpart, uint32_t cols,
+                                    int8_t *e, hipStream_t s) {
+  hipLaunchKernelGGL(balance_exponents_kernel, dim3(1), dim3(kThreads), 0, s, qpart, kpart, cols, e);
   return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 
 F32, BF16 = 0, 1
-HADAMARD128, GSCALE_GIVEN = 1, 2
+HADAMARD128, GSCALE_GIVEN, PAIR_Q = 1, 2, 4
 
 STATUS = {0: "NVFP4_OK", 1: "NVFP4_EINVAL", 2: "NVFP4_ESHAPE", 3: "NVFP4_EALIGN",
           4: "NVFP4_EWORKSPACE", 5: "NVFP4_EHIP"}
@@ -33,6 +33,11 @@ SIGNATURES = {
     "nvfp4_quantize_noalloc": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _u32, _vp, _vp, _vp,
                                 _vp], _i32),
     "nvfp4_noalloc_scratch_bytes": ([], _sz),
+    "nvfp4_balance_workspace_bytes": ([_i64], _sz),
+    "nvfp4_balance_exponents": ([_vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _sz, _vp], _i32),
+    "nvfp4_quantize_balanced": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _u32, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _sz, _vp], _i32),
+    "nvfp4_hadamard128_balanced": ([_vp, _i32, _i64, _vp, _u32, _vp, _vp, _vp], _i32),
     "nvfp4_global_scale": ([_vp, _i32, _i64, _i64, _u32, _vp, _vp, _sz, _vp], _i32),
     "nvfp4_dequantize": ([_vp, _vp, _vp, _i64, _i64, _i32, _vp, _i32, _vp], _i32),
     "nvfp4_quantize_kv_sink": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
@@ -182,9 +187,21 @@ def _offsets(offsets):
     return lo, hi
 
 
+def _balance(balance, K, dev):
+    """(channel exponents, side) of the balancing pair: a device int8 tensor of K
+    exponents (16-byte aligned, contiguous) and "q" or "k"; returns (pointer, flag)."""
+    e, side = balance
+    _expect(e, "balance exponents", (K,), torch.int8, dev)
+    if e.data_ptr() % 16:
+        raise ValueError("balance exponents must be 16-byte aligned")
+    if side not in ("q", "k"):
+        raise ValueError('balance side must be "q" or "k"')
+    return e.data_ptr(), (PAIR_Q if side == "q" else 0)
+
+
 def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
              global_scale: torch.Tensor | None = None, block: int = 16, workspace=None,
-             signs=None, out=None):
+             signs=None, out=None, balance=None):
     """ScaleSearch NVFP4 quantize of x (last dim in blocks of 16).
 
     Returns (codes uint8[..., K/2], scales uint8[..., K/16], global_scale float32[1]).
@@ -192,6 +209,8 @@ def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
     ``signs`` (four uint32 words) selects the randomized Hadamard transform.
     ``out`` = (codes, scales, global_scale) tensors to write instead of new ones
     (the third is ignored when ``global_scale`` is given).
+    ``balance`` = (channel exponents, "q" or "k"): one side of the balancing pair
+    (x 2^-e for Q, x 2^e for K; see ``balance_exponents``) before anything else.
     """
     L = load()
     dev = _dev(x)
@@ -214,7 +233,16 @@ def quantize(x: torch.Tensor, offsets=(-2, 6), hadamard: bool = False,
         g = torch.empty(1, dtype=torch.float32, device=dev)
     ws, wsb = _workspace(workspace, int(L.nvfp4_workspace_bytes(R, K, flags)), dev)
     sw = _signs(signs)
-    if sw is None:
+    if balance is not None:
+        ep, pf = _balance(balance, K, dev)
+        if sw is not None:
+            flags |= HADAMARD128
+        st = L.nvfp4_quantize_balanced(x.data_ptr(), _dtype(x), R, K, block, f_lo, f_hi,
+                                       flags | pf, ep,
+                                       None if sw is None else ctypes.addressof(sw),
+                                       codes.data_ptr(), scales.data_ptr(), g.data_ptr(),
+                                       ws.data_ptr(), wsb, _stream(dev))
+    elif sw is None:
         st = L.nvfp4_quantize(x.data_ptr(), _dtype(x), R, K, block, f_lo, f_hi, flags,
                               codes.data_ptr(), scales.data_ptr(), g.data_ptr(), ws.data_ptr(),
                               wsb, _stream(dev))
@@ -361,16 +389,24 @@ def dequantize_kv_sink(codes, scales, global_scale, sink, T: int, n_first: int, 
     return y
 
 
-def hadamard128(x: torch.Tensor, signs=None) -> torch.Tensor:
+def hadamard128(x: torch.Tensor, signs=None, balance=None) -> torch.Tensor:
     """FP32 y = x H / sqrt(128) per 128-vector (x bf16), as the quantizer computes it;
-    with ``signs``, y = (x o s) H / sqrt(128)."""
+    with ``signs``, y = (x o s) H / sqrt(128); with ``balance`` = (exponents, side)
+    (x[..., 128] only), x is first scaled by 2^-e (side "q") or 2^e ("k")."""
     L = load()
     dev = _dev(x)
     if x.shape[-1] % 128:
         raise ValueError("last dimension must be a multiple of 128")
     y = torch.empty(x.shape, dtype=torch.float32, device=dev)
     sw = _signs(signs)
-    if sw is None:
+    if balance is not None:
+        if x.shape[-1] != 128:
+            raise ValueError("the balancing pair with the transform needs a last dimension of 128")
+        ep, pf = _balance(balance, 128, dev)
+        st = L.nvfp4_hadamard128_balanced(x.data_ptr(), _dtype(x), x.numel() // 128, ep, pf,
+                                          None if sw is None else ctypes.addressof(sw),
+                                          y.data_ptr(), _stream(dev))
+    elif sw is None:
         st = L.nvfp4_hadamard128(x.data_ptr(), _dtype(x), x.numel() // 128, y.data_ptr(),
                                  _stream(dev))
     else:
@@ -378,6 +414,25 @@ def hadamard128(x: torch.Tensor, signs=None) -> torch.Tensor:
                                      ctypes.addressof(sw), y.data_ptr(), _stream(dev))
     _check("nvfp4_hadamard128", st)
     return y
+
+
+def balance_exponents(q: torch.Tensor, k: torch.Tensor, workspace=None) -> torch.Tensor:
+    """Channel exponents (device int8 [D]) of the balancing pair Q' = Q 2^-e, K' = K 2^e
+    from calibration tensors q [..., D] and k [..., D] (same dtype, D % 16 == 0,
+    D <= 2048): per channel the integer e minimising its share of ||Q'||^2 + ||K'||^2."""
+    L = load()
+    dev = _dev(q)
+    _expect(k, "k", None, q.dtype, dev)
+    D = q.shape[-1]
+    if k.shape[-1] != D:
+        raise ValueError("q and k must have the same last dimension")
+    e = torch.empty(D, dtype=torch.int8, device=dev)
+    ws, wsb = _workspace(workspace, int(L.nvfp4_balance_workspace_bytes(D)), dev)
+    st = L.nvfp4_balance_exponents(q.data_ptr(), k.data_ptr(), _dtype(q), q.numel() // D,
+                                   k.numel() // D, D, e.data_ptr(), ws.data_ptr(), wsb,
+                                   _stream(dev))
+    _check("nvfp4_balance_exponents", st)
+    return e
 
 
 def kv_cache_alloc(B: int, H: int, D: int, capacity: int, n_first: int = 128, n_last: int = 128,

@@ -20,6 +20,10 @@ from .oracle import (  # noqa: F401
     hadamard128,
     hadamard128_rht,
     quantize_rht,
+    balance_exponent,
+    balance_exponents,
+    quantize_balanced,
+    hadamard128_balanced,
     quantize_mxfp4,
     dequantize_mxfp4,
     mx_block_sse,

@@ -401,6 +401,9 @@ typedef struct {
     int64_t v0, v1;
     float *y;
     const uint32_t *signs; /* NULL, or 128 bits: bit k set negates input feature k */
+    const int8_t *bal;     /* NULL, or the channel exponents of the balancing pair */
+    int bal_sign;          /* +1 or -1: the side of the pair */
+    int64_t cols;          /* row length (channels), with bal */
 } hjob_t;
 
 /* The Sylvester matrix, entry by entry from its definition; filled before any
@@ -421,6 +424,8 @@ static void hadamard_vectors(const hjob_t *J)
         double in[128];
         for (int k = 0; k < 128; ++k) {
             in[k] = (double)load_elem(J->x, J->dtype, v * 128 + k);
+            if (J->bal) /* exact: a power of two times a binary32 value, in double */
+                in[k] = ldexp(in[k], J->bal_sign * J->bal[(v * 128 + k) % J->cols]);
             if (J->signs && ((J->signs[k >> 5] >> (k & 31)) & 1u))
                 in[k] = -in[k];
         }
@@ -439,8 +444,19 @@ static void *hadamard_thread(void *arg)
     return NULL;
 }
 
+static int hadamard_threads_bal(const void *x, int dtype, int64_t nvec, float *y, int nthreads,
+                                const uint32_t *signs, const int8_t *bal, int bal_sign,
+                                int64_t cols);
+
 static int hadamard_threads(const void *x, int dtype, int64_t nvec, float *y, int nthreads,
                             const uint32_t *signs)
+{
+    return hadamard_threads_bal(x, dtype, nvec, y, nthreads, signs, NULL, 1, 128);
+}
+
+static int hadamard_threads_bal(const void *x, int dtype, int64_t nvec, float *y, int nthreads,
+                                const uint32_t *signs, const int8_t *bal, int bal_sign,
+                                int64_t cols)
 {
     if (nthreads < 1)
         nthreads = 1;
@@ -456,6 +472,9 @@ static int hadamard_threads(const void *x, int dtype, int64_t nvec, float *y, in
         jobs[t].v0 = nvec * t / nthreads;
         jobs[t].v1 = nvec * (t + 1) / nthreads;
         jobs[t].signs = signs;
+        jobs[t].bal = bal;
+        jobs[t].bal_sign = bal_sign;
+        jobs[t].cols = cols;
     }
     fill_hadamard();
     for (int t = 0; t < nthreads; ++t) {
@@ -469,22 +488,23 @@ static int hadamard_threads(const void *x, int dtype, int64_t nvec, float *y, in
     return ORACLE_OK;
 }
 
-int oracle_hadamard128(const void *x, int dtype, int64_t nvec, float *y)
+int oracle_hadamard128(const void *x, int dtype, int64_t nvec, float *y, int nthreads)
 {
     if (!x || !y || nvec < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
         return ORACLE_EINVAL;
-    return hadamard_threads(x, dtype, nvec, y, 1, NULL);
+    return hadamard_threads(x, dtype, nvec, y, nthreads, NULL);
 }
 
 /* Randomized Hadamard transform (QuIP#-style incoherence processing): each
  * 128-vector has the features whose bit is set in signs[4] negated, then is
  * transformed as above: y = (x o s) H / sqrt(128). The random signs are an
  * input (the caller draws them). */
-int oracle_hadamard128_rht(const void *x, int dtype, int64_t nvec, const uint32_t *signs, float *y)
+int oracle_hadamard128_rht(const void *x, int dtype, int64_t nvec, const uint32_t *signs, float *y,
+                           int nthreads)
 {
     if (!x || !y || !signs || nvec < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
         return ORACLE_EINVAL;
-    return hadamard_threads(x, dtype, nvec, y, 1, signs);
+    return hadamard_threads(x, dtype, nvec, y, nthreads, signs);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -571,6 +591,115 @@ int oracle_quantize_rht(const void *x, int dtype, int64_t rows, int64_t cols, co
                              codes, scales, NULL, nthreads);
     free(ybuf);
     return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The additional transform pair of [SSA] 非干渉処理（IP）と絶対値低減: a pair  */
+/* Q' = Q R^-T, K' = K R keeps every score of QK^T and lowers the mean-     */
+/* square magnitude of the projected tensors. The pages fix neither R nor   */
+/* how it is found. Reading: R is diagonal over the channels (the columns)  */
+/* with power-of-two entries, R = diag(2^e_j): then Q'_tj = Q_tj 2^-e_j and */
+/* K'_tj = K_tj 2^e_j, each score term is unchanged exactly, even in binary  */
+/* floating point, and a bf16 operand stays a bf16 value. With the Hadamard */
+/* transform the pair acts first, R_total = diag(2^e) H_s, so that           */
+/* (Q D^-1 H_s)(K D H_s)^T = Q K^T for the orthogonal H_s.                   */
+/* Calibration from a Q and a K tensor: a_j^2 = sum_t Q_tj^2 and b_j^2 =     */
+/* sum_t K_tj^2 (double, rows in order); channel j's share of ||Q'||^2 +     */
+/* ||K'||^2 is f(e) = a^2 4^-e + b^2 4^e, convex in e, and f(e) <= f(e + 1)  */
+/* exactly when a^2 <= b^2 4^(2e+1); e_j is the least e in [-16, 16] with    */
+/* that property (16 if none), so ties go to the smaller e; a channel with   */
+/* a or b zero keeps e_j = 0.                                                */
+/* ------------------------------------------------------------------------ */
+static void column_sumsq(const void *x, int dtype, int64_t rows, int64_t cols, double *out)
+{
+    for (int64_t j = 0; j < cols; ++j)
+        out[j] = 0.0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j) {
+            double v = (double)load_elem(x, dtype, r * cols + j);
+            out[j] += v * v;
+        }
+}
+
+int oracle_balance_exponent(double a2, double b2)
+{
+    if (!(a2 > 0.0) || !(b2 > 0.0))
+        return 0;
+    for (int e = -16; e <= 15; ++e)
+        if (a2 <= ldexp(b2, 2 * (2 * e + 1)))
+            return e;
+    return 16;
+}
+
+int oracle_balance_exponents(const void *q, const void *k, int dtype, int64_t rows_q,
+                             int64_t rows_k, int64_t cols, int8_t *e_out)
+{
+    if (!q || !k || !e_out || rows_q < 0 || rows_k < 0 || cols <= 0 ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    double *a2 = malloc(sizeof(double) * (size_t)cols), *b2 = malloc(sizeof(double) * (size_t)cols);
+    if (!a2 || !b2) {
+        free(a2);
+        free(b2);
+        return ORACLE_ENOMEM;
+    }
+    column_sumsq(q, dtype, rows_q, cols, a2);
+    column_sumsq(k, dtype, rows_k, cols, b2);
+    for (int64_t j = 0; j < cols; ++j)
+        e_out[j] = (int8_t)oracle_balance_exponent(a2[j], b2[j]);
+    free(a2);
+    free(b2);
+    return ORACLE_OK;
+}
+
+/* Quantize one side of the pair: x'_tj = x_tj 2^(side e_j) (side = -1 for Q,
+ * +1 for K; e_j clamped to [-32, 32]), then the quantizer. Without the Hadamard transform x' is formed
+ * in binary32 (exact unless it leaves the normal range) and quantized as FP32
+ * values; with it (hadamard, signs optional for the randomized transform),
+ * the scaled values enter the transform's double sum exactly. */
+int oracle_quantize_balanced(const void *x, int dtype, int64_t rows, int64_t cols,
+                             const int8_t *e, int side, int hadamard, const uint32_t *signs,
+                             int f_lo, int f_hi, int gscale_given, float *gscale,
+                             uint8_t *codes, uint8_t *scales, int nthreads)
+{
+    if (!x || !e || (side != 1 && side != -1) || rows < 0 || cols <= 0 || cols % 16 ||
+        (hadamard && cols % 128) || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    int8_t *ec = malloc((size_t)cols);
+    if (!ec)
+        return ORACLE_ENOMEM;
+    for (int64_t j = 0; j < cols; ++j) /* the exponents are clamped to [-32, 32] */
+        ec[j] = (int8_t)(e[j] < -32 ? -32 : (e[j] > 32 ? 32 : e[j]));
+    e = ec;
+    int64_t n = rows * cols;
+    float *ybuf = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!ybuf) {
+        free(ec);
+        return ORACLE_ENOMEM;
+    }
+    if (hadamard) {
+        hadamard_threads_bal(x, dtype, n / 128, ybuf, nthreads, signs, e, side, cols);
+    } else {
+        for (int64_t i = 0; i < n; ++i)
+            ybuf[i] = ldexpf(load_elem(x, dtype, i), side * e[i % cols]);
+    }
+    int rc = oracle_quantize(ybuf, ORACLE_F32, rows, cols, f_lo, f_hi, 0, gscale_given, gscale,
+                             codes, scales, NULL, nthreads);
+    free(ybuf);
+    free(ec);
+    return rc;
+}
+
+/* The transform alone (inspection and split parity): y = (x D^side o s) H /
+ * sqrt(128) per 128-vector, D = diag(2^e) over the row's cols channels. */
+int oracle_hadamard128_balanced(const void *x, int dtype, int64_t rows, int64_t cols,
+                                const int8_t *e, int side, const uint32_t *signs, float *y,
+                                int nthreads)
+{
+    if (!x || !y || !e || (side != 1 && side != -1) || rows < 0 || cols <= 0 || cols % 128 ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return ORACLE_EINVAL;
+    return hadamard_threads_bal(x, dtype, rows * cols / 128, y, nthreads, signs, e, side, cols);
 }
 
 /* Round binary32 to bfloat16, nearest-even (NaN -> quiet NaN, sign kept). */

@@ -72,12 +72,21 @@ def lib() -> ctypes.CDLL:
             L.oracle_dequantize_kv_sink.argtypes = [vp, vp, f32, vp, i32, i64, i64, i64, i64, i64,
                                                     i64, i32, vp]
             L.oracle_dequantize_kv_sink.restype = i32
-            L.oracle_hadamard128.argtypes = [vp, i32, i64, vp]
+            L.oracle_hadamard128.argtypes = [vp, i32, i64, vp, i32]
             L.oracle_hadamard128.restype = i32
-            L.oracle_hadamard128_rht.argtypes = [vp, i32, i64, vp, vp]
+            L.oracle_hadamard128_rht.argtypes = [vp, i32, i64, vp, vp, i32]
             L.oracle_hadamard128_rht.restype = i32
             L.oracle_quantize_rht.argtypes = [vp, i32, i64, i64, vp, i32, i32, i32, vp, vp, vp, i32]
             L.oracle_quantize_rht.restype = i32
+            L.oracle_balance_exponent.argtypes = [ctypes.c_double, ctypes.c_double]
+            L.oracle_balance_exponent.restype = i32
+            L.oracle_balance_exponents.argtypes = [vp, vp, i32, i64, i64, i64, vp]
+            L.oracle_balance_exponents.restype = i32
+            L.oracle_quantize_balanced.argtypes = [vp, i32, i64, i64, vp, i32, i32, vp, i32, i32,
+                                                   i32, vp, vp, vp, i32]
+            L.oracle_quantize_balanced.restype = i32
+            L.oracle_hadamard128_balanced.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, i32]
+            L.oracle_hadamard128_balanced.restype = i32
             L.oracle_quantize_mxfp4.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, i32]
             L.oracle_quantize_mxfp4.restype = i32
             L.oracle_dequantize_mxfp4.argtypes = [vp, vp, i64, i64, i32, vp]
@@ -209,13 +218,13 @@ def dequantize_kv_sink(codes, scales, gscale, sink, T: int, n_first: int, n_last
     return y
 
 
-def hadamard128(x: np.ndarray) -> np.ndarray:
+def hadamard128(x: np.ndarray, nthreads: int | None = None) -> np.ndarray:
     x = np.ascontiguousarray(x)
     dt = _dtype_of(x)
     if x.shape[-1] % 128:
         raise ValueError("last dimension must be a multiple of 128")
     y = np.empty(x.shape, dtype=np.float32)
-    rc = lib().oracle_hadamard128(_ptr(x), dt, x.size // 128, _ptr(y))
+    rc = lib().oracle_hadamard128(_ptr(x), dt, x.size // 128, _ptr(y), _threads(nthreads))
     if rc:
         raise ValueError(f"oracle_hadamard128 failed ({rc})")
     return y
@@ -229,12 +238,13 @@ def _signs_words(signs) -> np.ndarray:
     return w
 
 
-def hadamard128_rht(x: np.ndarray, signs) -> np.ndarray:
+def hadamard128_rht(x: np.ndarray, signs, nthreads: int | None = None) -> np.ndarray:
     x = np.ascontiguousarray(x)
     dt = _dtype_of(x)
     w = _signs_words(signs)
     y = np.empty(x.shape, dtype=np.float32)
-    rc = lib().oracle_hadamard128_rht(_ptr(x), dt, x.size // 128, _ptr(w), _ptr(y))
+    rc = lib().oracle_hadamard128_rht(_ptr(x), dt, x.size // 128, _ptr(w), _ptr(y),
+                                      _threads(nthreads))
     if rc:
         raise ValueError(f"oracle_hadamard128_rht failed ({rc})")
     return y
@@ -256,6 +266,69 @@ def quantize_rht(x: np.ndarray, signs, f_lo: int = -8, f_hi: int = 8, gscale: fl
         raise ValueError(f"oracle_quantize_rht failed ({rc})")
     shp = x.shape[:-1]
     return codes.reshape(*shp, K // 2), scales.reshape(*shp, K // 16), np.float32(g[0])
+
+
+def balance_exponent(a2: float, b2: float) -> int:
+    """The channel exponent of the balancing pair for sums of squares a2 (Q) and b2 (K)."""
+    return int(lib().oracle_balance_exponent(float(a2), float(b2)))
+
+
+def balance_exponents(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Channel exponents e (int8 [D]) of the balancing pair Q' = Q diag(2^-e),
+    K' = K diag(2^e), from calibration tensors q [..., D] and k [..., D] (same dtype)."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    dt = _dtype_of(q)
+    if _dtype_of(k) != dt or q.shape[-1] != k.shape[-1]:
+        raise ValueError("q and k: same dtype and last dimension")
+    D = q.shape[-1]
+    e = np.zeros(D, dtype=np.int8)
+    rc = lib().oracle_balance_exponents(_ptr(q), _ptr(k), dt, q.size // D, k.size // D, D, _ptr(e))
+    if rc:
+        raise ValueError(f"oracle_balance_exponents failed ({rc})")
+    return e
+
+
+def quantize_balanced(x: np.ndarray, e, side: int, f_lo: int = -2, f_hi: int = 6,
+                      hadamard: bool = False, signs=None, gscale: float | None = None,
+                      nthreads: int | None = None):
+    """Quantize one side of the balancing pair: x diag(2^(side e)) (side -1 for Q, +1
+    for K), optionally followed by the (randomized, with signs) Hadamard transform."""
+    x = np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    K = x.shape[-1]
+    R = x.size // K
+    e = np.ascontiguousarray(e, dtype=np.int8)
+    if e.shape != (K,):
+        raise ValueError("e: one exponent per column")
+    w = None if signs is None else _signs_words(signs)
+    codes = np.empty((R, K // 2), dtype=np.uint8)
+    scales = np.empty((R, K // 16), dtype=np.uint8)
+    g = np.array([0.0 if gscale is None else gscale], dtype=np.float32)
+    rc = lib().oracle_quantize_balanced(_ptr(x), dt, R, K, _ptr(e), int(side), int(hadamard),
+                                        None if w is None else _ptr(w), f_lo, f_hi,
+                                        int(gscale is not None), _ptr(g), _ptr(codes),
+                                        _ptr(scales), _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_quantize_balanced failed ({rc})")
+    shp = x.shape[:-1]
+    return codes.reshape(*shp, K // 2), scales.reshape(*shp, K // 16), np.float32(g[0])
+
+
+def hadamard128_balanced(x: np.ndarray, e, side: int, signs=None,
+                         nthreads: int | None = None) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    K = x.shape[-1]
+    e = np.ascontiguousarray(e, dtype=np.int8)
+    w = None if signs is None else _signs_words(signs)
+    y = np.empty(x.shape, dtype=np.float32)
+    rc = lib().oracle_hadamard128_balanced(_ptr(x), dt, x.size // K, K, _ptr(e), int(side),
+                                           None if w is None else _ptr(w), _ptr(y),
+                                           _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_hadamard128_balanced failed ({rc})")
+    return y
 
 
 def quantize_mxfp4(x: np.ndarray, f_lo: int = 0, f_hi: int = 0, nthreads: int | None = None):

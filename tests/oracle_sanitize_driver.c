@@ -16,8 +16,13 @@ int oracle_quantize_kv_sink(const void *, int, int64_t, int64_t, int64_t, int64_
                             int);
 int oracle_dequantize_kv_sink(const uint8_t *, const uint8_t *, float, const void *, int, int64_t,
                               int64_t, int64_t, int64_t, int64_t, int64_t, int, void *);
-int oracle_hadamard128(const void *, int, int64_t, float *);
-int oracle_hadamard128_rht(const void *, int, int64_t, const uint32_t *, float *);
+int oracle_hadamard128(const void *, int, int64_t, float *, int);
+int oracle_hadamard128_rht(const void *, int, int64_t, const uint32_t *, float *, int);
+int oracle_balance_exponents(const void *, const void *, int, int64_t, int64_t, int64_t, int8_t *);
+int oracle_quantize_balanced(const void *, int, int64_t, int64_t, const int8_t *, int, int,
+                             const uint32_t *, int, int, int, float *, uint8_t *, uint8_t *, int);
+int oracle_hadamard128_balanced(const void *, int, int64_t, int64_t, const int8_t *, int,
+                                const uint32_t *, float *, int);
 int oracle_quantize_rht(const void *, int, int64_t, int64_t, const uint32_t *, int, int, int,
                         float *, uint8_t *, uint8_t *, int);
 int oracle_quantize_mxfp4(const void *, int, int64_t, int64_t, int, int, uint8_t *, uint8_t *,
@@ -76,10 +81,22 @@ int main(void) {
     CHECK(oracle_quantize(xb, 1, R, K, -8, 8, 1, 0, &g, codes, scales, NULL, 2));
     CHECK(oracle_dequantize(codes, scales, g, R, K, 0, y));
     CHECK(oracle_dequantize(codes, scales, g, R, K, 1, xb));
-    CHECK(oracle_hadamard128(xb, 1, R * K / 128, y));
+    CHECK(oracle_hadamard128(xb, 1, R * K / 128, y, 2));
     uint32_t signs[4] = {0x12345678u, 0x9abcdef0u, 0x0f0f0f0fu, 0xdeadbeefu};
-    CHECK(oracle_hadamard128_rht(xb, 1, R * K / 128, signs, y));
+    CHECK(oracle_hadamard128_rht(xb, 1, R * K / 128, signs, y, 2));
     CHECK(oracle_quantize_rht(xb, 1, R, K, signs, -8, 8, 0, &g, codes, scales, 2));
+    /* the balancing pair: calibration, both sides, with and without the transform */
+    int8_t *e = malloc(K);
+    CHECK(oracle_balance_exponents(xb, x, 1, R, 0, K, e)); /* K rows 0: every e is 0 */
+    CHECK(oracle_balance_exponents(xb, xb, 1, R / 2, R - R / 2, K, e));
+    for (int j = 0; j < K; j += 7) e[j] = (int8_t)(j % 5 - 2);
+    e[3] = 100; /* clamped */
+    CHECK(oracle_quantize_balanced(xb, 1, R, K, e, -1, 0, NULL, -2, 6, 0, &g, codes, scales, 2));
+    CHECK(oracle_quantize_balanced(x, 0, R, K, e, 1, 0, NULL, -8, 8, 0, &g, codes, scales, 2));
+    CHECK(oracle_quantize_balanced(xb, 1, R * 2, 128, e, 1, 1, signs, -8, 8, 0, &g, codes, scales,
+                                   2));
+    CHECK(oracle_hadamard128_balanced(xb, 1, R * 2, 128, e, -1, NULL, y, 2));
+    free(e);
     CHECK(oracle_quantize_mxfp4(x, 0, R, K, -1, 1, codes, scales, 2));
     CHECK(oracle_dequantize_mxfp4(codes, scales, R, K, 1, xb));
 

@@ -279,3 +279,39 @@ def test_kv_append2_argument_checks(lib):
     bad = ref(P + 68)
     assert f(addr(k), addr(bad), *shape()) == 3          # V's length not 8-byte aligned
     assert f(addr(k), addr(v), *shape(t_new=0)) == 0     # nothing to append: no launch
+
+
+def _call(fn, names, defaults, kw):
+    a = {**defaults, **kw}
+    return fn(*[a[n] for n in names])
+
+
+def test_balance_argument_checks(lib):
+    """The balancing pair's entry points check on the host before any launch."""
+    qn = ("x", "xdt", "rows", "cols", "block", "f_lo", "f_hi", "flags", "e", "signs", "codes",
+          "scales", "gs", "ws", "wsb", "stream")
+    qd = dict(x=P, xdt=1, rows=4, cols=128, block=16, f_lo=-2, f_hi=6, flags=0, e=P, signs=None,
+              codes=P, scales=P, gs=P, ws=P, wsb=1 << 20, stream=None)
+    bq = lambda **kw: _call(lib.nvfp4_quantize_balanced, qn, qd, kw)
+    assert bq(e=None) == 1                      # no exponents
+    assert bq(flags=8) == 1                     # unknown flag
+    assert bq(signs=P) == 1                     # signs without the transform
+    assert bq(flags=1, cols=256) == 2           # transform needs cols == 128
+    assert bq(flags=1, xdt=0) == 1              # transform needs bf16
+    assert bq(e=P + 8) == 3                     # exponents 16-byte aligned
+    assert bq(wsb=16) == 4
+    assert bq(cols=24) == 2
+    ws = lib.nvfp4_balance_workspace_bytes
+    assert ws(128) == 2 * 256 * 128 * 8 and ws(0) == 0 and ws(4096) == 0
+    en = ("q", "k", "dt", "rq", "rk", "cols", "e", "ws", "wsb", "stream")
+    ed = dict(q=P, k=P, dt=1, rq=8, rk=8, cols=128, e=P, ws=P, wsb=1 << 20, stream=None)
+    be = lambda **kw: _call(lib.nvfp4_balance_exponents, en, ed, kw)
+    assert be(e=None) == 1 and be(dt=5) == 1 and be(q=None) == 1
+    assert be(cols=24) == 2 and be(cols=4096) == 2 and be(rq=-1) == 2
+    assert be(k=P + 4) == 3
+    assert be(wsb=1024) == 4 and be(ws=P + 4) == 4
+    hn = ("x", "xdt", "rows", "e", "flags", "signs", "y", "stream")
+    hd = dict(x=P, xdt=1, rows=4, e=P, flags=0, signs=None, y=P, stream=None)
+    hb = lambda **kw: _call(lib.nvfp4_hadamard128_balanced, hn, hd, kw)
+    assert hb(xdt=0) == 1 and hb(e=None) == 1 and hb(flags=1) == 1 and hb(rows=-1) == 2
+    assert hb(y=P + 4) == 3
