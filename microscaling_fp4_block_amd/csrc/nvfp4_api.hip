@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstring>
 #include <mutex>
 
 #include "../../include/mxfp4.h"
@@ -16,7 +17,18 @@ namespace {
 
 constexpr int64_t kMaxBlocks = 1ll << 29;  // 32-bit chunk and block indices never overflow
 
-bool dtype_ok(nvfp4_dtype d) { return d == NVFP4_F32 || d == NVFP4_BF16; }
+// A C caller may pass any int as an enum argument; read it as an int, so that an
+// out-of-range value is rejected without being loaded as the C++ enum type.
+template <class E>
+int enum_int(const E &e) {
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+bool dtype_ok(const nvfp4_dtype &d) {
+  const int v = enum_int(d);
+  return v == NVFP4_F32 || v == NVFP4_BF16;
+}
 // a * b <= lim for a, b >= 0, decided without forming a product that could overflow
 bool prod_le(int64_t a, int64_t b, int64_t lim) { return a == 0 || b <= lim / a; }
 constexpr int64_t k2p31 = 1ll << 31;
@@ -110,12 +122,12 @@ nvfp4_status check_offsets(int block, int f_lo, int f_hi) {
   return NVFP4_OK;
 }
 
-nvfp4_status check_shape(int64_t rows, int64_t cols, uint32_t flags, nvfp4_dtype dt) {
+nvfp4_status check_shape(int64_t rows, int64_t cols, uint32_t flags, const nvfp4_dtype &dt) {
   if (rows < 0 || cols <= 0 || cols % 16) return NVFP4_ESHAPE;
   if (cols > (1ll << 30) || (rows > 0 && rows > kMaxBlocks / (cols / 16))) return NVFP4_ESHAPE;
   if (flags & ~(NVFP4_HADAMARD128 | NVFP4_GSCALE_GIVEN)) return NVFP4_EINVAL;
   if (flags & NVFP4_HADAMARD128) {
-    if (dt != NVFP4_BF16) return NVFP4_EINVAL;
+    if (enum_int(dt) != NVFP4_BF16) return NVFP4_EINVAL;
     if (cols % 128) return NVFP4_ESHAPE;
   }
   return NVFP4_OK;
@@ -126,7 +138,7 @@ nvfp4_status check_shape(int64_t rows, int64_t cols, uint32_t flags, nvfp4_dtype
 extern "C" {
 
 const char *nvfp4_status_str(nvfp4_status s) {
-  switch (s) {
+  switch (enum_int(s)) {
     case NVFP4_OK: return "ok";
     case NVFP4_EINVAL: return "invalid argument";
     case NVFP4_ESHAPE: return "invalid shape";
@@ -153,7 +165,7 @@ namespace {
 // The entry points below with signs == nullptr (plain transform or none), and
 // the *_rht entry points with the caller's signs and the transform forced on.
 
-nvfp4_status global_scale_impl(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols,
+nvfp4_status global_scale_impl(const void *x, const nvfp4_dtype &xdt, int64_t rows, int64_t cols,
                                uint32_t flags, const uint32_t *signs, float *global_scale,
                                void *workspace, size_t workspace_bytes, void *stream) {
   if (!global_scale || !dtype_ok(xdt)) return NVFP4_EINVAL;
@@ -163,11 +175,11 @@ nvfp4_status global_scale_impl(const void *x, nvfp4_dtype xdt, int64_t rows, int
   if (!aligned(x, 16)) return NVFP4_EALIGN;
   if (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4))
     return NVFP4_EWORKSPACE;
-  return run_global_scale(x, xdt == NVFP4_BF16, flags & NVFP4_HADAMARD128, make_signs(signs),
+  return run_global_scale(x, enum_int(xdt) == NVFP4_BF16, flags & NVFP4_HADAMARD128, make_signs(signs),
                           plain_map(rows, cols), global_scale, workspace, (hipStream_t)stream);
 }
 
-nvfp4_status quantize_impl(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t cols, int block,
+nvfp4_status quantize_impl(const void *x, const nvfp4_dtype &xdt, int64_t rows, int64_t cols, int block,
                            int f_lo, int f_hi, uint32_t flags, const uint32_t *signs,
                            uint8_t *codes, uint8_t *scales, float *global_scale, void *workspace,
                            size_t workspace_bytes, void *stream) {
@@ -182,7 +194,7 @@ nvfp4_status quantize_impl(const void *x, nvfp4_dtype xdt, int64_t rows, int64_t
   if (!given && (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4)))
     return NVFP4_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = xdt == NVFP4_BF16;
+  const bool bf16 = enum_int(xdt) == NVFP4_BF16;
   const bool had = flags & NVFP4_HADAMARD128;
   return run_quantize_region(x, bf16, had, make_signs(signs), given, plain_map(rows, cols), f_lo,
                              f_hi, codes, scales, global_scale, workspace, s);
@@ -302,14 +314,14 @@ nvfp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
   if (!aligned(codes, 8) || !aligned(y, 16)) return NVFP4_EALIGN;
   DequantArgs a{codes, scales, global_scale, y, (uint32_t)(rows * (cols / 16))};
   if (a.nblocks == 0) return NVFP4_OK;
-  return hip_status(launch_dequantize(a, ydt == NVFP4_BF16, (hipStream_t)stream));
+  return hip_status(launch_dequantize(a, enum_int(ydt) == NVFP4_BF16, (hipStream_t)stream));
 }
 
 }  // extern "C"
 
 namespace {
 
-nvfp4_status kv_sink_impl(const void *kv, nvfp4_dtype dt, int64_t B, int64_t H, int64_t T,
+nvfp4_status kv_sink_impl(const void *kv, const nvfp4_dtype &dt, int64_t B, int64_t H, int64_t T,
                           int64_t D, int64_t n_first, int64_t n_last, int block, int f_lo,
                           int f_hi, uint32_t flags, const uint32_t *signs, uint8_t *codes,
                           uint8_t *scales, float *global_scale, void *sink, void *workspace,
@@ -331,7 +343,7 @@ nvfp4_status kv_sink_impl(const void *kv, nvfp4_dtype dt, int64_t B, int64_t H, 
   if (!given && (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4)))
     return NVFP4_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dt == NVFP4_BF16;
+  const bool bf16 = enum_int(dt) == NVFP4_BF16;
   const bool had = flags & NVFP4_HADAMARD128;
   const uint32_t es = bf16 ? 2u : 4u;
 
@@ -425,14 +437,14 @@ nvfp4_status nvfp4_dequantize_kv_sink(const uint8_t *codes, const uint8_t *scale
   a.n_last = (uint32_t)n_last;
   if (a.nblocks == 0) return NVFP4_OK;
   return hip_status(
-      launch_dequantize_kv(a, sink_dt == NVFP4_BF16, ydt == NVFP4_BF16, (hipStream_t)stream));
+      launch_dequantize_kv(a, enum_int(sink_dt) == NVFP4_BF16, enum_int(ydt) == NVFP4_BF16, (hipStream_t)stream));
 }
 
 }  // extern "C"
 
 namespace {
 
-nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H, int64_t T,
+nvfp4_status kv_append_impl(const void *kv_new, const nvfp4_dtype &dt, int64_t B, int64_t H, int64_t T,
                             int64_t t_new, int64_t D, int64_t n_first, int64_t n_last,
                             int64_t cap, int block, int f_lo, int f_hi, uint32_t flags,
                             const uint32_t *signs, const float *global_scale, void *head,
@@ -449,7 +461,7 @@ nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64
     return NVFP4_ESHAPE;
   if (T + t_new > k2p31) return NVFP4_ESHAPE;
   const bool had = flags & NVFP4_HADAMARD128;
-  if (had && (dt != NVFP4_BF16)) return NVFP4_EINVAL;
+  if (had && (enum_int(dt) != NVFP4_BF16)) return NVFP4_EINVAL;
   if (had && D % 128) return NVFP4_ESHAPE;
   const int64_t BH = B * H, T2 = T + t_new;
   // tokens entering the middle: [lo, hi); the middle must hold rows up to hi - n_first
@@ -468,7 +480,7 @@ nvfp4_status kv_append_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64
   if (!aligned(kv_new, 16) || !aligned(head, 16) || !aligned(tail, 16) || !aligned(codes, 8))
     return NVFP4_EALIGN;
   hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dt == NVFP4_BF16;
+  const bool bf16 = enum_int(dt) == NVFP4_BF16;
   const uint32_t es = bf16 ? 2u : 4u;
 
   // 1. code the tokens that leave the recent window (before the ring is overwritten)
@@ -532,7 +544,7 @@ struct KvAppendPlan {
   bool empty, small;
 };
 
-nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, int64_t H,
+nvfp4_status kv_append_dev_impl(const void *kv_new, const nvfp4_dtype &dt, int64_t B, int64_t H,
                                 int64_t t_new, int64_t D, int64_t n_first, int64_t n_last,
                                 int64_t cap, int block, int f_lo, int f_hi, uint32_t flags,
                                 const uint32_t *signs, const float *global_scale, void *head,
@@ -549,7 +561,7 @@ nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, i
   const int64_t total = n_first + cap + n_last;
   if (total > k2p31) return NVFP4_ESHAPE;
   const bool had = flags & NVFP4_HADAMARD128;
-  if (had && (dt != NVFP4_BF16)) return NVFP4_EINVAL;
+  if (had && (enum_int(dt) != NVFP4_BF16)) return NVFP4_EINVAL;
   if (had && D % 128) return NVFP4_ESHAPE;
   const int64_t BH = B * H;
   st = check_shape(BH * t_new, D, 0, dt);
@@ -566,7 +578,7 @@ nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, i
   if (plan) plan->empty = t_new == 0;
   if (t_new == 0) return NVFP4_OK;
   hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dt == NVFP4_BF16;
+  const bool bf16 = enum_int(dt) == NVFP4_BF16;
   const uint32_t es = bf16 ? 2u : 4u;
   QuantArgs q{};
   q.gscale = (float *)global_scale;
@@ -626,9 +638,9 @@ nvfp4_status kv_append_dev_impl(const void *kv_new, nvfp4_dtype dt, int64_t B, i
   return hip_status(launch_advance_length(length, (uint32_t)t_new, (uint32_t)total, s));
 }
 
-nvfp4_status hadamard_impl(const void *x, nvfp4_dtype xdt, int64_t rows, const uint32_t *signs,
+nvfp4_status hadamard_impl(const void *x, const nvfp4_dtype &xdt, int64_t rows, const uint32_t *signs,
                            float *y, void *stream) {
-  if (xdt != NVFP4_BF16) return NVFP4_EINVAL;
+  if (enum_int(xdt) != NVFP4_BF16) return NVFP4_EINVAL;
   if (rows < 0 || rows > kMaxBlocks / 8) return NVFP4_ESHAPE;
   if (rows == 0) return NVFP4_OK;
   if (!x || !y) return NVFP4_EINVAL;
@@ -698,7 +710,7 @@ nvfp4_status nvfp4_kv_append2_dev(const nvfp4_kv_cache_ref *k, const nvfp4_kv_ca
       p.len[i] = r[i]->length;
     }
     p.row_bytes = plan[0].c.chunks_per_row * 16u;
-    return hip_status(launch_kv_append_small_pair(p, dt == NVFP4_BF16, (hipStream_t)stream));
+    return hip_status(launch_kv_append_small_pair(p, enum_int(dt) == NVFP4_BF16, (hipStream_t)stream));
   }
   for (int i = 0; i < 2; ++i) {
     const nvfp4_kv_cache_ref &c = *r[i];
@@ -733,7 +745,7 @@ nvfp4_status mxfp4_quantize(const void *x, nvfp4_dtype xdt, int64_t rows, int64_
   if (!x || !codes || !scales) return NVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16)) return NVFP4_EALIGN;
   MxArgs a{x, codes, scales, (uint32_t)(rows * (cols / 32)), f_lo, f_hi};
-  return hip_status(launch_mx_quantize(a, xdt == NVFP4_BF16, (hipStream_t)stream));
+  return hip_status(launch_mx_quantize(a, enum_int(xdt) == NVFP4_BF16, (hipStream_t)stream));
 }
 
 nvfp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
@@ -745,7 +757,7 @@ nvfp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64
   if (!codes || !scales || !y) return NVFP4_EINVAL;
   if (!aligned(codes, 16) || !aligned(y, 16)) return NVFP4_EALIGN;
   MxDequantArgs a{codes, scales, y, (uint32_t)(rows * (cols / 32))};
-  return hip_status(launch_mx_dequantize(a, ydt == NVFP4_BF16, (hipStream_t)stream));
+  return hip_status(launch_mx_dequantize(a, enum_int(ydt) == NVFP4_BF16, (hipStream_t)stream));
 }
 
 nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_scales,
@@ -784,7 +796,7 @@ nvfp4_status nvfp4_attention(const uint8_t *q_codes, const uint8_t *q_scales,
   a.Nk = (uint32_t)Nk;
   a.causal = causal ? 1u : 0u;
   a.tau_log2e = (float)(1.4426950408889634 / sqrt(128.0));
-  return hip_status(launch_attention(a, out_dt == NVFP4_BF16, (hipStream_t)stream));
+  return hip_status(launch_attention(a, enum_int(out_dt) == NVFP4_BF16, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -803,11 +815,11 @@ nvfp4_status attention_kv_cache_impl(
     const uint8_t *q_codes, const uint8_t *q_scales, const float *q_gscale, const void *k_head,
     const void *k_tail, const uint8_t *k_codes, const uint8_t *k_scales, const float *k_gscale,
     const void *v_head, const void *v_tail, const uint8_t *v_codes, const uint8_t *v_scales,
-    const float *v_gscale, nvfp4_dtype cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+    const float *v_gscale, const nvfp4_dtype &cache_dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
     int64_t T, const int64_t *len_dev, int64_t D, int64_t n_first, int64_t n_last, int64_t cap,
-    int64_t split, void *workspace, size_t workspace_bytes, void *out, nvfp4_dtype out_dt,
+    int64_t split, void *workspace, size_t workspace_bytes, void *out, const nvfp4_dtype &out_dt,
     void *stream) {
-  if (!dtype_ok(out_dt) || cache_dt != NVFP4_BF16) return NVFP4_EINVAL;
+  if (!dtype_ok(out_dt) || enum_int(cache_dt) != NVFP4_BF16) return NVFP4_EINVAL;
   if (split < 0 || split % 32 || split > (1ll << 30)) return NVFP4_EINVAL;
   if (D != 128) return NVFP4_ESHAPE;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Nq < 0 || T < 0 || n_first < 0 || n_last < 0 ||
@@ -870,7 +882,7 @@ nvfp4_status attention_kv_cache_impl(
     a.part = (float *)workspace;
     a.ml = (float2 *)((float *)workspace + part);
   }
-  return hip_status(launch_attention(a, out_dt == NVFP4_BF16, (hipStream_t)stream));
+  return hip_status(launch_attention(a, enum_int(out_dt) == NVFP4_BF16, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -982,7 +994,7 @@ nvfp4_status nvfp4_balance_exponents(const void *q, const void *k, nvfp4_dtype d
   if (!workspace || workspace_bytes < balance_ws(cols) || !aligned(workspace, 8))
     return NVFP4_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dt == NVFP4_BF16;
+  const bool bf16 = enum_int(dt) == NVFP4_BF16;
   double *qp = (double *)workspace, *kp = qp + (size_t)kColSumGroups * (size_t)cols;
   if (launch_colsumsq(ColSumArgs{q, (uint32_t)rows_q, (uint32_t)cols, qp}, bf16, s) != hipSuccess)
     return NVFP4_EHIP;
@@ -1010,7 +1022,7 @@ nvfp4_status nvfp4_quantize_balanced(const void *x, nvfp4_dtype xdt, int64_t row
   const bool given = flags & NVFP4_GSCALE_GIVEN;
   if (!given && (!workspace || workspace_bytes < workspace_needed() || !aligned(workspace, 4)))
     return NVFP4_EWORKSPACE;
-  return run_quantize_region(x, xdt == NVFP4_BF16, had, make_signs(signs), given,
+  return run_quantize_region(x, enum_int(xdt) == NVFP4_BF16, had, make_signs(signs), given,
                              plain_map(rows, cols), f_lo, f_hi, codes, scales, global_scale,
                              workspace, (hipStream_t)stream, make_balance(chan_exp, flags));
 }
@@ -1018,7 +1030,7 @@ nvfp4_status nvfp4_quantize_balanced(const void *x, nvfp4_dtype xdt, int64_t row
 nvfp4_status nvfp4_hadamard128_balanced(const void *x, nvfp4_dtype xdt, int64_t rows,
                                         const int8_t *chan_exp, uint32_t flags,
                                         const uint32_t *signs, float *y, void *stream) {
-  if (xdt != NVFP4_BF16 || !chan_exp || (flags & ~NVFP4_PAIR_Q)) return NVFP4_EINVAL;
+  if (enum_int(xdt) != NVFP4_BF16 || !chan_exp || (flags & ~NVFP4_PAIR_Q)) return NVFP4_EINVAL;
   if (rows < 0 || rows > kMaxBlocks / 8) return NVFP4_ESHAPE;
   if (!aligned(chan_exp, 16)) return NVFP4_EALIGN;
   if (rows == 0) return NVFP4_OK;

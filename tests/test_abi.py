@@ -15,6 +15,13 @@ HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 def lib():
     from microscaling_fp4_block_amd import build, nvfp4
 
+    alt = os.environ.get("NVFP4_ABI_TEST_LIB")
+    if alt:  # a separately built copy (the sanitizer run of tests/test_api_sanitizers.py)
+        L = ctypes.CDLL(alt)
+        for name, (args, res) in nvfp4.SIGNATURES.items():
+            getattr(L, name).argtypes = args
+            getattr(L, name).restype = res
+        return L
     if not os.path.exists(nvfp4.LIB_PATH):
         build.build()
     return nvfp4.load()
