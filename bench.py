@@ -656,6 +656,24 @@ def attention_profile(torch, nv, workloads, launches: int = 5):
     torch.cuda.synchronize()
 
 
+def hadamard_profile(torch, nv, workloads, launches: int = 5):
+    """Short run for rocprofv3: workload 5 (bf16 Q [1, 32, 32768, 128]) quantized with the
+    Hadamard transform and offsets [-8, 8] -- `launches` whole calls (amax pass with the
+    transform, then the search pass with it), then the three 1 GiB device copies that
+    calibrate the byte counters."""
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(workloads.workload(5).view(np.int16)).view(torch.bfloat16).to(dev)
+    ws = torch.empty(nv.workspace_bytes(x.numel() // 128, 128), dtype=torch.uint8, device=dev)
+    for _ in range(launches):
+        nv.quantize(x, (-8, 8), hadamard=True, workspace=ws)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("[bench] hadamard profile run done", file=sys.stderr, flush=True)
+
+
 def decode_profile(torch, nv, workloads, split: int = 160, launches: int = 5):
     """Short run for rocprofv3: K and V sink caches of 128 + 32768 + 128 tokens
     ([1, 8, *, 128], workload-3 recipe, ScaleSearch [-2, 6]), one query per head for 32
@@ -763,6 +781,9 @@ def main():
                          "head over 32K-token caches")
     ap.add_argument("--decode-split", type=int, default=160,
                     help="piece size of --decode-profile (middle tokens per unit)")
+    ap.add_argument("--hadamard-profile", action="store_true",
+                    help="short run for rocprofv3: workload 5 quantized with the Hadamard "
+                         "transform, offsets [-8, 8]")
     ap.add_argument("--attention-profile", action="store_true",
                     help="short run for rocprofv3: five non-causal attention launches at 32K")
     ap.add_argument("--sources", choices=sorted(SOURCE_GROUPS), default="quantize",
@@ -803,6 +824,9 @@ def main():
         return
     if args.attention_profile:
         attention_profile(torch, nv, workloads)
+        return
+    if args.hadamard_profile:
+        hadamard_profile(torch, nv, workloads)
         return
     dev = torch.device("cuda:0")
     print(f"[bench] generating workload 4 ({ROWS}x{COLS} bf16)", file=sys.stderr, flush=True)

@@ -621,18 +621,23 @@ __global__ __launch_bounds__(kThreads) void quantize_rule_kernel(QuantArgs a) {
 //    it) a_i > amax/128: every nonzero product and partial sum is a multiple
 //    of 2^(E-15) below 2^(E+8), E the exponent of amax (23 bits). S2 is a
 //    multiple of 1/4 below 577.
-//  * K_f = d^2 S2 - 2d S1 is formed in FP64: d has at most 24 significant
-//    bits, so d^2 and 2d S1 (at most 48 bits each) are exact; K_0 takes one
-//    rounding, D_f = K_f - K_0 two (-2d S1 - K_0, then + d^2 S2), each
-//    relative 2^-53 of terms below 3 A2.
+//  * K_f = 2d (d/2 S2 - S1) is formed in FP32: d/2 and 2d are exact, the
+//    fused multiply-add rounds once and the multiply once, so K_f is within
+//    2u |K_f| (u = 2^-24), and D_f = K_f - K_0 rounds once more. With
+//    |K_0| <= A2 (E_0 <= A2 up to rounding: a nearest code is never farther
+//    from the value than 0 is) and |K_f| <= A2 + |D_f|, D_f is within
+//    4u A2 + 3u |D_f| of its real value.
 //  * The contract's FP32 SSE differs from E_f by at most
 //    delta_f <= 2u (sum x^_i^2 / 8 + 14 E_f) (u = 2^-24): per element the
 //    rounding of x^, e and e^2 moves e^2 by <= 2u(V_i d |t_i| + t_i^2) to
 //    first order, bounded with Cauchy-Schwarz and 2ab <= a^2/8 + 8b^2; the 15
 //    sequential adds contribute <= 15u E_f. With sum x^^2 <= 2 (A2 + E_f) and
-//    E_f <= |K_f - K_0| + E_0 this gives a per-candidate margin
-//    M_f = 2^-18 |D_f| + 2^-23 (0.3 A2 + 15 E_0) (+ FP64/FP32 rounding),
-//    D_f = K_f - K_0 (candidate 0 = offset 0 as reference).
+//    E_f <= |K_f - K_0| + E_0 this is at most
+//    2^-23 (0.25 A2 + 14.25 E_0 + 14.25 |D_f|); adding the error of D_f
+//    gives a per-candidate margin
+//    M_f = 2^-18 |D_f| + 2^-23 (2.3 A2 + 15 E_0), D_f = K_f - K_0
+//    (candidate 0 = offset 0 as reference), whose slack also covers the FP32
+//    rounding of A2 (8 chained adds), of E_0's bound and of M_f itself.
 //  * Winner w = first candidate with least D_f; U_f = D_f + M_f and
 //    L_f = D_f - M_f are both increasing in D_f, so w also has the least U.
 //    If every other candidate has L_f > U_w (it suffices to test the
@@ -674,6 +679,15 @@ __device__ __forceinline__ float dot2_first(bf16x2 a, bf16x2 b) {
 // the convert's power-of-two scale operand divides by 2^SC_LOG2 exactly before
 // rounding. Each code word is converted in place over the candidate's
 // previous word (all four byte selects overwrite it).
+// A register whose value is never read: the first of a code word's four byte-select
+// converts overwrites the byte it selects and the other three fill the rest, so
+// the word needs no initial value (and no copy of an older word).
+__device__ __forceinline__ uint32_t fresh_word() {
+  uint32_t v;
+  asm volatile("" : "=v"(v));
+  return v;
+}
+
 template <int SC_LOG2>
 __device__ __forceinline__ void candidate_stats_y(const float (&y)[16], const uint32_t (&w)[8],
                                                   uint32_t (&cw)[2], float &s1, float &s2) {
@@ -681,7 +695,7 @@ __device__ __forceinline__ void candidate_stats_y(const float (&y)[16], const ui
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     switch (j & 3) {
-      case 0: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw[j >> 2], y[2 * j], y[2 * j + 1], sc, 0); break;
+      case 0: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(fresh_word(), y[2 * j], y[2 * j + 1], sc, 0); break;
       case 1: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw[j >> 2], y[2 * j], y[2 * j + 1], sc, 1); break;
       case 2: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw[j >> 2], y[2 * j], y[2 * j + 1], sc, 2); break;
       default: cw[j >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw[j >> 2], y[2 * j], y[2 * j + 1], sc, 3); break;
@@ -712,14 +726,13 @@ __device__ __forceinline__ void candidate_codes(const float (&x)[16], float r, u
 }
 
 
-// Per pattern: d^2 and -2d in FP64 (both exact: d has at most 24 significant
-// bits) and the encode scale r = 1/d. Rows past pattern 126 are zero: a
-// candidate there codes every element to 0 and scores K = 0, i.e. the block's
-// full energy, which no eligible block's leader or contender can reach (the
-// offset-0 candidate already removes more than 0.99 amax^2 of it).
+// Per pattern: d / 2 and 2 d (both exact) and the encode scale r = 1/d. Rows past
+// pattern 126 are zero: a candidate there codes every element to 0 and scores
+// K = 0, i.e. the block's full energy, which no eligible block's leader or
+// contender can reach (the offset-0 candidate already removes more than
+// 0.99 amax^2 of it).
 struct CertEntry {
-  double dd2, ntw;
-  float r, pad0, pad1, pad2;
+  float hd, td, r, pad;
 };
 constexpr int kCertRows = 136;
 
@@ -744,8 +757,7 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
   build_scale_table(tbl, sg);
   if (threadIdx.x < kCertRows) {
     const f32x2 dr = threadIdx.x < 127 ? tbl[threadIdx.x] : f32x2{0.0f, 0.0f};
-    const double dd = (double)dr.x;
-    ctbl[threadIdx.x] = CertEntry{dd * dd, -2.0 * dd, dr.y, 0.0f, 0.0f, 0.0f};
+    ctbl[threadIdx.x] = CertEntry{0.5f * dr.x, 2.0f * dr.x, dr.y, 0.0f};
   }
   __syncthreads();
   // Default pattern in one multiply: q = fl(am * c6), c6 = 1/(6 S_g) rounded
@@ -795,7 +807,6 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
         for (int k = 1; k < 8; ++k)
           a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
                                                __builtin_bit_cast(bf16x2, w[k]), a2, false);
-        const double a2ub = (double)a2 * (1.0 + 0x1p-18) + 0x1p-120;
 
         // Leader = first candidate with the least D (the margin is monotone in
         // D, so this is also a candidate with the least U = D + M); only the
@@ -803,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
         // L = D - M reaches the leader's U.
         constexpr EvalOrder<FLO, FHI> ord;
         float D[NC];  // by visiting slot
-        double k0 = 0.0;
+        float k0 = 0.0f;
         float cst = 0.0f;  // block part of the margin
         float best_d = 0.0f, second_d = INFINITY;
         uint32_t cw[2] = {0u, 0u};
@@ -825,19 +836,19 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
             candidate_stats_y<1>(y, w, cw, s1, s2);
           else
             candidate_stats_y<-1>(y, w, cw, s1, s2);
+          // K_f = 2d (d/2 S2 - S1): the fused product d/2 S2 is exact inside the
+          // FMA, one rounding there and one in the multiply.
+          const float kf = ce.td * __builtin_fmaf(ce.hd, s2, -s1);
           float df;
           if (k == 0) {
-            // K_0 = d^2 S2 - 2d S1: both products exact, one rounding.
-            const double kf = __builtin_fma(ce.dd2, (double)s2, ce.ntw * (double)s1);
             k0 = kf;
             df = 0.0f;
-            const double e0ub = kf + a2ub + __builtin_fabs(kf) * 0x1p-50;
-            cst = (float)((0.3 * a2ub + 15.0 * (e0ub > 0.0 ? e0ub : 0.0)) * 0x1p-23 +
-                          (__builtin_fabs(kf) + a2ub) * 0x1p-50) * (1.0f + 0x1p-20f) +
-                  0x1p-120f;
+            // E_0 = A2 + K_0 <= A2 (nearest-value codes never do worse than 0),
+            // bounded from above with K_0's own error 2u A2
+            const float e0ub = fminf(fmaxf(kf + a2 * (1.0f + 0x1p-21f), 0.0f), a2);
+            cst = (2.3f * a2 + 15.0f * e0ub) * (0x1p-23f * (1.0f + 0x1p-20f)) + 0x1p-120f;
           } else {
-            // D_f = K_f - K_0 = d^2 S2 + (-2d S1 - K_0): two FP64 roundings.
-            df = (float)__builtin_fma(ce.dd2, (double)s2, __builtin_fma(ce.ntw, (double)s1, -k0));
+            df = kf - k0;
           }
           if (!RANGE_FIXED && (f < a.f_lo || f > a.f_hi)) df = INFINITY;
           D[sl] = df;
@@ -908,8 +919,8 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
 // order that makes accumulator v of lane l hold feature 32 t + 16 (l >> 5) + v
 // of vector l & 31, i.e. one whole 16-element quantization block per lane and
 // per 32-feature tile t. The products are exact; the FP32 accumulation may
-// round, so the transform is within a few FP32 ulps of the exact one. The sum
-// is scaled in FP64 by the double nearest 2^-3.5 and rounded once to FP32.
+// round, and the sum is scaled by the binary32 nearest 2^-3.5 (one more
+// rounding), so the transform is within a few FP32 ulps of the exact one.
 //
 // Randomized variant (random +-1 signs before H, as in QuIP#'s incoherence
 // processing): y = (x o s) H / sqrt(128). The signs flip the sign bits of the
@@ -920,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr double kInvSqrt128 = 0x1.6a09e667f3bcdp-4;  // nearest double to 2^-3.5
+constexpr float kInvSqrt128f = 0x1.6a09e6p-4f;  // nearest binary32 to 2^-3.5
 
 // Feature (row of H) held by accumulator row i of tile t.
 __device__ __forceinline__ uint32_t hadamard_feature(uint32_t t, uint32_t i) {
@@ -1024,7 +1035,7 @@ __device__ __forceinline__ void hadamard_tile(const HadamardLane &h, const uint4
                                                       : hadamard_a(h, t, ks),
                                                   __builtin_bit_cast(bf16x8, b[ks]), acc, 0, 0, 0);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) y[v] = (float)((double)acc[v] * kInvSqrt128);
+  for (int v = 0; v < 16; ++v) y[v] = acc[v] * kInvSqrt128f;
 }
 
 // Quantize with the Hadamard pre-transform (bf16 input, cols % 128 == 0). One

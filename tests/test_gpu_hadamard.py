@@ -41,11 +41,11 @@ def test_closed_forms(gpu):
     xb = workloads.to_bf16_bits(x)
     y = to_host(gpu.hadamard128(to_dev(xb)))
     assert y[0, 0] == np.float32(np.sqrt(128.0)) and np.all(y[0, 1:] == 0)
-    c64 = np.sqrt(1.0 / 128.0)  # nearest double to 2^-3.5
-    assert np.all(np.abs(y[1]) == np.float32(c64))
-    # a single nonzero input: every output is +-x times that double, rounded once
+    c32 = np.float32(np.sqrt(1.0 / 128.0))  # binary32 nearest 2^-3.5, the kernel's scale
+    assert np.all(np.abs(y[1]) == c32)
+    # a single nonzero input: every output is +-x times that scale, one binary32 rounding
     for r in range(3, 64):
-        assert np.all(np.abs(y[r]) == np.float32(r * c64))
+        assert np.all(np.abs(y[r]) == np.float32(np.float32(r) * c32))
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 333, 128), (5, 256), (1, 1, 31, 128), (3, 1024)])

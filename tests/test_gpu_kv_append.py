@@ -2,7 +2,10 @@
 the ScaleSearch summary page, ScaleSearchAttention, アテンション・シンク対応混合精度
 キャッシング): after every append the cache must hold exactly what the one-shot sink
 mode gives for the whole sequence under the same given tensor scale — checked
-bit for bit against the oracle."""
+bit for bit against the oracle. With the Hadamard transform the contract is that of
+the transform: the oracle's quantizer on the GPU's own FP32 transform of the middle
+tokens gives the cache's codes bit for bit, and against the oracle's exactly rounded
+transform at most 1e-4 of the blocks differ."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +16,7 @@ from gpu_util import to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def check_against_oracle(orc, cache, kv_all, sg, offsets, hadamard):
+def check_against_oracle(orc, cache, kv_all, sg, offsets, hadamard, nv=None):
     nf, nl, T = cache["n_first"], cache["n_last"], cache["length"]
     if T < nf + nl:
         np.testing.assert_array_equal(to_host(cache["head"])[:, :, :min(T, nf)],
@@ -22,8 +25,20 @@ def check_against_oracle(orc, cache, kv_all, sg, offsets, hadamard):
     rc, rs, _, rsink = orc.quantize_kv_sink(np.ascontiguousarray(kv_all[:, :, :T]), nf, nl,
                                             *offsets, hadamard=hadamard, gscale=float(sg))
     tm = T - nf - nl
-    np.testing.assert_array_equal(to_host(cache["codes"])[:, :, :tm], rc)
-    np.testing.assert_array_equal(to_host(cache["scales"])[:, :, :tm], rs)
+    gc, gs = to_host(cache["codes"])[:, :, :tm], to_host(cache["scales"])[:, :, :tm]
+    if hadamard:
+        # split parity on the GPU's own transform of the middle tokens
+        mid = to_dev(np.ascontiguousarray(kv_all[:, :, nf:T - nl]))
+        y = to_host(nv.hadamard128(mid)).reshape(-1, mid.shape[-1])
+        pc, ps, _ = orc.quantize(y, *offsets, gscale=float(sg))
+        np.testing.assert_array_equal(gc.reshape(pc.shape), pc)
+        np.testing.assert_array_equal(gs.reshape(ps.shape), ps)
+        bad = (gs.reshape(-1) != rs.reshape(-1)) | np.any(
+            gc.reshape(-1, 8) != rc.reshape(-1, 8), axis=1)
+        assert bad.mean() <= 1e-4, f"{bad.sum()} of {bad.size} blocks differ end to end"
+    else:
+        np.testing.assert_array_equal(gc, rc)
+        np.testing.assert_array_equal(gs, rs)
     np.testing.assert_array_equal(to_host(cache["head"]), rsink[:, :, :nf])
     if nl:
         ring = to_host(cache["tail"])
@@ -63,7 +78,7 @@ def test_append_sequence_matches_one_shot(gpu, orc, nf, nl, steps, dtype_bf16, h
                       hadamard=hadamard)
         torch.cuda.synchronize()
         t += k
-        check_against_oracle(orc, cache, kv_all, sg, offsets, hadamard)
+        check_against_oracle(orc, cache, kv_all, sg, offsets, hadamard, gpu)
 
 
 def test_append_capacity_check(gpu):
