@@ -504,8 +504,6 @@ __device__ __forceinline__ void search_block_twins(const float (&x)[16], float s
   }
 }
 
-// Blocks first, first + stride, ... of the region with the exact search.
-// FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI] (twin-sharing search).
 // Balancing pair: x_i 2^(side e_i) in binary32 for the block's 16 columns.
 __device__ __forceinline__ void balance_block(const Balance &bal, const RegionMap &m, uint32_t b,
                                               float (&x)[16]) {
@@ -514,39 +512,6 @@ __device__ __forceinline__ void balance_block(const Balance &bal, const RegionMa
   const uint32_t w[4] = {ew.x, ew.y, ew.z, ew.w};
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = ldexpf(x[i], bal_exp(w[i >> 2], i & 3, bal.side));
-}
-
-template <bool BF16, int FLO, int FHI, bool FIXED, bool BAL = false>
-__device__ __forceinline__ void quantize_blocks(const QuantArgs &a, const f32x2 *tbl, float sg,
-                                                bool sg_ok, uint32_t first, uint32_t stride,
-                                                uint32_t t_dev) {
-  for (uint32_t b = first; b < a.map.nblocks; b += stride) {
-    float x[16];
-    const BlockIO io = block_io(a.x, a.map, b, BF16 ? 2u : 4u, t_dev);
-    if (!io.valid) continue;
-    load_block_at<BF16>(io.src, x);
-    if (BAL) balance_block(a.bal, a.map, b, x);
-    uint32_t best_p, bc0, bc1;
-    if (FIXED)
-      search_block_twins<FLO, FHI>(x, sg, sg_ok, tbl, best_p, bc0, bc1);
-    else
-      search_block(x, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
-    *(uint2 *)(a.codes + io.dst * 8u) = make_uint2(bc0, bc1);
-    a.scales[io.dst] = (uint8_t)best_p;
-  }
-}
-
-// BAL: the blocks are those of the balancing pair's scaled values (plain
-// regions only), searched exactly as FP32 values.
-template <bool BF16, int FLO, int FHI, bool FIXED, bool BAL = false>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
-  __shared__ f32x2 tbl[128];
-  const float sg = resolve_tensor_scale(a);
-  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
-  build_scale_table(tbl, sg);
-  quantize_blocks<BF16, FLO, FHI, FIXED, BAL>(a, tbl, sg, sg_ok,
-                                              blockIdx.x * kThreads + threadIdx.x,
-                                              gridDim.x * kThreads, map_length(a.map));
 }
 
 // Max scaling alone (offsets [0, 0]: one candidate, nothing to score) with two
@@ -688,9 +653,11 @@ __device__ __forceinline__ uint32_t fresh_word() {
   return v;
 }
 
-template <int SC_LOG2>
-__device__ __forceinline__ void candidate_stats_y(const float (&y)[16], const uint32_t (&w)[8],
-                                                  uint32_t (&cw)[2], float &s1, float &s2) {
+template <int SC_LOG2, int NP>
+__device__ __forceinline__ void candidate_stats_parts(const float (&y)[16],
+                                                      const uint32_t (&prt)[NP][8],
+                                                      uint32_t (&cw)[2], float (&s1)[NP],
+                                                      float &s2) {
   constexpr float sc = SC_LOG2 == 0 ? 1.0f : (SC_LOG2 > 0 ? 2.0f : 0.5f);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -702,15 +669,20 @@ __device__ __forceinline__ void candidate_stats_y(const float (&y)[16], const ui
     }
   }
   bf16x2 v = fp4_decode_pair_bf16(cw[0], 0);
-  float a = dot2_first(__builtin_bit_cast(bf16x2, w[0]), v);
+  float a[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) a[q] = dot2_first(__builtin_bit_cast(bf16x2, prt[q][0]), v);
   float b = dot2_first(v, v);
 #pragma unroll
   for (int j = 1; j < 8; ++j) {
     v = fp4_decode_pair_bf16(cw[j >> 2], j);
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), v, a, false);
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+      a[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, prt[q][j]), v, a[q], false);
     b = __builtin_amdgcn_fdot2_f32_bf16(v, v, b, false);
   }
-  s1 = a;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) s1[q] = a[q];
   s2 = b;
 }
 
@@ -746,6 +718,207 @@ __device__ __forceinline__ uint32_t bf16_block_absmax_bits(const uint32_t (&w)[8
   return (uint32_t)max(m.x, m.y) << 16;
 }
 
+// The per-workgroup tables of the certified search (after build_scale_table).
+__device__ __forceinline__ void build_cert_table(const f32x2 *tbl, CertEntry *ctbl) {
+  if (threadIdx.x < kCertRows) {
+    const f32x2 dr = threadIdx.x < 127 ? tbl[threadIdx.x] : f32x2{0.0f, 0.0f};
+    ctbl[threadIdx.x] = CertEntry{0.5f * dr.x, 2.0f * dr.x, dr.y, 0.0f};
+  }
+}
+
+// Default pattern in one multiply: q = fl(am * c6), c6 = 1/(6 S_g) rounded
+// once, and the contract's t = fl(fl(am / 6) / S_g) are each within 2^-23
+// (relative) of am / (6 S_g), so they differ by at most 4 ulps of q. RNE to
+// E4M3 changes only at midpoints (low 20 bits of the binary32 pattern 0x80000
+// in E4M3's normal range), so when q is more than 8 ulps from a midpoint, q and
+// t give the same pattern. Otherwise (or for q in E4M3's subnormal range, or
+// S_g outside [2^-100, 2^100]) t is formed as the contract does.
+__device__ __forceinline__ uint32_t default_pattern(uint32_t am, float sg, float c6, bool c6_ok) {
+  float t = __uint_as_float(am) * c6;
+  const bool near_mid = ((__float_as_uint(t) - 0x80000u + 8u) & 0xFFFFFu) <= 16u;
+  if (!c6_ok || near_mid || !(t >= 0x1p-6f || am == 0u)) t = (__uint_as_float(am) / 6.0f) / sg;
+  return e4m3_rne_sat(t);
+}
+
+// Three-way split of a binary32 block for exact dot products with E2M1 values:
+// x = h + m + l with h the top 8 significand bits of x, m the next 8 and l the
+// last 8 (fixed bit positions, so m and l are multiples of 2^(e-15) and
+// 2^(e-23), e the exponent of x). Each part has at most 8 significant bits and
+// is exact in bf16 (its binary32 pattern has zero low half); the parts are
+// packed as bf16 pairs (elements 2k, 2k+1).
+__device__ __forceinline__ void split3_block(const float (&x)[16], uint32_t (&prt)[3][8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t be = __float_as_uint(x[2 * k]), bo = __float_as_uint(x[2 * k + 1]);
+    const float te = __uint_as_float(be & 0xFFFFFF00u), to = __uint_as_float(bo & 0xFFFFFF00u);
+    const float me = te - __uint_as_float(be & 0xFFFF0000u);
+    const float mo = to - __uint_as_float(bo & 0xFFFF0000u);
+    const float le = x[2 * k] - te, lo = x[2 * k + 1] - to;
+    prt[0][k] = __builtin_amdgcn_perm(bo, be, 0x07060302u);
+    prt[1][k] = __builtin_amdgcn_perm(__float_as_uint(mo), __float_as_uint(me), 0x07060302u);
+    prt[2][k] = __builtin_amdgcn_perm(__float_as_uint(lo), __float_as_uint(le), 0x07060302u);
+  }
+}
+
+// Twin codes identical: candidate patterns p and p + 8 (both normal) reconstruct
+// every element alike iff E2M1(y) = 2 E2M1(y / 2) for each product y of the
+// finer one, which holds iff no code of the finer candidate is +-0.5 or +-1.5
+// (code magnitudes 1 and 3: bit 0 set, bit 2 clear) and its largest product is
+// below 7 (7 itself codes to 6 against 2 * 4). Their contract SSEs are then
+// equal bit for bit.
+__device__ __forceinline__ bool twin_codes_identical(uint32_t c0, uint32_t c1, float ymax) {
+  const uint32_t half = (c0 & ~(c0 >> 2)) | (c1 & ~(c1 >> 2));
+  return (half & 0x11111111u) == 0u && ymax < 7.0f;
+}
+
+// The certified search of one block (bf16 values with NP = 1: parts = the bf16
+// words; binary32 values with NP = 3: the three-way split), from the default
+// pattern p0. Writes the winner as the exact contract would.
+//
+// K_f = 2d (d/2 S2 - S1): with one part the fused product d/2 S2 is exact inside
+// the FMA, one rounding there and one in the multiply (K within 2u |K|). With
+// three parts S1 = S1h + S1m + S1l is not a binary32 value; t = fl(fl(d/2 S2 -
+// S1h) - fl(S1m + S1l)) then K = fl(2d t): S1m + S1l < 2^-7 S1, so K is within
+// 3.1u (|K| + 2^-6 2d S1) <= 3.2u (A2 + |D|), and D = fl(K - K_0) within
+// 6.4u A2 + 4.2u |D|; the margin's A2 coefficient is 3.6 instead of 2.3 and
+// the |D| coefficient stays below 2^-18.
+//
+// TIES (binary32 path): a twin eight patterns above its group's first candidate
+// f in [-2, 0] whose codes are identical to the finer one's (twin_codes_identical)
+// has the same contract SSE and comes later in visiting order, so it can never
+// be the choice; it is dropped (K = inf) instead of contesting.
+// PRUNE: candidates with offset <= -5 are skipped wave-wide when no lane can
+// need them: the contract SSE is at least its own amax term, and the best
+// candidate's contract SSE is at most A2 + K_best + 2^-18 A2 (K error, the
+// delta bound and the roundings of the bound itself).
+template <int FLO, int FHI, int NP, bool RANGE_FIXED, bool TIES, bool PRUNE>
+__device__ __forceinline__ void certified_search(const float (&x)[16],
+                                                 const uint32_t (&prt)[NP][8], uint32_t am,
+                                                 uint32_t p0, float a2, const f32x2 *tbl,
+                                                 const CertEntry *ctbl, int f_lo, int f_hi,
+                                                 uint32_t &best_p, uint32_t &bc0,
+                                                 uint32_t &bc1) {
+  constexpr int NC = FHI - FLO + 1;
+  constexpr float kA2Coef = NP == 1 ? 2.3f : 3.6f;
+  // certificate applies: every candidate pattern normal, amax in
+  // [2^-40, 2^60]; other blocks take the exact path below. Candidates
+  // above pattern 126 read the zero rows of the table.
+  const bool eligible = ((int)p0 + FLO >= 8) && am >= 0x2B800000u && am <= 0x5D800000u;
+  const int p0b = max((int)p0, -FLO);  // keeps table indices >= 0
+  const float amax = __uint_as_float(am);
+
+  // Leader = candidate with the least K (first in evaluation order among
+  // equal K). D = fl(K - K_0) is non-decreasing in K and the margin is
+  // monotone in D, so only the runner-up's K is needed to decide whether
+  // any other candidate's L = D - M reaches the leader's U; equal K, or
+  // K values whose D rounds equal, contest.
+  constexpr EvalOrder<FLO, FHI> ord;
+  float kk[NC];  // K by visiting slot
+  float k0 = 0.0f;
+  float cst = 0.0f;  // block part of the margin
+  float best_k = 0.0f, second_k = INFINITY;
+  int best_f = 0;
+  uint32_t cw[2] = {0u, 0u}, gw[2] = {0u, 0u};
+  float y[16];
+  float gymax = 0.0f;  // largest product of the group's first candidate
+  const CertEntry *crow = ctbl + (p0b + FLO);
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int f = ord.off[k];
+    const int sl = ord.slot_of[k];
+    const CertEntry ce = crow[f - FLO];
+    // a group's first candidate with an offset in [-2, 0] may have an identical twin
+    const bool tie_group = TIES && ord.shift[k] == 0 && f >= -2 && f <= 0;
+    const bool tie_twin = TIES && ord.shift[k] > 0 && f - 8 >= -2 && f - 8 <= 0;
+    if (ord.shift[k] == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = x[i] * ce.r;
+      if (tie_group) gymax = amax * ce.r;
+    }
+    if (PRUNE && k > 0 && f <= -5) {
+      const float ub = (a2 + best_k) + a2 * 0x1p-18f;
+      const bool live = eligible && !(amax_term(amax, 0.5f * ce.td, ce.r) > ub);
+      if (__ballot(live) == 0ull) {
+        kk[sl] = INFINITY;
+        continue;
+      }
+    }
+    float s1[NP], s2;
+    if (ord.shift[k] == 0)
+      candidate_stats_parts<0, NP>(y, prt, cw, s1, s2);
+    else if (ord.shift[k] > 0)
+      candidate_stats_parts<1, NP>(y, prt, cw, s1, s2);
+    else
+      candidate_stats_parts<-1, NP>(y, prt, cw, s1, s2);
+    float kf;
+    if constexpr (NP == 1)
+      kf = ce.td * __builtin_fmaf(ce.hd, s2, -s1[0]);
+    else
+      kf = ce.td * (__builtin_fmaf(ce.hd, s2, -s1[0]) - (s1[1] + s1[2]));
+    if (k == 0) {
+      k0 = kf;
+      // E_0 = A2 + K_0 <= A2 (nearest-value codes never do worse than 0),
+      // bounded from above with K_0's own error (at most 3.2u A2)
+      const float e0ub = fminf(fmaxf(kf + a2 * (1.0f + 0x1p-21f), 0.0f), a2);
+      cst = (kA2Coef * a2 + 15.0f * e0ub) * (0x1p-23f * (1.0f + 0x1p-20f)) + 0x1p-120f;
+    }
+    if (tie_twin && twin_codes_identical(gw[0], gw[1], gymax)) kf = INFINITY;
+    if (tie_group) {
+      gw[0] = cw[0];
+      gw[1] = cw[1];
+    }
+    if (!RANGE_FIXED && (f < f_lo || f > f_hi)) kf = INFINITY;
+    kk[sl] = kf;
+    if (k == 0) {
+      best_k = kf;
+      bc0 = cw[0];
+      bc1 = cw[1];
+    } else {
+      const bool lt = kf < best_k;
+      second_k = __builtin_amdgcn_fmed3f(best_k, second_k, kf);
+      best_k = fminf(best_k, kf);
+      best_f = lt ? f : best_f;
+      bc0 = lt ? cw[0] : bc0;
+      bc1 = lt ? cw[1] : bc1;
+      // select here: keeps each candidate's code words from staying live to the end
+      asm volatile("" : "+v"(bc0), "+v"(bc1));
+    }
+  }
+  best_p = (uint32_t)(p0b + best_f);
+  const float best_d = best_k - k0, second_d = second_k - k0;
+  const float best_u = best_d + __builtin_fmaf(__builtin_fabsf(best_d), 0x1p-18f, cst);
+  const bool contested =
+      second_d - __builtin_fmaf(__builtin_fabsf(second_d), 0x1p-18f, cst) <= best_u;
+  if (!eligible || best_p > 126u || contested) {
+    // Exact contract evaluation over the candidates that could win,
+    // in visiting order.
+    const uint32_t lead = best_p;
+    float best = INFINITY;
+    bool have = false;
+#pragma unroll
+    for (int sl = 0; sl < NC; ++sl) {
+      const int f = slot_offset<FLO>(sl);
+      const int p = (int)p0 + f;
+      const bool valid = (RANGE_FIXED || (f >= f_lo && f <= f_hi)) && p >= 0 && p <= 126;
+      const float dsl = kk[sl] - k0;
+      const float lf = dsl - __builtin_fmaf(__builtin_fabsf(dsl), 0x1p-18f, cst);
+      const bool need = valid && (!eligible || (uint32_t)p == lead || lf <= best_u);
+      if (need) {
+        const f32x2 dr = tbl[p];
+        uint32_t c0, c1;
+        const float sse = candidate_sse(x, dr.x, dr.y, c0, c1);
+        if (!have || sse < best) {
+          have = true;
+          best = sse;
+          best_p = (uint32_t)p;
+          bc0 = c0;
+          bc1 = c1;
+        }
+      }
+    }
+  }
+}
+
 // RANGE_FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI].
 template <int FLO, int FHI, bool RANGE_FIXED>
 __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs a) {
@@ -755,19 +928,8 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
   const float sg = resolve_tensor_scale(a);
   const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
   build_scale_table(tbl, sg);
-  if (threadIdx.x < kCertRows) {
-    const f32x2 dr = threadIdx.x < 127 ? tbl[threadIdx.x] : f32x2{0.0f, 0.0f};
-    ctbl[threadIdx.x] = CertEntry{0.5f * dr.x, 2.0f * dr.x, dr.y, 0.0f};
-  }
+  build_cert_table(tbl, ctbl);
   __syncthreads();
-  // Default pattern in one multiply: q = fl(am * c6), c6 = 1/(6 S_g) rounded
-  // once, and the contract's t = fl(fl(am / 6) / S_g) are each within
-  // 2^-23 (relative) of am / (6 S_g), so they differ by at most 4 ulps of q.
-  // RNE to E4M3 changes only at midpoints (low 20 bits of the binary32
-  // pattern 0x80000 in E4M3's normal range), so when q is more than 8 ulps
-  // from a midpoint, q and t give the same pattern. Otherwise (or for q in
-  // E4M3's subnormal range, or S_g outside [2^-100, 2^100]) t is formed as
-  // the contract does.
   const float c6 = (float)(1.0 / (6.0 * (double)sg));
   const bool c6_ok = sg_ok && sg >= 0x1p-100f && sg <= 0x1p100f;
 
@@ -777,132 +939,107 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
     const BlockIO io = block_io(a.x, a.map, b, 2u, t_dev);
     if (!io.valid) continue;
     const uint4 q0 = load_stream(io.src), q1 = load_stream(io.src + 16);
-    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const uint32_t w[1][8] = {{q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w}};
     float x[16];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      x[2 * k] = __uint_as_float(w[k] << 16);
-      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      x[2 * k] = __uint_as_float(w[0][k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[0][k] & 0xFFFF0000u);
     }
-    const uint32_t am = bf16_block_absmax_bits(w);
+    const uint32_t am = bf16_block_absmax_bits(w[0]);
 
     uint32_t best_p = 0x7Fu, bc0 = 0u, bc1 = 0u;
     if (sg_ok && am < 0x7F800000u) {
-      float t = __uint_as_float(am) * c6;
-      const bool near_mid = ((__float_as_uint(t) - 0x80000u + 8u) & 0xFFFFFu) <= 16u;
-      if (!c6_ok || near_mid || !(t >= 0x1p-6f || am == 0u))
-        t = (__uint_as_float(am) / 6.0f) / sg;
-      const uint32_t p0 = e4m3_rne_sat(t);
+      const uint32_t p0 = default_pattern(am, sg, c6, c6_ok);
       if (NC == 1) {
         best_p = p0;
         candidate_codes(x, tbl[p0].y, bc0, bc1);
       } else {
-        // certificate applies: every candidate pattern normal, amax in
-        // [2^-40, 2^60]; other blocks take the exact path below. Candidates
-        // above pattern 126 read the zero rows of the table.
-        const bool eligible = ((int)p0 + FLO >= 8) && am >= 0x2B800000u && am <= 0x5D800000u;
-        const int p0b = max((int)p0, -FLO);  // keeps table indices >= 0
-        float a2 = dot2_first(__builtin_bit_cast(bf16x2, w[0]), __builtin_bit_cast(bf16x2, w[0]));
+        // A2 from the bf16 words: exact squares, eight FP32 roundings.
+        float a2 = dot2_first(__builtin_bit_cast(bf16x2, w[0][0]), __builtin_bit_cast(bf16x2, w[0][0]));
 #pragma unroll
         for (int k = 1; k < 8; ++k)
-          a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
-                                               __builtin_bit_cast(bf16x2, w[k]), a2, false);
-
-        // Leader = first candidate with the least D (the margin is monotone in
-        // D, so this is also a candidate with the least U = D + M); only the
-        // runner-up's D is needed to decide whether any other candidate's
-        // L = D - M reaches the leader's U.
-        constexpr EvalOrder<FLO, FHI> ord;
-        float D[NC];  // by visiting slot
-        float k0 = 0.0f;
-        float cst = 0.0f;  // block part of the margin
-        float best_d = 0.0f, second_d = INFINITY;
-        uint32_t cw[2] = {0u, 0u};
-        float y[16];
-#pragma unroll
-        for (int k = 0; k < NC; ++k) {
-          const int f = ord.off[k];
-          const int sl = ord.slot_of[k];
-          const int p = p0b + f;
-          const CertEntry ce = ctbl[p];
-          if (ord.shift[k] == 0) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) y[i] = x[i] * ce.r;
-          }
-          float s1, s2;
-          if (ord.shift[k] == 0)
-            candidate_stats_y<0>(y, w, cw, s1, s2);
-          else if (ord.shift[k] > 0)
-            candidate_stats_y<1>(y, w, cw, s1, s2);
-          else
-            candidate_stats_y<-1>(y, w, cw, s1, s2);
-          // K_f = 2d (d/2 S2 - S1): the fused product d/2 S2 is exact inside the
-          // FMA, one rounding there and one in the multiply.
-          const float kf = ce.td * __builtin_fmaf(ce.hd, s2, -s1);
-          float df;
-          if (k == 0) {
-            k0 = kf;
-            df = 0.0f;
-            // E_0 = A2 + K_0 <= A2 (nearest-value codes never do worse than 0),
-            // bounded from above with K_0's own error 2u A2
-            const float e0ub = fminf(fmaxf(kf + a2 * (1.0f + 0x1p-21f), 0.0f), a2);
-            cst = (2.3f * a2 + 15.0f * e0ub) * (0x1p-23f * (1.0f + 0x1p-20f)) + 0x1p-120f;
-          } else {
-            df = kf - k0;
-          }
-          if (!RANGE_FIXED && (f < a.f_lo || f > a.f_hi)) df = INFINITY;
-          D[sl] = df;
-          if (k == 0) {
-            best_d = df;
-            best_p = (uint32_t)p;
-            bc0 = cw[0];
-            bc1 = cw[1];
-          } else {
-            const bool lt = df < best_d;
-            second_d = lt ? best_d : (df < second_d ? df : second_d);
-            if (lt) {
-              best_d = df;
-              best_p = (uint32_t)p;
-              bc0 = cw[0];
-              bc1 = cw[1];
-            }
-          }
-        }
-        const float best_u = best_d + __builtin_fmaf(__builtin_fabsf(best_d), 0x1p-18f, cst);
-        const bool contested =
-            second_d - __builtin_fmaf(__builtin_fabsf(second_d), 0x1p-18f, cst) <= best_u;
-        if (!eligible || best_p > 126u || contested) {
-          // Exact contract evaluation over the candidates that could win,
-          // in visiting order.
-          const uint32_t lead = best_p;
-          float best = INFINITY;
-          bool have = false;
-#pragma unroll
-          for (int sl = 0; sl < NC; ++sl) {
-            const int f = slot_offset<FLO>(sl);
-            const int p = (int)p0 + f;
-            const bool valid = (RANGE_FIXED || (f >= a.f_lo && f <= a.f_hi)) && p >= 0 && p <= 126;
-            const float lf = D[sl] - __builtin_fmaf(__builtin_fabsf(D[sl]), 0x1p-18f, cst);
-            const bool need = valid && (!eligible || (uint32_t)p == lead || lf <= best_u);
-            if (need) {
-              const f32x2 dr = tbl[p];
-              uint32_t c0, c1;
-              const float sse = candidate_sse(x, dr.x, dr.y, c0, c1);
-              if (!have || sse < best) {
-                have = true;
-                best = sse;
-                best_p = (uint32_t)p;
-                bc0 = c0;
-                bc1 = c1;
-              }
-            }
-          }
-        }
+          a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0][k]),
+                                               __builtin_bit_cast(bf16x2, w[0][k]), a2, false);
+        certified_search<FLO, FHI, 1, RANGE_FIXED, false, false>(
+            x, w, am, p0, a2, tbl, ctbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
       }
     }
     *(uint2 *)(a.codes + io.dst * 8u) = make_uint2(bc0, bc1);
     a.scales[io.dst] = (uint8_t)best_p;
   }
+}
+
+// The certified search for binary32 blocks (the Hadamard path): the split
+// makes S1 exact, A2 comes from an FMA chain (within 16u, bounded from above
+// by the factor 1 + 2^-19), and blocks with a non-finite element, or whose A2
+// overflows, take the exact search.
+template <int FLO, int FHI>
+__device__ __forceinline__ void search_block_cert32(const float (&x)[16], float sg, bool sg_ok,
+                                                    float c6, bool c6_ok, const f32x2 *tbl,
+                                                    const CertEntry *ctbl, uint32_t &best_p,
+                                                    uint32_t &bc0, uint32_t &bc1) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  float a2 = x[0] * x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) a2 = __builtin_fmaf(x[i], x[i], a2);
+  a2 *= 1.0f + 0x1p-19f;
+  if (!(sg_ok && am < 0x7F800000u && a2 < INFINITY)) {
+    search_block_twins<FLO, FHI>(x, sg, sg_ok, tbl, best_p, bc0, bc1);
+    return;
+  }
+  uint32_t prt[3][8];
+  split3_block(x, prt);
+  const uint32_t p0 = default_pattern(am, sg, c6, c6_ok);
+  certified_search<FLO, FHI, 3, true, true, (FLO <= -5)>(x, prt, am, p0, a2, tbl, ctbl, FLO,
+                                                          FHI, best_p, bc0, bc1);
+}
+
+// Blocks first, first + stride, ... of the region. FIXED: the launch guarantees
+// [f_lo, f_hi] == [FLO, FHI] (certified search on binary32 values); otherwise
+// the exact search over [f_lo, f_hi].
+template <bool BF16, int FLO, int FHI, bool FIXED, bool BAL = false>
+__device__ __forceinline__ void quantize_blocks(const QuantArgs &a, const f32x2 *tbl, float sg,
+                                                bool sg_ok, uint32_t first, uint32_t stride,
+                                                uint32_t t_dev, const CertEntry *ctbl = nullptr,
+                                                float c6 = 0.0f, bool c6_ok = false) {
+  for (uint32_t b = first; b < a.map.nblocks; b += stride) {
+    float x[16];
+    const BlockIO io = block_io(a.x, a.map, b, BF16 ? 2u : 4u, t_dev);
+    if (!io.valid) continue;
+    load_block_at<BF16>(io.src, x);
+    if (BAL) balance_block(a.bal, a.map, b, x);
+    uint32_t best_p, bc0, bc1;
+    if (FIXED)
+      search_block_cert32<FLO, FHI>(x, sg, sg_ok, c6, c6_ok, tbl, ctbl, best_p, bc0, bc1);
+    else
+      search_block(x, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
+    *(uint2 *)(a.codes + io.dst * 8u) = make_uint2(bc0, bc1);
+    a.scales[io.dst] = (uint8_t)best_p;
+  }
+}
+
+// BAL: the blocks are those of the balancing pair's scaled values (plain
+// regions only), searched as binary32 values.
+template <bool BF16, int FLO, int FHI, bool FIXED, bool BAL = false>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  __shared__ f32x2 tbl[128];
+  __shared__ CertEntry ctbl[FIXED ? kCertRows : 1];
+  const float sg = resolve_tensor_scale(a);
+  const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+  build_scale_table(tbl, sg);
+  if (FIXED) {
+    build_cert_table(tbl, ctbl);
+    __syncthreads();
+  }
+  const float c6 = (float)(1.0 / (6.0 * (double)sg));
+  const bool c6_ok = sg_ok && sg >= 0x1p-100f && sg <= 0x1p100f;
+  quantize_blocks<BF16, FLO, FHI, FIXED, BAL>(a, tbl, sg, sg_ok,
+                                              blockIdx.x * kThreads + threadIdx.x,
+                                              gridDim.x * kThreads, map_length(a.map), ctbl, c6,
+                                              c6_ok);
 }
 
 // ---------------------------------------------------------------------------
@@ -1041,19 +1178,35 @@ __device__ __forceinline__ void hadamard_tile(const HadamardLane &h, const uint4
 // Quantize with the Hadamard pre-transform (bf16 input, cols % 128 == 0). One
 // wave per 32 vectors; each lane codes four blocks of its vector.
 template <bool SIGNS, int FLO, int FHI, bool FIXED, bool BAL = false>
-__global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void quantize_hadamard_kernel(QuantArgs a) {
   __shared__ f32x2 tbl[128];
+  __shared__ CertEntry ctbl[FIXED ? kCertRows : 1];
   __shared__ __attribute__((aligned(16))) uint32_t ew[64];
   if (BAL) build_balance_bits(a.bal, ew);  // the table build below synchronizes
   const float sg = resolve_tensor_scale(a);
   const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
   build_scale_table(tbl, sg);
+  // sign masks of the randomized transform, per lane half and K slice (read
+  // through a volatile reference where used, so they are not held in registers)
+  __shared__ uint4 smask[FIXED && SIGNS ? 2 : 1][8];
+  if (FIXED) {
+    build_cert_table(tbl, ctbl);
+    if (SIGNS && threadIdx.x < 16) smask[threadIdx.x >> 3][threadIdx.x & 7] =
+        hadamard_sign_mask(a.hs, threadIdx.x & 7, threadIdx.x >> 3);
+    __syncthreads();
+  }
+  const float c6 = (float)(1.0 / (6.0 * (double)sg));
+  const bool c6_ok = sg_ok && sg >= 0x1p-100f && sg <= 0x1p100f;
 
   const HadamardLane h = hadamard_lane_setup();
   const uint32_t nvec = a.map.nblocks / 8u;
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
   const uint32_t t_dev = map_length(a.map);
+  // Each wave parks its B operand (the 32 input vectors, 8 KiB) in LDS between
+  // the four tiles, so the registers it would hold are free for the search.
+  __shared__ uint4 bpark[FIXED ? kThreads / 64 : 1][8][64];
+  uint4(&bw)[8][64] = bpark[FIXED ? threadIdx.x >> 6 : 0];
   for (uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile * 32u < nvec;
        tile += nwaves) {
     const uint32_t vec = tile * 32u + (lane & 31u);
@@ -1061,15 +1214,33 @@ __global__ __launch_bounds__(kThreads) void quantize_hadamard_kernel(QuantArgs a
     uint4 b[8];
     const BlockIO io = block_io(a.x, a.map, valid ? vec * 8u : 0u, 2u, t_dev);
     const bool live = valid && io.valid;  // the 8 blocks of a vector share one row
-    hadamard_load<SIGNS>((const uint16_t *)io.src, 0, live, h.g, a.hs, b);
+    hadamard_load<SIGNS && !FIXED>((const uint16_t *)io.src, 0, live, h.g, a.hs, b);
+    if (FIXED) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (SIGNS) {
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 m = *(volatile u32x4 *)&smask[SIGNS ? h.g : 0][ks];
+          b[ks] = make_uint4(b[ks].x ^ m.x, b[ks].y ^ m.y, b[ks].z ^ m.z, b[ks].w ^ m.w);
+        }
+        bw[ks][lane] = b[ks];
+      }
+    }
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
-      hadamard_tile<BAL>(h, b, t, y, (const uint4 *)ew);  // every lane takes part
+      if (FIXED) {
+        uint4 bt[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) bt[ks] = bw[ks][lane];
+        hadamard_tile<BAL>(h, bt, t, y, (const uint4 *)ew);  // every lane takes part
+      } else {
+        hadamard_tile<BAL>(h, b, t, y, (const uint4 *)ew);
+      }
       if (live) {
         uint32_t best_p, bc0, bc1;
         if (FIXED)
-          search_block_twins<FLO, FHI>(y, sg, sg_ok, tbl, best_p, bc0, bc1);
+          search_block_cert32<FLO, FHI>(y, sg, sg_ok, c6, c6_ok, tbl, ctbl, best_p, bc0, bc1);
         else
           search_block(y, sg, sg_ok, tbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
         const uint64_t blk = io.dst + 2u * t + h.g;
@@ -1749,6 +1920,7 @@ static hipError_t launch_quantize_balanced(const QuantArgs &a, bool bf16, int g,
 
 hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.map.nblocks, kMaxQuantGroups);
+  const int gc = grid_for(a.map.nblocks, kMaxCertGroups);
   if (a.bal.e) return launch_quantize_balanced(a, bf16, g, s);
   if (a.f_lo == 0 && a.f_hi == 0) {
     const int gr = grid_for((uint64_t)a.map.nblocks * 2u, kMaxQuantGroups);
@@ -1757,11 +1929,11 @@ hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
     else
       hipLaunchKernelGGL(quantize_rule_kernel<false>, dim3(gr), dim3(kThreads), 0, s, a);
   } else if (bf16 && a.f_lo == -2 && a.f_hi == 6)
-    hipLaunchKernelGGL((quantize_certified_kernel<-2, 6, true>), dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((quantize_certified_kernel<-2, 6, true>), dim3(gc), dim3(kThreads), 0, s, a);
   else if (bf16 && a.f_lo == -8 && a.f_hi == 8)
-    hipLaunchKernelGGL((quantize_certified_kernel<-8, 8, true>), dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((quantize_certified_kernel<-8, 8, true>), dim3(gc), dim3(kThreads), 0, s, a);
   else if (bf16 && a.f_lo >= -8 && a.f_hi <= 8)
-    hipLaunchKernelGGL((quantize_certified_kernel<-8, 8, false>), dim3(g), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((quantize_certified_kernel<-8, 8, false>), dim3(gc), dim3(kThreads), 0, s, a);
   else if (bf16)
     hipLaunchKernelGGL((quantize_kernel<true, 0, 0, false>), dim3(g), dim3(kThreads), 0, s, a);
   else if (a.f_lo == -2 && a.f_hi == 6)

@@ -1,9 +1,10 @@
-"""The certified search (bf16 input; FP32 values take the exact search) must give
-the contract's result on blocks where the certificate cannot decide: candidates
-whose SSEs tie exactly or differ by a few parts per million. Inputs are chosen on
-the CPU with the independent NumPy reference (no GPU output is used to build
-them); results are compared bit for bit with the oracle under the same tensor
-scale."""
+"""The certified search (bf16 values with exact one-part sums; binary32 values,
+the Hadamard path's among them, with exact three-part sums) must give the
+contract's result on blocks where the certificate cannot decide: candidates whose
+SSEs tie exactly or differ by a few parts per million, and twins eight patterns
+apart whose codes reconstruct every element alike. Inputs are chosen on the CPU
+with the independent NumPy reference (no GPU output is used to build them);
+results are compared bit for bit with the oracle under the same tensor scale."""
 import numpy as np
 import pytest
 import torch
@@ -104,10 +105,44 @@ def test_mined_near_ties_f32(gpu, orc):
     sg = np.float32(np.abs(xf).max() / np.float32(2688))
     for offsets in [(-2, 6), (-8, 8)]:
         gaps = _relative_gaps(xf, sg, *offsets)
-        pick = np.argsort(gaps, kind="stable")[:1024]
-        print(f"[near-ties f32] {offsets}: gaps min {gaps[pick].min():.2e} max {gaps[pick].max():.2e}")
+        order = np.argsort(gaps, kind="stable")
+        ties = order[gaps[order] == 0][:256]
+        near = order[gaps[order] > 0][:1024 - ties.size]
+        pick = np.concatenate([ties, near])
+        print(f"[near-ties f32] {offsets}: {ties.size} exact ties, nonzero gaps "
+              f"min {gaps[near].min():.2e} max {gaps[near].max():.2e}")
         sel = np.ascontiguousarray(xf[pick].reshape(64, 256))
         check_given(gpu, orc, sel, sg, offsets)
+
+
+def test_twin_ties_f32(gpu, orc):
+    """Blocks whose values sit inside the E2M1 cells {0, 1, 2, 3, 4, 6} of a pattern p
+    (never the 0.5 or 1.5 cells) with the block maximum at 6..7 times its scale: the
+    default pattern is p, p + 1 or p + 2, and the candidate at p and its twin at p + 8
+    reconstruct every element alike (offset pairs (0, 8), (-1, 7), (-2, 6)); half of
+    the blocks are then moved by 1..3 ulps in one element."""
+    rng = np.random.default_rng(51)
+    n = 8192
+    vals = R.e4m3_values()
+    p = rng.integers(40, 110, n)
+    cells = np.array([[0.0, 0.24], [0.76, 1.24], [1.76, 2.49], [2.51, 3.49], [3.51, 4.99],
+                      [5.01, 6.99]], np.float64)
+    k = rng.integers(0, 6, (n, 16))
+    v = rng.uniform(cells[k, 0], cells[k, 1])
+    v[:, 0] = rng.uniform(6.0, 6.99, n)
+    sign = rng.integers(0, 2, (n, 16)) * 2 - 1
+    x = (sign * v * vals[p][:, None]).astype(np.float32)
+    bits = x.view(np.uint32)
+    idx = rng.integers(1, 16, n)
+    bump = np.where(np.arange(n) % 2 == 0, 0, rng.integers(1, 4, n)).astype(np.uint32)
+    nz = (bits[np.arange(n), idx] & 0x7FFFFFFF) != 0
+    bits[np.arange(n)[nz], idx[nz]] += bump[nz]
+    x = bits.view(np.float32)
+    for offsets in [(-8, 8), (-2, 6)]:
+        gaps = _relative_gaps(x, np.float32(1.0), *offsets)
+        print(f"[twin ties] {offsets}: {int((gaps == 0).sum())} exact ties of {n}")
+        assert (gaps == 0).sum() > (n // 8 if offsets == (-8, 8) else 40)
+        check_given(gpu, orc, np.ascontiguousarray(x.reshape(-1, 256)), np.float32(1.0), offsets)
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
