@@ -787,7 +787,7 @@ __device__ __forceinline__ bool twin_codes_identical(uint32_t c0, uint32_t c1, f
 // f in [-2, 0] whose codes are identical to the finer one's (twin_codes_identical)
 // has the same contract SSE and comes later in visiting order, so it can never
 // be the choice; it is dropped (K = inf) instead of contesting.
-// PRUNE: candidates with offset <= -5 are skipped wave-wide when no lane can
+// PRUNE: candidates with offset <= -4 are skipped wave-wide when no lane can
 // need them: the contract SSE is at least its own amax term, and the best
 // candidate's contract SSE is at most A2 + K_best + 2^-18 A2 (K error, the
 // delta bound and the roundings of the bound itself).
@@ -835,7 +835,7 @@ __device__ __forceinline__ void certified_search(const float (&x)[16],
       for (int i = 0; i < 16; ++i) y[i] = x[i] * ce.r;
       if (tie_group) gymax = amax * ce.r;
     }
-    if (PRUNE && k > 0 && f <= -5) {
+    if (PRUNE && k > 0 && f <= -4) {
       const float ub = (a2 + best_k) + a2 * 0x1p-18f;
       const bool live = eligible && !(amax_term(amax, 0.5f * ce.td, ce.r) > ub);
       if (__ballot(live) == 0ull) {
@@ -876,7 +876,7 @@ __device__ __forceinline__ void certified_search(const float (&x)[16],
     } else {
       const bool lt = kf < best_k;
       second_k = __builtin_amdgcn_fmed3f(best_k, second_k, kf);
-      best_k = fminf(best_k, kf);
+      best_k = lt ? kf : best_k;
       best_f = lt ? f : best_f;
       bc0 = lt ? cw[0] : bc0;
       bc1 = lt ? cw[1] : bc1;
@@ -979,9 +979,12 @@ __device__ __forceinline__ void search_block_cert32(const float (&x)[16], float 
                                                     float c6, bool c6_ok, const f32x2 *tbl,
                                                     const CertEntry *ctbl, uint32_t &best_p,
                                                     uint32_t &bc0, uint32_t &bc1) {
-  uint32_t am = 0;
+  // amax by float max of |x| (a NaN would be skipped; it makes A2 NaN, which
+  // sends the block to the exact search)
+  float amf = fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1]));
 #pragma unroll
-  for (int i = 0; i < 16; ++i) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  for (int i = 2; i < 16; ++i) amf = fmaxf(amf, __builtin_fabsf(x[i]));
+  const uint32_t am = __float_as_uint(amf);
   float a2 = x[0] * x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) a2 = __builtin_fmaf(x[i], x[i], a2);
@@ -993,7 +996,7 @@ __device__ __forceinline__ void search_block_cert32(const float (&x)[16], float 
   uint32_t prt[3][8];
   split3_block(x, prt);
   const uint32_t p0 = default_pattern(am, sg, c6, c6_ok);
-  certified_search<FLO, FHI, 3, true, true, (FLO <= -5)>(x, prt, am, p0, a2, tbl, ctbl, FLO,
+  certified_search<FLO, FHI, 3, true, true, (FLO <= -4)>(x, prt, am, p0, a2, tbl, ctbl, FLO,
                                                           FHI, best_p, bc0, bc1);
 }
 
@@ -1107,6 +1110,45 @@ __device__ __forceinline__ bf16x8 hadamard_a(const HadamardLane &h, uint32_t t, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// The A operand of every (tile t, K slice ks) is one of four per-lane quads: the
+// sign (-1)^popcount(feat & (16 ks + 8 g)) splits into a per-lane part (feature
+// bit 3 with g, feature bit 4 with bit 0 of ks) and a wave-uniform part
+// popcount((ks >> 1) & t) (feature bits 5 and 6 are t), so the quads are the
+// base signs times the lane part for even and odd ks, and their negations.
+struct HadamardAQuads {
+  uint4 q[4];  // +even, +odd, -even, -odd
+};
+
+__device__ __forceinline__ HadamardAQuads hadamard_a_quads(const HadamardLane &h) {
+  const uint32_t i = threadIdx.x & 31u;
+  const uint32_t c1 = h.g & ((i >> 4) & 1u), c2 = (i >> 2) & 1u;
+  const uint32_t me = c1 ? 0x80008000u : 0u, mo = (c1 ^ c2) ? 0x80008000u : 0u;
+  HadamardAQuads a;
+  a.q[0] = make_uint4(h.base[0] ^ me, h.base[1] ^ me, h.base[2] ^ me, h.base[3] ^ me);
+  a.q[1] = make_uint4(h.base[0] ^ mo, h.base[1] ^ mo, h.base[2] ^ mo, h.base[3] ^ mo);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    a.q[2 + k] = make_uint4(a.q[k].x ^ 0x80008000u, a.q[k].y ^ 0x80008000u,
+                            a.q[k].z ^ 0x80008000u, a.q[k].w ^ 0x80008000u);
+  return a;
+}
+
+// Tile T (compile-time) of the transform from the quads.
+template <int T>
+__device__ __forceinline__ void hadamard_tile_q(const HadamardAQuads &a, const uint4 (&b)[8],
+                                                float (&y)[16]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int u = __builtin_popcount((ks >> 1) & T) & 1;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, a.q[2 * u + (ks & 1)]), __builtin_bit_cast(bf16x8, b[ks]), acc,
+        0, 0, 0);
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) y[v] = acc[v] * kInvSqrt128f;
+}
+
 // Balancing pair folded into the transform: y = (x diag(2^e)) H' = x (diag(2^e) H'),
 // so the A operand's entry for input feature k becomes +-2^e_k (still exact in
 // bf16, and every product x_k 2^e_k stays exact in FP32). ew holds, per K slice
@@ -1207,6 +1249,7 @@ __global__ __launch_bounds__(kThreads, 3) void quantize_hadamard_kernel(QuantArg
   // the four tiles, so the registers it would hold are free for the search.
   __shared__ uint4 bpark[FIXED ? kThreads / 64 : 1][8][64];
   uint4(&bw)[8][64] = bpark[FIXED ? threadIdx.x >> 6 : 0];
+  const HadamardAQuads aq = hadamard_a_quads(h);
   for (uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile * 32u < nvec;
        tile += nwaves) {
     const uint32_t vec = tile * 32u + (lane & 31u);
@@ -1233,7 +1276,16 @@ __global__ __launch_bounds__(kThreads, 3) void quantize_hadamard_kernel(QuantArg
         uint4 bt[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) bt[ks] = bw[ks][lane];
-        hadamard_tile<BAL>(h, bt, t, y, (const uint4 *)ew);  // every lane takes part
+        if (BAL) {
+          hadamard_tile<BAL>(h, bt, t, y, (const uint4 *)ew);  // every lane takes part
+        } else {
+          switch (t) {
+            case 0: hadamard_tile_q<0>(aq, bt, y); break;
+            case 1: hadamard_tile_q<1>(aq, bt, y); break;
+            case 2: hadamard_tile_q<2>(aq, bt, y); break;
+            default: hadamard_tile_q<3>(aq, bt, y); break;
+          }
+        }
       } else {
         hadamard_tile<BAL>(h, b, t, y, (const uint4 *)ew);
       }
