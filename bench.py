@@ -435,8 +435,9 @@ def kv_append_table(torch, nv, workloads, iters: int = 200):
     # split into pieces of S tokens (each piece on its own workgroups, then merged).
     steps, warm = 100, 5
     variants = [("append", 0), ("append2", 0)] + \
-        [("append+attention", s) for s in (0, 128, 160, 256)] + [("append2+attention", 160)] + \
-        [("attention", s) for s in (0, 64, 128, 160, 192, 256, 512, 1024)]
+        [("append+attention", s) for s in (0, 128, 160, 256)] + \
+        [("append2+attention", s) for s in (96, 128, 160)] + \
+        [("attention", s) for s in (0, 64, 96, 128, 160, 192, 256, 512, 1024)]
     cap = 32768 + (steps + warm) * len(variants) + 8
     kc = nv.kv_cache_alloc(B, H, D, cap, nf, nl, torch.bfloat16, dev)
     vc = nv.kv_cache_alloc(B, H, D, cap, nf, nl, torch.bfloat16, dev)

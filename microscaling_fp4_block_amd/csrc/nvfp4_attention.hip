@@ -955,21 +955,24 @@ __global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
 
 // The units' states of one output row merged: with M the largest base-2 max,
 // w_u = 2^(m_u - M), O = S_P sum_u w_u acc_u / sum_u w_u l_u (0 with no key).
-// One workgroup of kMergeGroups x 32 lanes per row: group j takes the units
-// u = j mod kMergeGroups (four outputs per lane) with its loads independent of
-// one another, and the groups' sums are added in a fixed order, so a grid that
-// covers more units (all empty) gives the same sums. A unit that saw no key
-// holds m_u = -inf, l_u = 0 and a zero accumulator: its weight and terms are 0.
-constexpr uint32_t kMergeGroups = 16;
-constexpr uint32_t kMergeThreads = 32 * kMergeGroups;
+// One workgroup of 256 lanes per (row, slice of 16 outputs): 64 groups of four
+// lanes take the units u = j mod 64 (four outputs per lane) with their loads
+// independent of one another; the groups' sums are then added over a fixed
+// tree (lane shuffles inside each wave, then the four waves in order), so the
+// sums do not depend on timing and a grid that covers more units (all empty)
+// gives the same sums. Every slice forms the same sum of weights. A unit that
+// saw no key holds m_u = -inf, l_u = 0 and a zero accumulator: its weight and
+// terms are 0.
+constexpr uint32_t kMergeSlices = kAttnD / 16;
+constexpr uint32_t kMergeThreads = 256;
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs a,
                                                                         uint32_t units) {
   __shared__ float wmax[kMergeThreads / 64];
-  __shared__ float4 sacc[kMergeGroups][32];
-  __shared__ float sl[kMergeGroups];
-  const uint32_t row = blockIdx.x, tid = threadIdx.x;
+  __shared__ float4 sacc[kMergeThreads / 64][4];
+  __shared__ float sl[kMergeThreads / 64];
+  const uint32_t row = blockIdx.x, slice = blockIdx.y, tid = threadIdx.x;
   const float2 *ml = a.ml + (uint64_t)row * a.ustride;
   const float *part = a.part + (uint64_t)row * a.ustride * kAttnD;
   float mx = -INFINITY;
@@ -981,12 +984,13 @@ __global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs
   float M = wmax[0];
 #pragma unroll
   for (uint32_t w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, wmax[w]);
-  const uint32_t grp = tid >> 5, d0 = 4u * (tid & 31u);
+  const uint32_t grp = tid >> 2, q = tid & 3u;
+  const uint32_t d0 = 16u * slice + 4u * q;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float L = 0.0f;
   if (M != -INFINITY) {
 #pragma unroll 4
-    for (uint32_t u = grp; u < units; u += kMergeGroups) {
+    for (uint32_t u = grp; u < units; u += kMergeThreads / 4) {
       const float2 st = ml[u];
       const float4 p = *(const float4 *)(part + (uint64_t)u * kAttnD + d0);
       const float w = __builtin_amdgcn_exp2f(st.x - M);
@@ -997,30 +1001,43 @@ __global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs
       L += w * st.y;
     }
   }
-  sacc[grp][tid & 31u] = acc;
-  if ((tid & 31u) == 0u) sl[grp] = L;
+  // the 16 groups of this wave (lane bits 2..5): a butterfly, both partners
+  // forming the same sum
+#pragma unroll
+  for (int k = 4; k < 64; k <<= 1) {
+    acc.x += __shfl_xor(acc.x, k);
+    acc.y += __shfl_xor(acc.y, k);
+    acc.z += __shfl_xor(acc.z, k);
+    acc.w += __shfl_xor(acc.w, k);
+    L += __shfl_xor(L, k);
+  }
+  if ((tid & 63u) < 4u) {
+    sacc[tid >> 6][q] = acc;
+    if (q == 0u) sl[tid >> 6] = L;
+  }
   __syncthreads();
-  if (tid >= 32u) return;
+  if (tid >= 4u) return;
   float4 t = sacc[0][tid];
   float lt = sl[0];
-#pragma unroll 8
-  for (uint32_t j = 1; j < kMergeGroups; ++j) {
-    const float4 v = sacc[j][tid];
+#pragma unroll
+  for (uint32_t w = 1; w < kMergeThreads / 64; ++w) {
+    const float4 v = sacc[w][tid];
     t.x += v.x;
     t.y += v.y;
     t.z += v.z;
     t.w += v.w;
-    lt += sl[j];
+    lt += sl[w];
   }
   const float f = lt > 0.0f ? (1.0f / 2688.0f) / lt : 0.0f;
   const float y0 = t.x * f, y1 = t.y * f, y2 = t.z * f, y3 = t.w * f;
+  const uint32_t o0 = 16u * slice + 4u * tid;
   if (OUT_BF16) {
     const bf16x2 lo = __builtin_convertvector((f32x2{y0, y1}), bf16x2);
     const bf16x2 hi = __builtin_convertvector((f32x2{y2, y3}), bf16x2);
-    *(uint2 *)((uint16_t *)a.o + (uint64_t)row * kAttnD + d0) =
+    *(uint2 *)((uint16_t *)a.o + (uint64_t)row * kAttnD + o0) =
         make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
   } else {
-    *(float4 *)((float *)a.o + (uint64_t)row * kAttnD + d0) = make_float4(y0, y1, y2, y3);
+    *(float4 *)((float *)a.o + (uint64_t)row * kAttnD + o0) = make_float4(y0, y1, y2, y3);
   }
 }
 
@@ -1054,7 +1071,7 @@ hipError_t launch_attention(const AttnArgs &a, bool out_bf16, hipStream_t s) {
 
 hipError_t launch_attention_merge(const AttnArgs &a, uint32_t units, bool out_bf16,
                                   hipStream_t s) {
-  const dim3 grid(a.B * a.Hq * a.Nq);
+  const dim3 grid(a.B * a.Hq * a.Nq, kMergeSlices);
   if (out_bf16)
     hipLaunchKernelGGL((attention_merge_kernel<true>), grid, dim3(kMergeThreads), 0, s, a, units);
   else

@@ -919,10 +919,46 @@ __device__ __forceinline__ void certified_search(const float (&x)[16],
   }
 }
 
+// One bf16 block (its 32 bytes as two words of four) through the certified
+// search: default pattern, A2, candidates; writes the contract's choice.
+template <int FLO, int FHI, bool RANGE_FIXED>
+__device__ __forceinline__ void certified_block_bf16(uint4 q0, uint4 q1, float sg, bool sg_ok,
+                                                     float c6, bool c6_ok, const f32x2 *tbl,
+                                                     const CertEntry *ctbl, int f_lo, int f_hi,
+                                                     uint32_t &best_p, uint32_t &bc0,
+                                                     uint32_t &bc1) {
+  constexpr int NC = FHI - FLO + 1;
+  const uint32_t w[1][8] = {{q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w}};
+  float x[16];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    x[2 * k] = __uint_as_float(w[0][k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[0][k] & 0xFFFF0000u);
+  }
+  const uint32_t am = bf16_block_absmax_bits(w[0]);
+  best_p = 0x7Fu;
+  bc0 = 0u;
+  bc1 = 0u;
+  if (!(sg_ok && am < 0x7F800000u)) return;
+  const uint32_t p0 = default_pattern(am, sg, c6, c6_ok);
+  if (NC == 1) {
+    best_p = p0;
+    candidate_codes(x, tbl[p0].y, bc0, bc1);
+    return;
+  }
+  // A2 from the bf16 words: exact squares, eight FP32 roundings.
+  float a2 = dot2_first(__builtin_bit_cast(bf16x2, w[0][0]), __builtin_bit_cast(bf16x2, w[0][0]));
+#pragma unroll
+  for (int k = 1; k < 8; ++k)
+    a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0][k]),
+                                         __builtin_bit_cast(bf16x2, w[0][k]), a2, false);
+  certified_search<FLO, FHI, 1, RANGE_FIXED, false, false>(x, w, am, p0, a2, tbl, ctbl, f_lo,
+                                                            f_hi, best_p, bc0, bc1);
+}
+
 // RANGE_FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI].
 template <int FLO, int FHI, bool RANGE_FIXED>
 __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs a) {
-  constexpr int NC = FHI - FLO + 1;  // visiting slots (offset 0 included)
   __shared__ f32x2 tbl[128];
   __shared__ CertEntry ctbl[kCertRows];
   const float sg = resolve_tensor_scale(a);
@@ -939,32 +975,9 @@ __global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs 
     const BlockIO io = block_io(a.x, a.map, b, 2u, t_dev);
     if (!io.valid) continue;
     const uint4 q0 = load_stream(io.src), q1 = load_stream(io.src + 16);
-    const uint32_t w[1][8] = {{q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w}};
-    float x[16];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      x[2 * k] = __uint_as_float(w[0][k] << 16);
-      x[2 * k + 1] = __uint_as_float(w[0][k] & 0xFFFF0000u);
-    }
-    const uint32_t am = bf16_block_absmax_bits(w[0]);
-
-    uint32_t best_p = 0x7Fu, bc0 = 0u, bc1 = 0u;
-    if (sg_ok && am < 0x7F800000u) {
-      const uint32_t p0 = default_pattern(am, sg, c6, c6_ok);
-      if (NC == 1) {
-        best_p = p0;
-        candidate_codes(x, tbl[p0].y, bc0, bc1);
-      } else {
-        // A2 from the bf16 words: exact squares, eight FP32 roundings.
-        float a2 = dot2_first(__builtin_bit_cast(bf16x2, w[0][0]), __builtin_bit_cast(bf16x2, w[0][0]));
-#pragma unroll
-        for (int k = 1; k < 8; ++k)
-          a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0][k]),
-                                               __builtin_bit_cast(bf16x2, w[0][k]), a2, false);
-        certified_search<FLO, FHI, 1, RANGE_FIXED, false, false>(
-            x, w, am, p0, a2, tbl, ctbl, a.f_lo, a.f_hi, best_p, bc0, bc1);
-      }
-    }
+    uint32_t best_p, bc0, bc1;
+    certified_block_bf16<FLO, FHI, RANGE_FIXED>(q0, q1, sg, sg_ok, c6, c6_ok, tbl, ctbl, a.f_lo,
+                                                a.f_hi, best_p, bc0, bc1);
     *(uint2 *)(a.codes + io.dst * 8u) = make_uint2(bc0, bc1);
     a.scales[io.dst] = (uint8_t)best_p;
   }
@@ -1529,15 +1542,17 @@ __global__ void advance_length_kernel(int64_t *len, uint32_t t_new, uint32_t tot
 // append would otherwise be two or three launches of a few lanes each). The
 // device-resident length (len, the same as c.len_dev and q.map.len_dev; null
 // for a host-held one) is read once, and the admit's sources, which do not
-// depend on it, are loaded at once; after the scale table's barrier every lane
-// has its copy of the length, so it is advanced there; the tokens that leave
-// the recent window are coded with the exact search; a barrier (the admit
-// overwrites ring slots the coding reads); the new full-precision tokens are
-// stored. The tensor scale is the caller's.
+// depend on it, are loaded at once; so is each lane's block leaving the recent
+// window (at most one: nblocks <= kThreads), before the tables are built, so
+// its latency overlaps theirs. After the tables' barrier every lane has its
+// copy of the length, so it is advanced there; the leaving blocks are coded
+// (bf16 with offsets [-2, 6]: the certified search, else the exact one); a
+// barrier (the admit overwrites ring slots the coding reads); the new
+// full-precision tokens are stored. The tensor scale is the caller's.
 template <bool BF16>
 __device__ __forceinline__ void kv_append_small(const QuantArgs &q, const AdmitArgs &c,
                                                 uint32_t row_bytes, int64_t *len,
-                                                f32x2 *tbl) {
+                                                f32x2 *tbl, CertEntry *ctbl) {
   constexpr uint32_t kPer = kSmallAppendChunks / kThreads;
   const uint32_t t_old = len ? (uint32_t)*len : c.t_old;
   const bool fits = !len || (uint64_t)t_old + c.t_new <= c.total;
@@ -1553,10 +1568,53 @@ __device__ __forceinline__ void kv_append_small(const QuantArgs &q, const AdmitA
     }
   }
   const float sg = *q.gscale;
+  BlockIO io{nullptr, 0, false};
+  uint4 r[4] = {};  // the block's bytes: 32 (bf16) or 64 (FP32)
+  if (threadIdx.x < q.map.nblocks) {
+    io = block_io(q.x, q.map, threadIdx.x, BF16 ? 2u : 4u, t_old);
+    if (io.valid) {
+#pragma unroll
+      for (int k = 0; k < (BF16 ? 2 : 4); ++k) r[k] = ((const uint4 *)io.src)[k];
+    }
+  }
   const bool sg_ok = (sg > 0.0f) && (sg < INFINITY);
+  const bool cert = BF16 && q.f_lo == -2 && q.f_hi == 6;
   build_scale_table(tbl, sg);
+  if (cert) {
+    build_cert_table(tbl, ctbl);
+    __syncthreads();
+  }
   if (len && fits && threadIdx.x == 0) *len = (int64_t)t_old + c.t_new;
-  quantize_blocks<BF16, 0, 0, false>(q, tbl, sg, sg_ok, threadIdx.x, kThreads, t_old);
+  if (io.valid) {
+    uint32_t best_p, bc0, bc1;
+    if (cert) {
+      const float c6 = (float)(1.0 / (6.0 * (double)sg));
+      const bool c6_ok = sg_ok && sg >= 0x1p-100f && sg <= 0x1p100f;
+      certified_block_bf16<-2, 6, true>(r[0], r[1], sg, sg_ok, c6, c6_ok, tbl, ctbl, -2, 6,
+                                        best_p, bc0, bc1);
+    } else {
+      float x[16];
+      if (BF16) {
+        const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          x[2 * k] = __uint_as_float(w[k] << 16);
+          x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[4 * k] = __uint_as_float(r[k].x);
+          x[4 * k + 1] = __uint_as_float(r[k].y);
+          x[4 * k + 2] = __uint_as_float(r[k].z);
+          x[4 * k + 3] = __uint_as_float(r[k].w);
+        }
+      }
+      search_block(x, sg, sg_ok, tbl, q.f_lo, q.f_hi, best_p, bc0, bc1);
+    }
+    *(uint2 *)(q.codes + io.dst * 8u) = make_uint2(bc0, bc1);
+    q.scales[io.dst] = (uint8_t)best_p;
+  }
   __syncthreads();
   if (!fits) return;
 #pragma unroll
@@ -1575,7 +1633,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_small_kernel(QuantArgs q, 
                                                                    uint32_t row_bytes,
                                                                    int64_t *len) {
   __shared__ f32x2 tbl[128];
-  kv_append_small<BF16>(q, c, row_bytes, len, tbl);
+  __shared__ CertEntry ctbl[BF16 ? kCertRows : 1];
+  kv_append_small<BF16>(q, c, row_bytes, len, tbl, ctbl);
 }
 
 // Two small appends in one launch, one workgroup each (the K and V caches of a
@@ -1584,10 +1643,11 @@ __global__ __launch_bounds__(kThreads) void kv_append_small_kernel(QuantArgs q, 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void kv_append_small_pair_kernel(KvAppendPair p) {
   __shared__ f32x2 tbl[128];
+  __shared__ CertEntry ctbl[BF16 ? kCertRows : 1];
   if (blockIdx.x == 0)
-    kv_append_small<BF16>(p.q[0], p.c[0], p.row_bytes, p.len[0], tbl);
+    kv_append_small<BF16>(p.q[0], p.c[0], p.row_bytes, p.len[0], tbl, ctbl);
   else
-    kv_append_small<BF16>(p.q[1], p.c[1], p.row_bytes, p.len[1], tbl);
+    kv_append_small<BF16>(p.q[1], p.c[1], p.row_bytes, p.len[1], tbl, ctbl);
 }
 
 // y[BH][T][D] from the sink tokens and the dequantized middle, one 16-element
