@@ -11,10 +11,11 @@ constexpr int kThreads = 256;          // 4 wave64 per workgroup
 constexpr int kMaxAmaxGroups = 512;    // partial maxima kept in the workspace
 constexpr int kMaxStreamGroups = 1024; // grid cap of the streaming dequantize
 constexpr int kMaxQuantGroups = 8192;  // grid cap of the block-parallel kernels
-// Grid cap of the certified search: up to two blocks per lane, so the last
+// Grid cap of the certified search: up to four blocks per lane, so the last
 // round of workgroups is short (measured 253 us against 256 us at 8192 groups
-// on an 8192 x 28672 bf16 tensor; a persistent grid of 1792 took 282 us).
-constexpr int kMaxCertGroups = 28672;
+// on an 8192 x 28672 bf16 tensor, the same as at 28672 groups, which repeat
+// the per-workgroup set-up twice as often; a persistent grid of 1792 took 282 us).
+constexpr int kMaxCertGroups = 14336;
 
 // Division by a runtime constant with one high multiply (Granlund and
 // Montgomery, "Division by invariant integers using multiplication", 1994,
