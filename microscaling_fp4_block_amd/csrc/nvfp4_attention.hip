@@ -566,10 +566,13 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 // four busy; here each workgroup is one wave. Its K operands go from registers
 // to the matrix instructions (each lane loads and decodes the code words of its
 // own operand slices), so only V, transposed, passes through LDS: 12 KB a
-// workgroup, and three waves share each SIMD. A single wave needs no barrier:
-// its LDS accesses run in order, so the next chunk's V is stored into the same
-// buffer once this one's reads are issued, while the codes of the chunk after
-// are in flight in registers. Writes the unit's state for attention_merge_kernel.
+// workgroup. A single wave needs no barrier: its LDS accesses run in order, so
+// the next chunk's V is stored into the same buffer once this one's reads are
+// issued, while the chunk after is in flight in registers (codes, or for the
+// head and tail units the bf16 K and V rows, whose loads would otherwise sit in
+// the dependent chain of every chunk). Two waves share each SIMD (the sink
+// prefetch takes 64 registers), so up to 2,048 units' waves run at once.
+// Writes the unit's state for attention_merge_kernel.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kDecKeys = 32;                // keys per chunk = one softmax tile
 constexpr uint32_t kDecVtStride = kDecKeys + 4;  // fp16 per V^T row (18 dwords)
@@ -650,23 +653,50 @@ __device__ __forceinline__ uint64_t sink_row(const AttnArgs &a, uint32_t kvh, bo
   return head ? (uint64_t)kvh * a.nf + j : (uint64_t)kvh * a.nl + j % a.nl;
 }
 
-// V of a chunk of sink keys transposed into LDS as bf16 bits; keys past hi are zeros.
-__device__ __forceinline__ void dec_store_sink_v(const AttnArgs &a, uint32_t kvh, bool head,
-                                                 uint32_t c0, uint32_t hi, uint32_t t,
-                                                 _Float16 *Vt) {
-  const uint32_t key = t >> 1, d0 = 64u * (t & 1u), j = c0 + key;
-  uint4 q[8];
+// One chunk of sink keys as this lane loads them, one chunk ahead of its use
+// (as the coded chunks): K rows of keys c0 + 16 h + (t & 15), elements
+// 32 (t >> 4) .. +31 (the A operands of Sᵀ), and the V row of key c0 + (t >> 1),
+// elements 64 (t & 1) .. +63 (for the transpose into LDS). Keys past hi stay zero.
+struct SinkRegs {
+  uint4 k[2][4];
+  uint4 v[8];
+};
+
+__device__ __forceinline__ SinkRegs sink_load(const AttnArgs &a, uint32_t kvh, bool head,
+                                              uint32_t c0, uint32_t hi, uint32_t t) {
+  SinkRegs r;
+  const uint32_t g = t >> 4, qc = t & 15u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (j < hi) {
-    const uint4 *vr = (const uint4 *)((head ? a.vh : a.vt) + sink_row(a, kvh, head, j) * kAttnD + d0);
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t j = c0 + 16u * h + qc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = vr[i];
+    for (int s4 = 0; s4 < 4; ++s4) r.k[h][s4] = make_uint4(0u, 0u, 0u, 0u);
+    if (j < hi) {
+      const uint4 *kr = (const uint4 *)((head ? a.kh : a.kt) + sink_row(a, kvh, head, j) * kAttnD +
+                                        32u * g);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) r.k[h][s4] = kr[s4];
+    }
   }
+  const uint32_t jv = c0 + (t >> 1), d0 = 64u * (t & 1u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.v[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (jv < hi) {
+    const uint4 *vr =
+        (const uint4 *)((head ? a.vh : a.vt) + sink_row(a, kvh, head, jv) * kAttnD + d0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.v[i] = vr[i];
+  }
+  return r;
+}
+
+// V of a loaded sink chunk transposed into LDS as bf16 bits.
+__device__ __forceinline__ void sink_store_v(const SinkRegs &r, uint32_t t, _Float16 *Vt) {
+  const uint32_t key = t >> 1, d0 = 64u * (t & 1u);
   uint16_t *vt = (uint16_t *)Vt;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+    const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       vt[dec_vt_index(d0 + 8u * i + e, key)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
@@ -755,7 +785,7 @@ __device__ __forceinline__ float softmax_code_tile16(const f32x4 &s0, const f32x
 // 16 h + 4 g + v.
 // Oᵀ += Vᵀ Pᵀ per 16-row slice of d: the K index 8 g + e runs over keys
 // 4 g + e (e < 4) and 16 + 4 g + e - 4, the order the lane holds its P in.
-__global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 Vt[kAttnD * kDecVtStride];
   __shared__ f32x2 ptbl[128];
   __shared__ f32x2 pthr2[127];
@@ -851,30 +881,21 @@ __global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
   struct Scores {
     f32x4 h[2];
   };
-  auto scores = [&](auto sink_tag, uint32_t c0, const DecRegs &r) {
-    constexpr bool SINK = decltype(sink_tag)::value;
+  auto scores = [&](const auto &r) {
+    constexpr bool SINK = std::is_same<std::decay_t<decltype(r)>, SinkRegs>::value;
     Scores sc;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       sc.h[h] = f32x4{};
-      if (!SINK) {
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
+      for (int s4 = 0; s4 < 4; ++s4) {
+        if constexpr (!SINK)
           sc.h[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dec_k_operand(r, h, s4, sf16), qf[s4],
                                                            sc.h[h], 0, 0, 0);
-      } else {
-        const bool head = z == 0u;
-        const uint32_t j = c0 + 16u * h + qc;
-        const uint4 *kr = (const uint4 *)((head ? a.kh : a.kt) +
-                                          sink_row(a, kvh, head, j < hi ? j : c0) * kAttnD +
-                                          32u * g);
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const uint4 kq = j < hi ? kr[s4] : make_uint4(0u, 0u, 0u, 0u);
+        else
           sc.h[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, kq), __builtin_bit_cast(bf16x8, qf[s4]), sc.h[h], 0, 0,
-              0);
-        }
+              __builtin_bit_cast(bf16x8, r.k[h][s4]), __builtin_bit_cast(bf16x8, qf[s4]), sc.h[h],
+              0, 0, 0);
       }
     }
     return sc;
@@ -889,15 +910,28 @@ __global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
     constexpr bool SINK = decltype(sink_tag)::value;
     const bool head = z == 0u;
     if (lo >= hi) return;
-    if (SINK)
-      dec_store_sink_v(a, kvh, head, lo, hi, t, Vt);
-    else
+    SinkRegs scur, snxt;
+    if constexpr (SINK) {
+      scur = sink_load(a, kvh, head, lo, hi, t);
+      if (lo + kDecKeys < hi) snxt = sink_load(a, kvh, head, lo + kDecKeys, hi, t);
+      sink_store_v(scur, t, Vt);
+    } else {
       dec_store_v(cur, t, sf16, Vt);
-    Scores sc = scores(sink_tag, lo, cur);
+    }
+    Scores sc;
+    if constexpr (SINK)
+      sc = scores(scur);
+    else
+      sc = scores(cur);
     for (uint32_t c0 = lo; c0 < hi; c0 += kDecKeys) {
       const uint32_t c1 = c0 + kDecKeys;
       Scores sn;
-      if (c1 < hi) sn = scores(sink_tag, c1, nxt);
+      if (c1 < hi) {
+        if constexpr (SINK)
+          sn = scores(snxt);
+        else
+          sn = scores(nxt);
+      }
       if (c1 > hi) {  // keys past the unit's end score -inf
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -927,8 +961,9 @@ __global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
       // the next chunk's V into the same buffer (this one's reads are issued and
       // LDS runs one wave's accesses in order), the codes of the one after in flight
       if (c1 < hi) {
-        if (SINK) {
-          dec_store_sink_v(a, kvh, head, c1, hi, t, Vt);
+        if constexpr (SINK) {
+          sink_store_v(snxt, t, Vt);
+          if (c1 + kDecKeys < hi) snxt = sink_load(a, kvh, head, c1 + kDecKeys, hi, t);
         } else {
           dec_store_v(nxt, t, sf16, Vt);
           if (c1 + kDecKeys < hi) nxt = dec_load(a, coded_base, c1 + kDecKeys, hi, t);
@@ -956,15 +991,18 @@ __global__ __launch_bounds__(64, 3) void attention_decode_kernel(AttnArgs a) {
 // The units' states of one output row merged: with M the largest base-2 max,
 // w_u = 2^(m_u - M), O = S_P sum_u w_u acc_u / sum_u w_u l_u (0 with no key).
 // One workgroup of 256 lanes per (row, slice of 16 outputs): 64 groups of four
-// lanes take the units u = j mod 64 (four outputs per lane) with their loads
-// independent of one another; the groups' sums are then added over a fixed
-// tree (lane shuffles inside each wave, then the four waves in order), so the
-// sums do not depend on timing and a grid that covers more units (all empty)
-// gives the same sums. Every slice forms the same sum of weights. A unit that
-// saw no key holds m_u = -inf, l_u = 0 and a zero accumulator: its weight and
-// terms are 0.
+// lanes take the units u = j mod 64 (four outputs per lane). A lane loads the
+// states and accumulator slices of its first kMergePre units together, so one
+// memory round trip serves both the maximum and the sums; the groups' sums are
+// then added over a fixed tree (lane shuffles inside each wave, then the four
+// waves in order), so the sums do not depend on timing and a grid that covers
+// more units (all empty) gives the same sums. Every slice forms the same sum of
+// weights. A unit that saw no key holds m_u = -inf, l_u = 0 and a zero
+// accumulator: its weight and terms are 0.
 constexpr uint32_t kMergeSlices = kAttnD / 16;
 constexpr uint32_t kMergeThreads = 256;
+constexpr uint32_t kMergeGroups = kMergeThreads / 4;
+constexpr uint32_t kMergePre = 8;
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs a,
@@ -975,8 +1013,25 @@ __global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs
   const uint32_t row = blockIdx.x, slice = blockIdx.y, tid = threadIdx.x;
   const float2 *ml = a.ml + (uint64_t)row * a.ustride;
   const float *part = a.part + (uint64_t)row * a.ustride * kAttnD;
+  const uint32_t grp = tid >> 2, q = tid & 3u;
+  const uint32_t d0 = 16u * slice + 4u * q;
+  float2 st[kMergePre];
+  float4 pv[kMergePre];
+#pragma unroll
+  for (uint32_t k = 0; k < kMergePre; ++k) {
+    const uint32_t u = grp + kMergeGroups * k;
+    st[k] = make_float2(-INFINITY, 0.0f);
+    pv[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (u < units) {
+      st[k] = ml[u];
+      pv[k] = *(const float4 *)(part + (uint64_t)u * kAttnD + d0);
+    }
+  }
   float mx = -INFINITY;
-  for (uint32_t u = tid; u < units; u += kMergeThreads) mx = fmaxf(mx, ml[u].x);
+#pragma unroll
+  for (uint32_t k = 0; k < kMergePre; ++k) mx = fmaxf(mx, st[k].x);
+  for (uint32_t u = grp + kMergeGroups * kMergePre; u < units; u += kMergeGroups)
+    mx = fmaxf(mx, ml[u].x);
 #pragma unroll
   for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
   if ((tid & 63u) == 0u) wmax[tid >> 6] = mx;
@@ -984,21 +1039,27 @@ __global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs
   float M = wmax[0];
 #pragma unroll
   for (uint32_t w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, wmax[w]);
-  const uint32_t grp = tid >> 2, q = tid & 3u;
-  const uint32_t d0 = 16u * slice + 4u * q;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float L = 0.0f;
   if (M != -INFINITY) {
-#pragma unroll 4
-    for (uint32_t u = grp; u < units; u += kMergeThreads / 4) {
-      const float2 st = ml[u];
+#pragma unroll
+    for (uint32_t k = 0; k < kMergePre; ++k) {
+      const float w = __builtin_amdgcn_exp2f(st[k].x - M);
+      acc.x += w * pv[k].x;
+      acc.y += w * pv[k].y;
+      acc.z += w * pv[k].z;
+      acc.w += w * pv[k].w;
+      L += w * st[k].y;
+    }
+    for (uint32_t u = grp + kMergeGroups * kMergePre; u < units; u += kMergeGroups) {
+      const float2 s2 = ml[u];
       const float4 p = *(const float4 *)(part + (uint64_t)u * kAttnD + d0);
-      const float w = __builtin_amdgcn_exp2f(st.x - M);
+      const float w = __builtin_amdgcn_exp2f(s2.x - M);
       acc.x += w * p.x;
       acc.y += w * p.y;
       acc.z += w * p.z;
       acc.w += w * p.w;
-      L += w * st.y;
+      L += w * s2.y;
     }
   }
   // the 16 groups of this wave (lane bits 2..5): a butterfly, both partners
