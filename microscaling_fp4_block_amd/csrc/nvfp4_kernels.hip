@@ -581,11 +581,13 @@ __global__ __launch_bounds__(kThreads) void quantize_rule_kernel(QuantArgs a) {
 //    A2 = sum a_i^2. Then E_f = A2 + K_f with K_f = d (d S2 - 2 S1),
 //    S1 = sum a_i V_i, S2 = sum V_i^2.
 //  * S1 and S2 are exact in FP32 (v_dot2_f32_bf16): V_i is a multiple of 1/2
-//    up to 6; an element with V_i > 0 has y > 1/4, so for candidates within
-//    8 normal E4M3 steps of the default pattern (d within a factor 2.6 of
-//    it) a_i > amax/128: every nonzero product and partial sum is a multiple
-//    of 2^(E-15) below 2^(E+8), E the exponent of amax (23 bits). S2 is a
-//    multiple of 1/4 below 577.
+//    up to 6; an element with V_i > 0 has y > 1/4. When the default pattern
+//    is not saturated (amax / (6 S_g) <= 447, so d_0 >= amax / 6.375), a
+//    candidate within 8 normal E4M3 steps below it has d >= d_0 / 2, so
+//    a_i > amax / 51 > amax / 64: every nonzero product and partial sum is a
+//    multiple of 2^(E-14) below 2^(E+8), E the exponent of amax (22 bits). S2
+//    is a multiple of 1/4 below 577. (A caller-given S_g can saturate a
+//    block's pattern; such blocks take the exact path.)
 //  * K_f = 2d (d/2 S2 - S1) is formed in FP32: d/2 and 2d are exact, the
 //    fused multiply-add rounds once and the multiply once, so K_f is within
 //    2u |K_f| (u = 2^-24), and D_f = K_f - K_0 rounds once more. With
@@ -608,8 +610,9 @@ __global__ __launch_bounds__(kThreads) void quantize_rule_kernel(QuantArgs a) {
 //    If every other candidate has L_f > U_w (it suffices to test the
 //    runner-up in D), its SSE is certainly larger and w is the contract's
 //    choice. Otherwise (near-ties, or a block outside the
-//    range where the argument holds: non-normal candidate patterns, amax
-//    outside [2^-40, 2^60]) the lane evaluates the contract's FP32 SSE
+//    range where the argument holds: non-normal candidate patterns, a
+//    saturated default pattern, amax outside [2^-40, 2^60]) the lane
+//    evaluates the contract's FP32 SSE
 //    exactly for the candidates that could win and applies the visiting-order
 //    rule among them.
 //
@@ -794,16 +797,19 @@ __device__ __forceinline__ bool twin_codes_identical(uint32_t c0, uint32_t c1, f
 template <int FLO, int FHI, int NP, bool RANGE_FIXED, bool TIES, bool PRUNE>
 __device__ __forceinline__ void certified_search(const float (&x)[16],
                                                  const uint32_t (&prt)[NP][8], uint32_t am,
-                                                 uint32_t p0, float a2, const f32x2 *tbl,
-                                                 const CertEntry *ctbl, int f_lo, int f_hi,
-                                                 uint32_t &best_p, uint32_t &bc0,
-                                                 uint32_t &bc1) {
+                                                 uint32_t p0, bool unsat, float a2,
+                                                 const f32x2 *tbl, const CertEntry *ctbl,
+                                                 int f_lo, int f_hi, uint32_t &best_p,
+                                                 uint32_t &bc0, uint32_t &bc1) {
   constexpr int NC = FHI - FLO + 1;
   constexpr float kA2Coef = NP == 1 ? 2.3f : 3.6f;
-  // certificate applies: every candidate pattern normal, amax in
-  // [2^-40, 2^60]; other blocks take the exact path below. Candidates
-  // above pattern 126 read the zero rows of the table.
-  const bool eligible = ((int)p0 + FLO >= 8) && am >= 0x2B800000u && am <= 0x5D800000u;
+  // certificate applies: every candidate pattern normal, the default pattern
+  // not saturated (unsat: amax / (6 S_g) <= 447, so d_0 is within 1/16 of
+  // amax / 6; a caller-given S_g can saturate blocks), amax in [2^-40, 2^60];
+  // other blocks take the exact path below. Candidates above pattern 126 read
+  // the zero rows of the table.
+  const bool eligible =
+      unsat && ((int)p0 + FLO >= 8) && am >= 0x2B800000u && am <= 0x5D800000u;
   const int p0b = max((int)p0, -FLO);  // keeps table indices >= 0
   const float amax = __uint_as_float(am);
 
@@ -952,8 +958,9 @@ __device__ __forceinline__ void certified_block_bf16(uint4 q0, uint4 q1, float s
   for (int k = 1; k < 8; ++k)
     a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0][k]),
                                          __builtin_bit_cast(bf16x2, w[0][k]), a2, false);
-  certified_search<FLO, FHI, 1, RANGE_FIXED, false, false>(x, w, am, p0, a2, tbl, ctbl, f_lo,
-                                                            f_hi, best_p, bc0, bc1);
+  const bool unsat = c6_ok && __uint_as_float(am) * c6 <= 447.0f;
+  certified_search<FLO, FHI, 1, RANGE_FIXED, false, false>(x, w, am, p0, unsat, a2, tbl, ctbl,
+                                                            f_lo, f_hi, best_p, bc0, bc1);
 }
 
 // RANGE_FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI].
@@ -1009,8 +1016,9 @@ __device__ __forceinline__ void search_block_cert32(const float (&x)[16], float 
   uint32_t prt[3][8];
   split3_block(x, prt);
   const uint32_t p0 = default_pattern(am, sg, c6, c6_ok);
-  certified_search<FLO, FHI, 3, true, true, (FLO <= -4)>(x, prt, am, p0, a2, tbl, ctbl, FLO,
-                                                          FHI, best_p, bc0, bc1);
+  const bool unsat = c6_ok && amf * c6 <= 447.0f;
+  certified_search<FLO, FHI, 3, true, true, (FLO <= -4)>(x, prt, am, p0, unsat, a2, tbl, ctbl,
+                                                          FLO, FHI, best_p, bc0, bc1);
 }
 
 // Blocks first, first + stride, ... of the region. FIXED: the launch guarantees

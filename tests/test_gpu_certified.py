@@ -216,3 +216,25 @@ def test_default_pattern_near_e4m3_midpoints(gpu, orc):
                 check_given(gpu, orc, xh, sg, offsets)
     print(f"[p0] blocks within 8 ulps of an E4M3 midpoint: {near}, exactly on one: {ties}")
     assert near > 1000 and ties > 100
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_saturating_given_scale(gpu, orc, dt):
+    """A caller-given tensor scale 2^1 .. 2^7 below amax / 2688 (rows of widely
+    different magnitudes): the default patterns of the larger blocks saturate at
+    448, where the certificate's bounds do not hold, so those blocks take the
+    exact search."""
+    rng = np.random.default_rng(61)
+    x = (rng.standard_normal((64, 1024)) * np.exp(rng.normal(0.0, 1.5, (64, 1)))).astype(np.float32)
+    xin = workloads.to_bf16_bits(x) if dt == "bf16" else x
+    xf = workloads.bf16_bits_to_f32(xin) if dt == "bf16" else x
+    amax = np.abs(xf).reshape(-1, 16).max(1)
+    A = float(np.abs(xf).max())
+    for k in (1, 3, 7):
+        sg = np.float32(A / 2688.0 / 2.0 ** k)
+        t = ((amax / np.float32(6)).astype(np.float32) / sg).astype(np.float32)
+        print(f"[saturating] {dt} S_g = A / 2688 / 2^{k}: {int((t > 448).sum())} of {amax.size} "
+              "blocks saturated")
+        assert (t > 448).sum() > 0 and (t <= 447).sum() > 0
+        for offsets in [(-2, 6), (-8, 8)]:
+            check_given(gpu, orc, np.ascontiguousarray(xin), sg, offsets)

@@ -131,3 +131,20 @@ def test_hadamard_non_finite(gpu, orc):
     torch.cuda.synchronize()
     assert np.isnan(g.item())
     assert np.all(to_host(s) == 0x7F) and np.all(to_host(c) == 0)
+
+
+def test_hadamard_saturating_given_scale(gpu, orc):
+    """The Hadamard path with a caller-given tensor scale 2^4 below the transform's
+    amax / 2688: the blocks whose default pattern saturates take the exact search.
+    Split parity: the oracle quantizes the GPU's own transform under the same S_g."""
+    x = workloads.workload(5, (1, 2, 300, 128))
+    xd = to_dev(x)
+    y = to_host(gpu.hadamard128(xd)).reshape(-1, 128)
+    sg = np.float32(np.abs(y).max() / 2688.0 / 16.0)
+    g = torch.tensor([sg], dtype=torch.float32, device="cuda:0")
+    for offsets in [(-8, 8), (-2, 6)]:
+        c, s, _ = gpu.quantize(xd, offsets, hadamard=True, global_scale=g)
+        torch.cuda.synchronize()
+        rc, rs, _ = orc.quantize(y, *offsets, gscale=float(sg))
+        assert np.array_equal(to_host(s).reshape(rs.shape), rs)
+        assert np.array_equal(to_host(c).reshape(rc.shape), rc)
