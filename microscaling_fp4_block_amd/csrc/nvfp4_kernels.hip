@@ -736,11 +736,16 @@ __device__ __forceinline__ void build_cert_table(const f32x2 *tbl, CertEntry *ct
 // in E4M3's normal range), so when q is more than 8 ulps from a midpoint, q and
 // t give the same pattern. Otherwise (or for q in E4M3's subnormal range, or
 // S_g outside [2^-100, 2^100]) t is formed as the contract does.
+// On the fast path q is normal in E4M3 (>= 2^-6), where nearest-even onto the
+// pattern grid is a rounding of q's binary32 pattern at bit 20 (saturating at
+// 126); zero, subnormal and near-midpoint quotients take the contract's steps.
 __device__ __forceinline__ uint32_t default_pattern(uint32_t am, float sg, float c6, bool c6_ok) {
-  float t = __uint_as_float(am) * c6;
-  const bool near_mid = ((__float_as_uint(t) - 0x80000u + 8u) & 0xFFFFFu) <= 16u;
-  if (!c6_ok || near_mid || !(t >= 0x1p-6f || am == 0u)) t = (__uint_as_float(am) / 6.0f) / sg;
-  return e4m3_rne_sat(t);
+  const float q = __uint_as_float(am) * c6;
+  const uint32_t b = __float_as_uint(q);
+  const bool near_mid = ((b - 0x80000u + 8u) & 0xFFFFFu) <= 16u;
+  if (!c6_ok || near_mid || !(q >= 0x1p-6f))
+    return e4m3_rne_sat((__uint_as_float(am) / 6.0f) / sg);
+  return min(((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u, 126u);
 }
 
 // Three-way split of a binary32 block for exact dot products with E2M1 values:
