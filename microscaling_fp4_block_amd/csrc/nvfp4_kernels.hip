@@ -968,9 +968,11 @@ __device__ __forceinline__ void certified_block_bf16(uint4 q0, uint4 q1, float s
                                                             f_lo, f_hi, best_p, bc0, bc1);
 }
 
-// RANGE_FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI].
+// RANGE_FIXED: the launch guarantees [f_lo, f_hi] == [FLO, FHI]. Up to nine
+// candidates fit in 64 registers: eight waves per SIMD.
 template <int FLO, int FHI, bool RANGE_FIXED>
-__global__ __launch_bounds__(kThreads) void quantize_certified_kernel(QuantArgs a) {
+__global__ __launch_bounds__(kThreads, (FHI - FLO + 1 <= 9) ? 8 : 1) void quantize_certified_kernel(
+    QuantArgs a) {
   __shared__ f32x2 tbl[128];
   __shared__ CertEntry ctbl[kCertRows];
   const float sg = resolve_tensor_scale(a);
