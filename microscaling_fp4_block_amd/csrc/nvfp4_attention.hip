@@ -990,30 +990,40 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
 
 // The units' states of one output row merged: with M the largest base-2 max,
 // w_u = 2^(m_u - M), O = S_P sum_u w_u acc_u / sum_u w_u l_u (0 with no key).
-// One workgroup of 256 lanes per (row, slice of 16 outputs): 64 groups of four
-// lanes take the units u = j mod 64 (four outputs per lane). A lane loads the
-// states and accumulator slices of its first kMergePre units together, so one
-// memory round trip serves both the maximum and the sums; the groups' sums are
-// then added over a fixed tree (lane shuffles inside each wave, then the four
-// waves in order), so the sums do not depend on timing and a grid that covers
-// more units (all empty) gives the same sums. Every slice forms the same sum of
-// weights. A unit that saw no key holds m_u = -inf, l_u = 0 and a zero
-// accumulator: its weight and terms are 0.
+// One wave per (row, slice of 16 outputs): 16 groups of four lanes take the
+// units u = j mod 16 (four outputs per lane). A lane loads the states and
+// accumulator slices of its first kMergePre units together, so one memory round
+// trip serves both the maximum and the sums, then the groups' maxima and sums
+// are combined inside the wave (row rotations, then the permlane swaps between
+// rows): no LDS and no barrier. The combination order is fixed, so the sums do
+// not depend on timing, and a grid that covers more units (all empty: weight 0,
+// zero terms) gives the same sums. Every slice forms the same sum of weights. A
+// unit that saw no key holds m_u = -inf, l_u = 0 and a zero accumulator: its
+// weight and terms are 0.
 constexpr uint32_t kMergeSlices = kAttnD / 16;
-constexpr uint32_t kMergeThreads = 256;
-constexpr uint32_t kMergeGroups = kMergeThreads / 4;
-constexpr uint32_t kMergePre = 8;
+constexpr uint32_t kMergeGroups = 16;
+constexpr uint32_t kMergePre = 16;
+
+// v combined with the lanes 4, 8 and 12 further round its row of 16 (row
+// rotations: every lane of the row gets the combination of its four groups).
+__device__ __forceinline__ float row_groups_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF,
+                                                           false)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF,
+                                                             0xF, false)));
+}
+__device__ __forceinline__ float row_groups_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF,
+                                                        false));
+}
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs a,
-                                                                        uint32_t units) {
-  __shared__ float wmax[kMergeThreads / 64];
-  __shared__ float4 sacc[kMergeThreads / 64][4];
-  __shared__ float sl[kMergeThreads / 64];
-  const uint32_t row = blockIdx.x, slice = blockIdx.y, tid = threadIdx.x;
+__global__ __launch_bounds__(64) void attention_merge_kernel(AttnArgs a, uint32_t units) {
+  const uint32_t row = blockIdx.x, slice = blockIdx.y, lane = threadIdx.x;
   const float2 *ml = a.ml + (uint64_t)row * a.ustride;
   const float *part = a.part + (uint64_t)row * a.ustride * kAttnD;
-  const uint32_t grp = tid >> 2, q = tid & 3u;
+  const uint32_t grp = lane >> 2, q = lane & 3u;
   const uint32_t d0 = 16u * slice + 4u * q;
   float2 st[kMergePre];
   float4 pv[kMergePre];
@@ -1032,13 +1042,7 @@ __global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs
   for (uint32_t k = 0; k < kMergePre; ++k) mx = fmaxf(mx, st[k].x);
   for (uint32_t u = grp + kMergeGroups * kMergePre; u < units; u += kMergeGroups)
     mx = fmaxf(mx, ml[u].x);
-#pragma unroll
-  for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
-  if ((tid & 63u) == 0u) wmax[tid >> 6] = mx;
-  __syncthreads();
-  float M = wmax[0];
-#pragma unroll
-  for (uint32_t w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, wmax[w]);
+  const float M = pair_max32(pair_max16(row_groups_max(mx)));
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float L = 0.0f;
   if (M != -INFINITY) {
@@ -1062,43 +1066,21 @@ __global__ __launch_bounds__(kMergeThreads) void attention_merge_kernel(AttnArgs
       L += w * s2.y;
     }
   }
-  // the 16 groups of this wave (lane bits 2..5): a butterfly, both partners
-  // forming the same sum
-#pragma unroll
-  for (int k = 4; k < 64; k <<= 1) {
-    acc.x += __shfl_xor(acc.x, k);
-    acc.y += __shfl_xor(acc.y, k);
-    acc.z += __shfl_xor(acc.z, k);
-    acc.w += __shfl_xor(acc.w, k);
-    L += __shfl_xor(L, k);
-  }
-  if ((tid & 63u) < 4u) {
-    sacc[tid >> 6][q] = acc;
-    if (q == 0u) sl[tid >> 6] = L;
-  }
-  __syncthreads();
-  if (tid >= 4u) return;
-  float4 t = sacc[0][tid];
-  float lt = sl[0];
-#pragma unroll
-  for (uint32_t w = 1; w < kMergeThreads / 64; ++w) {
-    const float4 v = sacc[w][tid];
-    t.x += v.x;
-    t.y += v.y;
-    t.z += v.z;
-    t.w += v.w;
-    lt += sl[w];
-  }
-  const float f = lt > 0.0f ? (1.0f / 2688.0f) / lt : 0.0f;
-  const float y0 = t.x * f, y1 = t.y * f, y2 = t.z * f, y3 = t.w * f;
-  const uint32_t o0 = 16u * slice + 4u * tid;
+  acc.x = pair_sum32(pair_sum16(row_groups_sum(acc.x)));
+  acc.y = pair_sum32(pair_sum16(row_groups_sum(acc.y)));
+  acc.z = pair_sum32(pair_sum16(row_groups_sum(acc.z)));
+  acc.w = pair_sum32(pair_sum16(row_groups_sum(acc.w)));
+  L = pair_sum32(pair_sum16(row_groups_sum(L)));
+  if (grp != 0u) return;
+  const float f = L > 0.0f ? (1.0f / 2688.0f) / L : 0.0f;
+  const float y0 = acc.x * f, y1 = acc.y * f, y2 = acc.z * f, y3 = acc.w * f;
   if (OUT_BF16) {
     const bf16x2 lo = __builtin_convertvector((f32x2{y0, y1}), bf16x2);
     const bf16x2 hi = __builtin_convertvector((f32x2{y2, y3}), bf16x2);
-    *(uint2 *)((uint16_t *)a.o + (uint64_t)row * kAttnD + o0) =
+    *(uint2 *)((uint16_t *)a.o + (uint64_t)row * kAttnD + d0) =
         make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
   } else {
-    *(float4 *)((float *)a.o + (uint64_t)row * kAttnD + o0) = make_float4(y0, y1, y2, y3);
+    *(float4 *)((float *)a.o + (uint64_t)row * kAttnD + d0) = make_float4(y0, y1, y2, y3);
   }
 }
 
@@ -1134,9 +1116,9 @@ hipError_t launch_attention_merge(const AttnArgs &a, uint32_t units, bool out_bf
                                   hipStream_t s) {
   const dim3 grid(a.B * a.Hq * a.Nq, kMergeSlices);
   if (out_bf16)
-    hipLaunchKernelGGL((attention_merge_kernel<true>), grid, dim3(kMergeThreads), 0, s, a, units);
+    hipLaunchKernelGGL((attention_merge_kernel<true>), grid, dim3(64), 0, s, a, units);
   else
-    hipLaunchKernelGGL((attention_merge_kernel<false>), grid, dim3(kMergeThreads), 0, s, a, units);
+    hipLaunchKernelGGL((attention_merge_kernel<false>), grid, dim3(64), 0, s, a, units);
   return hipGetLastError();
 }
 
