@@ -819,7 +819,7 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
 
   // Set-up loads in the order they are needed, so that each wait leaves the
   // later ones in flight: the tables, this lane's Q codes, then (coded units)
-  // the codes of the first two chunks, which arrive while the tables and Q are
+  // the codes of the first chunk, which arrive while the tables and Q are
   // stored and decoded.
   f32x2 tb_r[2], tb_t[2];
   uint16_t tb_s[4];
@@ -839,10 +839,7 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
   }
   const uint64_t coded_base = (uint64_t)kvh * a.cap;
   DecRegs cur{}, nxt{};
-  if (!sink && lo < hi) {
-    cur = dec_load(a, coded_base, lo, hi, t);
-    if (lo + kDecKeys < hi) nxt = dec_load(a, coded_base, lo + kDecKeys, hi, t);
-  }
+  if (!sink && lo < hi) cur = dec_load(a, coded_base, lo, hi, t);
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -906,76 +903,96 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
   // Software-pipelined by one chunk: the next chunk's scores depend only on its
   // keys and Q, so their products are issued before this chunk's softmax, P
   // coding and PV products, which hold the dependent chain.
-  auto run = [&](auto sink_tag) {
+  // Keys of the chunk at c0 past the unit's end score -inf.
+  auto mask_tail = [&](Scores &sc, uint32_t c0) {
+    if (c0 + kDecKeys > hi) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          sc.h[h][v] = c0 + 16u * h + 4u * g + v < hi ? sc.h[h][v] : -INFINITY;
+    }
+  };
+  // The chunk's online softmax, P coding and O^T += V^T P^T (V^T in LDS).
+  auto consume = [&](auto sink_tag, Scores &sc, uint32_t c0) {
     constexpr bool SINK = decltype(sink_tag)::value;
+    mask_tail(sc, c0);
+    f16x8 pb;
+    const float alpha = softmax_code_tile16(sc.h[0], sc.h[1], c2, m, l, pthr2, ptbl, pb);
+    if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t d = 16u * i + qc;
+      const uint2 x0 = *(const uint2 *)&Vt[dec_vt_index(d, 4u * g)];
+      const uint2 x1 = *(const uint2 *)&Vt[dec_vt_index(d, 16u + 4u * g)];
+      const uint4 vv = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      if (!SINK)
+        o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vv), pb, o[i], 0,
+                                                      0, 0);
+      else
+        o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                       to_bf16x8(pb), o[i], 0, 0, 0);
+    }
+  };
+
+  // Sink units: the first two chunks' bf16 rows loaded at once, then the chunk
+  // loop pipelined by one chunk (the next chunk's score products, which need
+  // only its keys and Q, issued before this chunk's softmax, P coding and PV
+  // products, which hold the dependent chain; the next chunk's V stored into the
+  // same buffer once this one's reads are issued, as LDS runs one wave's
+  // accesses in order; the rows of the chunk after in flight).
+  auto run_sink = [&]() {
     const bool head = z == 0u;
     if (lo >= hi) return;
-    SinkRegs scur, snxt;
-    if constexpr (SINK) {
-      scur = sink_load(a, kvh, head, lo, hi, t);
+    SinkRegs snxt;
+    Scores sc;
+    {
+      const SinkRegs scur = sink_load(a, kvh, head, lo, hi, t);
       if (lo + kDecKeys < hi) snxt = sink_load(a, kvh, head, lo + kDecKeys, hi, t);
       sink_store_v(scur, t, Vt);
-    } else {
-      dec_store_v(cur, t, sf16, Vt);
-    }
-    Scores sc;
-    if constexpr (SINK)
       sc = scores(scur);
-    else
-      sc = scores(cur);
+    }
     for (uint32_t c0 = lo; c0 < hi; c0 += kDecKeys) {
       const uint32_t c1 = c0 + kDecKeys;
       Scores sn;
+      if (c1 < hi) sn = scores(snxt);
+      consume(std::true_type{}, sc, c0);
       if (c1 < hi) {
-        if constexpr (SINK)
-          sn = scores(snxt);
-        else
-          sn = scores(nxt);
-      }
-      if (c1 > hi) {  // keys past the unit's end score -inf
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            sc.h[h][v] = c0 + 16u * h + 4u * g + v < hi ? sc.h[h][v] : -INFINITY;
-      }
-      f16x8 pb;
-      const float alpha = softmax_code_tile16(sc.h[0], sc.h[1], c2, m, l, pthr2, ptbl, pb);
-      if (__ballot(alpha != 1.0f) != 0ull) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] *= alpha;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t d = 16u * i + qc;
-        const uint2 x0 = *(const uint2 *)&Vt[dec_vt_index(d, 4u * g)];
-        const uint2 x1 = *(const uint2 *)&Vt[dec_vt_index(d, 16u + 4u * g)];
-        const uint4 vv = make_uint4(x0.x, x0.y, x1.x, x1.y);
-        if (!SINK)
-          o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vv), pb, o[i],
-                                                        0, 0, 0);
-        else
-          o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                         to_bf16x8(pb), o[i], 0, 0, 0);
-      }
-      // the next chunk's V into the same buffer (this one's reads are issued and
-      // LDS runs one wave's accesses in order), the codes of the one after in flight
-      if (c1 < hi) {
-        if constexpr (SINK) {
-          sink_store_v(snxt, t, Vt);
-          if (c1 + kDecKeys < hi) snxt = sink_load(a, kvh, head, c1 + kDecKeys, hi, t);
-        } else {
-          dec_store_v(nxt, t, sf16, Vt);
-          if (c1 + kDecKeys < hi) nxt = dec_load(a, coded_base, c1 + kDecKeys, hi, t);
-        }
+        sink_store_v(snxt, t, Vt);
+        if (c1 + kDecKeys < hi) snxt = sink_load(a, kvh, head, c1 + kDecKeys, hi, t);
         sc = sn;
       }
     }
   };
+
+  // Coded units: only the first chunk's codes are loaded in the set-up, so that
+  // the first chunks of all units, which every wave requests at once, arrive
+  // first; each wave asks for its second chunk once its first is in. The next
+  // chunk's V store and score products follow this chunk's PV products (they
+  // are needed only at the next chunk's softmax), the codes of the chunk after
+  // in flight meanwhile.
+  auto run_coded = [&]() {
+    if (lo >= hi) return;
+    dec_store_v(cur, t, sf16, Vt);
+    Scores sc = scores(cur);
+    if (lo + kDecKeys < hi) nxt = dec_load(a, coded_base, lo + kDecKeys, hi, t);
+    for (uint32_t c0 = lo; c0 < hi; c0 += kDecKeys) {
+      const uint32_t c1 = c0 + kDecKeys;
+      consume(std::false_type{}, sc, c0);
+      if (c1 < hi) {
+        dec_store_v(nxt, t, sf16, Vt);
+        sc = scores(nxt);
+        if (c1 + kDecKeys < hi) nxt = dec_load(a, coded_base, c1 + kDecKeys, hi, t);
+      }
+    }
+  };
   if (sink)
-    run(std::true_type{});
+    run_sink();
   else
-    run(std::false_type{});
+    run_coded();
 
   l = pair_sum32(pair_sum16(l));
   if (!qvalid) return;
