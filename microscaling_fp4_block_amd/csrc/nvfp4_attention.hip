@@ -798,29 +798,33 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
   const bool qvalid = qi < rows;
   const uint64_t row = (uint64_t)kvh * rows + (qvalid ? qi : 0u);
 
-  // keys present (the device-resident count if there is one) and this unit's range
-  const uint32_t Nk = a.nk_dev ? (uint32_t)min<int64_t>(*a.nk_dev, (int64_t)a.nf + a.cap + a.nl)
-                               : a.Nk;
-  const uint32_t mid_hi = max(Nk > a.nl ? Nk - a.nl : 0u, a.nf);
   const uint32_t z = blockIdx.z;
   const bool sink = z < 2u;
-  uint32_t lo, hi;
-  if (z == 0u) {
-    lo = 0u;
-    hi = min(a.nf, Nk);
-  } else if (z == 1u) {
-    lo = max(mid_hi, a.nf);
-    hi = Nk;
-  } else {
-    const uint64_t l64 = (uint64_t)a.nf + (uint64_t)(z - 2u) * a.split;
-    lo = (uint32_t)min<uint64_t>(l64, mid_hi);
-    hi = (uint32_t)min<uint64_t>(l64 + a.split, mid_hi);
+  // A middle unit's piece of the cache's capacity (rows nf .. nf + cap): its first
+  // chunk is loaded from it before the token count is known (every row in
+  // bounds), and the keys at or past the count are dropped once it is.
+  const uint64_t coded_base = (uint64_t)kvh * a.cap;
+  const uint64_t l64 = (uint64_t)a.nf + (uint64_t)(sink ? 0u : z - 2u) * a.split;
+  const uint32_t slo = (uint32_t)min<uint64_t>(l64, (uint64_t)a.nf + a.cap);
+  const uint32_t shi = (uint32_t)min<uint64_t>(l64 + a.split, (uint64_t)a.nf + a.cap);
+  DecRegs cur{}, nxt{};
+  if (!sink && slo < shi) cur = dec_load(a, coded_base, slo, shi, t);
+  // The device-resident token count, if there is one, read by a vector load (the
+  // pointer is hidden from the uniformity analysis): scalar loads may complete in
+  // any order, so a wait for a later scalar would wait for this one too and hold
+  // the set-up loads below back by a round trip. The three tensor scales (every
+  // call passes all three) go out with it.
+  int64_t nk_raw = a.Nk;
+  if (a.nk_dev) {
+    uint64_t pv = (uint64_t)a.nk_dev;
+    asm volatile("" : "+v"(pv));
+    nk_raw = *(const __attribute__((address_space(1))) int64_t *)pv;
   }
+  const float qg = *a.qg, kg = *a.kg, vg = *a.vg;
 
   // Set-up loads in the order they are needed, so that each wait leaves the
-  // later ones in flight: the tables, this lane's Q codes, then (coded units)
-  // the codes of the first chunk, which arrive while the tables and Q are
-  // stored and decoded.
+  // later ones in flight (a coded unit's first chunk went first): the tables,
+  // then this lane's Q codes, stored and decoded while the codes arrive.
   f32x2 tb_r[2], tb_t[2];
   uint16_t tb_s[4];
 #pragma unroll
@@ -837,9 +841,6 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
     qw = *(const uint4 *)(a.qc + row * 64u + 16u * g);
     qsb = *(const uint16_t *)(a.qs + row * 8u + 2u * g);
   }
-  const uint64_t coded_base = (uint64_t)kvh * a.cap;
-  DecRegs cur{}, nxt{};
-  if (!sink && lo < hi) cur = dec_load(a, coded_base, lo, hi, t);
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -865,13 +866,36 @@ __global__ __launch_bounds__(64, 2) void attention_decode_kernel(AttnArgs a) {
     for (int s4 = 0; s4 < 4; ++s4) qf[s4] = __builtin_bit_cast(f16x8, to_bf16x8(qf[s4]));
   }
 
-  const float qg = *a.qg;
-  const float c2 = sink ? qg * a.tau_log2e : (qg * *a.kg) * a.tau_log2e;
-  const float unit = sink ? 1.0f : *a.vg;  // the factor the accumulator is counted in
+  const float c2 = sink ? qg * a.tau_log2e : (qg * kg) * a.tau_log2e;
+  const float unit = sink ? 1.0f : vg;  // the factor the accumulator is counted in
   f32x4 o[8];  // o[i][v]: output d = 16 i + 4 g + v of query qi
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{};
   float m = -INFINITY, l = 0.0f;
+
+  // keys present and this unit's range; a middle unit's [lo, hi) lies in
+  // [slo, shi), with lo = slo when it is not empty (the middle ends at nf + cap)
+  const uint32_t Nk = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)min<int64_t>(nk_raw, (int64_t)a.nf + a.cap + a.nl));
+  const uint32_t mid_hi = max(Nk > a.nl ? Nk - a.nl : 0u, a.nf);
+  uint32_t lo, hi;
+  if (z == 0u) {
+    lo = 0u;
+    hi = min(a.nf, Nk);
+  } else if (z == 1u) {
+    lo = max(mid_hi, a.nf);
+    hi = Nk;
+  } else {
+    lo = (uint32_t)min<uint64_t>(l64, mid_hi);
+    hi = (uint32_t)min<uint64_t>(l64 + a.split, mid_hi);
+  }
+  // the first chunk's keys past hi (loaded before hi was known) score -inf in the
+  // chunk loop; their V, which may hold any bits, is zeroed here
+  if (slo + (t >> 1) >= hi) {
+    cur.v0 = make_uint4(0u, 0u, 0u, 0u);
+    cur.v1 = make_uint4(0u, 0u, 0u, 0u);
+    cur.vs = 0u;
+  }
 
   // Scores Sᵀ of the chunk at c0: coded keys from loaded codes r, sink keys read
   // here (rows past hi read as zeros).
