@@ -678,7 +678,8 @@ def hadamard_profile(torch, nv, workloads, launches: int = 5):
 def decode_profile(torch, nv, workloads, split: int = 160, launches: int = 5):
     """Short run for rocprofv3: K and V sink caches of 128 + 32768 + 128 tokens
     ([1, 8, *, 128], workload-3 recipe, ScaleSearch [-2, 6]), one query per head for 32
-    query heads, then `launches` split-key cache attention calls (pieces of `split`)."""
+    query heads, then `launches` split-key cache attention calls (pieces of `split`,
+    the token count read from device memory)."""
     dev = torch.device("cuda:0")
     B, H, D, nf, nl, T = 1, 8, 128, 128, 128, 32768 + 256
     x = torch.from_numpy(workloads.workload(3, (B, H, T, D)).view(np.int16)) \
@@ -686,12 +687,15 @@ def decode_profile(torch, nv, workloads, split: int = 160, launches: int = 5):
     g = nv.global_scale(x[:, :, nf:T - nl].contiguous())
     kc = nv.kv_cache_alloc(B, H, D, T, nf, nl, torch.bfloat16, dev)
     vc = nv.kv_cache_alloc(B, H, D, T, nf, nl, torch.bfloat16, dev)
-    nv.kv_append(kc, x, g)
-    nv.kv_append(vc, x, g)
+    nv.kv_append_dev(kc, x, g)
+    nv.kv_append_dev(vc, x, g)
     q = nv.quantize(torch.from_numpy(workloads.workload(5, (1, 32, 1, 128)).view(np.int16))
                     .view(torch.bfloat16).to(dev))
+    # the token count read from device memory, as in a captured decode step
+    ws = torch.empty(nv.attention_split_workspace_bytes(B, 32, 1, T - nf - nl, split),
+                     dtype=torch.uint8, device=dev)
     for _ in range(launches):
-        nv.attention_kv_cache(q, kc, g, vc, g, split=split)
+        nv.attention_kv_cache(q, kc, g, vc, g, device_length=True, split=split, workspace=ws)
     torch.cuda.synchronize()
 
 
