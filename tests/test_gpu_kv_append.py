@@ -236,3 +236,42 @@ def test_graph_replayed_decode_step(gpu, split, paired):
         assert torch.equal(out, ref), f"replay {i}"
         _same_cache(kh, kd, t + 1 - nf - nl)
         _same_cache(vh, vd, t + 1 - nf - nl)
+
+
+@pytest.mark.parametrize("split,tokens", [(32, 137), (64, 150), (160, 389)])
+def test_split_device_length_ignores_rows_past_the_tokens(gpu, split, tokens):
+    """The split decode kernel with the token count in device memory loads a middle
+    unit's first chunk from the cache's capacity before the count arrives, so rows past
+    the tokens present are read and must drop out: here they hold 0xFF bytes (NaN block
+    scales, largest codes), and the result must equal, bit for bit, the host-length
+    call on caches whose unused rows were never written."""
+    B, H, D, nf, nl, cap = 1, 2, 128, 32, 32, 512
+    rng = np.random.default_rng(11)
+    kall = to_dev(workloads.workload(3, (B, H, tokens, D)))
+    vall = to_dev(workloads.to_bf16_bits(rng.standard_normal((B, H, tokens, D))
+                                         .astype(np.float32)))
+    q = gpu.quantize(to_dev(workloads.to_bf16_bits(
+        rng.standard_normal((B, 2 * H, 1, D)).astype(np.float32))))
+    kg = gpu.global_scale(kall)
+    vg = gpu.global_scale(vall)
+    kd, vd = (gpu.kv_cache_alloc(B, H, D, cap, nf, nl) for _ in range(2))
+    kh, vh = (gpu.kv_cache_alloc(B, H, D, cap, nf, nl) for _ in range(2))
+    for c in (kd, vd):
+        c["codes"].fill_(0xFF)
+        c["scales"].fill_(0xFF)
+    for c in (kh, vh):
+        c["codes"].zero_()
+        c["scales"].zero_()
+    gpu.kv_append_dev(kd, kall, kg)
+    gpu.kv_append_dev(vd, vall, vg)
+    gpu.kv_append(kh, kall, kg)
+    gpu.kv_append(vh, vall, vg)
+    nws = gpu.attention_split_workspace_bytes(B, 2 * H, 1, cap - nf - nl, split)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    print(f"[case] split {split}, {tokens} tokens in a cache of {cap}", flush=True)
+    out = gpu.attention_kv_cache(q, kd, kg, vd, vg, device_length=True, split=split,
+                                 workspace=ws).clone()
+    ref = gpu.attention_kv_cache(q, kh, kg, vh, vg, split=split, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert torch.equal(out, ref)
