@@ -258,6 +258,31 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f16x8 h) {
   return r;
 }
 
+// Reductions over the lanes l, l ^ 32 (and l ^ 16) with the gfx950 permlane
+// swaps, which exchange rows of lanes in the VALU (a lane shuffle would take an
+// LDS round trip): after a swap of v with itself the two results hold the value
+// of each lane and of its partner, the same pair on both lanes.
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Online softmax of one 32-key tile held as an Sᵀ accumulator (sacc[v] = key
 // 8 (v >> 2) + 4 g + (v & 3) of the tile; this lane's query; base-2 scores
 // s = acc * c2, c2 > 0, so the max is taken on acc), then P to NVFP4 per 16
@@ -273,7 +298,7 @@ __device__ __forceinline__ float softmax_code_tile(const f32x16 &sacc, float c2,
   float mt = -INFINITY;
 #pragma unroll
   for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+  mt = pair_max32(mt) * c2;
   const float mn = fmaxf(m, mt);
   // with every score -inf so far, the exponent base 0 gives p = 0 and
   // alpha = 0 on an accumulator and sum that are still 0
@@ -292,7 +317,7 @@ __device__ __forceinline__ float softmax_code_tile(const f32x16 &sacc, float c2,
     float am = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) am = fmaxf(am, p[8 * blk + e]);
-    am = fmaxf(am, __shfl_xor(am, 32));
+    am = pair_max32(am);
     // a one-multiply estimate of the pattern E4M3(fl(fl(am / 6) / S_P)), never
     // more than one pattern off, corrected against the thresholds
     uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
@@ -535,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     run_segment(std::false_type{}, 0u, kend, false);
   }
 
-  l = l + __shfl_xor(l, 32);
+  l = pair_sum32(l);
   if (!qvalid) return;
   const uint64_t row = (uint64_t)bh * rows + qi;
   const float f = l > 0.0f ? (SP * unit) / l : 0.0f;
@@ -701,31 +726,6 @@ __device__ __forceinline__ void sink_store_v(const SinkRegs &r, uint32_t t, _Flo
     for (int e = 0; e < 8; ++e)
       vt[dec_vt_index(d0 + 8u * i + e, key)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
   }
-}
-
-// Reductions over the lanes l, l ^ 32 (and l ^ 16) with the gfx950 permlane
-// swaps, which exchange rows of lanes in the VALU (a lane shuffle would take an
-// LDS round trip): after a swap of v with itself the two results hold the value
-// of each lane and of its partner, the same pair on both lanes.
-__device__ __forceinline__ float pair_max32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_max16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float pair_sum16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Online softmax and P coding of one 32-key tile in the 16 x 16 layout of the
