@@ -48,7 +48,13 @@ constexpr uint32_t kQueriesPerGroup = 32 * kAttnWaves;
 constexpr uint32_t kKsStride = kAttnD + 8;     // fp16 per K row in LDS (16-byte pad)
 constexpr uint32_t kVtStride = kChunk + 4;     // fp16 per V^T row in LDS (34 dwords)
 
-__device__ __forceinline__ float scale_value(uint32_t p) { return p >= 127u ? NAN : e4m3_value(p); }
+// UE4M3 scale byte -> value, NaN for bytes 127..255. Below 127 the byte is an
+// OCP E4M3 bit pattern with the sign clear, so gfx950's FP8 convert gives its
+// value exactly (checked on the device against 2^(e-7)(1 + m/8) and m 2^-9 for
+// every byte).
+__device__ __forceinline__ float scale_value(uint32_t p) {
+  return p >= 127u ? NAN : __builtin_amdgcn_cvt_f32_fp8((int)p, 0);
+}
 
 // P's scale tables under S_P = fl(1/2688), evaluated by the compiler in IEEE
 // binary32 (round to nearest even: the rounding of the device's own float
