@@ -48,10 +48,9 @@ constexpr uint32_t kQueriesPerGroup = 32 * kAttnWaves;
 constexpr uint32_t kKsStride = kAttnD + 8;     // fp16 per K row in LDS (16-byte pad)
 constexpr uint32_t kVtStride = kChunk + 4;     // fp16 per V^T row in LDS (34 dwords)
 
-// UE4M3 scale byte -> value, NaN for bytes 127..255. Below 127 the byte is an
-// OCP E4M3 bit pattern with the sign clear, so gfx950's FP8 convert gives its
-// value exactly (checked on the device against 2^(e-7)(1 + m/8) and m 2^-9 for
-// every byte).
+// UE4M3 scale byte -> value, NaN for bytes 127..255. Below 127 the byte is also
+// an OCP E4M3 bit pattern with the sign clear, and that format gives it the same
+// value, 2^(e-7)(1 + m/8), or m 2^-9 at e = 0: gfx950's FP8 convert returns it.
 __device__ __forceinline__ float scale_value(uint32_t p) {
   return p >= 127u ? NAN : __builtin_amdgcn_cvt_f32_fp8((int)p, 0);
 }
