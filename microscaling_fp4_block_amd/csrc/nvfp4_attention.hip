@@ -288,6 +288,14 @@ __device__ __forceinline__ float pair_sum16(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The one-multiply estimate E4M3(fl(a * 448)) of a P block's pattern (a <= 1):
+// gfx950's FP32 -> FP8 (E4M3) convert rounds to nearest even exactly as the
+// UE4M3 rounding does on [0, 448] (compared on the device for every binary32 of
+// that range), in one instruction.
+__device__ __forceinline__ uint32_t p_pattern_estimate(float am) {
+  return min((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(am * 448.0f, 0.0f, 0, false) & 0xFFu, 126u);
+}
+
 // Online softmax of one 32-key tile held as an Sᵀ accumulator (sacc[v] = key
 // 8 (v >> 2) + 4 g + (v & 3) of the tile; this lane's query; base-2 scores
 // s = acc * c2, c2 > 0, so the max is taken on acc), then P to NVFP4 per 16
@@ -325,7 +333,7 @@ __device__ __forceinline__ float softmax_code_tile(const f32x16 &sacc, float c2,
     am = pair_max32(am);
     // a one-multiply estimate of the pattern E4M3(fl(fl(am / 6) / S_P)), never
     // more than one pattern off, corrected against the thresholds
-    uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
+    uint32_t pat = p_pattern_estimate(am);
     const f32x2 th = pthr2[pat];
     pat = am >= th.y ? pat + 1u : (am < th.x ? pat - 1u : pat);
     const f32x2 rs = ptbl[pat];
@@ -765,7 +773,7 @@ __device__ __forceinline__ float softmax_code_tile16(const f32x4 &s0, const f32x
   for (int blk = 0; blk < 2; ++blk) {
     const float am = pair_max32(pair_max16(
         fmaxf(fmaxf(p[4 * blk], p[4 * blk + 1]), fmaxf(p[4 * blk + 2], p[4 * blk + 3]))));
-    uint32_t pat = min(e4m3_rne_sat(am * 448.0f), 126u);
+    uint32_t pat = p_pattern_estimate(am);
     const f32x2 th = pthr2[pat];
     pat = am >= th.y ? pat + 1u : (am < th.x ? pat - 1u : pat);
     const f32x2 rs = ptbl[pat];
