@@ -90,6 +90,17 @@ NVFP4_API const char *nvfp4_status_str(nvfp4_status s);
 /* NVFP4_ABI_VERSION of the built library. */
 NVFP4_API int nvfp4_abi_version(void);
 
+/* Checks, on the current device, two properties of gfx950's converters that the
+ * attention kernels rely on; blocking (runs on the null stream, allocates 16 bytes
+ * of device memory for the call). counts (host int64[2]) receives: [0] the
+ * binary32 values t in [0, 448] whose hardware FP32 -> FP8 (E4M3) convert differs
+ * from the nearest-even UE4M3 rounding (their P block-pattern estimate); [1] the
+ * bytes 0..126 whose hardware FP8 -> FP32 convert differs from their UE4M3 value
+ * (their block-scale decode; the pages' block scales are UE4M3, which for these
+ * bytes coincides with OCP E4M3). Both are 0 on a conforming device.
+ * NVFP4_EINVAL for a null counts, NVFP4_EHIP for a runtime error. */
+NVFP4_API nvfp4_status nvfp4_hw_self_check(int64_t *counts);
+
 /* Bytes of device workspace the quantize calls need for a rows x cols region
  * (it holds the per-workgroup partial maxima of the global amax pass). */
 NVFP4_API size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags);

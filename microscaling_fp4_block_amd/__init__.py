@@ -14,6 +14,7 @@ from .nvfp4 import (  # noqa: F401
     dequantize_kv_sink,
     global_scale,
     hadamard128,
+    hw_self_check,
     kv_append,
     kv_append_dev,
     kv_append2_dev,

@@ -50,7 +50,8 @@ constexpr uint32_t kVtStride = kChunk + 4;     // fp16 per V^T row in LDS (34 dw
 
 // UE4M3 scale byte -> value, NaN for bytes 127..255. Below 127 the byte is also
 // an OCP E4M3 bit pattern with the sign clear, and that format gives it the same
-// value, 2^(e-7)(1 + m/8), or m 2^-9 at e = 0: gfx950's FP8 convert returns it.
+// value, 2^(e-7)(1 + m/8), or m 2^-9 at e = 0: gfx950's FP8 convert returns it
+// (nvfp4_hw_self_check compares every such byte on the device).
 __device__ __forceinline__ float scale_value(uint32_t p) {
   return p >= 127u ? NAN : __builtin_amdgcn_cvt_f32_fp8((int)p, 0);
 }
@@ -290,8 +291,8 @@ __device__ __forceinline__ float pair_sum16(float v) {
 
 // The one-multiply estimate E4M3(fl(a * 448)) of a P block's pattern (a <= 1):
 // gfx950's FP32 -> FP8 (E4M3) convert rounds to nearest even exactly as the
-// UE4M3 rounding does on [0, 448] (compared on the device for every binary32 of
-// that range), in one instruction.
+// UE4M3 rounding does on [0, 448] (nvfp4_hw_self_check compares every binary32
+// of that range on the device), in one instruction.
 __device__ __forceinline__ uint32_t p_pattern_estimate(float am) {
   return min((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(am * 448.0f, 0.0f, 0, false) & 0xFFu, 126u);
 }

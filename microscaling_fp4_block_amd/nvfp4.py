@@ -27,6 +27,7 @@ _vp, _sz = ctypes.c_void_p, ctypes.c_size_t
 SIGNATURES = {
     "nvfp4_status_str": ([_i32], ctypes.c_char_p),
     "nvfp4_abi_version": ([], _i32),
+    "nvfp4_hw_self_check": ([_vp], _i32),
     "nvfp4_workspace_bytes": ([_i64, _i64, _u32], _sz),
     "nvfp4_quantize": ([_vp, _i32, _i64, _i64, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp, _sz,
                         _vp], _i32),
@@ -167,6 +168,15 @@ def _workspace(ws, nbytes: int, dev):
 
 def workspace_bytes(rows: int, cols: int, flags: int = 0) -> int:
     return int(load().nvfp4_workspace_bytes(rows, cols, flags))
+
+
+def hw_self_check() -> tuple:
+    """nvfp4_hw_self_check on the current device: (values in [0, 448] whose hardware
+    FP32 -> FP8 convert differs from the UE4M3 nearest-even rounding, scale bytes
+    0..126 whose hardware FP8 -> FP32 convert differs from their UE4M3 value)."""
+    counts = (ctypes.c_int64 * 2)()
+    _check("nvfp4_hw_self_check", load().nvfp4_hw_self_check(ctypes.addressof(counts)))
+    return int(counts[0]), int(counts[1])
 
 
 def _signs(signs):

@@ -58,6 +58,7 @@ def test_version_and_status_text(lib):
     assert len(texts) == 6
     assert lib.nvfp4_status_str(99).decode() == "unknown status"
     assert lib.nvfp4_workspace_bytes(8192, 28672, 0) >= 4 * 256
+    assert lib.nvfp4_hw_self_check(None) == 1  # a null counts array: refused before any HIP call
 
 
 P = 0x10000  # a well-aligned fake device address: every call below fails its checks first
