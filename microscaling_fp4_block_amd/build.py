@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["nvfp4_kernels.hip", "nvfp4_attention.hip", "nvfp4_api.hip"]
+SOURCES = ["nvfp4_kernels.hip", "nvfp4_attention.hip", "nvfp4_api.hip", "nvfp4_selfcheck.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

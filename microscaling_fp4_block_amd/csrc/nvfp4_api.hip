@@ -151,21 +151,6 @@ const char *nvfp4_status_str(nvfp4_status s) {
 
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
 
-nvfp4_status nvfp4_hw_self_check(int64_t *counts) {
-  if (!counts) return NVFP4_EINVAL;
-  unsigned long long *d = nullptr;
-  if (hipMalloc(&d, 2 * sizeof(unsigned long long)) != hipSuccess) return NVFP4_EHIP;
-  unsigned long long h[2] = {0, 0};
-  hipError_t e = hipMemset(d, 0, sizeof(h));
-  if (e == hipSuccess) e = launch_hw_check(d, nullptr);
-  if (e == hipSuccess) e = hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
-  (void)hipFree(d);
-  if (e != hipSuccess) return NVFP4_EHIP;
-  counts[0] = (int64_t)h[0];
-  counts[1] = (int64_t)h[1];
-  return NVFP4_OK;
-}
-
 size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags) {
   (void)rows;
   (void)cols;

@@ -157,7 +157,6 @@ struct DequantKvArgs {
 
 // Launchers (nvfp4_kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_amax(const AmaxArgs &a, bool bf16, int groups, hipStream_t s);
-hipError_t launch_hw_check(unsigned long long *counts, hipStream_t s);
 hipError_t launch_finalize(const uint32_t *partials, int n, float *gscale, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s);
 int amax_hadamard_groups(uint32_t nblocks);

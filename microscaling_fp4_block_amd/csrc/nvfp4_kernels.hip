@@ -1693,36 +1693,6 @@ __global__ __launch_bounds__(kThreads) void dequantize_kv_kernel(DequantKvArgs a
 }
 
 // ---------------------------------------------------------------------------
-// Self-check of the converter facts the kernels rely on, run on the device at
-// hand: counts[0] the binary32 values t in [0, 448] whose FP32 -> FP8 (E4M3)
-// convert differs from the UE4M3 nearest-even rounding e4m3_rne_sat (the
-// attention's P pattern estimate); counts[1] the bytes 0..126 whose FP8 ->
-// FP32 convert differs from the UE4M3 value e4m3_value (the attention's block
-// scales). Every lane walks a strided range of bit patterns; counts are added
-// with vector atomics.
-// ---------------------------------------------------------------------------
-constexpr uint32_t kCheckLast = 0x43E00000u;  // 448.0f
-
-__global__ __launch_bounds__(kThreads) void hw_check_kernel(unsigned long long *counts) {
-  const uint32_t stride = gridDim.x * kThreads;
-  unsigned long long bad = 0;
-  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b <= kCheckLast; b += stride) {
-    const float t = __uint_as_float(b);
-    const uint32_t hw = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false) & 0xFFu;
-    bad += hw != e4m3_rne_sat(t);
-  }
-  if (bad) atomicAdd(&counts[0], bad);
-  const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
-  if (g < 127u && __builtin_amdgcn_cvt_f32_fp8((int)g, 0) != e4m3_value(g))
-    atomicAdd(&counts[1], 1ull);
-}
-
-hipError_t launch_hw_check(unsigned long long *counts, hipStream_t s) {
-  hipLaunchKernelGGL(hw_check_kernel, dim3(1024), dim3(kThreads), 0, s, counts);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // MXFP4 contrast format (power-of-two block scaling, set against NVFP4 on
 // "NVIDIAのFP4推論が50倍の効率を実現", 超低精度推論を支えるアーキテクチャ). Read as
 // the OCP Microscaling format: 32 elements share one E8M0 byte b = X + 127
