@@ -209,6 +209,18 @@ def test_attention_kv_cache_argument_checks(lib):
         assert f(*bad, 1, 1, 2, 1, 8, 300, 128, 16, 16, 300, P, 0, None) == 3
 
 
+def test_largest_accepted_tensor(lib):
+    """2^29 blocks of 16 (bf16 or FP32 [524288, 16384]) pass the shape checks: the
+    call stops only at the too-small workspace, before any launch. One more row,
+    or the same element count in rows of 16 (2^33 rows), is refused as a shape."""
+    for xdt in (0, 1):
+        assert q(lib, xdt=xdt, rows=524288, cols=16384, wsb=16) == 4
+        assert q(lib, xdt=xdt, rows=524289, cols=16384, wsb=16) == 2
+        assert q(lib, xdt=xdt, rows=1 << 29, cols=16, wsb=16) == 4
+        assert q(lib, xdt=xdt, rows=(1 << 29) + 1, cols=16, wsb=16) == 2
+    assert q(lib, rows=524288, cols=16384, wsb=16, flags=1) == 4  # Hadamard: same limit
+
+
 def test_huge_dimensions_are_refused_without_overflow(lib):
     """Dimensions whose products or sums would overflow 64 bits are refused as shapes
     (the checks bound each factor before multiplying)."""

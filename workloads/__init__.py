@@ -29,7 +29,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "to_bf16_bits", "bf16_bits_to_f32", "workload", "WORKLOADS",
+    "to_bf16_bits", "bf16_bits_to_f32", "workload", "WORKLOADS", "device_gaussian_planted",
 ]
 
 
@@ -89,6 +89,21 @@ def q_sparse_outliers(shape, seed: int) -> np.ndarray:
     mask = rng.random(shape) < 0.001
     x[mask] *= 30.0
     return to_bf16_bits(x.astype(np.float32))
+
+
+def device_gaussian_planted(rows: int, cols: int, seed: int, dtype, device, peak: float = 8.0):
+    """A tensor too large to draw on the host: N(0, 1) drawn on the device by torch's
+    seeded generator directly in ``dtype`` (torch.bfloat16 or torch.float32), clamped
+    to [-peak/2, peak/2], with element [rows - 1, 5] set to ``peak``, so that the
+    tensor's largest magnitude is ``peak`` by construction. Returns the device tensor."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(rows, cols, generator=g, dtype=dtype, device=device)
+    x.clamp_(-peak / 2, peak / 2)
+    x[rows - 1, 5] = peak
+    return x
 
 
 # name -> (generator, full shape, seed, description of the mode)
