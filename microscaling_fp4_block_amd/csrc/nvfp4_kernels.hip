@@ -1344,13 +1344,21 @@ __global__ __launch_bounds__(kThreads) void amax_hadamard_kernel(AmaxArgs a) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t nwaves = gridDim.x * (kThreads / 64);
   uint32_t m = 0;
-  for (uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile * 32u < nvec;
-       tile += nwaves) {
+  // The next tile's 32 vectors are loaded while this tile is transformed, so each
+  // wave keeps one tile's loads in flight through its whole loop.
+  auto load_tile = [&](uint32_t tile, uint4 (&b)[8]) {
     const uint32_t vec = tile * 32u + (lane & 31u);
     const bool valid = vec < nvec;
-    uint4 b[8];
     hadamard_load<SIGNS>((const uint16_t *)a.x, valid ? block_offset(a.map, vec * 8u) : 0, valid,
                          h.g, a.hs, b);
+  };
+  uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  uint4 b[8];
+  if (tile * 32u < nvec) load_tile(tile, b);
+  for (; tile * 32u < nvec; tile += nwaves) {
+    uint4 bn[8];
+    const uint32_t next = tile + nwaves;
+    if (next * 32u < nvec) load_tile(next, bn);
 #pragma unroll 1
     for (uint32_t t = 0; t < 4; ++t) {
       float y[16];
@@ -1358,6 +1366,8 @@ __global__ __launch_bounds__(kThreads) void amax_hadamard_kernel(AmaxArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) m = max(m, __float_as_uint(y[v]) & 0x7FFFFFFFu);
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) b[ks] = bn[ks];
   }
   m = group_max_u32(m);
   if (threadIdx.x == 0) a.partials[blockIdx.x] = m;
