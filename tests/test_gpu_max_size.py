@@ -2,7 +2,9 @@
 
 bf16 [524288, 16384] (17.2 GB) and FP32 of the same shape (34.4 GB), so that the
 kernels' 32-bit block and 16-byte-chunk indices reach the top of their range
-(2^29 blocks; 2^31 chunks for the FP32 input and output). The input is drawn on
+(2^29 blocks; 2^31 chunks for the FP32 input and output), and the attention-sink
+mode on a bf16 KV tensor [1, 8, 2^23, 128] of the same size, whose row map divides
+block indices by the blocks per row and the middle tokens per head. The input is drawn on
 the device (8.6 G values are too many to draw on the host in a test) by the
 seeded generator of the workloads module, with its largest magnitude planted in
 the last row, so the oracle, given sampled rows that include that row, derives
@@ -82,3 +84,45 @@ def test_hadamard_quantize_at_the_limit(gpu, orc):
     rc, rs, _ = orc.quantize(t, -8, 8, gscale=np.float32(0.004))
     assert np.array_equal(ss, rs), "scales: " + first_mismatch(ss, rs)
     assert np.array_equal(cs, rc), "codes: " + first_mismatch(cs, rc)
+
+
+def test_sink_mode_at_the_limit(gpu, orc):
+    """Sink mode (128 + 128 tokens kept) on bf16 [1, 8, 8388608, 128], 2^29 blocks, the
+    largest magnitude planted in the last middle token of the last head (the amax is
+    taken over the middle tokens only). Sampled middle tokens of three heads against
+    the oracle quantizer on those tokens; the kept tokens against the input; the
+    reassembled dequantize (bf16) on the same tokens."""
+    H, T, D, nf, nl = 8, 1 << 23, 128, 128, 128
+    print(f"[case] sink mode at the limit [1, {H}, {T}, {D}]", flush=True)
+    planted = (H - 1) * T + (T - nl - 1)
+    kv = workloads.device_gaussian_planted(H * T, D, 16, torch.bfloat16, "cuda:0",
+                                           row=planted).view(1, H, T, D)
+    rng = np.random.default_rng(17)
+    toks = np.unique(np.concatenate([[nf, nf + 1, T // 2, T - nl - 2, T - nl - 1],
+                                     rng.integers(nf, T - nl, size=11)]))
+    heads = [0, 3, H - 1]
+    try:
+        c, s, g, sink = gpu.quantize_kv_sink(kv, nf, nl, (-2, 6))
+        y = gpu.dequantize_kv_sink(c, s, g, sink, T, nf, nl, torch.bfloat16)
+        ti = torch.from_numpy(toks.astype(np.int64)).to(kv.device)
+        ki = torch.from_numpy(np.concatenate([np.arange(nf), np.arange(T - nl, T)])).to(kv.device)
+        xs = np.stack([to_host(kv[0, h].index_select(0, ti)) for h in heads])
+        cs = np.stack([to_host(c[0, h].index_select(0, ti - nf)) for h in heads])
+        ss = np.stack([to_host(s[0, h].index_select(0, ti - nf)) for h in heads])
+        ys = np.stack([to_host(y[0, h].index_select(0, ti)) for h in heads])
+        kept_in = np.stack([to_host(kv[0, h].index_select(0, ki)) for h in heads])
+        kept_out = np.stack([to_host(sink[0, h]) for h in heads])
+        kept_y = np.stack([to_host(y[0, h].index_select(0, ki)) for h in heads])
+        gg = np.float32(to_host(g)[0])
+        del c, s, sink, y
+    finally:
+        del kv
+        _free()
+    rc, rs, rg = orc.quantize(xs.reshape(-1, D), -2, 6)
+    assert rg == np.float32(np.float32(8.0) / np.float32(2688.0))
+    assert f"{gg!r}" == f"{rg!r}", (gg, rg)
+    assert np.array_equal(ss.reshape(-1, D // 16), rs), "scales: " + first_mismatch(ss.reshape(-1, D // 16), rs)
+    assert np.array_equal(cs.reshape(-1, D // 2), rc), "codes: " + first_mismatch(cs.reshape(-1, D // 2), rc)
+    assert_same_floats(ys.reshape(-1, D), orc.dequantize(rc, rs, rg, "bf16"))
+    assert np.array_equal(kept_out, kept_in)
+    assert np.array_equal(kept_y, kept_in)

@@ -91,18 +91,20 @@ def q_sparse_outliers(shape, seed: int) -> np.ndarray:
     return to_bf16_bits(x.astype(np.float32))
 
 
-def device_gaussian_planted(rows: int, cols: int, seed: int, dtype, device, peak: float = 8.0):
+def device_gaussian_planted(rows: int, cols: int, seed: int, dtype, device, peak: float = 8.0,
+                            row: int | None = None):
     """A tensor too large to draw on the host: N(0, 1) drawn on the device by torch's
     seeded generator directly in ``dtype`` (torch.bfloat16 or torch.float32), clamped
-    to [-peak/2, peak/2], with element [rows - 1, 5] set to ``peak``, so that the
-    tensor's largest magnitude is ``peak`` by construction. Returns the device tensor."""
+    to [-peak/2, peak/2], with element [row, 5] (default: the last row) set to
+    ``peak``, so that the tensor's largest magnitude is ``peak`` by construction.
+    Returns the device tensor."""
     import torch
 
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     x = torch.randn(rows, cols, generator=g, dtype=dtype, device=device)
     x.clamp_(-peak / 2, peak / 2)
-    x[rows - 1, 5] = peak
+    x[rows - 1 if row is None else row, 5] = peak
     return x
 
 
