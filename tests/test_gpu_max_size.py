@@ -4,7 +4,8 @@ bf16 [524288, 16384] (17.2 GB) and FP32 of the same shape (34.4 GB), so that the
 kernels' 32-bit block and 16-byte-chunk indices reach the top of their range
 (2^29 blocks; 2^31 chunks for the FP32 input and output), and the attention-sink
 mode on a bf16 KV tensor [1, 8, 2^23, 128] of the same size, whose row map divides
-block indices by the blocks per row and the middle tokens per head. The input is drawn on
+block indices by the blocks per row and the middle tokens per head; and MXFP4 (2^28
+blocks of 32) on the bf16 tensor. The input is drawn on
 the device (8.6 G values are too many to draw on the host in a test) by the
 seeded generator of the workloads module, with its largest magnitude planted in
 the last row, so the oracle, given sampled rows that include that row, derives
@@ -126,3 +127,26 @@ def test_sink_mode_at_the_limit(gpu, orc):
     assert_same_floats(ys.reshape(-1, D), orc.dequantize(rc, rs, rg, "bf16"))
     assert np.array_equal(kept_out, kept_in)
     assert np.array_equal(kept_y, kept_in)
+
+
+@pytest.mark.parametrize("offsets", [(0, 0), (-1, 1)], ids=["rule", "search"])
+def test_mxfp4_at_the_limit(gpu, orc, offsets):
+    """MXFP4 on bf16 [524288, 16384] (2^28 blocks of 32: the rule kernel's four lanes a
+    block and the FP32 dequantize's 2^31 chunks at the top of their range); sampled rows
+    against the oracle, codes, scales and the FP32 dequantize."""
+    x = _max_tensor(torch.bfloat16, 18)
+    try:
+        c, s = gpu.mxfp4_quantize(x, offsets)
+        y = gpu.mxfp4_dequantize(c, s, torch.float32)
+        idx = _sample_rows(19).to(x.device)
+        xs = to_host(x.index_select(0, idx))
+        cs, ss = to_host(c.index_select(0, idx)), to_host(s.index_select(0, idx))
+        ys = to_host(y.index_select(0, idx))
+        del c, s, y
+    finally:
+        del x
+        _free()
+    rc, rs = orc.quantize_mxfp4(xs, *offsets)
+    assert np.array_equal(ss, rs), "scales: " + first_mismatch(ss, rs)
+    assert np.array_equal(cs, rc), "codes: " + first_mismatch(cs, rc)
+    assert_same_floats(ys, orc.dequantize_mxfp4(rc, rs, "f32"))
