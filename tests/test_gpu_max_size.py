@@ -4,8 +4,9 @@ bf16 [524288, 16384] (17.2 GB) and FP32 of the same shape (34.4 GB), so that the
 kernels' 32-bit block and 16-byte-chunk indices reach the top of their range
 (2^29 blocks; 2^31 chunks for the FP32 input and output), and the attention-sink
 mode on a bf16 KV tensor [1, 8, 2^23, 128] of the same size, whose row map divides
-block indices by the blocks per row and the middle tokens per head; and MXFP4 (2^28
-blocks of 32) on the bf16 tensor. The input is drawn on
+block indices by the blocks per row and the middle tokens per head; MXFP4 (2^28
+blocks of 32) on the bf16 tensor; and a decode append into the last row of a KV
+cache of 2^23 tokens per head (8 heads), the most the ABI accepts. The input is drawn on
 the device (8.6 G values are too many to draw on the host in a test) by the
 seeded generator of the workloads module, with its largest magnitude planted in
 the last row, so the oracle, given sampled rows that include that row, derives
@@ -18,7 +19,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import assert_same_floats, first_mismatch, to_host
+from gpu_util import assert_same_floats, first_mismatch, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -150,3 +151,43 @@ def test_mxfp4_at_the_limit(gpu, orc, offsets):
     assert np.array_equal(ss, rs), "scales: " + first_mismatch(ss, rs)
     assert np.array_equal(cs, rc), "codes: " + first_mismatch(cs, rc)
     assert_same_floats(ys, orc.dequantize_mxfp4(rc, rs, "f32"))
+
+
+def test_append_into_the_last_row_of_the_largest_cache(gpu, orc):
+    """A one-token append at the device-held length 2^23 - 1 of a cache holding 2^23
+    tokens per head (8 heads, 128 + 128 kept): the token leaving the recent window (ring
+    slot 127) is coded into the last middle row (2^23 - 257) under the given tensor
+    scale, the new token takes its ring slot, the length reaches the capacity, and a
+    further append changes nothing."""
+    H, D, nf, nl, capacity = 8, 128, 128, 128, 1 << 23
+    print(f"[case] append at the end of a {capacity}-token cache, {H} heads", flush=True)
+    cache = gpu.kv_cache_alloc(1, H, D, capacity, nf, nl)
+    try:
+        ring = workloads.workload(3, (1, H, nl, D))
+        new = workloads.workload(4, (1, H, 1, D))
+        cache["tail"].copy_(to_dev(ring))
+        cache["length_dev"].fill_(capacity - 1)
+        gs = torch.tensor([0.01], dtype=torch.float32, device="cuda:0")
+        k_new = to_dev(new)
+        gpu.kv_append_dev(cache, k_new, gs)
+        length = gpu.kv_length(cache)
+        last = cache["codes"].shape[2] - 1
+        cs = to_host(cache["codes"][0, :, last])
+        ss = to_host(cache["scales"][0, :, last])
+        tail = to_host(cache["tail"])
+        gpu.kv_append_dev(cache, k_new, gs)  # the cache is full: a no-op
+        length2 = gpu.kv_length(cache)
+        cs2, ss2 = to_host(cache["codes"][0, :, last]), to_host(cache["scales"][0, :, last])
+        tail2 = to_host(cache["tail"])
+    finally:
+        del cache
+        _free()
+    assert last == capacity - nf - nl - 1
+    rc, rs, _ = orc.quantize(ring[0, :, nl - 1], -2, 6, gscale=np.float32(0.01))
+    assert np.array_equal(ss, rs), "scales: " + first_mismatch(ss, rs)
+    assert np.array_equal(cs, rc), "codes: " + first_mismatch(cs, rc)
+    want_tail = ring.copy()
+    want_tail[0, :, nl - 1] = new[0, :, 0]
+    assert np.array_equal(tail, want_tail)
+    assert length == capacity and length2 == capacity
+    assert np.array_equal(cs2, cs) and np.array_equal(ss2, ss) and np.array_equal(tail2, tail)
