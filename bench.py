@@ -802,7 +802,7 @@ def main():
         rocpd_summary(args.rocpd_summary)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the quantizer has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
