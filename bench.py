@@ -322,7 +322,8 @@ def rocpd_summary(dbs):
 
 def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
     """Markdown table of every workload, passes timed with HIP events: per-call GPU time
-    of calls captured in a HIP graph (host out of the loop), the eager call rate, the
+    of calls captured in a HIP graph (host out of the loop), the eager call rate (with
+    the binding allocating the outputs and workspace per call, and with them passed), the
     search pass's per-launch p50 with p10 and p90, and its p50 with the Infinity Cache
     flushed before every launch; the oracle beside."""
     import oracle
@@ -332,7 +333,7 @@ def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     flush = CacheFlush(torch, dev)
-    print("| # | workload | quantize call GB/s (eager; graph) | search pass us, graph (GB/s) | "
+    print("| # | workload | quantize call GB/s (eager; eager, outputs and workspace passed; graph) | search pass us, graph (GB/s) | "
           "search pass us per launch: p50 [p10, p90] warm; p50 cold | amax pass us | "
           "max-scaling control us | SS / control | dequantize us (GB/s) | oracle quantize s "
           f"({threads} threads) |")
@@ -355,6 +356,7 @@ def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
             ns = B * H * (nf + nl) * D
             call = lambda: nv.quantize_kv_sink(x, nf, nl, offs, hadamard=had)
             c, s, g, snk = call()
+            call_pre = None  # the sink call allocates its outputs
             gfix = g.clone()
             search = lambda: nv.quantize_kv_sink(x, nf, nl, offs, hadamard=had, global_scale=gfix)
             control = lambda: nv.quantize_kv_sink(x, nf, nl, (0, 0), hadamard=had,
@@ -370,6 +372,10 @@ def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
             call = lambda: nv.quantize(x, offs, hadamard=had)
             c, s, g = call()
             gfix = g.clone()
+            wsp = torch.empty(nv.workspace_bytes(n // x.shape[-1], x.shape[-1]),
+                              dtype=torch.uint8, device=dev)
+            outp = (torch.empty_like(c), torch.empty_like(s), torch.empty_like(g))
+            call_pre = lambda: nv.quantize(x, offs, hadamard=had, workspace=wsp, out=outp)
             search = lambda: nv.quantize(x, offs, hadamard=had, global_scale=gfix)
             control = lambda: nv.quantize(x, (0, 0), hadamard=had, global_scale=gfix)
             amax = lambda: nv.global_scale(x, hadamard=had)
@@ -386,6 +392,8 @@ def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
               for k, f in (("call", call), ("search", search), ("amax", amax),
                            ("control", control), ("deq", deq))}
         ms["call_eager"] = event_time_ms(torch, call, iters, stream)
+        if call_pre is not None:
+            ms["call_eager_pre"] = event_time_ms(torch, call_pre, iters, stream)
         warm = percentiles(launch_times_ms(torch, search, iters, stream))
         cold = percentiles(launch_times_ms(torch, search, 30, stream, between=flush))
         t1 = time.perf_counter()
@@ -395,7 +403,8 @@ def workloads_table(torch, nv, workloads, iters: int = 50, warm_s: float = 0.1):
             oracle.quantize(xh, *offs, hadamard=had, nthreads=threads)
         t_or = time.perf_counter() - t1
         gbs = lambda b, m: b / (m * 1e-3) / 1e9
-        print(f"| {idx} | {w['name']} | {gbs(qbytes, ms['call_eager']):.0f}; "
+        pre = f"{gbs(qbytes, ms['call_eager_pre']):.0f}" if call_pre is not None else "-"
+        print(f"| {idx} | {w['name']} | {gbs(qbytes, ms['call_eager']):.0f}; {pre}; "
               f"{gbs(qbytes, ms['call']):.0f} | "
               f"{ms['search'] * 1e3:.1f} ({gbs(qbytes, ms['search']):.0f}) | "
               f"{warm[1] * 1e3:.1f} [{warm[0] * 1e3:.1f}, {warm[2] * 1e3:.1f}]; "
