@@ -2055,12 +2055,17 @@ static hipError_t launch_quantize_balanced(const QuantArgs &a, bool bf16, int g,
   return hipGetLastError();
 }
 
+// Grid cap of the max-scaling rule kernels (NVFP4 and MXFP4): on the 8192 x 28672
+// bf16 tensor 2048 workgroups beat 8192 by 4% (106.1 -> 102.1 us; MXFP4 102.1 -> 98.1 us),
+// while 1024 and 512 lose (121.6 and 195.7 us).
+constexpr int kRuleGroups = 2048;
+
 hipError_t launch_quantize(const QuantArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.map.nblocks, kMaxQuantGroups);
   const int gc = grid_for(a.map.nblocks, kMaxCertGroups);
   if (a.bal.e) return launch_quantize_balanced(a, bf16, g, s);
   if (a.f_lo == 0 && a.f_hi == 0) {
-    const int gr = grid_for((uint64_t)a.map.nblocks * 2u, kMaxQuantGroups);
+    const int gr = grid_for((uint64_t)a.map.nblocks * 2u, kRuleGroups);
     if (bf16)
       hipLaunchKernelGGL(quantize_rule_kernel<true>, dim3(gr), dim3(kThreads), 0, s, a);
     else
@@ -2175,7 +2180,7 @@ hipError_t launch_mx_quantize(const MxArgs &a, bool bf16, hipStream_t s) {
   const int g = grid_for(a.nblocks, kMaxQuantGroups);
   const bool search = a.f_lo != 0 || a.f_hi != 0;
   if (!search) {
-    const int gr = grid_for((uint64_t)a.nblocks * 4u, kMaxQuantGroups);
+    const int gr = grid_for((uint64_t)a.nblocks * 4u, kRuleGroups);
     if (bf16)
       hipLaunchKernelGGL(mx_rule_kernel<true>, dim3(gr), dim3(kThreads), 0, s, a);
     else
